@@ -1,0 +1,359 @@
+"""NumPy front end of the C oracle (``spec_oracle.c``).
+
+TEST INFRASTRUCTURE: only the test suite, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg may import this module.  It never imports the
+HIP package and the HIP package never imports it.
+
+The functions take and return NumPy arrays; all arithmetic happens in the C
+library in fp64.  ``step_chain`` and ``tree_step`` compose the per-request
+steps in the order the pages give them (scan, estimate, select, allocate,
+verify, commit).
+"""
+from __future__ import annotations
+
+import contextlib
+import ctypes as C
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "spec_oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+# flag bits (same meanings as the library's per-request out_flags)
+ACCEPT_NEAR, SAMPLE_NEAR, SELECT_NEAR, ALLOC_NEAR, TREE_NEAR, RESIDUAL_ZERO = (1 << i for i in range(6))
+BAD_TOKEN, BAD_LOGITS, CTX_OVERFLOW = 1 << 8, 1 << 9, 1 << 10
+NEAR_MASK = ACCEPT_NEAR | SAMPLE_NEAR | SELECT_NEAR | ALLOC_NEAR | TREE_NEAR
+SLOT_POINT_MASS, SLOT_FROM_NGRAM = 1, 2
+POLICIES = {"proposed": 0, "ngram_first": 1, "extension": 2, "model_only": 3, "ngram_only": 4}
+
+
+def build(force: bool = False) -> str:
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-shared", "-fPIC",
+                               "-o", LIB, SRC, "-lm"])
+    return LIB
+
+
+_lib = None
+
+
+def _load(path):
+    h = C.CDLL(path)
+    h.oracle_estimate_logit.restype = C.c_double
+    h.oracle_chain_value.restype = C.c_double
+    h.oracle_select.restype = C.c_int
+    h.oracle_tree_build.restype = C.c_int
+    return h
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        _lib = _load(build())
+    return _lib
+
+
+def build_mutant(path: str, mutation: int) -> str:
+    """Compile the oracle with a planted mistake (see SPEC_ORACLE_MUTATION)."""
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-shared", "-fPIC",
+                           f"-DSPEC_ORACLE_MUTATION={int(mutation)}", "-o", path, SRC, "-lm"])
+    return path
+
+
+@contextlib.contextmanager
+def using_library(path: str):
+    """Temporarily route every call through another build of the oracle."""
+    global _lib
+    old = _lib
+    _lib = _load(path)
+    try:
+        yield
+    finally:
+        _lib = old
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+class _Est(C.Structure):
+    _fields_ = [("beta", C.c_double * 15)] + [(n, C.c_double) for n in (
+        "w_first", "w_rest", "delta", "l_first", "l_rest", "k_first", "k_rest",
+        "n_ref", "n_full", "m_ref", "m_cap")]
+
+
+def _est(e) -> _Est:
+    s = _Est()
+    for i in range(15):
+        s.beta[i] = float(np.float32(e.beta[i]))
+    for n in ("w_first", "w_rest", "delta", "l_first", "l_rest", "k_first", "k_rest",
+              "n_ref", "n_full", "m_ref", "m_cap"):
+        setattr(s, n, float(getattr(e, n)))
+    return s
+
+
+# ---------------------------------------------------------------------------
+# n-gram draft
+# ---------------------------------------------------------------------------
+
+def ngram_draft(ctx, ctx_len, n_min, n_max, max_draft=15, copy_cap=256,
+                query_req=None, extra=None, extra_len=None):
+    ctx = _c(ctx, np.int32)
+    ctx_len = _c(ctx_len, np.int32)
+    nq = len(query_req) if query_req is not None else ctx.shape[0]
+    qr = None if query_req is None else _c(query_req, np.int32)
+    ex = None if extra is None else _c(extra, np.int32)
+    el = None if extra_len is None else _c(extra_len, np.int32)
+    draft = np.full((nq, max_draft), -1, np.int32)
+    dlen = np.zeros(nq, np.int32)
+    feat = np.zeros((nq, 4), np.int32)
+    lib().oracle_ngram_draft(C.c_int(nq), _p(ctx), C.c_int64(ctx.shape[1]), _p(ctx_len), _p(qr), _p(ex),
+                             C.c_int64(0 if ex is None else ex.shape[1]), _p(el),
+                             C.c_int(n_min), C.c_int(n_max), C.c_int(max_draft), C.c_int(copy_cap),
+                             _p(draft), _p(dlen), _p(feat))
+    return draft, dlen, feat
+
+
+# ---------------------------------------------------------------------------
+# estimator, survivals, selection, allocation
+# ---------------------------------------------------------------------------
+
+def estimate_logit(est, k, n, a, m) -> float:
+    e = _est(est)
+    return lib().oracle_estimate_logit(C.byref(e), C.c_int(k), C.c_int(n), C.c_int(a), C.c_int(m))
+
+
+def estimate(est, n, a, m, length) -> np.ndarray:
+    e = _est(est)
+    h = np.zeros(max(length, 1), np.float64)
+    lib().oracle_estimate(C.byref(e), C.c_int(n), C.c_int(a), C.c_int(m), C.c_int(length), _p(h))
+    return h[:length]
+
+
+def survival(alpha) -> np.ndarray:
+    a = _c(alpha, np.float64)
+    S = np.zeros(max(len(a), 1), np.float64)
+    lib().oracle_survival(_p(a), C.c_int(len(a)), _p(S))
+    return S[:len(a)]
+
+
+def chain_value(S, lam) -> float:
+    S = _c(S, np.float64)
+    return lib().oracle_chain_value(_p(S), C.c_int(len(S)), C.c_double(lam))
+
+
+def sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-np.asarray(x, np.float64)))
+
+
+def select(d, c, g, h, lam, policy="proposed", model_point_mass=True, K=None, ld=15):
+    d = _c(d, np.int32)
+    c = _c(c, np.float64)
+    g = _c(g, np.int32) if len(g) else np.zeros(1, np.int32)
+    glen = len(h)
+    h = _c(h, np.float64) if glen else np.zeros(1, np.float64)
+    K = len(d) if K is None else K
+    tok = np.full(ld, -1, np.int32)
+    fl = np.zeros(ld, np.uint8)
+    S = np.zeros(ld, np.float64)
+    src = C.c_int32(0)
+    near = C.c_int(0)
+    n = lib().oracle_select(C.c_int(K), _p(d), _p(c), C.c_int(len(d)), _p(g), _p(h), C.c_int(glen),
+                            C.c_double(lam), C.c_int(POLICIES[policy]), C.c_int(int(model_point_mass)),
+                            C.c_int(ld), _p(tok), _p(fl), _p(S), C.byref(src), C.byref(near))
+    return dict(tokens=tok, flags=fl, S=S, len=n, src=src.value, near=bool(near.value))
+
+
+def allocate(lens, S, budget, flags=None):
+    lens = _c(lens, np.int32)
+    S = _c(S, np.float64)
+    bs, ld = S.shape
+    alloc = np.zeros(bs, np.int32)
+    row_base = np.zeros(bs, np.int64)
+    total = C.c_int32(0)
+    fl = np.zeros(bs, np.uint32) if flags is None else flags
+    lib().oracle_allocate(C.c_int(bs), C.c_int(ld), _p(lens), _p(S), C.c_int(budget),
+                          _p(alloc), _p(row_base), C.byref(total), _p(fl))
+    return alloc, row_base, total.value, fl
+
+
+def allocate_budget(model_tokens, model_conf, conf_is_logit, model_point_mass, ng_draft, ng_len, ng_feat,
+                    est, lam, budget, policy="proposed", ld=15):
+    """Per request: estimate h from the scan's features, survivals, select one
+    chain; then allocate the batch budget over the chosen chains."""
+    bs, K = model_tokens.shape
+    conf = np.asarray(model_conf, np.float64)
+    c_all = sigmoid(conf) if conf_is_logit else conf
+    out = dict(tokens=np.full((bs, ld), -1, np.int32), slot_flags=np.zeros((bs, ld), np.uint8),
+               S=np.zeros((bs, ld), np.float64), chain_len=np.zeros(bs, np.int32),
+               chain_src=np.zeros(bs, np.int32), h=np.zeros((bs, ld), np.float64),
+               flags=np.zeros(bs, np.uint32))
+    for r in range(bs):
+        glen = int(ng_len[r])
+        n, a, m = (int(v) for v in ng_feat[r, :3])
+        h = estimate(est, n, a, m, glen) if glen else np.zeros(0)
+        out["h"][r, :glen] = h
+        sel = select(model_tokens[r], c_all[r], ng_draft[r, :glen], h, lam, policy,
+                     bool(model_point_mass[r]), K=K, ld=ld)
+        out["tokens"][r] = sel["tokens"]
+        out["slot_flags"][r] = sel["flags"]
+        out["S"][r] = sel["S"]
+        out["chain_len"][r] = sel["len"]
+        out["chain_src"][r] = sel["src"]
+        if sel["near"]:
+            out["flags"][r] |= SELECT_NEAR
+    alloc, row_base, total, fl = allocate(out["chain_len"], out["S"], budget, out["flags"])
+    out.update(alloc_len=alloc, row_base=row_base, total_rows=total, flags=fl)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# verification
+# ---------------------------------------------------------------------------
+
+def _logits(x):
+    """Accept fp32 arrays or uint16 bf16 bit patterns; returns (array, dtype code)."""
+    if x is None:
+        return None, 0
+    if x.dtype == np.uint16:
+        return np.ascontiguousarray(x), 1
+    return np.ascontiguousarray(x, dtype=np.float32), 0
+
+
+def verify_chain(logits, row_base, tokens, slot_flags, n_slots, u_acc, u_smp, temperature,
+                 draft_logits=None, draft_row_base=None, flags=None):
+    """logits: [rows, V] (fp32 or bf16 bits); tokens/slot_flags/u_acc: [bs, ld]."""
+    lg, dt = _logits(logits)
+    dl, ddt = _logits(draft_logits)
+    V = lg.shape[-1]
+    lg2 = lg.reshape(-1, V)
+    dl2 = None if dl is None else dl.reshape(-1, V)
+    tokens = _c(tokens, np.int32)
+    bs, ld = tokens.shape
+    slot_flags = _c(slot_flags, np.uint8)
+    n_slots = _c(n_slots, np.int32)
+    u_acc = _c(u_acc, np.float32)
+    u_smp = _c(u_smp, np.float32)
+    row_base = _c(row_base, np.int64)
+    drb = None if draft_row_base is None else _c(draft_row_base, np.int64)
+    out_tokens = np.full((bs, ld + 1), -1, np.int32)
+    out_num = np.zeros(bs, np.int32)
+    out_acc = np.zeros(bs, np.int32)
+    out_p = np.zeros((bs, ld), np.float64)
+    out_q = np.zeros((bs, ld), np.float64)
+    fl = np.zeros(bs, np.uint32) if flags is None else flags.astype(np.uint32).copy()
+    lib().oracle_verify_chain(C.c_int(bs), C.c_int(V), C.c_double(temperature),
+                              _p(lg2), C.c_int(dt), C.c_int64(V), _p(row_base),
+                              _p(dl2), C.c_int(ddt), C.c_int64(V), _p(drb),
+                              _p(tokens), _p(slot_flags), C.c_int(ld), _p(n_slots), _p(u_acc), _p(u_smp),
+                              _p(out_tokens), _p(out_num), _p(out_acc), _p(out_p), _p(out_q), _p(fl))
+    return dict(out_tokens=out_tokens, out_num=out_num, out_accepted=out_acc, out_p=out_p, out_q=out_q,
+                flags=fl)
+
+
+def commit(ctx, ctx_len, ctx_cap, out_tokens, out_num, flags):
+    ctx = np.ascontiguousarray(ctx, np.int32)
+    ctx_len = np.ascontiguousarray(ctx_len, np.int32)
+    out_tokens = _c(out_tokens, np.int32)
+    out_num = _c(out_num, np.int32)
+    lib().oracle_commit(C.c_int(ctx.shape[0]), _p(ctx), C.c_int64(ctx.shape[1]), _p(ctx_len),
+                        C.c_int(ctx_cap), _p(out_tokens), C.c_int(out_tokens.shape[1]), _p(out_num), _p(flags))
+    return ctx, ctx_len
+
+
+# ---------------------------------------------------------------------------
+# trees
+# ---------------------------------------------------------------------------
+
+def tree_build(block, ng_draft, ng_len, w_node, w_none, depth_max=32, rows_cap=16):
+    """block: [P, Kc]; ng_draft: [P+1, L]; returns the verify rows and the forest."""
+    block = _c(block, np.int32)
+    P, Kc = block.shape
+    ng = _c(ng_draft, np.int32)
+    L = ng.shape[1]
+    ngl = _c(ng_len, np.int32)
+    wn = _c(w_node, np.float32)
+    wz = _c(w_none, np.float32)
+    c_max = len(wn)
+    node_token = np.full(rows_cap, -1, np.int32)
+    parent_row = np.full(rows_cap, -1, np.int32)
+    Q = np.zeros(rows_cap, np.float64)
+    n_rows = C.c_int32(0)
+    ft = np.zeros(c_max, np.int32)
+    fp = np.zeros(c_max, np.int32)
+    fk = np.zeros(c_max, np.int32)
+    fQ = np.zeros(c_max, np.float64)
+    flag = C.c_uint32(0)
+    cnt = lib().oracle_tree_build(C.c_int(P), C.c_int(Kc), _p(block), C.c_int(L), _p(ng), _p(ngl),
+                                  _p(wn), _p(wz), C.c_int(c_max), C.c_int(depth_max), C.c_int(rows_cap),
+                                  _p(node_token), _p(parent_row), _p(Q), C.byref(n_rows),
+                                  _p(ft), _p(fp), _p(fk), _p(fQ), C.byref(flag))
+    return dict(node_token=node_token, parent_row=parent_row, Q=Q, n_rows=n_rows.value, count=cnt,
+                f_token=ft[:cnt], f_parent=fp[:cnt], f_kind=fk[:cnt], f_Q=fQ[:cnt], flag=flag.value)
+
+
+def tree_build_batch(block, ng_draft, ng_len, w_node, w_none, depth_max=32, rows_cap=16):
+    """block [BS,P,Kc], ng_draft [BS*(P+1), L], ng_len [BS*(P+1)], weights [BS, c_max]."""
+    BS, P, _ = block.shape
+    L = ng_draft.shape[1]
+    ng = ng_draft.reshape(BS, P + 1, L)
+    ngl = ng_len.reshape(BS, P + 1)
+    out = dict(node_token=np.full((BS, rows_cap), -1, np.int32), parent_row=np.full((BS, rows_cap), -1, np.int32),
+               Q=np.zeros((BS, rows_cap)), n_rows=np.zeros(BS, np.int32), count=np.zeros(BS, np.int32),
+               flags=np.zeros(BS, np.uint32), forests=[])
+    for r in range(BS):
+        t = tree_build(block[r], ng[r], ngl[r], w_node[r], w_none[r], depth_max, rows_cap)
+        for k in ("node_token", "parent_row", "Q"):
+            out[k][r] = t[k]
+        out["n_rows"][r] = t["n_rows"]
+        out["count"][r] = t["count"]
+        out["flags"][r] = t["flag"]
+        out["forests"].append(t)
+    out["row_base"] = np.concatenate([[0], np.cumsum(out["n_rows"])[:-1]]).astype(np.int64)
+    return out
+
+
+def verify_tree(logits, row_base, node_token, parent_row, n_rows, flags=None):
+    lg, dt = _logits(logits)
+    V = lg.shape[-1]
+    lg2 = lg.reshape(-1, V)
+    node_token = _c(node_token, np.int32)
+    bs, rows_max = node_token.shape
+    parent_row = _c(parent_row, np.int32)
+    n_rows = _c(n_rows, np.int32)
+    row_base = _c(row_base, np.int64)
+    out_tokens = np.full((bs, rows_max), -1, np.int32)
+    out_num = np.zeros(bs, np.int32)
+    out_path = np.full((bs, rows_max), -1, np.int32)
+    out_arg = np.full((bs, rows_max), -1, np.int32)
+    fl = np.zeros(bs, np.uint32) if flags is None else flags.astype(np.uint32).copy()
+    lib().oracle_verify_tree(C.c_int(bs), C.c_int(V), _p(lg2), C.c_int(dt), C.c_int64(V), _p(row_base),
+                             _p(node_token), _p(parent_row), _p(n_rows), C.c_int(rows_max),
+                             _p(out_tokens), _p(out_num), _p(out_path), _p(out_arg), _p(fl))
+    return dict(out_tokens=out_tokens, out_num=out_num, out_path_rows=out_path, out_argmax=out_arg, flags=fl)
+
+
+# ---------------------------------------------------------------------------
+# the composed chain step (draft -> allocate -> verify -> commit)
+# ---------------------------------------------------------------------------
+
+def step_chain(ctx, ctx_len, ctx_cap, model_tokens, model_conf_logit, model_point_mass, est, lam, budget,
+               target, target_row_base, u_acc, u_smp, temperature, n_min=5, n_max=15, max_draft=15,
+               copy_cap=256, policy="proposed", ld=15):
+    """One whole step over a batch.  ``target``: [rows, V] with request r's row
+    k at ``target_row_base[r] + k``.  Returns every intermediate result."""
+    draft, dlen, feat = ngram_draft(ctx, ctx_len, n_min, n_max, max_draft, copy_cap)
+    al = allocate_budget(model_tokens, model_conf_logit, True, model_point_mass, draft, dlen, feat, est,
+                         lam, budget, policy, ld)
+    ver = verify_chain(target, target_row_base, al["tokens"], al["slot_flags"], al["alloc_len"],
+                       u_acc[:, :ld], u_smp, temperature, flags=al["flags"])
+    ctx2, len2 = commit(ctx.copy(), ctx_len.copy(), ctx_cap, ver["out_tokens"], ver["out_num"], ver["flags"])
+    return dict(draft=draft, draft_len=dlen, feat=feat, alloc=al, verify=ver, ctx=ctx2, ctx_len=len2)

@@ -1,0 +1,141 @@
+"""Oracle pins: tree build (AdaSpark Section 3.1 Proposition 1, Section 3.3 n-gram
+fill) and greedy tree verification (Section 2.2)."""
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+
+
+def random_forest_inputs(rng, P, Kc, L, V=6):
+    block = np.zeros((P, Kc), np.int32)
+    for p in range(P):
+        block[p] = rng.choice(V, Kc, replace=False)
+    ng = np.full((P + 1, L), -1, np.int32)
+    ngl = rng.integers(0, L + 1, P + 1).astype(np.int32)
+    for s in range(P + 1):
+        ng[s, :ngl[s]] = rng.integers(0, V, ngl[s])
+    c_max = 1 + P * Kc + (P + 1) * L
+    return block, ng, ngl, rng.standard_exponential(c_max).astype(np.float32), \
+        rng.standard_exponential(c_max).astype(np.float32)
+
+
+def parent_closed_best(parent, Q, k):
+    """Max sum of Q over all parent-closed sets of k non-anchor nodes."""
+    nodes = range(1, len(parent))
+    best = -1.0
+    for comb in itertools.combinations(nodes, k):
+        s = set(comb) | {0}
+        if all(parent[j] in s for j in comb):
+            best = max(best, sum(Q[j] for j in comb))
+    return best
+
+
+def test_proposition1_best_first_prefix_is_optimal_tree():
+    rng = np.random.Generator(np.random.Philox(31))
+    checked = 0
+    for trial in range(60):
+        P, Kc, L = int(rng.integers(1, 4)), int(rng.integers(1, 3)), int(rng.integers(0, 3))
+        block, ng, ngl, wn, wz = random_forest_inputs(rng, P, Kc, max(L, 1))
+        full = O.tree_build(block, ng, ngl, wn, wz, rows_cap=64)
+        cnt = full["count"]
+        if cnt > 13:
+            continue
+        fpar, fQ = full["f_parent"], full["f_Q"]
+        assert all(fpar[j] < j for j in range(1, cnt))          # parents precede children
+        assert all(fQ[j] <= fQ[fpar[j]] for j in range(1, cnt))
+        for rows in range(2, cnt + 1):
+            t = O.tree_build(block, ng, ngl, wn, wz, rows_cap=rows)
+            n = t["n_rows"]
+            assert n == rows
+            pr = t["parent_row"][:n]
+            assert pr[0] == -1 and all(0 <= pr[i] < i for i in range(1, n))   # depth-first, a tree
+            got = t["Q"][1:n].sum()
+            assert got == pytest.approx(parent_closed_best(fpar, fQ, rows - 1), rel=1e-12)
+            checked += 1
+    assert checked > 100
+
+
+def test_uniform_weights_give_equal_shares():
+    # all weights 1: each of a parent's c children gets q = 1/(c+1) (the 'none'
+    # outcome takes the same share), so Q is a product of such shares
+    P, Kc, L = 3, 2, 4
+    block = np.array([[1, 2], [3, 4], [5, 0]], np.int32)
+    ng = np.full((P + 1, L), -1, np.int32)
+    ngl = np.zeros(P + 1, np.int32)
+    c_max = 1 + P * Kc + (P + 1) * L
+    t = O.tree_build(block, ng, ngl, np.ones(c_max, np.float32), np.ones(c_max, np.float32), rows_cap=64)
+    fQ = t["f_Q"]
+    assert fQ[1] == pytest.approx(1 / 3) and fQ[2] == pytest.approx(1 / 3)       # position 1 under anchor
+    assert fQ[3] == pytest.approx(1 / 9) and fQ[5] == pytest.approx(1 / 27)
+
+
+def test_ngram_fill_agrees_and_branches():
+    P, Kc, L = 3, 2, 6
+    block = np.array([[10, 11], [20, 21], [30, 31]], np.int32)
+    ng = np.full((P + 1, L), -1, np.int32)
+    ngl = np.zeros(P + 1, np.int32)
+    ng[0, :5] = [10, 20, 99, 98, 97]      # follows two picks, then branches below pick 2
+    ngl[0] = 5
+    ng[2, :2] = [31, 50]                  # from pick 2: agrees with a sibling at position 3, then new
+    ngl[2] = 2
+    c_max = 1 + P * Kc + (P + 1) * L
+    t = O.tree_build(block, ng, ngl, np.ones(c_max, np.float32), np.ones(c_max, np.float32), rows_cap=64)
+    tok, par, kind = t["f_token"], t["f_parent"], t["f_kind"]
+    assert t["count"] == 1 + 6 + 3 + 1
+    assert kind[1] & 4 and kind[3] & 4                 # picks 1, 2 agreed
+    assert list(tok[7:10]) == [99, 98, 97] and par[7] == 3 and par[8] == 7 and par[9] == 8
+    assert kind[6] & 4 and tok[10] == 50 and par[10] == 6   # sibling (30/31 rank 1) agreed, then new node
+    # depth limit: nothing deeper than depth_max below the anchor
+    t2 = O.tree_build(block, ng, ngl, np.ones(c_max, np.float32), np.ones(c_max, np.float32),
+                      depth_max=3, rows_cap=64)
+    assert t2["count"] == 1 + 6 + 1 + 0     # only 99 at depth 3 from the anchor chain; 50 would be depth 4
+
+
+def chain_tree(tokens):
+    n = len(tokens) + 1
+    node_token = np.full(n, -1, np.int32)
+    node_token[1:] = tokens
+    parent = np.arange(-1, n - 1, dtype=np.int32)
+    return node_token, parent
+
+
+def test_chain_tree_equals_chain_verify_at_t0():
+    rng = np.random.Generator(np.random.Philox(5))
+    V, B, bs = 40, 6, 64
+    z = rng.standard_normal((bs, B + 1, V)).astype(np.float32)
+    am = np.argmax(z, -1)
+    y = np.where(rng.random((bs, B)) < 0.7, am[:, :B], rng.integers(0, V, (bs, B))).astype(np.int32)
+    ch = O.verify_chain(z.reshape(-1, V), np.arange(bs) * (B + 1), y, np.ones((bs, B), np.uint8),
+                        np.full(bs, B, np.int32), np.zeros((bs, B), np.float32), np.zeros(bs, np.float32), 0.0)
+    nt = np.zeros((bs, B + 1), np.int32)
+    pr = np.zeros((bs, B + 1), np.int32)
+    for r in range(bs):
+        nt[r], pr[r] = chain_tree(y[r])
+    tr = O.verify_tree(z.reshape(-1, V), np.arange(bs) * (B + 1), nt, pr, np.full(bs, B + 1, np.int32))
+    assert np.array_equal(tr["out_num"], ch["out_num"])
+    for r in range(bs):
+        n = ch["out_num"][r]
+        assert list(tr["out_tokens"][r, :n]) == list(ch["out_tokens"][r, :n])
+
+
+def test_tree_walk_is_greedy_decode_of_markov_target():
+    # rows are a Markov target p(.|token of the row's node); the committed
+    # tokens are the greedy continuation for as long as the tree holds it
+    rng = np.random.Generator(np.random.Philox(6))
+    V = 5
+    Z = rng.standard_normal((V, V)).astype(np.float32)
+    g = [int(np.argmax(Z[0]))]
+    for _ in range(8):
+        g.append(int(np.argmax(Z[g[-1]])))
+    # tree: anchor (token 0) -> greedy path of 4 nodes, plus wrong siblings
+    node_token = [-1, g[0], (g[0] + 1) % V, g[1], g[2], (g[2] + 2) % V, g[3]]
+    parent = [-1, 0, 0, 1, 3, 3, 4]
+    rows = np.stack([Z[0 if i == 0 else node_token[i]] for i in range(len(node_token))])
+    res = O.verify_tree(rows, np.array([0]), np.array([node_token], np.int32), np.array([parent], np.int32),
+                        np.array([len(node_token)], np.int32))
+    assert res["out_num"][0] == 5 and list(res["out_tokens"][0, :5]) == g[:5]
+    assert list(res["out_path_rows"][0, :5]) == [0, 1, 3, 4, 6]
+    # at most one child of an accepted node matches: a path
+    assert len(set(res["out_path_rows"][0, :5])) == 5
