@@ -1,0 +1,15 @@
+"""MI355X (gfx950) speculative-decoding step: n-gram draft, verification-budget
+allocation, lossless chain verification and greedy tree verification.
+
+The compute lives in ``libspec_hip.so`` (hand-written HIP kernels behind the C
+ABI of include/spec.h); this package is its thin binding.
+"""
+from ._lib import (  # noqa: F401
+    LIB_PATH,
+    POLICIES,
+    spec_allocate_budget,
+    spec_ngram_draft,
+    spec_verify_chain,
+    spec_verify_tree,
+)
+from . import _lib  # noqa: F401

@@ -1,0 +1,384 @@
+"""ctypes binding of ``libspec_hip.so`` (the C ABI declared in include/spec.h).
+
+Argument marshalling only: every function takes ``torch`` device tensors,
+allocates outputs and workspace with torch (device memory plumbing), and calls
+the C entry point of the same name on the current HIP stream.  No step of the
+method runs here, and there is no fallback: if the library is missing the
+import fails.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspec_hip.so")
+
+i32, i64, f32, vp, sz = C.c_int32, C.c_int64, C.c_float, C.c_void_p, C.c_size_t
+
+# ---- constants mirrored from spec.h ----------------------------------------
+SPEC_OK, SPEC_EINVAL, SPEC_EWORKSPACE, SPEC_EHIP = 0, -1, -2, -3
+SPEC_F32, SPEC_BF16 = 0, 1
+FLAG_RESIDUAL_ZERO, FLAG_BAD_TOKEN, FLAG_BAD_LOGITS, FLAG_CTX_OVERFLOW, FLAG_BAD_LENGTH = (
+    1 << 5, 1 << 8, 1 << 9, 1 << 10, 1 << 11)
+SLOT_POINT_MASS, SLOT_FROM_NGRAM = 1, 2
+SRC_MODEL, SRC_NGRAM, SRC_MERGED, SRC_EXTENDED = 0, 1, 2, 3
+POLICIES = {"proposed": 0, "ngram_first": 1, "extension": 2, "model_only": 3, "ngram_only": 4}
+ALLOC_CHAIN, ALLOC_TREE = 0, 1
+OP_NGRAM, OP_ALLOCATE, OP_VERIFY_CHAIN, OP_VERIFY_TREE = 0, 1, 2, 3
+MAX_DRAFT, MAX_CAP, MAX_ROWS, MAX_FOREST = 32, 1024, 64, 1024
+
+
+class NgramArgs(C.Structure):
+    _fields_ = [("bs", i32), ("nq", i32), ("ctx", vp), ("ctx_stride", i64), ("ctx_len", vp),
+                ("query_req", vp), ("extra", vp), ("extra_stride", i64), ("extra_len", vp),
+                ("n_min", i32), ("n_max", i32), ("max_draft", i32), ("copy_cap", i32),
+                ("draft", vp), ("draft_len", vp), ("feat", vp), ("workspace", vp), ("workspace_bytes", sz)]
+
+
+class Estimator(C.Structure):
+    _fields_ = [("beta", f32 * 15)] + [(n, f32) for n in (
+        "w_first", "w_rest", "delta", "l_first", "l_rest", "k_first", "k_rest",
+        "n_ref", "n_full", "m_ref", "m_cap")]
+
+
+class ChainAlloc(C.Structure):
+    _fields_ = [("bs", i32), ("K", i32), ("ld", i32), ("model_tokens", vp), ("model_conf", vp),
+                ("conf_is_logit", i32), ("model_point_mass", vp), ("ngram_draft", vp), ("ngram_ld", i32),
+                ("ngram_len", vp), ("ngram_feat", vp), ("est", Estimator), ("lam", f32), ("budget", i32),
+                ("policy", i32), ("chain_tokens", vp), ("slot_flags", vp), ("chain_len", vp), ("chain_src", vp),
+                ("survival", vp), ("alloc_len", vp), ("row_base", vp), ("total_rows", vp), ("out_flags", vp)]
+
+
+class TreeAlloc(C.Structure):
+    _fields_ = [("bs", i32), ("P", i32), ("Kc", i32), ("block", vp), ("ngram_draft", vp), ("ngram_ld", i32),
+                ("ngram_len", vp), ("w_node", vp), ("w_none", vp), ("c_max", i32), ("depth_max", i32),
+                ("rows_cap", i32), ("node_token", vp), ("parent_row", vp), ("Q", vp), ("n_rows", vp),
+                ("row_base", vp), ("total_rows", vp), ("forest_count", vp), ("out_flags", vp)]
+
+
+class AllocArgs(C.Structure):
+    _fields_ = [("mode", i32), ("chain", ChainAlloc), ("tree", TreeAlloc), ("workspace", vp),
+                ("workspace_bytes", sz)]
+
+
+class VerifyArgs(C.Structure):
+    _fields_ = [("bs", i32), ("vocab", i32), ("temperature", f32), ("logits", vp), ("dtype", i32),
+                ("row_stride", i64), ("row_base", vp), ("n_logit_rows", i64), ("draft_logits", vp),
+                ("draft_dtype", i32), ("draft_row_stride", i64), ("draft_row_base", vp), ("n_draft_rows", i64),
+                ("tokens", vp), ("slot_flags", vp), ("ld", i32), ("n_slots", vp), ("u_accept", vp),
+                ("u_sample", vp), ("out_tokens", vp), ("out_num", vp), ("out_accepted", vp), ("out_p", vp),
+                ("out_q", vp), ("out_flags", vp), ("ctx", vp), ("ctx_stride", i64), ("ctx_len", vp),
+                ("ctx_cap", i32), ("workspace", vp), ("workspace_bytes", sz)]
+
+
+class TreeVerifyArgs(C.Structure):
+    _fields_ = [("bs", i32), ("vocab", i32), ("rows_max", i32), ("logits", vp), ("dtype", i32),
+                ("row_stride", i64), ("row_base", vp), ("n_logit_rows", i64), ("node_token", vp),
+                ("parent_row", vp), ("n_rows", vp), ("out_tokens", vp), ("out_num", vp), ("out_path_rows", vp),
+                ("out_argmax", vp), ("out_flags", vp), ("ctx", vp), ("ctx_stride", i64), ("ctx_len", vp),
+                ("ctx_cap", i32), ("workspace", vp), ("workspace_bytes", sz)]
+
+
+STRUCTS = {"spec_ngram_args": NgramArgs, "spec_estimator": Estimator, "spec_chain_alloc": ChainAlloc,
+           "spec_tree_alloc": TreeAlloc, "spec_alloc_args": AllocArgs, "spec_verify_args": VerifyArgs,
+           "spec_tree_verify_args": TreeVerifyArgs}
+EXPORTS = ("spec_ngram_draft", "spec_allocate_budget", "spec_verify_chain", "spec_verify_tree",
+           "spec_workspace_bytes", "spec_strerror", "spec_last_hip_error", "spec_abi_version")
+
+
+def load(path: str = LIB_PATH) -> C.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+                          "(the HIP path has no fallback)")
+    lib = C.CDLL(path)
+    for name in ("spec_ngram_draft", "spec_allocate_budget", "spec_verify_chain", "spec_verify_tree"):
+        getattr(lib, name).argtypes = [vp, vp]
+        getattr(lib, name).restype = C.c_int
+    lib.spec_workspace_bytes.argtypes = [C.c_int, vp]
+    lib.spec_workspace_bytes.restype = sz
+    lib.spec_strerror.argtypes = [C.c_int]
+    lib.spec_strerror.restype = C.c_char_p
+    lib.spec_last_hip_error.restype = C.c_char_p
+    lib.spec_abi_version.restype = C.c_int
+    return lib
+
+
+_lib: Optional[C.CDLL] = None
+
+
+def lib() -> C.CDLL:
+    global _lib
+    if _lib is None:
+        _lib = load()
+    return _lib
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, dtype, name, dim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims")
+    return t
+
+
+def _stream(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return C.c_void_p(s.cuda_stream)
+
+
+def _check(rc: int):
+    if rc != SPEC_OK:
+        l = lib()
+        msg = l.spec_strerror(rc).decode()
+        if rc == SPEC_EHIP:
+            msg += ": " + l.spec_last_hip_error().decode()
+        raise RuntimeError(f"libspec_hip: {msg} (code {rc})")
+
+
+def _workspace(op, args, device, workspace):
+    need = lib().spec_workspace_bytes(op, C.byref(args))
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=device)
+    elif workspace.numel() < need + 256:
+        raise ValueError(f"workspace too small: {workspace.numel()} < {need + 256}")
+    base = workspace.data_ptr()
+    aligned = (base + 255) // 256 * 256
+    return workspace, (aligned, need)
+
+
+def _logits_dtype(t):
+    if t.dtype == torch.float32:
+        return SPEC_F32
+    if t.dtype == torch.bfloat16:
+        return SPEC_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _rows2d(t, name):
+    if t.dim() < 2:
+        raise ValueError(f"{name} must be [..., V]")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name} rows must be contiguous")
+    t2 = t.reshape(-1, t.shape[-1]) if t.is_contiguous() else t
+    if t2.dim() != 2:
+        raise ValueError(f"{name} must be reshapeable to [rows, V]")
+    return t2
+
+
+def estimator_struct(est) -> Estimator:
+    s = Estimator()
+    for i in range(15):
+        s.beta[i] = float(est.beta[i])
+    for n in ("w_first", "w_rest", "delta", "l_first", "l_rest", "k_first", "k_rest",
+              "n_ref", "n_full", "m_ref", "m_cap"):
+        setattr(s, n, float(getattr(est, n)))
+    return s
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def spec_ngram_draft(ctx, ctx_len, n_min, n_max, max_draft=15, copy_cap=256, query_req=None, extra=None,
+                     extra_len=None, out=None, workspace=None, stream=None):
+    """N-gram drafts for every query; returns (draft [nq, max_draft], draft_len [nq], feat [nq, 4])."""
+    _dev(ctx, torch.int32, "ctx", 2)
+    _dev(ctx_len, torch.int32, "ctx_len", 1)
+    dev = ctx.device
+    nq = query_req.shape[0] if query_req is not None else ctx.shape[0]
+    if query_req is not None:
+        _dev(query_req, torch.int32, "query_req", 1)
+    if extra is not None:
+        _dev(extra, torch.int32, "extra", 2)
+        _dev(extra_len, torch.int32, "extra_len", 1)
+    if out is None:
+        out = (torch.empty((nq, max_draft), dtype=torch.int32, device=dev),
+               torch.empty(nq, dtype=torch.int32, device=dev),
+               torch.empty((nq, 4), dtype=torch.int32, device=dev))
+    draft, dlen, feat = out
+    a = NgramArgs(bs=ctx.shape[0], nq=nq, ctx=_ptr(ctx), ctx_stride=ctx.shape[1], ctx_len=_ptr(ctx_len),
+                  query_req=_ptr(query_req), extra=_ptr(extra),
+                  extra_stride=0 if extra is None else extra.shape[1], extra_len=_ptr(extra_len),
+                  n_min=n_min, n_max=n_max, max_draft=max_draft, copy_cap=copy_cap,
+                  draft=_ptr(draft), draft_len=_ptr(dlen), feat=_ptr(feat))
+    ws, w = _workspace(OP_NGRAM, a, dev, workspace)
+    if w:
+        a.workspace, a.workspace_bytes = w
+    _check(lib().spec_ngram_draft(C.byref(a), _stream(dev, stream)))
+    return draft, dlen, feat
+
+
+def _chain_alloc(model_tokens, model_conf, ngram_draft, ngram_len, ngram_feat, est, lam, budget,
+                 policy="proposed", conf_is_logit=True, model_point_mass=None, ld=15, out=None,
+                 workspace=None, stream=None):
+    _dev(model_tokens, torch.int32, "model_tokens", 2)
+    _dev(model_conf, torch.float32, "model_conf", 2)
+    _dev(ngram_draft, torch.int32, "ngram_draft", 2)
+    _dev(ngram_len, torch.int32, "ngram_len", 1)
+    _dev(ngram_feat, torch.int32, "ngram_feat", 2)
+    if model_point_mass is not None:
+        _dev(model_point_mass, torch.uint8, "model_point_mass", 1)
+    bs, K = model_tokens.shape
+    dev = model_tokens.device
+    if out is None:
+        out = dict(chain_tokens=torch.empty((bs, ld), dtype=torch.int32, device=dev),
+                   slot_flags=torch.empty((bs, ld), dtype=torch.uint8, device=dev),
+                   chain_len=torch.empty(bs, dtype=torch.int32, device=dev),
+                   chain_src=torch.empty(bs, dtype=torch.int32, device=dev),
+                   survival=torch.empty((bs, ld), dtype=torch.float32, device=dev),
+                   alloc_len=torch.empty(bs, dtype=torch.int32, device=dev),
+                   row_base=torch.empty(bs, dtype=torch.int64, device=dev),
+                   total_rows=torch.empty(1, dtype=torch.int32, device=dev),
+                   out_flags=torch.empty(bs, dtype=torch.int32, device=dev))
+    ca = ChainAlloc(bs=bs, K=K, ld=ld, model_tokens=_ptr(model_tokens), model_conf=_ptr(model_conf),
+                    conf_is_logit=int(conf_is_logit), model_point_mass=_ptr(model_point_mass),
+                    ngram_draft=_ptr(ngram_draft), ngram_ld=ngram_draft.shape[1], ngram_len=_ptr(ngram_len),
+                    ngram_feat=_ptr(ngram_feat), est=estimator_struct(est), lam=float(lam), budget=int(budget),
+                    policy=POLICIES[policy] if isinstance(policy, str) else int(policy),
+                    **{k: _ptr(v) for k, v in out.items()})
+    a = AllocArgs(mode=ALLOC_CHAIN, chain=ca)
+    ws, w = _workspace(OP_ALLOCATE, a, dev, workspace)
+    if w:
+        a.workspace, a.workspace_bytes = w
+    _check(lib().spec_allocate_budget(C.byref(a), _stream(dev, stream)))
+    return out
+
+
+def _tree_alloc(block, ngram_draft, ngram_len, w_node, w_none, depth_max=32, rows_cap=16, out=None,
+                stream=None):
+    _dev(block, torch.int32, "block", 3)
+    _dev(ngram_draft, torch.int32, "ngram_draft", 2)
+    _dev(ngram_len, torch.int32, "ngram_len", 1)
+    _dev(w_node, torch.float32, "w_node", 2)
+    _dev(w_none, torch.float32, "w_none", 2)
+    bs, P, Kc = block.shape
+    dev = block.device
+    if out is None:
+        out = dict(node_token=torch.empty((bs, rows_cap), dtype=torch.int32, device=dev),
+                   parent_row=torch.empty((bs, rows_cap), dtype=torch.int32, device=dev),
+                   Q=torch.empty((bs, rows_cap), dtype=torch.float32, device=dev),
+                   n_rows=torch.empty(bs, dtype=torch.int32, device=dev),
+                   row_base=torch.empty(bs, dtype=torch.int64, device=dev),
+                   total_rows=torch.empty(1, dtype=torch.int32, device=dev),
+                   forest_count=torch.empty(bs, dtype=torch.int32, device=dev),
+                   out_flags=torch.empty(bs, dtype=torch.int32, device=dev))
+    ta = TreeAlloc(bs=bs, P=P, Kc=Kc, block=_ptr(block), ngram_draft=_ptr(ngram_draft),
+                   ngram_ld=ngram_draft.shape[1], ngram_len=_ptr(ngram_len), w_node=_ptr(w_node),
+                   w_none=_ptr(w_none), c_max=w_node.shape[1], depth_max=depth_max, rows_cap=rows_cap,
+                   **{k: _ptr(v) for k, v in out.items()})
+    a = AllocArgs(mode=ALLOC_TREE, tree=ta)
+    _check(lib().spec_allocate_budget(C.byref(a), _stream(dev, stream)))
+    return out
+
+
+def spec_allocate_budget(mode="chain", **kw):
+    """Chain mode: chain selection + budget allocation; tree mode: best-first tree build."""
+    if mode == "chain":
+        return _chain_alloc(**kw)
+    if mode == "tree":
+        return _tree_alloc(**kw)
+    raise ValueError(mode)
+
+
+def spec_verify_chain(logits, row_base, tokens, n_slots, temperature, u_accept=None, u_sample=None,
+                      slot_flags=None, draft_logits=None, draft_row_base=None, out_flags=None,
+                      ctx=None, ctx_len=None, ctx_cap=None, out=None, workspace=None, stream=None):
+    """Rejection-sampling verification of one chain per request (optional commit into ctx)."""
+    lg = _rows2d(logits, "logits")
+    _dev(row_base, torch.int64, "row_base", 1)
+    _dev(tokens, torch.int32, "tokens", 2)
+    _dev(n_slots, torch.int32, "n_slots", 1)
+    bs, ld = tokens.shape
+    dev = tokens.device
+    if slot_flags is not None:
+        _dev(slot_flags, torch.uint8, "slot_flags", 2)
+    if u_accept is not None:
+        _dev(u_accept, torch.float32, "u_accept", 2)
+        if u_accept.shape != (bs, ld):
+            raise ValueError("u_accept must be [bs, ld]")
+        _dev(u_sample, torch.float32, "u_sample", 1)
+    dl = None
+    if draft_logits is not None:
+        dl = _rows2d(draft_logits, "draft_logits")
+        _dev(draft_row_base, torch.int64, "draft_row_base", 1)
+    if out is None:
+        out = dict(out_tokens=torch.empty((bs, ld + 1), dtype=torch.int32, device=dev),
+                   out_num=torch.empty(bs, dtype=torch.int32, device=dev),
+                   out_accepted=torch.empty(bs, dtype=torch.int32, device=dev),
+                   out_p=torch.empty((bs, ld), dtype=torch.float32, device=dev),
+                   out_q=torch.empty((bs, ld), dtype=torch.float32, device=dev))
+    if out_flags is None:
+        out_flags = torch.zeros(bs, dtype=torch.int32, device=dev)
+    out["out_flags"] = out_flags
+    a = VerifyArgs(bs=bs, vocab=lg.shape[1], temperature=float(temperature), logits=_ptr(lg),
+                   dtype=_logits_dtype(lg), row_stride=lg.stride(0), row_base=_ptr(row_base),
+                   n_logit_rows=lg.shape[0], tokens=_ptr(tokens), slot_flags=_ptr(slot_flags), ld=ld,
+                   n_slots=_ptr(n_slots), u_accept=_ptr(u_accept), u_sample=_ptr(u_sample),
+                   **{k: _ptr(v) for k, v in out.items()})
+    if dl is not None:
+        a.draft_logits, a.draft_dtype, a.draft_row_stride = _ptr(dl), _logits_dtype(dl), dl.stride(0)
+        a.draft_row_base, a.n_draft_rows = _ptr(draft_row_base), dl.shape[0]
+    if ctx is not None:
+        _dev(ctx, torch.int32, "ctx", 2)
+        _dev(ctx_len, torch.int32, "ctx_len", 1)
+        a.ctx, a.ctx_stride, a.ctx_len = _ptr(ctx), ctx.shape[1], _ptr(ctx_len)
+        a.ctx_cap = ctx.shape[1] if ctx_cap is None else int(ctx_cap)
+    ws, w = _workspace(OP_VERIFY_CHAIN, a, dev, workspace)
+    if w:
+        a.workspace, a.workspace_bytes = w
+    _check(lib().spec_verify_chain(C.byref(a), _stream(dev, stream)))
+    return out
+
+
+def spec_verify_tree(logits, row_base, node_token, parent_row, n_rows, out_flags=None, ctx=None, ctx_len=None,
+                     ctx_cap=None, out=None, workspace=None, stream=None):
+    """Greedy verification of one tree per request (optional commit into ctx)."""
+    lg = _rows2d(logits, "logits")
+    _dev(row_base, torch.int64, "row_base", 1)
+    _dev(node_token, torch.int32, "node_token", 2)
+    _dev(parent_row, torch.int32, "parent_row", 2)
+    _dev(n_rows, torch.int32, "n_rows", 1)
+    bs, rm = node_token.shape
+    dev = node_token.device
+    if out is None:
+        out = dict(out_tokens=torch.empty((bs, rm), dtype=torch.int32, device=dev),
+                   out_num=torch.empty(bs, dtype=torch.int32, device=dev),
+                   out_path_rows=torch.empty((bs, rm), dtype=torch.int32, device=dev),
+                   out_argmax=torch.empty((bs, rm), dtype=torch.int32, device=dev))
+    if out_flags is None:
+        out_flags = torch.zeros(bs, dtype=torch.int32, device=dev)
+    out["out_flags"] = out_flags
+    a = TreeVerifyArgs(bs=bs, vocab=lg.shape[1], rows_max=rm, logits=_ptr(lg), dtype=_logits_dtype(lg),
+                       row_stride=lg.stride(0), row_base=_ptr(row_base), n_logit_rows=lg.shape[0],
+                       node_token=_ptr(node_token), parent_row=_ptr(parent_row), n_rows=_ptr(n_rows),
+                       **{k: _ptr(v) for k, v in out.items()})
+    if ctx is not None:
+        _dev(ctx, torch.int32, "ctx", 2)
+        _dev(ctx_len, torch.int32, "ctx_len", 1)
+        a.ctx, a.ctx_stride, a.ctx_len = _ptr(ctx), ctx.shape[1], _ptr(ctx_len)
+        a.ctx_cap = ctx.shape[1] if ctx_cap is None else int(ctx_cap)
+    ws, w = _workspace(OP_VERIFY_TREE, a, dev, workspace)
+    if w:
+        a.workspace, a.workspace_bytes = w
+    _check(lib().spec_verify_tree(C.byref(a), _stream(dev, stream)))
+    return out

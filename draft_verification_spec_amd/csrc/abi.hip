@@ -1,0 +1,203 @@
+// C-ABI entry points: argument validation, workspace sizing, dispatch.
+// Every host-detectable error returns before anything is enqueued.
+#include <string.h>
+
+#include "common.hpp"
+
+size_t spec_ngram_ws(const spec_ngram_args* a);
+int spec_ngram_launch(const spec_ngram_args* a, hipStream_t st);
+size_t spec_alloc_ws(const spec_alloc_args* a);
+int spec_alloc_launch(const spec_alloc_args* a, hipStream_t st);
+size_t spec_verify_chain_ws(int32_t bs, int32_t vocab, int32_t ld);
+int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st);
+size_t spec_verify_tree_ws(int32_t bs, int32_t vocab, int32_t rows_max);
+int spec_verify_tree_launch(const spec_tree_verify_args* a, hipStream_t st);
+
+static thread_local char g_hip_error[256] = "";
+
+int spec_record_hip_error(hipError_t e)
+{
+    if (e == hipSuccess) return SPEC_OK;
+    const char* s = hipGetErrorString(e);
+    strncpy(g_hip_error, s ? s : "unknown HIP error", sizeof(g_hip_error) - 1);
+    g_hip_error[sizeof(g_hip_error) - 1] = 0;
+    return SPEC_EHIP;
+}
+
+#define REQUIRE(c) \
+    do {           \
+        if (!(c)) return SPEC_EINVAL; \
+    } while (0)
+
+static int check_ngram(const spec_ngram_args* a)
+{
+    REQUIRE(a);
+    REQUIRE(a->bs >= 1 && a->nq >= 0);
+    REQUIRE(a->ctx && a->ctx_len && a->ctx_stride >= 1);
+    REQUIRE(a->query_req || a->nq <= a->bs);
+    REQUIRE(!a->extra || (a->extra_len && a->extra_stride >= 0));
+    REQUIRE(a->ctx_stride + (a->extra ? a->extra_stride : 0) < ((int64_t)1 << 31));
+    REQUIRE(a->n_min >= 1 && a->n_max >= a->n_min);
+    REQUIRE(a->max_draft >= 1 && a->max_draft <= SPEC_MAX_DRAFT);
+    REQUIRE(a->copy_cap >= a->n_min && a->copy_cap <= SPEC_MAX_CAP);
+    REQUIRE(a->nq == 0 || (a->draft && a->draft_len && a->feat));
+    return SPEC_OK;
+}
+
+static int check_chain_alloc(const spec_chain_alloc* c)
+{
+    REQUIRE(c->bs >= 1 && c->bs < (1 << 27) - 1);
+    REQUIRE(c->ld >= 1 && c->ld <= SPEC_MAX_DRAFT);
+    REQUIRE(c->K >= 0 && c->K <= c->ld);
+    REQUIRE(c->ngram_ld >= 0 && c->ngram_ld <= c->ld);
+    REQUIRE(c->K == 0 || (c->model_tokens && c->model_conf));
+    REQUIRE(c->ngram_draft && c->ngram_len && c->ngram_feat);
+    REQUIRE(c->budget >= 0);
+    REQUIRE(c->policy >= SPEC_POLICY_PROPOSED && c->policy <= SPEC_POLICY_NGRAM_ONLY);
+    REQUIRE(c->lambda == c->lambda);
+    REQUIRE(c->chain_tokens && c->slot_flags && c->chain_len && c->chain_src && c->survival);
+    REQUIRE(c->alloc_len && c->row_base && c->total_rows && c->out_flags);
+    return SPEC_OK;
+}
+
+static int check_tree_alloc(const spec_tree_alloc* t)
+{
+    REQUIRE(t->bs >= 1);
+    REQUIRE(t->P >= 0 && t->Kc >= 1);
+    REQUIRE(t->P == 0 || t->block);
+    REQUIRE(t->c_max >= 1 + t->P * t->Kc && t->c_max <= SPEC_MAX_FOREST);
+    REQUIRE(t->ngram_ld >= 0 && (t->ngram_ld == 0 || t->ngram_draft) && t->ngram_len);
+    REQUIRE(t->w_node && t->w_none);
+    REQUIRE(t->depth_max >= 1);
+    REQUIRE(t->rows_cap >= 1 && t->rows_cap <= SPEC_MAX_ROWS);
+    REQUIRE(t->node_token && t->parent_row && t->Q && t->n_rows && t->row_base && t->total_rows);
+    REQUIRE(t->forest_count && t->out_flags);
+    return SPEC_OK;
+}
+
+static int check_alloc(const spec_alloc_args* a)
+{
+    REQUIRE(a);
+    if (a->mode == SPEC_ALLOC_CHAIN) return check_chain_alloc(&a->chain);
+    if (a->mode == SPEC_ALLOC_TREE) return check_tree_alloc(&a->tree);
+    return SPEC_EINVAL;
+}
+
+static bool dtype_ok(int dt) { return dt == SPEC_F32 || dt == SPEC_BF16; }
+
+static int check_verify(const spec_verify_args* a)
+{
+    REQUIRE(a);
+    REQUIRE(a->bs >= 1 && a->vocab >= 1);
+    REQUIRE(a->temperature >= 0.0f && a->temperature < 1e30f);
+    REQUIRE(a->logits && a->row_base && dtype_ok(a->dtype) && a->row_stride >= a->vocab && a->n_logit_rows >= 1);
+    if (a->draft_logits) {
+        REQUIRE(a->draft_row_base && dtype_ok(a->draft_dtype));
+        REQUIRE(a->draft_row_stride >= a->vocab && a->n_draft_rows >= 1);
+    }
+    REQUIRE(a->tokens && a->n_slots && a->ld >= 1 && a->ld <= SPEC_MAX_DRAFT);
+    REQUIRE(a->temperature == 0.0f || (a->u_accept && a->u_sample));
+    REQUIRE(a->out_tokens && a->out_num && a->out_accepted && a->out_flags);
+    if (a->ctx) REQUIRE(a->ctx_len && a->ctx_cap >= 0 && a->ctx_cap <= a->ctx_stride);
+    return SPEC_OK;
+}
+
+static int check_tree_verify(const spec_tree_verify_args* a)
+{
+    REQUIRE(a);
+    REQUIRE(a->bs >= 1 && a->vocab >= 1);
+    REQUIRE(a->rows_max >= 1 && a->rows_max <= SPEC_MAX_ROWS);
+    REQUIRE(a->logits && a->row_base && dtype_ok(a->dtype) && a->row_stride >= a->vocab && a->n_logit_rows >= 1);
+    REQUIRE(a->node_token && a->parent_row && a->n_rows);
+    REQUIRE(a->out_tokens && a->out_num && a->out_path_rows && a->out_flags);
+    if (a->ctx) REQUIRE(a->ctx_len && a->ctx_cap >= 0 && a->ctx_cap <= a->ctx_stride);
+    return SPEC_OK;
+}
+
+static int check_workspace(void* ws, size_t have, size_t need)
+{
+    if (need == 0) return SPEC_OK;
+    if (!ws || have < need) return SPEC_EWORKSPACE;
+    if ((uintptr_t)ws % 256 != 0) return SPEC_EWORKSPACE;
+    return SPEC_OK;
+}
+
+extern "C" {
+
+int spec_abi_version(void) { return SPEC_ABI_VERSION; }
+
+const char* spec_strerror(int code)
+{
+    switch (code) {
+    case SPEC_OK: return "ok";
+    case SPEC_EINVAL: return "invalid argument";
+    case SPEC_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case SPEC_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+const char* spec_last_hip_error(void) { return g_hip_error; }
+
+size_t spec_workspace_bytes(int op, const void* args)
+{
+    if (!args) return 0;
+    switch (op) {
+    case SPEC_OP_NGRAM: {
+        const spec_ngram_args* a = (const spec_ngram_args*)args;
+        return check_ngram(a) == SPEC_OK ? spec_ngram_ws(a) : 0;
+    }
+    case SPEC_OP_ALLOCATE: {
+        const spec_alloc_args* a = (const spec_alloc_args*)args;
+        return check_alloc(a) == SPEC_OK ? spec_alloc_ws(a) : 0;
+    }
+    case SPEC_OP_VERIFY_CHAIN: {
+        const spec_verify_args* a = (const spec_verify_args*)args;
+        return check_verify(a) == SPEC_OK ? spec_verify_chain_ws(a->bs, a->vocab, a->ld) : 0;
+    }
+    case SPEC_OP_VERIFY_TREE: {
+        const spec_tree_verify_args* a = (const spec_tree_verify_args*)args;
+        return check_tree_verify(a) == SPEC_OK ? spec_verify_tree_ws(a->bs, a->vocab, a->rows_max) : 0;
+    }
+    default: return 0;
+    }
+}
+
+int spec_ngram_draft(const spec_ngram_args* a, void* stream)
+{
+    int rc = check_ngram(a);
+    if (rc) return rc;
+    rc = check_workspace(a->workspace, a->workspace_bytes, spec_ngram_ws(a));
+    if (rc) return rc;
+    if (a->nq == 0) return SPEC_OK;
+    return spec_ngram_launch(a, (hipStream_t)stream);
+}
+
+int spec_allocate_budget(const spec_alloc_args* a, void* stream)
+{
+    int rc = check_alloc(a);
+    if (rc) return rc;
+    rc = check_workspace(a->workspace, a->workspace_bytes, spec_alloc_ws(a));
+    if (rc) return rc;
+    return spec_alloc_launch(a, (hipStream_t)stream);
+}
+
+int spec_verify_chain(const spec_verify_args* a, void* stream)
+{
+    int rc = check_verify(a);
+    if (rc) return rc;
+    rc = check_workspace(a->workspace, a->workspace_bytes, spec_verify_chain_ws(a->bs, a->vocab, a->ld));
+    if (rc) return rc;
+    return spec_verify_chain_launch(a, (hipStream_t)stream);
+}
+
+int spec_verify_tree(const spec_tree_verify_args* a, void* stream)
+{
+    int rc = check_tree_verify(a);
+    if (rc) return rc;
+    rc = check_workspace(a->workspace, a->workspace_bytes, spec_verify_tree_ws(a->bs, a->vocab, a->rows_max));
+    if (rc) return rc;
+    return spec_verify_tree_launch(a, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+// Internal helpers shared by the HIP kernels of libspec_hip (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "spec.h"
+
+namespace spec {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// launch geometry shared by host launchers and workspace sizing
+// ---------------------------------------------------------------------------
+
+// Logit rows are cut into chunks of a multiple of 64 elements (so every chunk
+// start keeps 16-byte alignment for fp32 and bf16); enough chunks are used to
+// put about `target_blocks` workgroups in flight across the batch.
+struct RowSplit {
+    int64_t chunk;   // elements per chunk
+    int32_t splits;  // chunks per row
+};
+
+inline RowSplit row_split(int32_t bs, int32_t vocab, int32_t target_blocks = 2048)
+{
+    int64_t want = (target_blocks + bs - 1) / (bs > 0 ? bs : 1);
+    int64_t max_splits = vocab / 2048;            // keep chunks >= 2048 elements
+    if (max_splits < 1) max_splits = 1;
+    if (want > max_splits) want = max_splits;
+    if (want < 1) want = 1;
+    int64_t chunk = (vocab + want - 1) / want;
+    chunk = (chunk + 63) / 64 * 64;
+    RowSplit s;
+    s.chunk = chunk;
+    s.splits = (int32_t)((vocab + chunk - 1) / chunk);
+    return s;
+}
+
+constexpr int64_t kNgramChunk = 2048;            // end positions per scan workgroup
+
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __uint_as_float(h << 16); }
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v)
+{
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        T u = __shfl_xor(v, o, kWave);
+        v = u > v ? u : v;
+    }
+    return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v)
+{
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        uint64_t u = __shfl_xor(v, o, kWave);
+        v = u > v ? u : v;
+    }
+    return v;
+}
+
+// Top-2 of unique 64-bit keys (0 = empty).
+struct Top2 {
+    uint64_t a, b;  // a > b or b == 0
+};
+
+__device__ __forceinline__ Top2 top2_merge(Top2 x, Top2 y)
+{
+    Top2 r;
+    if (x.a >= y.a) {
+        r.a = x.a;
+        r.b = x.b > y.a ? x.b : y.a;
+    } else {
+        r.a = y.a;
+        r.b = y.b > x.a ? y.b : x.a;
+    }
+    return r;
+}
+
+__device__ __forceinline__ Top2 top2_insert(Top2 t, uint64_t k)
+{
+    if (k > t.a) {
+        t.b = t.a;
+        t.a = k;
+    } else if (k > t.b) {
+        t.b = k;
+    }
+    return t;
+}
+
+__device__ __forceinline__ Top2 wave_top2(Top2 t)
+{
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        Top2 u;
+        u.a = __shfl_xor(t.a, o, kWave);
+        u.b = __shfl_xor(t.b, o, kWave);
+        t = top2_merge(t, u);
+    }
+    return t;
+}
+
+}  // namespace spec
+
+// Host-side launch status bookkeeping (defined in abi.hip).
+int spec_record_hip_error(hipError_t e);

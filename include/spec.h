@@ -1,0 +1,338 @@
+/*
+ * spec.h -- C ABI of the GPU-resident speculative-decoding step for MI355X
+ * (gfx950): n-gram draft, verification-budget allocation (chains and trees),
+ * lossless chain verification by rejection sampling, greedy tree
+ * verification.
+ *
+ * Sources (page titles):
+ *   [HS] "Hybrid Spark: Adaptive Speculative Decoding That Lets the Content
+ *        Choose the Drafter"
+ *   [AS] "AdaSpark: Adaptive DSpark with Online Learning for Tree Verification
+ *        and N-gram Fill"
+ *   [LS] "Efficient speculative decoding with a fixed-cost parallel drafter"
+ *        (LongSpark), Section 2.1
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers marked "device" are HIP device (or managed) memory; everything
+ *   else is host memory read during the call.  The caller owns every buffer.
+ *   The library keeps no state between calls and allocates nothing: scratch
+ *   memory comes from the caller's `workspace` (query its size with
+ *   spec_workspace_bytes; any alignment of 256 bytes is enough).
+ * - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *   and the call returns at once.  The library never synchronises, never
+ *   copies device to host and never calls hipDeviceSynchronize, so a whole
+ *   step can be captured in a HIP graph.
+ * - Return value: SPEC_OK, or a negative code.  A host-detectable error
+ *   (null pointer, bad size, bad enum, short workspace) enqueues nothing.  A
+ *   launch failure returns SPEC_EHIP; spec_last_hip_error() names it.
+ * - Data errors only the device can see never fault: they set bits in the
+ *   per-request out_flags (SPEC_FLAG_*) and the request's outputs follow the
+ *   documented fallback.
+ * - Calls are re-entrant and thread-safe; calls that share output or
+ *   workspace buffers must be ordered by the caller (same stream).
+ */
+#ifndef SPEC_H
+#define SPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_ABI_VERSION 1
+
+/* ---- return codes ---------------------------------------------------- */
+#define SPEC_OK          0
+#define SPEC_EINVAL     (-1)  /* null pointer, bad size or enum             */
+#define SPEC_EWORKSPACE (-2)  /* workspace missing or smaller than needed   */
+#define SPEC_EHIP       (-3)  /* a HIP launch or query failed               */
+
+/* ---- logits element types --------------------------------------------- */
+#define SPEC_F32  0
+#define SPEC_BF16 1           /* upcast to fp32 exactly on load             */
+
+/* ---- per-request out_flags bits ---------------------------------------- */
+#define SPEC_FLAG_RESIDUAL_ZERO (1u << 5)  /* residual had no mass: sampled from p  */
+#define SPEC_FLAG_BAD_TOKEN     (1u << 8)  /* a draft token outside [0, vocab): the
+                                              slot is rejected                       */
+#define SPEC_FLAG_BAD_LOGITS    (1u << 9)  /* a read row had NaN/+Inf, or no finite
+                                              entry; its outputs are unspecified     */
+#define SPEC_FLAG_CTX_OVERFLOW  (1u << 10) /* commit skipped: context capacity       */
+#define SPEC_FLAG_BAD_LENGTH    (1u << 11) /* a length argument was clamped          */
+
+/* ---- slot flags (chain slots) ----------------------------------------- */
+#define SPEC_SLOT_POINT_MASS 1u  /* verify as a point mass, q = delta_y         */
+#define SPEC_SLOT_FROM_NGRAM 2u  /* the token came from the n-gram chain        */
+
+/* ---- chosen-chain source ---------------------------------------------- */
+#define SPEC_SRC_MODEL    0
+#define SPEC_SRC_NGRAM    1
+#define SPEC_SRC_MERGED   2   /* contains rule: n-gram chain, merged survivals */
+#define SPEC_SRC_EXTENDED 3   /* extension policy: model chain + n-gram tail   */
+
+/* ---- chain-selection policies ([HS] Section 4.3, Appendix H) ----------- */
+#define SPEC_POLICY_PROPOSED    0  /* contains rule, then value rule at lambda */
+#define SPEC_POLICY_NGRAM_FIRST 1  /* n-gram chain whenever it matched          */
+#define SPEC_POLICY_EXTENSION   2  /* model chain; append n-gram tail if prefix */
+#define SPEC_POLICY_MODEL_ONLY  3
+#define SPEC_POLICY_NGRAM_ONLY  4
+
+/* ---- allocation modes --------------------------------------------------- */
+#define SPEC_ALLOC_CHAIN 0
+#define SPEC_ALLOC_TREE  1
+
+/* ---- operation ids for spec_workspace_bytes ------------------------------ */
+#define SPEC_OP_NGRAM        0
+#define SPEC_OP_ALLOCATE     1
+#define SPEC_OP_VERIFY_CHAIN 2
+#define SPEC_OP_VERIFY_TREE  3
+
+/* Limits. */
+#define SPEC_MAX_DRAFT   32   /* n-gram draft length, chain leading dim      */
+#define SPEC_MAX_CAP   1024   /* n-gram comparison cap (copy_cap)            */
+#define SPEC_MAX_ROWS    64   /* tree rows per request                       */
+#define SPEC_MAX_FOREST 1024  /* tree candidates per request                 */
+
+/* ========================================================================
+ * spec_ngram_draft -- prompt-lookup n-gram drafter ([HS] Section 4.1 "One
+ * step", Section 4.2 match features; Algorithm 1, the NGRAMSCAN call).
+ *
+ * For query q its text x is ctx[req][0 .. ctx_len[req]) followed by
+ * extra[q][0 .. extra_len[q]), with req = query_req ? query_req[q] : q.  Every
+ * earlier end position j (j <= |x|-2) has a match length l_j, the number of
+ * trailing tokens of x[..j] equal to the trailing tokens of x, compared up to
+ * min(j+1, copy_cap).  Among positions with l_j >= n_min the best is the
+ * longest, ties to the latest j; the runner-up is the next in that order.
+ * Outputs: draft[q] = up to max_draft tokens after the best match (padded
+ * with -1), draft_len[q], and feat[q] = (n, a, m, j) with
+ * n = min(l_best, n_max), m = l_best if l_best >= n_max else 0, a = 1 if there
+ * is no runner-up or it is followed by the same token, j = best end position
+ * (-1 and zeros when nothing matched).  Integer only; deterministic.
+ * Lengths outside [0, stride] are clamped.
+ * ======================================================================== */
+typedef struct spec_ngram_args {
+    int32_t bs;                  /* requests (rows of ctx)                        */
+    int32_t nq;                  /* queries                                       */
+    const int32_t* ctx;          /* device [bs, ctx_stride] token ids             */
+    int64_t ctx_stride;          /* elements between request rows, >= 1          */
+    const int32_t* ctx_len;      /* device [bs]                                   */
+    const int32_t* query_req;    /* device [nq] or NULL (then nq <= bs)           */
+    const int32_t* extra;        /* device [nq, extra_stride] or NULL             */
+    int64_t extra_stride;        /* 0 when extra is NULL                          */
+    const int32_t* extra_len;    /* device [nq] or NULL                           */
+    int32_t n_min;               /* >= 1                                          */
+    int32_t n_max;               /* >= n_min                                      */
+    int32_t max_draft;           /* 1 .. SPEC_MAX_DRAFT                           */
+    int32_t copy_cap;            /* n_min .. SPEC_MAX_CAP (256 on the pages)      */
+    int32_t* draft;              /* device [nq, max_draft]                        */
+    int32_t* draft_len;          /* device [nq]                                   */
+    int32_t* feat;               /* device [nq, 4]                                */
+    void* workspace;             /* device scratch                                */
+    size_t workspace_bytes;
+} spec_ngram_args;
+
+/* ========================================================================
+ * spec_allocate_budget
+ *
+ * Chain mode ([HS] Algorithm 1, Sections 4.2-4.4): per request, the n-gram
+ * acceptance estimates (Eq. (1)),
+ *   h_k = sigmoid(beta_k + w_pos(k)(n - n_ref) + delta a
+ *                 + [n >= n_full](l_pos(k) + kappa_pos(k) ln(min(m, m_cap)/m_ref))),
+ * the survivals S^g_k = prod h, S^d_k = prod c (c = model confidences), one
+ * chosen chain per request by `policy` (proposed: contains rule, else value
+ * rule V = sum_k max(S_k - lambda, 0) with ties to the n-gram chain, Eq. (3)),
+ * and the batch-wide allocation of `budget` draft slots to the highest
+ * survivals (ties: lower position, then lower request; keys are the
+ * survivals rounded to fp32), so every request keeps a prefix.  Rows per
+ * request = allocated slots + 1; row_base is their exclusive prefix sum.
+ * Estimates, survivals and values are computed in fp64.
+ *
+ * Tree mode ([AS] Sections 2.2, 3.1, 3.3): the candidate forest of a drafter
+ * block (P positions x Kc ranked candidates: the pick at p hangs from the pick
+ * at p-1, siblings from the same parent) plus n-gram chains from the anchor
+ * and each pick (a step equal to an existing child descends into it, else a
+ * new node; no node deeper than depth_max); acceptance estimates by the form
+ * of Eq. (6), q_j = w_node[j] / (w_none[parent] + sum of w_node over the
+ * parent's children), Q = product of q along the path; the best rows_cap-1
+ * candidates by Q (ties to the lower index) laid out depth-first (row 0 = the
+ * anchor, children in index order).
+ * ======================================================================== */
+typedef struct spec_estimator {
+    float beta[15];              /* per-position intercepts                       */
+    float w_first, w_rest;       /* match-length weights                          */
+    float delta;                 /* agreement weight                              */
+    float l_first, l_rest;       /* full-match bonus                              */
+    float k_first, k_rest;       /* copy-length weights                           */
+    float n_ref;                 /* 5 on the pages                                */
+    float n_full;                /* 15                                            */
+    float m_ref;                 /* 15                                            */
+    float m_cap;                 /* 256                                           */
+} spec_estimator;
+
+typedef struct spec_chain_alloc {
+    int32_t bs;
+    int32_t K;                   /* model chain length (7), 0..ld                 */
+    int32_t ld;                  /* leading dim of chain outputs, max(K,L)..32    */
+    const int32_t* model_tokens; /* device [bs, K]                                */
+    const float* model_conf;     /* device [bs, K] confidences                    */
+    int32_t conf_is_logit;       /* 1: model_conf are logits (c = sigmoid)        */
+    const uint8_t* model_point_mass; /* device [bs] (1 = greedy drafting) or NULL = all 1 */
+    const int32_t* ngram_draft;  /* device [bs, ngram_ld] (spec_ngram_draft)      */
+    int32_t ngram_ld;            /* <= ld                                         */
+    const int32_t* ngram_len;    /* device [bs]                                   */
+    const int32_t* ngram_feat;   /* device [bs, 4]                                */
+    spec_estimator est;
+    float lambda;                /* slot price                                    */
+    int32_t budget;              /* b*, verified draft slots for the batch, >= 0  */
+    int32_t policy;              /* SPEC_POLICY_*                                 */
+    int32_t* chain_tokens;       /* device [bs, ld], -1 padded                    */
+    uint8_t* slot_flags;         /* device [bs, ld] SPEC_SLOT_*                   */
+    int32_t* chain_len;          /* device [bs]                                   */
+    int32_t* chain_src;          /* device [bs] SPEC_SRC_*                        */
+    float* survival;             /* device [bs, ld] (0 past chain_len)            */
+    int32_t* alloc_len;          /* device [bs] slots to verify (a chain prefix)  */
+    int64_t* row_base;           /* device [bs]                                   */
+    int32_t* total_rows;         /* device [1] = budget used + bs                 */
+    uint32_t* out_flags;         /* device [bs], written (not OR-ed)              */
+} spec_chain_alloc;
+
+typedef struct spec_tree_alloc {
+    int32_t bs;
+    int32_t P;                   /* drafter block positions                      */
+    int32_t Kc;                  /* ranked candidates per position               */
+    const int32_t* block;        /* device [bs, P, Kc], rank 0 = the pick         */
+    const int32_t* ngram_draft;  /* device [bs*(P+1), ngram_ld]: source s = 0 is
+                                    the anchor, s = i the pick at position i      */
+    int32_t ngram_ld;
+    const int32_t* ngram_len;    /* device [bs*(P+1)]                             */
+    const float* w_node;         /* device [bs, c_max] > 0, by candidate index    */
+    const float* w_none;         /* device [bs, c_max] > 0, 'none' of a parent    */
+    int32_t c_max;               /* 1 + P*Kc .. SPEC_MAX_FOREST                   */
+    int32_t depth_max;           /* >= 1 (32 on the pages)                        */
+    int32_t rows_cap;            /* 1 .. SPEC_MAX_ROWS                            */
+    int32_t* node_token;         /* device [bs, rows_cap] (row 0: -1)             */
+    int32_t* parent_row;         /* device [bs, rows_cap] (row 0: -1)             */
+    float* Q;                    /* device [bs, rows_cap]                         */
+    int32_t* n_rows;             /* device [bs]                                   */
+    int64_t* row_base;           /* device [bs] exclusive prefix sum of n_rows    */
+    int32_t* total_rows;         /* device [1]                                    */
+    int32_t* forest_count;       /* device [bs] candidates incl. the anchor       */
+    uint32_t* out_flags;         /* device [bs], written                          */
+} spec_tree_alloc;
+
+typedef struct spec_alloc_args {
+    int32_t mode;                /* SPEC_ALLOC_CHAIN or SPEC_ALLOC_TREE           */
+    spec_chain_alloc chain;
+    spec_tree_alloc tree;
+    void* workspace;
+    size_t workspace_bytes;
+} spec_alloc_args;
+
+/* ========================================================================
+ * spec_verify_chain -- lossless verification of one chain per request
+ * ([LS] Section 2.1 with the speculative-sampling rule that [HS] Section 2
+ * cites; point-mass slots per [HS] Section 5.8 and Appendix H).
+ *
+ * Request r has b = n_slots[r] slots with tokens y_1..y_b.  Target row
+ * row_base[r] + k (k = 0..b) scores slot k+1 (k = b is the bonus row); draft
+ * row draft_row_base[r] + k scores slot k+1 for probabilistic slots.
+ * T > 0: p = softmax(z/T), q = softmax(w/T) (q = delta_y for point-mass
+ * slots); slot i is accepted iff u_accept[r][i] < p(y_i)/q(y_i) (fp64); at
+ * the first rejection the correction is drawn from norm(max(0, p - q)), or
+ * the bonus from p of row b when all pass, by inverse CDF in token order with
+ * u_sample[r].  T = 0: accept iff y_i = argmax z (ties to the lowest id); the
+ * correction / bonus is the argmax.  Out: out_tokens[r][0..out_num) = the
+ * accepted tokens then the correction or bonus, out_num = accepted + 1,
+ * out_p / out_q = p(y_i) / q(y_i) for every slot (q = 1 for point masses and
+ * at T = 0, where p is 1 or 0).  out_flags is OR-ed.  If ctx is not NULL the
+ * emitted tokens are appended to ctx[r] at ctx_len[r] (skipped and flagged if
+ * ctx_len + out_num > ctx_cap).  n_slots outside [0, ld] are clamped.
+ * ======================================================================== */
+typedef struct spec_verify_args {
+    int32_t bs;
+    int32_t vocab;
+    float temperature;           /* >= 0; 0 = greedy                              */
+    const void* logits;          /* device target rows                            */
+    int32_t dtype;               /* SPEC_F32 / SPEC_BF16                          */
+    int64_t row_stride;          /* elements between rows, >= vocab               */
+    const int64_t* row_base;     /* device [bs]                                   */
+    int64_t n_logit_rows;        /* rows in the logits buffer: a row index outside
+                                    [0, n_logit_rows) is never read (flagged)     */
+    const void* draft_logits;    /* device draft rows; NULL if every slot is a
+                                    point mass or T = 0                           */
+    int32_t draft_dtype;
+    int64_t draft_row_stride;
+    const int64_t* draft_row_base; /* device [bs] or NULL with draft_logits       */
+    int64_t n_draft_rows;        /* rows in the draft buffer                      */
+    const int32_t* tokens;       /* device [bs, ld]                               */
+    const uint8_t* slot_flags;   /* device [bs, ld] or NULL = all point masses    */
+    int32_t ld;                  /* 1 .. SPEC_MAX_DRAFT                           */
+    const int32_t* n_slots;      /* device [bs]                                   */
+    const float* u_accept;       /* device [bs, ld] uniforms in [0,1)             */
+    const float* u_sample;       /* device [bs]                                   */
+    int32_t* out_tokens;         /* device [bs, ld+1], -1 padded                  */
+    int32_t* out_num;            /* device [bs]                                   */
+    int32_t* out_accepted;       /* device [bs]                                   */
+    float* out_p;                /* device [bs, ld] or NULL                       */
+    float* out_q;                /* device [bs, ld] or NULL                       */
+    uint32_t* out_flags;         /* device [bs], OR-ed                            */
+    int32_t* ctx;                /* optional commit: device [bs, ctx_stride]      */
+    int64_t ctx_stride;
+    int32_t* ctx_len;            /* device [bs]                                   */
+    int32_t ctx_cap;             /* <= ctx_stride                                 */
+    void* workspace;
+    size_t workspace_bytes;
+} spec_verify_args;
+
+/* ========================================================================
+ * spec_verify_tree -- greedy tree verification ([AS] Section 2.2): starting
+ * at the anchor (row 0), a child is accepted when its token equals the
+ * argmax (ties to the lowest id) of its parent's row; the accepted nodes form
+ * one path; out_tokens = the path's tokens then the argmax at its last node,
+ * out_num = path length + 1, out_path_rows = the rows of the anchor and the
+ * accepted nodes.  T = 0 only.  Optional commit as in spec_verify_chain.
+ * ======================================================================== */
+typedef struct spec_tree_verify_args {
+    int32_t bs;
+    int32_t vocab;
+    int32_t rows_max;            /* leading dim of the tree arrays, <= SPEC_MAX_ROWS */
+    const void* logits;          /* device rows                                   */
+    int32_t dtype;
+    int64_t row_stride;
+    const int64_t* row_base;     /* device [bs]                                   */
+    int64_t n_logit_rows;        /* rows in the logits buffer (bounds)            */
+    const int32_t* node_token;   /* device [bs, rows_max]                         */
+    const int32_t* parent_row;   /* device [bs, rows_max]                         */
+    const int32_t* n_rows;       /* device [bs], 1..rows_max (clamped)            */
+    int32_t* out_tokens;         /* device [bs, rows_max]                         */
+    int32_t* out_num;            /* device [bs]                                   */
+    int32_t* out_path_rows;      /* device [bs, rows_max]                         */
+    int32_t* out_argmax;         /* device [bs, rows_max] or NULL                 */
+    uint32_t* out_flags;         /* device [bs], OR-ed                            */
+    int32_t* ctx;
+    int64_t ctx_stride;
+    int32_t* ctx_len;
+    int32_t ctx_cap;
+    void* workspace;
+    size_t workspace_bytes;
+} spec_tree_verify_args;
+
+int spec_ngram_draft(const spec_ngram_args* args, void* stream);
+int spec_allocate_budget(const spec_alloc_args* args, void* stream);
+int spec_verify_chain(const spec_verify_args* args, void* stream);
+int spec_verify_tree(const spec_tree_verify_args* args, void* stream);
+
+/* Workspace bytes the call with these arguments needs (0 = none); a host-only
+ * query that reads sizes from args and never touches device memory. */
+size_t spec_workspace_bytes(int op, const void* args);
+const char* spec_strerror(int code);
+const char* spec_last_hip_error(void);   /* thread-local, last SPEC_EHIP cause */
+int spec_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPEC_H */

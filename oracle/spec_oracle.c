@@ -150,7 +150,8 @@ void oracle_ngram_draft(int nq, const int32_t* ctx, int64_t ctx_stride, const in
  * [HS] Section 4.2, Eq. (1):
  *   h_k = sigma(beta_k + w_pos(k) (n - n_ref) + delta a
  *               + [n >= n_full] (l_pos(k) + kappa_pos(k) ln(min(m, m_cap) / m_ref)))
- * with pos(k) = first iff k = 1.  The copy term's garbled form is read as
+ * with pos(k) = first iff k = 1 (positions past 15, beyond the pages'
+ * chains, reuse beta_15).  The copy term's garbled form is read as
  * ln(min(m,256)/15), the reading under which a 256-token copy adds
  * kappa_first ln(256/15) ~ 5.7 logits (Appendix D).  m >= 1 whenever the
  * term applies in consistent settings; the clamp only guards others.
@@ -164,7 +165,8 @@ typedef struct {
 double oracle_estimate_logit(const oracle_estimator* e, int k, int n, int a, int m)
 {
     int first = (k == 1);
-    double z = e->beta[k - 1] + (first ? e->w_first : e->w_rest) * ((double)n - e->n_ref)
+    /* positions past the fifteenth share the last intercept */
+    double z = e->beta[(k <= 15 ? k : 15) - 1] + (first ? e->w_first : e->w_rest) * ((double)n - e->n_ref)
              + e->delta * (double)a;
     if ((double)n >= e->n_full) {
         double mm = (double)m;

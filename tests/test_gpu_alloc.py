@@ -1,0 +1,133 @@
+"""GPU parity: spec_allocate_budget (chains and trees) against the oracle, on
+the oracle's own upstream n-gram outputs."""
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from tests.gpu_helpers import assert_close, assert_rows_equal, dev, host, ok_rows
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_chain_alloc(model_tokens, conf, conf_is_logit, pm, draft, dlen, feat, est, lam, budget, policy, ld=15):
+    import torch
+    import draft_verification_spec_amd as S
+    print(f"alloc chain: bs {model_tokens.shape[0]} budget {budget} lambda {lam} policy {policy}", flush=True)
+    out = S.spec_allocate_budget(mode="chain", model_tokens=dev(model_tokens), model_conf=dev(conf),
+                                 ngram_draft=dev(draft), ngram_len=dev(dlen), ngram_feat=dev(feat), est=est,
+                                 lam=lam, budget=budget, policy=policy, conf_is_logit=conf_is_logit,
+                                 model_point_mass=None if pm is None else dev(pm), ld=ld)
+    torch.cuda.synchronize()
+    return {k: host(v) for k, v in out.items()}
+
+
+def compare_chain_alloc(g, o, budget):
+    ok = ok_rows(o["flags"])
+    for k in ("tokens", "slot_flags"):
+        assert_rows_equal(g["chain_tokens" if k == "tokens" else k], o[k], ok, k)
+    assert_rows_equal(g["chain_len"], o["chain_len"], ok, "chain_len")
+    assert_rows_equal(g["chain_src"], o["chain_src"], ok, "chain_src")
+    assert_rows_equal(g["alloc_len"], o["alloc_len"], ok, "alloc_len")
+    assert_close(g["survival"], o["S"], "survival")
+    # row bases: consistent with the GPU's own allocation, equal to the oracle's
+    # up to the first excused request
+    rb = np.concatenate([[0], np.cumsum(g["alloc_len"] + 1)[:-1]])
+    assert np.array_equal(g["row_base"], rb)
+    first_bad = np.argmin(ok) if not ok.all() else len(ok)
+    assert np.array_equal(g["row_base"][:first_bad + 1][:len(ok)], o["row_base"][:first_bad + 1][:len(ok)])
+    assert g["total_rows"][0] == int(g["alloc_len"].sum()) + len(ok)
+    if ok.all():
+        assert g["total_rows"][0] == o["total_rows"]
+    assert g["alloc_len"].sum() == min(budget, int(g["chain_len"].sum()))
+    assert np.all(g["alloc_len"] <= g["chain_len"])
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_chain_alloc_configs(cfg):
+    c = synth.config2() if cfg == 2 else synth.config4()
+    draft, dlen, feat = O.ngram_draft(c["ctx"], c["ctx_len"], c["n_min"], c["n_max"], 15, 256)
+    o = O.allocate_budget(c["model_tokens"], c["model_conf_logit"], True, c["model_point_mass"], draft, dlen, feat,
+                          c["estimator"], c["lam"], c["budget"], "proposed", ld=15)
+    g = gpu_chain_alloc(c["model_tokens"], c["model_conf_logit"], True, c["model_point_mass"], draft, dlen, feat,
+                        c["estimator"], c["lam"], c["budget"], "proposed")
+    compare_chain_alloc(g, o, c["budget"])
+    print("sources:", np.bincount(g["chain_src"], minlength=4), "flags excused:", (~ok_rows(o["flags"])).sum())
+
+
+@pytest.mark.parametrize("policy", list(O.POLICIES))
+def test_chain_alloc_random_policies(policy):
+    rng = np.random.Generator(np.random.Philox(500 + O.POLICIES[policy]))
+    bs, K, ld = 300, 7, 15
+    truth = rng.integers(0, 50, (bs, 20)).astype(np.int32)
+    d = truth[:, :K].copy()
+    flip = rng.random((bs, K)) < 0.3
+    d[flip] = rng.integers(0, 50, int(flip.sum()))
+    dlen = rng.integers(0, 16, bs).astype(np.int32)
+    draft = np.full((bs, 15), -1, np.int32)
+    for r in range(bs):
+        draft[r, :dlen[r]] = truth[r, :dlen[r]] if rng.random() < 0.5 else rng.integers(0, 50, dlen[r])
+    draft[:20, :K] = d[:20]                       # contains-rule cases
+    dlen[:20] = np.maximum(dlen[:20], K + 1)
+    for r in range(20):
+        draft[r, K:dlen[r]] = rng.integers(0, 50, dlen[r] - K)
+    n = np.where(dlen > 0, rng.integers(5, 16, bs), 0)
+    feat = np.stack([n, rng.integers(0, 2, bs), np.where(n >= 15, rng.integers(15, 400, bs), 0),
+                     np.full(bs, 3)], 1).astype(np.int32)
+    conf = rng.standard_normal((bs, K)).astype(np.float32) + 1
+    pm = (rng.random(bs) < 0.5).astype(np.uint8)
+    est = synth.estimator_qwen3_4b()
+    for budget in (0, 1, 257, 10_000):
+        for lam in (0.0, 0.309):
+            o = O.allocate_budget(d, conf, True, pm, draft, dlen, feat, est, lam, budget, policy, ld=ld)
+            g = gpu_chain_alloc(d, conf, True, pm, draft, dlen, feat, est, lam, budget, policy)
+            compare_chain_alloc(g, o, budget)
+    # probabilities instead of logits
+    probs = (1 / (1 + np.exp(-conf.astype(np.float64)))).astype(np.float32)
+    o = O.allocate_budget(d, probs, False, pm, draft, dlen, feat, est, 0.309, 100, policy, ld=ld)
+    g = gpu_chain_alloc(d, probs, False, pm, draft, dlen, feat, est, 0.309, 100, policy)
+    compare_chain_alloc(g, o, 100)
+
+
+def test_tree_build_config3():
+    import torch
+    import draft_verification_spec_amd as S
+    c = synth.config3_inputs()
+    qr, ex, el = synth.tree_queries(c["ctx"], c["ctx_len"], c["block"])
+    draft, dlen, feat = O.ngram_draft(c["ctx"], c["ctx_len"], c["n_min"], c["n_max"], c["L"], 256,
+                                      query_req=qr, extra=ex, extra_len=el)
+    o = O.tree_build_batch(c["block"], draft, dlen, c["w_node"], c["w_none"], c["depth_max"], c["rows_cap"])
+    print("tree build: bs", c["BS"], "forest sizes", o["count"].min(), o["count"].max(), flush=True)
+    g = S.spec_allocate_budget(mode="tree", block=dev(c["block"]), ngram_draft=dev(draft), ngram_len=dev(dlen),
+                               w_node=dev(c["w_node"]), w_none=dev(c["w_none"]), depth_max=c["depth_max"],
+                               rows_cap=c["rows_cap"])
+    torch.cuda.synchronize()
+    g = {k: host(v) for k, v in g.items()}
+    ok = ok_rows(o["flags"])
+    assert_rows_equal(g["forest_count"], o["count"], np.ones(len(ok), bool), "forest_count")
+    for k in ("node_token", "parent_row", "n_rows"):
+        assert_rows_equal(g[k], o[k], ok, k)
+    assert_close(g["Q"], o["Q"], "Q")
+    if ok.all():
+        assert np.array_equal(g["row_base"], o["row_base"])
+    assert g["total_rows"][0] == g["n_rows"].sum()
+    # small random forests, all row caps
+    rng = np.random.Generator(np.random.Philox(9))
+    BS, P, Kc, L = 40, 3, 3, 6
+    block = np.stack([np.stack([rng.choice(8, Kc, replace=False) for _ in range(P)]) for _ in range(BS)]).astype(np.int32)
+    ngl = rng.integers(0, L + 1, BS * (P + 1)).astype(np.int32)
+    ng = rng.integers(0, 8, (BS * (P + 1), L)).astype(np.int32)
+    cm = 1 + P * Kc + (P + 1) * L
+    wn = rng.standard_exponential((BS, cm)).astype(np.float32)
+    wz = rng.standard_exponential((BS, cm)).astype(np.float32)
+    for rows_cap in (1, 2, 5, 16, 40):
+        for dmax in (1, 2, 32):
+            o = O.tree_build_batch(block, ng, ngl, wn, wz, dmax, rows_cap)
+            g = S.spec_allocate_budget(mode="tree", block=dev(block), ngram_draft=dev(ng), ngram_len=dev(ngl),
+                                       w_node=dev(wn), w_none=dev(wz), depth_max=dmax, rows_cap=rows_cap)
+            torch.cuda.synchronize()
+            g = {k: host(v) for k, v in g.items()}
+            ok = ok_rows(o["flags"])
+            for k in ("node_token", "parent_row", "n_rows"):
+                assert_rows_equal(g[k], o[k], ok, f"{k} cap {rows_cap} depth {dmax}")
+            assert_close(g["Q"], o["Q"], "Q")

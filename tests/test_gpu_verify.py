@@ -1,0 +1,179 @@
+"""GPU parity: spec_verify_chain and spec_verify_tree against the oracle.
+
+Token decisions must be bit-exact except for requests the oracle flags as
+near ties; p(y), q(y) within 1e-5 relative."""
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from tests.gpu_helpers import assert_close, assert_rows_equal, dev, excused_fraction, host, ok_rows
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def as_logits(x):
+    """numpy fp32 or bf16 bits -> torch tensor on the GPU (bf16 kept as bf16)."""
+    import torch
+    if x.dtype == np.uint16:
+        return synth.as_torch_bf16(x).to("cuda:0")
+    return dev(x)
+
+
+def verify_both(target, row_base, tokens, flags, n_slots, u_acc, u_smp, T, draft=None, drow_base=None, tag=""):
+    import torch
+    import draft_verification_spec_amd as S
+    V = target.shape[-1]
+    print(f"verify chain {tag}: bs {tokens.shape[0]} ld {tokens.shape[1]} V {V} T {T} "
+          f"dtype {target.dtype} draft {draft is not None}", flush=True)
+    g = S.spec_verify_chain(as_logits(target).reshape(-1, V), dev(row_base.astype(np.int64)), dev(tokens),
+                            dev(n_slots), T, u_accept=dev(u_acc), u_sample=dev(u_smp), slot_flags=dev(flags),
+                            draft_logits=None if draft is None else as_logits(draft).reshape(-1, V),
+                            draft_row_base=None if draft is None else dev(drow_base.astype(np.int64)))
+    torch.cuda.synchronize()
+    g = {k: host(v) for k, v in g.items()}
+    o = O.verify_chain(target.reshape(-1, V), row_base, tokens, flags, n_slots, u_acc, u_smp, T,
+                       draft_logits=None if draft is None else draft.reshape(-1, V), draft_row_base=drow_base)
+    ok = ok_rows(o["flags"])
+    assert_rows_equal(g["out_num"], o["out_num"], ok, "out_num")
+    assert_rows_equal(g["out_accepted"], o["out_accepted"], ok, "out_accepted")
+    assert_rows_equal(g["out_tokens"], o["out_tokens"], ok, "out_tokens")
+    ld = tokens.shape[1]
+    live = np.arange(ld)[None, :] < n_slots[:, None]
+    assert_close(g["out_p"], o["out_p"], "p(y)", mask=live)
+    assert_close(g["out_q"], o["out_q"], "q(y)", mask=live)
+    data_bits = O.BAD_TOKEN | O.BAD_LOGITS | O.CTX_OVERFLOW
+    assert np.array_equal(g["out_flags"].astype(np.uint32) & data_bits, o["flags"] & data_bits)
+    print(f"  accepted mean {o['out_accepted'].mean():.2f}, excused {excused_fraction(o['flags']):.3f}", flush=True)
+    return g, o
+
+
+def test_config0_probabilistic():
+    c = synth.config0()
+    BS, B = c["BS"], c["B"]
+    verify_both(c["target"], np.arange(BS) * (B + 1), c["tokens"], np.zeros((BS, B), np.uint8),
+                np.full(BS, B, np.int32), c["u_acc"], c["u_smp"], c["temperature"], c["draft"], np.arange(BS) * B)
+
+
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_config1_model_chain(T):
+    c = synth.config1(temperature=T)
+    BS, B = c["BS"], c["B"]
+    verify_both(c["target"], np.arange(BS) * (B + 1), c["tokens"], np.zeros((BS, B), np.uint8),
+                np.full(BS, B, np.int32), c["u_acc"], c["u_smp"], T, c["draft"], np.arange(BS) * B, tag="c1 model")
+
+
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_config1_ngram_chain_point_masses(T):
+    c = synth.config1()
+    draft, dlen, feat = O.ngram_draft(c["ctx"], c["ctx_len"], 3, 3, 15, 256)
+    BS = c["BS"]
+    g, o = verify_both(c["ngram_target"], np.arange(BS) * 16, draft, np.full((BS, 15), 3, np.uint8), dlen,
+                       c["u_acc_ng"], c["u_smp_ng"], T, tag="c1 ngram")
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_allocated_chains_bf16(cfg):
+    c = synth.config2() if cfg == 2 else synth.config4()
+    draft, dlen, feat = O.ngram_draft(c["ctx"], c["ctx_len"], c["n_min"], c["n_max"], 15, 256)
+    al = O.allocate_budget(c["model_tokens"], c["model_conf_logit"], True, c["model_point_mass"], draft, dlen, feat,
+                           c["estimator"], c["lam"], c["budget"], "proposed", ld=15)
+    BS = c["BS"]
+    verify_both(c["target_bf16"], np.arange(BS) * 16, al["tokens"], al["slot_flags"], al["alloc_len"],
+                c["u_acc"][:, :15], c["u_smp"], c["temperature"], tag=f"c{cfg}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [20011, 4099])
+def test_ragged_unaligned_and_edges(V, dtype):
+    rng = np.random.Generator(np.random.Philox(1000 + V))
+    BS, ld = 37, 9
+    z = (rng.standard_normal((BS, ld + 1, V)) * 3).astype(np.float32)
+    w = (z[:, :ld] + rng.standard_normal((BS, ld, V)).astype(np.float32)).astype(np.float32)
+    y = rng.integers(0, V, (BS, ld)).astype(np.int32)
+    am = np.argmax(w, -1)
+    take = rng.random((BS, ld)) < 0.6
+    y[take] = am[take]
+    y[0, 0] = V + 5                                 # out-of-range token
+    y[1, 2] = -3
+    n_slots = rng.integers(0, ld + 1, BS).astype(np.int32)
+    n_slots[:3] = [ld, ld, 0]
+    flags = (rng.random((BS, ld)) < 0.4).astype(np.uint8)
+    u_acc = rng.random((BS, ld), dtype=np.float32)
+    u_smp = rng.random(BS, dtype=np.float32)
+    if dtype == "bf16":
+        z, w = synth.f32_to_bf16_bits(z), synth.f32_to_bf16_bits(w)
+    for T in (0.0, 0.6, 1.0, 2.5):
+        verify_both(z, np.arange(BS) * (ld + 1), y, flags, n_slots, u_acc, u_smp, T, w, np.arange(BS) * ld,
+                    tag=f"ragged {V} {dtype}")
+
+
+def test_bad_rows_are_flagged_not_read():
+    import torch
+    import draft_verification_spec_amd as S
+    V, BS, ld = 3001, 4, 3
+    rng = np.random.Generator(np.random.Philox(3))
+    z = rng.standard_normal((8, V)).astype(np.float32)
+    z[1, 17] = np.nan
+    z[5, :] = -np.inf
+    row_base = np.array([0, 4, 7, 100], np.int64)     # request 2's rows run off the end, 3 is outside
+    y = np.zeros((BS, ld), np.int32)
+    g = S.spec_verify_chain(dev(z), dev(row_base), dev(y), dev(np.full(BS, 2, np.int32)), 1.0,
+                            u_accept=dev(rng.random((BS, ld), dtype=np.float32)),
+                            u_sample=dev(rng.random(BS, dtype=np.float32)))
+    torch.cuda.synchronize()
+    fl = host(g["out_flags"]).astype(np.uint32)
+    assert np.all(fl & O.BAD_LOGITS)                 # NaN / all -inf / rows outside the buffer
+    assert np.all(host(g["out_num"]) >= 1)
+
+
+def test_commit_appends_and_overflows():
+    import torch
+    import draft_verification_spec_amd as S
+    c = synth.config0()
+    BS, B, V = c["BS"], c["B"], c["V"]
+    ctx = np.zeros((BS, 530), np.int32)
+    ctx[:, :512] = c["ctx"]
+    ctx_len = np.array([512, 512, 525, 512], np.int32)
+    cap = np.int32(530)
+    tc, tl = dev(ctx), dev(ctx_len)
+    g = S.spec_verify_chain(dev(c["target"]).reshape(-1, V), dev(np.arange(BS) * (B + 1)), dev(c["tokens"]),
+                            dev(np.full(BS, B, np.int32)), 1.0, u_accept=dev(c["u_acc"]), u_sample=dev(c["u_smp"]),
+                            slot_flags=dev(np.zeros((BS, B), np.uint8)), draft_logits=dev(c["draft"]).reshape(-1, V),
+                            draft_row_base=dev(np.arange(BS) * B), ctx=tc, ctx_len=tl, ctx_cap=cap)
+    torch.cuda.synchronize()
+    num = host(g["out_num"])
+    fl = np.zeros(BS, np.uint32)
+    ref_ctx, ref_len = O.commit(ctx.copy(), ctx_len.copy(), int(cap), host(g["out_tokens"]), num, fl)
+    assert np.array_equal(host(tl), ref_len) and np.array_equal(host(tc), ref_ctx)
+    assert np.array_equal(host(g["out_flags"]).astype(np.uint32) & O.CTX_OVERFLOW, fl & O.CTX_OVERFLOW)
+
+
+def test_tree_verify_config3():
+    import torch
+    import draft_verification_spec_amd as S
+    c = synth.config3_inputs()
+    qr, ex, el = synth.tree_queries(c["ctx"], c["ctx_len"], c["block"])
+    draft, dlen, feat = O.ngram_draft(c["ctx"], c["ctx_len"], c["n_min"], c["n_max"], c["L"], 256,
+                                      query_req=qr, extra=ex, extra_len=el)
+    t = O.tree_build_batch(c["block"], draft, dlen, c["w_node"], c["w_none"], c["depth_max"], c["rows_cap"])
+    rows = synth.tree_target_rows(3, t["node_token"], t["parent_row"], t["n_rows"], c["truth"], c["V"], c["rows_cap"])
+    BS, R, V = rows.shape
+    rb = np.arange(BS, dtype=np.int64) * R
+    print(f"verify tree: bs {BS} rows {R} V {V}", flush=True)
+    g = S.spec_verify_tree(dev(rows).reshape(-1, V), dev(rb), dev(t["node_token"]), dev(t["parent_row"]),
+                           dev(t["n_rows"]))
+    torch.cuda.synchronize()
+    g = {k: host(v) for k, v in g.items()}
+    o = O.verify_tree(rows.reshape(-1, V), rb, t["node_token"], t["parent_row"], t["n_rows"])
+    every = np.ones(BS, bool)
+    for k in ("out_tokens", "out_num", "out_path_rows", "out_argmax"):
+        assert_rows_equal(g[k], o[k], every, k)
+    print("  mean committed per tree:", o["out_num"].mean(), flush=True)
+    # a bf16 copy of the same rows
+    bits = synth.f32_to_bf16_bits(rows)
+    g2 = S.spec_verify_tree(as_logits(bits).reshape(-1, V), dev(rb), dev(t["node_token"]), dev(t["parent_row"]),
+                            dev(t["n_rows"]))
+    torch.cuda.synchronize()
+    o2 = O.verify_tree(bits.reshape(-1, V), rb, t["node_token"], t["parent_row"], t["n_rows"])
+    assert_rows_equal(host(g2["out_tokens"]), o2["out_tokens"], every, "bf16 out_tokens")
