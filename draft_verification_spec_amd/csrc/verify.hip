@@ -401,6 +401,10 @@ __global__ __launch_bounds__(kDecideBlock) void k_decide(ChainParams P)
         if (P.out_q) P.out_q[off] = (float)q;
         if (!acc) atomicOr((unsigned long long*)&sRej, 1ull << t);
         if (fl) atomicOr(&sFlags, fl);
+    } else if (t < ld) {
+        const int64_t off = (int64_t)r * ld + t;
+        if (P.out_p) P.out_p[off] = 0.0f;
+        if (P.out_q) P.out_q[off] = 0.0f;
     }
     __syncthreads();
     const uint64_t rej = sRej;
@@ -801,6 +805,7 @@ int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st)
 
     RowSet tr{a->logits, a->row_stride, a->row_base, a->n_logit_rows, a->n_slots, 0, a->ld, 1, nullptr, a->ld, 0};
     const bool at = aligned16(a->logits, a->row_stride, a->dtype);
+    if (a->prof_begin) hipEventRecord((hipEvent_t)a->prof_begin, st);
     if (P.greedy) launch_stats<true>(a->dtype, at, tr, a->vocab, sp, a->bs, P.c, P.part, NR, st);
     else launch_stats<false>(a->dtype, at, tr, a->vocab, sp, a->bs, P.c, P.part, NR, st);
     if (!P.greedy && P.dlogits) {
@@ -811,6 +816,7 @@ int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st)
             launch_stats<false>(a->draft_dtype, ad, dr, a->vocab, sp, a->bs, P.c, P.part, NR, st);
         }
     }
+    if (a->prof_end) hipEventRecord((hipEvent_t)a->prof_end, st);
     hipLaunchKernelGGL(k_decide, dim3(a->bs), dim3(kDecideBlock), 0, st, P);
     const bool need_final = !P.greedy || P.ctx;
     if (!P.greedy) {
@@ -844,8 +850,10 @@ int spec_verify_tree_launch(const spec_tree_verify_args* a, hipStream_t st)
     P.part = (Partial*)a->workspace;
     P.splits = sp.splits;
     RowSet rs{a->logits, a->row_stride, a->row_base, a->n_logit_rows, a->n_rows, 1, a->rows_max, 0, nullptr, 0, 0};
+    if (a->prof_begin) hipEventRecord((hipEvent_t)a->prof_begin, st);
     launch_stats<true>(a->dtype, aligned16(a->logits, a->row_stride, a->dtype), rs, a->vocab, sp, a->bs, 1.0f, P.part,
                        a->rows_max, st);
+    if (a->prof_end) hipEventRecord((hipEvent_t)a->prof_end, st);
     hipLaunchKernelGGL(k_tree_walk, dim3(a->bs), dim3(kWave), 0, st, P);
     return spec_record_hip_error(hipGetLastError());
 }

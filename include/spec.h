@@ -283,6 +283,8 @@ typedef struct spec_verify_args {
     int64_t ctx_stride;
     int32_t* ctx_len;            /* device [bs]                                   */
     int32_t ctx_cap;             /* <= ctx_stride                                 */
+    void* prof_begin;            /* optional hipEvent_t pair recorded on `stream`  */
+    void* prof_end;              /* right before / after the row-statistics pass  */
     void* workspace;
     size_t workspace_bytes;
 } spec_verify_args;
@@ -316,6 +318,8 @@ typedef struct spec_tree_verify_args {
     int64_t ctx_stride;
     int32_t* ctx_len;
     int32_t ctx_cap;
+    void* prof_begin;            /* optional hipEvent_t pair (as in spec_verify_args) */
+    void* prof_end;
     void* workspace;
     size_t workspace_bytes;
 } spec_tree_verify_args;
