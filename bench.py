@@ -8,10 +8,12 @@ V = 151,936, a 7-token model chain and a 15-token n-gram chain per request,
 budget 256 verified draft slots, bf16 target rows, T = 1.0, 8,192-token
 contexts (synthetic, seeded; see workloads/synth.py).
 
-Every step restores the context lengths first, so all K timed steps do the
-same work.  Two timed regions on one stream: K eager steps with an event pair
-around every verification statistics pass (that kernel's live average
-duration, and an eager throughput), then the K steps captured in one HIP
+The commit appends each request's emitted tokens after its context and writes
+the new lengths to a separate buffer, so every one of the K timed steps reads
+the same contexts and does the same work.  Two timed regions on one stream:
+K eager steps with an event pair attached to the dispatch of every
+verification statistics kernel (that kernel's live average duration, and an
+eager throughput), then the K steps captured in one HIP
 graph (checked against the eager step first) replayed once between two
 events, which gives the reported throughput.  Prints one JSON line.
 """
@@ -29,7 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verify+draft steps/sec at BS128, V=151936, B=7; achieved HBM GB/s vs peak"
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E, AMD's published figure
-STATS_KERNEL = "k_row_stats"   # the HBM-bound pass of the step
+STATS_KERNEL = "k_stats"   # the HBM-bound pass of the step
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "verify_stats_bs128_v151936_bf16_counters.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "draft_verification_spec_amd", "csrc", f)
                   for f in ("verify.hip", "common.hpp")]
@@ -144,8 +146,8 @@ def main():
     BS, V, L = c["BS"], c["V"], 15
     g = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     ctx = g(c["ctx"])
-    ctx_len0 = g(c["ctx_len"])
-    ctx_len = ctx_len0.clone()
+    ctx_len = g(c["ctx_len"])
+    ctx_len_new = torch.empty_like(ctx_len)
     tokens_d, conf_d, pm_d = g(c["model_tokens"]), g(c["model_conf_logit"]), g(c["model_point_mass"])
     target = synth.as_torch_bf16(c["target_bf16"]).to(dev).reshape(-1, V)
     row_base = g(np.arange(BS, dtype=np.int64) * c["target_rows_per_req"])
@@ -157,7 +159,6 @@ def main():
     bufs = {}
 
     def step(prof=None):
-        ctx_len.copy_(ctx_len0)
         d, dl, f = S.spec_ngram_draft(ctx, ctx_len, c["n_min"], c["n_max"], L, c["copy_cap"],
                                       out=bufs.get("ng"), workspace=bufs.get("ws_ng"))
         al = S.spec_allocate_budget(mode="chain", model_tokens=tokens_d, model_conf=conf_d, ngram_draft=d,
@@ -166,7 +167,8 @@ def main():
                                     out=bufs.get("al"), workspace=bufs.get("ws_al"))
         out = S.spec_verify_chain(target, row_base, al["chain_tokens"], al["alloc_len"], c["temperature"],
                                   u_accept=u_acc, u_sample=u_smp, slot_flags=al["slot_flags"],
-                                  out_flags=al["out_flags"], ctx=ctx, ctx_len=ctx_len, out=bufs.get("vf"),
+                                  out_flags=al["out_flags"], ctx=ctx, ctx_len=ctx_len, ctx_len_out=ctx_len_new,
+                                  out=bufs.get("vf"),
                                   workspace=bufs.get("ws_v"), prof_events=prof)
         bufs.setdefault("ng", (d, dl, f))
         bufs.setdefault("al", al)
@@ -192,8 +194,8 @@ def main():
     t0, t1, t2, t3 = (hip.event() for _ in range(4))
     s = stream.cuda_stream
 
-    # Region 1, eager launches: an event pair around every statistics pass
-    # gives that kernel's live average duration on the step's stream.
+    # Region 1, eager launches: an event pair attached to every statistics
+    # kernel's dispatch gives that kernel's live average duration.
     with torch.cuda.stream(stream):
         for _ in range(W):
             step()

@@ -29,7 +29,7 @@ SRC_MODEL, SRC_NGRAM, SRC_MERGED, SRC_EXTENDED = 0, 1, 2, 3
 POLICIES = {"proposed": 0, "ngram_first": 1, "extension": 2, "model_only": 3, "ngram_only": 4}
 ALLOC_CHAIN, ALLOC_TREE = 0, 1
 OP_NGRAM, OP_ALLOCATE, OP_VERIFY_CHAIN, OP_VERIFY_TREE = 0, 1, 2, 3
-MAX_DRAFT, MAX_CAP, MAX_ROWS, MAX_FOREST = 32, 1024, 64, 1024
+MAX_DRAFT, MAX_CAP, MAX_ROWS, MAX_FOREST, MAX_VOCAB = 32, 1024, 64, 1024, 8388608
 
 
 class NgramArgs(C.Structure):
@@ -72,7 +72,7 @@ class VerifyArgs(C.Structure):
                 ("tokens", vp), ("slot_flags", vp), ("ld", i32), ("n_slots", vp), ("u_accept", vp),
                 ("u_sample", vp), ("out_tokens", vp), ("out_num", vp), ("out_accepted", vp), ("out_p", vp),
                 ("out_q", vp), ("out_flags", vp), ("ctx", vp), ("ctx_stride", i64), ("ctx_len", vp),
-                ("ctx_cap", i32), ("prof_begin", vp), ("prof_end", vp), ("workspace", vp),
+                ("ctx_len_out", vp), ("ctx_cap", i32), ("prof_begin", vp), ("prof_end", vp), ("workspace", vp),
                 ("workspace_bytes", sz)]
 
 
@@ -81,7 +81,8 @@ class TreeVerifyArgs(C.Structure):
                 ("row_stride", i64), ("row_base", vp), ("n_logit_rows", i64), ("node_token", vp),
                 ("parent_row", vp), ("n_rows", vp), ("out_tokens", vp), ("out_num", vp), ("out_path_rows", vp),
                 ("out_argmax", vp), ("out_flags", vp), ("ctx", vp), ("ctx_stride", i64), ("ctx_len", vp),
-                ("ctx_cap", i32), ("prof_begin", vp), ("prof_end", vp), ("workspace", vp), ("workspace_bytes", sz)]
+                ("ctx_len_out", vp), ("ctx_cap", i32), ("prof_begin", vp), ("prof_end", vp), ("workspace", vp),
+                ("workspace_bytes", sz)]
 
 
 STRUCTS = {"spec_ngram_args": NgramArgs, "spec_estimator": Estimator, "spec_chain_alloc": ChainAlloc,
@@ -303,8 +304,8 @@ def spec_allocate_budget(mode="chain", **kw):
 
 def spec_verify_chain(logits, row_base, tokens, n_slots, temperature, u_accept=None, u_sample=None,
                       slot_flags=None, draft_logits=None, draft_row_base=None, out_flags=None,
-                      ctx=None, ctx_len=None, ctx_cap=None, out=None, workspace=None, stream=None,
-                      prof_events=None):
+                      ctx=None, ctx_len=None, ctx_cap=None, ctx_len_out=None, out=None, workspace=None,
+                      stream=None, prof_events=None):
     """Rejection-sampling verification of one chain per request (optional commit into ctx).
     ``prof_events``: optional pair of raw hipEvent_t handles recorded around the
     row-statistics pass."""
@@ -347,6 +348,9 @@ def spec_verify_chain(logits, row_base, tokens, n_slots, temperature, u_accept=N
         _dev(ctx_len, torch.int32, "ctx_len", 1)
         a.ctx, a.ctx_stride, a.ctx_len = _ptr(ctx), ctx.shape[1], _ptr(ctx_len)
         a.ctx_cap = ctx.shape[1] if ctx_cap is None else int(ctx_cap)
+        if ctx_len_out is not None:
+            _dev(ctx_len_out, torch.int32, "ctx_len_out", 1)
+            a.ctx_len_out = _ptr(ctx_len_out)
     if prof_events is not None:
         a.prof_begin, a.prof_end = prof_events
     ws, w = _workspace(OP_VERIFY_CHAIN, a, dev, workspace)
@@ -357,7 +361,7 @@ def spec_verify_chain(logits, row_base, tokens, n_slots, temperature, u_accept=N
 
 
 def spec_verify_tree(logits, row_base, node_token, parent_row, n_rows, out_flags=None, ctx=None, ctx_len=None,
-                     ctx_cap=None, out=None, workspace=None, stream=None, prof_events=None):
+                     ctx_cap=None, ctx_len_out=None, out=None, workspace=None, stream=None, prof_events=None):
     """Greedy verification of one tree per request (optional commit into ctx)."""
     lg = _rows2d(logits, "logits")
     _dev(row_base, torch.int64, "row_base", 1)
@@ -383,6 +387,9 @@ def spec_verify_tree(logits, row_base, node_token, parent_row, n_rows, out_flags
         _dev(ctx_len, torch.int32, "ctx_len", 1)
         a.ctx, a.ctx_stride, a.ctx_len = _ptr(ctx), ctx.shape[1], _ptr(ctx_len)
         a.ctx_cap = ctx.shape[1] if ctx_cap is None else int(ctx_cap)
+        if ctx_len_out is not None:
+            _dev(ctx_len_out, torch.int32, "ctx_len_out", 1)
+            a.ctx_len_out = _ptr(ctx_len_out)
     if prof_events is not None:
         a.prof_begin, a.prof_end = prof_events
     ws, w = _workspace(OP_VERIFY_TREE, a, dev, workspace)

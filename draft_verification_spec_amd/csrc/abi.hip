@@ -88,7 +88,7 @@ static bool dtype_ok(int dt) { return dt == SPEC_F32 || dt == SPEC_BF16; }
 static int check_verify(const spec_verify_args* a)
 {
     REQUIRE(a);
-    REQUIRE(a->bs >= 1 && a->vocab >= 1);
+    REQUIRE(a->bs >= 1 && a->vocab >= 1 && a->vocab <= SPEC_MAX_VOCAB);
     REQUIRE(a->temperature >= 0.0f && a->temperature < 1e30f);
     REQUIRE(a->logits && a->row_base && dtype_ok(a->dtype) && a->row_stride >= a->vocab && a->n_logit_rows >= 1);
     if (a->draft_logits) {
@@ -105,7 +105,7 @@ static int check_verify(const spec_verify_args* a)
 static int check_tree_verify(const spec_tree_verify_args* a)
 {
     REQUIRE(a);
-    REQUIRE(a->bs >= 1 && a->vocab >= 1);
+    REQUIRE(a->bs >= 1 && a->vocab >= 1 && a->vocab <= SPEC_MAX_VOCAB);
     REQUIRE(a->rows_max >= 1 && a->rows_max <= SPEC_MAX_ROWS);
     REQUIRE(a->logits && a->row_base && dtype_ok(a->dtype) && a->row_stride >= a->vocab && a->n_logit_rows >= 1);
     REQUIRE(a->node_token && a->parent_row && a->n_rows);

@@ -1,17 +1,21 @@
 // Verification-budget allocation.
 //
-// Chains (Hybrid Spark, Algorithm 1 and Sections 4.2-4.4):
-//   k_select  : one thread per request computes the n-gram estimates (Eq. (1)),
-//               both survival curves, the chain choice (contains rule, value
-//               rule of Eq. (3) with ties to the n-gram chain, or a lossless
-//               policy of Appendix H) in fp64, writes the chosen chain to
-//               fixed-size buffers and one 64-bit ranking key per slot:
-//               fp32(S) bits | (31 - position) | (2^27 - 1 - request), so the
-//               largest key is "highest survival, then lower position, then
-//               lower request" and keys are unique.
-//   k_topk    : one workgroup finds the exact budget-th largest key by an
-//               8-bit radix select over LDS histograms, counts each request's
-//               verified prefix and writes the CSR row bases.
+// Chains (Hybrid Spark, Algorithm 1 and Sections 4.2-4.4), one launch of one
+// 1024-thread workgroup (k_alloc_chain):
+//   * every n-gram estimate (Eq. (1)) and model confidence is evaluated in
+//     fp64 by its own thread into LDS, next to both chains' tokens (all input
+//     is read once, coalesced); then one thread per request forms the
+//     survival running products, the chain values of Eq. (3) and the choice
+//     (contains rule, value rule with ties to the n-gram chain, or a lossless
+//     policy of Appendix H) and leaves the chosen chain's survivals in LDS;
+//   * one thread per slot writes the chosen chain and one 64-bit ranking key:
+//     fp32(S) bits | (31 - position) | (2^27 - 1 - request), so the largest
+//     key is "highest survival, then lower position, then lower request" and
+//     keys are unique;
+//   * the exact budget-th largest key by an 8-bit radix select over an LDS
+//     histogram (the digit is found by a wave-wide suffix scan), stopping as
+//     soon as the boundary bucket is taken whole;
+//   * each request's verified prefix and the CSR row bases.
 // Trees (AdaSpark, Sections 2.2, 3.1, 3.3):
 //   k_tree    : one wave per request builds the candidate forest in LDS
 //               (drafter block + n-gram chains), the acceptance estimates of
@@ -22,115 +26,97 @@
 
 namespace spec {
 
-constexpr int kLdMax = SPEC_MAX_DRAFT;
+constexpr int kAllocBlock = 1024;
+constexpr int kLdsKeys = 4096;          // ranking keys kept in LDS (32 KB); more go to the workspace
+constexpr int kLdsVals = 10240;         // fp64 per-slot values kept in LDS (80 KB); more go to the workspace
 
 struct SelectParams {
     spec_chain_alloc a;
-    uint64_t* keys;  // [bs, ld]
+    uint64_t* keys;  // workspace fallback: [bs, ld]
+    double* vals;    // workspace fallback for the staging area below
 };
+
+// Staging area, in 8-byte units per request: ld estimates (later survivals),
+// K confidences, the copy-length log term, four int32 words (length state,
+// n, a, choice) and the slot tokens of both chains (2 x ld int32).
+__host__ __device__ __forceinline__ int64_t vals_count(int64_t bs, int64_t ld, int64_t K) { return bs * (2 * ld + K + 3); }
+
+// length-state word: n-gram length (clamped) | flags
+constexpr int kGlMask = 0xFF;
+constexpr int kGlMismatch = 1 << 28;   // n-gram and model tokens differ within the first K
+constexpr int kGlPointMass = 1 << 29;  // model slots are point masses
+constexpr int kGlBadLen = 1 << 30;     // the given n-gram length was out of range
 
 __device__ __forceinline__ double sigm(double x) { return 1.0 / (1.0 + exp(-x)); }
 
-__device__ double est_logit(const spec_estimator& e, int k, int n, int a, int m)
+// Eq. (1) logit of position k (1-based); `lnm` = ln(min(max(m,1), m_cap) / m_ref).
+__device__ __forceinline__ double est_logit(const spec_estimator& e, int k, int n, int a, double lnm)
 {
     const bool first = (k == 1);
-    double z = (double)e.beta[k - 1] + (double)(first ? e.w_first : e.w_rest) * ((double)n - (double)e.n_ref) +
-               (double)e.delta * (double)a;
-    if ((double)n >= (double)e.n_full) {
-        double mm = (double)m;
-        if (mm < 1.0) mm = 1.0;
-        if (mm > (double)e.m_cap) mm = (double)e.m_cap;
-        z += (double)(first ? e.l_first : e.l_rest) + (double)(first ? e.k_first : e.k_rest) * log(mm / (double)e.m_ref);
-    }
+    double z = (double)e.beta[(k <= 15 ? k : 15) - 1] +
+               (double)(first ? e.w_first : e.w_rest) * ((double)n - (double)e.n_ref) + (double)e.delta * (double)a;
+    if ((double)n >= (double)e.n_full)
+        z += (double)(first ? e.l_first : e.l_rest) + (double)(first ? e.k_first : e.k_rest) * lnm;
     return z;
 }
 
-__device__ __forceinline__ double chain_value(const double* S, int len, double lam)
+// Request r: chain values from its estimates h[0..glen) and confidences
+// c[0..K) (the survival running products are left folds, as defined), the
+// chain choice, then the chosen chain's survivals written over h (slot k's
+// survival replaces h[k] once h[k] has been used).  `gl` is the request's
+// length-state word.  Returns (source << 8) | length.
+__device__ int select_fold(const spec_chain_alloc& A, int gl, double* h, const double* cc)
 {
-    double v = 0.0;
-    for (int k = 0; k < len; ++k) v += (S[k] > lam) ? (S[k] - lam) : 0.0;
-    return v;
-}
-
-__global__ __launch_bounds__(64) void k_select(SelectParams P)
-{
-    const spec_chain_alloc& A = P.a;
-    const int r = blockIdx.x * blockDim.x + threadIdx.x;
-    if (r >= A.bs) return;
     const int K = A.K, ld = A.ld;
-    uint32_t flags = 0;
-    int glen = A.ngram_len[r];
-    const int gcap = A.ngram_ld < ld ? A.ngram_ld : ld;
-    if (glen < 0 || glen > gcap) { flags |= SPEC_FLAG_BAD_LENGTH; glen = glen < 0 ? 0 : gcap; }
-    const int n = A.ngram_feat[4 * (int64_t)r + 0];
-    const int am = A.ngram_feat[4 * (int64_t)r + 1];
-    const int m = A.ngram_feat[4 * (int64_t)r + 2];
-    double h[kLdMax], Sg[kLdMax], Sd[kLdMax];
-    double s = 1.0;
+    const int glen = gl & kGlMask;
+    const double lam = (double)A.lambda;
+    double sg = 1.0, sd = 1.0, vg = 0.0, vd = 0.0;
     for (int k = 0; k < glen; ++k) {
-        h[k] = sigm(est_logit(A.est, k + 1 < 15 ? k + 1 : 15, n, am, m));
-        s *= h[k];
-        Sg[k] = s;
+        sg *= h[k];
+        vg += sg > lam ? sg - lam : 0.0;
     }
-    s = 1.0;
     for (int k = 0; k < K; ++k) {
-        const double cv = (double)A.model_conf[(int64_t)r * K + k];
-        s *= A.conf_is_logit ? sigm(cv) : cv;
-        Sd[k] = s;
+        sd *= cc[k];
+        vd += sd > lam ? sd - lam : 0.0;
     }
-    const int32_t* d = A.model_tokens + (int64_t)r * K;
-    const int32_t* g = A.ngram_draft + (int64_t)r * A.ngram_ld;
-    bool prefix = glen > K;
-    for (int i = 0; prefix && i < K; ++i) prefix = (g[i] == d[i]);
+    const bool prefix = glen > K && !(gl & kGlMismatch);
     int use = SPEC_SRC_MODEL;
     switch (A.policy) {
     case SPEC_POLICY_PROPOSED:
         if (prefix) use = SPEC_SRC_MERGED;
-        else if (glen >= 1) use = (chain_value(Sg, glen, (double)A.lambda) >= chain_value(Sd, K, (double)A.lambda)) ? SPEC_SRC_NGRAM : SPEC_SRC_MODEL;
+        else if (glen >= 1) use = vg >= vd ? SPEC_SRC_NGRAM : SPEC_SRC_MODEL;
         break;
     case SPEC_POLICY_NGRAM_FIRST: use = glen >= 1 ? SPEC_SRC_NGRAM : SPEC_SRC_MODEL; break;
     case SPEC_POLICY_EXTENSION: use = prefix ? SPEC_SRC_EXTENDED : SPEC_SRC_MODEL; break;
     case SPEC_POLICY_NGRAM_ONLY: use = SPEC_SRC_NGRAM; break;
     default: use = SPEC_SRC_MODEL;
     }
-    const bool mpm = !A.model_point_mass || A.model_point_mass[r];
-    const uint8_t mfl = mpm ? SPEC_SLOT_POINT_MASS : 0;
-    const uint8_t gfl = SPEC_SLOT_POINT_MASS | SPEC_SLOT_FROM_NGRAM;
     const int len = (use == SPEC_SRC_MODEL) ? K : glen;
+    sg = 1.0;
+    sd = 1.0;
     double prev = 1.0;
     for (int k = 0; k < ld; ++k) {
-        int32_t tk = -1;
-        uint8_t fl = 0;
+        const double hk = (k < glen) ? h[k] : 0.0;
+        if (k < glen) sg *= hk;
+        if (k < K) sd *= cc[k];
         double S = 0.0;
         if (k < len) {
-            if (use == SPEC_SRC_MODEL) { tk = d[k]; fl = mfl; S = Sd[k]; }
-            else if (use == SPEC_SRC_NGRAM) { tk = g[k]; fl = gfl; S = Sg[k]; }
-            else if (use == SPEC_SRC_MERGED) { tk = g[k]; fl = gfl; S = (k < K) ? (Sg[k] > Sd[k] ? Sg[k] : Sd[k]) : prev * h[k]; }
-            else { tk = g[k]; if (k < K) { fl = mfl; S = Sd[k]; } else { fl = gfl; S = prev * h[k]; } }
+            if (use == SPEC_SRC_MODEL) S = sd;
+            else if (use == SPEC_SRC_NGRAM) S = sg;
+            else if (use == SPEC_SRC_MERGED) S = (k < K) ? (sg > sd ? sg : sd) : prev * hk;
+            else S = (k < K) ? sd : prev * hk;
             prev = S;
         }
-        const int64_t o = (int64_t)r * ld + k;
-        A.chain_tokens[o] = tk;
-        A.slot_flags[o] = fl;
-        A.survival[o] = (float)S;
-        uint64_t key = 0;
-        if (k < len) {
-            const float sf = (float)S;
-            key = ((uint64_t)__float_as_uint(sf) << 32) | ((uint64_t)(31 - k) << 27) | (uint64_t)(0x7FFFFFF - r);
-        }
-        P.keys[o] = key;
+        h[k] = S;
     }
-    A.chain_len[r] = len;
-    A.chain_src[r] = use;
-    A.out_flags[r] = flags;
+    return (use << 8) | len;
 }
-
-constexpr int kTopkBlock = 1024;
 
 __device__ int64_t block_exclusive_i64(int64_t v, int64_t* total)
 {
-    __shared__ int64_t sh[kTopkBlock / kWave];
+    __shared__ int64_t sh[32];
     const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+    const int nw = (int)(blockDim.x / kWave);
     int64_t inc = v;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -141,7 +127,7 @@ __device__ int64_t block_exclusive_i64(int64_t v, int64_t* total)
     if (lane == kWave - 1) sh[wid] = inc;
     __syncthreads();
     int64_t before = 0, tot = 0;
-    for (int w = 0; w < (int)(blockDim.x / kWave); ++w) {
+    for (int w = 0; w < nw; ++w) {
         if (w < wid) before += sh[w];
         tot += sh[w];
     }
@@ -149,59 +135,191 @@ __device__ int64_t block_exclusive_i64(int64_t v, int64_t* total)
     return before + inc - v;
 }
 
-__global__ __launch_bounds__(kTopkBlock) void k_topk(SelectParams P)
+// Histogram increment with the lanes that share the first active lane's digit
+// folded into one LDS atomic (at the top digits nearly every key agrees).
+__device__ __forceinline__ void hist_add(uint32_t* hist, bool active, int dg)
+{
+    const uint64_t act = __ballot(active);
+    if (act == 0) return;
+    const int leader = __builtin_ctzll(act);
+    const int ldg = __shfl(dg, leader, kWave);
+    const uint64_t peers = __ballot(active && dg == ldg);
+    const int lane = threadIdx.x % kWave;
+    if (lane == leader) atomicAdd(&hist[ldg], (uint32_t)__popcll(peers));
+    else if (active && dg != ldg) atomicAdd(&hist[dg], 1u);
+}
+
+// Chain selection for every request, then the exact budget-th largest key by
+// an 8-bit radix select, the verified prefix per request and the row bases.
+__global__ __launch_bounds__(kAllocBlock) void k_alloc_chain(SelectParams P)
 {
     const spec_chain_alloc& A = P.a;
-    const int64_t N = (int64_t)A.bs * A.ld;
+    const int bs = A.bs, ld = A.ld, K = A.K;
+    const int64_t N = (int64_t)bs * ld;
+    __shared__ uint64_t lkeys[kLdsKeys];
+    __shared__ double lvals[kLdsVals];
     __shared__ uint32_t hist[256];
-    __shared__ uint64_t sh_prefix, sh_mask;
+    __shared__ uint64_t sh_prefix, sh_min;
     __shared__ int64_t sh_rem, sh_valid;
-    if (threadIdx.x == 0) { sh_prefix = 0; sh_mask = 0; sh_valid = 0; }
+    __shared__ int sh_done;
+    uint64_t* keys = (N <= kLdsKeys) ? lkeys : P.keys;
+    double* H = (vals_count(bs, ld, K) <= kLdsVals) ? lvals : P.vals;
+    double* Cc = H + N;
+    double* LNM = Cc + (int64_t)bs * K;
+    int32_t* GL = (int32_t*)(LNM + bs);
+    int32_t* FN = GL + bs;
+    int32_t* FA = FN + bs;
+    int32_t* CH = FA + bs;
+    int32_t* TD = CH + bs;      // model token per slot
+    int32_t* TG = TD + N;       // n-gram token per slot
+    const int wid = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    if (threadIdx.x == 0) { sh_prefix = 0; sh_valid = 0; sh_done = 0; sh_min = ~0ull; }
+    // 1a. per request: lengths, match features, the copy-length log term
+    for (int r = threadIdx.x; r < bs; r += kAllocBlock) {
+        const int rl = A.ngram_len[r];
+        const int n = A.ngram_feat[4 * (int64_t)r + 0];
+        const int am = A.ngram_feat[4 * (int64_t)r + 1];
+        double mm = (double)A.ngram_feat[4 * (int64_t)r + 2];
+        const bool mpm = !A.model_point_mass || A.model_point_mass[r];
+        const int gcap = A.ngram_ld < ld ? A.ngram_ld : ld;
+        const int glen = rl < 0 ? 0 : (rl > gcap ? gcap : rl);
+        GL[r] = glen | (mpm ? kGlPointMass : 0) | ((rl < 0 || rl > gcap) ? kGlBadLen : 0);
+        FN[r] = n;
+        FA[r] = am;
+        mm = mm < 1.0 ? 1.0 : (mm > (double)A.est.m_cap ? (double)A.est.m_cap : mm);
+        LNM[r] = ((double)n >= (double)A.est.n_full) ? log(mm / (double)A.est.m_ref) : 0.0;
+    }
     __syncthreads();
-    // number of real slots
+    // 1b. per slot: tokens of both chains, the model confidence and the
+    // n-gram estimate (fp64), the first-K agreement of the two chains
+    for (int64_t i = threadIdx.x; i < N; i += kAllocBlock) {
+        const int r = (int)(i / ld), k = (int)(i - (int64_t)r * ld);
+        int32_t td = -1, tg = -1;
+        double cv = 0.0;
+        if (k < K) {
+            td = A.model_tokens[(int64_t)r * K + k];
+            cv = (double)A.model_conf[(int64_t)r * K + k];
+        }
+        if (k < A.ngram_ld) tg = A.ngram_draft[(int64_t)r * A.ngram_ld + k];
+        const int gl = GL[r];
+        const int glen = gl & kGlMask;
+        H[i] = (k < glen) ? sigm(est_logit(A.est, k + 1, FN[r], FA[r], LNM[r])) : 0.0;
+        if (k < K) Cc[(int64_t)r * K + k] = A.conf_is_logit ? sigm(cv) : cv;
+        TD[i] = td;
+        TG[i] = tg;
+        if (k < K && glen > K && td != tg) atomicOr(&GL[r], kGlMismatch);
+    }
+    __syncthreads();
+    // 1c. one thread per request: values, choice, survivals (over H)
     {
-        int64_t c = 0;
-        for (int64_t i = threadIdx.x; i < N; i += kTopkBlock) c += P.keys[i] != 0;
-        atomicAdd((unsigned long long*)&sh_valid, (unsigned long long)c);
+        int64_t valid = 0;
+        for (int r = threadIdx.x; r < bs; r += kAllocBlock) {
+            const int gl = GL[r];
+            const int ch = select_fold(A, gl, H + (int64_t)r * ld, Cc + (int64_t)r * K);
+            CH[r] = ch;
+            valid += ch & 255;
+            A.chain_len[r] = ch & 255;
+            A.chain_src[r] = ch >> 8;
+            A.out_flags[r] = (gl & kGlBadLen) ? SPEC_FLAG_BAD_LENGTH : 0u;
+        }
+        valid = wave_sum(valid);
+        if (lane == 0) atomicAdd((unsigned long long*)&sh_valid, (unsigned long long)valid);
+    }
+    __syncthreads();
+    // 1d. per-slot outputs and ranking keys
+    for (int64_t i = threadIdx.x; i < N; i += kAllocBlock) {
+        const int r = (int)(i / ld), k = (int)(i - (int64_t)r * ld);
+        const int ch = CH[r], use = ch >> 8, len = ch & 255;
+        int32_t tk = -1;
+        uint8_t fl = 0;
+        const double S = H[i];
+        if (k < len) {
+            const bool model_slot = use == SPEC_SRC_MODEL || (use == SPEC_SRC_EXTENDED && k < K);
+            const bool mpm = (GL[r] & kGlPointMass) != 0;
+            tk = (use == SPEC_SRC_MODEL) ? TD[i] : TG[i];
+            fl = model_slot ? (mpm ? SPEC_SLOT_POINT_MASS : 0) : (SPEC_SLOT_POINT_MASS | SPEC_SLOT_FROM_NGRAM);
+        }
+        A.chain_tokens[i] = tk;
+        A.slot_flags[i] = fl;
+        A.survival[i] = (float)S;
+        keys[i] = (k < len) ? (((uint64_t)__float_as_uint((float)S) << 32) | ((uint64_t)(31 - k) << 27) |
+                               (uint64_t)(0x7FFFFFF - r))
+                            : 0ull;
     }
     __syncthreads();
     const int64_t take = (A.budget < sh_valid) ? A.budget : sh_valid;
     uint64_t theta = ~0ull;  // nothing selected
     if (take > 0) {
         if (threadIdx.x == 0) sh_rem = take;
+        uint64_t mask = 0;
         for (int shift = 56; shift >= 0; shift -= 8) {
-            for (int i = threadIdx.x; i < 256; i += kTopkBlock) hist[i] = 0;
+            for (int i = threadIdx.x; i < 256; i += kAllocBlock) hist[i] = 0;
             __syncthreads();
-            const uint64_t pre = sh_prefix, msk = sh_mask;
-            for (int64_t i = threadIdx.x; i < N; i += kTopkBlock) {
-                const uint64_t k = P.keys[i];
-                if (k != 0 && (k & msk) == pre) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+            const uint64_t pre = sh_prefix;
+            const int64_t rounds = (N + kAllocBlock - 1) / kAllocBlock;
+            for (int64_t u = 0; u < rounds; ++u) {
+                const int64_t i = threadIdx.x + u * kAllocBlock;
+                const uint64_t k = i < N ? keys[i] : 0ull;
+                hist_add(hist, k != 0 && (k & mask) == pre, (int)((k >> shift) & 255u));
             }
             __syncthreads();
-            if (threadIdx.x == 0) {
-                int64_t rem = sh_rem, cum = 0;
-                int dsel = 0;
-                for (int dg = 255; dg >= 0; --dg) {
-                    if (cum + hist[dg] >= rem) { dsel = dg; break; }
-                    cum += hist[dg];
+            if (wid == 0) {
+                // lane l owns digits 255-4l .. 252-4l (descending); suffix counts from the top
+                uint32_t c4[4];
+                uint32_t own = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) { c4[j] = hist[255 - 4 * lane - j]; own += c4[j]; }
+                uint32_t inc = own;
+#pragma unroll
+                for (int o = 1; o < kWave; o <<= 1) {
+                    uint32_t u = __shfl_up(inc, o, kWave);
+                    if (lane >= o) inc += u;
                 }
-                sh_rem = rem - cum;
-                sh_prefix = pre | ((uint64_t)dsel << shift);
-                sh_mask = msk | (255ull << shift);
+                const int64_t rem = sh_rem;
+                const int64_t above = (int64_t)(inc - own);
+                if (above < rem && (int64_t)inc >= rem) {
+                    int64_t cum = above;
+                    for (int j = 0; j < 4; ++j) {
+                        if (cum + c4[j] >= rem) {
+                            sh_rem = rem - cum;
+                            sh_prefix = pre | ((uint64_t)(255 - 4 * lane - j) << shift);
+                            // every key of the boundary bucket is taken: the threshold is its smallest key
+                            sh_done = (cum + c4[j] == rem);
+                            break;
+                        }
+                        cum += c4[j];
+                    }
+                }
             }
+            mask |= 255ull << shift;
             __syncthreads();
+            if (sh_done) break;
         }
         theta = sh_prefix;
+        if (sh_done && mask != ~0ull) {
+            uint64_t mn = ~0ull;
+            for (int64_t i = threadIdx.x; i < N; i += kAllocBlock) {
+                const uint64_t k = keys[i];
+                if (k != 0 && (k & mask) == theta && k < mn) mn = k;
+            }
+#pragma unroll
+            for (int o = kWave / 2; o > 0; o >>= 1) {
+                const uint64_t v = __shfl_xor(mn, o, kWave);
+                mn = v < mn ? v : mn;
+            }
+            if (lane == 0) atomicMin((unsigned long long*)&sh_min, (unsigned long long)mn);
+            __syncthreads();
+            theta = sh_min;
+        }
     }
-    // per-request verified prefix, then CSR row bases over (alloc + 1)
-    const int bs = A.bs;
-    const int per = (bs + kTopkBlock - 1) / kTopkBlock;
+    // 3. verified prefix per request, row bases over (alloc + 1)
+    const int per = (bs + (int)blockDim.x - 1) / (int)blockDim.x;
     const int r0 = threadIdx.x * per;
     int64_t local = 0;
     for (int r = r0; r < r0 + per && r < bs; ++r) {
         int cnt = 0;
-        for (int k = 0; k < A.ld; ++k) {
-            const uint64_t key = P.keys[(int64_t)r * A.ld + k];
+        for (int k = 0; k < ld; ++k) {
+            const uint64_t key = keys[(int64_t)r * ld + k];
             cnt += (key != 0 && key >= theta);
         }
         A.alloc_len[r] = cnt;
@@ -310,10 +428,10 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
         fsel[j] = rank < keep;
     }
     __syncthreads();
+    __shared__ int32_t st_n[SPEC_MAX_ROWS], st_p[SPEC_MAX_ROWS];
     if (lane == 0) {
         fsel[0] = 1;
         // depth-first layout, children in index order
-        int st_n[SPEC_MAX_ROWS], st_p[SPEC_MAX_ROWS];
         int sp = 0, row = 0;
         st_n[sp] = 0; st_p[sp] = -1; ++sp;
         int32_t* nt = A.node_token + (int64_t)r * A.rows_cap;
@@ -336,9 +454,9 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
     }
 }
 
-__global__ __launch_bounds__(kTopkBlock) void k_rows_scan(const int32_t* n_rows, int bs, int64_t* row_base, int32_t* total_rows)
+__global__ __launch_bounds__(kAllocBlock) void k_rows_scan(const int32_t* n_rows, int bs, int64_t* row_base, int32_t* total_rows)
 {
-    const int per = (bs + kTopkBlock - 1) / kTopkBlock;
+    const int per = (bs + kAllocBlock - 1) / kAllocBlock;
     const int r0 = threadIdx.x * per;
     int64_t local = 0;
     for (int r = r0; r < r0 + per && r < bs; ++r) local += n_rows[r];
@@ -357,8 +475,13 @@ using namespace spec;
 
 size_t spec_alloc_ws(const spec_alloc_args* a)
 {
-    if (a->mode == SPEC_ALLOC_CHAIN) return align256((size_t)a->chain.bs * a->chain.ld * sizeof(uint64_t));
-    return 0;
+    if (a->mode != SPEC_ALLOC_CHAIN) return 0;
+    const int64_t N = (int64_t)a->chain.bs * a->chain.ld;
+    const int64_t NV = vals_count(a->chain.bs, a->chain.ld, a->chain.K);
+    size_t b = 0;
+    if (N > kLdsKeys) b += align256((size_t)N * sizeof(uint64_t));
+    if (NV > kLdsVals) b += align256((size_t)NV * sizeof(double));
+    return b;
 }
 
 int spec_alloc_launch(const spec_alloc_args* a, hipStream_t st)
@@ -366,14 +489,20 @@ int spec_alloc_launch(const spec_alloc_args* a, hipStream_t st)
     if (a->mode == SPEC_ALLOC_CHAIN) {
         SelectParams P;
         P.a = a->chain;
-        P.keys = (uint64_t*)a->workspace;
-        hipLaunchKernelGGL(k_select, dim3((a->chain.bs + 63) / 64), dim3(64), 0, st, P);
-        hipLaunchKernelGGL(k_topk, dim3(1), dim3(kTopkBlock), 0, st, P);
+        const int64_t N = (int64_t)a->chain.bs * a->chain.ld;
+        char* ws = (char*)a->workspace;
+        P.keys = nullptr;
+        if (N > kLdsKeys) {
+            P.keys = (uint64_t*)ws;
+            ws += align256((size_t)N * sizeof(uint64_t));
+        }
+        P.vals = (double*)ws;
+        hipLaunchKernelGGL(k_alloc_chain, dim3(1), dim3(kAllocBlock), 0, st, P);
     } else {
         TreeBuildParams P;
         P.a = a->tree;
         hipLaunchKernelGGL(k_tree, dim3(a->tree.bs), dim3(kWave), 0, st, P);
-        hipLaunchKernelGGL(k_rows_scan, dim3(1), dim3(kTopkBlock), 0, st, a->tree.n_rows, a->tree.bs, a->tree.row_base,
+        hipLaunchKernelGGL(k_rows_scan, dim3(1), dim3(kAllocBlock), 0, st, a->tree.n_rows, a->tree.bs, a->tree.row_base,
                            a->tree.total_rows);
     }
     return spec_record_hip_error(hipGetLastError());

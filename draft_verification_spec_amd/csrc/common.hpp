@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 #include "spec.h"
@@ -15,30 +16,27 @@ constexpr float kLog2e = 1.4426950408889634f;
 // launch geometry shared by host launchers and workspace sizing
 // ---------------------------------------------------------------------------
 
-// Logit rows are cut into chunks of a multiple of 64 elements (so every chunk
-// start keeps 16-byte alignment for fp32 and bf16); enough chunks are used to
-// put about `target_blocks` workgroups in flight across the batch.
+// Logit rows are cut into chunks of 8192 elements (16 KB of bf16, 32 KB of
+// fp32; a multiple of 64 elements keeps 16-byte alignment), fewer for short
+// rows so that a row still spans about four chunks.
 struct RowSplit {
     int64_t chunk;   // elements per chunk
     int32_t splits;  // chunks per row
 };
 
-inline RowSplit row_split(int32_t bs, int32_t vocab, int32_t target_blocks = 2048)
+inline RowSplit row_split(int32_t /*bs*/, int32_t vocab)
 {
-    int64_t want = (target_blocks + bs - 1) / (bs > 0 ? bs : 1);
-    int64_t max_splits = vocab / 2048;            // keep chunks >= 2048 elements
-    if (max_splits < 1) max_splits = 1;
-    if (want > max_splits) want = max_splits;
-    if (want < 1) want = 1;
-    int64_t chunk = (vocab + want - 1) / want;
+    int64_t chunk = (vocab + 3) / 4;
     chunk = (chunk + 63) / 64 * 64;
+    if (chunk > 8192) chunk = 8192;
+    if (chunk < 64) chunk = 64;
     RowSplit s;
     s.chunk = chunk;
     s.splits = (int32_t)((vocab + chunk - 1) / chunk);
     return s;
 }
 
-constexpr int64_t kNgramChunk = 2048;            // end positions per scan workgroup
+constexpr int32_t kMaxSplits = 1024;             // rows up to 8,388,608 entries
 
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 

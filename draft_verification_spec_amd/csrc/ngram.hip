@@ -1,21 +1,23 @@
 // N-gram prompt-lookup drafter (Hybrid Spark, Section 4.1 "One step" and
 // Section 4.2 match features; Algorithm 1, NGRAMSCAN).
 //
-// k_ngram_scan : one workgroup per (chunk of end positions, query).  The
-//                query's trailing copy_cap tokens are staged in LDS; each
-//                thread tests end positions j (consecutive threads read
-//                consecutive tokens, so the first comparison -- where almost
-//                every position stops -- is one coalesced load) and extends a
-//                match backwards while tokens agree.  Matches become keys
-//                (length << 32 | j), so "longest, then latest" is the largest
-//                key; each workgroup keeps its top two.
-// k_ngram_final: one wave per query merges the chunk top-2s, derives the
-//                features (n, a, m, j) and copies the draft.
+// One workgroup of 1024 threads per query, one launch:
+//   * the query's trailing copy_cap tokens are staged in LDS;
+//   * each thread tests end positions j = t, t + 1024, ...: it loads the token
+//     at j for a batch of 16 positions (independent coalesced loads, one memory
+//     round trip per batch), and for the rare hits compares up to 4 tokens
+//     backwards itself; positions still matching after 4 go to a candidate list
+//     that whole waves extend 64 tokens per step with a ballot (compared up to
+//     min(j + 1, copy_cap));
+//   * a match of length l >= n_min becomes the key (l << 32 | j), so "longest,
+//     then latest" is the largest key; the workgroup keeps the top two;
+//   * thread 0 derives (n, a, m, j) and the first lanes copy the draft.
 #include "common.hpp"
 
 namespace spec {
 
-constexpr int kScanBlock = 256;
+constexpr int kScanBlock = 1024;
+constexpr int kBatch = 16;
 
 struct NgramParams {
     int32_t bs, nq;
@@ -24,7 +26,6 @@ struct NgramParams {
     const int32_t* extra; int64_t extra_stride; const int32_t* extra_len;
     int32_t n_min, n_max, max_draft, cap;
     int32_t* draft; int32_t* draft_len; int32_t* feat;
-    Top2* part; int32_t nsplit;
 };
 
 struct Text {
@@ -37,7 +38,7 @@ struct Text {
 __device__ __forceinline__ Text query_text(const NgramParams& P, int q)
 {
     Text x;
-    int req = P.query_req ? P.query_req[q] : q;
+    const int req = P.query_req ? P.query_req[q] : q;
     int64_t tl = 0, el = 0;
     x.a = nullptr;
     x.b = nullptr;
@@ -56,74 +57,122 @@ __device__ __forceinline__ Text query_text(const NgramParams& P, int q)
     return x;
 }
 
-__device__ __forceinline__ int32_t tok(const Text& x, int64_t p) { return p < x.na ? x.a[p] : x.b[p - x.na]; }
-
-__global__ __launch_bounds__(kScanBlock) void k_ngram_scan(NgramParams P)
+// Token p of the text: the address is selected first, so a batch of these is
+// a batch of independent loads rather than branches around them.
+__device__ __forceinline__ int32_t tok(const Text& x, int64_t p)
 {
-    const int s = blockIdx.x, q = blockIdx.y;
-    const Text x = query_text(P, q);
-    __shared__ int32_t suf[SPEC_MAX_CAP];
-    const int64_t jlo = (int64_t)s * kNgramChunk;
-    const int64_t jhi = (jlo + kNgramChunk < x.n - 1) ? jlo + kNgramChunk : x.n - 1;  // j <= n-2
-    Top2 best{0, 0};
-    if (jlo < jhi) {
-        const int64_t ns = x.n < P.cap ? x.n : P.cap;
-        for (int64_t i = threadIdx.x; i < ns; i += kScanBlock) suf[i] = tok(x, x.n - 1 - i);
-        __syncthreads();
-        for (int64_t j = jlo + threadIdx.x; j < jhi; j += kScanBlock) {
-            const int64_t lim = (j + 1 < P.cap) ? j + 1 : P.cap;
-            int64_t l = 0;
-            while (l < lim && tok(x, j - l) == suf[l]) ++l;
-            if (l >= P.n_min) best = top2_insert(best, ((uint64_t)l << 32) | (uint64_t)j);
-        }
-    }
-    best = wave_top2(best);
-    __shared__ Top2 sh[kScanBlock / kWave];
-    const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-    if (lane == 0) sh[wid] = best;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        Top2 t = sh[0];
-        for (int w = 1; w < kScanBlock / kWave; ++w) t = top2_merge(t, sh[w]);
-        P.part[(int64_t)q * P.nsplit + s] = t;
-    }
+    const uintptr_t pa = (uintptr_t)(x.a + p);
+    const uintptr_t pb = (uintptr_t)x.b + (uintptr_t)((p - x.na) * (int64_t)sizeof(int32_t));
+    return *(const int32_t*)(p < x.na ? pa : pb);
 }
 
-__global__ __launch_bounds__(kWave) void k_ngram_final(NgramParams P)
+constexpr int kPre = 4;          // tokens each thread compares before handing a match to its wave
+constexpr int kMaxCand = 2048;   // candidate list in LDS; overflow is extended by the thread itself
+
+__global__ __launch_bounds__(kScanBlock) void k_ngram(NgramParams P)
 {
-    const int q = blockIdx.x, t = threadIdx.x;
+    const int q = blockIdx.x;
     const Text x = query_text(P, q);
+    __shared__ int32_t suf[SPEC_MAX_CAP];
+    __shared__ Top2 sh[kScanBlock / kWave];
+    __shared__ int32_t cand[kMaxCand];
+    __shared__ int32_t n_cand;
+    const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+    const int64_t jend = x.n - 1;                 // end positions j < n - 1
+    const int64_t ns = x.n < P.cap ? x.n : P.cap;
+    for (int64_t i = threadIdx.x; i < ns; i += kScanBlock) suf[i] = tok(x, x.n - 1 - i);
+    if (threadIdx.x == 0) n_cand = 0;
+    __syncthreads();
     Top2 best{0, 0};
-    for (int s = t; s < P.nsplit; s += kWave) best = top2_merge(best, P.part[(int64_t)q * P.nsplit + s]);
-    best = wave_top2(best);
-    int32_t* d = P.draft + (int64_t)q * P.max_draft;
-    if (best.a == 0) {
-        for (int k = t; k < P.max_draft; k += kWave) d[k] = -1;
-        if (t == 0) {
-            P.draft_len[q] = 0;
-            P.feat[4 * (int64_t)q + 0] = 0;
-            P.feat[4 * (int64_t)q + 1] = 0;
-            P.feat[4 * (int64_t)q + 2] = 0;
-            P.feat[4 * (int64_t)q + 3] = -1;
+    if (jend > 0) {
+        // phase 1: first kPre tokens per position, thread-private
+        const int32_t s0 = suf[0];
+        for (int64_t base = 0; base < jend; base += (int64_t)kScanBlock * kBatch) {
+            int32_t v[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int64_t j = base + threadIdx.x + (int64_t)u * kScanBlock;
+                const int32_t t = tok(x, j < jend ? j : jend - 1);   // unconditional load, in bounds
+                v[u] = (j < jend) ? t : ~s0;
+            }
+            uint32_t hits = 0;
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) hits |= (uint32_t)(v[u] == s0) << u;
+            while (hits) {
+                const int u = __builtin_ctz(hits);
+                hits &= hits - 1;
+                const int64_t j = base + threadIdx.x + (int64_t)u * kScanBlock;
+                const int64_t lim = (j + 1 < P.cap) ? j + 1 : P.cap;
+                int64_t l = 1;
+                while (l < lim && l < kPre && tok(x, j - l) == suf[l]) ++l;
+                if (l == kPre && l < lim) {
+                    const int c = atomicAdd(&n_cand, 1);
+                    if (c < kMaxCand) {
+                        cand[c] = (int32_t)j;
+                        continue;
+                    }
+                    while (l < lim && tok(x, j - l) == suf[l]) ++l;   // list full: extend here
+                }
+                if (l >= P.n_min) best = top2_insert(best, ((uint64_t)l << 32) | (uint64_t)j);
+            }
         }
-        return;
     }
-    const int64_t l = (int64_t)(best.a >> 32);
-    const int64_t j = (int64_t)(best.a & 0xFFFFFFFFu);
-    const int64_t avail = x.n - 1 - j;
-    const int64_t len = avail < P.max_draft ? avail : P.max_draft;
-    for (int k = t; k < P.max_draft; k += kWave) d[k] = (k < len) ? tok(x, j + 1 + k) : -1;
-    if (t == 0) {
-        int a = 1;
-        if (best.b != 0) {
-            const int64_t jr = (int64_t)(best.b & 0xFFFFFFFFu);
-            a = tok(x, jr + 1) == tok(x, j + 1);
+    __syncthreads();
+    // phase 2: each wave extends listed candidates 64 tokens per step
+    const int nc = n_cand < kMaxCand ? n_cand : kMaxCand;
+    for (int c = wid; c < nc; c += kScanBlock / kWave) {
+        const int64_t j = cand[c];
+        const int64_t lim = (j + 1 < P.cap) ? j + 1 : P.cap;
+        int64_t l = kPre;
+        for (;;) {
+            const int64_t i = l + lane;
+            const bool eq = i < lim && tok(x, j - i) == suf[i];
+            const uint64_t miss = ~__ballot(eq);
+            if (miss == 0) {
+                l += kWave;
+                continue;
+            }
+            l += (int64_t)__builtin_ctzll(miss);
+            break;
         }
-        P.draft_len[q] = (int32_t)len;
-        P.feat[4 * (int64_t)q + 0] = (int32_t)(l < P.n_max ? l : P.n_max);
-        P.feat[4 * (int64_t)q + 1] = a;
-        P.feat[4 * (int64_t)q + 2] = (l >= P.n_max) ? (int32_t)l : 0;
-        P.feat[4 * (int64_t)q + 3] = (int32_t)j;
+        if (l > lim) l = lim;
+        if (lane == 0 && l >= P.n_min) best = top2_insert(best, ((uint64_t)l << 32) | (uint64_t)j);
+    }
+    best = wave_top2(best);
+    if (lane == 0) sh[wid] = best;
+    __syncthreads();
+    if (wid == 0) {
+        Top2 t = lane < kScanBlock / kWave ? sh[lane] : Top2{0, 0};
+        t = wave_top2(t);
+        int32_t* d = P.draft + (int64_t)q * P.max_draft;
+        if (t.a == 0) {
+            for (int k = lane; k < P.max_draft; k += kWave) d[k] = -1;
+            if (lane == 0) {
+                P.draft_len[q] = 0;
+                P.feat[4 * (int64_t)q + 0] = 0;
+                P.feat[4 * (int64_t)q + 1] = 0;
+                P.feat[4 * (int64_t)q + 2] = 0;
+                P.feat[4 * (int64_t)q + 3] = -1;
+            }
+            return;
+        }
+        const int64_t l = (int64_t)(t.a >> 32);
+        const int64_t j = (int64_t)(t.a & 0xFFFFFFFFu);
+        const int64_t avail = x.n - 1 - j;
+        const int64_t len = avail < P.max_draft ? avail : P.max_draft;
+        for (int k = lane; k < P.max_draft; k += kWave) d[k] = (k < len) ? tok(x, j + 1 + k) : -1;
+        if (lane == 0) {
+            int a = 1;
+            if (t.b != 0) {
+                const int64_t jr = (int64_t)(t.b & 0xFFFFFFFFu);
+                a = tok(x, jr + 1) == tok(x, j + 1);
+            }
+            P.draft_len[q] = (int32_t)len;
+            P.feat[4 * (int64_t)q + 0] = (int32_t)(l < P.n_max ? l : P.n_max);
+            P.feat[4 * (int64_t)q + 1] = a;
+            P.feat[4 * (int64_t)q + 2] = (l >= P.n_max) ? (int32_t)l : 0;
+            P.feat[4 * (int64_t)q + 3] = (int32_t)j;
+        }
     }
 }
 
@@ -131,14 +180,7 @@ __global__ __launch_bounds__(kWave) void k_ngram_final(NgramParams P)
 
 using namespace spec;
 
-static int32_t ngram_splits(const spec_ngram_args* a)
-{
-    const int64_t tmax = a->ctx_stride + (a->extra ? a->extra_stride : 0);
-    int64_t n = (tmax - 1 + kNgramChunk - 1) / kNgramChunk;
-    return (int32_t)(n < 1 ? 1 : n);
-}
-
-size_t spec_ngram_ws(const spec_ngram_args* a) { return align256((size_t)a->nq * ngram_splits(a) * sizeof(Top2)); }
+size_t spec_ngram_ws(const spec_ngram_args*) { return 0; }
 
 int spec_ngram_launch(const spec_ngram_args* a, hipStream_t st)
 {
@@ -149,9 +191,6 @@ int spec_ngram_launch(const spec_ngram_args* a, hipStream_t st)
     P.extra = a->extra; P.extra_stride = a->extra ? a->extra_stride : 0; P.extra_len = a->extra_len;
     P.n_min = a->n_min; P.n_max = a->n_max; P.max_draft = a->max_draft; P.cap = a->copy_cap;
     P.draft = a->draft; P.draft_len = a->draft_len; P.feat = a->feat;
-    P.part = (Top2*)a->workspace;
-    P.nsplit = ngram_splits(a);
-    hipLaunchKernelGGL(k_ngram_scan, dim3(P.nsplit, a->nq), dim3(kScanBlock), 0, st, P);
-    hipLaunchKernelGGL(k_ngram_final, dim3(a->nq), dim3(kWave), 0, st, P);
+    hipLaunchKernelGGL(k_ngram, dim3(a->nq), dim3(kScanBlock), 0, st, P);
     return spec_record_hip_error(hipGetLastError());
 }

@@ -1,38 +1,51 @@
 // Chain and tree verification kernels.
 //
-// Chain rule: speculative sampling as in the LongSpark page ("Efficient
+// Chain rule: speculative sampling as on the LongSpark page ("Efficient
 // speculative decoding with a fixed-cost parallel drafter", Section 2.1) --
 // accept y_i with probability min(1, p_i(y_i)/q_i(y_i)); at the first reject
 // draw from norm(max(0, p_i - q_i)); after the last slot draw the bonus from
 // p_{b+1}.  Point-mass slots (Hybrid Spark, Section 5.8 and Appendix H) use
-// q = delta_y.  At T = 0 a draft is accepted iff it is the target argmax
-// (Hybrid Spark, Appendix H; AdaSpark, Section 2.2).
+// q = delta_y, so their residual is p without y.  At T = 0 a draft is
+// accepted iff it is the target argmax (Hybrid Spark, Appendix H; AdaSpark,
+// Section 2.2).
 //
 // Data flow (one stream, no host synchronisation):
-//   k_row_stats   : every read logit row is cut into chunks; one workgroup per
-//                   (chunk, request) streams the request's rows through that
-//                   chunk with 16-byte loads and keeps an online (max, sum of
-//                   2^(z*c - max*c)) per thread, c = log2(e)/T; at T = 0 a
-//                   (max, first argmax) pair instead.  Partials go to the
-//                   workspace.  This is the HBM-bound pass.
-//   k_decide      : one workgroup per request merges the chunk partials of its
-//                   rows, evaluates p(y), q(y) for every slot in parallel,
-//                   finds the first rejection and records what to sample.
-//   k_sample_part : chunk sums (fp64) of the residual / bonus weights.
-//   k_sample_final: finds the chunk holding u*W, rescans it tile by tile with a
-//                   workgroup prefix sum, writes the token, commits.
+//   k_stats      : the HBM-bound pass.  Work items are (verified row, chunk)
+//                  pairs flattened over the whole batch, so requests with many
+//                  rows do not serialise; a workgroup strides over items.  Per
+//                  item it streams a 32 KB chunk with 16-byte loads and keeps
+//                  an online maximum m and sum of 2^(z*c - m*c) (c = log2(e)/T;
+//                  pairwise fp32 within a 32-element tile, fp64 across tiles),
+//                  or at T = 0 the maximum and its first index.  Chain items
+//                  also stream the paired draft row of a probabilistic slot.
+//   k_decide     : one workgroup per request merges its chunk partials, finds
+//                  p(y), q(y) of every slot in parallel, the first rejection,
+//                  and -- for the bonus row and point-mass residuals -- draws
+//                  the token from the chunk sums it already has plus one chunk
+//                  rescan; then commits.
+//   k_sample_part, k_sample_final: only for probabilistic residuals
+//                  max(0, p - q), whose chunk sums need both rows.
 #include "common.hpp"
 
 namespace spec {
 
 constexpr int kBlock = 256;
+constexpr int kTile = 4;              // 16-byte vectors in flight per thread per step
+constexpr int kMaxLdsPrefix = 4096;   // batch sizes whose row prefix fits in LDS
+
+// Chunk partial: T > 0: (m, -, s); T = 0: (best, idx | bad << 31, -).
+struct Partial {
+    float m;
+    int32_t idx;
+    double s;
+};
 
 struct Dec {
-    int32_t mode;   // 0: nothing to draw; 1: from p of row_t; 2: max(0, p - q); 3: p without y
+    int32_t mode;   // 0: done; 2: draw from max(0, p - q) in the second pass
     int32_t nacc;
     int32_t y;
     float Ot, Od;   // base-2 offsets of the target / draft rows
-    float pad0;
+    int32_t pad;
     int64_t row_t, row_d;
     double Zt, Zd;  // base-2 normalisers relative to the offsets
 };
@@ -42,12 +55,12 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 template <int DT>
 __device__ __forceinline__ float load1(const void* base, int64_t e)
 {
-    if constexpr (DT == SPEC_F32) {
-        return ((const float*)base)[e];
-    } else {
-        return bf16_bits_to_float(((const uint16_t*)base)[e]);
-    }
+    if constexpr (DT == SPEC_F32) return ((const float*)base)[e];
+    else return bf16_bits_to_float(((const uint16_t*)base)[e]);
 }
+
+template <int DT>
+constexpr int vec_of() { return DT == SPEC_F32 ? 4 : 8; }
 
 template <int DT, int VEC>
 __device__ __forceinline__ void loadv(const void* base, int64_t e, float* v)
@@ -58,17 +71,13 @@ __device__ __forceinline__ void loadv(const void* base, int64_t e, float* v)
         static_assert(VEC == 4, "fp32 vectors are 16 bytes");
         float4 x = *(const float4*)((const float*)base + e);
         v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-    } else if constexpr (VEC == 8) {
+    } else {
+        static_assert(VEC == 8, "bf16 vectors are 16 bytes");
         uint4 x = *(const uint4*)((const uint16_t*)base + e);
         v[0] = __uint_as_float(x.x << 16); v[1] = __uint_as_float(x.x & 0xFFFF0000u);
         v[2] = __uint_as_float(x.y << 16); v[3] = __uint_as_float(x.y & 0xFFFF0000u);
         v[4] = __uint_as_float(x.z << 16); v[5] = __uint_as_float(x.z & 0xFFFF0000u);
         v[6] = __uint_as_float(x.w << 16); v[7] = __uint_as_float(x.w & 0xFFFF0000u);
-    } else {
-        static_assert(VEC == 4, "bf16 vectors are 8 or 16 bytes");
-        uint2 x = *(const uint2*)((const uint16_t*)base + e);
-        v[0] = __uint_as_float(x.x << 16); v[1] = __uint_as_float(x.x & 0xFFFF0000u);
-        v[2] = __uint_as_float(x.y << 16); v[3] = __uint_as_float(x.y & 0xFFFF0000u);
     }
 }
 
@@ -78,46 +87,61 @@ __device__ __forceinline__ const void* row_ptr(const void* base, int64_t row, in
     return (const char*)base + row * stride * (DT == SPEC_F32 ? 4 : 2);
 }
 
+__device__ __forceinline__ float logit_at(const void* base, int dt, int64_t row, int64_t stride, int64_t v)
+{
+    return dt == SPEC_F32 ? ((const float*)base)[row * stride + v]
+                          : bf16_bits_to_float(((const uint16_t*)base)[row * stride + v]);
+}
+
 // ---------------------------------------------------------------------------
-// online softmax statistics
+// online softmax statistics, fp64 accumulation
 // ---------------------------------------------------------------------------
 
-// (m, s): m = largest raw logit seen, s = sum of 2^(z*c - m*c) (the offset m*c
-// is always recomputed the same way, so rescaling stays consistent).
 template <int N>
-__device__ __forceinline__ void sm_update(const float* v, float c, float& m, float& s)
+__device__ __forceinline__ float pairwise_sum(float* t)
+{
+#pragma unroll
+    for (int w = 1; w < N; w <<= 1)
+#pragma unroll
+        for (int i = 0; i + w < N; i += 2 * w) t[i] += t[i + w];
+    return t[0];
+}
+
+// Fold N values into (m, s): m = largest raw logit, s = sum of 2^(z*c - m*c).
+template <int N>
+__device__ __forceinline__ void sm_update(const float* v, float c, float& m, double& s)
 {
     float tm = v[0];
 #pragma unroll
     for (int i = 1; i < N; ++i) tm = fmaxf(tm, v[i]);
     if (tm > m) {
-        float on = tm * c;
-        s = (m == -INFINITY) ? 0.0f : s * fast_exp2(m * c - on);
+        if (m != -INFINITY) s *= (double)fast_exp2((float)((double)(m * c) - (double)(tm * c)));
         m = tm;
     }
     if (m != -INFINITY) {
         const float o = m * c;
+        float t[N];
 #pragma unroll
-        for (int i = 0; i < N; ++i) s += fast_exp2(fmaf(v[i], c, -o));
+        for (int i = 0; i < N; ++i) t[i] = fast_exp2(fmaf(v[i], c, -o));
+        s += (double)pairwise_sum<N>(t);
     } else if (tm != tm) {
-        s = __builtin_nanf("");  // a tile of NaN before any finite value
+        s = __builtin_nan("");  // a tile of NaN before any finite value
     }
 }
 
-__device__ __forceinline__ void sm_combine(float& m, float& s, float m2, float s2, float c)
+__device__ __forceinline__ void sm_combine(float& m, double& s, float m2, double s2, float c)
 {
     if (m2 > m) {
         float t = m; m = m2; m2 = t;
-        t = s; s = s2; s2 = t;
+        double u = s; s = s2; s2 = u;
     }
     if (m2 == -INFINITY) {
         if (s2 != s2) s = s2;
         return;
     }
-    s = s + s2 * fast_exp2(m2 * c - m * c);
+    s += s2 * (double)fast_exp2((float)((double)(m2 * c) - (double)(m * c)));
 }
 
-// (best, idx, bad): largest logit, its lowest index, any NaN/+Inf seen.
 struct ArgAcc {
     float best;
     int32_t idx;
@@ -136,17 +160,17 @@ __device__ __forceinline__ void am_combine(ArgAcc& a, const ArgAcc& b)
     a.bad |= b.bad;
 }
 
-template <int DT, int VEC, int U>
-__device__ __forceinline__ void chunk_softmax(const void* row, int64_t lo, int64_t hi, float c, float& m, float& s)
+template <int DT, int VEC>
+__device__ __forceinline__ void chunk_softmax(const void* row, int64_t lo, int64_t hi, float c, float& m, double& s)
 {
     const int64_t hv = lo + (hi - lo) / VEC * VEC;
     constexpr int64_t STEP = (int64_t)kBlock * VEC;
     int64_t e = lo + (int64_t)threadIdx.x * VEC;
-    for (; e + (U - 1) * STEP < hv; e += U * STEP) {
-        float v[U * VEC];
+    for (; e + (kTile - 1) * STEP < hv; e += kTile * STEP) {
+        float v[kTile * VEC];
 #pragma unroll
-        for (int u = 0; u < U; ++u) loadv<DT, VEC>(row, e + u * STEP, v + u * VEC);
-        sm_update<U * VEC>(v, c, m, s);
+        for (int u = 0; u < kTile; ++u) loadv<DT, VEC>(row, e + u * STEP, v + u * VEC);
+        sm_update<kTile * VEC>(v, c, m, s);
     }
     for (; e < hv; e += STEP) {
         float v[VEC];
@@ -159,18 +183,18 @@ __device__ __forceinline__ void chunk_softmax(const void* row, int64_t lo, int64
     }
 }
 
-template <int DT, int VEC, int U>
+template <int DT, int VEC>
 __device__ __forceinline__ void chunk_argmax(const void* row, int64_t lo, int64_t hi, ArgAcc& a)
 {
     const int64_t hv = lo + (hi - lo) / VEC * VEC;
     constexpr int64_t STEP = (int64_t)kBlock * VEC;
     int64_t e = lo + (int64_t)threadIdx.x * VEC;
-    for (; e + (U - 1) * STEP < hv; e += U * STEP) {
-        float v[U * VEC];
+    for (; e + (kTile - 1) * STEP < hv; e += kTile * STEP) {
+        float v[kTile * VEC];
 #pragma unroll
-        for (int u = 0; u < U; ++u) loadv<DT, VEC>(row, e + u * STEP, v + u * VEC);
+        for (int u = 0; u < kTile; ++u) loadv<DT, VEC>(row, e + u * STEP, v + u * VEC);
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int u = 0; u < kTile; ++u)
 #pragma unroll
             for (int k = 0; k < VEC; ++k) am_update(v[u * VEC + k], (int32_t)(e + u * STEP + k), a);
     }
@@ -183,118 +207,221 @@ __device__ __forceinline__ void chunk_argmax(const void* row, int64_t lo, int64_
     for (int64_t t = hv + threadIdx.x; t < hi; t += kBlock) am_update(load1<DT>(row, t), (int32_t)t, a);
 }
 
-// Partial of one (row, chunk): T > 0 -> (m, s); T = 0 -> (best, idx bits | bad in sign of a NaN).
-struct Partial {
-    float a;
-    float b;
-};
-
-// Row set of a request: rows row_base[r] + k, k < count, count from a device
-// array clamped to [cmin, cmax] plus cadd.  A draft pass skips point-mass slots.
-struct RowSet {
-    const void* logits;
-    int64_t stride;
-    const int64_t* row_base;
-    int64_t n_rows;          // rows in the logits buffer (bounds)
-    const int32_t* counts;
-    int32_t cmin, cmax, cadd;
-    const uint8_t* skip_pm;  // slot flags [bs, ld] or null
-    int32_t ld;
-    int32_t slot_base;       // partial row index offset
-};
-
+// One chunk of one row -> one partial (workgroup-wide; every thread calls it).
 template <int DT, int VEC, bool GREEDY>
-__global__ __launch_bounds__(kBlock) void k_row_stats(RowSet rs, int32_t vocab, int64_t chunk, int32_t splits,
-                                                      float c, Partial* __restrict__ part, int32_t NR)
+__device__ void row_chunk(const void* rp, int64_t lo, int64_t hi, float c, Partial* out)
 {
-    const int s = blockIdx.x;
-    const int r = blockIdx.y;
-    int cnt = rs.counts[r];
-    cnt = (cnt < rs.cmin ? rs.cmin : (cnt > rs.cmax ? rs.cmax : cnt)) + rs.cadd;
-    const int64_t lo = (int64_t)s * chunk;
-    const int64_t hi = (lo + chunk < vocab) ? lo + chunk : vocab;
-    const int64_t base = rs.row_base[r];
-    __shared__ float sh_a[kBlock / kWave];
-    __shared__ float sh_b[kBlock / kWave];
+    __shared__ float sh_m[kBlock / kWave];
+    __shared__ double sh_s[kBlock / kWave];
     __shared__ int32_t sh_i[kBlock / kWave];
     const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-    for (int k = 0; k < cnt; ++k) {
-        if (rs.skip_pm && (rs.skip_pm[(int64_t)r * rs.ld + k] & SPEC_SLOT_POINT_MASS)) continue;
-        Partial* out = part + ((int64_t)r * NR + rs.slot_base + k) * splits + s;
-        const int64_t row = base + k;
-        if (row < 0 || row >= rs.n_rows) {
-            if (threadIdx.x == 0) { out->a = __builtin_nanf(""); out->b = __builtin_nanf(""); }
-            continue;
+    if constexpr (!GREEDY) {
+        float m = -INFINITY;
+        double s = 0.0;
+        chunk_softmax<DT, VEC>(rp, lo, hi, c, m, s);
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1) {
+            const float m2 = __shfl_xor(m, o, kWave);
+            const double s2 = __shfl_xor(s, o, kWave);
+            sm_combine(m, s, m2, s2, c);
         }
-        const void* rp = row_ptr<DT>(rs.logits, row, rs.stride);
-        if constexpr (!GREEDY) {
-            float m = -INFINITY, sum = 0.0f;
-            chunk_softmax<DT, VEC, 2>(rp, lo, hi, c, m, sum);
+        if (lane == 0) { sh_m[wid] = m; sh_s[wid] = s; }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            for (int w = 1; w < kBlock / kWave; ++w) sm_combine(m, s, sh_m[w], sh_s[w], c);
+            Partial p;
+            p.m = m; p.idx = 0; p.s = s;
+            *out = p;
+        }
+        __syncthreads();
+    } else {
+        ArgAcc acc{-INFINITY, 0x7FFFFFFF, 0};
+        chunk_argmax<DT, VEC>(rp, lo, hi, acc);
 #pragma unroll
-            for (int o = kWave / 2; o > 0; o >>= 1) {
-                float m2 = __shfl_xor(m, o, kWave), s2 = __shfl_xor(sum, o, kWave);
-                sm_combine(m, sum, m2, s2, c);
+        for (int o = kWave / 2; o > 0; o >>= 1) {
+            ArgAcc b{__shfl_xor(acc.best, o, kWave), __shfl_xor(acc.idx, o, kWave), __shfl_xor(acc.bad, o, kWave)};
+            am_combine(acc, b);
+        }
+        if (lane == 0) { sh_m[wid] = acc.best; sh_i[wid] = acc.idx | (acc.bad ? (int32_t)0x80000000 : 0); }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            ArgAcc t{-INFINITY, 0x7FFFFFFF, 0};
+            for (int w = 0; w < kBlock / kWave; ++w) {
+                ArgAcc b{sh_m[w], sh_i[w] & 0x7FFFFFFF, (sh_i[w] >> 31) & 1};
+                am_combine(t, b);
             }
-            if (lane == 0) { sh_a[wid] = m; sh_b[wid] = sum; }
-            __syncthreads();
-            if (threadIdx.x == 0) {
-                for (int w = 1; w < kBlock / kWave; ++w) sm_combine(m, sum, sh_a[w], sh_b[w], c);
-                out->a = m;
-                out->b = sum;
-            }
-            __syncthreads();
-        } else {
-            ArgAcc acc{-INFINITY, 0x7FFFFFFF, 0};
-            chunk_argmax<DT, VEC, 2>(rp, lo, hi, acc);
+            Partial p;
+            p.m = t.best; p.idx = t.idx | (t.bad ? (int32_t)0x80000000 : 0); p.s = 0.0;
+            *out = p;
+        }
+        __syncthreads();
+    }
+}
+
+__device__ __forceinline__ void bad_partial(Partial* out)
+{
+    if (threadIdx.x == 0) {
+        Partial p;
+        p.m = __builtin_nanf(""); p.idx = (int32_t)0x80000000; p.s = __builtin_nan("");
+        *out = p;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// the statistics pass
+// ---------------------------------------------------------------------------
+
+struct StatsParams {
+    const void* logits; int64_t stride; const int64_t* row_base; int64_t n_rows;
+    const void* dlogits; int64_t dstride; const int64_t* drow_base; int64_t dn_rows;
+    const int32_t* counts;        // target rows of request r = clamp(counts[r], cmin, cmax) + cadd
+    int32_t cmin, cmax, cadd;
+    const uint8_t* slot_flags;    // chain: draft row k exists iff k < clamp(counts) and the slot is probabilistic
+    int32_t ld;
+    int32_t bs, vocab;
+    int64_t chunk;
+    int32_t splits;
+    float c;
+    Partial* part;
+    int32_t NR;                   // partial rows per request
+    int32_t draft_base;           // partial row of draft row k = draft_base + k
+    const int32_t* gprefix;       // [bs + 1] row prefix in global memory (large batches) or null
+};
+
+__device__ __forceinline__ int32_t target_rows(const StatsParams& P, int r)
+{
+    int c = P.counts[r];
+    c = c < P.cmin ? P.cmin : (c > P.cmax ? P.cmax : c);
+    return c + P.cadd;
+}
+
+// Exclusive prefix of the per-request target rows over the workgroup; returns the total.
+__device__ int32_t row_prefix(const StatsParams& P, int32_t* pre)
+{
+    __shared__ int32_t sh[kBlock / kWave];
+    const int per = (P.bs + kBlock - 1) / kBlock;
+    const int r0 = threadIdx.x * per;
+    int32_t local = 0;
+    for (int r = r0; r < r0 + per && r < P.bs; ++r) local += target_rows(P, r);
+    const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+    int32_t inc = local;
 #pragma unroll
-            for (int o = kWave / 2; o > 0; o >>= 1) {
-                ArgAcc b{__shfl_xor(acc.best, o, kWave), __shfl_xor(acc.idx, o, kWave), __shfl_xor(acc.bad, o, kWave)};
-                am_combine(acc, b);
+    for (int o = 1; o < kWave; o <<= 1) {
+        int32_t u = __shfl_up(inc, o, kWave);
+        if (lane >= o) inc += u;
+    }
+    if (lane == kWave - 1) sh[wid] = inc;
+    __syncthreads();
+    int32_t before = 0, tot = 0;
+    for (int w = 0; w < kBlock / kWave; ++w) {
+        if (w < wid) before += sh[w];
+        tot += sh[w];
+    }
+    int32_t run = before + inc - local;
+    for (int r = r0; r < r0 + per && r < P.bs; ++r) {
+        pre[r] = run;
+        run += target_rows(P, r);
+    }
+    if (threadIdx.x == 0) pre[P.bs] = tot;
+    __syncthreads();
+    return tot;
+}
+
+__global__ __launch_bounds__(kBlock) void k_plan(StatsParams P, int32_t* pre)
+{
+    row_prefix(P, pre);
+}
+
+template <int DT, int VEC, int DDT, int DVEC, bool GREEDY, bool DRAFT, bool GPRE>
+__global__ __launch_bounds__(kBlock) void k_stats(StatsParams P)
+{
+    __shared__ int32_t lpre[GPRE ? 1 : kMaxLdsPrefix + 1];
+    const int32_t* pre;
+    int32_t total;
+    if constexpr (GPRE) {
+        pre = P.gprefix;
+        total = pre[P.bs];
+    } else {
+        total = row_prefix(P, lpre);
+        pre = lpre;
+    }
+    // each workgroup takes a contiguous range of items (consecutive chunks of
+    // the same rows), so the row lookup is redone only when the row changes
+    const int64_t items = (int64_t)total * P.splits;
+    const int64_t per = (items + gridDim.x - 1) / gridDim.x;
+    const int64_t it0 = (int64_t)blockIdx.x * per;
+    const int64_t it1 = (it0 + per < items) ? it0 + per : items;
+    int64_t cur_rowf = -1;
+    int r = 0, k = 0;
+    int64_t row = 0, drow = 0;
+    bool draft_row = false;
+    for (int64_t it = it0; it < it1; ++it) {
+        const int64_t rowf = it / P.splits;
+        const int s = (int)(it - rowf * P.splits);
+        if (rowf != cur_rowf) {
+            cur_rowf = rowf;
+            int lo = 0, hi = P.bs;   // pre[lo] <= rowf < pre[hi]
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (pre[mid] <= rowf) lo = mid; else hi = mid;
             }
-            if (lane == 0) { sh_a[wid] = acc.best; sh_i[wid] = acc.idx | (acc.bad ? (int32_t)0x80000000 : 0); }
-            __syncthreads();
-            if (threadIdx.x == 0) {
-                acc.bad = 0;
-                for (int w = 0; w < kBlock / kWave; ++w) {
-                    ArgAcc b{sh_a[w], sh_i[w] & 0x7FFFFFFF, (sh_i[w] >> 31) & 1};
-                    am_combine(acc, b);
-                }
-                out->a = acc.best;
-                out->b = __int_as_float(acc.idx | (acc.bad ? (int32_t)0x80000000 : 0));
+            r = lo;
+            k = (int)(rowf - pre[r]);
+            row = P.row_base[r] + k;
+            if constexpr (DRAFT) {
+                const int b = target_rows(P, r) - P.cadd;
+                draft_row = k < b && !(P.slot_flags[(int64_t)r * P.ld + k] & SPEC_SLOT_POINT_MASS);
+                if (draft_row) drow = P.drow_base[r] + k;
             }
-            __syncthreads();
+        }
+        const int64_t clo = (int64_t)s * P.chunk;
+        const int64_t chi = (clo + P.chunk < P.vocab) ? clo + P.chunk : P.vocab;
+        Partial* out = P.part + ((int64_t)r * P.NR + k) * P.splits + s;
+        if (row < 0 || row >= P.n_rows) bad_partial(out);
+        else row_chunk<DT, VEC, GREEDY>(row_ptr<DT>(P.logits, row, P.stride), clo, chi, P.c, out);
+        if constexpr (DRAFT) {
+            if (draft_row) {
+                Partial* dout = P.part + ((int64_t)r * P.NR + P.draft_base + k) * P.splits + s;
+                if (drow < 0 || drow >= P.dn_rows) bad_partial(dout);
+                else row_chunk<DDT, DVEC, false>(row_ptr<DDT>(P.dlogits, drow, P.dstride), clo, chi, P.c, dout);
+            }
         }
     }
 }
 
-// Merge the chunk partials of one row.  Softmax: returns false when the row
-// is unusable; *O = m*c, *Z = sum relative to O (fp64).
-__device__ bool merge_softmax(const Partial* p, int splits, float c, float* O, double* Z)
+// ---------------------------------------------------------------------------
+// merging partials
+// ---------------------------------------------------------------------------
+
+// Softmax row from its chunk partials p[0], p[st], ...: *O = m*c, *Z = sum
+// relative to O (fp64, one online pass); false when unusable.
+__device__ bool merge_softmax(const Partial* p, int splits, int st, float c, float* O, double* Z)
 {
     float m = -INFINITY;
+    double z = 0.0;
     bool nan = false;
     for (int s = 0; s < splits; ++s) {
-        m = fmaxf(m, p[s].a);
-        nan |= (p[s].a != p[s].a) || (p[s].b != p[s].b);
+        const Partial q = p[s * st];
+        nan |= (q.m != q.m) || (q.s != q.s);
+        if (q.m == -INFINITY) continue;
+        if (q.m > m) {
+            if (m != -INFINITY) z *= (double)fast_exp2((float)((double)(m * c) - (double)(q.m * c)));
+            m = q.m;
+        }
+        z += q.s * (double)fast_exp2((float)((double)(q.m * c) - (double)(m * c)));
     }
-    const float o = m * c;
-    double z = 0.0;
-    for (int s = 0; s < splits; ++s) {
-        if (p[s].a == -INFINITY) continue;
-        z += (double)p[s].b * (double)fast_exp2(p[s].a * c - o);
-    }
-    *O = o;
+    *O = m * c;
     *Z = z;
     return !nan && m != -INFINITY && m != INFINITY && z > 0.0 && z < INFINITY;
 }
 
-__device__ bool merge_argmax(const Partial* p, int splits, int32_t* idx)
+__device__ bool merge_argmax(const Partial* p, int splits, int st, int32_t* idx)
 {
     ArgAcc acc{-INFINITY, 0x7FFFFFFF, 0};
     for (int s = 0; s < splits; ++s) {
-        int32_t bits = __float_as_int(p[s].b);
-        ArgAcc b{p[s].a, bits & 0x7FFFFFFF, (bits >> 31) & 1};
-        if (p[s].a != p[s].a) b.bad = 1;
+        const Partial q = p[s * st];
+        ArgAcc b{q.m, q.idx & 0x7FFFFFFF, (q.idx >> 31) & 1};
+        if (q.m != q.m) b.bad = 1;
         am_combine(acc, b);
     }
     *idx = acc.idx;
@@ -302,7 +429,7 @@ __device__ bool merge_argmax(const Partial* p, int splits, int32_t* idx)
 }
 
 // ---------------------------------------------------------------------------
-// decide
+// drawing a token by inverse CDF
 // ---------------------------------------------------------------------------
 
 struct ChainParams {
@@ -314,174 +441,20 @@ struct ChainParams {
     const int32_t* tokens; const uint8_t* slot_flags; const int32_t* n_slots;
     const float* u_acc; const float* u_smp;
     int32_t* out_tokens; int32_t* out_num; int32_t* out_acc; float* out_p; float* out_q; uint32_t* out_flags;
-    int32_t* ctx; int64_t ctx_stride; int32_t* ctx_len; int32_t ctx_cap;
+    int32_t* ctx; int64_t ctx_stride; const int32_t* ctx_len; int32_t* ctx_len_out; int32_t ctx_cap;
     Partial* part; int32_t NR; int32_t splits; int64_t chunk;
     Dec* dec; double* sums;
+    bool t_aligned, d_aligned;  // rows allow 16-byte vector loads
 };
 
-__device__ __forceinline__ float logit_at(const void* base, int dt, int64_t row, int64_t stride, int64_t v)
-{
-    return dt == SPEC_F32 ? ((const float*)base)[row * stride + v]
-                          : bf16_bits_to_float(((const uint16_t*)base)[row * stride + v]);
-}
-
-constexpr int kDecideBlock = 128;  // >= 2 * SPEC_MAX_DRAFT + 1 rows
-
-__global__ __launch_bounds__(kDecideBlock) void k_decide(ChainParams P)
-{
-    const int r = blockIdx.x;
-    const int t = threadIdx.x;
-    const int ld = P.ld;
-    int b = P.n_slots[r];
-    const bool badlen = (b < 0 || b > ld);
-    b = b < 0 ? 0 : (b > ld ? ld : b);
-    __shared__ float sO[kDecideBlock];
-    __shared__ double sZ[kDecideBlock];
-    __shared__ int32_t sArg[kDecideBlock];
-    __shared__ int32_t sOk[kDecideBlock];
-    __shared__ uint32_t sFlags;
-    __shared__ uint64_t sRej;
-    if (t == 0) { sFlags = badlen ? SPEC_FLAG_BAD_LENGTH : 0u; sRej = 0; }
-    // row t: target rows 0..b, draft rows ld+1 .. ld+b (probabilistic slots, T > 0)
-    bool is_row = false;
-    if (t <= b) is_row = true;
-    else if (!P.greedy && P.dlogits && t >= ld + 1 && t <= ld + b) {
-        const int i = t - ld - 1;
-        is_row = !(P.slot_flags && (P.slot_flags[(int64_t)r * ld + i] & SPEC_SLOT_POINT_MASS));
-    }
-    sOk[t] = 0;
-    if (is_row) {
-        const Partial* p = P.part + ((int64_t)r * P.NR + t) * P.splits;
-        if (P.greedy) {
-            int32_t idx;
-            sOk[t] = merge_argmax(p, P.splits, &idx);
-            sArg[t] = idx;
-        } else {
-            float O; double Z;
-            sOk[t] = merge_softmax(p, P.splits, P.c, &O, &Z);
-            sO[t] = O;
-            sZ[t] = Z;
-        }
-    }
-    __syncthreads();
-    // slot i = t < b: p(y), q(y), accept
-    bool acc = true;
-    uint32_t fl = 0;
-    if (t < b) {
-        const int64_t off = (int64_t)r * ld + t;
-        const int32_t y = P.tokens[off];
-        const bool pm = !P.slot_flags || (P.slot_flags[off] & SPEC_SLOT_POINT_MASS);
-        const bool bad = (y < 0 || y >= P.vocab);
-        if (bad) fl |= SPEC_FLAG_BAD_TOKEN;
-        const int64_t trow = P.row_base[r] + t;
-        if (!sOk[t]) fl |= SPEC_FLAG_BAD_LOGITS;
-        double p = 0.0, q = 1.0;
-        if (P.greedy) {
-            p = (!bad && sOk[t] && sArg[t] == y) ? 1.0 : 0.0;
-            acc = (p == 1.0);
-        } else {
-            if (!bad && sOk[t]) {
-                float z = logit_at(P.logits, P.dt, trow, P.stride, y);
-                p = (double)fast_exp2(fmaf(z, P.c, -sO[t])) / sZ[t];
-            }
-            if (!pm) {
-                const int dr = ld + 1 + t;
-                if (!sOk[dr]) fl |= SPEC_FLAG_BAD_LOGITS;
-                q = 0.0;
-                if (!bad && sOk[dr] && P.dlogits) {
-                    const int64_t drow = P.drow_base[r] + t;
-                    float w = logit_at(P.dlogits, P.ddt, drow, P.dstride, y);
-                    q = (double)fast_exp2(fmaf(w, P.c, -sO[dr])) / sZ[dr];
-                }
-            }
-            const double rho = q > 0.0 ? p / q : 0.0;
-            acc = (double)P.u_acc[off] < rho;
-        }
-        if (P.out_p) P.out_p[off] = (float)p;
-        if (P.out_q) P.out_q[off] = (float)q;
-        if (!acc) atomicOr((unsigned long long*)&sRej, 1ull << t);
-        if (fl) atomicOr(&sFlags, fl);
-    } else if (t < ld) {
-        const int64_t off = (int64_t)r * ld + t;
-        if (P.out_p) P.out_p[off] = 0.0f;
-        if (P.out_q) P.out_q[off] = 0.0f;
-    }
-    __syncthreads();
-    const uint64_t rej = sRej;
-    const int nacc = rej ? (int)__builtin_ctzll(rej) : b;
-    // outputs: accepted prefix, -1 padding
-    for (int i = t; i <= ld; i += kDecideBlock)
-        P.out_tokens[(int64_t)r * (ld + 1) + i] = (i < nacc) ? P.tokens[(int64_t)r * ld + i] : -1;
-    if (t == 0) {
-        uint32_t flags = sFlags;
-        if (nacc == b && !sOk[b]) flags |= SPEC_FLAG_BAD_LOGITS;
-        P.out_num[r] = nacc + 1;
-        P.out_acc[r] = nacc;
-        Dec d;
-        d.nacc = nacc;
-        d.mode = 0;
-        d.y = -1;
-        d.Ot = d.Od = 0.0f;
-        d.pad0 = 0.0f;
-        d.row_t = P.row_base[r] + nacc;
-        d.row_d = -1;
-        d.Zt = d.Zd = 1.0;
-        if (P.greedy) {
-            int32_t tok = sOk[nacc] ? sArg[nacc] : -1;
-            if (tok == 0x7FFFFFFF) tok = -1;
-            P.out_tokens[(int64_t)r * (ld + 1) + nacc] = tok;
-        } else if (!(d.row_t >= 0 && d.row_t < P.n_rows) || !sOk[nacc]) {
-            d.mode = 0;          // unusable row: the token stays -1, flagged above
-            flags |= SPEC_FLAG_BAD_LOGITS;
-        } else {
-            d.Ot = sO[nacc];
-            d.Zt = sZ[nacc];
-            if (nacc == b) {
-                d.mode = 1;
-            } else {
-                const int64_t off = (int64_t)r * ld + nacc;
-                const int32_t y = P.tokens[off];
-                const bool pm = !P.slot_flags || (P.slot_flags[off] & SPEC_SLOT_POINT_MASS);
-                const bool bad = (y < 0 || y >= P.vocab);
-                const int dr = ld + 1 + nacc;
-                if (bad) {
-                    d.mode = 1;
-                } else if (pm) {
-                    d.mode = 3;
-                    d.y = y;
-                } else if (sOk[dr] && P.dlogits) {
-                    d.mode = 2;
-                    d.y = y;
-                    d.row_d = P.drow_base[r] + nacc;
-                    d.Od = sO[dr];
-                    d.Zd = sZ[dr];
-                } else {
-                    d.mode = 1;  // unusable draft row (flagged): fall back to p
-                }
-            }
-        }
-        P.dec[r] = d;
-        if (flags) atomicOr(&P.out_flags[r], flags);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// sampling
-// ---------------------------------------------------------------------------
-
-// Weight of token v (fp64) for the draw described by d.
-template <int DTT, int DTD>
-__device__ __forceinline__ double draw_weight(const ChainParams& P, const Dec& d, int mode, double ratio, int64_t v)
-{
-    const float z = logit_at(P.logits, DTT, d.row_t, P.stride, v);
-    const double ep = (double)fast_exp2(fmaf(z, P.c, -d.Ot));
-    if (mode == 1) return ep;
-    if (mode == 3) return v == d.y ? 0.0 : ep;
-    const float w = logit_at(P.dlogits, DTD, d.row_d, P.dstride, v);
-    const double eq = (double)fast_exp2(fmaf(w, P.c, -d.Od));
-    const double x = ep - eq * ratio;
-    return x > 0.0 ? x : 0.0;
-}
+// Weight of token v: mode 1 = 2^(z*c - Ot) ; 3 = the same with y removed ; 2 = max(0, ep - eq * Zt/Zd).
+struct Draw {
+    int32_t mode;
+    int32_t y;
+    float Ot, Od;
+    int64_t row_t, row_d;
+    double ratio;
+};
 
 __device__ double block_sum_f64(double v)
 {
@@ -496,7 +469,6 @@ __device__ double block_sum_f64(double v)
     return tot;
 }
 
-// Exclusive prefix sum over the workgroup (thread order); also returns the total.
 __device__ double block_exclusive_f64(double v, double* total)
 {
     __shared__ double sh[kBlock / kWave];
@@ -519,144 +491,443 @@ __device__ double block_exclusive_f64(double v, double* total)
     return before + inc - v;
 }
 
-template <int DTT, int DTD>
-__global__ __launch_bounds__(kBlock) void k_sample_partial(ChainParams P)
+// Each thread owns a contiguous segment of up to kSeg entries of a chunk and
+// loads it with 16-byte vectors when the rows allow (chunks are <= 8192
+// entries, so 256 threads x 32 entries cover one).
+constexpr int kSeg = 32;
+
+template <int DT>
+__device__ __forceinline__ void load_seg(const void* row, bool aligned, int64_t a, int64_t b, float* v)
 {
-    const int s = blockIdx.x, r = blockIdx.y;
-    const Dec d = P.dec[r];
-    if (d.mode == 0) return;
-    const int64_t lo = (int64_t)s * P.chunk;
-    const int64_t hi = (lo + P.chunk < P.vocab) ? lo + P.chunk : P.vocab;
-    const double ratio = d.Zt / d.Zd;
-    double acc = 0.0;
-    for (int64_t v = lo + threadIdx.x; v < hi; v += kBlock) acc += draw_weight<DTT, DTD>(P, d, d.mode, ratio, v);
-    const double tot = block_sum_f64(acc);
-    if (threadIdx.x == 0) P.sums[(int64_t)r * P.splits + s] = tot;
+    if (aligned && b - a == kSeg) {
+        constexpr int VEC = vec_of<DT>();
+#pragma unroll
+        for (int u = 0; u < kSeg / VEC; ++u) loadv<DT, VEC>(row, a + u * VEC, v + u * VEC);
+    } else {
+#pragma unroll
+        for (int u = 0; u < kSeg; ++u) v[u] = (a + u < b) ? load1<DT>(row, a + u) : -INFINITY;
+    }
 }
 
-// Search [lo, hi) for the first token whose running weight exceeds t, tile by
-// tile in index order.  Returns -1 when rounding left t past the range.
+// Weights of the segment [a, b) of the draw's row(s), written to w.
 template <int DTT, int DTD>
-__device__ int64_t search_range(const ChainParams& P, const Dec& d, int mode, double ratio, int64_t lo, int64_t hi,
-                                double t, int64_t* last_pos)
+__device__ __forceinline__ void seg_weights(const ChainParams& P, const Draw& d, int64_t a, int64_t b, double* w)
 {
-    // Tile by tile in index order: each thread holds E consecutive weights, a
-    // workgroup exclusive scan gives its running start; the lowest position
-    // whose running sum passes t wins (atomicMin keeps the choice unique when
-    // rounding lets two neighbours both claim it).
-    __shared__ unsigned long long sh_found;
-    __shared__ double sh_base;
-    __shared__ unsigned long long sh_lp;
-    if (threadIdx.x == 0) { sh_found = ~0ull; sh_base = 0.0; sh_lp = 0ull; }
-    int64_t lp = -1;
-    __syncthreads();
-    constexpr int E = 4;
-    for (int64_t tile = lo; tile < hi; tile += (int64_t)kBlock * E) {
-        const int64_t a = tile + (int64_t)threadIdx.x * E;
-        double w[E];
-        double mine = 0.0;
+    float z[kSeg];
+    load_seg<DTT>(row_ptr<DTT>(P.logits, d.row_t, P.stride), P.t_aligned, a, b, z);
+    if (d.mode == 2) {
+        float x[kSeg];
+        load_seg<DTD>(row_ptr<DTD>(P.dlogits, d.row_d, P.dstride), P.d_aligned, a, b, x);
 #pragma unroll
-        for (int k = 0; k < E; ++k) {
-            w[k] = (a + k < hi) ? draw_weight<DTT, DTD>(P, d, mode, ratio, a + k) : 0.0;
-            mine += w[k];
-            if (w[k] > 0.0) lp = a + k;
+        for (int u = 0; u < kSeg; ++u) {
+            const double ep = (double)fast_exp2(fmaf(z[u], P.c, -d.Ot));
+            const double eq = (double)fast_exp2(fmaf(x[u], P.c, -d.Od));
+            const double v = ep - eq * d.ratio;
+            w[u] = (a + u < b && v > 0.0) ? v : 0.0;
         }
-        double total;
-        const double ex = block_exclusive_f64(mine, &total);
-        const double base = sh_base;
-        double c = base + ex;
-        if (c + mine > t) {
-            int64_t pos = -1, lastpos = -1;
-            for (int k = 0; k < E; ++k) {
-                if (w[k] > 0.0) {
-                    lastpos = a + k;
-                    if (pos < 0 && c + w[k] > t) pos = a + k;
-                }
-                c += w[k];
-            }
-            if (pos < 0) pos = lastpos;
-            if (pos >= 0) atomicMin(&sh_found, (unsigned long long)pos);
+    } else {
+#pragma unroll
+        for (int u = 0; u < kSeg; ++u) {
+            const double ep = (double)fast_exp2(fmaf(z[u], P.c, -d.Ot));
+            w[u] = (a + u < b && !(d.mode == 3 && a + u == d.y)) ? ep : 0.0;
         }
-        __syncthreads();
-        if (threadIdx.x == 0) sh_base = base + total;
-        __syncthreads();
-        if (sh_found != ~0ull) break;
     }
-    if (lp >= 0) atomicMax(&sh_lp, (unsigned long long)(lp + 1));
+}
+
+__device__ __forceinline__ void seg_of(int64_t lo, int64_t hi, int64_t* a, int64_t* b)
+{
+    int64_t x = lo + (int64_t)threadIdx.x * kSeg;
+    int64_t y = x + kSeg;
+    *a = x < hi ? x : hi;
+    *b = y < hi ? y : hi;
+}
+
+// Sum of the weights over one chunk [lo, hi) (fp64, workgroup-wide).
+template <int DTT, int DTD>
+__device__ double range_sum(const ChainParams& P, const Draw& d, int64_t lo, int64_t hi)
+{
+    int64_t a, b;
+    seg_of(lo, hi, &a, &b);
+    double acc = 0.0;
+    if (a < b) {
+        double w[kSeg];
+        seg_weights<DTT, DTD>(P, d, a, b, w);
+#pragma unroll
+        for (int u = 0; u < kSeg; ++u) acc += w[u];
+    }
+    return block_sum_f64(acc);
+}
+
+// First token of the chunk [lo, hi) whose running weight (index order)
+// exceeds t; when rounding leaves t past the chunk, its last positive-weight
+// token; -1 if the chunk has no weight.
+template <int DTT, int DTD>
+__device__ int64_t search_range(const ChainParams& P, const Draw& d, int64_t lo, int64_t hi, double t)
+{
+    __shared__ unsigned long long sh_found;
+    __shared__ long long sh_lp[kBlock / kWave];
     __syncthreads();
-    *last_pos = (int64_t)sh_lp - 1;
-    return sh_found == ~0ull ? -1 : (int64_t)sh_found;
+    if (threadIdx.x == 0) sh_found = ~0ull;
+    __syncthreads();
+    int64_t a, b;
+    seg_of(lo, hi, &a, &b);
+    double w[kSeg];
+    double mine = 0.0;
+    int64_t lp = -1;
+    if (a < b) {
+        seg_weights<DTT, DTD>(P, d, a, b, w);
+#pragma unroll
+        for (int u = 0; u < kSeg; ++u) {
+            mine += w[u];
+            if (w[u] > 0.0) lp = a + u;
+        }
+    }
+    double total;
+    double cum = block_exclusive_f64(mine, &total);
+    if (a < b && cum + mine > t) {
+        int64_t pos = -1;
+#pragma unroll
+        for (int u = 0; u < kSeg; ++u) {
+            if (w[u] > 0.0 && pos < 0 && cum + w[u] > t) pos = a + u;
+            cum += w[u];
+        }
+        if (pos < 0) pos = lp;
+        if (pos >= 0) atomicMin(&sh_found, (unsigned long long)pos);
+    }
+    __syncthreads();
+    int64_t res = sh_found != ~0ull ? (int64_t)sh_found : -1;
+    if (res < 0) {
+        // rounding left t past the chunk: its last positive-weight token
+        const long long m = wave_max((long long)lp);
+        if (threadIdx.x % kWave == 0) sh_lp[threadIdx.x / kWave] = m;
+        __syncthreads();
+        for (int w2 = 0; w2 < kBlock / kWave; ++w2) res = sh_lp[w2] > res ? sh_lp[w2] : res;
+    }
+    __syncthreads();
+    return res;
+}
+
+// Draw with chunk sums W[0..splits) (fp64, in LDS): pick the chunk holding
+// u * W, rescan it.  Returns the token, or -1 if the total is unusable.
+template <int DTT, int DTD>
+__device__ int32_t draw_from_chunks(const ChainParams& P, const Draw& d, const double* W, double u)
+{
+    __shared__ int32_t sh_chunk;
+    __shared__ double sh_t;
+    __shared__ int32_t sh_ok;
+    if (threadIdx.x < kWave) {
+        // wave 0: total, then the first chunk whose running sum passes u * total
+        const int lane = threadIdx.x;
+        double tot = 0.0;
+        for (int s0 = 0; s0 < P.splits; s0 += kWave) tot += (s0 + lane < P.splits) ? W[s0 + lane] : 0.0;
+        tot = wave_sum(tot);
+        const double t = u * tot;
+        double carry = 0.0;
+        int found = -1, lastpos = -1;
+        double before = 0.0;
+        for (int s0 = 0; s0 < P.splits && found < 0; s0 += kWave) {
+            const double x = (s0 + lane < P.splits) ? W[s0 + lane] : 0.0;
+            double inc = x;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const double y = __shfl_up(inc, o, kWave);
+                if (lane >= o) inc += y;
+            }
+            const uint64_t hit = __ballot(s0 + lane < P.splits && carry + inc > t);
+            const uint64_t pos = __ballot(s0 + lane < P.splits && x > 0.0);
+            if (pos) lastpos = s0 + 63 - (int)__builtin_clzll(pos);
+            if (hit) {
+                const int l = (int)__builtin_ctzll(hit);
+                found = s0 + l;
+                before = carry + __shfl(inc - x, l, kWave);
+            }
+            carry += __shfl(inc, kWave - 1, kWave);
+        }
+        if (lane == 0) {
+            sh_ok = tot > 0.0 && tot < INFINITY && (found >= 0 || lastpos >= 0);
+            // rounding left t past every running sum: the last positive-weight
+            // token of the last chunk with weight (t = inf finds no crossing)
+            sh_chunk = found >= 0 ? found : (lastpos >= 0 ? lastpos : 0);
+            sh_t = found >= 0 ? t - before : INFINITY;
+        }
+    }
+    __syncthreads();
+    if (!sh_ok) return -1;
+    const int64_t lo = (int64_t)sh_chunk * P.chunk;
+    const int64_t hi = (lo + P.chunk < P.vocab) ? lo + P.chunk : P.vocab;
+    return (int32_t)search_range<DTT, DTD>(P, d, lo, hi, sh_t);
+}
+
+// Draw from p of the draw's target row (fallback when a residual has no mass):
+// chunk sums recomputed over the whole row into W, then the usual draw.
+template <int DTT, int DTD>
+__device__ int32_t draw_from_p(const ChainParams& P, const Draw& d, double* W, double u)
+{
+    Draw d1 = d;
+    d1.mode = 1;
+    for (int s = 0; s < P.splits; ++s) {
+        const int64_t lo = (int64_t)s * P.chunk;
+        const int64_t hi = (lo + P.chunk < P.vocab) ? lo + P.chunk : P.vocab;
+        const double x = range_sum<DTT, DTD>(P, d1, lo, hi);
+        if (threadIdx.x == 0) W[s] = x;
+        __syncthreads();
+    }
+    return draw_from_chunks<DTT, DTD>(P, d1, W, u);
+}
+
+// Appends the emitted tokens (token `last` at position nacc) and writes the new length.
+__device__ void commit(const ChainParams& P, int r, int n, int nacc, int32_t last, uint32_t* fl)
+{
+    const int32_t len = P.ctx_len[r];
+    const bool ok = (len >= 0 && len + n <= P.ctx_cap);
+    if (ok) {
+        for (int i = threadIdx.x; i < n; i += blockDim.x) {
+            const int32_t tok = (i == nacc) ? last : P.tokens[(int64_t)r * P.ld + i];
+            P.ctx[(int64_t)r * P.ctx_stride + len + i] = tok;
+        }
+    } else if (threadIdx.x == 0) {
+        *fl |= SPEC_FLAG_CTX_OVERFLOW;
+    }
+    if (threadIdx.x == 0) P.ctx_len_out[r] = ok ? len + n : len;
+}
+
+// ---------------------------------------------------------------------------
+// decide (+ draw for bonus rows and point-mass residuals, + commit)
+// ---------------------------------------------------------------------------
+
+constexpr int kMaxPartsLds = 2048;   // partials of one request staged in LDS (32 KB)
+
+template <int DTT>
+__global__ __launch_bounds__(kBlock) void k_decide(ChainParams P)
+{
+    const int r = blockIdx.x;
+    const int t = threadIdx.x;
+    const int ld = P.ld;
+    int b = P.n_slots[r];
+    const bool badlen = (b < 0 || b > ld);
+    b = b < 0 ? 0 : (b > ld ? ld : b);
+    __shared__ Partial sp[kMaxPartsLds];
+    __shared__ float sO[2 * SPEC_MAX_DRAFT + 1];
+    __shared__ double sZ[2 * SPEC_MAX_DRAFT + 1];
+    __shared__ int32_t sArg[2 * SPEC_MAX_DRAFT + 1];
+    __shared__ int32_t sOk[2 * SPEC_MAX_DRAFT + 1];
+    __shared__ double sW[kMaxSplits];
+    __shared__ uint32_t sFlags;
+    __shared__ unsigned long long sRej;
+    if (t == 0) { sFlags = badlen ? SPEC_FLAG_BAD_LENGTH : 0u; sRej = 0; }
+    // stage this request's partials (contiguous) in LDS
+    const int nparts = P.NR * P.splits;
+    const bool staged = nparts <= kMaxPartsLds;
+    const Partial* gp = P.part + (int64_t)r * nparts;
+    // split-major in LDS (sp[s * NR + row]) so row-per-thread merges read
+    // consecutive entries
+    if (staged)
+        for (int i = t; i < nparts; i += kBlock) {
+            const int row = i / P.splits, s = i - row * P.splits;
+            sp[s * P.NR + row] = gp[i];
+        }
+    __syncthreads();
+    const Partial* rp = staged ? sp : gp;
+    const int rs = staged ? P.NR : 1;               // stride between a row's splits
+    const int rr = staged ? 1 : P.splits;           // stride between rows
+    // rows: target 0..b, draft ld+1 .. ld+b (probabilistic slots, T > 0)
+    if (t < P.NR) {
+        bool is_row = t <= b;
+        if (!is_row && !P.greedy && P.dlogits && t >= ld + 1 && t <= ld + b) {
+            const int i = t - ld - 1;
+            is_row = !(P.slot_flags && (P.slot_flags[(int64_t)r * ld + i] & SPEC_SLOT_POINT_MASS));
+        }
+        sOk[t] = 0;
+        if (is_row) {
+            if (P.greedy) {
+                int32_t idx;
+                sOk[t] = merge_argmax(rp + t * rr, P.splits, rs, &idx);
+                sArg[t] = idx;
+            } else {
+                float O; double Z;
+                sOk[t] = merge_softmax(rp + t * rr, P.splits, rs, P.c, &O, &Z);
+                sO[t] = O;
+                sZ[t] = Z;
+            }
+        }
+    }
+    __syncthreads();
+    // slot i = t < b: p(y), q(y), accept
+    if (t < b) {
+        bool acc = true;
+        uint32_t fl = 0;
+        const int64_t off = (int64_t)r * ld + t;
+        const int32_t y = P.tokens[off];
+        const bool pm = !P.slot_flags || (P.slot_flags[off] & SPEC_SLOT_POINT_MASS);
+        const bool bad = (y < 0 || y >= P.vocab);
+        if (bad) fl |= SPEC_FLAG_BAD_TOKEN;
+        if (!sOk[t]) fl |= SPEC_FLAG_BAD_LOGITS;
+        double p = 0.0, q = 1.0;
+        if (P.greedy) {
+            p = (!bad && sOk[t] && sArg[t] == y) ? 1.0 : 0.0;
+            acc = (p == 1.0);
+        } else {
+            if (!bad && sOk[t]) {
+                const float z = logit_at(P.logits, DTT, P.row_base[r] + t, P.stride, y);
+                p = (double)fast_exp2(fmaf(z, P.c, -sO[t])) / sZ[t];
+            }
+            if (!pm) {
+                const int dr = ld + 1 + t;
+                if (!sOk[dr]) fl |= SPEC_FLAG_BAD_LOGITS;
+                q = 0.0;
+                if (!bad && sOk[dr] && P.dlogits) {
+                    const float w = logit_at(P.dlogits, P.ddt, P.drow_base[r] + t, P.dstride, y);
+                    q = (double)fast_exp2(fmaf(w, P.c, -sO[dr])) / sZ[dr];
+                }
+            }
+            const double rho = q > 0.0 ? p / q : 0.0;
+            acc = (double)P.u_acc[off] < rho;
+        }
+        if (P.out_p) P.out_p[off] = (float)p;
+        if (P.out_q) P.out_q[off] = (float)q;
+        if (!acc) atomicOr(&sRej, 1ull << t);
+        if (fl) atomicOr(&sFlags, fl);
+    } else if (t < ld) {
+        const int64_t off = (int64_t)r * ld + t;
+        if (P.out_p) P.out_p[off] = 0.0f;
+        if (P.out_q) P.out_q[off] = 0.0f;
+    }
+    __syncthreads();
+    const uint64_t rej = sRej;
+    const int nacc = rej ? (int)__builtin_ctzll(rej) : b;
+    for (int i = t; i <= ld; i += kBlock)
+        P.out_tokens[(int64_t)r * (ld + 1) + i] = (i < nacc) ? P.tokens[(int64_t)r * ld + i] : -1;
+    if (t == 0) {
+        P.out_num[r] = nacc + 1;
+        P.out_acc[r] = nacc;
+        if (nacc == b && !sOk[b]) sFlags |= SPEC_FLAG_BAD_LOGITS;
+    }
+    // what to draw
+    Draw d;
+    d.mode = 0; d.y = -1; d.Ot = d.Od = 0.0f; d.row_t = P.row_base[r] + nacc; d.row_d = -1; d.ratio = 1.0;
+    int32_t last = -1;
+    bool deferred = false;
+    if (P.greedy) {
+        last = sOk[nacc] ? sArg[nacc] : -1;
+        if (last == 0x7FFFFFFF) last = -1;
+    } else if (sOk[nacc] && d.row_t >= 0 && d.row_t < P.n_rows) {
+        d.Ot = sO[nacc];
+        if (nacc == b) {
+            d.mode = 1;
+        } else {
+            const int64_t off = (int64_t)r * ld + nacc;
+            const int32_t y = P.tokens[off];
+            const bool pm = !P.slot_flags || (P.slot_flags[off] & SPEC_SLOT_POINT_MASS);
+            const bool bad = (y < 0 || y >= P.vocab);
+            const int dr = ld + 1 + nacc;
+            if (bad) d.mode = 1;
+            else if (pm) { d.mode = 3; d.y = y; }
+            else if (sOk[dr] && P.dlogits) {
+                d.mode = 2; d.y = y; d.row_d = P.drow_base[r] + nacc; d.Od = sO[dr]; d.ratio = sZ[nacc] / sZ[dr];
+            } else d.mode = 1;   // unusable draft row (flagged): fall back to p
+        }
+    }
+    if (d.mode == 2) {
+        deferred = true;
+        if (t == 0) {
+            Dec dd;
+            dd.mode = 2; dd.nacc = nacc; dd.y = d.y; dd.Ot = d.Ot; dd.Od = d.Od; dd.pad = 0;
+            dd.row_t = d.row_t; dd.row_d = d.row_d; dd.Zt = sZ[nacc]; dd.Zd = sZ[ld + 1 + nacc];
+            P.dec[r] = dd;
+        }
+    } else {
+        if (t == 0 && P.dec) P.dec[r].mode = 0;
+        if (d.mode == 1 || d.mode == 3) {
+            // chunk sums of the row from its partials; the y chunk is rescanned without y
+            const Partial* row = rp + nacc * rr;
+            for (int s = t; s < P.splits; s += kBlock) {
+                const Partial q = row[s * rs];
+                sW[s] = (q.m == -INFINITY) ? 0.0 : q.s * (double)fast_exp2((float)((double)(q.m * P.c) - (double)d.Ot));
+            }
+            __syncthreads();
+            if (d.mode == 3) {
+                const int sy = (int)(d.y / P.chunk);
+                const int64_t lo = (int64_t)sy * P.chunk;
+                const int64_t hi = (lo + P.chunk < P.vocab) ? lo + P.chunk : P.vocab;
+                const double wy = range_sum<DTT, DTT>(P, d, lo, hi);
+                if (t == 0) sW[sy] = wy;
+            }
+            __syncthreads();
+            last = draw_from_chunks<DTT, DTT>(P, d, sW, (double)P.u_smp[r]);
+            if (last < 0) {
+                // the residual had no mass (not reachable in exact arithmetic): draw from p
+                if (t == 0) sFlags |= SPEC_FLAG_RESIDUAL_ZERO;
+                last = draw_from_p<DTT, DTT>(P, d, sW, (double)P.u_smp[r]);
+            }
+        } else if (!P.greedy) {
+            if (t == 0) sFlags |= SPEC_FLAG_BAD_LOGITS;
+        }
+        if (t == 0) P.out_tokens[(int64_t)r * (ld + 1) + nacc] = last;
+    }
+    __syncthreads();
+    uint32_t fl = sFlags;
+    if (!deferred && P.ctx) {
+        __shared__ uint32_t sCommit;
+        if (t == 0) sCommit = 0;
+        __syncthreads();
+        commit(P, r, nacc + 1, nacc, last, &sCommit);
+        __syncthreads();
+        fl |= sCommit;
+    }
+    if (t == 0 && fl) atomicOr(&P.out_flags[r], fl);
+}
+
+// ---------------------------------------------------------------------------
+// second pass for probabilistic residuals max(0, p - q)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ Draw draw_of(const Dec& dd)
+{
+    Draw d;
+    d.mode = dd.mode; d.y = dd.y; d.Ot = dd.Ot; d.Od = dd.Od; d.row_t = dd.row_t; d.row_d = dd.row_d;
+    d.ratio = dd.Zt / dd.Zd;
+    return d;
+}
+
+template <int DTT, int DTD>
+__global__ __launch_bounds__(kBlock) void k_sample_part(ChainParams P)
+{
+    const int s = blockIdx.x, r = blockIdx.y;
+    const Dec dd = P.dec[r];
+    if (dd.mode != 2) return;
+    const Draw d = draw_of(dd);
+    const int64_t lo = (int64_t)s * P.chunk;
+    const int64_t hi = (lo + P.chunk < P.vocab) ? lo + P.chunk : P.vocab;
+    const double tot = range_sum<DTT, DTD>(P, d, lo, hi);
+    if (threadIdx.x == 0) P.sums[(int64_t)r * P.splits + s] = tot;
 }
 
 template <int DTT, int DTD>
 __global__ __launch_bounds__(kBlock) void k_sample_final(ChainParams P)
 {
     const int r = blockIdx.x;
-    const Dec d = P.dec[r];
-    const int ld = P.ld;
-    __shared__ int32_t sh_tok;
-    __shared__ uint32_t sh_fl;
-    if (threadIdx.x == 0) { sh_tok = -1; sh_fl = 0; }
+    const Dec dd = P.dec[r];
+    if (dd.mode != 2) return;
+    const Draw d = draw_of(dd);
+    __shared__ double sW[kMaxSplits];
+    for (int s = threadIdx.x; s < P.splits; s += kBlock) sW[s] = P.sums[(int64_t)r * P.splits + s];
     __syncthreads();
-    if (d.mode != 0) {
-        // locate the chunk
-        __shared__ int32_t sh_chunk;
-        __shared__ double sh_t, sh_W;
-        if (threadIdx.x == 0) {
-            double W = 0.0;
-            for (int s = 0; s < P.splits; ++s) W += P.sums[(int64_t)r * P.splits + s];
-            sh_W = W;
-            const double t = (double)P.u_smp[r] * W;
-            double cum = 0.0;
-            int sc = P.splits - 1;
-            for (int s = 0; s < P.splits; ++s) {
-                const double x = P.sums[(int64_t)r * P.splits + s];
-                if (cum + x > t) { sc = s; break; }
-                cum += x;
-            }
-            sh_chunk = sc;
-            sh_t = t - cum;
-        }
-        __syncthreads();
-        const double ratio = d.Zt / d.Zd;
-        int64_t lastp = -1, found = -1;
-        if (sh_W > 0.0 && sh_W < INFINITY) {
-            const int64_t lo = (int64_t)sh_chunk * P.chunk;
-            const int64_t hi = (lo + P.chunk < P.vocab) ? lo + P.chunk : P.vocab;
-            found = search_range<DTT, DTD>(P, d, d.mode, ratio, lo, hi, sh_t, &lastp);
-        } else {
-            // the residual had no mass (not reachable in exact arithmetic): draw from p
-            if (threadIdx.x == 0) sh_fl |= SPEC_FLAG_RESIDUAL_ZERO;
-            double acc = 0.0;
-            for (int64_t v = threadIdx.x; v < P.vocab; v += kBlock) acc += draw_weight<DTT, DTD>(P, d, 1, ratio, v);
-            const double W1 = block_sum_f64(acc);
-            found = search_range<DTT, DTD>(P, d, 1, ratio, 0, P.vocab, (double)P.u_smp[r] * W1, &lastp);
-        }
-        if (threadIdx.x == 0) sh_tok = (int32_t)(found >= 0 ? found : lastp);
-        __syncthreads();
-        if (threadIdx.x == 0) P.out_tokens[(int64_t)r * (ld + 1) + d.nacc] = sh_tok;
+    uint32_t fl = 0;
+    int32_t last = draw_from_chunks<DTT, DTD>(P, d, sW, (double)P.u_smp[r]);
+    if (last < 0) {
+        fl |= SPEC_FLAG_RESIDUAL_ZERO;
+        last = draw_from_p<DTT, DTD>(P, d, sW, (double)P.u_smp[r]);
     }
-    // commit
+    if (threadIdx.x == 0) P.out_tokens[(int64_t)r * (P.ld + 1) + dd.nacc] = last;
     if (P.ctx) {
-        __shared__ int32_t sh_len, sh_n, sh_ok;
-        if (threadIdx.x == 0) {
-            sh_len = P.ctx_len[r];
-            sh_n = P.out_num[r];
-            sh_ok = (sh_len >= 0 && sh_len + sh_n <= P.ctx_cap);
-            if (!sh_ok) sh_fl |= SPEC_FLAG_CTX_OVERFLOW;
-        }
+        __shared__ uint32_t sCommit;
+        if (threadIdx.x == 0) sCommit = 0;
         __syncthreads();
-        if (sh_ok) {
-            for (int i = threadIdx.x; i < sh_n; i += kBlock) {
-                int32_t tok = (d.mode != 0 && i == d.nacc) ? sh_tok : P.out_tokens[(int64_t)r * (ld + 1) + i];
-                P.ctx[(int64_t)r * P.ctx_stride + sh_len + i] = tok;
-            }
-            __syncthreads();
-            if (threadIdx.x == 0) P.ctx_len[r] = sh_len + sh_n;
-        }
+        commit(P, r, dd.nacc + 1, dd.nacc, last, &sCommit);
+        __syncthreads();
+        fl |= sCommit;
     }
-    __syncthreads();
-    if (threadIdx.x == 0 && sh_fl) atomicOr(&P.out_flags[r], sh_fl);
+    if (threadIdx.x == 0 && fl) atomicOr(&P.out_flags[r], fl);
 }
 
 // ---------------------------------------------------------------------------
@@ -665,10 +936,9 @@ __global__ __launch_bounds__(kBlock) void k_sample_final(ChainParams P)
 
 struct TreeParams {
     int32_t bs, vocab, rows_max;
-    const int64_t* row_base; int64_t n_rows_buf;
     const int32_t* node_token; const int32_t* parent_row; const int32_t* n_rows;
     int32_t* out_tokens; int32_t* out_num; int32_t* out_path; int32_t* out_argmax; uint32_t* out_flags;
-    int32_t* ctx; int64_t ctx_stride; int32_t* ctx_len; int32_t ctx_cap;
+    int32_t* ctx; int64_t ctx_stride; const int32_t* ctx_len; int32_t* ctx_len_out; int32_t ctx_cap;
     Partial* part; int32_t splits;
 };
 
@@ -689,7 +959,7 @@ __global__ __launch_bounds__(kWave) void k_tree_walk(TreeParams P)
     __shared__ uint32_t sFl;
     if (t < n) {
         int32_t idx;
-        sOk[t] = merge_argmax(P.part + ((int64_t)r * rm + t) * P.splits, P.splits, &idx);
+        sOk[t] = merge_argmax(P.part + ((int64_t)r * rm + t) * P.splits, P.splits, 1, &idx);
         sArg[t] = (idx == 0x7FFFFFFF) ? -1 : idx;
         sTok[t] = P.node_token[(int64_t)r * rm + t];
         sPar[t] = P.parent_row[(int64_t)r * rm + t];
@@ -731,7 +1001,7 @@ __global__ __launch_bounds__(kWave) void k_tree_walk(TreeParams P)
             fl |= SPEC_FLAG_CTX_OVERFLOW;
         }
         __syncthreads();
-        if (t == 0 && ok) P.ctx_len[r] = len + sNum;
+        if (t == 0) P.ctx_len_out[r] = ok ? len + sNum : len;
     }
     if (t == 0 && fl) atomicOr(&P.out_flags[r], fl);
 }
@@ -740,42 +1010,99 @@ __global__ __launch_bounds__(kWave) void k_tree_walk(TreeParams P)
 // host launchers
 // ---------------------------------------------------------------------------
 
-template <bool GREEDY>
-static void launch_stats(int dt, bool aligned, RowSet rs, int vocab, RowSplit sp, int bs, float c, Partial* part,
-                         int NR, hipStream_t st)
-{
-    dim3 grid(sp.splits, bs);
-    if (dt == SPEC_F32) {
-        if (aligned) hipLaunchKernelGGL((k_row_stats<SPEC_F32, 4, GREEDY>), grid, dim3(kBlock), 0, st, rs, vocab, sp.chunk, sp.splits, c, part, NR);
-        else hipLaunchKernelGGL((k_row_stats<SPEC_F32, 1, GREEDY>), grid, dim3(kBlock), 0, st, rs, vocab, sp.chunk, sp.splits, c, part, NR);
-    } else {
-        if (aligned) hipLaunchKernelGGL((k_row_stats<SPEC_BF16, 8, GREEDY>), grid, dim3(kBlock), 0, st, rs, vocab, sp.chunk, sp.splits, c, part, NR);
-        else hipLaunchKernelGGL((k_row_stats<SPEC_BF16, 1, GREEDY>), grid, dim3(kBlock), 0, st, rs, vocab, sp.chunk, sp.splits, c, part, NR);
-    }
-}
-
 static bool aligned16(const void* p, int64_t stride, int dt)
 {
     const int64_t es = dt == SPEC_F32 ? 4 : 2;
     return ((uintptr_t)p % 16 == 0) && ((stride * es) % 16 == 0);
 }
 
+static int stats_grid(int32_t bs, int rows_per_req_max, const RowSplit& sp)
+{
+    const int64_t max_items = (int64_t)bs * rows_per_req_max * sp.splits;
+    const int64_t cap = 256 * 8;   // about eight resident workgroups per compute unit
+    return (int)(max_items < cap ? max_items : cap);
+}
+
+// Stream plus the optional event pair that brackets the statistics kernel
+// itself (attached to its dispatch, so the pair times exactly that kernel).
+struct StatsLaunch {
+    hipStream_t st;
+    hipEvent_t e0, e1;
+};
+
+template <int DT, bool A, int DDT, bool DA, bool GREEDY, bool DRAFT, bool GPRE>
+static void launch_stats_t(const StatsParams& P, int grid, const StatsLaunch& L)
+{
+    constexpr int VEC = A ? vec_of<DT>() : 1;
+    constexpr int DVEC = DA ? vec_of<DDT>() : 1;
+    if (L.e0 || L.e1)
+        hipExtLaunchKernelGGL((k_stats<DT, VEC, DDT, DVEC, GREEDY, DRAFT, GPRE>), dim3(grid), dim3(kBlock), 0, L.st,
+                              L.e0, L.e1, 0, P);
+    else
+        hipLaunchKernelGGL((k_stats<DT, VEC, DDT, DVEC, GREEDY, DRAFT, GPRE>), dim3(grid), dim3(kBlock), 0, L.st, P);
+}
+
+template <int DT, bool A, bool GREEDY, bool GPRE>
+static void launch_stats_d(const StatsParams& P, int ddt, bool da, bool draft, int grid, const StatsLaunch& st)
+{
+    if (!draft) { launch_stats_t<DT, A, SPEC_F32, false, GREEDY, false, GPRE>(P, grid, st); return; }
+    if (ddt == SPEC_F32) {
+        if (da) launch_stats_t<DT, A, SPEC_F32, true, GREEDY, true, GPRE>(P, grid, st);
+        else launch_stats_t<DT, A, SPEC_F32, false, GREEDY, true, GPRE>(P, grid, st);
+    } else {
+        if (da) launch_stats_t<DT, A, SPEC_BF16, true, GREEDY, true, GPRE>(P, grid, st);
+        else launch_stats_t<DT, A, SPEC_BF16, false, GREEDY, true, GPRE>(P, grid, st);
+    }
+}
+
+template <bool GREEDY, bool GPRE>
+static void launch_stats_g(const StatsParams& P, int dt, bool a, int ddt, bool da, bool draft, int grid,
+                           const StatsLaunch& st)
+{
+    if (dt == SPEC_F32) {
+        if (a) launch_stats_d<SPEC_F32, true, GREEDY, GPRE>(P, ddt, da, draft, grid, st);
+        else launch_stats_d<SPEC_F32, false, GREEDY, GPRE>(P, ddt, da, draft, grid, st);
+    } else {
+        if (a) launch_stats_d<SPEC_BF16, true, GREEDY, GPRE>(P, ddt, da, draft, grid, st);
+        else launch_stats_d<SPEC_BF16, false, GREEDY, GPRE>(P, ddt, da, draft, grid, st);
+    }
+}
+
+static void launch_stats(StatsParams P, int dt, bool a, int ddt, bool da, bool draft, bool greedy, int grid,
+                         int32_t* gpre, const StatsLaunch& st)
+{
+    const bool gp = P.bs > kMaxLdsPrefix;
+    if (gp) {
+        P.gprefix = gpre;
+        hipLaunchKernelGGL(k_plan, dim3(1), dim3(kBlock), 0, st.st, P, gpre);
+    }
+    if (greedy) {
+        if (gp) launch_stats_g<true, true>(P, dt, a, ddt, da, draft, grid, st);
+        else launch_stats_g<true, false>(P, dt, a, ddt, da, draft, grid, st);
+    } else {
+        if (gp) launch_stats_g<false, true>(P, dt, a, ddt, da, draft, grid, st);
+        else launch_stats_g<false, false>(P, dt, a, ddt, da, draft, grid, st);
+    }
+}
+
 }  // namespace spec
 
 using namespace spec;
 
+// Verify workspace: partials [bs, NR, splits] | decisions [bs] | chunk sums [bs, splits] | row prefix [bs + 1]
 size_t spec_verify_chain_ws(int32_t bs, int32_t vocab, int32_t ld)
 {
     RowSplit sp = row_split(bs, vocab);
     const int NR = 2 * ld + 1;
     return align256((size_t)bs * NR * sp.splits * sizeof(Partial)) + align256((size_t)bs * sizeof(Dec)) +
-           align256((size_t)bs * sp.splits * sizeof(double));
+           align256((size_t)bs * sp.splits * sizeof(double)) + align256((size_t)(bs + 1) * sizeof(int32_t));
 }
 
 size_t spec_verify_tree_ws(int32_t bs, int32_t vocab, int32_t rows_max)
 {
     RowSplit sp = row_split(bs, vocab);
-    return align256((size_t)bs * rows_max * sp.splits * sizeof(Partial));
+    return align256((size_t)bs * rows_max * sp.splits * sizeof(Partial)) +
+           align256((size_t)(bs + 1) * sizeof(int32_t));
 }
 
 int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st)
@@ -795,44 +1122,51 @@ int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st)
     P.u_acc = a->u_accept; P.u_smp = a->u_sample;
     P.out_tokens = a->out_tokens; P.out_num = a->out_num; P.out_acc = a->out_accepted;
     P.out_p = a->out_p; P.out_q = a->out_q; P.out_flags = a->out_flags;
-    P.ctx = a->ctx; P.ctx_stride = a->ctx_stride; P.ctx_len = a->ctx_len; P.ctx_cap = a->ctx_cap;
+    P.ctx = a->ctx; P.ctx_stride = a->ctx_stride; P.ctx_len = a->ctx_len;
+    P.ctx_len_out = a->ctx_len_out ? a->ctx_len_out : a->ctx_len; P.ctx_cap = a->ctx_cap;
     P.part = (Partial*)ws;
     ws += align256((size_t)a->bs * NR * sp.splits * sizeof(Partial));
     P.dec = (Dec*)ws;
     ws += align256((size_t)a->bs * sizeof(Dec));
     P.sums = (double*)ws;
+    ws += align256((size_t)a->bs * sp.splits * sizeof(double));
+    int32_t* gpre = (int32_t*)ws;
     P.NR = NR; P.splits = sp.splits; P.chunk = sp.chunk;
+    P.t_aligned = aligned16(a->logits, a->row_stride, a->dtype);
+    P.d_aligned = P.dlogits && aligned16(a->draft_logits, a->draft_row_stride, a->draft_dtype);
 
-    RowSet tr{a->logits, a->row_stride, a->row_base, a->n_logit_rows, a->n_slots, 0, a->ld, 1, nullptr, a->ld, 0};
+    const bool draft = !P.greedy && P.dlogits && a->slot_flags;
+    StatsParams S;
+    S.logits = a->logits; S.stride = a->row_stride; S.row_base = a->row_base; S.n_rows = a->n_logit_rows;
+    S.dlogits = draft ? a->draft_logits : nullptr; S.dstride = a->draft_row_stride; S.drow_base = a->draft_row_base;
+    S.dn_rows = a->n_draft_rows;
+    S.counts = a->n_slots; S.cmin = 0; S.cmax = a->ld; S.cadd = 1;
+    S.slot_flags = a->slot_flags; S.ld = a->ld;
+    S.bs = a->bs; S.vocab = a->vocab; S.chunk = sp.chunk; S.splits = sp.splits; S.c = P.c;
+    S.part = P.part; S.NR = NR; S.draft_base = a->ld + 1; S.gprefix = nullptr;
     const bool at = aligned16(a->logits, a->row_stride, a->dtype);
-    if (a->prof_begin) hipEventRecord((hipEvent_t)a->prof_begin, st);
-    if (P.greedy) launch_stats<true>(a->dtype, at, tr, a->vocab, sp, a->bs, P.c, P.part, NR, st);
-    else launch_stats<false>(a->dtype, at, tr, a->vocab, sp, a->bs, P.c, P.part, NR, st);
-    if (!P.greedy && P.dlogits) {
-        RowSet dr{a->draft_logits, a->draft_row_stride, a->draft_row_base, a->n_draft_rows, a->n_slots, 0, a->ld, 0,
-                  a->slot_flags ? a->slot_flags : nullptr, a->ld, a->ld + 1};
-        if (a->slot_flags) {
-            const bool ad = aligned16(a->draft_logits, a->draft_row_stride, a->draft_dtype);
-            launch_stats<false>(a->draft_dtype, ad, dr, a->vocab, sp, a->bs, P.c, P.part, NR, st);
+    const bool ad = draft && aligned16(a->draft_logits, a->draft_row_stride, a->draft_dtype);
+    const int grid = stats_grid(a->bs, a->ld + 1, sp);
+    const StatsLaunch L{st, (hipEvent_t)a->prof_begin, (hipEvent_t)a->prof_end};
+    launch_stats(S, a->dtype, at, a->draft_dtype, ad, draft, P.greedy, grid, gpre, L);
+    if (a->dtype == SPEC_F32) hipLaunchKernelGGL((k_decide<SPEC_F32>), dim3(a->bs), dim3(kBlock), 0, st, P);
+    else hipLaunchKernelGGL((k_decide<SPEC_BF16>), dim3(a->bs), dim3(kBlock), 0, st, P);
+    if (draft) {
+        dim3 grid2(sp.splits, a->bs);
+        const int tt = a->dtype, dd = a->draft_dtype;
+        if (tt == SPEC_F32 && dd == SPEC_F32) {
+            hipLaunchKernelGGL((k_sample_part<SPEC_F32, SPEC_F32>), grid2, dim3(kBlock), 0, st, P);
+            hipLaunchKernelGGL((k_sample_final<SPEC_F32, SPEC_F32>), dim3(a->bs), dim3(kBlock), 0, st, P);
+        } else if (tt == SPEC_F32) {
+            hipLaunchKernelGGL((k_sample_part<SPEC_F32, SPEC_BF16>), grid2, dim3(kBlock), 0, st, P);
+            hipLaunchKernelGGL((k_sample_final<SPEC_F32, SPEC_BF16>), dim3(a->bs), dim3(kBlock), 0, st, P);
+        } else if (dd == SPEC_F32) {
+            hipLaunchKernelGGL((k_sample_part<SPEC_BF16, SPEC_F32>), grid2, dim3(kBlock), 0, st, P);
+            hipLaunchKernelGGL((k_sample_final<SPEC_BF16, SPEC_F32>), dim3(a->bs), dim3(kBlock), 0, st, P);
+        } else {
+            hipLaunchKernelGGL((k_sample_part<SPEC_BF16, SPEC_BF16>), grid2, dim3(kBlock), 0, st, P);
+            hipLaunchKernelGGL((k_sample_final<SPEC_BF16, SPEC_BF16>), dim3(a->bs), dim3(kBlock), 0, st, P);
         }
-    }
-    if (a->prof_end) hipEventRecord((hipEvent_t)a->prof_end, st);
-    hipLaunchKernelGGL(k_decide, dim3(a->bs), dim3(kDecideBlock), 0, st, P);
-    const bool need_final = !P.greedy || P.ctx;
-    if (!P.greedy) {
-        dim3 grid(sp.splits, a->bs);
-        const int tt = a->dtype, dd = P.dlogits ? a->draft_dtype : a->dtype;
-        if (tt == SPEC_F32 && dd == SPEC_F32) hipLaunchKernelGGL((k_sample_partial<SPEC_F32, SPEC_F32>), grid, dim3(kBlock), 0, st, P);
-        else if (tt == SPEC_F32) hipLaunchKernelGGL((k_sample_partial<SPEC_F32, SPEC_BF16>), grid, dim3(kBlock), 0, st, P);
-        else if (dd == SPEC_F32) hipLaunchKernelGGL((k_sample_partial<SPEC_BF16, SPEC_F32>), grid, dim3(kBlock), 0, st, P);
-        else hipLaunchKernelGGL((k_sample_partial<SPEC_BF16, SPEC_BF16>), grid, dim3(kBlock), 0, st, P);
-    }
-    if (need_final) {
-        const int tt = a->dtype, dd = P.dlogits ? a->draft_dtype : a->dtype;
-        if (tt == SPEC_F32 && dd == SPEC_F32) hipLaunchKernelGGL((k_sample_final<SPEC_F32, SPEC_F32>), dim3(a->bs), dim3(kBlock), 0, st, P);
-        else if (tt == SPEC_F32) hipLaunchKernelGGL((k_sample_final<SPEC_F32, SPEC_BF16>), dim3(a->bs), dim3(kBlock), 0, st, P);
-        else if (dd == SPEC_F32) hipLaunchKernelGGL((k_sample_final<SPEC_BF16, SPEC_F32>), dim3(a->bs), dim3(kBlock), 0, st, P);
-        else hipLaunchKernelGGL((k_sample_final<SPEC_BF16, SPEC_BF16>), dim3(a->bs), dim3(kBlock), 0, st, P);
     }
     return spec_record_hip_error(hipGetLastError());
 }
@@ -840,20 +1174,28 @@ int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st)
 int spec_verify_tree_launch(const spec_tree_verify_args* a, hipStream_t st)
 {
     RowSplit sp = row_split(a->bs, a->vocab);
+    char* ws = (char*)a->workspace;
     TreeParams P;
     P.bs = a->bs; P.vocab = a->vocab; P.rows_max = a->rows_max;
-    P.row_base = a->row_base; P.n_rows_buf = a->n_logit_rows;
     P.node_token = a->node_token; P.parent_row = a->parent_row; P.n_rows = a->n_rows;
     P.out_tokens = a->out_tokens; P.out_num = a->out_num; P.out_path = a->out_path_rows; P.out_argmax = a->out_argmax;
     P.out_flags = a->out_flags;
-    P.ctx = a->ctx; P.ctx_stride = a->ctx_stride; P.ctx_len = a->ctx_len; P.ctx_cap = a->ctx_cap;
-    P.part = (Partial*)a->workspace;
+    P.ctx = a->ctx; P.ctx_stride = a->ctx_stride; P.ctx_len = a->ctx_len;
+    P.ctx_len_out = a->ctx_len_out ? a->ctx_len_out : a->ctx_len; P.ctx_cap = a->ctx_cap;
+    P.part = (Partial*)ws;
     P.splits = sp.splits;
-    RowSet rs{a->logits, a->row_stride, a->row_base, a->n_logit_rows, a->n_rows, 1, a->rows_max, 0, nullptr, 0, 0};
-    if (a->prof_begin) hipEventRecord((hipEvent_t)a->prof_begin, st);
-    launch_stats<true>(a->dtype, aligned16(a->logits, a->row_stride, a->dtype), rs, a->vocab, sp, a->bs, 1.0f, P.part,
-                       a->rows_max, st);
-    if (a->prof_end) hipEventRecord((hipEvent_t)a->prof_end, st);
+    int32_t* gpre = (int32_t*)(ws + align256((size_t)a->bs * a->rows_max * sp.splits * sizeof(Partial)));
+    StatsParams S;
+    S.logits = a->logits; S.stride = a->row_stride; S.row_base = a->row_base; S.n_rows = a->n_logit_rows;
+    S.dlogits = nullptr; S.dstride = 0; S.drow_base = nullptr; S.dn_rows = 0;
+    S.counts = a->n_rows; S.cmin = 1; S.cmax = a->rows_max; S.cadd = 0;
+    S.slot_flags = nullptr; S.ld = 0;
+    S.bs = a->bs; S.vocab = a->vocab; S.chunk = sp.chunk; S.splits = sp.splits; S.c = 1.0f;
+    S.part = P.part; S.NR = a->rows_max; S.draft_base = 0; S.gprefix = nullptr;
+    const int grid = stats_grid(a->bs, a->rows_max, sp);
+    const StatsLaunch L{st, (hipEvent_t)a->prof_begin, (hipEvent_t)a->prof_end};
+    launch_stats(S, a->dtype, aligned16(a->logits, a->row_stride, a->dtype), SPEC_F32, false, false, true, grid,
+                 gpre, L);
     hipLaunchKernelGGL(k_tree_walk, dim3(a->bs), dim3(kWave), 0, st, P);
     return spec_record_hip_error(hipGetLastError());
 }

@@ -95,6 +95,7 @@ extern "C" {
 #define SPEC_MAX_CAP   1024   /* n-gram comparison cap (copy_cap)            */
 #define SPEC_MAX_ROWS    64   /* tree rows per request                       */
 #define SPEC_MAX_FOREST 1024  /* tree candidates per request                 */
+#define SPEC_MAX_VOCAB  8388608 /* logits per row                            */
 
 /* ========================================================================
  * spec_ngram_draft -- prompt-lookup n-gram drafter ([HS] Section 4.1 "One
@@ -282,9 +283,12 @@ typedef struct spec_verify_args {
     int32_t* ctx;                /* optional commit: device [bs, ctx_stride]      */
     int64_t ctx_stride;
     int32_t* ctx_len;            /* device [bs]                                   */
+    int32_t* ctx_len_out;        /* device [bs] or NULL: new lengths go here and
+                                    ctx_len is left as it was (NULL = in place)   */
     int32_t ctx_cap;             /* <= ctx_stride                                 */
-    void* prof_begin;            /* optional hipEvent_t pair recorded on `stream`  */
-    void* prof_end;              /* right before / after the row-statistics pass  */
+    void* prof_begin;            /* optional hipEvent_t pair (created with timing) */
+    void* prof_end;              /* attached to the row-statistics kernel's own
+                                    dispatch: begin = its start, end = its end    */
     void* workspace;
     size_t workspace_bytes;
 } spec_verify_args;
@@ -317,6 +321,7 @@ typedef struct spec_tree_verify_args {
     int32_t* ctx;
     int64_t ctx_stride;
     int32_t* ctx_len;
+    int32_t* ctx_len_out;        /* as in spec_verify_args                        */
     int32_t ctx_cap;
     void* prof_begin;            /* optional hipEvent_t pair (as in spec_verify_args) */
     void* prof_end;

@@ -66,9 +66,7 @@ def test_validation_rejects_bad_arguments_without_gpu(L):
     a.max_draft = 40
     assert lib.spec_ngram_draft(C.byref(a), None) == L.SPEC_EINVAL           # draft too long
     a.max_draft = 15
-    need = lib.spec_workspace_bytes(L.OP_NGRAM, C.byref(a))
-    assert need > 0
-    assert lib.spec_ngram_draft(C.byref(a), None) == L.SPEC_EWORKSPACE       # no workspace
+    assert lib.spec_workspace_bytes(L.OP_NGRAM, C.byref(a)) == 0             # the drafter needs no scratch
     v = L.VerifyArgs(bs=2, vocab=100, temperature=-1.0, logits=fake, row_stride=100, row_base=fake,
                      n_logit_rows=4, tokens=fake, ld=3, n_slots=fake, out_tokens=fake, out_num=fake,
                      out_accepted=fake, out_flags=fake)
@@ -80,6 +78,10 @@ def test_validation_rejects_bad_arguments_without_gpu(L):
     assert lib.spec_verify_chain(C.byref(v), None) == L.SPEC_EINVAL          # bad dtype
     v.dtype = 0
     assert lib.spec_workspace_bytes(L.OP_VERIFY_CHAIN, C.byref(v)) > 0
+    assert lib.spec_verify_chain(C.byref(v), None) == L.SPEC_EWORKSPACE      # no workspace
+    v.vocab = (1 << 23) + 1
+    v.row_stride = v.vocab
+    assert lib.spec_verify_chain(C.byref(v), None) == L.SPEC_EINVAL          # vocabulary too large
     al = L.AllocArgs(mode=5)
     assert lib.spec_allocate_budget(C.byref(al), None) == L.SPEC_EINVAL      # bad mode
     al.mode = L.ALLOC_CHAIN

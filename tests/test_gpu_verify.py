@@ -145,6 +145,15 @@ def test_commit_appends_and_overflows():
     ref_ctx, ref_len = O.commit(ctx.copy(), ctx_len.copy(), int(cap), host(g["out_tokens"]), num, fl)
     assert np.array_equal(host(tl), ref_len) and np.array_equal(host(tc), ref_ctx)
     assert np.array_equal(host(g["out_flags"]).astype(np.uint32) & O.CTX_OVERFLOW, fl & O.CTX_OVERFLOW)
+    # out of place: lengths go to a separate buffer, the inputs stay
+    tc, tl, tn = dev(ctx), dev(ctx_len), dev(np.zeros(BS, np.int32))
+    S.spec_verify_chain(dev(c["target"]).reshape(-1, V), dev(np.arange(BS) * (B + 1)), dev(c["tokens"]),
+                        dev(np.full(BS, B, np.int32)), 1.0, u_accept=dev(c["u_acc"]), u_sample=dev(c["u_smp"]),
+                        slot_flags=dev(np.zeros((BS, B), np.uint8)), draft_logits=dev(c["draft"]).reshape(-1, V),
+                        draft_row_base=dev(np.arange(BS) * B), ctx=tc, ctx_len=tl, ctx_cap=cap, ctx_len_out=tn)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(tl), ctx_len) and np.array_equal(host(tn), ref_len)
+    assert np.array_equal(host(tc), ref_ctx)
 
 
 def test_tree_verify_config3():
