@@ -8,9 +8,9 @@ size_t spec_ngram_ws(const spec_ngram_args* a);
 int spec_ngram_launch(const spec_ngram_args* a, hipStream_t st);
 size_t spec_alloc_ws(const spec_alloc_args* a);
 int spec_alloc_launch(const spec_alloc_args* a, hipStream_t st);
-size_t spec_verify_chain_ws(int32_t bs, int32_t vocab, int32_t ld);
+size_t spec_verify_chain_ws(int32_t bs, int32_t vocab, int32_t ld, int32_t dtype);
 int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st);
-size_t spec_verify_tree_ws(int32_t bs, int32_t vocab, int32_t rows_max);
+size_t spec_verify_tree_ws(int32_t bs, int32_t vocab, int32_t rows_max, int32_t dtype);
 int spec_verify_tree_launch(const spec_tree_verify_args* a, hipStream_t st);
 
 static thread_local char g_hip_error[256] = "";
@@ -153,11 +153,11 @@ size_t spec_workspace_bytes(int op, const void* args)
     }
     case SPEC_OP_VERIFY_CHAIN: {
         const spec_verify_args* a = (const spec_verify_args*)args;
-        return check_verify(a) == SPEC_OK ? spec_verify_chain_ws(a->bs, a->vocab, a->ld) : 0;
+        return check_verify(a) == SPEC_OK ? spec_verify_chain_ws(a->bs, a->vocab, a->ld, a->dtype) : 0;
     }
     case SPEC_OP_VERIFY_TREE: {
         const spec_tree_verify_args* a = (const spec_tree_verify_args*)args;
-        return check_tree_verify(a) == SPEC_OK ? spec_verify_tree_ws(a->bs, a->vocab, a->rows_max) : 0;
+        return check_tree_verify(a) == SPEC_OK ? spec_verify_tree_ws(a->bs, a->vocab, a->rows_max, a->dtype) : 0;
     }
     default: return 0;
     }
@@ -186,7 +186,7 @@ int spec_verify_chain(const spec_verify_args* a, void* stream)
 {
     int rc = check_verify(a);
     if (rc) return rc;
-    rc = check_workspace(a->workspace, a->workspace_bytes, spec_verify_chain_ws(a->bs, a->vocab, a->ld));
+    rc = check_workspace(a->workspace, a->workspace_bytes, spec_verify_chain_ws(a->bs, a->vocab, a->ld, a->dtype));
     if (rc) return rc;
     return spec_verify_chain_launch(a, (hipStream_t)stream);
 }
@@ -195,7 +195,7 @@ int spec_verify_tree(const spec_tree_verify_args* a, void* stream)
 {
     int rc = check_tree_verify(a);
     if (rc) return rc;
-    rc = check_workspace(a->workspace, a->workspace_bytes, spec_verify_tree_ws(a->bs, a->vocab, a->rows_max));
+    rc = check_workspace(a->workspace, a->workspace_bytes, spec_verify_tree_ws(a->bs, a->vocab, a->rows_max, a->dtype));
     if (rc) return rc;
     return spec_verify_tree_launch(a, (hipStream_t)stream);
 }

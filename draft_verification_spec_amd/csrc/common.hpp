@@ -16,19 +16,23 @@ constexpr float kLog2e = 1.4426950408889634f;
 // launch geometry shared by host launchers and workspace sizing
 // ---------------------------------------------------------------------------
 
-// Logit rows are cut into chunks of 8192 elements (16 KB of bf16, 32 KB of
-// fp32; a multiple of 64 elements keeps 16-byte alignment), fewer for short
-// rows so that a row still spans about four chunks.
+// Logit rows are cut into chunks of 16 KB (8192 bf16 or 4096 fp32 entries: a
+// workgroup of 256 threads reads one with four 16-byte loads per thread),
+// fewer entries for short rows so that a row still spans about four chunks
+// (a multiple of 64 entries keeps 16-byte alignment).
 struct RowSplit {
     int64_t chunk;   // elements per chunk
     int32_t splits;  // chunks per row
 };
 
-inline RowSplit row_split(int32_t /*bs*/, int32_t vocab)
+constexpr int kChunkBytes = 16384;
+
+inline RowSplit row_split(int32_t vocab, int elem_bytes)
 {
+    const int64_t full = kChunkBytes / elem_bytes;
     int64_t chunk = (vocab + 3) / 4;
     chunk = (chunk + 63) / 64 * 64;
-    if (chunk > 8192) chunk = 8192;
+    if (chunk > full) chunk = full;
     if (chunk < 64) chunk = 64;
     RowSplit s;
     s.chunk = chunk;
@@ -36,7 +40,7 @@ inline RowSplit row_split(int32_t /*bs*/, int32_t vocab)
     return s;
 }
 
-constexpr int32_t kMaxSplits = 1024;             // rows up to 8,388,608 entries
+constexpr int32_t kMaxSplits = 2048;             // rows up to 8,388,608 entries
 
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 

@@ -25,6 +25,10 @@
 //                  rescan; then commits.
 //   k_sample_part, k_sample_final: only for probabilistic residuals
 //                  max(0, p - q), whose chunk sums need both rows.
+#include <mutex>
+#include <utility>
+#include <vector>
+
 #include "common.hpp"
 
 namespace spec {
@@ -160,43 +164,134 @@ __device__ __forceinline__ void am_combine(ArgAcc& a, const ArgAcc& b)
     a.bad |= b.bad;
 }
 
+template <int DT>
+__device__ __forceinline__ void unpack(const uint4& x, float* v)
+{
+    if constexpr (DT == SPEC_F32) {
+        v[0] = __uint_as_float(x.x); v[1] = __uint_as_float(x.y); v[2] = __uint_as_float(x.z); v[3] = __uint_as_float(x.w);
+    } else {
+        v[0] = __uint_as_float(x.x << 16); v[1] = __uint_as_float(x.x & 0xFFFF0000u);
+        v[2] = __uint_as_float(x.y << 16); v[3] = __uint_as_float(x.y & 0xFFFF0000u);
+        v[4] = __uint_as_float(x.z << 16); v[5] = __uint_as_float(x.z & 0xFFFF0000u);
+        v[6] = __uint_as_float(x.w << 16); v[7] = __uint_as_float(x.w & 0xFFFF0000u);
+    }
+}
+
+// Fold kTile raw 16-byte vectors into (m, s); the sum is the pairwise tree of
+// sm_update over the kTile * VEC values, unpacked one vector at a time so the
+// values never all sit in registers.
+template <int DT>
+__device__ __forceinline__ void sm_update_raw(const uint4* raw, float c, float& m, double& s)
+{
+    constexpr int VEC = vec_of<DT>();
+    float tm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kTile; ++u) {
+        float v[VEC];
+        unpack<DT>(raw[u], v);
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) tm = fmaxf(tm, v[q]);
+    }
+    if (tm > m) {
+        if (m != -INFINITY) s *= (double)fast_exp2((float)((double)(m * c) - (double)(tm * c)));
+        m = tm;
+    }
+    if (m != -INFINITY) {
+        const float o = m * c;
+        float vs[kTile];
+#pragma unroll
+        for (int u = 0; u < kTile; ++u) {
+            float v[VEC];
+            unpack<DT>(raw[u], v);
+#pragma unroll
+            for (int q = 0; q < VEC; ++q) v[q] = fast_exp2(fmaf(v[q], c, -o));
+            vs[u] = pairwise_sum<VEC>(v);
+        }
+        s += (double)pairwise_sum<kTile>(vs);
+    } else if (tm != tm) {
+        s = __builtin_nan("");
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void am_update_raw(const uint4* raw, int64_t e, ArgAcc& a)
+{
+    constexpr int VEC = vec_of<DT>();
+    constexpr int64_t STEP = (int64_t)kBlock * VEC;
+#pragma unroll
+    for (int u = 0; u < kTile; ++u) {
+        float v[VEC];
+        unpack<DT>(raw[u], v);
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) am_update(v[q], (int32_t)(e + u * STEP + q), a);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void load_raw(const void* row, int64_t e, uint4* raw)
+{
+    constexpr int VEC = vec_of<DT>();
+    constexpr int64_t STEP = (int64_t)kBlock * VEC;
+    const char* b = (const char*)row + e * (DT == SPEC_F32 ? 4 : 2);
+#pragma unroll
+    for (int u = 0; u < kTile; ++u) raw[u] = *(const uint4*)(b + u * STEP * (DT == SPEC_F32 ? 4 : 2));
+}
+
+// Thread t of a 256-thread group folds its share of [lo, hi) (the whole
+// workgroup when the group is the workgroup).
 template <int DT, int VEC>
-__device__ __forceinline__ void chunk_softmax(const void* row, int64_t lo, int64_t hi, float c, float& m, double& s)
+__device__ __forceinline__ void chunk_softmax(const void* row, int64_t lo, int64_t hi, float c, float& m, double& s,
+                                              int t = (int)threadIdx.x)
 {
     const int64_t hv = lo + (hi - lo) / VEC * VEC;
     constexpr int64_t STEP = (int64_t)kBlock * VEC;
-    int64_t e = lo + (int64_t)threadIdx.x * VEC;
-    for (; e + (kTile - 1) * STEP < hv; e += kTile * STEP) {
-        float v[kTile * VEC];
+    int64_t e = lo + (int64_t)t * VEC;
+    if constexpr (VEC > 1) {
+        for (; e + (kTile - 1) * STEP < hv; e += kTile * STEP) {
+            uint4 raw[kTile];
+            load_raw<DT>(row, e, raw);
+            sm_update_raw<DT>(raw, c, m, s);
+        }
+    } else {
+        for (; e + (kTile - 1) * STEP < hv; e += kTile * STEP) {
+            float v[kTile];
 #pragma unroll
-        for (int u = 0; u < kTile; ++u) loadv<DT, VEC>(row, e + u * STEP, v + u * VEC);
-        sm_update<kTile * VEC>(v, c, m, s);
+            for (int u = 0; u < kTile; ++u) v[u] = load1<DT>(row, e + u * STEP);
+            sm_update<kTile>(v, c, m, s);
+        }
     }
     for (; e < hv; e += STEP) {
         float v[VEC];
         loadv<DT, VEC>(row, e, v);
         sm_update<VEC>(v, c, m, s);
     }
-    for (int64_t t = hv + threadIdx.x; t < hi; t += kBlock) {
-        float v = load1<DT>(row, t);
+    for (int64_t x = hv + t; x < hi; x += kBlock) {
+        float v = load1<DT>(row, x);
         sm_update<1>(&v, c, m, s);
     }
 }
 
 template <int DT, int VEC>
-__device__ __forceinline__ void chunk_argmax(const void* row, int64_t lo, int64_t hi, ArgAcc& a)
+__device__ __forceinline__ void chunk_argmax(const void* row, int64_t lo, int64_t hi, ArgAcc& a,
+                                             int t = (int)threadIdx.x)
 {
     const int64_t hv = lo + (hi - lo) / VEC * VEC;
     constexpr int64_t STEP = (int64_t)kBlock * VEC;
-    int64_t e = lo + (int64_t)threadIdx.x * VEC;
-    for (; e + (kTile - 1) * STEP < hv; e += kTile * STEP) {
-        float v[kTile * VEC];
+    int64_t e = lo + (int64_t)t * VEC;
+    if constexpr (VEC > 1) {
+        for (; e + (kTile - 1) * STEP < hv; e += kTile * STEP) {
+            uint4 raw[kTile];
+            load_raw<DT>(row, e, raw);
+            am_update_raw<DT>(raw, e, a);
+        }
+    } else {
+        for (; e + (kTile - 1) * STEP < hv; e += kTile * STEP) {
+            float v[kTile];
 #pragma unroll
-        for (int u = 0; u < kTile; ++u) loadv<DT, VEC>(row, e + u * STEP, v + u * VEC);
+            for (int u = 0; u < kTile; ++u) v[u] = load1<DT>(row, e + u * STEP);
 #pragma unroll
-        for (int u = 0; u < kTile; ++u)
-#pragma unroll
-            for (int k = 0; k < VEC; ++k) am_update(v[u * VEC + k], (int32_t)(e + u * STEP + k), a);
+            for (int u = 0; u < kTile; ++u) am_update(v[u], (int32_t)(e + u * STEP), a);
+        }
     }
     for (; e < hv; e += STEP) {
         float v[VEC];
@@ -204,58 +299,7 @@ __device__ __forceinline__ void chunk_argmax(const void* row, int64_t lo, int64_
 #pragma unroll
         for (int k = 0; k < VEC; ++k) am_update(v[k], (int32_t)(e + k), a);
     }
-    for (int64_t t = hv + threadIdx.x; t < hi; t += kBlock) am_update(load1<DT>(row, t), (int32_t)t, a);
-}
-
-// One chunk of one row -> one partial (workgroup-wide; every thread calls it).
-template <int DT, int VEC, bool GREEDY>
-__device__ void row_chunk(const void* rp, int64_t lo, int64_t hi, float c, Partial* out)
-{
-    __shared__ float sh_m[kBlock / kWave];
-    __shared__ double sh_s[kBlock / kWave];
-    __shared__ int32_t sh_i[kBlock / kWave];
-    const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-    if constexpr (!GREEDY) {
-        float m = -INFINITY;
-        double s = 0.0;
-        chunk_softmax<DT, VEC>(rp, lo, hi, c, m, s);
-#pragma unroll
-        for (int o = kWave / 2; o > 0; o >>= 1) {
-            const float m2 = __shfl_xor(m, o, kWave);
-            const double s2 = __shfl_xor(s, o, kWave);
-            sm_combine(m, s, m2, s2, c);
-        }
-        if (lane == 0) { sh_m[wid] = m; sh_s[wid] = s; }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            for (int w = 1; w < kBlock / kWave; ++w) sm_combine(m, s, sh_m[w], sh_s[w], c);
-            Partial p;
-            p.m = m; p.idx = 0; p.s = s;
-            *out = p;
-        }
-        __syncthreads();
-    } else {
-        ArgAcc acc{-INFINITY, 0x7FFFFFFF, 0};
-        chunk_argmax<DT, VEC>(rp, lo, hi, acc);
-#pragma unroll
-        for (int o = kWave / 2; o > 0; o >>= 1) {
-            ArgAcc b{__shfl_xor(acc.best, o, kWave), __shfl_xor(acc.idx, o, kWave), __shfl_xor(acc.bad, o, kWave)};
-            am_combine(acc, b);
-        }
-        if (lane == 0) { sh_m[wid] = acc.best; sh_i[wid] = acc.idx | (acc.bad ? (int32_t)0x80000000 : 0); }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            ArgAcc t{-INFINITY, 0x7FFFFFFF, 0};
-            for (int w = 0; w < kBlock / kWave; ++w) {
-                ArgAcc b{sh_m[w], sh_i[w] & 0x7FFFFFFF, (sh_i[w] >> 31) & 1};
-                am_combine(t, b);
-            }
-            Partial p;
-            p.m = t.best; p.idx = t.idx | (t.bad ? (int32_t)0x80000000 : 0); p.s = 0.0;
-            *out = p;
-        }
-        __syncthreads();
-    }
+    for (int64_t x = hv + t; x < hi; x += kBlock) am_update(load1<DT>(row, x), (int32_t)x, a);
 }
 
 __device__ __forceinline__ void bad_partial(Partial* out)
@@ -295,14 +339,20 @@ __device__ __forceinline__ int32_t target_rows(const StatsParams& P, int r)
     return c + P.cadd;
 }
 
-// Exclusive prefix of the per-request target rows over the workgroup; returns the total.
-__device__ int32_t row_prefix(const StatsParams& P, int32_t* pre)
+// Exclusive prefix of the per-request target rows over a workgroup of NT
+// threads; returns the total.  With `rb` the row bases are staged too, in the
+// same round trip.
+template <int NT = kBlock>
+__device__ int32_t row_prefix(const StatsParams& P, int32_t* pre, int64_t* rb = nullptr)
 {
-    __shared__ int32_t sh[kBlock / kWave];
-    const int per = (P.bs + kBlock - 1) / kBlock;
+    __shared__ int32_t sh[NT / kWave];
+    const int per = (P.bs + NT - 1) / NT;
     const int r0 = threadIdx.x * per;
     int32_t local = 0;
-    for (int r = r0; r < r0 + per && r < P.bs; ++r) local += target_rows(P, r);
+    for (int r = r0; r < r0 + per && r < P.bs; ++r) {
+        local += target_rows(P, r);
+        if (rb) rb[r] = P.row_base[r];
+    }
     const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
     int32_t inc = local;
 #pragma unroll
@@ -313,7 +363,7 @@ __device__ int32_t row_prefix(const StatsParams& P, int32_t* pre)
     if (lane == kWave - 1) sh[wid] = inc;
     __syncthreads();
     int32_t before = 0, tot = 0;
-    for (int w = 0; w < kBlock / kWave; ++w) {
+    for (int w = 0; w < NT / kWave; ++w) {
         if (w < wid) before += sh[w];
         tot += sh[w];
     }
@@ -329,64 +379,411 @@ __device__ int32_t row_prefix(const StatsParams& P, int32_t* pre)
 
 __global__ __launch_bounds__(kBlock) void k_plan(StatsParams P, int32_t* pre)
 {
-    row_prefix(P, pre);
+    row_prefix<kBlock>(P, pre);
 }
 
+// Where one work item (verified row, chunk) lives.
+struct ItemLoc {
+    int r, k, s;
+    int64_t row, drow;
+    bool draft_row;
+};
+
+// Partials of one chunk per wave, double-buffered by item parity so that one
+// barrier per item suffices.
+struct BlockRed {
+    float m[2][kBlock / kWave];
+    double s[2][kBlock / kWave];
+    int32_t i[2][kBlock / kWave];
+};
+
+// Workgroup combine of per-thread softmax state (m, s) into *out (thread 0).
+__device__ __forceinline__ void block_softmax_out(float m, double s, float c, BlockRed& R, int par, Partial* out)
+{
+    const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        const float m2 = __shfl_xor(m, o, kWave);
+        const double s2 = __shfl_xor(s, o, kWave);
+        sm_combine(m, s, m2, s2, c);
+    }
+    if (lane == 0) { R.m[par][wid] = m; R.s[par][wid] = s; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < kBlock / kWave; ++w) sm_combine(m, s, R.m[par][w], R.s[par][w], c);
+        Partial p;
+        p.m = m; p.idx = 0; p.s = s;
+        *out = p;
+    }
+}
+
+__device__ __forceinline__ void block_argmax_out(ArgAcc acc, BlockRed& R, int par, Partial* out)
+{
+    const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        ArgAcc b{__shfl_xor(acc.best, o, kWave), __shfl_xor(acc.idx, o, kWave), __shfl_xor(acc.bad, o, kWave)};
+        am_combine(acc, b);
+    }
+    if (lane == 0) { R.m[par][wid] = acc.best; R.i[par][wid] = acc.idx | (acc.bad ? (int32_t)0x80000000 : 0); }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        ArgAcc t{-INFINITY, 0x7FFFFFFF, 0};
+        for (int w = 0; w < kBlock / kWave; ++w) {
+            ArgAcc b{R.m[par][w], R.i[par][w] & 0x7FFFFFFF, (R.i[par][w] >> 31) & 1};
+            am_combine(t, b);
+        }
+        Partial p;
+        p.m = t.best; p.idx = t.idx | (t.bad ? (int32_t)0x80000000 : 0); p.s = 0.0;
+        *out = p;
+    }
+}
+
+// Any chunk, read directly by the whole (256-thread) workgroup.
+template <int DT, int VEC, bool GREEDY>
+__device__ __forceinline__ void chunk_direct(const void* rp, int64_t lo, int64_t hi, float c, BlockRed& R, int par,
+                                             Partial* out)
+{
+    if constexpr (GREEDY) {
+        ArgAcc acc{-INFINITY, 0x7FFFFFFF, 0};
+        chunk_argmax<DT, VEC>(rp, lo, hi, acc);
+        block_argmax_out(acc, R, par, out);
+    } else {
+        float m = -INFINITY;
+        double s = 0.0;
+        chunk_softmax<DT, VEC>(rp, lo, hi, c, m, s);
+        block_softmax_out(m, s, c, R, par, out);
+    }
+}
+
+constexpr int kRowBaseLds = 512;   // batches whose row bases are staged in LDS
+constexpr int kRowMapLds = 4096;   // verified rows whose request is looked up in an LDS map
+
+// The statistics pass for any layout (unaligned rows, large batches): items
+// are dealt round-robin (item = block + j * grid), so the chunks the whole
+// grid reads at one time form one contiguous span, and each is read directly.
 template <int DT, int VEC, int DDT, int DVEC, bool GREEDY, bool DRAFT, bool GPRE>
 __global__ __launch_bounds__(kBlock) void k_stats(StatsParams P)
 {
     __shared__ int32_t lpre[GPRE ? 1 : kMaxLdsPrefix + 1];
+    __shared__ int64_t lrb[GPRE ? 1 : kRowBaseLds];
+    __shared__ int32_t lmap[GPRE ? 1 : kRowMapLds];
+    __shared__ BlockRed R;
     const int32_t* pre;
     int32_t total;
+    bool rb_lds = false, map_lds = false;
     if constexpr (GPRE) {
         pre = P.gprefix;
         total = pre[P.bs];
     } else {
-        total = row_prefix(P, lpre);
+        rb_lds = P.bs <= kRowBaseLds;
+        total = row_prefix<kBlock>(P, lpre, rb_lds ? lrb : nullptr);
         pre = lpre;
+        map_lds = total <= kRowMapLds;
+        if (map_lds) {
+            // request of every verified row
+            for (int r = threadIdx.x; r < P.bs; r += blockDim.x)
+                for (int q = pre[r]; q < pre[r + 1]; ++q) lmap[q] = r;
+            __syncthreads();
+        }
     }
-    // each workgroup takes a contiguous range of items (consecutive chunks of
-    // the same rows), so the row lookup is redone only when the row changes
     const int64_t items = (int64_t)total * P.splits;
-    const int64_t per = (items + gridDim.x - 1) / gridDim.x;
-    const int64_t it0 = (int64_t)blockIdx.x * per;
-    const int64_t it1 = (it0 + per < items) ? it0 + per : items;
-    int64_t cur_rowf = -1;
-    int r = 0, k = 0;
-    int64_t row = 0, drow = 0;
-    bool draft_row = false;
-    for (int64_t it = it0; it < it1; ++it) {
-        const int64_t rowf = it / P.splits;
-        const int s = (int)(it - rowf * P.splits);
-        if (rowf != cur_rowf) {
-            cur_rowf = rowf;
-            int lo = 0, hi = P.bs;   // pre[lo] <= rowf < pre[hi]
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (pre[mid] <= rowf) lo = mid; else hi = mid;
-            }
-            r = lo;
-            k = (int)(rowf - pre[r]);
-            row = P.row_base[r] + k;
-            if constexpr (DRAFT) {
-                const int b = target_rows(P, r) - P.cadd;
-                draft_row = k < b && !(P.slot_flags[(int64_t)r * P.ld + k] & SPEC_SLOT_POINT_MASS);
-                if (draft_row) drow = P.drow_base[r] + k;
-            }
+    auto req_of = [&](int64_t rowf) -> int {
+        if (map_lds) return lmap[rowf];
+        int lo = 0, hi = P.bs;   // pre[lo] <= rowf < pre[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (pre[mid] <= rowf) lo = mid; else hi = mid;
         }
-        const int64_t clo = (int64_t)s * P.chunk;
-        const int64_t chi = (clo + P.chunk < P.vocab) ? clo + P.chunk : P.vocab;
-        Partial* out = P.part + ((int64_t)r * P.NR + k) * P.splits + s;
-        if (row < 0 || row >= P.n_rows) bad_partial(out);
-        else row_chunk<DT, VEC, GREEDY>(row_ptr<DT>(P.logits, row, P.stride), clo, chi, P.c, out);
+        return lo;
+    };
+    int par = 0;   // flips after each reduction (each has one barrier)
+    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+        const int64_t rowf = it / P.splits;
+        ItemLoc L;
+        const int r = req_of(rowf);
+        L.r = r;
+        L.k = (int)(rowf - pre[r]);
+        L.row = (rb_lds ? lrb[r] : P.row_base[r]) + L.k;
+        L.s = (int)(it - rowf * P.splits);
+        L.draft_row = false;
+        L.drow = 0;
         if constexpr (DRAFT) {
-            if (draft_row) {
-                Partial* dout = P.part + ((int64_t)r * P.NR + P.draft_base + k) * P.splits + s;
-                if (drow < 0 || drow >= P.dn_rows) bad_partial(dout);
-                else row_chunk<DDT, DVEC, false>(row_ptr<DDT>(P.dlogits, drow, P.dstride), clo, chi, P.c, dout);
+            const int b = target_rows(P, r) - P.cadd;
+            L.draft_row = L.k < b && !(P.slot_flags[(int64_t)r * P.ld + L.k] & SPEC_SLOT_POINT_MASS);
+            if (L.draft_row) L.drow = P.drow_base[r] + L.k;
+        }
+        const int64_t clo = (int64_t)L.s * P.chunk;
+        const int64_t chi = (clo + P.chunk < P.vocab) ? clo + P.chunk : P.vocab;
+        Partial* out = P.part + ((int64_t)L.r * P.NR + L.k) * P.splits + L.s;
+        if (L.row < 0 || L.row >= P.n_rows) {
+            bad_partial(out);
+        } else {
+            chunk_direct<DT, VEC, GREEDY>(row_ptr<DT>(P.logits, L.row, P.stride), clo, chi, P.c, R, par, out);
+            par ^= 1;
+        }
+        if constexpr (DRAFT) {
+            if (L.draft_row) {
+                Partial* dout = P.part + ((int64_t)L.r * P.NR + P.draft_base + L.k) * P.splits + L.s;
+                if (L.drow < 0 || L.drow >= P.dn_rows) {
+                    bad_partial(dout);
+                } else {
+                    chunk_direct<DDT, DVEC, false>(row_ptr<DDT>(P.dlogits, L.drow, P.dstride), clo, chi, P.c, R,
+                                                   par, dout);
+                    par ^= 1;
+                }
             }
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// the statistics pass, pipelined form
+// ---------------------------------------------------------------------------
+//
+// Items are dealt round-robin (item = block + j * grid), so the chunks the
+// whole grid reads at one time form one contiguous span and spread over every
+// HBM channel.  Each thread keeps the next item's four 16-byte loads in flight
+// while it reduces the current one; two register buffers alternate (the loop
+// body appears twice, so no buffer is copied).  For the compiler's wait
+// counts to let those loads stay in flight, every value the control flow
+// depends on is wave-uniform (scalar branches), every path reads every buffer
+// it loaded, and an item past the end, or of a row outside the logits, still
+// goes through the (fully masked) reduction: only the final write differs.
+
+constexpr int kGroups = 1;                 // 256-thread groups per workgroup
+constexpr int kPipeBlock = kGroups * kBlock;
+constexpr int kPipeMap = kRowMapLds;       // verified rows whose request the LDS map holds
+
+struct GroupRed {
+    float m[2][kGroups][kBlock / kWave];
+    double s[2][kGroups][kBlock / kWave];
+    int32_t i[2][kGroups][kBlock / kWave];
+};
+
+__device__ __forceinline__ Partial bad_value()
+{
+    Partial p;
+    p.m = __builtin_nanf(""); p.idx = (int32_t)0x80000000; p.s = __builtin_nan("");
+    return p;
+}
+
+// Group combine of per-thread softmax state; exactly one barrier.  Thread 0 of
+// the group writes *out (the bad-row value when `bad`) unless out is null.
+__device__ __forceinline__ void group_softmax_out(float m, double s, float c, GroupRed& R, int par, int g, int t,
+                                                  Partial* out, bool bad)
+{
+    const int lane = t % kWave, w = t / kWave;
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        const float m2 = __shfl_xor(m, o, kWave);
+        const double s2 = __shfl_xor(s, o, kWave);
+        sm_combine(m, s, m2, s2, c);
+    }
+    if (lane == 0) { R.m[par][g][w] = m; R.s[par][g][w] = s; }
+    __syncthreads();
+    if (t == 0 && out) {
+        for (int w2 = 1; w2 < kBlock / kWave; ++w2) sm_combine(m, s, R.m[par][g][w2], R.s[par][g][w2], c);
+        Partial p;
+        p.m = m; p.idx = 0; p.s = s;
+        *out = bad ? bad_value() : p;
+    }
+}
+
+__device__ __forceinline__ void group_argmax_out(ArgAcc acc, GroupRed& R, int par, int g, int t, Partial* out, bool bad)
+{
+    const int lane = t % kWave, w = t / kWave;
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        ArgAcc b{__shfl_xor(acc.best, o, kWave), __shfl_xor(acc.idx, o, kWave), __shfl_xor(acc.bad, o, kWave)};
+        am_combine(acc, b);
+    }
+    if (lane == 0) { R.m[par][g][w] = acc.best; R.i[par][g][w] = acc.idx | (acc.bad ? (int32_t)0x80000000 : 0); }
+    __syncthreads();
+    if (t == 0 && out) {
+        ArgAcc a{-INFINITY, 0x7FFFFFFF, 0};
+        for (int w2 = 0; w2 < kBlock / kWave; ++w2) {
+            ArgAcc b{R.m[par][g][w2], R.i[par][g][w2] & 0x7FFFFFFF, (R.i[par][g][w2] >> 31) & 1};
+            am_combine(a, b);
+        }
+        Partial p;
+        p.m = a.best; p.idx = a.idx | (a.bad ? (int32_t)0x80000000 : 0); p.s = 0.0;
+        *out = bad ? bad_value() : p;
+    }
+}
+
+// Loads thread t's kTile vectors of [clo, chi) of a row (vector u at
+// clo + t * VEC + u * kBlock * VEC); vectors at or past chi, and every vector
+// when !go, load the first vector of row 0 instead (always valid, unused).
+template <int DT>
+__device__ __forceinline__ void group_issue(const void* logits, int64_t stride, int64_t row, bool go, int64_t clo,
+                                            int64_t chi, int t, uint4* raw)
+{
+    constexpr int64_t VEC = vec_of<DT>();
+    constexpr int64_t STEP = (int64_t)kBlock * VEC;
+    constexpr int ES = DT == SPEC_F32 ? 4 : 2;
+    const char* rp = (const char*)row_ptr<DT>(logits, go ? row : 0, stride);
+    const int64_t hi = go ? chi : 0;
+    const int64_t e0 = clo + (int64_t)t * VEC;
+#pragma unroll
+    for (int u = 0; u < kTile; ++u) {
+        const int64_t e = e0 + u * STEP;
+        raw[u] = *(const uint4*)(rp + (e < hi ? e : 0) * ES);
+    }
+}
+
+// Group statistics of one chunk held in registers; vectors at or past hi read
+// as -inf (they add nothing to a sum and win no argmax), and every register of
+// the buffer is read on every path.
+template <int DT, bool GREEDY>
+__device__ __forceinline__ void group_chunk(const uint4* raw, int64_t lo, int64_t hi, float c, GroupRed& R, int par,
+                                            int g, int t, Partial* out, bool bad)
+{
+    constexpr int64_t VEC = vec_of<DT>();
+    constexpr int64_t STEP = (int64_t)kBlock * VEC;
+    const uint32_t ninf = DT == SPEC_F32 ? 0xFF800000u : 0xFF80FF80u;   // -inf in every lane of a vector
+    const int64_t e = lo + (int64_t)t * VEC;
+    uint4 r2[kTile];
+#pragma unroll
+    for (int u = 0; u < kTile; ++u) {
+        const bool ok = e + u * STEP < hi;
+        r2[u].x = ok ? raw[u].x : ninf; r2[u].y = ok ? raw[u].y : ninf;
+        r2[u].z = ok ? raw[u].z : ninf; r2[u].w = ok ? raw[u].w : ninf;
+    }
+    if constexpr (GREEDY) {
+        ArgAcc acc{-INFINITY, 0x7FFFFFFF, 0};
+        am_update_raw<DT>(r2, e, acc);
+        group_argmax_out(acc, R, par, g, t, out, bad);
+    } else {
+        float m = -INFINITY;
+        double s = 0.0;
+        sm_update_raw<DT>(r2, c, m, s);
+        group_softmax_out(m, s, c, R, par, g, t, out, bad);
+    }
+}
+
+// Reads every register of a load buffer without using it: the loads have
+// landed once it runs.  Used where the loop leaves with a prefetch that will
+// never be reduced, so that the compiler's wait counts at the loop latch stay
+// exact (otherwise that exit path makes every iteration wait for all loads).
+__device__ __forceinline__ void drain(const uint4* raw)
+{
+#pragma unroll
+    for (int u = 0; u < kTile; ++u) asm volatile("" : : "v"(raw[u].x), "v"(raw[u].y), "v"(raw[u].z), "v"(raw[u].w));
+}
+
+__device__ __forceinline__ int64_t uniform64(int64_t v)
+{
+    return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(v >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)v));
+}
+
+struct PipeLoc {
+    int r, k, s;
+    int64_t row, drow;
+    bool valid;      // a real item
+    bool row_ok;     // its target row lies in the logits
+    bool draft_row;  // it has a probabilistic draft row
+    bool drow_ok;
+};
+
+// Requires 16-byte aligned target rows, a vocabulary that is a multiple of one
+// vector, bs <= kRowBaseLds and at most kPipeMap verified rows.  The
+// workgroup is kGroups groups of 256 threads; each iteration the groups take
+// kGroups consecutive items.
+template <int DT, int DDT, int DVEC, bool GREEDY, bool DRAFT>
+__global__ __launch_bounds__(kPipeBlock) void k_stats_pipe(StatsParams P)
+{
+    __shared__ int32_t lpre[kRowBaseLds + 1];
+    __shared__ int64_t lrb[kRowBaseLds];
+    __shared__ int32_t lmap[kPipeMap];
+    __shared__ GroupRed R;
+    // wave-uniform, so that the loop control below is scalar
+    const int32_t total = __builtin_amdgcn_readfirstlane(row_prefix<kPipeBlock>(P, lpre, lrb));
+    for (int r = threadIdx.x; r < P.bs; r += kPipeBlock)
+        for (int q = lpre[r]; q < lpre[r + 1] && q < kPipeMap; ++q) lmap[q] = r;
+    __syncthreads();
+    // at most kPipeMap rows of at most kMaxSplits chunks: 32-bit counts, so
+    // that the loop control compiles to scalar compares
+    const int32_t items = (total <= kPipeMap) ? total * P.splits : 0;   // host guarantees the bound
+    const int32_t nsup = (items + kGroups - 1) / kGroups;
+    const int32_t G = gridDim.x;
+    int32_t S = blockIdx.x;
+    if (S >= nsup) return;   // the whole workgroup
+    const int g = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kBlock)), t = threadIdx.x % kBlock;   // g is wave-uniform
+    auto locate = [&](int32_t item) -> PipeLoc {
+        PipeLoc L;
+        L.valid = item < items;
+        const int32_t it = L.valid ? item : 0;
+        const int32_t rowf = it / P.splits;
+        const int r = __builtin_amdgcn_readfirstlane(lmap[rowf]);
+        L.r = r;
+        L.k = (int)(rowf - __builtin_amdgcn_readfirstlane(lpre[r]));
+        L.s = (int)(it - rowf * P.splits);
+        L.row = uniform64(lrb[r]) + L.k;
+        L.row_ok = L.row >= 0 && L.row < P.n_rows;
+        L.draft_row = false;
+        L.drow = 0;
+        L.drow_ok = false;
+        if constexpr (DRAFT) {
+            const int b = target_rows(P, r) - P.cadd;
+            L.draft_row = L.valid && L.k < b && !(P.slot_flags[(int64_t)r * P.ld + L.k] & SPEC_SLOT_POINT_MASS);
+            if (L.draft_row) L.drow = P.drow_base[r] + L.k;
+            L.drow_ok = L.drow >= 0 && L.drow < P.dn_rows;
+        }
+        return L;
+    };
+    auto issue = [&](const PipeLoc& L, uint4* raw) {
+        const int64_t clo = (int64_t)L.s * P.chunk;
+        const int64_t chi = (clo + P.chunk < P.vocab) ? clo + P.chunk : P.vocab;
+        group_issue<DT>(P.logits, P.stride, L.row, L.valid && L.row_ok, clo, chi, t, raw);
+    };
+    int par = 0;
+    auto reduce = [&](const PipeLoc& L, const uint4* raw) {
+        const int64_t clo = (int64_t)L.s * P.chunk;
+        const int64_t chi = (clo + P.chunk < P.vocab) ? clo + P.chunk : P.vocab;
+        Partial* out = L.valid ? P.part + ((int64_t)L.r * P.NR + L.k) * P.splits + L.s : nullptr;
+        group_chunk<DT, GREEDY>(raw, clo, (L.valid && L.row_ok) ? chi : clo, P.c, R, par, g, t, out, !L.row_ok);
+        par ^= 1;
+        if constexpr (DRAFT) {
+            // every group takes this barrier too, with an empty range when it has no draft row
+            const bool go = L.draft_row && L.drow_ok;
+            Partial* dout = L.draft_row ? P.part + ((int64_t)L.r * P.NR + P.draft_base + L.k) * P.splits + L.s : nullptr;
+            float m = -INFINITY;
+            double s = 0.0;
+            chunk_softmax<DDT, DVEC>(row_ptr<DDT>(P.dlogits, go ? L.drow : 0, P.dstride), clo, go ? chi : clo, P.c,
+                                     m, s, t);
+            group_softmax_out(m, s, P.c, R, par, g, t, dout, !L.drow_ok);
+            par ^= 1;
+        }
+    };
+    // One exit, at the latch, and both paths into it have read `rb`: the
+    // compiler's wait counts at the loop header then cover only the loads of
+    // the item about to be reduced.
+    uint4 ra[kTile], rb[kTile];
+    PipeLoc la = locate(S * kGroups + g), lb = la;
+    issue(la, ra);
+    bool more;
+    do {
+        const int32_t S1 = S + G;
+        const bool m1 = S1 < nsup;   // uniform over the workgroup
+        lb = locate(m1 ? S1 * kGroups + g : items);
+        issue(lb, rb);
+        reduce(la, ra);
+        bool m2 = false;
+        if (m1) {
+            const int32_t S2 = S1 + G;
+            m2 = S2 < nsup;
+            la = locate(m2 ? S2 * kGroups + g : items);
+            issue(la, ra);
+            reduce(lb, rb);
+            S = S2;
+        } else {
+            drain(rb);
+        }
+        more = m1 && m2;
+    } while (more);
+    drain(ra);
 }
 
 // ---------------------------------------------------------------------------
@@ -1016,11 +1413,48 @@ static bool aligned16(const void* p, int64_t stride, int dt)
     return ((uintptr_t)p % 16 == 0) && ((stride * es) % 16 == 0);
 }
 
-static int stats_grid(int32_t bs, int rows_per_req_max, const RowSplit& sp)
+// Upper bound of the statistics items (the exact count is on the device).
+static int64_t stats_items(int32_t bs, int rows_per_req_max, const RowSplit& sp)
 {
-    const int64_t max_items = (int64_t)bs * rows_per_req_max * sp.splits;
-    const int64_t cap = 256 * 8;   // about eight resident workgroups per compute unit
-    return (int)(max_items < cap ? max_items : cap);
+    return (int64_t)bs * rows_per_req_max * sp.splits;
+}
+
+// Compute units of the current device (cached per device).
+static int device_cus()
+{
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+// Workgroups of `block` threads that one compute unit holds at once (cached
+// per kernel).
+static int blocks_per_cu(const void* kernel, int block)
+{
+    static std::mutex mu;
+    static std::vector<std::pair<const void*, int>> cache;
+    std::lock_guard<std::mutex> lock(mu);
+    for (const auto& e : cache)
+        if (e.first == kernel) return e.second;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, block, 0) != hipSuccess || n <= 0) n = 1;
+    cache.emplace_back(kernel, n);
+    return n;
+}
+
+// One resident wave of workgroups (a second round would only add a tail),
+// at most one per unit of work.
+static int resident_grid(const void* kernel, int block, int64_t work)
+{
+    const int64_t cap = (int64_t)blocks_per_cu(kernel, block) * device_cus();
+    const int64_t g = work < cap ? work : cap;
+    return (int)(g > 0 ? g : 1);
 }
 
 // Stream plus the optional event pair that brackets the statistics kernel
@@ -1030,58 +1464,100 @@ struct StatsLaunch {
     hipEvent_t e0, e1;
 };
 
+template <typename K>
+static void launch_timed(K kern, int grid, int block, const StatsParams& P, const StatsLaunch& L)
+{
+    if (L.e0 || L.e1)
+        hipExtLaunchKernelGGL(kern, dim3(grid), dim3(block), 0, L.st, L.e0, L.e1, 0, P);
+    else
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(block), 0, L.st, P);
+}
+
 template <int DT, bool A, int DDT, bool DA, bool GREEDY, bool DRAFT, bool GPRE>
-static void launch_stats_t(const StatsParams& P, int grid, const StatsLaunch& L)
+static void launch_stats_t(const StatsParams& P, int64_t items, const StatsLaunch& L)
 {
     constexpr int VEC = A ? vec_of<DT>() : 1;
     constexpr int DVEC = DA ? vec_of<DDT>() : 1;
-    if (L.e0 || L.e1)
-        hipExtLaunchKernelGGL((k_stats<DT, VEC, DDT, DVEC, GREEDY, DRAFT, GPRE>), dim3(grid), dim3(kBlock), 0, L.st,
-                              L.e0, L.e1, 0, P);
-    else
-        hipLaunchKernelGGL((k_stats<DT, VEC, DDT, DVEC, GREEDY, DRAFT, GPRE>), dim3(grid), dim3(kBlock), 0, L.st, P);
+    auto kern = k_stats<DT, VEC, DDT, DVEC, GREEDY, DRAFT, GPRE>;
+    launch_timed(kern, resident_grid((const void*)kern, kBlock, items), kBlock, P, L);
 }
 
 template <int DT, bool A, bool GREEDY, bool GPRE>
-static void launch_stats_d(const StatsParams& P, int ddt, bool da, bool draft, int grid, const StatsLaunch& st)
+static void launch_stats_d(const StatsParams& P, int ddt, bool da, bool draft, int64_t items, const StatsLaunch& st)
 {
-    if (!draft) { launch_stats_t<DT, A, SPEC_F32, false, GREEDY, false, GPRE>(P, grid, st); return; }
+    if (!draft) { launch_stats_t<DT, A, SPEC_F32, false, GREEDY, false, GPRE>(P, items, st); return; }
     if (ddt == SPEC_F32) {
-        if (da) launch_stats_t<DT, A, SPEC_F32, true, GREEDY, true, GPRE>(P, grid, st);
-        else launch_stats_t<DT, A, SPEC_F32, false, GREEDY, true, GPRE>(P, grid, st);
+        if (da) launch_stats_t<DT, A, SPEC_F32, true, GREEDY, true, GPRE>(P, items, st);
+        else launch_stats_t<DT, A, SPEC_F32, false, GREEDY, true, GPRE>(P, items, st);
     } else {
-        if (da) launch_stats_t<DT, A, SPEC_BF16, true, GREEDY, true, GPRE>(P, grid, st);
-        else launch_stats_t<DT, A, SPEC_BF16, false, GREEDY, true, GPRE>(P, grid, st);
+        if (da) launch_stats_t<DT, A, SPEC_BF16, true, GREEDY, true, GPRE>(P, items, st);
+        else launch_stats_t<DT, A, SPEC_BF16, false, GREEDY, true, GPRE>(P, items, st);
     }
 }
 
 template <bool GREEDY, bool GPRE>
-static void launch_stats_g(const StatsParams& P, int dt, bool a, int ddt, bool da, bool draft, int grid,
+static void launch_stats_g(const StatsParams& P, int dt, bool a, int ddt, bool da, bool draft, int64_t items,
                            const StatsLaunch& st)
 {
     if (dt == SPEC_F32) {
-        if (a) launch_stats_d<SPEC_F32, true, GREEDY, GPRE>(P, ddt, da, draft, grid, st);
-        else launch_stats_d<SPEC_F32, false, GREEDY, GPRE>(P, ddt, da, draft, grid, st);
+        if (a) launch_stats_d<SPEC_F32, true, GREEDY, GPRE>(P, ddt, da, draft, items, st);
+        else launch_stats_d<SPEC_F32, false, GREEDY, GPRE>(P, ddt, da, draft, items, st);
     } else {
-        if (a) launch_stats_d<SPEC_BF16, true, GREEDY, GPRE>(P, ddt, da, draft, grid, st);
-        else launch_stats_d<SPEC_BF16, false, GREEDY, GPRE>(P, ddt, da, draft, grid, st);
+        if (a) launch_stats_d<SPEC_BF16, true, GREEDY, GPRE>(P, ddt, da, draft, items, st);
+        else launch_stats_d<SPEC_BF16, false, GREEDY, GPRE>(P, ddt, da, draft, items, st);
     }
 }
 
-static void launch_stats(StatsParams P, int dt, bool a, int ddt, bool da, bool draft, bool greedy, int grid,
-                         int32_t* gpre, const StatsLaunch& st)
+template <int DT, int DDT, bool DA, bool GREEDY, bool DRAFT>
+static void launch_pipe_t(const StatsParams& P, int64_t items, const StatsLaunch& L)
 {
+    constexpr int DVEC = DA ? vec_of<DDT>() : 1;
+    auto kern = k_stats_pipe<DT, DDT, DVEC, GREEDY, DRAFT>;
+    launch_timed(kern, resident_grid((const void*)kern, kPipeBlock, (items + kGroups - 1) / kGroups), kPipeBlock, P,
+                 L);
+}
+
+template <int DT, bool GREEDY>
+static void launch_pipe_d(const StatsParams& P, int ddt, bool da, bool draft, int64_t items, const StatsLaunch& L)
+{
+    if (!draft) { launch_pipe_t<DT, SPEC_F32, false, GREEDY, false>(P, items, L); return; }
+    if (ddt == SPEC_F32) {
+        if (da) launch_pipe_t<DT, SPEC_F32, true, GREEDY, true>(P, items, L);
+        else launch_pipe_t<DT, SPEC_F32, false, GREEDY, true>(P, items, L);
+    } else {
+        if (da) launch_pipe_t<DT, SPEC_BF16, true, GREEDY, true>(P, items, L);
+        else launch_pipe_t<DT, SPEC_BF16, false, GREEDY, true>(P, items, L);
+    }
+}
+
+// `items` bounds the work from above; `rows_max` bounds the target rows of one
+// request.
+static void launch_stats(StatsParams P, int dt, bool a, int ddt, bool da, bool draft, bool greedy, int64_t items,
+                         int rows_max, int32_t* gpre, const StatsLaunch& st)
+{
+    const int vec = dt == SPEC_F32 ? vec_of<SPEC_F32>() : vec_of<SPEC_BF16>();
+    const bool pipe = a && P.vocab % vec == 0 && P.bs <= kRowBaseLds && (int64_t)P.bs * rows_max <= kPipeMap;
+    if (pipe) {
+        if (dt == SPEC_F32) {
+            if (greedy) launch_pipe_d<SPEC_F32, true>(P, ddt, da, draft, items, st);
+            else launch_pipe_d<SPEC_F32, false>(P, ddt, da, draft, items, st);
+        } else {
+            if (greedy) launch_pipe_d<SPEC_BF16, true>(P, ddt, da, draft, items, st);
+            else launch_pipe_d<SPEC_BF16, false>(P, ddt, da, draft, items, st);
+        }
+        return;
+    }
     const bool gp = P.bs > kMaxLdsPrefix;
     if (gp) {
         P.gprefix = gpre;
         hipLaunchKernelGGL(k_plan, dim3(1), dim3(kBlock), 0, st.st, P, gpre);
     }
     if (greedy) {
-        if (gp) launch_stats_g<true, true>(P, dt, a, ddt, da, draft, grid, st);
-        else launch_stats_g<true, false>(P, dt, a, ddt, da, draft, grid, st);
+        if (gp) launch_stats_g<true, true>(P, dt, a, ddt, da, draft, items, st);
+        else launch_stats_g<true, false>(P, dt, a, ddt, da, draft, items, st);
     } else {
-        if (gp) launch_stats_g<false, true>(P, dt, a, ddt, da, draft, grid, st);
-        else launch_stats_g<false, false>(P, dt, a, ddt, da, draft, grid, st);
+        if (gp) launch_stats_g<false, true>(P, dt, a, ddt, da, draft, items, st);
+        else launch_stats_g<false, false>(P, dt, a, ddt, da, draft, items, st);
     }
 }
 
@@ -1089,25 +1565,28 @@ static void launch_stats(StatsParams P, int dt, bool a, int ddt, bool da, bool d
 
 using namespace spec;
 
+static int elem_bytes(int dt) { return dt == SPEC_F32 ? 4 : 2; }
+
 // Verify workspace: partials [bs, NR, splits] | decisions [bs] | chunk sums [bs, splits] | row prefix [bs + 1]
-size_t spec_verify_chain_ws(int32_t bs, int32_t vocab, int32_t ld)
+size_t spec_verify_chain_ws(int32_t bs, int32_t vocab, int32_t ld, int32_t dtype)
 {
-    RowSplit sp = row_split(bs, vocab);
+    RowSplit sp = row_split(vocab, elem_bytes(dtype));
     const int NR = 2 * ld + 1;
     return align256((size_t)bs * NR * sp.splits * sizeof(Partial)) + align256((size_t)bs * sizeof(Dec)) +
            align256((size_t)bs * sp.splits * sizeof(double)) + align256((size_t)(bs + 1) * sizeof(int32_t));
 }
 
-size_t spec_verify_tree_ws(int32_t bs, int32_t vocab, int32_t rows_max)
+// Tree verify workspace: partials [bs, rows_max, splits] | row prefix [bs + 1]
+size_t spec_verify_tree_ws(int32_t bs, int32_t vocab, int32_t rows_max, int32_t dtype)
 {
-    RowSplit sp = row_split(bs, vocab);
+    RowSplit sp = row_split(vocab, elem_bytes(dtype));
     return align256((size_t)bs * rows_max * sp.splits * sizeof(Partial)) +
            align256((size_t)(bs + 1) * sizeof(int32_t));
 }
 
 int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st)
 {
-    RowSplit sp = row_split(a->bs, a->vocab);
+    RowSplit sp = row_split(a->vocab, elem_bytes(a->dtype));
     const int NR = 2 * a->ld + 1;
     char* ws = (char*)a->workspace;
     ChainParams P;
@@ -1146,9 +1625,9 @@ int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st)
     S.part = P.part; S.NR = NR; S.draft_base = a->ld + 1; S.gprefix = nullptr;
     const bool at = aligned16(a->logits, a->row_stride, a->dtype);
     const bool ad = draft && aligned16(a->draft_logits, a->draft_row_stride, a->draft_dtype);
-    const int grid = stats_grid(a->bs, a->ld + 1, sp);
+    const int64_t items = stats_items(a->bs, a->ld + 1, sp);
     const StatsLaunch L{st, (hipEvent_t)a->prof_begin, (hipEvent_t)a->prof_end};
-    launch_stats(S, a->dtype, at, a->draft_dtype, ad, draft, P.greedy, grid, gpre, L);
+    launch_stats(S, a->dtype, at, a->draft_dtype, ad, draft, P.greedy, items, a->ld + 1, gpre, L);
     if (a->dtype == SPEC_F32) hipLaunchKernelGGL((k_decide<SPEC_F32>), dim3(a->bs), dim3(kBlock), 0, st, P);
     else hipLaunchKernelGGL((k_decide<SPEC_BF16>), dim3(a->bs), dim3(kBlock), 0, st, P);
     if (draft) {
@@ -1173,7 +1652,7 @@ int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st)
 
 int spec_verify_tree_launch(const spec_tree_verify_args* a, hipStream_t st)
 {
-    RowSplit sp = row_split(a->bs, a->vocab);
+    RowSplit sp = row_split(a->vocab, elem_bytes(a->dtype));
     char* ws = (char*)a->workspace;
     TreeParams P;
     P.bs = a->bs; P.vocab = a->vocab; P.rows_max = a->rows_max;
@@ -1192,10 +1671,10 @@ int spec_verify_tree_launch(const spec_tree_verify_args* a, hipStream_t st)
     S.slot_flags = nullptr; S.ld = 0;
     S.bs = a->bs; S.vocab = a->vocab; S.chunk = sp.chunk; S.splits = sp.splits; S.c = 1.0f;
     S.part = P.part; S.NR = a->rows_max; S.draft_base = 0; S.gprefix = nullptr;
-    const int grid = stats_grid(a->bs, a->rows_max, sp);
+    const int64_t items = stats_items(a->bs, a->rows_max, sp);
     const StatsLaunch L{st, (hipEvent_t)a->prof_begin, (hipEvent_t)a->prof_end};
-    launch_stats(S, a->dtype, aligned16(a->logits, a->row_stride, a->dtype), SPEC_F32, false, false, true, grid,
-                 gpre, L);
+    launch_stats(S, a->dtype, aligned16(a->logits, a->row_stride, a->dtype), SPEC_F32, false, false, true, items,
+                 a->rows_max, gpre, L);
     hipLaunchKernelGGL(k_tree_walk, dim3(a->bs), dim3(kWave), 0, st, P);
     return spec_record_hip_error(hipGetLastError());
 }
