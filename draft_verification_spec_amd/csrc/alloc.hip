@@ -1,21 +1,18 @@
 // Verification-budget allocation.
 //
-// Chains (Hybrid Spark, Algorithm 1 and Sections 4.2-4.4), one launch of one
-// 1024-thread workgroup (k_alloc_chain):
-//   * every n-gram estimate (Eq. (1)) and model confidence is evaluated in
-//     fp64 by its own thread into LDS, next to both chains' tokens (all input
-//     is read once, coalesced); then one thread per request forms the
-//     survival running products, the chain values of Eq. (3) and the choice
-//     (contains rule, value rule with ties to the n-gram chain, or a lossless
-//     policy of Appendix H) and leaves the chosen chain's survivals in LDS;
-//   * one thread per slot writes the chosen chain and one 64-bit ranking key:
-//     fp32(S) bits | (31 - position) | (2^27 - 1 - request), so the largest
-//     key is "highest survival, then lower position, then lower request" and
-//     keys are unique;
-//   * the exact budget-th largest key by an 8-bit radix select over an LDS
-//     histogram (the digit is found by a wave-wide suffix scan), stopping as
-//     soon as the boundary bucket is taken whole;
-//   * each request's verified prefix and the CSR row bases.
+// Chains (Hybrid Spark, Algorithm 1 and Sections 4.2-4.4), two launches:
+//   k_alloc_slots: one wave per request evaluates every n-gram estimate
+//     (Eq. (1)) and model confidence in fp64 on its lanes, forms the survival
+//     running products, the chain values of Eq. (3) and the choice (contains
+//     rule, value rule with ties to the n-gram chain, or a lossless policy of
+//     Appendix H), and writes the chosen chain and one 64-bit ranking key per
+//     slot: fp32(S) bits | (31 - position) | (2^27 - 1 - request), so the
+//     largest key is "highest survival, then lower position, then lower
+//     request" and keys are unique;
+//   k_alloc_topk: one workgroup finds the exact budget-th largest key by an
+//     8-bit radix select over an LDS histogram (the digit is found by a
+//     wave-wide suffix scan), stopping as soon as the boundary bucket is taken
+//     whole, then each request's verified prefix and the CSR row bases.
 // Trees (AdaSpark, Sections 2.2, 3.1, 3.3):
 //   k_tree    : one wave per request builds the candidate forest in LDS
 //               (drafter block + n-gram chains), the acceptance estimates of
@@ -27,25 +24,14 @@
 namespace spec {
 
 constexpr int kAllocBlock = 1024;
-constexpr int kLdsKeys = 4096;          // ranking keys kept in LDS (32 KB); more go to the workspace
-constexpr int kLdsVals = 10240;         // fp64 per-slot values kept in LDS (80 KB); more go to the workspace
+constexpr int kSlotBlock = 256;                 // four requests (one wave each) per workgroup
+constexpr int kSlotReqs = kSlotBlock / kWave;
+constexpr int kLdsKeys = 4096;                  // ranking keys the select kernel keeps in LDS (32 KB)
 
 struct SelectParams {
     spec_chain_alloc a;
-    uint64_t* keys;  // workspace fallback: [bs, ld]
-    double* vals;    // workspace fallback for the staging area below
+    uint64_t* keys;  // [bs, ld] ranking keys, in the workspace
 };
-
-// Staging area, in 8-byte units per request: ld estimates (later survivals),
-// K confidences, the copy-length log term, four int32 words (length state,
-// n, a, choice) and the slot tokens of both chains (2 x ld int32).
-__host__ __device__ __forceinline__ int64_t vals_count(int64_t bs, int64_t ld, int64_t K) { return bs * (2 * ld + K + 3); }
-
-// length-state word: n-gram length (clamped) | flags
-constexpr int kGlMask = 0xFF;
-constexpr int kGlMismatch = 1 << 28;   // n-gram and model tokens differ within the first K
-constexpr int kGlPointMass = 1 << 29;  // model slots are point masses
-constexpr int kGlBadLen = 1 << 30;     // the given n-gram length was out of range
 
 __device__ __forceinline__ double sigm(double x) { return 1.0 / (1.0 + exp(-x)); }
 
@@ -60,26 +46,61 @@ __device__ __forceinline__ double est_logit(const spec_estimator& e, int k, int 
     return z;
 }
 
-// Request r: chain values from its estimates h[0..glen) and confidences
-// c[0..K) (the survival running products are left folds, as defined), the
-// chain choice, then the chosen chain's survivals written over h (slot k's
-// survival replaces h[k] once h[k] has been used).  `gl` is the request's
-// length-state word.  Returns (source << 8) | length.
-__device__ int select_fold(const spec_chain_alloc& A, int gl, double* h, const double* cc)
+// Lane k's double, broadcast to the wave (k wave-uniform).
+__device__ __forceinline__ double lane_value(double v, int k)
 {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFFll), k);
+    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), k);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// One wave per request.  Lane k evaluates slot k's n-gram estimate (Eq. (1))
+// and model confidence in fp64; the survival running products, the chain
+// values of Eq. (3) and the choice (contains rule, value rule with ties to the
+// n-gram chain, or a lossless policy of Appendix H) are then computed by every
+// lane alike, as the same left folds the definition uses, with lane k's values
+// broadcast in turn; finally lane k writes slot k of the chosen chain and its
+// ranking key.
+__global__ __launch_bounds__(kSlotBlock) void k_alloc_slots(SelectParams P)
+{
+    const spec_chain_alloc& A = P.a;
+    const int lane = threadIdx.x % kWave;
+    const int r = blockIdx.x * kSlotReqs + (int)(threadIdx.x / kWave);
+    if (r >= A.bs) return;   // the whole wave (no workgroup barrier in this kernel)
     const int K = A.K, ld = A.ld;
-    const int glen = gl & kGlMask;
+    const int rl = A.ngram_len[r];
+    const int gcap = A.ngram_ld < ld ? A.ngram_ld : ld;
+    const int glen = rl < 0 ? 0 : (rl > gcap ? gcap : rl);
+    const int n = A.ngram_feat[4 * (int64_t)r + 0];
+    const int am = A.ngram_feat[4 * (int64_t)r + 1];
+    double mm = (double)A.ngram_feat[4 * (int64_t)r + 2];
+    mm = mm < 1.0 ? 1.0 : (mm > (double)A.est.m_cap ? (double)A.est.m_cap : mm);
+    const double lnm = ((double)n >= (double)A.est.n_full) ? log(mm / (double)A.est.m_ref) : 0.0;
+    const bool mpm = !A.model_point_mass || A.model_point_mass[r];
+    const int k = lane;
+    int32_t td = -1, tg = -1;
+    double h = 0.0, c = 0.0;
+    if (k < K) {
+        td = A.model_tokens[(int64_t)r * K + k];
+        const double cv = (double)A.model_conf[(int64_t)r * K + k];
+        c = A.conf_is_logit ? sigm(cv) : cv;
+    }
+    if (k < gcap) tg = A.ngram_draft[(int64_t)r * A.ngram_ld + k];
+    if (k < glen) h = sigm(est_logit(A.est, k + 1, n, am, lnm));
+    const bool mismatch = __ballot(k < K && td != tg) != 0;
+    // chain values (Eq. (3)) from the running products
     const double lam = (double)A.lambda;
     double sg = 1.0, sd = 1.0, vg = 0.0, vd = 0.0;
-    for (int k = 0; k < glen; ++k) {
-        sg *= h[k];
+    for (int q = 0; q < glen; ++q) {
+        sg *= lane_value(h, q);
         vg += sg > lam ? sg - lam : 0.0;
     }
-    for (int k = 0; k < K; ++k) {
-        sd *= cc[k];
+    for (int q = 0; q < K; ++q) {
+        sd *= lane_value(c, q);
         vd += sd > lam ? sd - lam : 0.0;
     }
-    const bool prefix = glen > K && !(gl & kGlMismatch);
+    const bool prefix = glen > K && !mismatch;
     int use = SPEC_SRC_MODEL;
     switch (A.policy) {
     case SPEC_POLICY_PROPOSED:
@@ -92,24 +113,45 @@ __device__ int select_fold(const spec_chain_alloc& A, int gl, double* h, const d
     default: use = SPEC_SRC_MODEL;
     }
     const int len = (use == SPEC_SRC_MODEL) ? K : glen;
+    // survivals of the chosen chain; lane k keeps S_k
     sg = 1.0;
     sd = 1.0;
-    double prev = 1.0;
-    for (int k = 0; k < ld; ++k) {
-        const double hk = (k < glen) ? h[k] : 0.0;
-        if (k < glen) sg *= hk;
-        if (k < K) sd *= cc[k];
-        double S = 0.0;
-        if (k < len) {
-            if (use == SPEC_SRC_MODEL) S = sd;
-            else if (use == SPEC_SRC_NGRAM) S = sg;
-            else if (use == SPEC_SRC_MERGED) S = (k < K) ? (sg > sd ? sg : sd) : prev * hk;
-            else S = (k < K) ? sd : prev * hk;
-            prev = S;
-        }
-        h[k] = S;
+    double prev = 1.0, mine = 0.0;
+    for (int q = 0; q < len; ++q) {
+        const double hq = (q < glen) ? lane_value(h, q) : 0.0;
+        if (q < glen) sg *= hq;
+        if (q < K) sd *= lane_value(c, q);
+        double S;
+        if (use == SPEC_SRC_MODEL) S = sd;
+        else if (use == SPEC_SRC_NGRAM) S = sg;
+        else if (use == SPEC_SRC_MERGED) S = (q < K) ? (sg > sd ? sg : sd) : prev * hq;
+        else S = (q < K) ? sd : prev * hq;
+        prev = S;
+        if (lane == q) mine = S;
     }
-    return (use << 8) | len;
+    if (k < ld) {
+        int32_t tk = -1;
+        uint8_t fl = 0;
+        if (k < len) {
+            const bool model_slot = use == SPEC_SRC_MODEL || (use == SPEC_SRC_EXTENDED && k < K);
+            tk = (use == SPEC_SRC_MODEL) ? td : tg;
+            fl = model_slot ? (mpm ? SPEC_SLOT_POINT_MASS : 0) : (SPEC_SLOT_POINT_MASS | SPEC_SLOT_FROM_NGRAM);
+        }
+        const int64_t o = (int64_t)r * ld + k;
+        A.chain_tokens[o] = tk;
+        A.slot_flags[o] = fl;
+        A.survival[o] = (float)mine;
+        // fp32(S) bits | (31 - position) | (2^27 - 1 - request): the largest key
+        // is "highest survival, then lower position, then lower request"
+        P.keys[o] = (k < len) ? (((uint64_t)__float_as_uint((float)mine) << 32) | ((uint64_t)(31 - k) << 27) |
+                                 (uint64_t)(0x7FFFFFF - r))
+                              : 0ull;
+    }
+    if (lane == 0) {
+        A.chain_len[r] = len;
+        A.chain_src[r] = use;
+        A.out_flags[r] = (rl < 0 || rl > gcap) ? SPEC_FLAG_BAD_LENGTH : 0u;
+    }
 }
 
 __device__ int64_t block_exclusive_i64(int64_t v, int64_t* total)
@@ -149,102 +191,33 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, bool active, int dg)
     else if (active && dg != ldg) atomicAdd(&hist[dg], 1u);
 }
 
-// Chain selection for every request, then the exact budget-th largest key by
-// an 8-bit radix select, the verified prefix per request and the row bases.
-__global__ __launch_bounds__(kAllocBlock) void k_alloc_chain(SelectParams P)
+// The exact budget-th largest ranking key by an 8-bit radix select (stopping
+// as soon as the boundary bucket is taken whole), each request's verified
+// prefix and the row bases.  One workgroup.
+__global__ __launch_bounds__(kAllocBlock) void k_alloc_topk(SelectParams P)
 {
     const spec_chain_alloc& A = P.a;
-    const int bs = A.bs, ld = A.ld, K = A.K;
+    const int bs = A.bs, ld = A.ld;
     const int64_t N = (int64_t)bs * ld;
     __shared__ uint64_t lkeys[kLdsKeys];
-    __shared__ double lvals[kLdsVals];
     __shared__ uint32_t hist[256];
     __shared__ uint64_t sh_prefix, sh_min;
     __shared__ int64_t sh_rem, sh_valid;
     __shared__ int sh_done;
-    uint64_t* keys = (N <= kLdsKeys) ? lkeys : P.keys;
-    double* H = (vals_count(bs, ld, K) <= kLdsVals) ? lvals : P.vals;
-    double* Cc = H + N;
-    double* LNM = Cc + (int64_t)bs * K;
-    int32_t* GL = (int32_t*)(LNM + bs);
-    int32_t* FN = GL + bs;
-    int32_t* FA = FN + bs;
-    int32_t* CH = FA + bs;
-    int32_t* TD = CH + bs;      // model token per slot
-    int32_t* TG = TD + N;       // n-gram token per slot
+    const bool in_lds = N <= kLdsKeys;
+    uint64_t* keys = in_lds ? lkeys : P.keys;
     const int wid = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     if (threadIdx.x == 0) { sh_prefix = 0; sh_valid = 0; sh_done = 0; sh_min = ~0ull; }
-    // 1a. per request: lengths, match features, the copy-length log term
-    for (int r = threadIdx.x; r < bs; r += kAllocBlock) {
-        const int rl = A.ngram_len[r];
-        const int n = A.ngram_feat[4 * (int64_t)r + 0];
-        const int am = A.ngram_feat[4 * (int64_t)r + 1];
-        double mm = (double)A.ngram_feat[4 * (int64_t)r + 2];
-        const bool mpm = !A.model_point_mass || A.model_point_mass[r];
-        const int gcap = A.ngram_ld < ld ? A.ngram_ld : ld;
-        const int glen = rl < 0 ? 0 : (rl > gcap ? gcap : rl);
-        GL[r] = glen | (mpm ? kGlPointMass : 0) | ((rl < 0 || rl > gcap) ? kGlBadLen : 0);
-        FN[r] = n;
-        FA[r] = am;
-        mm = mm < 1.0 ? 1.0 : (mm > (double)A.est.m_cap ? (double)A.est.m_cap : mm);
-        LNM[r] = ((double)n >= (double)A.est.n_full) ? log(mm / (double)A.est.m_ref) : 0.0;
-    }
-    __syncthreads();
-    // 1b. per slot: tokens of both chains, the model confidence and the
-    // n-gram estimate (fp64), the first-K agreement of the two chains
-    for (int64_t i = threadIdx.x; i < N; i += kAllocBlock) {
-        const int r = (int)(i / ld), k = (int)(i - (int64_t)r * ld);
-        int32_t td = -1, tg = -1;
-        double cv = 0.0;
-        if (k < K) {
-            td = A.model_tokens[(int64_t)r * K + k];
-            cv = (double)A.model_conf[(int64_t)r * K + k];
-        }
-        if (k < A.ngram_ld) tg = A.ngram_draft[(int64_t)r * A.ngram_ld + k];
-        const int gl = GL[r];
-        const int glen = gl & kGlMask;
-        H[i] = (k < glen) ? sigm(est_logit(A.est, k + 1, FN[r], FA[r], LNM[r])) : 0.0;
-        if (k < K) Cc[(int64_t)r * K + k] = A.conf_is_logit ? sigm(cv) : cv;
-        TD[i] = td;
-        TG[i] = tg;
-        if (k < K && glen > K && td != tg) atomicOr(&GL[r], kGlMismatch);
-    }
-    __syncthreads();
-    // 1c. one thread per request: values, choice, survivals (over H)
     {
         int64_t valid = 0;
-        for (int r = threadIdx.x; r < bs; r += kAllocBlock) {
-            const int gl = GL[r];
-            const int ch = select_fold(A, gl, H + (int64_t)r * ld, Cc + (int64_t)r * K);
-            CH[r] = ch;
-            valid += ch & 255;
-            A.chain_len[r] = ch & 255;
-            A.chain_src[r] = ch >> 8;
-            A.out_flags[r] = (gl & kGlBadLen) ? SPEC_FLAG_BAD_LENGTH : 0u;
+        for (int64_t i = threadIdx.x; i < N; i += kAllocBlock) {
+            const uint64_t k = P.keys[i];
+            if (in_lds) lkeys[i] = k;
+            valid += k != 0;
         }
         valid = wave_sum(valid);
+        __syncthreads();   // sh_valid initialised
         if (lane == 0) atomicAdd((unsigned long long*)&sh_valid, (unsigned long long)valid);
-    }
-    __syncthreads();
-    // 1d. per-slot outputs and ranking keys
-    for (int64_t i = threadIdx.x; i < N; i += kAllocBlock) {
-        const int r = (int)(i / ld), k = (int)(i - (int64_t)r * ld);
-        const int ch = CH[r], use = ch >> 8, len = ch & 255;
-        int32_t tk = -1;
-        uint8_t fl = 0;
-        const double S = H[i];
-        if (k < len) {
-            const bool model_slot = use == SPEC_SRC_MODEL || (use == SPEC_SRC_EXTENDED && k < K);
-            const bool mpm = (GL[r] & kGlPointMass) != 0;
-            tk = (use == SPEC_SRC_MODEL) ? TD[i] : TG[i];
-            fl = model_slot ? (mpm ? SPEC_SLOT_POINT_MASS : 0) : (SPEC_SLOT_POINT_MASS | SPEC_SLOT_FROM_NGRAM);
-        }
-        A.chain_tokens[i] = tk;
-        A.slot_flags[i] = fl;
-        A.survival[i] = (float)S;
-        keys[i] = (k < len) ? (((uint64_t)__float_as_uint((float)S) << 32) | ((uint64_t)(31 - k) << 27) |
-                               (uint64_t)(0x7FFFFFF - r))
-                            : 0ull;
     }
     __syncthreads();
     const int64_t take = (A.budget < sh_valid) ? A.budget : sh_valid;
@@ -312,15 +285,18 @@ __global__ __launch_bounds__(kAllocBlock) void k_alloc_chain(SelectParams P)
             theta = sh_min;
         }
     }
-    // 3. verified prefix per request, row bases over (alloc + 1)
+    // verified prefix per request, row bases over (alloc + 1)
     const int per = (bs + (int)blockDim.x - 1) / (int)blockDim.x;
     const int r0 = threadIdx.x * per;
     int64_t local = 0;
     for (int r = r0; r < r0 + per && r < bs; ++r) {
         int cnt = 0;
-        for (int k = 0; k < ld; ++k) {
-            const uint64_t key = keys[(int64_t)r * ld + k];
-            cnt += (key != 0 && key >= theta);
+#pragma unroll
+        for (int k = 0; k < SPEC_MAX_DRAFT; ++k) {
+            if (k < ld) {
+                const uint64_t key = keys[(int64_t)r * ld + k];
+                cnt += (key != 0 && key >= theta);
+            }
         }
         A.alloc_len[r] = cnt;
         local += cnt + 1;
@@ -476,12 +452,7 @@ using namespace spec;
 size_t spec_alloc_ws(const spec_alloc_args* a)
 {
     if (a->mode != SPEC_ALLOC_CHAIN) return 0;
-    const int64_t N = (int64_t)a->chain.bs * a->chain.ld;
-    const int64_t NV = vals_count(a->chain.bs, a->chain.ld, a->chain.K);
-    size_t b = 0;
-    if (N > kLdsKeys) b += align256((size_t)N * sizeof(uint64_t));
-    if (NV > kLdsVals) b += align256((size_t)NV * sizeof(double));
-    return b;
+    return align256((size_t)a->chain.bs * a->chain.ld * sizeof(uint64_t));   // ranking keys
 }
 
 int spec_alloc_launch(const spec_alloc_args* a, hipStream_t st)
@@ -489,15 +460,10 @@ int spec_alloc_launch(const spec_alloc_args* a, hipStream_t st)
     if (a->mode == SPEC_ALLOC_CHAIN) {
         SelectParams P;
         P.a = a->chain;
-        const int64_t N = (int64_t)a->chain.bs * a->chain.ld;
-        char* ws = (char*)a->workspace;
-        P.keys = nullptr;
-        if (N > kLdsKeys) {
-            P.keys = (uint64_t*)ws;
-            ws += align256((size_t)N * sizeof(uint64_t));
-        }
-        P.vals = (double*)ws;
-        hipLaunchKernelGGL(k_alloc_chain, dim3(1), dim3(kAllocBlock), 0, st, P);
+        P.keys = (uint64_t*)a->workspace;
+        const int grid = (a->chain.bs + kSlotReqs - 1) / kSlotReqs;
+        hipLaunchKernelGGL(k_alloc_slots, dim3(grid), dim3(kSlotBlock), 0, st, P);
+        hipLaunchKernelGGL(k_alloc_topk, dim3(1), dim3(kAllocBlock), 0, st, P);
     } else {
         TreeBuildParams P;
         P.a = a->tree;
