@@ -69,6 +69,13 @@ __device__ __forceinline__ T wave_sum(T v)
     return v;
 }
 
+__device__ __forceinline__ uint32_t wave_or(uint32_t v)
+{
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v |= __shfl_xor(v, o, kWave);
+    return v;
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
 {
 #pragma unroll

@@ -957,46 +957,61 @@ __device__ double range_sum(const ChainParams& P, const Draw& d, int64_t lo, int
 
 // First token of the chunk [lo, hi) whose running weight (index order)
 // exceeds t; when rounding leaves t past the chunk, its last positive-weight
-// token; -1 if the chunk has no weight.
+// token; -1 if the chunk has no weight.  Only the thread whose segment holds
+// the crossing walks its weights; the threads past it can only offer their
+// first positive weight (adding a positive weight to a running sum already
+// above t stays above t), which the minimum over candidates discards.
 template <int DTT, int DTD>
 __device__ int64_t search_range(const ChainParams& P, const Draw& d, int64_t lo, int64_t hi, double t)
 {
-    __shared__ unsigned long long sh_found;
+    __shared__ long long sh_found[kBlock / kWave];   // each wave's first candidate
     __shared__ long long sh_lp[kBlock / kWave];
-    __syncthreads();
-    if (threadIdx.x == 0) sh_found = ~0ull;
-    __syncthreads();
+    const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
     int64_t a, b;
     seg_of(lo, hi, &a, &b);
     double w[kSeg];
     double mine = 0.0;
-    int64_t lp = -1;
+    uint32_t posmask = 0;   // segment offsets with positive weight
     if (a < b) {
         seg_weights<DTT, DTD>(P, d, a, b, w);
 #pragma unroll
         for (int u = 0; u < kSeg; ++u) {
             mine += w[u];
-            if (w[u] > 0.0) lp = a + u;
+            posmask |= (w[u] > 0.0 ? 1u : 0u) << u;
         }
     }
     double total;
-    double cum = block_exclusive_f64(mine, &total);
-    if (a < b && cum + mine > t) {
-        int64_t pos = -1;
+    const double cum = block_exclusive_f64(mine, &total);
+    // candidates are ordered like their positions, so a wave's first
+    // candidate lane holds its smallest position
+    const uint64_t cand = __ballot(a < b && posmask != 0u && cum + mine > t);
+    if (cand == 0) {
+        if (lane == 0) sh_found[wid] = -1;
+    } else if (lane == (int)__builtin_ctzll(cand)) {
+        int pu;
+        if (cum > t) {
+            pu = __builtin_ctz(posmask);
+        } else {
+            pu = -1;
+            double run = cum;
 #pragma unroll
-        for (int u = 0; u < kSeg; ++u) {
-            if (w[u] > 0.0 && pos < 0 && cum + w[u] > t) pos = a + u;
-            cum += w[u];
+            for (int u = 0; u < kSeg; ++u) {
+                run += w[u];
+                if (pu < 0 && w[u] > 0.0 && run > t) pu = u;
+            }
+            if (pu < 0) pu = 31 - __builtin_clz(posmask);
         }
-        if (pos < 0) pos = lp;
-        if (pos >= 0) atomicMin(&sh_found, (unsigned long long)pos);
+        sh_found[wid] = (long long)(a + pu);
     }
     __syncthreads();
-    int64_t res = sh_found != ~0ull ? (int64_t)sh_found : -1;
+    int64_t res = -1;
+    for (int w2 = 0; w2 < kBlock / kWave; ++w2)
+        if (sh_found[w2] >= 0 && (res < 0 || sh_found[w2] < res)) res = sh_found[w2];
     if (res < 0) {
         // rounding left t past the chunk: its last positive-weight token
-        const long long m = wave_max((long long)lp);
-        if (threadIdx.x % kWave == 0) sh_lp[threadIdx.x / kWave] = m;
+        const long long lp = posmask ? (long long)(a + 31 - __builtin_clz(posmask)) : -1ll;
+        const long long m = wave_max(lp);
+        if (lane == 0) sh_lp[wid] = m;
         __syncthreads();
         for (int w2 = 0; w2 < kBlock / kWave; ++w2) res = sh_lp[w2] > res ? sh_lp[w2] : res;
     }
@@ -1150,6 +1165,8 @@ __global__ __launch_bounds__(kBlock) void k_decide(ChainParams P)
     }
     __syncthreads();
     // slot i = t < b: p(y), q(y), accept
+    bool rejected = false;
+    uint32_t slot_fl = 0;
     if (t < b) {
         bool acc = true;
         uint32_t fl = 0;
@@ -1182,12 +1199,22 @@ __global__ __launch_bounds__(kBlock) void k_decide(ChainParams P)
         }
         if (P.out_p) P.out_p[off] = (float)p;
         if (P.out_q) P.out_q[off] = (float)q;
-        if (!acc) atomicOr(&sRej, 1ull << t);
-        if (fl) atomicOr(&sFlags, fl);
+        rejected = !acc;
+        slot_fl = fl;
     } else if (t < ld) {
         const int64_t off = (int64_t)r * ld + t;
         if (P.out_p) P.out_p[off] = 0.0f;
         if (P.out_q) P.out_q[off] = 0.0f;
+    }
+    // every slot thread is in wave 0 (b <= ld <= 32): a ballot and an OR
+    // across the wave instead of atomics
+    if (t < kWave) {
+        const uint64_t rj = __ballot(rejected);
+        const uint32_t f = wave_or(slot_fl);
+        if (t == 0) {
+            sRej = rj;
+            sFlags |= f;
+        }
     }
     __syncthreads();
     const uint64_t rej = sRej;
