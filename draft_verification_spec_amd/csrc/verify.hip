@@ -790,28 +790,7 @@ __global__ __launch_bounds__(kPipeBlock) void k_stats_pipe(StatsParams P)
 // merging partials
 // ---------------------------------------------------------------------------
 
-// Softmax row from its chunk partials p[0], p[st], ...: *O = m*c, *Z = sum
-// relative to O (fp64, one online pass); false when unusable.
-__device__ bool merge_softmax(const Partial* p, int splits, int st, float c, float* O, double* Z)
-{
-    float m = -INFINITY;
-    double z = 0.0;
-    bool nan = false;
-    for (int s = 0; s < splits; ++s) {
-        const Partial q = p[s * st];
-        nan |= (q.m != q.m) || (q.s != q.s);
-        if (q.m == -INFINITY) continue;
-        if (q.m > m) {
-            if (m != -INFINITY) z *= (double)fast_exp2((float)((double)(m * c) - (double)(q.m * c)));
-            m = q.m;
-        }
-        z += q.s * (double)fast_exp2((float)((double)(q.m * c) - (double)(m * c)));
-    }
-    *O = m * c;
-    *Z = z;
-    return !nan && m != -INFINITY && m != INFINITY && z > 0.0 && z < INFINITY;
-}
-
+// Argmax of a row from its chunk partials p[0], p[st], ... (first index on ties).
 __device__ bool merge_argmax(const Partial* p, int splits, int st, int32_t* idx)
 {
     ArgAcc acc{-INFINITY, 0x7FFFFFFF, 0};
@@ -1109,30 +1088,57 @@ __device__ void commit(const ChainParams& P, int r, int n, int nacc, int32_t las
 
 constexpr int kMaxPartsLds = 2048;   // partials of one request staged in LDS (32 KB)
 
+constexpr int kMergeLanes = 8;   // lanes that merge one row's chunk partials
+
 template <int DTT>
 __global__ __launch_bounds__(kBlock) void k_decide(ChainParams P)
 {
     const int r = blockIdx.x;
     const int t = threadIdx.x;
     const int ld = P.ld;
-    int b = P.n_slots[r];
-    const bool badlen = (b < 0 || b > ld);
-    b = b < 0 ? 0 : (b > ld ? ld : b);
     __shared__ Partial sp[kMaxPartsLds];
     __shared__ float sO[2 * SPEC_MAX_DRAFT + 1];
     __shared__ double sZ[2 * SPEC_MAX_DRAFT + 1];
     __shared__ int32_t sArg[2 * SPEC_MAX_DRAFT + 1];
     __shared__ int32_t sOk[2 * SPEC_MAX_DRAFT + 1];
+    __shared__ int32_t sTok[SPEC_MAX_DRAFT];
+    __shared__ uint8_t sPm[SPEC_MAX_DRAFT];
     __shared__ double sW[kMaxSplits];
     __shared__ uint32_t sFlags;
     __shared__ unsigned long long sRej;
+    // Slot inputs first (thread t = slot t), including the logits of each
+    // slot's token, so that these dependent loads overlap the staging and the
+    // merges below.
+    int b = P.n_slots[r];
+    const int64_t row_base = P.row_base[r];
+    int32_t y = -1;
+    bool pm = true;
+    float uacc = 0.0f, zt = 0.0f, zd = 0.0f;
+    if (t < ld) {
+        const int64_t off = (int64_t)r * ld + t;
+        y = P.tokens[off];
+        pm = !P.slot_flags || (P.slot_flags[off] & SPEC_SLOT_POINT_MASS);
+        const bool yok = y >= 0 && y < P.vocab;
+        if (!P.greedy) {
+            uacc = P.u_acc[off];
+            const int64_t row = row_base + t;
+            if (yok && row >= 0 && row < P.n_rows) zt = logit_at(P.logits, DTT, row, P.stride, y);
+            if (!pm && P.dlogits) {
+                const int64_t drow = P.drow_base[r] + t;
+                if (yok && drow >= 0 && drow < P.dn_rows) zd = logit_at(P.dlogits, P.ddt, drow, P.dstride, y);
+            }
+        }
+        sTok[t] = y;
+        sPm[t] = pm;
+    }
+    const bool badlen = (b < 0 || b > ld);
+    b = b < 0 ? 0 : (b > ld ? ld : b);
     if (t == 0) { sFlags = badlen ? SPEC_FLAG_BAD_LENGTH : 0u; sRej = 0; }
-    // stage this request's partials (contiguous) in LDS
+    // stage this request's partials (contiguous) in LDS, split-major
+    // (sp[s * NR + row])
     const int nparts = P.NR * P.splits;
     const bool staged = nparts <= kMaxPartsLds;
     const Partial* gp = P.part + (int64_t)r * nparts;
-    // split-major in LDS (sp[s * NR + row]) so row-per-thread merges read
-    // consecutive entries
     if (staged)
         for (int i = t; i < nparts; i += kBlock) {
             const int row = i / P.splits, s = i - row * P.splits;
@@ -1142,24 +1148,58 @@ __global__ __launch_bounds__(kBlock) void k_decide(ChainParams P)
     const Partial* rp = staged ? sp : gp;
     const int rs = staged ? P.NR : 1;               // stride between a row's splits
     const int rr = staged ? 1 : P.splits;           // stride between rows
-    // rows: target 0..b, draft ld+1 .. ld+b (probabilistic slots, T > 0)
-    if (t < P.NR) {
-        bool is_row = t <= b;
-        if (!is_row && !P.greedy && P.dlogits && t >= ld + 1 && t <= ld + b) {
-            const int i = t - ld - 1;
-            is_row = !(P.slot_flags && (P.slot_flags[(int64_t)r * ld + i] & SPEC_SLOT_POINT_MASS));
-        }
-        sOk[t] = 0;
-        if (is_row) {
-            if (P.greedy) {
-                int32_t idx;
-                sOk[t] = merge_argmax(rp + t * rr, P.splits, rs, &idx);
-                sArg[t] = idx;
-            } else {
-                float O; double Z;
-                sOk[t] = merge_softmax(rp + t * rr, P.splits, rs, P.c, &O, &Z);
-                sO[t] = O;
-                sZ[t] = Z;
+    // Rows: target 0..b, draft ld+1 .. ld+b (probabilistic slots, T > 0).
+    // kMergeLanes lanes merge one row: each folds every kMergeLanes-th chunk
+    // partial online, then the lanes combine pairwise.
+    for (int row0 = 0; row0 < P.NR; row0 += kBlock / kMergeLanes) {
+        const int row = row0 + t / kMergeLanes, j = t % kMergeLanes;
+        bool is_row = row < P.NR && row <= b;
+        if (!is_row && row < P.NR && !P.greedy && P.dlogits && row >= ld + 1 && row <= ld + b)
+            is_row = !sPm[row - ld - 1];
+        if (P.greedy) {
+            ArgAcc acc{-INFINITY, 0x7FFFFFFF, 0};
+            if (is_row)
+                for (int s = j; s < P.splits; s += kMergeLanes) {
+                    const Partial q = rp[row * rr + s * rs];
+                    ArgAcc bq{q.m, q.idx & 0x7FFFFFFF, (q.idx >> 31) & 1};
+                    if (q.m != q.m) bq.bad = 1;
+                    am_combine(acc, bq);
+                }
+#pragma unroll
+            for (int o = 1; o < kMergeLanes; o <<= 1) {
+                ArgAcc bq{__shfl_xor(acc.best, o, kWave), __shfl_xor(acc.idx, o, kWave), __shfl_xor(acc.bad, o, kWave)};
+                am_combine(acc, bq);
+            }
+            if (j == 0 && row < P.NR) {
+                sOk[row] = is_row && !acc.bad && acc.idx != 0x7FFFFFFF;
+                sArg[row] = acc.idx;
+            }
+        } else {
+            float m = -INFINITY;
+            double z = 0.0;
+            int nan = 0;
+            if (is_row)
+                for (int s = j; s < P.splits; s += kMergeLanes) {
+                    const Partial q = rp[row * rr + s * rs];
+                    nan |= (q.m != q.m) || (q.s != q.s);
+                    if (q.m == -INFINITY) continue;
+                    if (q.m > m) {
+                        if (m != -INFINITY) z *= (double)fast_exp2((float)((double)(m * P.c) - (double)(q.m * P.c)));
+                        m = q.m;
+                    }
+                    z += q.s * (double)fast_exp2((float)((double)(q.m * P.c) - (double)(m * P.c)));
+                }
+#pragma unroll
+            for (int o = 1; o < kMergeLanes; o <<= 1) {
+                const float m2 = __shfl_xor(m, o, kWave);
+                const double z2 = __shfl_xor(z, o, kWave);
+                nan |= __shfl_xor(nan, o, kWave);
+                sm_combine(m, z, m2, z2, P.c);
+            }
+            if (j == 0 && row < P.NR) {
+                sOk[row] = is_row && !nan && m != -INFINITY && m != INFINITY && z > 0.0 && z < INFINITY;
+                sO[row] = m * P.c;
+                sZ[row] = z;
             }
         }
     }
@@ -1171,8 +1211,6 @@ __global__ __launch_bounds__(kBlock) void k_decide(ChainParams P)
         bool acc = true;
         uint32_t fl = 0;
         const int64_t off = (int64_t)r * ld + t;
-        const int32_t y = P.tokens[off];
-        const bool pm = !P.slot_flags || (P.slot_flags[off] & SPEC_SLOT_POINT_MASS);
         const bool bad = (y < 0 || y >= P.vocab);
         if (bad) fl |= SPEC_FLAG_BAD_TOKEN;
         if (!sOk[t]) fl |= SPEC_FLAG_BAD_LOGITS;
@@ -1181,21 +1219,15 @@ __global__ __launch_bounds__(kBlock) void k_decide(ChainParams P)
             p = (!bad && sOk[t] && sArg[t] == y) ? 1.0 : 0.0;
             acc = (p == 1.0);
         } else {
-            if (!bad && sOk[t]) {
-                const float z = logit_at(P.logits, DTT, P.row_base[r] + t, P.stride, y);
-                p = (double)fast_exp2(fmaf(z, P.c, -sO[t])) / sZ[t];
-            }
+            if (!bad && sOk[t]) p = (double)fast_exp2(fmaf(zt, P.c, -sO[t])) / sZ[t];
             if (!pm) {
                 const int dr = ld + 1 + t;
                 if (!sOk[dr]) fl |= SPEC_FLAG_BAD_LOGITS;
                 q = 0.0;
-                if (!bad && sOk[dr] && P.dlogits) {
-                    const float w = logit_at(P.dlogits, P.ddt, P.drow_base[r] + t, P.dstride, y);
-                    q = (double)fast_exp2(fmaf(w, P.c, -sO[dr])) / sZ[dr];
-                }
+                if (!bad && sOk[dr] && P.dlogits) q = (double)fast_exp2(fmaf(zd, P.c, -sO[dr])) / sZ[dr];
             }
             const double rho = q > 0.0 ? p / q : 0.0;
-            acc = (double)P.u_acc[off] < rho;
+            acc = (double)uacc < rho;
         }
         if (P.out_p) P.out_p[off] = (float)p;
         if (P.out_q) P.out_q[off] = (float)q;
@@ -1219,8 +1251,7 @@ __global__ __launch_bounds__(kBlock) void k_decide(ChainParams P)
     __syncthreads();
     const uint64_t rej = sRej;
     const int nacc = rej ? (int)__builtin_ctzll(rej) : b;
-    for (int i = t; i <= ld; i += kBlock)
-        P.out_tokens[(int64_t)r * (ld + 1) + i] = (i < nacc) ? P.tokens[(int64_t)r * ld + i] : -1;
+    if (t <= ld) P.out_tokens[(int64_t)r * (ld + 1) + t] = (t < nacc) ? y : -1;
     if (t == 0) {
         P.out_num[r] = nacc + 1;
         P.out_acc[r] = nacc;
@@ -1228,7 +1259,7 @@ __global__ __launch_bounds__(kBlock) void k_decide(ChainParams P)
     }
     // what to draw
     Draw d;
-    d.mode = 0; d.y = -1; d.Ot = d.Od = 0.0f; d.row_t = P.row_base[r] + nacc; d.row_d = -1; d.ratio = 1.0;
+    d.mode = 0; d.y = -1; d.Ot = d.Od = 0.0f; d.row_t = row_base + nacc; d.row_d = -1; d.ratio = 1.0;
     int32_t last = -1;
     bool deferred = false;
     if (P.greedy) {
@@ -1239,15 +1270,14 @@ __global__ __launch_bounds__(kBlock) void k_decide(ChainParams P)
         if (nacc == b) {
             d.mode = 1;
         } else {
-            const int64_t off = (int64_t)r * ld + nacc;
-            const int32_t y = P.tokens[off];
-            const bool pm = !P.slot_flags || (P.slot_flags[off] & SPEC_SLOT_POINT_MASS);
-            const bool bad = (y < 0 || y >= P.vocab);
+            const int32_t yn = sTok[nacc];
+            const bool pmn = sPm[nacc];
+            const bool bad = (yn < 0 || yn >= P.vocab);
             const int dr = ld + 1 + nacc;
             if (bad) d.mode = 1;
-            else if (pm) { d.mode = 3; d.y = y; }
+            else if (pmn) { d.mode = 3; d.y = yn; }
             else if (sOk[dr] && P.dlogits) {
-                d.mode = 2; d.y = y; d.row_d = P.drow_base[r] + nacc; d.Od = sO[dr]; d.ratio = sZ[nacc] / sZ[dr];
+                d.mode = 2; d.y = yn; d.row_d = P.drow_base[r] + nacc; d.Od = sO[dr]; d.ratio = sZ[nacc] / sZ[dr];
             } else d.mode = 1;   // unusable draft row (flagged): fall back to p
         }
     }
