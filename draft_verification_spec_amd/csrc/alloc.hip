@@ -177,6 +177,25 @@ __device__ int64_t block_exclusive_i64(int64_t v, int64_t* total)
     return before + inc - v;
 }
 
+// Exclusive prefix over the workgroup of 32-bit counts; *total gets the sum.
+__device__ uint32_t block_exclusive_u32(uint32_t v, uint32_t* total)
+{
+    __shared__ uint32_t sh[32];
+    const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+    const int nw = (int)(blockDim.x / kWave);
+    const uint32_t inc = wave_incl_add(v);
+    __syncthreads();
+    if (lane == kWave - 1) sh[wid] = inc;
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+    for (int w = 0; w < nw; ++w) {
+        if (w < wid) before += sh[w];
+        tot += sh[w];
+    }
+    *total = tot;
+    return before + inc - v;
+}
+
 // Histogram increment with the lanes that share the first active lane's digit
 // folded into one LDS atomic (at the top digits nearly every key agrees).
 __device__ __forceinline__ void hist_add(uint32_t* hist, bool active, int dg)
@@ -184,23 +203,24 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, bool active, int dg)
     const uint64_t act = __ballot(active);
     if (act == 0) return;
     const int leader = __builtin_ctzll(act);
-    const int ldg = __shfl(dg, leader, kWave);
+    const int ldg = __builtin_amdgcn_readlane(dg, leader);
     const uint64_t peers = __ballot(active && dg == ldg);
     const int lane = threadIdx.x % kWave;
     if (lane == leader) atomicAdd(&hist[ldg], (uint32_t)__popcll(peers));
     else if (active && dg != ldg) atomicAdd(&hist[dg], 1u);
 }
 
-// The exact budget-th largest ranking key by an 8-bit radix select (stopping
-// as soon as the boundary bucket is taken whole), each request's verified
-// prefix and the row bases.  One workgroup.
+// The exact budget-th largest ranking key by an 8-bit radix select over the
+// survival and position bytes (stopping as soon as the boundary bucket is
+// taken whole), the request bits by one ordered scan, then each request's
+// verified prefix and the row bases.  One workgroup.
 __global__ __launch_bounds__(kAllocBlock) void k_alloc_topk(SelectParams P)
 {
     const spec_chain_alloc& A = P.a;
     const int bs = A.bs, ld = A.ld;
     const int64_t N = (int64_t)bs * ld;
     __shared__ uint64_t lkeys[kLdsKeys];
-    __shared__ uint32_t hist[256];
+    __shared__ uint32_t hist[2][256];
     __shared__ uint64_t sh_prefix, sh_min;
     __shared__ int64_t sh_rem, sh_valid;
     __shared__ int sh_done;
@@ -225,29 +245,27 @@ __global__ __launch_bounds__(kAllocBlock) void k_alloc_topk(SelectParams P)
     if (take > 0) {
         if (threadIdx.x == 0) sh_rem = take;
         uint64_t mask = 0;
-        for (int shift = 56; shift >= 0; shift -= 8) {
-            for (int i = threadIdx.x; i < 256; i += kAllocBlock) hist[i] = 0;
-            __syncthreads();
+        for (int i = threadIdx.x; i < 256; i += kAllocBlock) hist[0][i] = 0;
+        __syncthreads();
+        for (int shift = 56, hb = 0; shift >= 0; shift -= 8, hb ^= 1) {
+            // the histogram of this pass was cleared during the previous one
+            uint32_t* H = hist[hb];
             const uint64_t pre = sh_prefix;
             const int64_t rounds = (N + kAllocBlock - 1) / kAllocBlock;
             for (int64_t u = 0; u < rounds; ++u) {
                 const int64_t i = threadIdx.x + u * kAllocBlock;
                 const uint64_t k = i < N ? keys[i] : 0ull;
-                hist_add(hist, k != 0 && (k & mask) == pre, (int)((k >> shift) & 255u));
+                hist_add(H, k != 0 && (k & mask) == pre, (int)((k >> shift) & 255u));
             }
+            for (int i = threadIdx.x; i < 256; i += kAllocBlock) hist[hb ^ 1][i] = 0;
             __syncthreads();
             if (wid == 0) {
                 // lane l owns digits 255-4l .. 252-4l (descending); suffix counts from the top
                 uint32_t c4[4];
                 uint32_t own = 0;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) { c4[j] = hist[255 - 4 * lane - j]; own += c4[j]; }
-                uint32_t inc = own;
-#pragma unroll
-                for (int o = 1; o < kWave; o <<= 1) {
-                    uint32_t u = __shfl_up(inc, o, kWave);
-                    if (lane >= o) inc += u;
-                }
+                for (int j = 0; j < 4; ++j) { c4[j] = H[255 - 4 * lane - j]; own += c4[j]; }
+                const uint32_t inc = wave_incl_add(own);
                 const int64_t rem = sh_rem;
                 const int64_t above = (int64_t)(inc - own);
                 if (above < rem && (int64_t)inc >= rem) {
@@ -267,6 +285,33 @@ __global__ __launch_bounds__(kAllocBlock) void k_alloc_topk(SelectParams P)
             mask |= 255ull << shift;
             __syncthreads();
             if (sh_done) break;
+            if (shift == 24) {
+                // Survival and position are fixed: at most one key per
+                // request matches the prefix, and index order is request
+                // order, i.e. descending key order.  The threshold is the
+                // rem-th match in index order: one scan instead of three
+                // more passes.
+                const uint64_t pre2 = sh_prefix;
+                const int64_t per = (N + kAllocBlock - 1) / kAllocBlock;
+                const int64_t i0 = (int64_t)threadIdx.x * per;
+                uint32_t cnt = 0;
+                for (int64_t i = i0; i < i0 + per && i < N; ++i) {
+                    const uint64_t k = keys[i];
+                    cnt += (k != 0 && (k & mask) == pre2);
+                }
+                uint32_t all;
+                int64_t before = block_exclusive_u32(cnt, &all);
+                const int64_t rem = sh_rem;
+                if (before < rem && before + cnt >= rem) {
+                    for (int64_t i = i0; i < i0 + per && i < N; ++i) {
+                        const uint64_t k = keys[i];
+                        if (k != 0 && (k & mask) == pre2 && ++before == rem) sh_prefix = k;
+                    }
+                }
+                mask = ~0ull;
+                __syncthreads();
+                break;
+            }
         }
         theta = sh_prefix;
         if (sh_done && mask != ~0ull) {
@@ -288,7 +333,7 @@ __global__ __launch_bounds__(kAllocBlock) void k_alloc_topk(SelectParams P)
     // verified prefix per request, row bases over (alloc + 1)
     const int per = (bs + (int)blockDim.x - 1) / (int)blockDim.x;
     const int r0 = threadIdx.x * per;
-    int64_t local = 0;
+    uint32_t local = 0;
     for (int r = r0; r < r0 + per && r < bs; ++r) {
         int cnt = 0;
 #pragma unroll
@@ -301,8 +346,8 @@ __global__ __launch_bounds__(kAllocBlock) void k_alloc_topk(SelectParams P)
         A.alloc_len[r] = cnt;
         local += cnt + 1;
     }
-    int64_t total;
-    int64_t base = block_exclusive_i64(local, &total);
+    uint32_t total;
+    int64_t base = block_exclusive_u32(local, &total);
     for (int r = r0; r < r0 + per && r < bs; ++r) {
         A.row_base[r] = base;
         base += A.alloc_len[r] + 1;

@@ -69,6 +69,22 @@ __device__ __forceinline__ T wave_sum(T v)
     return v;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts by 1, 2,
+// 4 and 8 within each row of 16 lanes, then the last lane of row 0 (and of
+// row 2) added to row 1 (and row 3), then the last lane of row 1 added to rows
+// 2 and 3.
+__device__ __forceinline__ uint32_t wave_incl_add(uint32_t v)
+{
+    int x = (int)v;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return (uint32_t)x;
+}
+
 __device__ __forceinline__ uint32_t wave_or(uint32_t v)
 {
 #pragma unroll
