@@ -43,6 +43,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-dense", action="store_true", help="skip the dense verify + draft measurement")
     p.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -123,6 +124,74 @@ def cpu_baseline(c, budget_s=12.0):
             break
     return {"value": n / el, "unit": "steps/s", "cores": 1, "kind": "oracle",
             "sample": f"{n} whole steps over the full BS-128 batch (single-threaded C oracle, fp64), {el:.1f} s"}
+
+
+def dense_headline(K, W, hip):
+    """The dense verify + draft step at BS 128: bf16 target [128, 8, V] and
+    draft [128, 7, V] rows with probabilistic slots at T = 1, the commit of the
+    emitted tokens, then the n-gram draft over the updated contexts.  K steps
+    captured in one HIP graph (checked against an eager step first)."""
+    import numpy as np
+    import torch
+    import draft_verification_spec_amd as S
+    from workloads import synth
+    dev = torch.device("cuda:0")
+    c = synth.dense_headline(ctx_extra=64)
+    BS, V, B = c["BS"], c["V"], c["B"]
+    g = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    target = synth.as_torch_bf16(c["target_bf16"]).to(dev).reshape(-1, V)
+    draft = synth.as_torch_bf16(c["draft_bf16"]).to(dev).reshape(-1, V)
+    rb, drb = g(np.arange(BS, dtype=np.int64) * (B + 1)), g(np.arange(BS, dtype=np.int64) * B)
+    tokens, flags = g(c["tokens"]), g(np.zeros((BS, B), np.uint8))
+    n_slots = g(np.full(BS, B, np.int32))
+    u_acc, u_smp = g(c["u_acc"]), g(c["u_smp"])
+    ctx, ctx_len = g(c["ctx"]), g(c["ctx_len"])
+    ctx_len_new = torch.empty_like(ctx_len)
+    stream = torch.cuda.Stream()
+    bufs = {"ws_v": torch.empty(1 << 26, dtype=torch.uint8, device=dev),
+            "ws_ng": torch.empty(1 << 20, dtype=torch.uint8, device=dev)}
+
+    def step():
+        out = S.spec_verify_chain(target, rb, tokens, n_slots, c["temperature"], u_accept=u_acc, u_sample=u_smp,
+                                  slot_flags=flags, draft_logits=draft, draft_row_base=drb, ctx=ctx,
+                                  ctx_len=ctx_len, ctx_len_out=ctx_len_new, out=bufs.get("vf"),
+                                  workspace=bufs["ws_v"])
+        d = S.spec_ngram_draft(ctx, ctx_len_new, c["n_min"], c["n_max"], c["max_draft"], c["copy_cap"],
+                               out=bufs.get("ng"), workspace=bufs["ws_ng"])
+        bufs.setdefault("vf", {k: v for k, v in out.items() if k != "out_flags"})
+        bufs.setdefault("ng", d)
+        return out, d
+
+    with torch.cuda.stream(stream):
+        step()
+        out, d = step()
+        torch.cuda.synchronize()
+        ref = [t.cpu().clone() for t in list(out.values()) + list(d)]
+        gK = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gK, stream=stream):
+            for _ in range(K):
+                step()
+        gK.replay()
+        torch.cuda.synchronize()
+        got = [t.cpu() for t in list(out.values()) + list(d)]
+        assert all(torch.equal(a, b) for a, b in zip(got, ref)), "dense graph replay differs from the eager step"
+        for _ in range(max(1, W // K)):
+            gK.replay()
+        torch.cuda.synchronize()
+        t0, t1 = hip.event(), hip.event()
+        hip.record(t0, stream.cuda_stream)
+        gK.replay()
+        hip.record(t1, stream.cuda_stream)
+        torch.cuda.synchronize()
+    ms = hip.ms(t0, t1)
+    rows_bytes = BS * (2 * B + 1) * V * 2
+    ctx_bytes = int(c["ctx_len"].sum()) * 4
+    step_bytes = rows_bytes + ctx_bytes
+    gbps = step_bytes / (ms / K * 1e-3) / 1e9
+    return {"workload": "dense verify + commit + n-gram draft: BS=128, V=151936, B=7, bf16 target [128,8,V] and "
+                        "draft [128,7,V], probabilistic slots, T=1.0, 8192-token contexts",
+            "steps_per_s": K / (ms * 1e-3), "ms_per_step": ms / K, "algorithmic_bytes": step_bytes,
+            "GBps": gbps, "frac": gbps / PEAK_HBM_GBPS}
 
 
 def main():
@@ -282,6 +351,8 @@ def main():
         "step_hbm": {"algorithmic_bytes": step_bytes, "GBps": step_bytes / (ms_step * 1e-3) / 1e9,
                      "frac": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS},
     }
+    if not args.no_dense:
+        res["dense_headline"] = dense_headline(K, W, hip)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(c)
     print(json.dumps(res), flush=True)

@@ -5,10 +5,12 @@
 //   * the query's trailing copy_cap tokens are staged in LDS;
 //   * each thread tests end positions j = t, t + 1024, ...: it loads the token
 //     at j for a batch of 16 positions (independent coalesced loads, one memory
-//     round trip per batch), and for the rare hits compares up to 4 tokens
-//     backwards itself; positions still matching after 4 go to a candidate list
-//     that whole waves extend 64 tokens per step with a ballot (compared up to
-//     min(j + 1, copy_cap));
+//     round trip per batch, the first issued before the suffix is staged); the
+//     batch (16,384 tokens) is staged in LDS as well, so that the backward
+//     comparisons read LDS.  For the rare hits a thread compares up to 4
+//     tokens backwards itself; positions still matching after 4 go to a
+//     candidate list that whole waves extend 64 tokens per step with a ballot
+//     (compared up to min(j + 1, copy_cap));
 //   * a match of length l >= n_min becomes the key (l << 32 | j), so "longest,
 //     then latest" is the largest key; the workgroup keeps the top two;
 //   * thread 0 derives (n, a, m, j) and the first lanes copy the draft.
@@ -66,6 +68,7 @@ __device__ __forceinline__ int32_t tok(const Text& x, int64_t p)
     return *(const int32_t*)(p < x.na ? pa : pb);
 }
 
+constexpr int kWin = kScanBlock * kBatch;   // tokens of one batch, staged in LDS (64 KB)
 constexpr int kPre = 4;          // tokens each thread compares before handing a match to its wave
 constexpr int kMaxCand = 2048;   // candidate list in LDS; overflow is extended by the thread itself
 
@@ -74,44 +77,62 @@ __global__ __launch_bounds__(kScanBlock) void k_ngram(NgramParams P)
     const int q = blockIdx.x;
     const Text x = query_text(P, q);
     __shared__ int32_t suf[SPEC_MAX_CAP];
+    __shared__ int32_t win[kWin];
     __shared__ Top2 sh[kScanBlock / kWave];
     __shared__ int32_t cand[kMaxCand];
     __shared__ int32_t n_cand;
     const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
     const int64_t jend = x.n - 1;                 // end positions j < n - 1
     const int64_t ns = x.n < P.cap ? x.n : P.cap;
+    // batch loads: kBatch independent loads per thread; past the end they
+    // read position jend - 1 (in bounds) and are masked off later
+    int32_t v[kBatch];
+    auto load_batch = [&](int64_t base) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t j = base + threadIdx.x + (int64_t)u * kScanBlock;
+            v[u] = tok(x, j < jend ? j : jend - 1);
+        }
+    };
+    if (jend > 0) load_batch(0);   // in flight while the suffix is staged
     for (int64_t i = threadIdx.x; i < ns; i += kScanBlock) suf[i] = tok(x, x.n - 1 - i);
     if (threadIdx.x == 0) n_cand = 0;
-    __syncthreads();
+    // token at position p < jend: from the staged window when it holds p
+    int64_t wbase = 0;
+    auto at = [&](int64_t p) -> int32_t { return (p >= wbase && p < wbase + kWin) ? win[p - wbase] : tok(x, p); };
     Top2 best{0, 0};
     if (jend > 0) {
         // phase 1: first kPre tokens per position, thread-private
-        const int32_t s0 = suf[0];
-        for (int64_t base = 0; base < jend; base += (int64_t)kScanBlock * kBatch) {
-            int32_t v[kBatch];
+        for (int64_t base = 0; base < jend; base += kWin) {
+            if (base > 0) {
+                __syncthreads();   // the previous window is no longer read
+                load_batch(base);
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) win[threadIdx.x + u * kScanBlock] = v[u];
+            wbase = base;
+            __syncthreads();
+            const int32_t s0 = suf[0];
+            uint32_t hits = 0;
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
                 const int64_t j = base + threadIdx.x + (int64_t)u * kScanBlock;
-                const int32_t t = tok(x, j < jend ? j : jend - 1);   // unconditional load, in bounds
-                v[u] = (j < jend) ? t : ~s0;
+                hits |= (uint32_t)(j < jend && v[u] == s0) << u;
             }
-            uint32_t hits = 0;
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) hits |= (uint32_t)(v[u] == s0) << u;
             while (hits) {
                 const int u = __builtin_ctz(hits);
                 hits &= hits - 1;
                 const int64_t j = base + threadIdx.x + (int64_t)u * kScanBlock;
                 const int64_t lim = (j + 1 < P.cap) ? j + 1 : P.cap;
                 int64_t l = 1;
-                while (l < lim && l < kPre && tok(x, j - l) == suf[l]) ++l;
+                while (l < lim && l < kPre && at(j - l) == suf[l]) ++l;
                 if (l == kPre && l < lim) {
                     const int c = atomicAdd(&n_cand, 1);
                     if (c < kMaxCand) {
                         cand[c] = (int32_t)j;
                         continue;
                     }
-                    while (l < lim && tok(x, j - l) == suf[l]) ++l;   // list full: extend here
+                    while (l < lim && at(j - l) == suf[l]) ++l;   // list full: extend here
                 }
                 if (l >= P.n_min) best = top2_insert(best, ((uint64_t)l << 32) | (uint64_t)j);
             }
@@ -126,7 +147,7 @@ __global__ __launch_bounds__(kScanBlock) void k_ngram(NgramParams P)
         int64_t l = kPre;
         for (;;) {
             const int64_t i = l + lane;
-            const bool eq = i < lim && tok(x, j - i) == suf[i];
+            const bool eq = i < lim && at(j - i) == suf[i];
             const uint64_t miss = ~__ballot(eq);
             if (miss == 0) {
                 l += kWave;

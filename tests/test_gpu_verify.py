@@ -53,6 +53,17 @@ def test_config0_probabilistic():
                 np.full(BS, B, np.int32), c["u_acc"], c["u_smp"], c["temperature"], c["draft"], np.arange(BS) * B)
 
 
+def test_dense_headline_bf16_probabilistic():
+    """The dense verify workload at full vocabulary: bf16 target [BS, 8, V]
+    and draft [BS, 7, V] rows, probabilistic slots, T = 1 (residuals drawn
+    from max(0, p - q) need both rows).  BS 32 keeps the oracle to seconds."""
+    c = synth.dense_headline(BS=32)
+    BS, B = c["BS"], c["B"]
+    verify_both(c["target_bf16"], np.arange(BS) * (B + 1), c["tokens"], np.zeros((BS, B), np.uint8),
+                np.full(BS, B, np.int32), c["u_acc"], c["u_smp"], c["temperature"], c["draft_bf16"],
+                np.arange(BS) * B, tag="dense bf16")
+
+
 @pytest.mark.parametrize("T", [0.0, 1.0])
 def test_config1_model_chain(T):
     c = synth.config1(temperature=T)
