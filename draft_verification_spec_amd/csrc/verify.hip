@@ -339,19 +339,38 @@ __device__ __forceinline__ int32_t target_rows(const StatsParams& P, int r)
     return c + P.cadd;
 }
 
-// Exclusive prefix of the per-request target rows over a workgroup of NT
-// threads; returns the total.  With `rb` the row bases are staged too, in the
-// same round trip.
-template <int NT = kBlock>
-__device__ int32_t row_prefix(const StatsParams& P, int32_t* pre, int64_t* rb = nullptr)
+// Draft rows of request r: one per probabilistic slot k < clamp(counts[r]).
+__device__ __forceinline__ int32_t draft_rows(const StatsParams& P, int r)
+{
+    const int b = target_rows(P, r) - P.cadd;
+    int32_t n = 0;
+    for (int k = 0; k < b; ++k) n += !(P.slot_flags[(int64_t)r * P.ld + k] & SPEC_SLOT_POINT_MASS);
+    return n;
+}
+
+// Rows the statistics pass reads for request r: its target rows, and with
+// DITEMS its draft rows as well.
+template <bool DITEMS>
+__device__ __forceinline__ int32_t pass_rows(const StatsParams& P, int r)
+{
+    if constexpr (DITEMS) return target_rows(P, r) + draft_rows(P, r);
+    else return target_rows(P, r);
+}
+
+// Exclusive prefix of the per-request rows over a workgroup of NT threads;
+// returns the total.  With `rb` (and `drb`) the target (and draft) row bases
+// are staged too, in the same round trip.
+template <int NT = kBlock, bool DITEMS = false>
+__device__ int32_t row_prefix(const StatsParams& P, int32_t* pre, int64_t* rb = nullptr, int64_t* drb = nullptr)
 {
     __shared__ int32_t sh[NT / kWave];
     const int per = (P.bs + NT - 1) / NT;
     const int r0 = threadIdx.x * per;
     int32_t local = 0;
     for (int r = r0; r < r0 + per && r < P.bs; ++r) {
-        local += target_rows(P, r);
+        local += pass_rows<DITEMS>(P, r);
         if (rb) rb[r] = P.row_base[r];
+        if (drb) drb[r] = P.drow_base[r];
     }
     const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
     int32_t inc = local;
@@ -370,7 +389,7 @@ __device__ int32_t row_prefix(const StatsParams& P, int32_t* pre, int64_t* rb = 
     int32_t run = before + inc - local;
     for (int r = r0; r < r0 + per && r < P.bs; ++r) {
         pre[r] = run;
-        run += target_rows(P, r);
+        run += pass_rows<DITEMS>(P, r);
     }
     if (threadIdx.x == 0) pre[P.bs] = tot;
     __syncthreads();
@@ -679,29 +698,50 @@ __device__ __forceinline__ int64_t uniform64(int64_t v)
 }
 
 struct PipeLoc {
-    int r, k, s;
+    int r, prow, s;  // request, partial row, chunk
+    int k;           // slot (target row k, or the draft row of slot k)
     int64_t row, drow;
     bool valid;      // a real item
-    bool row_ok;     // its target row lies in the logits
-    bool draft_row;  // it has a probabilistic draft row
+    bool isd;        // a draft row taken as an item of its own
+    bool row_ok;     // its row lies in the logits it reads
+    bool draft_row;  // (inline drafts) the target row's slot has a probabilistic draft row
     bool drow_ok;
 };
 
+// How the pass treats draft rows: none (greedy, trees), as items of their own
+// (same dtype as the target rows), or read beside each target chunk.
+constexpr int kDraftNone = 0;
+constexpr int kDraftItems = 1;
+constexpr int kDraftInline = 2;
+
 // Requires 16-byte aligned target rows, a vocabulary that is a multiple of one
-// vector, bs <= kRowBaseLds and at most kPipeMap verified rows.  The
-// workgroup is kGroups groups of 256 threads; each iteration the groups take
-// kGroups consecutive items.
-template <int DT, int DDT, int DVEC, bool GREEDY, bool DRAFT>
+// vector, bs <= kRowBaseLds and at most kPipeMap rows in the pass (with
+// kDraftItems, target and draft rows together, and aligned draft rows of the
+// target dtype).  The workgroup is kGroups groups of 256 threads; each
+// iteration the groups take kGroups consecutive items.
+template <int DT, int DDT, int DVEC, bool GREEDY, int DMODE>
 __global__ __launch_bounds__(kPipeBlock) void k_stats_pipe(StatsParams P)
 {
+    constexpr bool DITEMS = DMODE == kDraftItems;
     __shared__ int32_t lpre[kRowBaseLds + 1];
     __shared__ int64_t lrb[kRowBaseLds];
-    __shared__ int32_t lmap[kPipeMap];
+    __shared__ int64_t ldrb[DITEMS ? kRowBaseLds : 1];
+    __shared__ int32_t lmap[kPipeMap];   // request | partial row << 10 | draft << 20
     __shared__ GroupRed R;
     // wave-uniform, so that the loop control below is scalar
-    const int32_t total = __builtin_amdgcn_readfirstlane(row_prefix<kPipeBlock>(P, lpre, lrb));
-    for (int r = threadIdx.x; r < P.bs; r += kPipeBlock)
-        for (int q = lpre[r]; q < lpre[r + 1] && q < kPipeMap; ++q) lmap[q] = r;
+    const int32_t total =
+        __builtin_amdgcn_readfirstlane(row_prefix<kPipeBlock, DITEMS>(P, lpre, lrb, DITEMS ? ldrb : nullptr));
+    for (int r = threadIdx.x; r < P.bs; r += kPipeBlock) {
+        int q = lpre[r];
+        const int nt = target_rows(P, r);
+        for (int k = 0; k < nt && q < kPipeMap; ++k) lmap[q++] = r | (k << 10);
+        if constexpr (DITEMS) {
+            const int b = nt - P.cadd;
+            for (int k = 0; k < b && q < kPipeMap; ++k)
+                if (!(P.slot_flags[(int64_t)r * P.ld + k] & SPEC_SLOT_POINT_MASS))
+                    lmap[q++] = r | ((P.draft_base + k) << 10) | (1 << 20);
+        }
+    }
     __syncthreads();
     // at most kPipeMap rows of at most kMaxSplits chunks: 32-bit counts, so
     // that the loop control compiles to scalar compares
@@ -716,16 +756,24 @@ __global__ __launch_bounds__(kPipeBlock) void k_stats_pipe(StatsParams P)
         L.valid = item < items;
         const int32_t it = L.valid ? item : 0;
         const int32_t rowf = it / P.splits;
-        const int r = __builtin_amdgcn_readfirstlane(lmap[rowf]);
+        const int32_t w = __builtin_amdgcn_readfirstlane(lmap[rowf]);
+        const int r = w & 1023;
         L.r = r;
-        L.k = (int)(rowf - __builtin_amdgcn_readfirstlane(lpre[r]));
+        L.prow = (w >> 10) & 1023;
+        L.isd = DITEMS && ((w >> 20) & 1);
+        L.k = L.isd ? L.prow - P.draft_base : L.prow;
         L.s = (int)(it - rowf * P.splits);
-        L.row = uniform64(lrb[r]) + L.k;
-        L.row_ok = L.row >= 0 && L.row < P.n_rows;
+        if constexpr (DITEMS) {
+            L.row = uniform64(L.isd ? ldrb[r] : lrb[r]) + L.k;
+            L.row_ok = L.row >= 0 && L.row < (L.isd ? P.dn_rows : P.n_rows);
+        } else {
+            L.row = uniform64(lrb[r]) + L.k;
+            L.row_ok = L.row >= 0 && L.row < P.n_rows;
+        }
         L.draft_row = false;
         L.drow = 0;
         L.drow_ok = false;
-        if constexpr (DRAFT) {
+        if constexpr (DMODE == kDraftInline) {
             const int b = target_rows(P, r) - P.cadd;
             L.draft_row = L.valid && L.k < b && !(P.slot_flags[(int64_t)r * P.ld + L.k] & SPEC_SLOT_POINT_MASS);
             if (L.draft_row) L.drow = P.drow_base[r] + L.k;
@@ -736,16 +784,22 @@ __global__ __launch_bounds__(kPipeBlock) void k_stats_pipe(StatsParams P)
     auto issue = [&](const PipeLoc& L, uint4* raw) {
         const int64_t clo = (int64_t)L.s * P.chunk;
         const int64_t chi = (clo + P.chunk < P.vocab) ? clo + P.chunk : P.vocab;
-        group_issue<DT>(P.logits, P.stride, L.row, L.valid && L.row_ok, clo, chi, t, raw);
+        const void* base = P.logits;
+        int64_t stride = P.stride;
+        if constexpr (DITEMS) {
+            base = L.isd ? P.dlogits : P.logits;
+            stride = L.isd ? P.dstride : P.stride;
+        }
+        group_issue<DT>(base, stride, L.row, L.valid && L.row_ok, clo, chi, t, raw);
     };
     int par = 0;
     auto reduce = [&](const PipeLoc& L, const uint4* raw) {
         const int64_t clo = (int64_t)L.s * P.chunk;
         const int64_t chi = (clo + P.chunk < P.vocab) ? clo + P.chunk : P.vocab;
-        Partial* out = L.valid ? P.part + ((int64_t)L.r * P.NR + L.k) * P.splits + L.s : nullptr;
+        Partial* out = L.valid ? P.part + ((int64_t)L.r * P.NR + L.prow) * P.splits + L.s : nullptr;
         group_chunk<DT, GREEDY>(raw, clo, (L.valid && L.row_ok) ? chi : clo, P.c, R, par, g, t, out, !L.row_ok);
         par ^= 1;
-        if constexpr (DRAFT) {
+        if constexpr (DMODE == kDraftInline) {
             // every group takes this barrier too, with an empty range when it has no draft row
             const bool go = L.draft_row && L.drow_ok;
             Partial* dout = L.draft_row ? P.part + ((int64_t)L.r * P.NR + P.draft_base + L.k) * P.splits + L.s : nullptr;
@@ -1565,45 +1619,53 @@ static void launch_stats_g(const StatsParams& P, int dt, bool a, int ddt, bool d
     }
 }
 
-template <int DT, int DDT, bool DA, bool GREEDY, bool DRAFT>
+template <int DT, int DDT, bool DA, bool GREEDY, int DMODE>
 static void launch_pipe_t(const StatsParams& P, int64_t items, const StatsLaunch& L)
 {
     constexpr int DVEC = DA ? vec_of<DDT>() : 1;
-    auto kern = k_stats_pipe<DT, DDT, DVEC, GREEDY, DRAFT>;
+    auto kern = k_stats_pipe<DT, DDT, DVEC, GREEDY, DMODE>;
     launch_timed(kern, resident_grid((const void*)kern, kPipeBlock, (items + kGroups - 1) / kGroups), kPipeBlock, P,
                  L);
 }
 
 template <int DT, bool GREEDY>
-static void launch_pipe_d(const StatsParams& P, int ddt, bool da, bool draft, int64_t items, const StatsLaunch& L)
+static void launch_pipe_d(const StatsParams& P, int ddt, bool da, bool draft, bool ditems, int64_t items,
+                          const StatsLaunch& L)
 {
-    if (!draft) { launch_pipe_t<DT, SPEC_F32, false, GREEDY, false>(P, items, L); return; }
-    if (ddt == SPEC_F32) {
-        if (da) launch_pipe_t<DT, SPEC_F32, true, GREEDY, true>(P, items, L);
-        else launch_pipe_t<DT, SPEC_F32, false, GREEDY, true>(P, items, L);
-    } else {
-        if (da) launch_pipe_t<DT, SPEC_BF16, true, GREEDY, true>(P, items, L);
-        else launch_pipe_t<DT, SPEC_BF16, false, GREEDY, true>(P, items, L);
+    if (GREEDY || !draft) { launch_pipe_t<DT, SPEC_F32, false, GREEDY, kDraftNone>(P, items, L); return; }
+    if constexpr (!GREEDY) {
+        if (ditems) { launch_pipe_t<DT, DT, true, false, kDraftItems>(P, items, L); return; }
+        if (ddt == SPEC_F32) {
+            if (da) launch_pipe_t<DT, SPEC_F32, true, false, kDraftInline>(P, items, L);
+            else launch_pipe_t<DT, SPEC_F32, false, false, kDraftInline>(P, items, L);
+        } else {
+            if (da) launch_pipe_t<DT, SPEC_BF16, true, false, kDraftInline>(P, items, L);
+            else launch_pipe_t<DT, SPEC_BF16, false, false, kDraftInline>(P, items, L);
+        }
     }
 }
 
-// `items` bounds the work from above; `rows_max` bounds the target rows of one
-// request.
-static void launch_stats(StatsParams P, int dt, bool a, int ddt, bool da, bool draft, bool greedy, int64_t items,
-                         int rows_max, int32_t* gpre, const StatsLaunch& st)
+// `rows_max` bounds the target rows of one request and `drows_max` its draft
+// rows (chunk items are rows times splits).
+static void launch_stats(StatsParams P, int dt, bool a, int ddt, bool da, bool draft, bool greedy, int rows_max,
+                         int drows_max, const RowSplit& sp, int32_t* gpre, const StatsLaunch& st)
 {
     const int vec = dt == SPEC_F32 ? vec_of<SPEC_F32>() : vec_of<SPEC_BF16>();
     const bool pipe = a && P.vocab % vec == 0 && P.bs <= kRowBaseLds && (int64_t)P.bs * rows_max <= kPipeMap;
     if (pipe) {
+        // draft rows as items of their own when they read like target rows and fit the map
+        const bool ditems = draft && ddt == dt && da && (int64_t)P.bs * (rows_max + drows_max) <= kPipeMap;
+        const int64_t items = stats_items(P.bs, rows_max + (ditems ? drows_max : 0), sp);
         if (dt == SPEC_F32) {
-            if (greedy) launch_pipe_d<SPEC_F32, true>(P, ddt, da, draft, items, st);
-            else launch_pipe_d<SPEC_F32, false>(P, ddt, da, draft, items, st);
+            if (greedy) launch_pipe_d<SPEC_F32, true>(P, ddt, da, draft, ditems, items, st);
+            else launch_pipe_d<SPEC_F32, false>(P, ddt, da, draft, ditems, items, st);
         } else {
-            if (greedy) launch_pipe_d<SPEC_BF16, true>(P, ddt, da, draft, items, st);
-            else launch_pipe_d<SPEC_BF16, false>(P, ddt, da, draft, items, st);
+            if (greedy) launch_pipe_d<SPEC_BF16, true>(P, ddt, da, draft, ditems, items, st);
+            else launch_pipe_d<SPEC_BF16, false>(P, ddt, da, draft, ditems, items, st);
         }
         return;
     }
+    const int64_t items = stats_items(P.bs, rows_max, sp);
     const bool gp = P.bs > kMaxLdsPrefix;
     if (gp) {
         P.gprefix = gpre;
@@ -1682,9 +1744,8 @@ int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st)
     S.part = P.part; S.NR = NR; S.draft_base = a->ld + 1; S.gprefix = nullptr;
     const bool at = aligned16(a->logits, a->row_stride, a->dtype);
     const bool ad = draft && aligned16(a->draft_logits, a->draft_row_stride, a->draft_dtype);
-    const int64_t items = stats_items(a->bs, a->ld + 1, sp);
     const StatsLaunch L{st, (hipEvent_t)a->prof_begin, (hipEvent_t)a->prof_end};
-    launch_stats(S, a->dtype, at, a->draft_dtype, ad, draft, P.greedy, items, a->ld + 1, gpre, L);
+    launch_stats(S, a->dtype, at, a->draft_dtype, ad, draft, P.greedy, a->ld + 1, a->ld, sp, gpre, L);
     if (a->dtype == SPEC_F32) hipLaunchKernelGGL((k_decide<SPEC_F32>), dim3(a->bs), dim3(kBlock), 0, st, P);
     else hipLaunchKernelGGL((k_decide<SPEC_BF16>), dim3(a->bs), dim3(kBlock), 0, st, P);
     if (draft) {
@@ -1728,10 +1789,9 @@ int spec_verify_tree_launch(const spec_tree_verify_args* a, hipStream_t st)
     S.slot_flags = nullptr; S.ld = 0;
     S.bs = a->bs; S.vocab = a->vocab; S.chunk = sp.chunk; S.splits = sp.splits; S.c = 1.0f;
     S.part = P.part; S.NR = a->rows_max; S.draft_base = 0; S.gprefix = nullptr;
-    const int64_t items = stats_items(a->bs, a->rows_max, sp);
     const StatsLaunch L{st, (hipEvent_t)a->prof_begin, (hipEvent_t)a->prof_end};
-    launch_stats(S, a->dtype, aligned16(a->logits, a->row_stride, a->dtype), SPEC_F32, false, false, true, items,
-                 a->rows_max, gpre, L);
+    launch_stats(S, a->dtype, aligned16(a->logits, a->row_stride, a->dtype), SPEC_F32, false, false, true,
+                 a->rows_max, 0, sp, gpre, L);
     hipLaunchKernelGGL(k_tree_walk, dim3(a->bs), dim3(kWave), 0, st, P);
     return spec_record_hip_error(hipGetLastError());
 }
