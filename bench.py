@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verify+draft steps/sec at BS128, V=151936, B=7; achieved HBM GB/s vs peak"
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E, AMD's published figure
-STATS_KERNEL = "k_stats_pipe"   # the HBM-bound pass of the step
+STATS_KERNEL = "k_stats_flat"   # the HBM-bound pass of the step
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "verify_stats_bs128_v151936_bf16_counters.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "draft_verification_spec_amd", "csrc", f)
                   for f in ("verify.hip", "common.hpp")]
@@ -237,7 +237,7 @@ def main():
         out = S.spec_verify_chain(target, row_base, al["chain_tokens"], al["alloc_len"], c["temperature"],
                                   u_accept=u_acc, u_sample=u_smp, slot_flags=al["slot_flags"],
                                   out_flags=al["out_flags"], ctx=ctx, ctx_len=ctx_len, ctx_len_out=ctx_len_new,
-                                  out=bufs.get("vf"),
+                                  out=bufs.get("vf"), max_slots=c["budget"],
                                   workspace=bufs.get("ws_v"), prof_events=prof)
         bufs.setdefault("ng", (d, dl, f))
         bufs.setdefault("al", al)

@@ -69,7 +69,7 @@ class VerifyArgs(C.Structure):
     _fields_ = [("bs", i32), ("vocab", i32), ("temperature", f32), ("logits", vp), ("dtype", i32),
                 ("row_stride", i64), ("row_base", vp), ("n_logit_rows", i64), ("draft_logits", vp),
                 ("draft_dtype", i32), ("draft_row_stride", i64), ("draft_row_base", vp), ("n_draft_rows", i64),
-                ("tokens", vp), ("slot_flags", vp), ("ld", i32), ("n_slots", vp), ("u_accept", vp),
+                ("tokens", vp), ("slot_flags", vp), ("ld", i32), ("n_slots", vp), ("max_slots", i32), ("u_accept", vp),
                 ("u_sample", vp), ("out_tokens", vp), ("out_num", vp), ("out_accepted", vp), ("out_p", vp),
                 ("out_q", vp), ("out_flags", vp), ("ctx", vp), ("ctx_stride", i64), ("ctx_len", vp),
                 ("ctx_len_out", vp), ("ctx_cap", i32), ("prof_begin", vp), ("prof_end", vp), ("workspace", vp),
@@ -305,10 +305,11 @@ def spec_allocate_budget(mode="chain", **kw):
 def spec_verify_chain(logits, row_base, tokens, n_slots, temperature, u_accept=None, u_sample=None,
                       slot_flags=None, draft_logits=None, draft_row_base=None, out_flags=None,
                       ctx=None, ctx_len=None, ctx_cap=None, ctx_len_out=None, out=None, workspace=None,
-                      stream=None, prof_events=None):
+                      stream=None, prof_events=None, max_slots=0):
     """Rejection-sampling verification of one chain per request (optional commit into ctx).
     ``prof_events``: optional pair of raw hipEvent_t handles recorded around the
-    row-statistics pass."""
+    row-statistics pass.  ``max_slots``: optional bound of the total slots
+    (e.g. the allocation budget), which sizes the statistics grid."""
     lg = _rows2d(logits, "logits")
     _dev(row_base, torch.int64, "row_base", 1)
     _dev(tokens, torch.int32, "tokens", 2)
@@ -338,7 +339,8 @@ def spec_verify_chain(logits, row_base, tokens, n_slots, temperature, u_accept=N
     a = VerifyArgs(bs=bs, vocab=lg.shape[1], temperature=float(temperature), logits=_ptr(lg),
                    dtype=_logits_dtype(lg), row_stride=lg.stride(0), row_base=_ptr(row_base),
                    n_logit_rows=lg.shape[0], tokens=_ptr(tokens), slot_flags=_ptr(slot_flags), ld=ld,
-                   n_slots=_ptr(n_slots), u_accept=_ptr(u_accept), u_sample=_ptr(u_sample),
+                   n_slots=_ptr(n_slots), max_slots=int(max_slots), u_accept=_ptr(u_accept),
+                   u_sample=_ptr(u_sample),
                    **{k: _ptr(v) for k, v in out.items()})
     if dl is not None:
         a.draft_logits, a.draft_dtype, a.draft_row_stride = _ptr(dl), _logits_dtype(dl), dl.stride(0)

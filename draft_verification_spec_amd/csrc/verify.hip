@@ -330,6 +330,8 @@ struct StatsParams {
     int32_t NR;                   // partial rows per request
     int32_t draft_base;           // partial row of draft row k = draft_base + k
     const int32_t* gprefix;       // [bs + 1] row prefix in global memory (large batches) or null
+    int2* plan;                   // flat pass: the rows it reads (k_plan_rows) ...
+    int32_t* plan_count;          // ... and their count
 };
 
 __device__ __forceinline__ int32_t target_rows(const StatsParams& P, int r)
@@ -841,6 +843,110 @@ __global__ __launch_bounds__(kPipeBlock) void k_stats_pipe(StatsParams P)
 }
 
 // ---------------------------------------------------------------------------
+// the statistics pass, flat form
+// ---------------------------------------------------------------------------
+//
+// One (row, chunk) item per workgroup, items in row-major order over a row
+// list that one small workgroup writes first.  The hardware dispatcher hands
+// a compute unit its next workgroup as soon as one retires, which balances
+// the load better than any static deal of items over resident workgroups,
+// and each item costs a single scalar load of its plan entry before its
+// chunk loads go out.  The grid is sized by the host from a bound of the rows
+// (surplus workgroups exit at once; a short grid strides over the rest).
+
+// The rows of the pass in request order -- target rows 0..n-1, then with
+// DITEMS the draft rows of the probabilistic slots -- as (row in its logits
+// buffer or -1 outside it, partial row r * NR + prow with bit 31 set for a
+// draft row); then their count.  One workgroup.
+template <bool DITEMS>
+__global__ __launch_bounds__(kBlock) void k_plan_rows(StatsParams P)
+{
+    __shared__ int32_t wsum[kBlock / kWave];
+    const int t = threadIdx.x, lane = t % kWave, wid = t / kWave;
+    int32_t carry = 0;
+    for (int r0 = 0; r0 < P.bs; r0 += kBlock) {
+        const int r = r0 + t;
+        int32_t nt = 0;
+        uint32_t prob = 0;   // probabilistic slots among the first b (b <= 32)
+        int64_t tb = 0, db = 0;
+        if (r < P.bs) {
+            nt = target_rows(P, r);
+            tb = P.row_base[r];
+            if constexpr (DITEMS) {
+                db = P.drow_base[r];
+                // all of the request's flag loads in flight at once
+                const int b = nt - P.cadd;
+                const uint8_t* fl = P.slot_flags + (int64_t)r * P.ld;
+#pragma unroll
+                for (int k = 0; k < SPEC_MAX_DRAFT; ++k)
+                    if (k < b) prob |= (uint32_t)!(fl[k] & SPEC_SLOT_POINT_MASS) << k;
+            }
+        }
+        const int32_t n = nt + (int32_t)__popc(prob);
+        const int32_t inc = (int32_t)wave_incl_add((uint32_t)n);
+        if (lane == kWave - 1) wsum[wid] = inc;
+        __syncthreads();
+        int32_t q = carry + inc - n, tile = 0;
+        for (int w = 0; w < kBlock / kWave; ++w) {
+            if (w < wid) q += wsum[w];
+            tile += wsum[w];
+        }
+        if (r < P.bs) {
+            for (int k = 0; k < nt; ++k) {
+                const int64_t row = tb + k;
+                P.plan[q++] = make_int2(row >= 0 && row < P.n_rows ? (int32_t)row : -1, r * P.NR + k);
+            }
+            if constexpr (DITEMS) {
+                for (uint32_t m = prob; m; m &= m - 1) {
+                    const int k = __builtin_ctz(m);
+                    const int64_t row = db + k;
+                    P.plan[q++] = make_int2(row >= 0 && row < P.dn_rows ? (int32_t)row : -1,
+                                            (r * P.NR + P.draft_base + k) | (int32_t)0x80000000);
+                }
+            }
+        }
+        carry += tile;
+        __syncthreads();   // wsum is rewritten by the next tile
+    }
+    if (t == 0) *P.plan_count = carry;
+}
+
+// Requires 16-byte aligned rows, a vocabulary that is a multiple of one
+// vector and (with DITEMS) draft rows of the target dtype, also aligned.
+template <int DT, bool GREEDY, bool DITEMS>
+__global__ __launch_bounds__(kBlock) void k_stats_flat(StatsParams P)
+{
+    __shared__ GroupRed R;
+    const int t = threadIdx.x;
+    // the host sizes the plan for every row the pass can have, so the first
+    // entry is read before the count is known (both loads in one round trip)
+    const uint32_t splits = (uint32_t)P.splits;
+    uint32_t it = blockIdx.x;   // < 2^31, and so is the grid: it + grid does not wrap
+    int2 e = P.plan[it / splits];
+    const uint32_t items = (uint32_t)__builtin_amdgcn_readfirstlane(*P.plan_count) * splits;
+    int par = 0;
+    while (it < items) {
+        const uint32_t q = it / splits;
+        const int32_t s = (int32_t)(it - q * splits);
+        const int32_t row = __builtin_amdgcn_readfirstlane(e.x);
+        const int32_t pr = __builtin_amdgcn_readfirstlane(e.y);
+        const bool isd = DITEMS && pr < 0;
+        const void* base = isd ? P.dlogits : P.logits;
+        const int64_t stride = isd ? P.dstride : P.stride;
+        const bool ok = row >= 0;
+        const int64_t clo = (int64_t)s * P.chunk;
+        const int64_t chi = (clo + P.chunk < P.vocab) ? clo + P.chunk : P.vocab;
+        uint4 raw[kTile];
+        group_issue<DT>(base, stride, row, ok, clo, chi, t, raw);
+        Partial* out = P.part + (int64_t)(pr & 0x7FFFFFFF) * P.splits + s;
+        group_chunk<DT, GREEDY>(raw, clo, ok ? chi : clo, P.c, R, par, 0, t, out, !ok);
+        par ^= 1;
+        it += gridDim.x;
+        if (it < items) e = P.plan[it / splits];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // merging partials
 // ---------------------------------------------------------------------------
 
@@ -874,7 +980,9 @@ struct ChainParams {
     int32_t* ctx; int64_t ctx_stride; const int32_t* ctx_len; int32_t* ctx_len_out; int32_t ctx_cap;
     Partial* part; int32_t NR; int32_t splits; int64_t chunk;
     Dec* dec; double* sums;
+    uint32_t* done;             // [bs] chunk workgroups finished per request (reset by k_decide)
     bool t_aligned, d_aligned;  // rows allow 16-byte vector loads
+    bool coal;                  // same dtype, aligned rows, vocab a multiple of a vector
 };
 
 // Weight of token v: mode 1 = 2^(z*c - Ot) ; 3 = the same with y removed ; 2 = max(0, ep - eq * Zt/Zd).
@@ -1342,7 +1450,9 @@ __global__ __launch_bounds__(kBlock) void k_decide(ChainParams P)
             dd.mode = 2; dd.nacc = nacc; dd.y = d.y; dd.Ot = d.Ot; dd.Od = d.Od; dd.pad = 0;
             dd.row_t = d.row_t; dd.row_d = d.row_d; dd.Zt = sZ[nacc]; dd.Zd = sZ[ld + 1 + nacc];
             P.dec[r] = dd;
+            P.done[r] = 0;
         }
+        for (int j = t; j < P.splits; j += kBlock) P.sums[(int64_t)r * P.splits + j] = -1.0;   // not yet summed
     } else {
         if (t == 0 && P.dec) P.dec[r].mode = 0;
         if (d.mode == 1 || d.mode == 3) {
@@ -1397,8 +1507,44 @@ __device__ __forceinline__ Draw draw_of(const Dec& dd)
     return d;
 }
 
+// Sum of max(0, p - q) weights over the chunk [lo, hi) with the statistics
+// pass's load layout (vector u of thread t at lo + (t + 256 u) * VEC), for
+// target and draft rows of one dtype, 16-byte aligned, vocabulary a multiple
+// of a vector.
+template <int DT>
+__device__ double residual_sum_vec(const ChainParams& P, const Draw& d, int64_t lo, int64_t hi)
+{
+    constexpr int VEC = vec_of<DT>();
+    constexpr int64_t STEP = (int64_t)kBlock * VEC;
+    const int t = threadIdx.x;
+    uint4 rt[kTile], rd[kTile];
+    group_issue<DT>(P.logits, P.stride, d.row_t, true, lo, hi, t, rt);
+    group_issue<DT>(P.dlogits, P.dstride, d.row_d, true, lo, hi, t, rd);
+    const int64_t e = lo + (int64_t)t * VEC;
+    double acc = 0.0;
+#pragma unroll
+    for (int u = 0; u < kTile; ++u) {
+        float z[VEC], x[VEC];
+        unpack<DT>(rt[u], z);
+        unpack<DT>(rd[u], x);
+        double part = 0.0;
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            const double ep = (double)fast_exp2(fmaf(z[k], P.c, -d.Ot));
+            const double eq = (double)fast_exp2(fmaf(x[k], P.c, -d.Od));
+            const double v = ep - eq * d.ratio;
+            part += v > 0.0 ? v : 0.0;
+        }
+        acc += (e + u * STEP < hi) ? part : 0.0;
+    }
+    return block_sum_f64(acc);
+}
+
+// Residual draws max(0, p - q): workgroup (s, r) sums chunk s of request r;
+// the request's last workgroup to finish (its counter reaches the number of
+// chunks) draws from the chunk sums, writes the token and commits.
 template <int DTT, int DTD>
-__global__ __launch_bounds__(kBlock) void k_sample_part(ChainParams P)
+__global__ __launch_bounds__(kBlock) void k_sample(ChainParams P)
 {
     const int s = blockIdx.x, r = blockIdx.y;
     const Dec dd = P.dec[r];
@@ -1406,19 +1552,36 @@ __global__ __launch_bounds__(kBlock) void k_sample_part(ChainParams P)
     const Draw d = draw_of(dd);
     const int64_t lo = (int64_t)s * P.chunk;
     const int64_t hi = (lo + P.chunk < P.vocab) ? lo + P.chunk : P.vocab;
-    const double tot = range_sum<DTT, DTD>(P, d, lo, hi);
-    if (threadIdx.x == 0) P.sums[(int64_t)r * P.splits + s] = tot;
-}
-
-template <int DTT, int DTD>
-__global__ __launch_bounds__(kBlock) void k_sample_final(ChainParams P)
-{
-    const int r = blockIdx.x;
-    const Dec dd = P.dec[r];
-    if (dd.mode != 2) return;
-    const Draw d = draw_of(dd);
+    double tot;
+    if constexpr (DTT == DTD) {
+        if (P.coal) tot = residual_sum_vec<DTT>(P, d, lo, hi);
+        else tot = range_sum<DTT, DTD>(P, d, lo, hi);
+    } else {
+        tot = range_sum<DTT, DTD>(P, d, lo, hi);
+    }
+    // Publication without an L2-wide write-back per workgroup: the sum goes
+    // out as an agent-scope store (written through to the agent's coherence
+    // point), and the count that reports it is only issued once that store
+    // has completed.  The last workgroup reads the sums with agent-scope
+    // loads; k_decide filled them with -1 (a sum is >= 0), so a sum not yet
+    // visible is waited for (a bounded wait that in practice never spins).
+    __shared__ int32_t sLast;
+    if (threadIdx.x == 0) {
+        __hip_atomic_store(&P.sums[(int64_t)r * P.splits + s], tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+        const uint32_t before = __hip_atomic_fetch_add(&P.done[r], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sLast = before + 1 == (uint32_t)P.splits;
+    }
+    __syncthreads();
+    if (!sLast) return;
     __shared__ double sW[kMaxSplits];
-    for (int s = threadIdx.x; s < P.splits; s += kBlock) sW[s] = P.sums[(int64_t)r * P.splits + s];
+    for (int j = threadIdx.x; j < P.splits; j += kBlock) {
+        double* w = &P.sums[(int64_t)r * P.splits + j];
+        double v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int tries = 0; v < 0.0 && tries < (1 << 20); ++tries)
+            v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sW[j] = v;
+    }
     __syncthreads();
     uint32_t fl = 0;
     int32_t last = draw_from_chunks<DTT, DTD>(P, d, sW, (double)P.u_smp[r]);
@@ -1645,23 +1808,48 @@ static void launch_pipe_d(const StatsParams& P, int ddt, bool da, bool draft, bo
     }
 }
 
+template <int DT, bool GREEDY, bool DITEMS>
+static void launch_flat_t(const StatsParams& P, int64_t grid, const StatsLaunch& L)
+{
+    hipLaunchKernelGGL(k_plan_rows<DITEMS>, dim3(1), dim3(kBlock), 0, L.st, P);
+    launch_timed(k_stats_flat<DT, GREEDY, DITEMS>, (int)grid, kBlock, P, L);
+}
+
+template <int DT>
+static void launch_flat_d(const StatsParams& P, bool greedy, bool draft, int64_t grid, const StatsLaunch& L)
+{
+    if (greedy) launch_flat_t<DT, true, false>(P, grid, L);
+    else if (draft) launch_flat_t<DT, false, true>(P, grid, L);
+    else launch_flat_t<DT, false, false>(P, grid, L);
+}
+
 // `rows_max` bounds the target rows of one request and `drows_max` its draft
-// rows (chunk items are rows times splits).
+// rows; `rows_bound` bounds the rows of the whole pass (target and draft) and
+// only sizes the flat grid.  P.plan must hold bs * (rows_max + drows_max)
+// entries.
 static void launch_stats(StatsParams P, int dt, bool a, int ddt, bool da, bool draft, bool greedy, int rows_max,
-                         int drows_max, const RowSplit& sp, int32_t* gpre, const StatsLaunch& st)
+                         int drows_max, int64_t rows_bound, const RowSplit& sp, int32_t* gpre, const StatsLaunch& st)
 {
     const int vec = dt == SPEC_F32 ? vec_of<SPEC_F32>() : vec_of<SPEC_BF16>();
+    const int64_t cap = (int64_t)P.bs * (rows_max + drows_max);
+    const bool flat = a && P.vocab % vec == 0 && (!draft || (ddt == dt && da)) && cap * sp.splits < INT32_MAX &&
+                      (int64_t)P.bs * P.NR < INT32_MAX && P.n_rows <= INT32_MAX && P.dn_rows <= INT32_MAX;
+    if (flat) {
+        const int64_t rows = rows_bound < cap ? (rows_bound > 0 ? rows_bound : 1) : cap;
+        const int64_t grid = rows * sp.splits;
+        if (dt == SPEC_F32) launch_flat_d<SPEC_F32>(P, greedy, draft, grid, st);
+        else launch_flat_d<SPEC_BF16>(P, greedy, draft, grid, st);
+        return;
+    }
     const bool pipe = a && P.vocab % vec == 0 && P.bs <= kRowBaseLds && (int64_t)P.bs * rows_max <= kPipeMap;
     if (pipe) {
-        // draft rows as items of their own when they read like target rows and fit the map
-        const bool ditems = draft && ddt == dt && da && (int64_t)P.bs * (rows_max + drows_max) <= kPipeMap;
-        const int64_t items = stats_items(P.bs, rows_max + (ditems ? drows_max : 0), sp);
+        const int64_t items = stats_items(P.bs, rows_max, sp);
         if (dt == SPEC_F32) {
-            if (greedy) launch_pipe_d<SPEC_F32, true>(P, ddt, da, draft, ditems, items, st);
-            else launch_pipe_d<SPEC_F32, false>(P, ddt, da, draft, ditems, items, st);
+            if (greedy) launch_pipe_d<SPEC_F32, true>(P, ddt, da, draft, false, items, st);
+            else launch_pipe_d<SPEC_F32, false>(P, ddt, da, draft, false, items, st);
         } else {
-            if (greedy) launch_pipe_d<SPEC_BF16, true>(P, ddt, da, draft, ditems, items, st);
-            else launch_pipe_d<SPEC_BF16, false>(P, ddt, da, draft, ditems, items, st);
+            if (greedy) launch_pipe_d<SPEC_BF16, true>(P, ddt, da, draft, false, items, st);
+            else launch_pipe_d<SPEC_BF16, false>(P, ddt, da, draft, false, items, st);
         }
         return;
     }
@@ -1686,21 +1874,26 @@ using namespace spec;
 
 static int elem_bytes(int dt) { return dt == SPEC_F32 ? 4 : 2; }
 
-// Verify workspace: partials [bs, NR, splits] | decisions [bs] | chunk sums [bs, splits] | row prefix [bs + 1]
+// Row plan of the statistics pass: [rows] entries, then the count.
+static size_t plan_bytes(int64_t rows) { return align256((size_t)rows * sizeof(int2)) + align256(sizeof(int32_t)); }
+
+// Verify workspace: partials [bs, NR, splits] | decisions [bs] | chunk sums [bs, splits] | row prefix [bs + 1] |
+// row plan [bs * NR] | finished-chunk counters [bs]
 size_t spec_verify_chain_ws(int32_t bs, int32_t vocab, int32_t ld, int32_t dtype)
 {
     RowSplit sp = row_split(vocab, elem_bytes(dtype));
     const int NR = 2 * ld + 1;
     return align256((size_t)bs * NR * sp.splits * sizeof(Partial)) + align256((size_t)bs * sizeof(Dec)) +
-           align256((size_t)bs * sp.splits * sizeof(double)) + align256((size_t)(bs + 1) * sizeof(int32_t));
+           align256((size_t)bs * sp.splits * sizeof(double)) + align256((size_t)(bs + 1) * sizeof(int32_t)) +
+           plan_bytes((int64_t)bs * NR) + align256((size_t)bs * sizeof(uint32_t));
 }
 
-// Tree verify workspace: partials [bs, rows_max, splits] | row prefix [bs + 1]
+// Tree verify workspace: partials [bs, rows_max, splits] | row prefix [bs + 1] | row plan [bs * rows_max]
 size_t spec_verify_tree_ws(int32_t bs, int32_t vocab, int32_t rows_max, int32_t dtype)
 {
     RowSplit sp = row_split(vocab, elem_bytes(dtype));
     return align256((size_t)bs * rows_max * sp.splits * sizeof(Partial)) +
-           align256((size_t)(bs + 1) * sizeof(int32_t));
+           align256((size_t)(bs + 1) * sizeof(int32_t)) + plan_bytes((int64_t)bs * rows_max);
 }
 
 int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st)
@@ -1729,9 +1922,16 @@ int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st)
     P.sums = (double*)ws;
     ws += align256((size_t)a->bs * sp.splits * sizeof(double));
     int32_t* gpre = (int32_t*)ws;
+    ws += align256((size_t)(a->bs + 1) * sizeof(int32_t));
+    int2* plan = (int2*)ws;
+    int32_t* plan_count = (int32_t*)(ws + align256((size_t)a->bs * NR * sizeof(int2)));
+    ws += plan_bytes((int64_t)a->bs * NR);
+    P.done = (uint32_t*)ws;
     P.NR = NR; P.splits = sp.splits; P.chunk = sp.chunk;
     P.t_aligned = aligned16(a->logits, a->row_stride, a->dtype);
     P.d_aligned = P.dlogits && aligned16(a->draft_logits, a->draft_row_stride, a->draft_dtype);
+    P.coal = P.t_aligned && P.d_aligned && a->dtype == a->draft_dtype &&
+             a->vocab % (a->dtype == SPEC_F32 ? vec_of<SPEC_F32>() : vec_of<SPEC_BF16>()) == 0;
 
     const bool draft = !P.greedy && P.dlogits && a->slot_flags;
     StatsParams S;
@@ -1742,28 +1942,24 @@ int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st)
     S.slot_flags = a->slot_flags; S.ld = a->ld;
     S.bs = a->bs; S.vocab = a->vocab; S.chunk = sp.chunk; S.splits = sp.splits; S.c = P.c;
     S.part = P.part; S.NR = NR; S.draft_base = a->ld + 1; S.gprefix = nullptr;
+    S.plan = plan; S.plan_count = plan_count;
+    // rows of the pass: b + 1 target rows per request and a draft row per slot
+    const int64_t slots_all = (int64_t)a->bs * a->ld;
+    const int64_t slots = a->max_slots > 0 && a->max_slots < slots_all ? a->max_slots : slots_all;
     const bool at = aligned16(a->logits, a->row_stride, a->dtype);
     const bool ad = draft && aligned16(a->draft_logits, a->draft_row_stride, a->draft_dtype);
     const StatsLaunch L{st, (hipEvent_t)a->prof_begin, (hipEvent_t)a->prof_end};
-    launch_stats(S, a->dtype, at, a->draft_dtype, ad, draft, P.greedy, a->ld + 1, a->ld, sp, gpre, L);
+    launch_stats(S, a->dtype, at, a->draft_dtype, ad, draft, P.greedy, a->ld + 1, draft ? a->ld : 0,
+                 a->bs + slots + (draft ? slots : 0), sp, gpre, L);
     if (a->dtype == SPEC_F32) hipLaunchKernelGGL((k_decide<SPEC_F32>), dim3(a->bs), dim3(kBlock), 0, st, P);
     else hipLaunchKernelGGL((k_decide<SPEC_BF16>), dim3(a->bs), dim3(kBlock), 0, st, P);
     if (draft) {
         dim3 grid2(sp.splits, a->bs);
         const int tt = a->dtype, dd = a->draft_dtype;
-        if (tt == SPEC_F32 && dd == SPEC_F32) {
-            hipLaunchKernelGGL((k_sample_part<SPEC_F32, SPEC_F32>), grid2, dim3(kBlock), 0, st, P);
-            hipLaunchKernelGGL((k_sample_final<SPEC_F32, SPEC_F32>), dim3(a->bs), dim3(kBlock), 0, st, P);
-        } else if (tt == SPEC_F32) {
-            hipLaunchKernelGGL((k_sample_part<SPEC_F32, SPEC_BF16>), grid2, dim3(kBlock), 0, st, P);
-            hipLaunchKernelGGL((k_sample_final<SPEC_F32, SPEC_BF16>), dim3(a->bs), dim3(kBlock), 0, st, P);
-        } else if (dd == SPEC_F32) {
-            hipLaunchKernelGGL((k_sample_part<SPEC_BF16, SPEC_F32>), grid2, dim3(kBlock), 0, st, P);
-            hipLaunchKernelGGL((k_sample_final<SPEC_BF16, SPEC_F32>), dim3(a->bs), dim3(kBlock), 0, st, P);
-        } else {
-            hipLaunchKernelGGL((k_sample_part<SPEC_BF16, SPEC_BF16>), grid2, dim3(kBlock), 0, st, P);
-            hipLaunchKernelGGL((k_sample_final<SPEC_BF16, SPEC_BF16>), dim3(a->bs), dim3(kBlock), 0, st, P);
-        }
+        if (tt == SPEC_F32 && dd == SPEC_F32) hipLaunchKernelGGL((k_sample<SPEC_F32, SPEC_F32>), grid2, dim3(kBlock), 0, st, P);
+        else if (tt == SPEC_F32) hipLaunchKernelGGL((k_sample<SPEC_F32, SPEC_BF16>), grid2, dim3(kBlock), 0, st, P);
+        else if (dd == SPEC_F32) hipLaunchKernelGGL((k_sample<SPEC_BF16, SPEC_F32>), grid2, dim3(kBlock), 0, st, P);
+        else hipLaunchKernelGGL((k_sample<SPEC_BF16, SPEC_BF16>), grid2, dim3(kBlock), 0, st, P);
     }
     return spec_record_hip_error(hipGetLastError());
 }
@@ -1782,6 +1978,8 @@ int spec_verify_tree_launch(const spec_tree_verify_args* a, hipStream_t st)
     P.part = (Partial*)ws;
     P.splits = sp.splits;
     int32_t* gpre = (int32_t*)(ws + align256((size_t)a->bs * a->rows_max * sp.splits * sizeof(Partial)));
+    int2* plan = (int2*)((char*)gpre + align256((size_t)(a->bs + 1) * sizeof(int32_t)));
+    int32_t* plan_count = (int32_t*)((char*)plan + align256((size_t)a->bs * a->rows_max * sizeof(int2)));
     StatsParams S;
     S.logits = a->logits; S.stride = a->row_stride; S.row_base = a->row_base; S.n_rows = a->n_logit_rows;
     S.dlogits = nullptr; S.dstride = 0; S.drow_base = nullptr; S.dn_rows = 0;
@@ -1789,9 +1987,10 @@ int spec_verify_tree_launch(const spec_tree_verify_args* a, hipStream_t st)
     S.slot_flags = nullptr; S.ld = 0;
     S.bs = a->bs; S.vocab = a->vocab; S.chunk = sp.chunk; S.splits = sp.splits; S.c = 1.0f;
     S.part = P.part; S.NR = a->rows_max; S.draft_base = 0; S.gprefix = nullptr;
+    S.plan = plan; S.plan_count = plan_count;
     const StatsLaunch L{st, (hipEvent_t)a->prof_begin, (hipEvent_t)a->prof_end};
     launch_stats(S, a->dtype, aligned16(a->logits, a->row_stride, a->dtype), SPEC_F32, false, false, true,
-                 a->rows_max, 0, sp, gpre, L);
+                 a->rows_max, 0, (int64_t)a->bs * a->rows_max, sp, gpre, L);
     hipLaunchKernelGGL(k_tree_walk, dim3(a->bs), dim3(kWave), 0, st, P);
     return spec_record_hip_error(hipGetLastError());
 }

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 1
+#define SPEC_ABI_VERSION 2
 
 /* ---- return codes ---------------------------------------------------- */
 #define SPEC_OK          0
@@ -272,6 +272,10 @@ typedef struct spec_verify_args {
     const uint8_t* slot_flags;   /* device [bs, ld] or NULL = all point masses    */
     int32_t ld;                  /* 1 .. SPEC_MAX_DRAFT                           */
     const int32_t* n_slots;      /* device [bs]                                   */
+    int32_t max_slots;           /* optional host bound of the sum of the clamped
+                                    n_slots (e.g. the allocation budget); 0 = bs*ld.
+                                    Sizes the row-statistics grid only: a bound
+                                    that is too small costs speed, not results   */
     const float* u_accept;       /* device [bs, ld] uniforms in [0,1)             */
     const float* u_sample;       /* device [bs]                                   */
     int32_t* out_tokens;         /* device [bs, ld+1], -1 padded                  */

@@ -20,16 +20,18 @@ def as_logits(x):
     return dev(x)
 
 
-def verify_both(target, row_base, tokens, flags, n_slots, u_acc, u_smp, T, draft=None, drow_base=None, tag=""):
+def verify_both(target, row_base, tokens, flags, n_slots, u_acc, u_smp, T, draft=None, drow_base=None, tag="",
+                max_slots=0):
     import torch
     import draft_verification_spec_amd as S
     V = target.shape[-1]
     print(f"verify chain {tag}: bs {tokens.shape[0]} ld {tokens.shape[1]} V {V} T {T} "
-          f"dtype {target.dtype} draft {draft is not None}", flush=True)
+          f"dtype {target.dtype} draft {draft is not None} max_slots {max_slots}", flush=True)
     g = S.spec_verify_chain(as_logits(target).reshape(-1, V), dev(row_base.astype(np.int64)), dev(tokens),
                             dev(n_slots), T, u_accept=dev(u_acc), u_sample=dev(u_smp), slot_flags=dev(flags),
                             draft_logits=None if draft is None else as_logits(draft).reshape(-1, V),
-                            draft_row_base=None if draft is None else dev(drow_base.astype(np.int64)))
+                            draft_row_base=None if draft is None else dev(drow_base.astype(np.int64)),
+                            max_slots=max_slots)
     torch.cuda.synchronize()
     g = {k: host(v) for k, v in g.items()}
     o = O.verify_chain(target.reshape(-1, V), row_base, tokens, flags, n_slots, u_acc, u_smp, T,
@@ -89,7 +91,19 @@ def test_allocated_chains_bf16(cfg):
                            c["estimator"], c["lam"], c["budget"], "proposed", ld=15)
     BS = c["BS"]
     verify_both(c["target_bf16"], np.arange(BS) * 16, al["tokens"], al["slot_flags"], al["alloc_len"],
-                c["u_acc"][:, :15], c["u_smp"], c["temperature"], tag=f"c{cfg}")
+                c["u_acc"][:, :15], c["u_smp"], c["temperature"], tag=f"c{cfg}", max_slots=c["budget"])
+
+
+def test_mixed_dtypes_and_short_grid():
+    """A bf16 target with fp32 draft rows (drafts read beside their target
+    chunks), and a slot bound far below the real slots (the statistics grid
+    is then shorter than the work and its workgroups stride)."""
+    c = synth.config0()
+    BS, B = c["BS"], c["B"]
+    args = (np.arange(BS) * (B + 1), c["tokens"], np.zeros((BS, B), np.uint8), np.full(BS, B, np.int32),
+            c["u_acc"], c["u_smp"], c["temperature"])
+    verify_both(synth.f32_to_bf16_bits(c["target"]), *args, c["draft"], np.arange(BS) * B, tag="mixed")
+    verify_both(c["target"], *args, c["draft"], np.arange(BS) * B, tag="short grid", max_slots=1)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
