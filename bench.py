@@ -155,10 +155,11 @@ def dense_headline(K, W, hip):
         out = S.spec_verify_chain(target, rb, tokens, n_slots, c["temperature"], u_accept=u_acc, u_sample=u_smp,
                                   slot_flags=flags, draft_logits=draft, draft_row_base=drb, ctx=ctx,
                                   ctx_len=ctx_len, ctx_len_out=ctx_len_new, out=bufs.get("vf"),
-                                  workspace=bufs["ws_v"])
+                                  out_flags=bufs.get("vfl"), write_flags=True, workspace=bufs["ws_v"])
         d = S.spec_ngram_draft(ctx, ctx_len_new, c["n_min"], c["n_max"], c["max_draft"], c["copy_cap"],
                                out=bufs.get("ng"), workspace=bufs["ws_ng"])
         bufs.setdefault("vf", {k: v for k, v in out.items() if k != "out_flags"})
+        bufs.setdefault("vfl", out["out_flags"])
         bufs.setdefault("ng", d)
         return out, d
 

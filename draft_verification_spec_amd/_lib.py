@@ -71,9 +71,9 @@ class VerifyArgs(C.Structure):
                 ("draft_dtype", i32), ("draft_row_stride", i64), ("draft_row_base", vp), ("n_draft_rows", i64),
                 ("tokens", vp), ("slot_flags", vp), ("ld", i32), ("n_slots", vp), ("max_slots", i32), ("u_accept", vp),
                 ("u_sample", vp), ("out_tokens", vp), ("out_num", vp), ("out_accepted", vp), ("out_p", vp),
-                ("out_q", vp), ("out_flags", vp), ("ctx", vp), ("ctx_stride", i64), ("ctx_len", vp),
-                ("ctx_len_out", vp), ("ctx_cap", i32), ("prof_begin", vp), ("prof_end", vp), ("workspace", vp),
-                ("workspace_bytes", sz)]
+                ("out_q", vp), ("out_flags", vp), ("write_flags", i32), ("ctx", vp), ("ctx_stride", i64),
+                ("ctx_len", vp), ("ctx_len_out", vp), ("ctx_cap", i32), ("prof_begin", vp), ("prof_end", vp),
+                ("workspace", vp), ("workspace_bytes", sz)]
 
 
 class TreeVerifyArgs(C.Structure):
@@ -305,11 +305,13 @@ def spec_allocate_budget(mode="chain", **kw):
 def spec_verify_chain(logits, row_base, tokens, n_slots, temperature, u_accept=None, u_sample=None,
                       slot_flags=None, draft_logits=None, draft_row_base=None, out_flags=None,
                       ctx=None, ctx_len=None, ctx_cap=None, ctx_len_out=None, out=None, workspace=None,
-                      stream=None, prof_events=None, max_slots=0):
+                      stream=None, prof_events=None, max_slots=0, write_flags=False):
     """Rejection-sampling verification of one chain per request (optional commit into ctx).
     ``prof_events``: optional pair of raw hipEvent_t handles recorded around the
     row-statistics pass.  ``max_slots``: optional bound of the total slots
-    (e.g. the allocation budget), which sizes the statistics grid."""
+    (e.g. the allocation budget), which sizes the statistics grid.
+    ``write_flags``: out_flags receive this call's flags instead of OR-ing
+    them in (a new out_flags tensor is then not zeroed first)."""
     lg = _rows2d(logits, "logits")
     _dev(row_base, torch.int64, "row_base", 1)
     _dev(tokens, torch.int32, "tokens", 2)
@@ -334,14 +336,14 @@ def spec_verify_chain(logits, row_base, tokens, n_slots, temperature, u_accept=N
                    out_p=torch.empty((bs, ld), dtype=torch.float32, device=dev),
                    out_q=torch.empty((bs, ld), dtype=torch.float32, device=dev))
     if out_flags is None:
-        out_flags = torch.zeros(bs, dtype=torch.int32, device=dev)
+        out_flags = (torch.empty if write_flags else torch.zeros)(bs, dtype=torch.int32, device=dev)
     out["out_flags"] = out_flags
     a = VerifyArgs(bs=bs, vocab=lg.shape[1], temperature=float(temperature), logits=_ptr(lg),
                    dtype=_logits_dtype(lg), row_stride=lg.stride(0), row_base=_ptr(row_base),
                    n_logit_rows=lg.shape[0], tokens=_ptr(tokens), slot_flags=_ptr(slot_flags), ld=ld,
                    n_slots=_ptr(n_slots), max_slots=int(max_slots), u_accept=_ptr(u_accept),
                    u_sample=_ptr(u_sample),
-                   **{k: _ptr(v) for k, v in out.items()})
+                   write_flags=int(bool(write_flags)), **{k: _ptr(v) for k, v in out.items()})
     if dl is not None:
         a.draft_logits, a.draft_dtype, a.draft_row_stride = _ptr(dl), _logits_dtype(dl), dl.stride(0)
         a.draft_row_base, a.n_draft_rows = _ptr(draft_row_base), dl.shape[0]

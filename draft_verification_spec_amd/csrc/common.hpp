@@ -85,6 +85,29 @@ __device__ __forceinline__ uint32_t wave_incl_add(uint32_t v)
     return (uint32_t)x;
 }
 
+// One DPP step of the same pattern on a double (both halves moved alike;
+// lanes the step does not reach read 0).
+template <int CTRL, int ROWS, bool BOUND>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROWS, 0xf, BOUND);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROWS, 0xf, BOUND);
+    return __hiloint2double(hi, lo);
+}
+
+// Sum over the 64 lanes of a wave, valid in lane 63 (the inclusive scan
+// pattern of wave_incl_add, in fp64).
+__device__ __forceinline__ double wave_total_f64(double v)
+{
+    v += dpp_f64<0x111, 0xf, true>(v);
+    v += dpp_f64<0x112, 0xf, true>(v);
+    v += dpp_f64<0x114, 0xf, true>(v);
+    v += dpp_f64<0x118, 0xf, true>(v);
+    v += dpp_f64<0x142, 0xa, false>(v);
+    v += dpp_f64<0x143, 0xc, false>(v);
+    return v;
+}
+
 __device__ __forceinline__ uint32_t wave_or(uint32_t v)
 {
 #pragma unroll

@@ -10,21 +10,24 @@
 // Section 2.2).
 //
 // Data flow (one stream, no host synchronisation):
-//   k_stats      : the HBM-bound pass.  Work items are (verified row, chunk)
-//                  pairs flattened over the whole batch, so requests with many
-//                  rows do not serialise; a workgroup strides over items.  Per
-//                  item it streams a 32 KB chunk with 16-byte loads and keeps
-//                  an online maximum m and sum of 2^(z*c - m*c) (c = log2(e)/T;
-//                  pairwise fp32 within a 32-element tile, fp64 across tiles),
-//                  or at T = 0 the maximum and its first index.  Chain items
-//                  also stream the paired draft row of a probabilistic slot.
-//   k_decide     : one workgroup per request merges its chunk partials, finds
-//                  p(y), q(y) of every slot in parallel, the first rejection,
-//                  and -- for the bonus row and point-mass residuals -- draws
-//                  the token from the chunk sums it already has plus one chunk
-//                  rescan; then commits.
-//   k_sample_part, k_sample_final: only for probabilistic residuals
-//                  max(0, p - q), whose chunk sums need both rows.
+//   k_plan_rows  : one workgroup lists the rows the statistics pass reads
+//                  (request order: target rows, then the draft rows of
+//                  probabilistic slots) and counts them.
+//   k_stats_flat : the HBM-bound pass.  One workgroup per (row, chunk) item
+//                  of 16 KB, so the hardware dispatcher balances the load.
+//                  Per item: an online maximum m and sum of 2^(z*c - m*c)
+//                  (c = log2(e)/T; pairwise fp32 within a 32-element tile,
+//                  fp64 across tiles), or at T = 0 the maximum and its first
+//                  index.  (k_stats and k_stats_pipe cover rows that are not
+//                  16-byte aligned and draft rows of another dtype.)
+//   k_decide     : one 1024-thread workgroup per request merges its chunk
+//                  partials, finds p(y), q(y) of every slot in parallel and
+//                  the first rejection, then draws: the bonus row and
+//                  point-mass residuals from the chunk sums it already has
+//                  plus one chunk rescan; a probabilistic residual
+//                  max(0, p - q) by streaming its target and draft rows for
+//                  the chunk sums first.  Then it commits.
+#include <algorithm>
 #include <mutex>
 #include <utility>
 #include <vector>
@@ -42,16 +45,6 @@ struct Partial {
     float m;
     int32_t idx;
     double s;
-};
-
-struct Dec {
-    int32_t mode;   // 0: done; 2: draw from max(0, p - q) in the second pass
-    int32_t nacc;
-    int32_t y;
-    float Ot, Od;   // base-2 offsets of the target / draft rows
-    int32_t pad;
-    int64_t row_t, row_d;
-    double Zt, Zd;  // base-2 normalisers relative to the offsets
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -332,6 +325,8 @@ struct StatsParams {
     const int32_t* gprefix;       // [bs + 1] row prefix in global memory (large batches) or null
     int2* plan;                   // flat pass: the rows it reads (k_plan_rows) ...
     int32_t* plan_count;          // ... and their count
+    uint32_t* done;               // chain draws: counters k_plan_rows zeroes ([bs]) ...
+    double* sums;                 // ... and chunk sums it sets to -1 ([bs, splits]); or null
 };
 
 __device__ __forceinline__ int32_t target_rows(const StatsParams& P, int r)
@@ -874,12 +869,14 @@ __global__ __launch_bounds__(kBlock) void k_plan_rows(StatsParams P)
             tb = P.row_base[r];
             if constexpr (DITEMS) {
                 db = P.drow_base[r];
-                // all of the request's flag loads in flight at once
-                const int b = nt - P.cadd;
+                // every flag load of the request in flight at once, beside the
+                // count's (the bound is ld, not the count)
                 const uint8_t* fl = P.slot_flags + (int64_t)r * P.ld;
 #pragma unroll
                 for (int k = 0; k < SPEC_MAX_DRAFT; ++k)
-                    if (k < b) prob |= (uint32_t)!(fl[k] & SPEC_SLOT_POINT_MASS) << k;
+                    if (k < P.ld) prob |= (uint32_t)!(fl[k] & SPEC_SLOT_POINT_MASS) << k;
+                const int b = nt - P.cadd;   // slots k < b only
+                prob &= b >= 32 ? ~0u : ((1u << b) - 1u);
             }
         }
         const int32_t n = nt + (int32_t)__popc(prob);
@@ -909,6 +906,10 @@ __global__ __launch_bounds__(kBlock) void k_plan_rows(StatsParams P)
         __syncthreads();   // wsum is rewritten by the next tile
     }
     if (t == 0) *P.plan_count = carry;
+    if (P.done) {
+        for (int r = t; r < P.bs; r += kBlock) P.done[r] = 0;
+        for (int64_t i = t; i < (int64_t)P.bs * P.splits; i += kBlock) P.sums[i] = -1.0;
+    }
 }
 
 // Requires 16-byte aligned rows, a vocabulary that is a multiple of one
@@ -946,6 +947,67 @@ __global__ __launch_bounds__(kBlock) void k_stats_flat(StatsParams P)
     }
 }
 
+// The same pass without a row list, for batches whose rows per request are
+// close to their bound: grid ((TM + DM) * splits, bs) with TM the target rows
+// and DM the draft slots a request can have; workgroup (x, r) takes chunk
+// x % splits of request r's target row j = x / splits (j < TM) or of the
+// draft row of slot j - TM, and exits when the request has no such row.  Its
+// inputs are a handful of uniform words, read with scalar loads in one round
+// trip (the slot's flag byte through its aligned word).  Workgroup (0, r) also
+// resets request r's residual bookkeeping.
+template <int DT, bool GREEDY, bool DITEMS>
+__global__ __launch_bounds__(kBlock) void k_stats_rows(StatsParams P, int32_t TM)
+{
+    __shared__ GroupRed R;
+    const int t = threadIdx.x;
+    const int r = blockIdx.y;
+    const int32_t j = (int32_t)blockIdx.x / P.splits;
+    const int32_t s = (int32_t)blockIdx.x - j * P.splits;
+    const int k = j - TM;   // the draft slot, when j >= TM
+    // every input first, before any store (so that they stay scalar loads)
+    const int32_t nt = target_rows(P, r);
+    const int64_t tb = P.row_base[r];
+    int64_t db = 0;
+    uint32_t f = 0;
+    if constexpr (DITEMS) {
+        db = P.drow_base[r];
+        const int64_t off = (int64_t)r * P.ld + (k < 0 ? 0 : k);
+        f = *(const uint32_t*)(P.slot_flags + (off & ~(int64_t)3)) >> (8 * (off & 3));   // via the aligned word
+    }
+    // all of them in one round trip: without this the compiler sinks each
+    // load into the branch that uses it, one dependent trip after another
+    asm volatile("" : : "s"(nt), "s"(tb), "s"(db), "s"(f));
+    int64_t row;
+    int32_t prow;
+    bool isd = false;
+    bool live;
+    if (j < TM) {
+        live = j < nt;
+        row = tb + j;
+        prow = j;
+    } else {
+        live = DITEMS && k < nt - P.cadd && !(f & SPEC_SLOT_POINT_MASS);
+        row = db + k;
+        prow = P.draft_base + k;
+        isd = true;
+    }
+    if (live) {
+        const bool ok = row >= 0 && row < (isd ? P.dn_rows : P.n_rows);
+        const void* base = isd ? P.dlogits : P.logits;
+        const int64_t stride = isd ? P.dstride : P.stride;
+        const int64_t clo = (int64_t)s * P.chunk;
+        const int64_t chi = (clo + P.chunk < P.vocab) ? clo + P.chunk : P.vocab;
+        uint4 raw[kTile];
+        group_issue<DT>(base, stride, row, ok, clo, chi, t, raw);
+        Partial* out = P.part + ((int64_t)r * P.NR + prow) * P.splits + s;
+        group_chunk<DT, GREEDY>(raw, clo, ok ? chi : clo, P.c, R, 0, 0, t, out, !ok);
+    }
+    if (P.done && blockIdx.x == 0) {
+        if (t == 0) P.done[r] = 0;
+        for (int i = t; i < P.splits; i += kBlock) P.sums[(int64_t)r * P.splits + i] = -1.0;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // merging partials
 // ---------------------------------------------------------------------------
@@ -977,10 +1039,11 @@ struct ChainParams {
     const int32_t* tokens; const uint8_t* slot_flags; const int32_t* n_slots;
     const float* u_acc; const float* u_smp;
     int32_t* out_tokens; int32_t* out_num; int32_t* out_acc; float* out_p; float* out_q; uint32_t* out_flags;
+    int32_t write_flags;        // out_flags written (by the drawing workgroup) rather than OR-ed
     int32_t* ctx; int64_t ctx_stride; const int32_t* ctx_len; int32_t* ctx_len_out; int32_t ctx_cap;
     Partial* part; int32_t NR; int32_t splits; int64_t chunk;
-    Dec* dec; double* sums;
-    uint32_t* done;             // [bs] chunk workgroups finished per request (reset by k_decide)
+    double* sums;               // [bs, splits] residual chunk sums (-1 until written)
+    uint32_t* done;             // [bs] workgroups of a request done with their residual chunks
     bool t_aligned, d_aligned;  // rows allow 16-byte vector loads
     bool coal;                  // same dtype, aligned rows, vocab a multiple of a vector
 };
@@ -994,22 +1057,26 @@ struct Draw {
     double ratio;
 };
 
+// A decide workgroup is kDBlock threads.
+constexpr int kDBlock = 512;
+constexpr int kDWaves = kDBlock / kWave;
+
 __device__ double block_sum_f64(double v)
 {
-    __shared__ double sh[kBlock / kWave];
+    __shared__ double sh[kDWaves];
     v = wave_sum(v);
     const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
     __syncthreads();
     if (lane == 0) sh[wid] = v;
     __syncthreads();
     double tot = 0.0;
-    for (int w = 0; w < kBlock / kWave; ++w) tot += sh[w];
+    for (int w = 0; w < kDWaves; ++w) tot += sh[w];
     return tot;
 }
 
 __device__ double block_exclusive_f64(double v, double* total)
 {
-    __shared__ double sh[kBlock / kWave];
+    __shared__ double sh[kDWaves];
     const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
     double inc = v;
 #pragma unroll
@@ -1021,7 +1088,7 @@ __device__ double block_exclusive_f64(double v, double* total)
     if (lane == kWave - 1) sh[wid] = inc;
     __syncthreads();
     double before = 0.0, tot = 0.0;
-    for (int w = 0; w < kBlock / kWave; ++w) {
+    for (int w = 0; w < kDWaves; ++w) {
         if (w < wid) before += sh[w];
         tot += sh[w];
     }
@@ -1031,8 +1098,9 @@ __device__ double block_exclusive_f64(double v, double* total)
 
 // Each thread owns a contiguous segment of up to kSeg entries of a chunk and
 // loads it with 16-byte vectors when the rows allow (chunks are <= 8192
-// entries, so 256 threads x 32 entries cover one).
-constexpr int kSeg = 32;
+// entries, so kDBlock threads x kSeg entries cover one).
+constexpr int kSeg = 16;
+static_assert(kDBlock * kSeg * 2 == kChunkBytes, "a decide workgroup covers one bf16 chunk");
 
 template <int DT>
 __device__ __forceinline__ void load_seg(const void* row, bool aligned, int64_t a, int64_t b, float* v)
@@ -1105,8 +1173,8 @@ __device__ double range_sum(const ChainParams& P, const Draw& d, int64_t lo, int
 template <int DTT, int DTD>
 __device__ int64_t search_range(const ChainParams& P, const Draw& d, int64_t lo, int64_t hi, double t)
 {
-    __shared__ long long sh_found[kBlock / kWave];   // each wave's first candidate
-    __shared__ long long sh_lp[kBlock / kWave];
+    __shared__ long long sh_found[kDWaves];   // each wave's first candidate
+    __shared__ long long sh_lp[kDWaves];
     const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
     int64_t a, b;
     seg_of(lo, hi, &a, &b);
@@ -1146,7 +1214,7 @@ __device__ int64_t search_range(const ChainParams& P, const Draw& d, int64_t lo,
     }
     __syncthreads();
     int64_t res = -1;
-    for (int w2 = 0; w2 < kBlock / kWave; ++w2)
+    for (int w2 = 0; w2 < kDWaves; ++w2)
         if (sh_found[w2] >= 0 && (res < 0 || sh_found[w2] < res)) res = sh_found[w2];
     if (res < 0) {
         // rounding left t past the chunk: its last positive-weight token
@@ -1154,7 +1222,7 @@ __device__ int64_t search_range(const ChainParams& P, const Draw& d, int64_t lo,
         const long long m = wave_max(lp);
         if (lane == 0) sh_lp[wid] = m;
         __syncthreads();
-        for (int w2 = 0; w2 < kBlock / kWave; ++w2) res = sh_lp[w2] > res ? sh_lp[w2] : res;
+        for (int w2 = 0; w2 < kDWaves; ++w2) res = sh_lp[w2] > res ? sh_lp[w2] : res;
     }
     __syncthreads();
     return res;
@@ -1228,10 +1296,10 @@ __device__ int32_t draw_from_p(const ChainParams& P, const Draw& d, double* W, d
     return draw_from_chunks<DTT, DTD>(P, d1, W, u);
 }
 
-// Appends the emitted tokens (token `last` at position nacc) and writes the new length.
-__device__ void commit(const ChainParams& P, int r, int n, int nacc, int32_t last, uint32_t* fl)
+// Appends the emitted tokens (token `last` at position nacc) at ctx_len[r] = len
+// and writes the new length.
+__device__ void commit(const ChainParams& P, int r, int n, int nacc, int32_t last, int32_t len, uint32_t* fl)
 {
-    const int32_t len = P.ctx_len[r];
     const bool ok = (len >= 0 && len + n <= P.ctx_cap);
     if (ok) {
         for (int i = threadIdx.x; i < n; i += blockDim.x) {
@@ -1244,20 +1312,157 @@ __device__ void commit(const ChainParams& P, int r, int n, int nacc, int32_t las
     if (threadIdx.x == 0) P.ctx_len_out[r] = ok ? len + n : len;
 }
 
+// Residual chunk sums.  The K workgroups of a request split its chunks (chunk
+// c goes to workgroup c mod K) and stream the target and draft rows of the
+// draw: each thread takes kVecs 16-byte vectors of each chunk (vectors t and
+// t + kDBlock ...), kRound chunks per round, the next round's loads in flight
+// while a round is summed (two register buffers, the loop body twice).  A
+// chunk's sum goes out as an agent-scope store; once every store of the
+// workgroup has completed, one agent-scope count per workgroup reports them,
+// and the workgroup that brings the count to K draws.  Rows of one dtype,
+// 16-byte aligned, vocabulary a multiple of a vector.
+constexpr int kVecs = kChunkBytes / 16 / kDBlock;   // vectors per thread per chunk
+constexpr int kRound = 2;                           // chunks per round
+
+template <int DT>
+__device__ __forceinline__ void residual_issue(const char* tp, const char* dp, const ChainParams& P, int c0, int step,
+                                               int t, uint4* a, uint4* b)
+{
+    constexpr int VEC = vec_of<DT>();
+    constexpr int ES = DT == SPEC_F32 ? 4 : 2;
+#pragma unroll
+    for (int u = 0; u < kRound; ++u)
+#pragma unroll
+        for (int v = 0; v < kVecs; ++v) {
+            const int64_t e = (int64_t)(c0 + u * step) * P.chunk + (int64_t)(t + v * kDBlock) * VEC;
+            const int64_t eo = e < P.vocab ? e : 0;   // past the row: its first vector, unused
+            a[u * kVecs + v] = *(const uint4*)(tp + eo * ES);
+            b[u * kVecs + v] = *(const uint4*)(dp + eo * ES);
+        }
+    // keep the scheduler from hoisting the previous round's arithmetic above
+    // these loads (which would wait for everything in flight first)
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Sums one round (every register of both buffers is read) into the wave slots.
+template <int DT>
+__device__ __forceinline__ void residual_round(const ChainParams& P, const Draw& d, int c0, int step, int t,
+                                               const uint4* a, const uint4* b, double (*red)[kRound])
+{
+    constexpr int VEC = vec_of<DT>();
+    const int lane = t % kWave, wid = t / kWave;
+    double part[kRound];
+#pragma unroll
+    for (int u = 0; u < kRound; ++u) {
+        double acc = 0.0;
+#pragma unroll
+        for (int v = 0; v < kVecs; ++v) {
+            float z[VEC], x[VEC];
+            unpack<DT>(a[u * kVecs + v], z);
+            unpack<DT>(b[u * kVecs + v], x);
+            double w = 0.0;
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                const double ep = (double)fast_exp2(fmaf(z[k], P.c, -d.Ot));
+                const double eq = (double)fast_exp2(fmaf(x[k], P.c, -d.Od));
+                w += fmax(ep - eq * d.ratio, 0.0);
+            }
+            const int64_t e = (int64_t)(c0 + u * step) * P.chunk + (int64_t)(t + v * kDBlock) * VEC;
+            acc += e < P.vocab ? w : 0.0;
+        }
+        part[u] = wave_total_f64(acc);
+    }
+    if (lane == kWave - 1)
+#pragma unroll
+        for (int u = 0; u < kRound; ++u) red[wid][u] = part[u];
+}
+
+// This workgroup's chunk sums (chunks kk, kk + K, ...) of request r, published;
+// returns true in the workgroup that completes the request's count.
+template <int DT>
+__device__ bool residual_publish(const ChainParams& P, const Draw& d, int r, int kk, int K)
+{
+    static_assert(kVecs * kDBlock * 16 == kChunkBytes, "whole vectors per thread per chunk");
+    __shared__ double red[2][kDWaves][kRound];
+    __shared__ int32_t sLast;
+    const int t = threadIdx.x;
+    const char* tp = (const char*)row_ptr<DT>(P.logits, d.row_t, P.stride);
+    const char* dp = (const char*)row_ptr<DT>(P.dlogits, d.row_d, P.dstride);
+    const int n = kk < P.splits ? (P.splits - kk + K - 1) / K : 0;   // chunks of this workgroup
+    const int rounds = (n + kRound - 1) / kRound;
+    const int stride = K * kRound;                                    // chunk step between rounds
+    // round i's sums from the wave slots, after the barrier that follows it
+    auto finish = [&](int i, int par) {
+        const int j = i * kRound + t;
+        if (t < kRound && j < n) {
+            double sum = 0.0;
+            for (int w = 0; w < kDWaves; ++w) sum += red[par][w][t];
+            __hip_atomic_store(&P.sums[(int64_t)r * P.splits + kk + j * K], sum, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
+    uint4 a0[kRound * kVecs], b0[kRound * kVecs], a1[kRound * kVecs], b1[kRound * kVecs];
+    residual_issue<DT>(tp, dp, P, kk, K, t, a0, b0);
+    // rounds 2i (buffers 0) and 2i + 1 (buffers 1); red[i & 1] alternates so
+    // one barrier per round suffices (chunks past the row read first vectors)
+    for (int i = 0; i < rounds; i += 2) {
+        const int c0 = kk + i * stride, c1 = c0 + stride;
+        residual_issue<DT>(tp, dp, P, c1, K, t, a1, b1);
+        residual_round<DT>(P, d, c0, K, t, a0, b0, red[0]);
+        __syncthreads();
+        finish(i, 0);
+        residual_issue<DT>(tp, dp, P, c1 + stride, K, t, a0, b0);
+        residual_round<DT>(P, d, c1, K, t, a1, b1, red[1]);
+        __syncthreads();
+        finish(i + 1, 1);
+    }
+    // every sum store of the workgroup completes before the count reports them
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t == 0) {
+        const uint32_t before = __hip_atomic_fetch_add(&P.done[r], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sLast = before + 1 == (uint32_t)K;
+    }
+    __syncthreads();
+    return sLast != 0;
+}
+
+// The request's chunk sums into W (the drawing workgroup): a sum still -1 is
+// not yet visible and is read again (a bounded wait that in practice never
+// spins).
+__device__ void residual_collect(const ChainParams& P, int r, double* W)
+{
+    for (int j = threadIdx.x; j < P.splits; j += kDBlock) {
+        double* w = &P.sums[(int64_t)r * P.splits + j];
+        double v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int tries = 0; v < 0.0 && tries < (1 << 20); ++tries)
+            v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        W[j] = v;
+    }
+    __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
-// decide (+ draw for bonus rows and point-mass residuals, + commit)
+// decide, draw, commit: one workgroup per request
 // ---------------------------------------------------------------------------
 
 constexpr int kMaxPartsLds = 2048;   // partials of one request staged in LDS (32 KB)
 
 constexpr int kMergeLanes = 8;   // lanes that merge one row's chunk partials
 
-template <int DTT>
-__global__ __launch_bounds__(kBlock) void k_decide(ChainParams P)
+// Grid (bs, K): the K workgroups of a request all merge its partials and find
+// the first rejection (cheap, and identical); workgroup 0 writes the slot
+// outputs and draws and commits, except that a probabilistic residual is
+// summed by all K and drawn by the last of them to finish.
+template <int DTT, int DTD>
+__global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
 {
     const int r = blockIdx.x;
+    const int kk = blockIdx.y, K = gridDim.y;
+    const bool lead = kk == 0;
     const int t = threadIdx.x;
     const int ld = P.ld;
+    const int32_t len0 = P.ctx ? P.ctx_len[r] : 0;   // loaded early, used by the commit
     __shared__ Partial sp[kMaxPartsLds];
     __shared__ float sO[2 * SPEC_MAX_DRAFT + 1];
     __shared__ double sZ[2 * SPEC_MAX_DRAFT + 1];
@@ -1302,7 +1507,7 @@ __global__ __launch_bounds__(kBlock) void k_decide(ChainParams P)
     const bool staged = nparts <= kMaxPartsLds;
     const Partial* gp = P.part + (int64_t)r * nparts;
     if (staged)
-        for (int i = t; i < nparts; i += kBlock) {
+        for (int i = t; i < nparts; i += kDBlock) {
             const int row = i / P.splits, s = i - row * P.splits;
             sp[s * P.NR + row] = gp[i];
         }
@@ -1313,7 +1518,7 @@ __global__ __launch_bounds__(kBlock) void k_decide(ChainParams P)
     // Rows: target 0..b, draft ld+1 .. ld+b (probabilistic slots, T > 0).
     // kMergeLanes lanes merge one row: each folds every kMergeLanes-th chunk
     // partial online, then the lanes combine pairwise.
-    for (int row0 = 0; row0 < P.NR; row0 += kBlock / kMergeLanes) {
+    for (int row0 = 0; row0 < P.NR; row0 += kDBlock / kMergeLanes) {
         const int row = row0 + t / kMergeLanes, j = t % kMergeLanes;
         bool is_row = row < P.NR && row <= b;
         if (!is_row && row < P.NR && !P.greedy && P.dlogits && row >= ld + 1 && row <= ld + b)
@@ -1391,11 +1596,11 @@ __global__ __launch_bounds__(kBlock) void k_decide(ChainParams P)
             const double rho = q > 0.0 ? p / q : 0.0;
             acc = (double)uacc < rho;
         }
-        if (P.out_p) P.out_p[off] = (float)p;
-        if (P.out_q) P.out_q[off] = (float)q;
+        if (P.out_p && lead) P.out_p[off] = (float)p;
+        if (P.out_q && lead) P.out_q[off] = (float)q;
         rejected = !acc;
         slot_fl = fl;
-    } else if (t < ld) {
+    } else if (t < ld && lead) {
         const int64_t off = (int64_t)r * ld + t;
         if (P.out_p) P.out_p[off] = 0.0f;
         if (P.out_q) P.out_q[off] = 0.0f;
@@ -1413,17 +1618,18 @@ __global__ __launch_bounds__(kBlock) void k_decide(ChainParams P)
     __syncthreads();
     const uint64_t rej = sRej;
     const int nacc = rej ? (int)__builtin_ctzll(rej) : b;
-    if (t <= ld) P.out_tokens[(int64_t)r * (ld + 1) + t] = (t < nacc) ? y : -1;
+    if (lead && t <= ld) P.out_tokens[(int64_t)r * (ld + 1) + t] = (t < nacc) ? y : -1;
     if (t == 0) {
-        P.out_num[r] = nacc + 1;
-        P.out_acc[r] = nacc;
+        if (lead) {
+            P.out_num[r] = nacc + 1;
+            P.out_acc[r] = nacc;
+        }
         if (nacc == b && !sOk[b]) sFlags |= SPEC_FLAG_BAD_LOGITS;
     }
     // what to draw
     Draw d;
     d.mode = 0; d.y = -1; d.Ot = d.Od = 0.0f; d.row_t = row_base + nacc; d.row_d = -1; d.ratio = 1.0;
     int32_t last = -1;
-    bool deferred = false;
     if (P.greedy) {
         last = sOk[nacc] ? sArg[nacc] : -1;
         if (last == 0x7FFFFFFF) last = -1;
@@ -1443,22 +1649,34 @@ __global__ __launch_bounds__(kBlock) void k_decide(ChainParams P)
             } else d.mode = 1;   // unusable draft row (flagged): fall back to p
         }
     }
-    if (d.mode == 2) {
-        deferred = true;
-        if (t == 0) {
-            Dec dd;
-            dd.mode = 2; dd.nacc = nacc; dd.y = d.y; dd.Ot = d.Ot; dd.Od = d.Od; dd.pad = 0;
-            dd.row_t = d.row_t; dd.row_d = d.row_d; dd.Zt = sZ[nacc]; dd.Zd = sZ[ld + 1 + nacc];
-            P.dec[r] = dd;
-            P.done[r] = 0;
+    // which workgroup draws: the lead, or for a streamed residual the last
+    // of the K to finish its chunks
+    bool streamed = false;
+    if constexpr (DTT == DTD) streamed = d.mode == 2 && P.coal;
+    if (streamed) {
+        const bool drawer = residual_publish<DTT>(P, d, r, kk, K);
+        if (!drawer) {
+            // the drawing workgroup reports the request's flags (it has them all)
+            return;
         }
-        for (int j = t; j < P.splits; j += kBlock) P.sums[(int64_t)r * P.splits + j] = -1.0;   // not yet summed
-    } else {
-        if (t == 0 && P.dec) P.dec[r].mode = 0;
-        if (d.mode == 1 || d.mode == 3) {
+        residual_collect(P, r, sW);
+    } else if (!lead) {
+        return;
+    }
+    if (d.mode != 0) {
+        if (d.mode == 2 && !streamed) {
+            // residual max(0, p - q) of rows that do not take the vector path: chunk by chunk
+            for (int s = 0; s < P.splits; ++s) {
+                const int64_t lo = (int64_t)s * P.chunk;
+                const int64_t hi = (lo + P.chunk < P.vocab) ? lo + P.chunk : P.vocab;
+                const double x = range_sum<DTT, DTD>(P, d, lo, hi);
+                if (t == 0) sW[s] = x;
+            }
+            __syncthreads();
+        } else if (d.mode != 2) {
             // chunk sums of the row from its partials; the y chunk is rescanned without y
             const Partial* row = rp + nacc * rr;
-            for (int s = t; s < P.splits; s += kBlock) {
+            for (int s = t; s < P.splits; s += kDBlock) {
                 const Partial q = row[s * rs];
                 sW[s] = (q.m == -INFINITY) ? 0.0 : q.s * (double)fast_exp2((float)((double)(q.m * P.c) - (double)d.Ot));
             }
@@ -1467,138 +1685,35 @@ __global__ __launch_bounds__(kBlock) void k_decide(ChainParams P)
                 const int sy = (int)(d.y / P.chunk);
                 const int64_t lo = (int64_t)sy * P.chunk;
                 const int64_t hi = (lo + P.chunk < P.vocab) ? lo + P.chunk : P.vocab;
-                const double wy = range_sum<DTT, DTT>(P, d, lo, hi);
+                const double wy = range_sum<DTT, DTD>(P, d, lo, hi);
                 if (t == 0) sW[sy] = wy;
             }
             __syncthreads();
-            last = draw_from_chunks<DTT, DTT>(P, d, sW, (double)P.u_smp[r]);
-            if (last < 0) {
-                // the residual had no mass (not reachable in exact arithmetic): draw from p
-                if (t == 0) sFlags |= SPEC_FLAG_RESIDUAL_ZERO;
-                last = draw_from_p<DTT, DTT>(P, d, sW, (double)P.u_smp[r]);
-            }
-        } else if (!P.greedy) {
-            if (t == 0) sFlags |= SPEC_FLAG_BAD_LOGITS;
         }
-        if (t == 0) P.out_tokens[(int64_t)r * (ld + 1) + nacc] = last;
+        last = draw_from_chunks<DTT, DTD>(P, d, sW, (double)P.u_smp[r]);
+        if (last < 0) {
+            // the residual had no mass (not reachable in exact arithmetic): draw from p
+            if (t == 0) sFlags |= SPEC_FLAG_RESIDUAL_ZERO;
+            last = draw_from_p<DTT, DTD>(P, d, sW, (double)P.u_smp[r]);
+        }
+    } else if (!P.greedy) {
+        if (t == 0) sFlags |= SPEC_FLAG_BAD_LOGITS;
     }
+    if (t == 0) P.out_tokens[(int64_t)r * (ld + 1) + nacc] = last;
     __syncthreads();
     uint32_t fl = sFlags;
-    if (!deferred && P.ctx) {
+    if (P.ctx) {
         __shared__ uint32_t sCommit;
         if (t == 0) sCommit = 0;
         __syncthreads();
-        commit(P, r, nacc + 1, nacc, last, &sCommit);
+        commit(P, r, nacc + 1, nacc, last, len0, &sCommit);
         __syncthreads();
         fl |= sCommit;
     }
-    if (t == 0 && fl) atomicOr(&P.out_flags[r], fl);
-}
-
-// ---------------------------------------------------------------------------
-// second pass for probabilistic residuals max(0, p - q)
-// ---------------------------------------------------------------------------
-
-__device__ __forceinline__ Draw draw_of(const Dec& dd)
-{
-    Draw d;
-    d.mode = dd.mode; d.y = dd.y; d.Ot = dd.Ot; d.Od = dd.Od; d.row_t = dd.row_t; d.row_d = dd.row_d;
-    d.ratio = dd.Zt / dd.Zd;
-    return d;
-}
-
-// Sum of max(0, p - q) weights over the chunk [lo, hi) with the statistics
-// pass's load layout (vector u of thread t at lo + (t + 256 u) * VEC), for
-// target and draft rows of one dtype, 16-byte aligned, vocabulary a multiple
-// of a vector.
-template <int DT>
-__device__ double residual_sum_vec(const ChainParams& P, const Draw& d, int64_t lo, int64_t hi)
-{
-    constexpr int VEC = vec_of<DT>();
-    constexpr int64_t STEP = (int64_t)kBlock * VEC;
-    const int t = threadIdx.x;
-    uint4 rt[kTile], rd[kTile];
-    group_issue<DT>(P.logits, P.stride, d.row_t, true, lo, hi, t, rt);
-    group_issue<DT>(P.dlogits, P.dstride, d.row_d, true, lo, hi, t, rd);
-    const int64_t e = lo + (int64_t)t * VEC;
-    double acc = 0.0;
-#pragma unroll
-    for (int u = 0; u < kTile; ++u) {
-        float z[VEC], x[VEC];
-        unpack<DT>(rt[u], z);
-        unpack<DT>(rd[u], x);
-        double part = 0.0;
-#pragma unroll
-        for (int k = 0; k < VEC; ++k) {
-            const double ep = (double)fast_exp2(fmaf(z[k], P.c, -d.Ot));
-            const double eq = (double)fast_exp2(fmaf(x[k], P.c, -d.Od));
-            const double v = ep - eq * d.ratio;
-            part += v > 0.0 ? v : 0.0;
-        }
-        acc += (e + u * STEP < hi) ? part : 0.0;
+    if (t == 0) {
+        if (P.write_flags) P.out_flags[r] = fl;
+        else if (fl) atomicOr(&P.out_flags[r], fl);
     }
-    return block_sum_f64(acc);
-}
-
-// Residual draws max(0, p - q): workgroup (s, r) sums chunk s of request r;
-// the request's last workgroup to finish (its counter reaches the number of
-// chunks) draws from the chunk sums, writes the token and commits.
-template <int DTT, int DTD>
-__global__ __launch_bounds__(kBlock) void k_sample(ChainParams P)
-{
-    const int s = blockIdx.x, r = blockIdx.y;
-    const Dec dd = P.dec[r];
-    if (dd.mode != 2) return;
-    const Draw d = draw_of(dd);
-    const int64_t lo = (int64_t)s * P.chunk;
-    const int64_t hi = (lo + P.chunk < P.vocab) ? lo + P.chunk : P.vocab;
-    double tot;
-    if constexpr (DTT == DTD) {
-        if (P.coal) tot = residual_sum_vec<DTT>(P, d, lo, hi);
-        else tot = range_sum<DTT, DTD>(P, d, lo, hi);
-    } else {
-        tot = range_sum<DTT, DTD>(P, d, lo, hi);
-    }
-    // Publication without an L2-wide write-back per workgroup: the sum goes
-    // out as an agent-scope store (written through to the agent's coherence
-    // point), and the count that reports it is only issued once that store
-    // has completed.  The last workgroup reads the sums with agent-scope
-    // loads; k_decide filled them with -1 (a sum is >= 0), so a sum not yet
-    // visible is waited for (a bounded wait that in practice never spins).
-    __shared__ int32_t sLast;
-    if (threadIdx.x == 0) {
-        __hip_atomic_store(&P.sums[(int64_t)r * P.splits + s], tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_s_waitcnt(0);
-        const uint32_t before = __hip_atomic_fetch_add(&P.done[r], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sLast = before + 1 == (uint32_t)P.splits;
-    }
-    __syncthreads();
-    if (!sLast) return;
-    __shared__ double sW[kMaxSplits];
-    for (int j = threadIdx.x; j < P.splits; j += kBlock) {
-        double* w = &P.sums[(int64_t)r * P.splits + j];
-        double v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (int tries = 0; v < 0.0 && tries < (1 << 20); ++tries)
-            v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sW[j] = v;
-    }
-    __syncthreads();
-    uint32_t fl = 0;
-    int32_t last = draw_from_chunks<DTT, DTD>(P, d, sW, (double)P.u_smp[r]);
-    if (last < 0) {
-        fl |= SPEC_FLAG_RESIDUAL_ZERO;
-        last = draw_from_p<DTT, DTD>(P, d, sW, (double)P.u_smp[r]);
-    }
-    if (threadIdx.x == 0) P.out_tokens[(int64_t)r * (P.ld + 1) + dd.nacc] = last;
-    if (P.ctx) {
-        __shared__ uint32_t sCommit;
-        if (threadIdx.x == 0) sCommit = 0;
-        __syncthreads();
-        commit(P, r, dd.nacc + 1, dd.nacc, last, &sCommit);
-        __syncthreads();
-        fl |= sCommit;
-    }
-    if (threadIdx.x == 0 && fl) atomicOr(&P.out_flags[r], fl);
 }
 
 // ---------------------------------------------------------------------------
@@ -1823,6 +1938,25 @@ static void launch_flat_d(const StatsParams& P, bool greedy, bool draft, int64_t
     else launch_flat_t<DT, false, false>(P, grid, L);
 }
 
+template <int DT, bool GREEDY, bool DITEMS>
+static void launch_rows_t(const StatsParams& P, int tm, int dm, const StatsLaunch& L)
+{
+    const dim3 grid((unsigned)((tm + dm) * P.splits), (unsigned)P.bs);
+    auto kern = k_stats_rows<DT, GREEDY, DITEMS>;
+    if (L.e0 || L.e1)
+        hipExtLaunchKernelGGL(kern, grid, dim3(kBlock), 0, L.st, L.e0, L.e1, 0, P, (int32_t)tm);
+    else
+        hipLaunchKernelGGL(kern, grid, dim3(kBlock), 0, L.st, P, (int32_t)tm);
+}
+
+template <int DT>
+static void launch_rows_d(const StatsParams& P, bool greedy, bool draft, int tm, int dm, const StatsLaunch& L)
+{
+    if (greedy) launch_rows_t<DT, true, false>(P, tm, dm, L);
+    else if (draft) launch_rows_t<DT, false, true>(P, tm, dm, L);
+    else launch_rows_t<DT, false, false>(P, tm, dm, L);
+}
+
 // `rows_max` bounds the target rows of one request and `drows_max` its draft
 // rows; `rows_bound` bounds the rows of the whole pass (target and draft) and
 // only sizes the flat grid.  P.plan must hold bs * (rows_max + drows_max)
@@ -1834,6 +1968,12 @@ static void launch_stats(StatsParams P, int dt, bool a, int ddt, bool da, bool d
     const int64_t cap = (int64_t)P.bs * (rows_max + drows_max);
     const bool flat = a && P.vocab % vec == 0 && (!draft || (ddt == dt && da)) && cap * sp.splits < INT32_MAX &&
                       (int64_t)P.bs * P.NR < INT32_MAX && P.n_rows <= INT32_MAX && P.dn_rows <= INT32_MAX;
+    if (flat && rows_bound * 4 >= cap * 3 && P.bs <= 65535) {
+        // the bound is close to every request's own: no row list
+        if (dt == SPEC_F32) launch_rows_d<SPEC_F32>(P, greedy, draft, rows_max, drows_max, st);
+        else launch_rows_d<SPEC_BF16>(P, greedy, draft, rows_max, drows_max, st);
+        return;
+    }
     if (flat) {
         const int64_t rows = rows_bound < cap ? (rows_bound > 0 ? rows_bound : 1) : cap;
         const int64_t grid = rows * sp.splits;
@@ -1841,6 +1981,8 @@ static void launch_stats(StatsParams P, int dt, bool a, int ddt, bool da, bool d
         else launch_flat_d<SPEC_BF16>(P, greedy, draft, grid, st);
         return;
     }
+    // the other forms need no plan, but the residual bookkeeping still needs its reset
+    if (P.done) hipLaunchKernelGGL(k_plan_rows<false>, dim3(1), dim3(kBlock), 0, st.st, P);
     const bool pipe = a && P.vocab % vec == 0 && P.bs <= kRowBaseLds && (int64_t)P.bs * rows_max <= kPipeMap;
     if (pipe) {
         const int64_t items = stats_items(P.bs, rows_max, sp);
@@ -1877,15 +2019,15 @@ static int elem_bytes(int dt) { return dt == SPEC_F32 ? 4 : 2; }
 // Row plan of the statistics pass: [rows] entries, then the count.
 static size_t plan_bytes(int64_t rows) { return align256((size_t)rows * sizeof(int2)) + align256(sizeof(int32_t)); }
 
-// Verify workspace: partials [bs, NR, splits] | decisions [bs] | chunk sums [bs, splits] | row prefix [bs + 1] |
-// row plan [bs * NR] | finished-chunk counters [bs]
+// Verify workspace: partials [bs, NR, splits] | row prefix [bs + 1] | row plan [bs * NR] |
+// residual chunk sums [bs, splits] | residual counters [bs]
 size_t spec_verify_chain_ws(int32_t bs, int32_t vocab, int32_t ld, int32_t dtype)
 {
     RowSplit sp = row_split(vocab, elem_bytes(dtype));
     const int NR = 2 * ld + 1;
-    return align256((size_t)bs * NR * sp.splits * sizeof(Partial)) + align256((size_t)bs * sizeof(Dec)) +
-           align256((size_t)bs * sp.splits * sizeof(double)) + align256((size_t)(bs + 1) * sizeof(int32_t)) +
-           plan_bytes((int64_t)bs * NR) + align256((size_t)bs * sizeof(uint32_t));
+    return align256((size_t)bs * NR * sp.splits * sizeof(Partial)) + align256((size_t)(bs + 1) * sizeof(int32_t)) +
+           plan_bytes((int64_t)bs * NR) + align256((size_t)bs * sp.splits * sizeof(double)) +
+           align256((size_t)bs * sizeof(uint32_t));
 }
 
 // Tree verify workspace: partials [bs, rows_max, splits] | row prefix [bs + 1] | row plan [bs * rows_max]
@@ -1912,20 +2054,18 @@ int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st)
     P.tokens = a->tokens; P.slot_flags = a->slot_flags; P.n_slots = a->n_slots;
     P.u_acc = a->u_accept; P.u_smp = a->u_sample;
     P.out_tokens = a->out_tokens; P.out_num = a->out_num; P.out_acc = a->out_accepted;
-    P.out_p = a->out_p; P.out_q = a->out_q; P.out_flags = a->out_flags;
+    P.out_p = a->out_p; P.out_q = a->out_q; P.out_flags = a->out_flags; P.write_flags = a->write_flags;
     P.ctx = a->ctx; P.ctx_stride = a->ctx_stride; P.ctx_len = a->ctx_len;
     P.ctx_len_out = a->ctx_len_out ? a->ctx_len_out : a->ctx_len; P.ctx_cap = a->ctx_cap;
     P.part = (Partial*)ws;
     ws += align256((size_t)a->bs * NR * sp.splits * sizeof(Partial));
-    P.dec = (Dec*)ws;
-    ws += align256((size_t)a->bs * sizeof(Dec));
-    P.sums = (double*)ws;
-    ws += align256((size_t)a->bs * sp.splits * sizeof(double));
     int32_t* gpre = (int32_t*)ws;
     ws += align256((size_t)(a->bs + 1) * sizeof(int32_t));
     int2* plan = (int2*)ws;
     int32_t* plan_count = (int32_t*)(ws + align256((size_t)a->bs * NR * sizeof(int2)));
     ws += plan_bytes((int64_t)a->bs * NR);
+    P.sums = (double*)ws;
+    ws += align256((size_t)a->bs * sp.splits * sizeof(double));
     P.done = (uint32_t*)ws;
     P.NR = NR; P.splits = sp.splits; P.chunk = sp.chunk;
     P.t_aligned = aligned16(a->logits, a->row_stride, a->dtype);
@@ -1943,6 +2083,7 @@ int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st)
     S.bs = a->bs; S.vocab = a->vocab; S.chunk = sp.chunk; S.splits = sp.splits; S.c = P.c;
     S.part = P.part; S.NR = NR; S.draft_base = a->ld + 1; S.gprefix = nullptr;
     S.plan = plan; S.plan_count = plan_count;
+    S.done = draft ? P.done : nullptr; S.sums = P.sums;   // residual bookkeeping, reset by k_plan_rows
     // rows of the pass: b + 1 target rows per request and a draft row per slot
     const int64_t slots_all = (int64_t)a->bs * a->ld;
     const int64_t slots = a->max_slots > 0 && a->max_slots < slots_all ? a->max_slots : slots_all;
@@ -1951,16 +2092,14 @@ int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st)
     const StatsLaunch L{st, (hipEvent_t)a->prof_begin, (hipEvent_t)a->prof_end};
     launch_stats(S, a->dtype, at, a->draft_dtype, ad, draft, P.greedy, a->ld + 1, draft ? a->ld : 0,
                  a->bs + slots + (draft ? slots : 0), sp, gpre, L);
-    if (a->dtype == SPEC_F32) hipLaunchKernelGGL((k_decide<SPEC_F32>), dim3(a->bs), dim3(kBlock), 0, st, P);
-    else hipLaunchKernelGGL((k_decide<SPEC_BF16>), dim3(a->bs), dim3(kBlock), 0, st, P);
-    if (draft) {
-        dim3 grid2(sp.splits, a->bs);
-        const int tt = a->dtype, dd = a->draft_dtype;
-        if (tt == SPEC_F32 && dd == SPEC_F32) hipLaunchKernelGGL((k_sample<SPEC_F32, SPEC_F32>), grid2, dim3(kBlock), 0, st, P);
-        else if (tt == SPEC_F32) hipLaunchKernelGGL((k_sample<SPEC_F32, SPEC_BF16>), grid2, dim3(kBlock), 0, st, P);
-        else if (dd == SPEC_F32) hipLaunchKernelGGL((k_sample<SPEC_BF16, SPEC_F32>), grid2, dim3(kBlock), 0, st, P);
-        else hipLaunchKernelGGL((k_sample<SPEC_BF16, SPEC_BF16>), grid2, dim3(kBlock), 0, st, P);
-    }
+    const int tt = a->dtype, dd = P.dlogits ? a->draft_dtype : a->dtype;
+    // residual chunks shared by K workgroups per request, about 5 each
+    const int K = draft && P.coal ? std::min(16, std::max(1, (sp.splits + 4) / 5)) : 1;
+    const dim3 g(a->bs, K), b(kDBlock);
+    if (tt == SPEC_F32 && dd == SPEC_F32) hipLaunchKernelGGL((k_decide<SPEC_F32, SPEC_F32>), g, b, 0, st, P);
+    else if (tt == SPEC_F32) hipLaunchKernelGGL((k_decide<SPEC_F32, SPEC_BF16>), g, b, 0, st, P);
+    else if (dd == SPEC_F32) hipLaunchKernelGGL((k_decide<SPEC_BF16, SPEC_F32>), g, b, 0, st, P);
+    else hipLaunchKernelGGL((k_decide<SPEC_BF16, SPEC_BF16>), g, b, 0, st, P);
     return spec_record_hip_error(hipGetLastError());
 }
 
@@ -1988,6 +2127,7 @@ int spec_verify_tree_launch(const spec_tree_verify_args* a, hipStream_t st)
     S.bs = a->bs; S.vocab = a->vocab; S.chunk = sp.chunk; S.splits = sp.splits; S.c = 1.0f;
     S.part = P.part; S.NR = a->rows_max; S.draft_base = 0; S.gprefix = nullptr;
     S.plan = plan; S.plan_count = plan_count;
+    S.done = nullptr; S.sums = nullptr;
     const StatsLaunch L{st, (hipEvent_t)a->prof_begin, (hipEvent_t)a->prof_end};
     launch_stats(S, a->dtype, aligned16(a->logits, a->row_stride, a->dtype), SPEC_F32, false, false, true,
                  a->rows_max, 0, (int64_t)a->bs * a->rows_max, sp, gpre, L);

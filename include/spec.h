@@ -248,7 +248,8 @@ typedef struct spec_alloc_args {
  * correction / bonus is the argmax.  Out: out_tokens[r][0..out_num) = the
  * accepted tokens then the correction or bonus, out_num = accepted + 1,
  * out_p / out_q = p(y_i) / q(y_i) for every slot (q = 1 for point masses and
- * at T = 0, where p is 1 or 0).  out_flags is OR-ed.  If ctx is not NULL the
+ * at T = 0, where p is 1 or 0).  out_flags is OR-ed (written with
+ * write_flags).  If ctx is not NULL the
  * emitted tokens are appended to ctx[r] at ctx_len[r] (skipped and flagged if
  * ctx_len + out_num > ctx_cap).  n_slots outside [0, ld] are clamped.
  * ======================================================================== */
@@ -283,7 +284,9 @@ typedef struct spec_verify_args {
     int32_t* out_accepted;       /* device [bs]                                   */
     float* out_p;                /* device [bs, ld] or NULL                       */
     float* out_q;                /* device [bs, ld] or NULL                       */
-    uint32_t* out_flags;         /* device [bs], OR-ed                            */
+    uint32_t* out_flags;         /* device [bs], OR-ed (see write_flags)          */
+    int32_t write_flags;         /* 1: out_flags[r] is written with this call's
+                                    flags instead (no zeroing needed before)      */
     int32_t* ctx;                /* optional commit: device [bs, ctx_stride]      */
     int64_t ctx_stride;
     int32_t* ctx_len;            /* device [bs]                                   */

@@ -141,13 +141,40 @@ def test_bad_rows_are_flagged_not_read():
     z[5, :] = -np.inf
     row_base = np.array([0, 4, 7, 100], np.int64)     # request 2's rows run off the end, 3 is outside
     y = np.zeros((BS, ld), np.int32)
+    ua, us = rng.random((BS, ld), dtype=np.float32), rng.random(BS, dtype=np.float32)
     g = S.spec_verify_chain(dev(z), dev(row_base), dev(y), dev(np.full(BS, 2, np.int32)), 1.0,
-                            u_accept=dev(rng.random((BS, ld), dtype=np.float32)),
-                            u_sample=dev(rng.random(BS, dtype=np.float32)))
+                            u_accept=dev(ua), u_sample=dev(us))
     torch.cuda.synchronize()
     fl = host(g["out_flags"]).astype(np.uint32)
     assert np.all(fl & O.BAD_LOGITS)                 # NaN / all -inf / rows outside the buffer
     assert np.all(host(g["out_num"]) >= 1)
+    # write_flags: the same flags land over whatever out_flags held
+    g2 = S.spec_verify_chain(dev(z), dev(row_base), dev(y), dev(np.full(BS, 2, np.int32)), 1.0,
+                             u_accept=dev(ua), u_sample=dev(us), out_flags=dev(np.full(BS, 0x5A5A5A5A, np.int32)),
+                             write_flags=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(g2["out_flags"]).astype(np.uint32), fl)
+
+
+def test_write_flags_equals_or_mode_on_drawn_residuals():
+    """Dense probabilistic chains (residuals summed by several workgroups per
+    request, drawn by the last): written flags and every output equal those
+    of the OR-ed call from zero."""
+    import torch
+    import draft_verification_spec_amd as S
+    c = synth.dense_headline(BS=16)
+    BS, B, V = c["BS"], c["B"], c["V"]
+    tgt = as_logits(c["target_bf16"]).reshape(-1, V)
+    drf = as_logits(c["draft_bf16"]).reshape(-1, V)
+    args = (tgt, dev(np.arange(BS, dtype=np.int64) * (B + 1)), dev(c["tokens"]), dev(np.full(BS, B, np.int32)),
+            c["temperature"])
+    kw = dict(u_accept=dev(c["u_acc"]), u_sample=dev(c["u_smp"]), slot_flags=dev(np.zeros((BS, B), np.uint8)),
+              draft_logits=drf, draft_row_base=dev(np.arange(BS, dtype=np.int64) * B))
+    a = S.spec_verify_chain(*args, **kw)
+    b = S.spec_verify_chain(*args, **kw, out_flags=dev(np.full(BS, -1, np.int32)), write_flags=True)
+    torch.cuda.synchronize()
+    for k in a:
+        assert np.array_equal(host(a[k]), host(b[k])), k
 
 
 def test_commit_appends_and_overflows():
