@@ -1,21 +1,23 @@
 #!/usr/bin/env python3
-"""Benchmark of the whole speculative-decoding step on one MI355X.
+"""Benchmark of the speculative-decoding step on one MI355X.
 
-One step = n-gram draft over every request's context -> chain selection and
-budget allocation -> rejection-sampling verification of the chosen chains ->
-commit of the emitted tokens, on the batch-allocation workload: BS 128,
-V = 151,936, a 7-token model chain and a 15-token n-gram chain per request,
-budget 256 verified draft slots, bf16 target rows, T = 1.0, 8,192-token
-contexts (synthetic, seeded; see workloads/synth.py).
+The reported step (the metric: verify + draft at BS 128, V = 151,936, B = 7)
+is the dense one: rejection-sampling verification of every request's 7-token
+model chain against bf16 target rows [128, 8, V] and draft rows [128, 7, V]
+(probabilistic slots, T = 1.0), the commit of the emitted tokens after each
+8,192-token context, then the n-gram draft over the updated contexts
+(synthetic, seeded; see workloads/synth.py).  The commit writes the new
+lengths to a separate buffer, so every timed step does the same work.
 
-The commit appends each request's emitted tokens after its context and writes
-the new lengths to a separate buffer, so every one of the K timed steps reads
-the same contexts and does the same work.  Two timed regions on one stream:
-K eager steps with an event pair attached to the dispatch of every
-verification statistics kernel (that kernel's live average duration, and an
-eager throughput), then the K steps captured in one HIP
-graph (checked against the eager step first) replayed once between two
-events, which gives the reported throughput.  Prints one JSON line.
+A second record times the batch-allocation step (n-gram draft -> chain
+selection and budget allocation of 256 slots -> verification -> commit) at
+BS 128 with the same timing.
+
+Timing, per workload, on one stream: K eager steps with an event pair
+attached to the dispatch of every statistics kernel (that kernel's live
+average duration), then the K steps captured in one HIP graph (checked
+against the eager step first) replayed once between two events, which gives
+the throughput.  Prints one JSON line.
 """
 import argparse
 import ctypes as C
@@ -31,8 +33,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verify+draft steps/sec at BS128, V=151936, B=7; achieved HBM GB/s vs peak"
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E, AMD's published figure
-STATS_KERNEL = "k_stats_flat"   # the HBM-bound pass of the step
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "verify_stats_bs128_v151936_bf16_counters.md")
+STATS_KERNEL = "k_stats_rows"   # the HBM-bound pass of the dense step
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "stats_rows_dense_bs128_v151936_bf16_counters.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "draft_verification_spec_amd", "csrc", f)
                   for f in ("verify.hip", "common.hpp")]
 
@@ -40,10 +42,11 @@ KERNEL_SOURCES = [os.path.join(ROOT, "draft_verification_spec_amd", "csrc", f)
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
+    # the step is ~0.1 ms: a few hundred warm-up steps bring the GPU to its steady clocks
     p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=500)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--no-dense", action="store_true", help="skip the dense verify + draft measurement")
+    p.add_argument("--no-budget", action="store_true", help="skip the batch-allocation step record")
     p.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -106,31 +109,102 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 10}), flush=True)
 
 
-def cpu_baseline(c, budget_s=12.0):
-    """The oracle, as it stands, on the same inputs: whole steps over the full
-    batch, repeated until about budget_s seconds of CPU work."""
+def cpu_baseline(c, sample=32, budget_s=12.0):
+    """The oracle, as it stands, on the first `sample` requests of the dense
+    step's inputs (verify, commit, n-gram draft), repeated until about
+    budget_s seconds of CPU work; scaled to whole BS-128 steps per second."""
     import numpy as np
     from oracle import oracle as O
     O.build()
+    BS, V, B = c["BS"], c["V"], c["B"]
+    m = min(sample, BS)
+    tgt = c["target_bf16"][:m].reshape(-1, V)
+    dft = c["draft_bf16"][:m].reshape(-1, V)
     n, t0 = 0, time.perf_counter()
     while True:
-        O.step_chain(c["ctx"], c["ctx_len"], c["ctx"].shape[1], c["model_tokens"], c["model_conf_logit"],
-                     c["model_point_mass"], c["estimator"], c["lam"], c["budget"],
-                     c["target_bf16"].reshape(-1, c["V"]), np.arange(c["BS"]) * 16, c["u_acc"], c["u_smp"],
-                     c["temperature"], c["n_min"], c["n_max"], 15, 256)
+        o = O.verify_chain(tgt, np.arange(m) * (B + 1), c["tokens"][:m], np.zeros((m, B), np.uint8),
+                           np.full(m, B, np.int32), c["u_acc"][:m], c["u_smp"][:m], c["temperature"],
+                           draft_logits=dft, draft_row_base=np.arange(m) * B)
+        ctx, ctx_len = O.commit(c["ctx"][:m].copy(), c["ctx_len"][:m].copy(), c["ctx"].shape[1], o["out_tokens"],
+                                o["out_num"], o["flags"])
+        O.ngram_draft(ctx, ctx_len, c["n_min"], c["n_max"], c["max_draft"], c["copy_cap"])
         n += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or n >= 20:
+        if el >= budget_s or n >= 200:
             break
-    return {"value": n / el, "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} whole steps over the full BS-128 batch (single-threaded C oracle, fp64), {el:.1f} s"}
+    return {"value": n * m / BS / el, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} runs of the dense step over the first {m} of {BS} requests (verify, commit, n-gram "
+                      f"draft; single-threaded C oracle, fp64) in {el:.1f} s, scaled by {m}/{BS}"}
 
 
-def dense_headline(K, W, hip):
-    """The dense verify + draft step at BS 128: bf16 target [128, 8, V] and
-    draft [128, 7, V] rows with probabilistic slots at T = 1, the commit of the
-    emitted tokens, then the n-gram draft over the updated contexts.  K steps
-    captured in one HIP graph (checked against an eager step first)."""
+def run_timed(step, outputs, K, W, hip, stream, eager_only=False):
+    """Times `step` (already run once, so its buffers exist): K eager steps
+    with the statistics kernel's event pair attached to its dispatch, then K
+    steps in one HIP graph, replayed once.  Every timed region's outputs must
+    equal the reference step's."""
+    import numpy as np
+    import torch
+    with torch.cuda.stream(stream):
+        step()
+        torch.cuda.synchronize()
+        ref = [t.cpu().clone() for t in outputs()]
+    ev_b = [hip.event() for _ in range(K)]
+    ev_e = [hip.event() for _ in range(K)]
+    t0, t1, t2, t3 = (hip.event() for _ in range(4))
+    s = stream.cuda_stream
+
+    def same(tag):
+        for i, (a, b) in enumerate(zip(outputs(), ref)):
+            assert torch.equal(a.cpu(), b), f"{tag}: output {i} differs from the reference step"
+
+    with torch.cuda.stream(stream):
+        for _ in range(W):
+            step()
+        torch.cuda.synchronize()
+        hip.record(t0, s)
+        for k in range(K):
+            step(prof=(ev_b[k], ev_e[k]))
+        hip.record(t1, s)
+        torch.cuda.synchronize()
+    eager_ms = hip.ms(t0, t1)
+    stats_ms = [hip.ms(a, b) for a, b in zip(ev_b, ev_e)]
+    same("eager timed steps")
+    mode, total_ms = "eager", eager_ms
+    if not eager_only:
+        try:
+            g1 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g1, stream=stream):
+                step()
+            gK = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gK, stream=stream):
+                for _ in range(K):
+                    step()
+            for rep in range(3):   # every replay equals the eager step, with eager work in between
+                g1.replay()
+                torch.cuda.synchronize()
+                same(f"graph replay {rep}")
+                with torch.cuda.stream(stream):
+                    step()
+                torch.cuda.synchronize()
+            with torch.cuda.stream(stream):
+                for _ in range(W):
+                    g1.replay()
+                torch.cuda.synchronize()
+                hip.record(t2, s)
+                gK.replay()
+                hip.record(t3, s)
+                torch.cuda.synchronize()
+            total_ms = hip.ms(t2, t3)
+            same("graph timed steps")
+            mode = "graph"
+        except Exception as e:  # capture unsupported here: keep the eager region's figure
+            print(f"[bench] graph capture failed ({e}); reporting the eager region", file=sys.stderr, flush=True)
+    return {"mode": mode, "ms_per_step": total_ms / K, "steps_per_s": K / (total_ms * 1e-3),
+            "eager_ms_per_step": eager_ms / K, "stats_ms": float(np.mean(stats_ms))}
+
+
+def headline(K, W, hip, eager_only):
+    """The dense verify + commit + n-gram draft step (the reported one)."""
     import numpy as np
     import torch
     import draft_verification_spec_amd as S
@@ -151,48 +225,83 @@ def dense_headline(K, W, hip):
     bufs = {"ws_v": torch.empty(1 << 26, dtype=torch.uint8, device=dev),
             "ws_ng": torch.empty(1 << 20, dtype=torch.uint8, device=dev)}
 
-    def step():
+    def step(prof=None):
         out = S.spec_verify_chain(target, rb, tokens, n_slots, c["temperature"], u_accept=u_acc, u_sample=u_smp,
                                   slot_flags=flags, draft_logits=draft, draft_row_base=drb, ctx=ctx,
                                   ctx_len=ctx_len, ctx_len_out=ctx_len_new, out=bufs.get("vf"),
-                                  out_flags=bufs.get("vfl"), write_flags=True, workspace=bufs["ws_v"])
+                                  out_flags=bufs.get("vfl"), write_flags=True, workspace=bufs["ws_v"],
+                                  prof_events=prof)
         d = S.spec_ngram_draft(ctx, ctx_len_new, c["n_min"], c["n_max"], c["max_draft"], c["copy_cap"],
                                out=bufs.get("ng"), workspace=bufs["ws_ng"])
         bufs.setdefault("vf", {k: v for k, v in out.items() if k != "out_flags"})
         bufs.setdefault("vfl", out["out_flags"])
         bufs.setdefault("ng", d)
-        return out, d
 
     with torch.cuda.stream(stream):
         step()
-        out, d = step()
-        torch.cuda.synchronize()
-        ref = [t.cpu().clone() for t in list(out.values()) + list(d)]
-        gK = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gK, stream=stream):
-            for _ in range(K):
-                step()
-        gK.replay()
-        torch.cuda.synchronize()
-        got = [t.cpu() for t in list(out.values()) + list(d)]
-        assert all(torch.equal(a, b) for a, b in zip(got, ref)), "dense graph replay differs from the eager step"
-        for _ in range(max(1, W // K)):
-            gK.replay()
-        torch.cuda.synchronize()
-        t0, t1 = hip.event(), hip.event()
-        hip.record(t0, stream.cuda_stream)
-        gK.replay()
-        hip.record(t1, stream.cuda_stream)
-        torch.cuda.synchronize()
-    ms = hip.ms(t0, t1)
-    rows_bytes = BS * (2 * B + 1) * V * 2
+    outputs = lambda: list(bufs["vf"].values()) + [bufs["vfl"], ctx_len_new, ctx] + list(bufs["ng"])
+    t = run_timed(step, outputs, K, W, hip, stream, eager_only)
+    rows_bytes = BS * (2 * B + 1) * V * 2                # every verified target and draft row, bf16
     ctx_bytes = int(c["ctx_len"].sum()) * 4
-    step_bytes = rows_bytes + ctx_bytes
-    gbps = step_bytes / (ms / K * 1e-3) / 1e9
-    return {"workload": "dense verify + commit + n-gram draft: BS=128, V=151936, B=7, bf16 target [128,8,V] and "
-                        "draft [128,7,V], probabilistic slots, T=1.0, 8192-token contexts",
-            "steps_per_s": K / (ms * 1e-3), "ms_per_step": ms / K, "algorithmic_bytes": step_bytes,
-            "GBps": gbps, "frac": gbps / PEAK_HBM_GBPS}
+    t.update(c=c, rows_bytes=rows_bytes, ctx_bytes=ctx_bytes, BS=BS, V=V, B=B, T_ctx=int(c["ctx"].shape[1] - 64))
+    return t
+
+
+def budget_step(K, W, hip, eager_only):
+    """The batch-allocation step: n-gram draft -> selection and allocation of
+    256 slots -> verification of the chosen chains -> commit."""
+    import numpy as np
+    import torch
+    import draft_verification_spec_amd as S
+    from workloads import synth
+    dev = torch.device("cuda:0")
+    c = synth.config2(ctx_extra=64)
+    BS, V, L = c["BS"], c["V"], 15
+    g = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    ctx, ctx_len = g(c["ctx"]), g(c["ctx_len"])
+    ctx_len_new = torch.empty_like(ctx_len)
+    tokens_d, conf_d, pm_d = g(c["model_tokens"]), g(c["model_conf_logit"]), g(c["model_point_mass"])
+    target = synth.as_torch_bf16(c["target_bf16"]).to(dev).reshape(-1, V)
+    row_base = g(np.arange(BS, dtype=np.int64) * c["target_rows_per_req"])
+    u_acc, u_smp = g(c["u_acc"][:, :L]), g(c["u_smp"])
+    stream = torch.cuda.Stream()
+    bufs = {"ws_ng": torch.empty(1 << 22, dtype=torch.uint8, device=dev),
+            "ws_al": torch.empty(1 << 20, dtype=torch.uint8, device=dev),
+            "ws_v": torch.empty(1 << 24, dtype=torch.uint8, device=dev)}
+
+    def step(prof=None):
+        d, dl, f = S.spec_ngram_draft(ctx, ctx_len, c["n_min"], c["n_max"], L, c["copy_cap"],
+                                      out=bufs.get("ng"), workspace=bufs["ws_ng"])
+        al = S.spec_allocate_budget(mode="chain", model_tokens=tokens_d, model_conf=conf_d, ngram_draft=d,
+                                    ngram_len=dl, ngram_feat=f, est=c["estimator"], lam=c["lam"],
+                                    budget=c["budget"], policy="proposed", conf_is_logit=True,
+                                    model_point_mass=pm_d, ld=L, out=bufs.get("al"), workspace=bufs["ws_al"])
+        out = S.spec_verify_chain(target, row_base, al["chain_tokens"], al["alloc_len"], c["temperature"],
+                                  u_accept=u_acc, u_sample=u_smp, slot_flags=al["slot_flags"],
+                                  out_flags=al["out_flags"], ctx=ctx, ctx_len=ctx_len, ctx_len_out=ctx_len_new,
+                                  out=bufs.get("vf"), max_slots=c["budget"], workspace=bufs["ws_v"],
+                                  prof_events=prof)
+        bufs.setdefault("ng", (d, dl, f))
+        bufs.setdefault("al", al)
+        bufs.setdefault("vf", {k: v for k, v in out.items() if k != "out_flags"})
+
+    with torch.cuda.stream(stream):
+        step()
+        torch.cuda.synchronize()
+    total_rows = int(bufs["al"]["total_rows"].item())
+    outputs = lambda: list(bufs["vf"].values()) + [bufs["al"]["out_flags"], ctx_len_new, ctx]
+    t = run_timed(step, outputs, K, W, hip, stream, eager_only)
+    rows_bytes = total_rows * V * 2
+    step_bytes = rows_bytes + int(c["ctx_len"].sum()) * 4
+    return {"workload": "batch budget allocation + verify + commit + n-gram draft: BS=128, V=151936, model chain "
+                        "B=7 (greedy) + n-gram chain up to 15 (n 5..15), budget 256 draft slots, lambda 0.309, "
+                        "bf16 target rows, T=1.0, 8192-token contexts",
+            "timing": t["mode"], "steps_per_s": t["steps_per_s"], "ms_per_step": t["ms_per_step"],
+            "verified_rows_per_step": total_rows, "algorithmic_bytes": step_bytes,
+            "GBps": step_bytes / (t["ms_per_step"] * 1e-3) / 1e9,
+            "frac": step_bytes / (t["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "stats_kernel": {"kernel": "k_stats_flat", "avg_launch_ms": t["stats_ms"],
+                             "GBps": rows_bytes / (t["stats_ms"] * 1e-3) / 1e9}}
 
 
 def main():
@@ -201,135 +310,18 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (the step shards by request; "
               "see DESIGN.md). Run with --gpus 1.", file=sys.stderr, flush=True)
         sys.exit(2)
-    import numpy as np
-    import torch
-
     if args.copy_calibration:
         copy_calibration()
         return
-
-    import draft_verification_spec_amd as S
-    from workloads import synth
-
-    dev = torch.device("cuda:0")
-    c = synth.config2(ctx_extra=64)
-    BS, V, L = c["BS"], c["V"], 15
-    g = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-    ctx = g(c["ctx"])
-    ctx_len = g(c["ctx_len"])
-    ctx_len_new = torch.empty_like(ctx_len)
-    tokens_d, conf_d, pm_d = g(c["model_tokens"]), g(c["model_conf_logit"]), g(c["model_point_mass"])
-    target = synth.as_torch_bf16(c["target_bf16"]).to(dev).reshape(-1, V)
-    row_base = g(np.arange(BS, dtype=np.int64) * c["target_rows_per_req"])
-    u_acc, u_smp = g(c["u_acc"][:, :L]), g(c["u_smp"])
-    est = c["estimator"]
-
-    stream = torch.cuda.Stream()
-    hip = Hip()
-    bufs = {}
-
-    def step(prof=None):
-        d, dl, f = S.spec_ngram_draft(ctx, ctx_len, c["n_min"], c["n_max"], L, c["copy_cap"],
-                                      out=bufs.get("ng"), workspace=bufs.get("ws_ng"))
-        al = S.spec_allocate_budget(mode="chain", model_tokens=tokens_d, model_conf=conf_d, ngram_draft=d,
-                                    ngram_len=dl, ngram_feat=f, est=est, lam=c["lam"], budget=c["budget"],
-                                    policy="proposed", conf_is_logit=True, model_point_mass=pm_d, ld=L,
-                                    out=bufs.get("al"), workspace=bufs.get("ws_al"))
-        out = S.spec_verify_chain(target, row_base, al["chain_tokens"], al["alloc_len"], c["temperature"],
-                                  u_accept=u_acc, u_sample=u_smp, slot_flags=al["slot_flags"],
-                                  out_flags=al["out_flags"], ctx=ctx, ctx_len=ctx_len, ctx_len_out=ctx_len_new,
-                                  out=bufs.get("vf"), max_slots=c["budget"],
-                                  workspace=bufs.get("ws_v"), prof_events=prof)
-        bufs.setdefault("ng", (d, dl, f))
-        bufs.setdefault("al", al)
-        bufs.setdefault("vf", {k: v for k, v in out.items() if k != "out_flags"})
-        return d, al, out
-
-    with torch.cuda.stream(stream):
-        # preallocate workspaces once (the graph must not allocate)
-        bufs["ws_ng"] = torch.empty(1 << 22, dtype=torch.uint8, device=dev)
-        bufs["ws_al"] = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
-        bufs["ws_v"] = torch.empty(1 << 24, dtype=torch.uint8, device=dev)
-        step()
-        torch.cuda.synchronize()
-        d, al, out = step()
-        torch.cuda.synchronize()
-        ref = {k: v.cpu().clone() for k, v in out.items()}
-        ref_ctx = ctx.cpu().clone()
-        total_rows = int(al["total_rows"].item())
-
     K, W = args.steps, args.warmup
-    ev_b = [hip.event() for _ in range(K)]
-    ev_e = [hip.event() for _ in range(K)]
-    t0, t1, t2, t3 = (hip.event() for _ in range(4))
-    s = stream.cuda_stream
-
-    # Region 1, eager launches: an event pair attached to every statistics
-    # kernel's dispatch gives that kernel's live average duration.
-    with torch.cuda.stream(stream):
-        for _ in range(W):
-            step()
-        torch.cuda.synchronize()
-        hip.record(t0, s)
-        for k in range(K):
-            step(prof=(ev_b[k], ev_e[k]))
-        hip.record(t1, s)
-        torch.cuda.synchronize()
-    eager_ms = hip.ms(t0, t1)
-    stats_ms = [hip.ms(a, b) for a, b in zip(ev_b, ev_e)]
-    for k2, v in out.items():
-        assert torch.equal(v.cpu(), ref[k2]), f"eager timed steps differ from the reference step in {k2}"
-
-    # Region 2, the K steps captured in one HIP graph, replayed once.
-    mode = "graph"
-    total_ms = eager_ms
-    if args.eager:
-        mode = "eager"
-    else:
-        try:
-            g1 = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g1, stream=stream):
-                step()
-            gK = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gK, stream=stream):
-                for k in range(K):
-                    step()
-            # every replay must equal the eager step (with eager work in between)
-            for rep in range(3):
-                g1.replay()
-                torch.cuda.synchronize()
-                for k2, v in out.items():
-                    assert torch.equal(v.cpu(), ref[k2]), f"graph replay {rep} differs in {k2}"
-                assert torch.equal(ctx.cpu(), ref_ctx)
-                with torch.cuda.stream(stream):
-                    step()
-                torch.cuda.synchronize()
-            with torch.cuda.stream(stream):
-                for _ in range(W):
-                    g1.replay()
-                torch.cuda.synchronize()
-                hip.record(t2, s)
-                gK.replay()
-                hip.record(t3, s)
-                torch.cuda.synchronize()
-            total_ms = hip.ms(t2, t3)
-            for k2, v in out.items():
-                assert torch.equal(v.cpu(), ref[k2]), f"graph timed steps differ from the reference step in {k2}"
-        except Exception as e:  # capture unsupported here: keep the eager region's figure
-            print(f"[bench] graph capture failed ({e}); reporting the eager region", file=sys.stderr, flush=True)
-            mode = "eager"
-            total_ms = eager_ms
-
-    ms_step = total_ms / K
-    stats_avg = float(np.mean(stats_ms))
-    stats_bytes = total_rows * V * 2                     # one bf16 read of every verified row
-    ctx_bytes = int(c["ctx_len"].sum()) * 4               # one read of every context
-    step_bytes = stats_bytes + ctx_bytes
-    achieved = stats_bytes / (stats_avg * 1e-3) / 1e9
-    traffic = traffic_from_profile()
+    hip = Hip()
+    h = headline(K, W, hip, args.eager)
+    ms_step = h["ms_per_step"]
+    step_bytes = h["rows_bytes"] + h["ctx_bytes"]
+    achieved = h["rows_bytes"] / (h["stats_ms"] * 1e-3) / 1e9
     res = {
         "metric": METRIC,
-        "value": K / (total_ms * 1e-3),
+        "value": h["steps_per_s"],
         "unit": "steps/s",
         "n_gpus": 1,
         "steps": K,
@@ -340,22 +332,21 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "batch budget allocation + verify + n-gram draft: BS=128, V=151936, model chain "
-                               "B=7 (greedy) + n-gram chain up to 15 (n 5..15), budget 256 draft slots, lambda 0.309, "
-                               "bf16 target rows, T=1.0, 8192-token contexts",
-                   "global_batch": BS, "seq_len": int(c["ctx"].shape[1] - 64), "timing": mode,
-                   "verified_rows_per_step": total_rows},
-        "eager": {"steps_per_s": K / (eager_ms * 1e-3), "ms_per_step": eager_ms / K},
+        "config": {"workload": "dense verify + commit + n-gram draft: BS=128, V=151936, B=7, bf16 target "
+                               "[128,8,V] and draft [128,7,V] rows, probabilistic slots, T=1.0, 8192-token "
+                               "contexts, n-gram n 5..15, up to 15 tokens",
+                   "global_batch": h["BS"], "seq_len": h["T_ctx"], "draft_len": h["B"], "timing": h["mode"]},
+        "eager": {"ms_per_step": h["eager_ms_per_step"]},
         "roofline": {"bound": "hbm", "kernel": STATS_KERNEL, "achieved": achieved, "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": traffic, "bytes_per_launch": stats_bytes, "avg_launch_ms": stats_avg},
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic_from_profile(),
+                     "bytes_per_launch": h["rows_bytes"], "avg_launch_ms": h["stats_ms"]},
         "step_hbm": {"algorithmic_bytes": step_bytes, "GBps": step_bytes / (ms_step * 1e-3) / 1e9,
                      "frac": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS},
     }
-    if not args.no_dense:
-        res["dense_headline"] = dense_headline(K, W, hip)
+    if not args.no_budget:
+        res["budget_step"] = budget_step(K, W, hip, args.eager)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(c)
+        res["cpu_baseline"] = cpu_baseline(h["c"])
     print(json.dumps(res), flush=True)
 
 

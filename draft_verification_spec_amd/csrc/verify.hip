@@ -1115,29 +1115,32 @@ __device__ __forceinline__ void load_seg(const void* row, bool aligned, int64_t 
     }
 }
 
-// Weights of the segment [a, b) of the draw's row(s), written to w.
+// Logits of the segment [a, b) of the draw's row(s): z of the target row and,
+// for a residual draw, x of the draft row (else zeros).
 template <int DTT, int DTD>
-__device__ __forceinline__ void seg_weights(const ChainParams& P, const Draw& d, int64_t a, int64_t b, double* w)
+__device__ __forceinline__ void seg_load(const ChainParams& P, const Draw& d, int64_t a, int64_t b, float* z, float* x)
 {
-    float z[kSeg];
     load_seg<DTT>(row_ptr<DTT>(P.logits, d.row_t, P.stride), P.t_aligned, a, b, z);
     if (d.mode == 2) {
-        float x[kSeg];
         load_seg<DTD>(row_ptr<DTD>(P.dlogits, d.row_d, P.dstride), P.d_aligned, a, b, x);
-#pragma unroll
-        for (int u = 0; u < kSeg; ++u) {
-            const double ep = (double)fast_exp2(fmaf(z[u], P.c, -d.Ot));
-            const double eq = (double)fast_exp2(fmaf(x[u], P.c, -d.Od));
-            const double v = ep - eq * d.ratio;
-            w[u] = (a + u < b && v > 0.0) ? v : 0.0;
-        }
     } else {
 #pragma unroll
-        for (int u = 0; u < kSeg; ++u) {
-            const double ep = (double)fast_exp2(fmaf(z[u], P.c, -d.Ot));
-            w[u] = (a + u < b && !(d.mode == 3 && a + u == d.y)) ? ep : 0.0;
-        }
+        for (int u = 0; u < kSeg; ++u) x[u] = 0.0f;
     }
+}
+
+// Weight of entry a + u of a segment [a, b) from its logits: mode 1 p's
+// weight, 3 the same with y removed, 2 the residual max(0, ep - eq Zt/Zd).
+__device__ __forceinline__ double seg_w(const ChainParams& P, const Draw& d, int64_t a, int64_t b, int u, float z,
+                                        float x)
+{
+    const double ep = (double)fast_exp2(fmaf(z, P.c, -d.Ot));
+    if (d.mode == 2) {
+        const double eq = (double)fast_exp2(fmaf(x, P.c, -d.Od));
+        const double v = ep - eq * d.ratio;
+        return (a + u < b && v > 0.0) ? v : 0.0;
+    }
+    return (a + u < b && !(d.mode == 3 && a + u == d.y)) ? ep : 0.0;
 }
 
 __device__ __forceinline__ void seg_of(int64_t lo, int64_t hi, int64_t* a, int64_t* b)
@@ -1156,10 +1159,10 @@ __device__ double range_sum(const ChainParams& P, const Draw& d, int64_t lo, int
     seg_of(lo, hi, &a, &b);
     double acc = 0.0;
     if (a < b) {
-        double w[kSeg];
-        seg_weights<DTT, DTD>(P, d, a, b, w);
+        float z[kSeg], x[kSeg];
+        seg_load<DTT, DTD>(P, d, a, b, z, x);
 #pragma unroll
-        for (int u = 0; u < kSeg; ++u) acc += w[u];
+        for (int u = 0; u < kSeg; ++u) acc += seg_w(P, d, a, b, u, z[u], x[u]);
     }
     return block_sum_f64(acc);
 }
@@ -1178,15 +1181,17 @@ __device__ int64_t search_range(const ChainParams& P, const Draw& d, int64_t lo,
     const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
     int64_t a, b;
     seg_of(lo, hi, &a, &b);
-    double w[kSeg];
+    // the logits stay in registers; weights are recomputed where needed
+    float z[kSeg], x[kSeg];
     double mine = 0.0;
     uint32_t posmask = 0;   // segment offsets with positive weight
     if (a < b) {
-        seg_weights<DTT, DTD>(P, d, a, b, w);
+        seg_load<DTT, DTD>(P, d, a, b, z, x);
 #pragma unroll
         for (int u = 0; u < kSeg; ++u) {
-            mine += w[u];
-            posmask |= (w[u] > 0.0 ? 1u : 0u) << u;
+            const double w = seg_w(P, d, a, b, u, z[u], x[u]);
+            mine += w;
+            posmask |= (w > 0.0 ? 1u : 0u) << u;
         }
     }
     double total;
@@ -1205,8 +1210,9 @@ __device__ int64_t search_range(const ChainParams& P, const Draw& d, int64_t lo,
             double run = cum;
 #pragma unroll
             for (int u = 0; u < kSeg; ++u) {
-                run += w[u];
-                if (pu < 0 && w[u] > 0.0 && run > t) pu = u;
+                const double w = seg_w(P, d, a, b, u, z[u], x[u]);
+                run += w;
+                if (pu < 0 && w > 0.0 && run > t) pu = u;
             }
             if (pu < 0) pu = 31 - __builtin_clz(posmask);
         }
@@ -1322,7 +1328,7 @@ __device__ void commit(const ChainParams& P, int r, int n, int nacc, int32_t las
 // and the workgroup that brings the count to K draws.  Rows of one dtype,
 // 16-byte aligned, vocabulary a multiple of a vector.
 constexpr int kVecs = kChunkBytes / 16 / kDBlock;   // vectors per thread per chunk
-constexpr int kRound = 2;                           // chunks per round
+constexpr int kRound = 1;                           // chunks per round
 
 template <int DT>
 __device__ __forceinline__ void residual_issue(const char* tp, const char* dp, const ChainParams& P, int c0, int step,
@@ -1454,8 +1460,10 @@ constexpr int kMergeLanes = 8;   // lanes that merge one row's chunk partials
 // the first rejection (cheap, and identical); workgroup 0 writes the slot
 // outputs and draws and commits, except that a probabilistic residual is
 // summed by all K and drawn by the last of them to finish.
+// Three workgroups of 8 waves per compute unit: 6 waves per SIMD, which caps
+// registers at 80.
 template <int DTT, int DTD>
-__global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
+__global__ __launch_bounds__(kDBlock) __attribute__((amdgpu_waves_per_eu(6))) void k_decide(ChainParams P)
 {
     const int r = blockIdx.x;
     const int kk = blockIdx.y, K = gridDim.y;
@@ -2093,8 +2101,8 @@ int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st)
     launch_stats(S, a->dtype, at, a->draft_dtype, ad, draft, P.greedy, a->ld + 1, draft ? a->ld : 0,
                  a->bs + slots + (draft ? slots : 0), sp, gpre, L);
     const int tt = a->dtype, dd = P.dlogits ? a->draft_dtype : a->dtype;
-    // residual chunks shared by K workgroups per request, about 5 each
-    const int K = draft && P.coal ? std::min(16, std::max(1, (sp.splits + 4) / 5)) : 1;
+    // residual chunks shared by K workgroups per request, about 3 each
+    const int K = draft && P.coal ? std::min(16, std::max(1, (sp.splits + 2) / 3)) : 1;
     const dim3 g(a->bs, K), b(kDBlock);
     if (tt == SPEC_F32 && dd == SPEC_F32) hipLaunchKernelGGL((k_decide<SPEC_F32, SPEC_F32>), g, b, 0, st, P);
     else if (tt == SPEC_F32) hipLaunchKernelGGL((k_decide<SPEC_F32, SPEC_BF16>), g, b, 0, st, P);
