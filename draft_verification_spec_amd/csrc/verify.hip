@@ -39,6 +39,7 @@ namespace spec {
 constexpr int kBlock = 256;
 constexpr int kTile = 4;              // 16-byte vectors in flight per thread per step
 constexpr int kMaxLdsPrefix = 4096;   // batch sizes whose row prefix fits in LDS
+constexpr int kSubSums = 16;          // residual sums per chunk (one per wave and vector slot of k_decide)
 
 // Chunk partial: T > 0: (m, -, s); T = 0: (best, idx | bad << 31, -).
 struct Partial {
@@ -326,7 +327,7 @@ struct StatsParams {
     int2* plan;                   // flat pass: the rows it reads (k_plan_rows) ...
     int32_t* plan_count;          // ... and their count
     uint32_t* done;               // chain draws: counters k_plan_rows zeroes ([bs]) ...
-    double* sums;                 // ... and chunk sums it sets to -1 ([bs, splits]); or null
+    double* sums;                 // ... and residual sums it sets to -1 ([bs, splits, kSubSums]); or null
 };
 
 __device__ __forceinline__ int32_t target_rows(const StatsParams& P, int r)
@@ -908,7 +909,7 @@ __global__ __launch_bounds__(kBlock) void k_plan_rows(StatsParams P)
     if (t == 0) *P.plan_count = carry;
     if (P.done) {
         for (int r = t; r < P.bs; r += kBlock) P.done[r] = 0;
-        for (int64_t i = t; i < (int64_t)P.bs * P.splits; i += kBlock) P.sums[i] = -1.0;
+        for (int64_t i = t; i < (int64_t)P.bs * P.splits * kSubSums; i += kBlock) P.sums[i] = -1.0;
     }
 }
 
@@ -1004,7 +1005,7 @@ __global__ __launch_bounds__(kBlock) void k_stats_rows(StatsParams P, int32_t TM
     }
     if (P.done && blockIdx.x == 0) {
         if (t == 0) P.done[r] = 0;
-        for (int i = t; i < P.splits; i += kBlock) P.sums[(int64_t)r * P.splits + i] = -1.0;
+        for (int i = t; i < P.splits * kSubSums; i += kBlock) P.sums[(int64_t)r * P.splits * kSubSums + i] = -1.0;
     }
 }
 
@@ -1042,7 +1043,7 @@ struct ChainParams {
     int32_t write_flags;        // out_flags written (by the drawing workgroup) rather than OR-ed
     int32_t* ctx; int64_t ctx_stride; const int32_t* ctx_len; int32_t* ctx_len_out; int32_t ctx_cap;
     Partial* part; int32_t NR; int32_t splits; int64_t chunk;
-    double* sums;               // [bs, splits] residual chunk sums (-1 until written)
+    double* sums;               // [bs, splits, kSubSums] residual sums (-1 until written)
     uint32_t* done;             // [bs] workgroups of a request done with their residual chunks
     bool t_aligned, d_aligned;  // rows allow 16-byte vector loads
     bool coal;                  // same dtype, aligned rows, vocab a multiple of a vector
@@ -1234,16 +1235,17 @@ __device__ int64_t search_range(const ChainParams& P, const Draw& d, int64_t lo,
     return res;
 }
 
-// Draw with chunk sums W[0..splits) (fp64, in LDS): pick the chunk holding
-// u * W, rescan it.  Returns the token, or -1 if the total is unusable.
-template <int DTT, int DTD>
-__device__ int32_t draw_from_chunks(const ChainParams& P, const Draw& d, const double* W, double u)
+// The chunk holding u * W from chunk sums W[0..splits) in LDS (wave 0 finds
+// it; every thread gets it): *chunk and the remaining target *rem inside it
+// (INFINITY when rounding left u * W past every running sum: then the last
+// chunk with weight, whose last positive entry is drawn).  Returns false if
+// the total is not a usable positive number.
+__device__ bool pick_chunk(const ChainParams& P, const double* W, double u, int* chunk, double* rem)
 {
     __shared__ int32_t sh_chunk;
     __shared__ double sh_t;
     __shared__ int32_t sh_ok;
     if (threadIdx.x < kWave) {
-        // wave 0: total, then the first chunk whose running sum passes u * total
         const int lane = threadIdx.x;
         double tot = 0.0;
         for (int s0 = 0; s0 < P.splits; s0 += kWave) tot += (s0 + lane < P.splits) ? W[s0 + lane] : 0.0;
@@ -1272,17 +1274,27 @@ __device__ int32_t draw_from_chunks(const ChainParams& P, const Draw& d, const d
         }
         if (lane == 0) {
             sh_ok = tot > 0.0 && tot < INFINITY && (found >= 0 || lastpos >= 0);
-            // rounding left t past every running sum: the last positive-weight
-            // token of the last chunk with weight (t = inf finds no crossing)
             sh_chunk = found >= 0 ? found : (lastpos >= 0 ? lastpos : 0);
             sh_t = found >= 0 ? t - before : INFINITY;
         }
     }
     __syncthreads();
-    if (!sh_ok) return -1;
-    const int64_t lo = (int64_t)sh_chunk * P.chunk;
+    *chunk = sh_chunk;
+    *rem = sh_t;
+    return sh_ok != 0;
+}
+
+// Draw with chunk sums W[0..splits) (fp64, in LDS): pick the chunk holding
+// u * W, rescan it.  Returns the token, or -1 if the total is unusable.
+template <int DTT, int DTD>
+__device__ int32_t draw_from_chunks(const ChainParams& P, const Draw& d, const double* W, double u)
+{
+    int c;
+    double rem;
+    if (!pick_chunk(P, W, u, &c, &rem)) return -1;
+    const int64_t lo = (int64_t)c * P.chunk;
     const int64_t hi = (lo + P.chunk < P.vocab) ? lo + P.chunk : P.vocab;
-    return (int32_t)search_range<DTT, DTD>(P, d, lo, hi, sh_t);
+    return (int32_t)search_range<DTT, DTD>(P, d, lo, hi, rem);
 }
 
 // Draw from p of the draw's target row (fallback when a residual has no mass):
@@ -1350,46 +1362,62 @@ __device__ __forceinline__ void residual_issue(const char* tp, const char* dp, c
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Sums one round (every register of both buffers is read) into the wave slots.
+// Residual weight sum of one 16-byte vector pair: max(0, ep - eq Zt/Zd) per
+// entry in fp32, added in entry order.  The final search recomputes exactly
+// this arithmetic, so its running sums agree with the published ones.
+template <int DT>
+__device__ __forceinline__ float residual_vec(const ChainParams& P, const Draw& d, float r32, const uint4& a,
+                                              const uint4& b, float* run = nullptr)
+{
+    constexpr int VEC = vec_of<DT>();
+    float z[VEC], x[VEC];
+    unpack<DT>(a, z);
+    unpack<DT>(b, x);
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+        const float ep = fast_exp2(fmaf(z[k], P.c, -d.Ot));
+        const float eq = fast_exp2(fmaf(x[k], P.c, -d.Od));
+        acc += fmaxf(fmaf(-eq, r32, ep), 0.0f);
+        if (run) run[k] = acc;
+    }
+    return acc;
+}
+
+// Sums one round (every register of both buffers is read) into the wave
+// slots: one sum per (chunk, vector slot) and wave, i.e. per block of 64
+// consecutive vectors.
 template <int DT>
 __device__ __forceinline__ void residual_round(const ChainParams& P, const Draw& d, int c0, int step, int t,
-                                               const uint4* a, const uint4* b, double (*red)[kRound])
+                                               const uint4* a, const uint4* b, double (*red)[kRound * kVecs])
 {
     constexpr int VEC = vec_of<DT>();
     const int lane = t % kWave, wid = t / kWave;
-    double part[kRound];
+    const float r32 = (float)d.ratio;
+    double part[kRound * kVecs];
 #pragma unroll
-    for (int u = 0; u < kRound; ++u) {
-        double acc = 0.0;
+    for (int u = 0; u < kRound; ++u)
 #pragma unroll
         for (int v = 0; v < kVecs; ++v) {
-            float z[VEC], x[VEC];
-            unpack<DT>(a[u * kVecs + v], z);
-            unpack<DT>(b[u * kVecs + v], x);
-            double w = 0.0;
-#pragma unroll
-            for (int k = 0; k < VEC; ++k) {
-                const double ep = (double)fast_exp2(fmaf(z[k], P.c, -d.Ot));
-                const double eq = (double)fast_exp2(fmaf(x[k], P.c, -d.Od));
-                w += fmax(ep - eq * d.ratio, 0.0);
-            }
+            const float w = residual_vec<DT>(P, d, r32, a[u * kVecs + v], b[u * kVecs + v]);
             const int64_t e = (int64_t)(c0 + u * step) * P.chunk + (int64_t)(t + v * kDBlock) * VEC;
-            acc += e < P.vocab ? w : 0.0;
+            part[u * kVecs + v] = wave_total_f64(e < P.vocab ? (double)w : 0.0);
         }
-        part[u] = wave_total_f64(acc);
-    }
     if (lane == kWave - 1)
 #pragma unroll
-        for (int u = 0; u < kRound; ++u) red[wid][u] = part[u];
+        for (int i = 0; i < kRound * kVecs; ++i) red[wid][i] = part[i];
 }
 
-// This workgroup's chunk sums (chunks kk, kk + K, ...) of request r, published;
-// returns true in the workgroup that completes the request's count.
+// This workgroup's residual sums (chunks kk, kk + K, ...) of request r,
+// published as kSubSums per chunk (block q = v * kDWaves + w covers vectors
+// [v * kDBlock + 64 w, + 64) of the chunk, so q runs in entry order); returns
+// true in the workgroup that completes the request's count.
 template <int DT>
 __device__ bool residual_publish(const ChainParams& P, const Draw& d, int r, int kk, int K)
 {
     static_assert(kVecs * kDBlock * 16 == kChunkBytes, "whole vectors per thread per chunk");
-    __shared__ double red[2][kDWaves][kRound];
+    static_assert(kVecs * kDWaves == kSubSums, "one residual sum per wave and vector slot");
+    __shared__ double red[2][kDWaves][kRound * kVecs];
     __shared__ int32_t sLast;
     const int t = threadIdx.x;
     const char* tp = (const char*)row_ptr<DT>(P.logits, d.row_t, P.stride);
@@ -1399,11 +1427,11 @@ __device__ bool residual_publish(const ChainParams& P, const Draw& d, int r, int
     const int stride = K * kRound;                                    // chunk step between rounds
     // round i's sums from the wave slots, after the barrier that follows it
     auto finish = [&](int i, int par) {
-        const int j = i * kRound + t;
-        if (t < kRound && j < n) {
-            double sum = 0.0;
-            for (int w = 0; w < kDWaves; ++w) sum += red[par][w][t];
-            __hip_atomic_store(&P.sums[(int64_t)r * P.splits + kk + j * K], sum, __ATOMIC_RELAXED,
+        const int u = t / kSubSums, q = t % kSubSums;
+        const int j = i * kRound + u;
+        if (u < kRound && j < n) {
+            const double sum = red[par][q % kDWaves][u * kVecs + q / kDWaves];
+            __hip_atomic_store(&P.sums[((int64_t)r * P.splits + kk + j * K) * kSubSums + q], sum, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
     };
@@ -1433,19 +1461,110 @@ __device__ bool residual_publish(const ChainParams& P, const Draw& d, int r, int
     return sLast != 0;
 }
 
-// The request's chunk sums into W (the drawing workgroup): a sum still -1 is
-// not yet visible and is read again (a bounded wait that in practice never
-// spins).
-__device__ void residual_collect(const ChainParams& P, int r, double* W)
+// One published residual sum; a sum still -1 is not yet visible and is read
+// again (a bounded wait that in practice never spins).
+__device__ __forceinline__ double residual_load(const double* w)
 {
-    for (int j = threadIdx.x; j < P.splits; j += kDBlock) {
-        double* w = &P.sums[(int64_t)r * P.splits + j];
-        double v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (int tries = 0; v < 0.0 && tries < (1 << 20); ++tries)
-            v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        W[j] = v;
+    double v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int tries = 0; v < 0.0 && tries < (1 << 20); ++tries)
+        v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return v;
+}
+
+// Draw of a streamed residual (the drawing workgroup; splits <= kDBlock):
+// thread s gathers chunk s's published sums, the chunk is picked from their
+// totals, then wave 0 picks the block of 64 vectors from the chunk's
+// kSubSums and finds the entry among the block's 64 x VEC with one load of
+// both rows per lane.  Returns the token, or -1 if the residual has no usable
+// mass.
+template <int DT>
+__device__ int32_t residual_draw(const ChainParams& P, const Draw& d, int r, double u, double* W)
+{
+    constexpr int VEC = vec_of<DT>();
+    constexpr int ES = DT == SPEC_F32 ? 4 : 2;
+    __shared__ double sSub[kSubSums];
+    __shared__ int32_t sTok;
+    const int t = threadIdx.x;
+    double mine[kSubSums];
+    if (t < P.splits) {
+        const double* src = P.sums + ((int64_t)r * P.splits + t) * kSubSums;
+        double tot = 0.0;
+#pragma unroll
+        for (int q = 0; q < kSubSums; ++q) {
+            mine[q] = residual_load(src + q);
+            tot += mine[q];
+        }
+        W[t] = tot;
     }
     __syncthreads();
+    int c;
+    double rem;
+    if (!pick_chunk(P, W, u, &c, &rem)) return -1;
+    if (t == c)
+#pragma unroll
+        for (int q = 0; q < kSubSums; ++q) sSub[q] = mine[q];
+    __syncthreads();
+    if (t < kWave) {
+        const int lane = t;
+        // the block of the chunk: inclusive running sums over kSubSums lanes
+        const double x = lane < kSubSums ? sSub[lane] : 0.0;
+        double inc = x;
+#pragma unroll
+        for (int o = 1; o < kSubSums; o <<= 1) {
+            const double y = __shfl_up(inc, o, kWave);
+            if (lane >= o) inc += y;
+        }
+        const uint64_t hit = __ballot(lane < kSubSums && inc > rem);
+        const uint64_t pos = __ballot(lane < kSubSums && x > 0.0);
+        const int q = hit ? (int)__builtin_ctzll(hit) : (pos ? 63 - (int)__builtin_clzll(pos) : 0);
+        const double remq = hit ? rem - __shfl(inc - x, q, kWave) : INFINITY;
+        // lane l: vector v * kDBlock + 64 w + l of chunk c, both rows
+        const int v = q / kDWaves, w = q % kDWaves;
+        const int64_t e = (int64_t)c * P.chunk + ((int64_t)v * kDBlock + 64 * w + lane) * VEC;
+        const int64_t eo = e < P.vocab ? e : 0;
+        const uint4 a = *(const uint4*)((const char*)row_ptr<DT>(P.logits, d.row_t, P.stride) + eo * ES);
+        const uint4 b = *(const uint4*)((const char*)row_ptr<DT>(P.dlogits, d.row_d, P.dstride) + eo * ES);
+        float run[VEC];
+        float wl = residual_vec<DT>(P, d, (float)d.ratio, a, b, run);
+        if (e >= P.vocab) {
+            wl = 0.0f;
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) run[k] = 0.0f;
+        }
+        // running sum over the lanes (fp64), then the first lane that passes
+        double li = (double)wl;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const double y = __shfl_up(li, o, kWave);
+            if (lane >= o) li += y;
+        }
+        const double before = li - (double)wl;
+        const uint64_t cross = __ballot(wl > 0.0f && li > remq);
+        const uint64_t lpos = __ballot(wl > 0.0f);
+        // the entry: the first of the lane whose running sum passes, else (rounding) its last positive one
+        auto entry = [&](bool search) {
+            int k = -1;
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                const bool positive = run[j] > (j ? run[j - 1] : 0.0f);
+                if (positive && (k < 0 || !search) && (!search || before + (double)run[j] > remq)) k = j;
+            }
+            if (k < 0)
+#pragma unroll
+                for (int j = 0; j < VEC; ++j)
+                    if (run[j] > (j ? run[j - 1] : 0.0f)) k = j;
+            return (int32_t)(e + (k < 0 ? 0 : k));
+        };
+        if (cross) {
+            if (lane == (int)__builtin_ctzll(cross)) sTok = entry(true);
+        } else if (lpos) {
+            if (lane == 63 - (int)__builtin_clzll(lpos)) sTok = entry(false);   // rounding: the block's last positive entry
+        } else if (lane == 0) {
+            sTok = -1;
+        }
+    }
+    __syncthreads();
+    return sTok;
 }
 
 // ---------------------------------------------------------------------------
@@ -1460,10 +1579,8 @@ constexpr int kMergeLanes = 8;   // lanes that merge one row's chunk partials
 // the first rejection (cheap, and identical); workgroup 0 writes the slot
 // outputs and draws and commits, except that a probabilistic residual is
 // summed by all K and drawn by the last of them to finish.
-// Three workgroups of 8 waves per compute unit: 6 waves per SIMD, which caps
-// registers at 80.
 template <int DTT, int DTD>
-__global__ __launch_bounds__(kDBlock) __attribute__((amdgpu_waves_per_eu(6))) void k_decide(ChainParams P)
+__global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
 {
     const int r = blockIdx.x;
     const int kk = blockIdx.y, K = gridDim.y;
@@ -1660,19 +1777,25 @@ __global__ __launch_bounds__(kDBlock) __attribute__((amdgpu_waves_per_eu(6))) vo
     // which workgroup draws: the lead, or for a streamed residual the last
     // of the K to finish its chunks
     bool streamed = false;
-    if constexpr (DTT == DTD) streamed = d.mode == 2 && P.coal;
+    if constexpr (DTT == DTD) streamed = d.mode == 2 && P.coal && P.splits <= kDBlock;
     if (streamed) {
         const bool drawer = residual_publish<DTT>(P, d, r, kk, K);
         if (!drawer) {
             // the drawing workgroup reports the request's flags (it has them all)
             return;
         }
-        residual_collect(P, r, sW);
     } else if (!lead) {
         return;
     }
-    if (d.mode != 0) {
-        if (d.mode == 2 && !streamed) {
+    if (streamed) {
+        last = residual_draw<DTT>(P, d, r, (double)P.u_smp[r], sW);
+        if (last < 0) {
+            // the residual had no mass (not reachable in exact arithmetic): draw from p
+            if (t == 0) sFlags |= SPEC_FLAG_RESIDUAL_ZERO;
+            last = draw_from_p<DTT, DTD>(P, d, sW, (double)P.u_smp[r]);
+        }
+    } else if (d.mode != 0) {
+        if (d.mode == 2) {
             // residual max(0, p - q) of rows that do not take the vector path: chunk by chunk
             for (int s = 0; s < P.splits; ++s) {
                 const int64_t lo = (int64_t)s * P.chunk;
@@ -1681,7 +1804,7 @@ __global__ __launch_bounds__(kDBlock) __attribute__((amdgpu_waves_per_eu(6))) vo
                 if (t == 0) sW[s] = x;
             }
             __syncthreads();
-        } else if (d.mode != 2) {
+        } else {
             // chunk sums of the row from its partials; the y chunk is rescanned without y
             const Partial* row = rp + nacc * rr;
             for (int s = t; s < P.splits; s += kDBlock) {
@@ -2028,13 +2151,13 @@ static int elem_bytes(int dt) { return dt == SPEC_F32 ? 4 : 2; }
 static size_t plan_bytes(int64_t rows) { return align256((size_t)rows * sizeof(int2)) + align256(sizeof(int32_t)); }
 
 // Verify workspace: partials [bs, NR, splits] | row prefix [bs + 1] | row plan [bs * NR] |
-// residual chunk sums [bs, splits] | residual counters [bs]
+// residual sums [bs, splits, kSubSums] | residual counters [bs]
 size_t spec_verify_chain_ws(int32_t bs, int32_t vocab, int32_t ld, int32_t dtype)
 {
     RowSplit sp = row_split(vocab, elem_bytes(dtype));
     const int NR = 2 * ld + 1;
     return align256((size_t)bs * NR * sp.splits * sizeof(Partial)) + align256((size_t)(bs + 1) * sizeof(int32_t)) +
-           plan_bytes((int64_t)bs * NR) + align256((size_t)bs * sp.splits * sizeof(double)) +
+           plan_bytes((int64_t)bs * NR) + align256((size_t)bs * sp.splits * kSubSums * sizeof(double)) +
            align256((size_t)bs * sizeof(uint32_t));
 }
 
@@ -2073,7 +2196,7 @@ int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st)
     int32_t* plan_count = (int32_t*)(ws + align256((size_t)a->bs * NR * sizeof(int2)));
     ws += plan_bytes((int64_t)a->bs * NR);
     P.sums = (double*)ws;
-    ws += align256((size_t)a->bs * sp.splits * sizeof(double));
+    ws += align256((size_t)a->bs * sp.splits * kSubSums * sizeof(double));
     P.done = (uint32_t*)ws;
     P.NR = NR; P.splits = sp.splits; P.chunk = sp.chunk;
     P.t_aligned = aligned16(a->logits, a->row_stride, a->dtype);
@@ -2101,8 +2224,8 @@ int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st)
     launch_stats(S, a->dtype, at, a->draft_dtype, ad, draft, P.greedy, a->ld + 1, draft ? a->ld : 0,
                  a->bs + slots + (draft ? slots : 0), sp, gpre, L);
     const int tt = a->dtype, dd = P.dlogits ? a->draft_dtype : a->dtype;
-    // residual chunks shared by K workgroups per request, about 3 each
-    const int K = draft && P.coal ? std::min(16, std::max(1, (sp.splits + 2) / 3)) : 1;
+    // residual chunks shared by K workgroups per request, about 5 each
+    const int K = draft && P.coal && sp.splits <= kDBlock ? std::min(16, std::max(1, (sp.splits + 4) / 5)) : 1;
     const dim3 g(a->bs, K), b(kDBlock);
     if (tt == SPEC_F32 && dd == SPEC_F32) hipLaunchKernelGGL((k_decide<SPEC_F32, SPEC_F32>), g, b, 0, st, P);
     else if (tt == SPEC_F32) hipLaunchKernelGGL((k_decide<SPEC_F32, SPEC_BF16>), g, b, 0, st, P);
