@@ -2,18 +2,21 @@
 // Section 4.2 match features; Algorithm 1, NGRAMSCAN).
 //
 // One workgroup of 1024 threads per query, one launch:
-//   * the query's trailing copy_cap tokens are staged in LDS;
 //   * each thread tests end positions j = t, t + 1024, ...: it loads the token
 //     at j for a batch of 16 positions (independent coalesced loads, one memory
-//     round trip per batch, the first issued before the suffix is staged); the
-//     batch (16,384 tokens) is staged in LDS as well, so that the backward
-//     comparisons read LDS.  For the rare hits a thread compares up to 4
-//     tokens backwards itself; positions still matching after 4 go to a
-//     candidate list that whole waves extend 64 tokens per step with a ballot
-//     (compared up to min(j + 1, copy_cap));
+//     round trip per batch; when query q is simply request q the first batch
+//     goes out before the context length is known), and the batch (16,384
+//     tokens) is staged in LDS so that every later comparison reads LDS;
+//   * the query's trailing copy_cap tokens are staged in LDS as well, from the
+//     window when the whole text fits in it;
+//   * for the rare hits a thread compares up to 4 tokens backwards itself;
+//     positions still matching after 4 go to a candidate list that whole waves
+//     extend 64 tokens per step with a ballot (compared up to
+//     min(j + 1, copy_cap));
 //   * a match of length l >= n_min becomes the key (l << 32 | j), so "longest,
 //     then latest" is the largest key; the workgroup keeps the top two;
-//   * thread 0 derives (n, a, m, j) and the first lanes copy the draft.
+//   * thread 0 derives (n, a, m, j) and the first lanes copy the draft, from
+//     the window when it holds the continuation.
 #include "common.hpp"
 
 namespace spec {
@@ -72,9 +75,22 @@ constexpr int kWin = kScanBlock * kBatch;   // tokens of one batch, staged in LD
 constexpr int kPre = 4;          // tokens each thread compares before handing a match to its wave
 constexpr int kMaxCand = 2048;   // candidate list in LDS; overflow is extended by the thread itself
 
+// PLAIN: query q is request q and there is no extra text, so the first batch
+// can be addressed before the length arrives (positions clamped into the row).
+template <bool PLAIN>
 __global__ __launch_bounds__(kScanBlock) void k_ngram(NgramParams P)
 {
     const int q = blockIdx.x;
+    int32_t v[kBatch];
+    if constexpr (PLAIN) {
+        const int32_t* row = P.ctx + (int64_t)q * P.ctx_stride;
+        const int64_t last = P.ctx_stride - 1;   // >= 0 (checked by the host)
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t j = threadIdx.x + (int64_t)u * kScanBlock;
+            v[u] = row[j < last ? j : last];
+        }
+    }
     const Text x = query_text(P, q);
     __shared__ int32_t suf[SPEC_MAX_CAP];
     __shared__ int32_t win[kWin];
@@ -84,20 +100,22 @@ __global__ __launch_bounds__(kScanBlock) void k_ngram(NgramParams P)
     const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
     const int64_t jend = x.n - 1;                 // end positions j < n - 1
     const int64_t ns = x.n < P.cap ? x.n : P.cap;
-    // batch loads: kBatch independent loads per thread; past the end they
-    // read position jend - 1 (in bounds) and are masked off later
-    int32_t v[kBatch];
+    // batch loads: kBatch independent loads per thread; past the text they
+    // read its last position (in bounds) and are masked off later, so a
+    // window holds every position of the text it covers
     auto load_batch = [&](int64_t base) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int64_t j = base + threadIdx.x + (int64_t)u * kScanBlock;
-            v[u] = tok(x, j < jend ? j : jend - 1);
+            v[u] = tok(x, j < x.n ? j : x.n - 1);
         }
     };
-    if (jend > 0) load_batch(0);   // in flight while the suffix is staged
-    for (int64_t i = threadIdx.x; i < ns; i += kScanBlock) suf[i] = tok(x, x.n - 1 - i);
+    if (!PLAIN && jend > 0) load_batch(0);   // in flight while the suffix is staged
+    const bool suf_in_win = x.n <= kWin;
+    if (!suf_in_win)
+        for (int64_t i = threadIdx.x; i < ns; i += kScanBlock) suf[i] = tok(x, x.n - 1 - i);
     if (threadIdx.x == 0) n_cand = 0;
-    // token at position p < jend: from the staged window when it holds p
+    // token at position p < n: from the staged window when it holds p
     int64_t wbase = 0;
     auto at = [&](int64_t p) -> int32_t { return (p >= wbase && p < wbase + kWin) ? win[p - wbase] : tok(x, p); };
     Top2 best{0, 0};
@@ -112,6 +130,10 @@ __global__ __launch_bounds__(kScanBlock) void k_ngram(NgramParams P)
             for (int u = 0; u < kBatch; ++u) win[threadIdx.x + u * kScanBlock] = v[u];
             wbase = base;
             __syncthreads();
+            if (base == 0 && suf_in_win) {
+                for (int64_t i = threadIdx.x; i < ns; i += kScanBlock) suf[i] = win[x.n - 1 - i];
+                __syncthreads();
+            }
             const int32_t s0 = suf[0];
             uint32_t hits = 0;
 #pragma unroll
@@ -181,12 +203,12 @@ __global__ __launch_bounds__(kScanBlock) void k_ngram(NgramParams P)
         const int64_t j = (int64_t)(t.a & 0xFFFFFFFFu);
         const int64_t avail = x.n - 1 - j;
         const int64_t len = avail < P.max_draft ? avail : P.max_draft;
-        for (int k = lane; k < P.max_draft; k += kWave) d[k] = (k < len) ? tok(x, j + 1 + k) : -1;
+        for (int k = lane; k < P.max_draft; k += kWave) d[k] = (k < len) ? at(j + 1 + k) : -1;
         if (lane == 0) {
             int a = 1;
             if (t.b != 0) {
                 const int64_t jr = (int64_t)(t.b & 0xFFFFFFFFu);
-                a = tok(x, jr + 1) == tok(x, j + 1);
+                a = at(jr + 1) == at(j + 1);
             }
             P.draft_len[q] = (int32_t)len;
             P.feat[4 * (int64_t)q + 0] = (int32_t)(l < P.n_max ? l : P.n_max);
@@ -212,6 +234,9 @@ int spec_ngram_launch(const spec_ngram_args* a, hipStream_t st)
     P.extra = a->extra; P.extra_stride = a->extra ? a->extra_stride : 0; P.extra_len = a->extra_len;
     P.n_min = a->n_min; P.n_max = a->n_max; P.max_draft = a->max_draft; P.cap = a->copy_cap;
     P.draft = a->draft; P.draft_len = a->draft_len; P.feat = a->feat;
-    hipLaunchKernelGGL(k_ngram, dim3(a->nq), dim3(kScanBlock), 0, st, P);
+    if (!a->query_req && !a->extra && a->nq == a->bs && a->ctx_stride >= 1)
+        hipLaunchKernelGGL(k_ngram<true>, dim3(a->nq), dim3(kScanBlock), 0, st, P);
+    else
+        hipLaunchKernelGGL(k_ngram<false>, dim3(a->nq), dim3(kScanBlock), 0, st, P);
     return spec_record_hip_error(hipGetLastError());
 }

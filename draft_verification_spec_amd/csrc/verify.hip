@@ -50,6 +50,15 @@ struct Partial {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// One 16-byte vector of logits that is read once: a non-temporal load, which
+// streams markedly faster than a plain load on gfx950.
+__device__ __forceinline__ uint4 load_stream(const void* p)
+{
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <int DT>
 __device__ __forceinline__ float load1(const void* base, int64_t e)
 {
@@ -67,11 +76,11 @@ __device__ __forceinline__ void loadv(const void* base, int64_t e, float* v)
         v[0] = load1<DT>(base, e);
     } else if constexpr (DT == SPEC_F32) {
         static_assert(VEC == 4, "fp32 vectors are 16 bytes");
-        float4 x = *(const float4*)((const float*)base + e);
-        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+        const uint4 x = load_stream((const float*)base + e);
+        v[0] = __uint_as_float(x.x); v[1] = __uint_as_float(x.y); v[2] = __uint_as_float(x.z); v[3] = __uint_as_float(x.w);
     } else {
         static_assert(VEC == 8, "bf16 vectors are 16 bytes");
-        uint4 x = *(const uint4*)((const uint16_t*)base + e);
+        const uint4 x = load_stream((const uint16_t*)base + e);
         v[0] = __uint_as_float(x.x << 16); v[1] = __uint_as_float(x.x & 0xFFFF0000u);
         v[2] = __uint_as_float(x.y << 16); v[3] = __uint_as_float(x.y & 0xFFFF0000u);
         v[4] = __uint_as_float(x.z << 16); v[5] = __uint_as_float(x.z & 0xFFFF0000u);
@@ -228,7 +237,7 @@ __device__ __forceinline__ void load_raw(const void* row, int64_t e, uint4* raw)
     constexpr int64_t STEP = (int64_t)kBlock * VEC;
     const char* b = (const char*)row + e * (DT == SPEC_F32 ? 4 : 2);
 #pragma unroll
-    for (int u = 0; u < kTile; ++u) raw[u] = *(const uint4*)(b + u * STEP * (DT == SPEC_F32 ? 4 : 2));
+    for (int u = 0; u < kTile; ++u) raw[u] = load_stream(b + u * STEP * (DT == SPEC_F32 ? 4 : 2));
 }
 
 // Thread t of a 256-thread group folds its share of [lo, hi) (the whole
@@ -645,7 +654,7 @@ __device__ __forceinline__ void group_issue(const void* logits, int64_t stride, 
 #pragma unroll
     for (int u = 0; u < kTile; ++u) {
         const int64_t e = e0 + u * STEP;
-        raw[u] = *(const uint4*)(rp + (e < hi ? e : 0) * ES);
+        raw[u] = load_stream(rp + (e < hi ? e : 0) * ES);
     }
 }
 
@@ -1354,8 +1363,8 @@ __device__ __forceinline__ void residual_issue(const char* tp, const char* dp, c
         for (int v = 0; v < kVecs; ++v) {
             const int64_t e = (int64_t)(c0 + u * step) * P.chunk + (int64_t)(t + v * kDBlock) * VEC;
             const int64_t eo = e < P.vocab ? e : 0;   // past the row: its first vector, unused
-            a[u * kVecs + v] = *(const uint4*)(tp + eo * ES);
-            b[u * kVecs + v] = *(const uint4*)(dp + eo * ES);
+            a[u * kVecs + v] = load_stream(tp + eo * ES);
+            b[u * kVecs + v] = load_stream(dp + eo * ES);
         }
     // keep the scheduler from hoisting the previous round's arithmetic above
     // these loads (which would wait for everything in flight first)
