@@ -222,20 +222,21 @@ def headline(K, W, hip, eager_only):
     ctx, ctx_len = g(c["ctx"]), g(c["ctx_len"])
     ctx_len_new = torch.empty_like(ctx_len)
     stream = torch.cuda.Stream()
-    bufs = {"ws_v": torch.empty(1 << 26, dtype=torch.uint8, device=dev),
-            "ws_ng": torch.empty(1 << 20, dtype=torch.uint8, device=dev)}
+    bufs = {"ws_v": torch.empty(1 << 26, dtype=torch.uint8, device=dev)}
 
     def step(prof=None):
+        # verification, commit and the next n-gram draft over the committed
+        # contexts, in one call (the draft runs in the drawing workgroups)
         out = S.spec_verify_chain(target, rb, tokens, n_slots, c["temperature"], u_accept=u_acc, u_sample=u_smp,
                                   slot_flags=flags, draft_logits=draft, draft_row_base=drb, ctx=ctx,
                                   ctx_len=ctx_len, ctx_len_out=ctx_len_new, out=bufs.get("vf"),
                                   out_flags=bufs.get("vfl"), write_flags=True, workspace=bufs["ws_v"],
-                                  prof_events=prof)
-        d = S.spec_ngram_draft(ctx, ctx_len_new, c["n_min"], c["n_max"], c["max_draft"], c["copy_cap"],
-                               out=bufs.get("ng"), workspace=bufs["ws_ng"])
-        bufs.setdefault("vf", {k: v for k, v in out.items() if k != "out_flags"})
+                                  prof_events=prof, ngram=(c["n_min"], c["n_max"], c["max_draft"], c["copy_cap"]),
+                                  ngram_out=bufs.get("ng"))
+        bufs.setdefault("vf", {k: v for k, v in out.items() if k not in ("out_flags", "ngram_draft", "ngram_len",
+                                                                          "ngram_feat")})
         bufs.setdefault("vfl", out["out_flags"])
-        bufs.setdefault("ng", d)
+        bufs.setdefault("ng", (out["ngram_draft"], out["ngram_len"], out["ngram_feat"]))
 
     with torch.cuda.stream(stream):
         step()

@@ -72,7 +72,9 @@ class VerifyArgs(C.Structure):
                 ("tokens", vp), ("slot_flags", vp), ("ld", i32), ("n_slots", vp), ("max_slots", i32), ("u_accept", vp),
                 ("u_sample", vp), ("out_tokens", vp), ("out_num", vp), ("out_accepted", vp), ("out_p", vp),
                 ("out_q", vp), ("out_flags", vp), ("write_flags", i32), ("ctx", vp), ("ctx_stride", i64),
-                ("ctx_len", vp), ("ctx_len_out", vp), ("ctx_cap", i32), ("prof_begin", vp), ("prof_end", vp),
+                ("ctx_len", vp), ("ctx_len_out", vp), ("ctx_cap", i32), ("ngram_draft", vp),
+                ("ngram_draft_len", vp), ("ngram_feat", vp), ("ngram_n_min", i32), ("ngram_n_max", i32),
+                ("ngram_max_draft", i32), ("ngram_copy_cap", i32), ("prof_begin", vp), ("prof_end", vp),
                 ("workspace", vp), ("workspace_bytes", sz)]
 
 
@@ -305,13 +307,17 @@ def spec_allocate_budget(mode="chain", **kw):
 def spec_verify_chain(logits, row_base, tokens, n_slots, temperature, u_accept=None, u_sample=None,
                       slot_flags=None, draft_logits=None, draft_row_base=None, out_flags=None,
                       ctx=None, ctx_len=None, ctx_cap=None, ctx_len_out=None, out=None, workspace=None,
-                      stream=None, prof_events=None, max_slots=0, write_flags=False):
+                      stream=None, prof_events=None, max_slots=0, write_flags=False, ngram=None, ngram_out=None):
     """Rejection-sampling verification of one chain per request (optional commit into ctx).
     ``prof_events``: optional pair of raw hipEvent_t handles recorded around the
     row-statistics pass.  ``max_slots``: optional bound of the total slots
     (e.g. the allocation budget), which sizes the statistics grid.
     ``write_flags``: out_flags receive this call's flags instead of OR-ing
-    them in (a new out_flags tensor is then not zeroed first)."""
+    them in (a new out_flags tensor is then not zeroed first).
+    ``ngram``: optional (n_min, n_max, max_draft, copy_cap): with a commit, the
+    next n-gram draft of every request over its committed context is computed
+    in the same launch and returned as out["ngram_draft"], out["ngram_len"],
+    out["ngram_feat"] (into ``ngram_out``, a (draft, len, feat) triple, if given)."""
     lg = _rows2d(logits, "logits")
     _dev(row_base, torch.int64, "row_base", 1)
     _dev(tokens, torch.int32, "tokens", 2)
@@ -355,12 +361,25 @@ def spec_verify_chain(logits, row_base, tokens, n_slots, temperature, u_accept=N
         if ctx_len_out is not None:
             _dev(ctx_len_out, torch.int32, "ctx_len_out", 1)
             a.ctx_len_out = _ptr(ctx_len_out)
+    if ngram is not None:
+        if ctx is None:
+            raise ValueError("the fused n-gram draft needs the commit (ctx)")
+        n_min, n_max, max_draft, copy_cap = (int(x) for x in ngram)
+        if ngram_out is None:
+            ngram_out = (torch.empty((bs, max_draft), dtype=torch.int32, device=dev),
+                         torch.empty(bs, dtype=torch.int32, device=dev),
+                         torch.empty((bs, 4), dtype=torch.int32, device=dev))
+        nd, nl, nf = ngram_out
+        a.ngram_draft, a.ngram_draft_len, a.ngram_feat = _ptr(nd), _ptr(nl), _ptr(nf)
+        a.ngram_n_min, a.ngram_n_max, a.ngram_max_draft, a.ngram_copy_cap = n_min, n_max, max_draft, copy_cap
     if prof_events is not None:
         a.prof_begin, a.prof_end = prof_events
     ws, w = _workspace(OP_VERIFY_CHAIN, a, dev, workspace)
     if w:
         a.workspace, a.workspace_bytes = w
     _check(lib().spec_verify_chain(C.byref(a), _stream(dev, stream)))
+    if ngram is not None:
+        out["ngram_draft"], out["ngram_len"], out["ngram_feat"] = ngram_out
     return out
 
 

@@ -99,6 +99,13 @@ static int check_verify(const spec_verify_args* a)
     REQUIRE(a->temperature == 0.0f || (a->u_accept && a->u_sample));
     REQUIRE(a->out_tokens && a->out_num && a->out_accepted && a->out_flags);
     if (a->ctx) REQUIRE(a->ctx_len && a->ctx_cap >= 0 && a->ctx_cap <= a->ctx_stride);
+    if (a->ngram_draft) {
+        REQUIRE(a->ctx && a->ctx_stride >= 1 && a->ctx_stride < ((int64_t)1 << 31));
+        REQUIRE(a->ngram_draft_len && a->ngram_feat);
+        REQUIRE(a->ngram_n_min >= 1 && a->ngram_n_max >= a->ngram_n_min);
+        REQUIRE(a->ngram_max_draft >= 1 && a->ngram_max_draft <= SPEC_MAX_DRAFT);
+        REQUIRE(a->ngram_copy_cap >= a->ngram_n_min && a->ngram_copy_cap <= SPEC_MAX_CAP);
+    }
     return SPEC_OK;
 }
 

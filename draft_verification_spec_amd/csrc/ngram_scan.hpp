@@ -1,0 +1,193 @@
+// The n-gram scan of one query by one workgroup of NT threads (Hybrid Spark,
+// Section 4.1 "One step" and Section 4.2 match features; Algorithm 1,
+// NGRAMSCAN), shared by the drafter kernel and by the chain verifier, which
+// drafts each request's next n-gram chain right after its commit.
+//
+//   * each thread tests end positions j = t, t + NT, ...: it loads the token at
+//     j for a batch of 16 positions (independent coalesced loads, one memory
+//     round trip per batch) and the batch (16 NT tokens) is staged in LDS, so
+//     that every later comparison reads LDS;
+//   * the query's trailing copy_cap tokens are staged in LDS as well, from the
+//     window when the whole text fits in it;
+//   * for the rare hits a thread compares up to 4 tokens backwards itself;
+//     positions still matching after 4 go to a candidate list that whole waves
+//     extend 64 tokens per step with a ballot (compared up to
+//     min(j + 1, copy_cap));
+//   * a match of length l >= n_min becomes the key (l << 32 | j), so "longest,
+//     then latest" is the largest key; the workgroup keeps the top two;
+//   * thread 0 derives (n, a, m, j) and the first lanes copy the draft, from
+//     the window when it holds the continuation.
+#pragma once
+
+#include "common.hpp"
+
+namespace spec {
+
+constexpr int kBatch = 16;       // positions per thread per batch (at most 32: a bit mask of hits)
+constexpr int kPre = 4;          // tokens each thread compares before handing a match to its wave
+constexpr int kMaxCand = 2048;   // candidate list in LDS; overflow is extended by the thread itself
+
+struct Text {
+    const int32_t* a;  // context row
+    int64_t na;
+    const int32_t* b;  // extra row (may be null)
+    int64_t n;         // total length
+};
+
+// Token p of the text: the address is selected first, so a batch of these is
+// a batch of independent loads rather than branches around them.
+__device__ __forceinline__ int32_t tok(const Text& x, int64_t p)
+{
+    const uintptr_t pa = (uintptr_t)(x.a + p);
+    const uintptr_t pb = (uintptr_t)x.b + (uintptr_t)((p - x.na) * (int64_t)sizeof(int32_t));
+    return *(const int32_t*)(p < x.na ? pa : pb);
+}
+
+template <int NT>
+struct NgramShared {
+    int32_t suf[SPEC_MAX_CAP];
+    Top2 sh[NT / kWave];
+    int32_t cand[kMaxCand];
+    int32_t n_cand;
+};
+
+struct NgramOut {
+    int32_t n_min, n_max, max_draft, cap;
+    int32_t* draft;      // [max_draft]
+    int32_t* draft_len;  // [1]
+    int32_t* feat;       // [4]
+};
+
+// Scans text x with the whole workgroup (every thread calls it): batches of
+// NB positions per thread, so win holds NT * NB tokens of LDS.  With `pre`, v
+// already holds the first batch (positions t + u * NT, any value past the
+// text).
+template <int NT, int NB = kBatch>
+__device__ void ngram_scan(const Text& x, int32_t* win, NgramShared<NT>& S, const NgramOut& O, int32_t (&v)[NB],
+                           bool pre)
+{
+    constexpr int64_t kWin = (int64_t)NT * NB;
+    const int t = threadIdx.x;
+    const int lane = t % kWave, wid = t / kWave;
+    const int64_t jend = x.n - 1;                 // end positions j < n - 1
+    const int64_t ns = x.n < O.cap ? x.n : O.cap;
+    // batch loads: kBatch independent loads per thread; past the text they
+    // read its last position (in bounds) and are masked off later, so a
+    // window holds every position of the text it covers
+    auto load_batch = [&](int64_t base) {
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int64_t j = base + t + (int64_t)u * NT;
+            v[u] = tok(x, j < x.n ? j : x.n - 1);
+        }
+    };
+    if (!pre && jend > 0) load_batch(0);   // in flight while the suffix is staged
+    const bool suf_in_win = x.n <= kWin;
+    if (!suf_in_win)
+        for (int64_t i = t; i < ns; i += NT) S.suf[i] = tok(x, x.n - 1 - i);
+    if (t == 0) S.n_cand = 0;
+    // token at position p < n: from the staged window when it holds p
+    int64_t wbase = 0;
+    auto at = [&](int64_t p) -> int32_t { return (p >= wbase && p < wbase + kWin) ? win[p - wbase] : tok(x, p); };
+    Top2 best{0, 0};
+    if (jend > 0) {
+        // phase 1: first kPre tokens per position, thread-private
+        for (int64_t base = 0; base < jend; base += kWin) {
+            if (base > 0) {
+                __syncthreads();   // the previous window is no longer read
+                load_batch(base);
+            }
+#pragma unroll
+            for (int u = 0; u < NB; ++u) win[t + u * NT] = v[u];
+            wbase = base;
+            __syncthreads();
+            if (base == 0 && suf_in_win) {
+                for (int64_t i = t; i < ns; i += NT) S.suf[i] = win[x.n - 1 - i];
+                __syncthreads();
+            }
+            const int32_t s0 = S.suf[0];
+            uint32_t hits = 0;
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                const int64_t j = base + t + (int64_t)u * NT;
+                hits |= (uint32_t)(j < jend && v[u] == s0) << u;
+            }
+            while (hits) {
+                const int u = __builtin_ctz(hits);
+                hits &= hits - 1;
+                const int64_t j = base + t + (int64_t)u * NT;
+                const int64_t lim = (j + 1 < O.cap) ? j + 1 : O.cap;
+                int64_t l = 1;
+                while (l < lim && l < kPre && at(j - l) == S.suf[l]) ++l;
+                if (l == kPre && l < lim) {
+                    const int c = atomicAdd(&S.n_cand, 1);
+                    if (c < kMaxCand) {
+                        S.cand[c] = (int32_t)j;
+                        continue;
+                    }
+                    while (l < lim && at(j - l) == S.suf[l]) ++l;   // list full: extend here
+                }
+                if (l >= O.n_min) best = top2_insert(best, ((uint64_t)l << 32) | (uint64_t)j);
+            }
+        }
+    }
+    __syncthreads();
+    // phase 2: each wave extends listed candidates 64 tokens per step
+    const int nc = S.n_cand < kMaxCand ? S.n_cand : kMaxCand;
+    for (int c = wid; c < nc; c += NT / kWave) {
+        const int64_t j = S.cand[c];
+        const int64_t lim = (j + 1 < O.cap) ? j + 1 : O.cap;
+        int64_t l = kPre;
+        for (;;) {
+            const int64_t i = l + lane;
+            const bool eq = i < lim && at(j - i) == S.suf[i];
+            const uint64_t miss = ~__ballot(eq);
+            if (miss == 0) {
+                l += kWave;
+                continue;
+            }
+            l += (int64_t)__builtin_ctzll(miss);
+            break;
+        }
+        if (l > lim) l = lim;
+        if (lane == 0 && l >= O.n_min) best = top2_insert(best, ((uint64_t)l << 32) | (uint64_t)j);
+    }
+    best = wave_top2(best);
+    if (lane == 0) S.sh[wid] = best;
+    __syncthreads();
+    if (wid == 0) {
+        Top2 tb = lane < NT / kWave ? S.sh[lane] : Top2{0, 0};
+        tb = wave_top2(tb);
+        int32_t* d = O.draft;
+        if (tb.a == 0) {
+            for (int k = lane; k < O.max_draft; k += kWave) d[k] = -1;
+            if (lane == 0) {
+                *O.draft_len = 0;
+                O.feat[0] = 0;
+                O.feat[1] = 0;
+                O.feat[2] = 0;
+                O.feat[3] = -1;
+            }
+        } else {
+            const int64_t l = (int64_t)(tb.a >> 32);
+            const int64_t j = (int64_t)(tb.a & 0xFFFFFFFFu);
+            const int64_t avail = x.n - 1 - j;
+            const int64_t len = avail < O.max_draft ? avail : O.max_draft;
+            for (int k = lane; k < O.max_draft; k += kWave) d[k] = (k < len) ? at(j + 1 + k) : -1;
+            if (lane == 0) {
+                int a = 1;
+                if (tb.b != 0) {
+                    const int64_t jr = (int64_t)(tb.b & 0xFFFFFFFFu);
+                    a = at(jr + 1) == at(j + 1);
+                }
+                *O.draft_len = (int32_t)len;
+                O.feat[0] = (int32_t)(l < O.n_max ? l : O.n_max);
+                O.feat[1] = a;
+                O.feat[2] = (l >= O.n_max) ? (int32_t)l : 0;
+                O.feat[3] = (int32_t)j;
+            }
+        }
+    }
+}
+
+}  // namespace spec

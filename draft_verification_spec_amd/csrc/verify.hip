@@ -26,13 +26,16 @@
 //                  point-mass residuals from the chunk sums it already has
 //                  plus one chunk rescan; a probabilistic residual
 //                  max(0, p - q) by streaming its target and draft rows for
-//                  the chunk sums first.  Then it commits.
+//                  the chunk sums first.  Then it commits and, when asked,
+//                  drafts the request's next n-gram chain from the committed
+//                  context (ngram_scan) in the same workgroup.
 #include <algorithm>
 #include <mutex>
 #include <utility>
 #include <vector>
 
 #include "common.hpp"
+#include "ngram_scan.hpp"
 
 namespace spec {
 
@@ -1051,6 +1054,8 @@ struct ChainParams {
     int32_t* out_tokens; int32_t* out_num; int32_t* out_acc; float* out_p; float* out_q; uint32_t* out_flags;
     int32_t write_flags;        // out_flags written (by the drawing workgroup) rather than OR-ed
     int32_t* ctx; int64_t ctx_stride; const int32_t* ctx_len; int32_t* ctx_len_out; int32_t ctx_cap;
+    int32_t* ng_draft; int32_t* ng_len; int32_t* ng_feat;   // next n-gram draft after the commit, or null
+    int32_t ng_min, ng_max, ng_ld, ng_cap;
     Partial* part; int32_t NR; int32_t splits; int64_t chunk;
     double* sums;               // [bs, splits, kSubSums] residual sums (-1 until written)
     uint32_t* done;             // [bs] workgroups of a request done with their residual chunks
@@ -1580,7 +1585,11 @@ __device__ int32_t residual_draw(const ChainParams& P, const Draw& d, int r, dou
 // decide, draw, commit: one workgroup per request
 // ---------------------------------------------------------------------------
 
-constexpr int kMaxPartsLds = 2048;   // partials of one request staged in LDS (32 KB)
+constexpr int kMaxPartsLds = 2176;   // partials of one request staged in LDS (34 KB)
+// The fused n-gram scan takes 17 positions per thread per batch: its window
+// (8,704 tokens, in the partials' LDS) holds a context of 8,192 tokens and
+// the tokens one step appends, so such a text needs one batch.
+constexpr int kNgBatch = 17;
 
 constexpr int kMergeLanes = 8;   // lanes that merge one row's chunk partials
 
@@ -1796,6 +1805,19 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
     } else if (!lead) {
         return;
     }
+    // the first batch of the n-gram window (the request's text before the
+    // commit), in flight while the draw runs; the committed tokens are
+    // patched in afterwards
+    int32_t ngv[kNgBatch];
+    if (P.ng_draft) {
+        const int32_t* row = P.ctx + (int64_t)r * P.ctx_stride;
+        const int64_t lastp = P.ctx_stride - 1;   // >= 0 (checked by the host)
+#pragma unroll
+        for (int u = 0; u < kNgBatch; ++u) {
+            const int64_t j = t + (int64_t)u * kDBlock;
+            ngv[u] = row[j < lastp ? j : lastp];
+        }
+    }
     if (streamed) {
         last = residual_draw<DTT>(P, d, r, (double)P.u_smp[r], sW);
         if (last < 0) {
@@ -1853,6 +1875,32 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
     if (t == 0) {
         if (P.write_flags) P.out_flags[r] = fl;
         else if (fl) atomicOr(&P.out_flags[r], fl);
+    }
+    if (P.ng_draft) {
+        // the next n-gram draft over the committed context: its stores are
+        // visible to the workgroup after the barrier, and the partials' and
+        // chunk sums' LDS is free for the scan's window and lists
+        static_assert(sizeof(sp) >= sizeof(int32_t) * kDBlock * kNgBatch, "scan window fits the partials' LDS");
+        static_assert(sizeof(sW) >= sizeof(NgramShared<kDBlock>), "scan lists fit the chunk sums' LDS");
+        const int32_t n = nacc + 1;
+        const bool appended = len0 >= 0 && len0 + n <= P.ctx_cap;   // as the commit decided
+        int64_t nl = appended ? (int64_t)len0 + n : (int64_t)len0;
+        nl = nl < 0 ? 0 : (nl > P.ctx_stride ? P.ctx_stride : nl);
+        if (appended)
+#pragma unroll
+            for (int u = 0; u < kNgBatch; ++u) {
+                const int64_t j = t + (int64_t)u * kDBlock - len0;
+                if (j >= 0 && j < n) ngv[u] = j < nacc ? sTok[j] : last;
+            }
+        Text x;
+        x.a = P.ctx + (int64_t)r * P.ctx_stride; x.na = nl; x.b = nullptr; x.n = nl;
+        NgramOut O;
+        O.n_min = P.ng_min; O.n_max = P.ng_max; O.max_draft = P.ng_ld; O.cap = P.ng_cap;
+        O.draft = P.ng_draft + (int64_t)r * P.ng_ld;
+        O.draft_len = P.ng_len + r;
+        O.feat = P.ng_feat + 4 * (int64_t)r;
+        __syncthreads();
+        ngram_scan<kDBlock, kNgBatch>(x, (int32_t*)sp, *(NgramShared<kDBlock>*)sW, O, ngv, true);
     }
 }
 
@@ -2197,6 +2245,8 @@ int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st)
     P.out_p = a->out_p; P.out_q = a->out_q; P.out_flags = a->out_flags; P.write_flags = a->write_flags;
     P.ctx = a->ctx; P.ctx_stride = a->ctx_stride; P.ctx_len = a->ctx_len;
     P.ctx_len_out = a->ctx_len_out ? a->ctx_len_out : a->ctx_len; P.ctx_cap = a->ctx_cap;
+    P.ng_draft = a->ctx ? a->ngram_draft : nullptr; P.ng_len = a->ngram_draft_len; P.ng_feat = a->ngram_feat;
+    P.ng_min = a->ngram_n_min; P.ng_max = a->ngram_n_max; P.ng_ld = a->ngram_max_draft; P.ng_cap = a->ngram_copy_cap;
     P.part = (Partial*)ws;
     ws += align256((size_t)a->bs * NR * sp.splits * sizeof(Partial));
     int32_t* gpre = (int32_t*)ws;

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 2
+#define SPEC_ABI_VERSION 3
 
 /* ---- return codes ---------------------------------------------------- */
 #define SPEC_OK          0
@@ -252,6 +252,11 @@ typedef struct spec_alloc_args {
  * write_flags).  If ctx is not NULL the
  * emitted tokens are appended to ctx[r] at ctx_len[r] (skipped and flagged if
  * ctx_len + out_num > ctx_cap).  n_slots outside [0, ld] are clamped.
+ * With ngram_draft (which needs ctx), the next step's n-gram draft of every
+ * request ([HS] Section 4.1 "One step": scan the request's own text after the
+ * commit) is computed in the same launch, over the committed context: the
+ * outputs equal spec_ngram_draft's with query q = request q over ctx and the
+ * new lengths, and n-gram parameters as documented there.
  * ======================================================================== */
 typedef struct spec_verify_args {
     int32_t bs;
@@ -293,6 +298,14 @@ typedef struct spec_verify_args {
     int32_t* ctx_len_out;        /* device [bs] or NULL: new lengths go here and
                                     ctx_len is left as it was (NULL = in place)   */
     int32_t ctx_cap;             /* <= ctx_stride                                 */
+    int32_t* ngram_draft;        /* optional next n-gram draft: device
+                                    [bs, ngram_max_draft] or NULL (none)          */
+    int32_t* ngram_draft_len;    /* device [bs]                                   */
+    int32_t* ngram_feat;         /* device [bs, 4]: (n, a, m, j)                  */
+    int32_t ngram_n_min;         /* as n_min, n_max, max_draft and copy_cap of    */
+    int32_t ngram_n_max;         /* spec_ngram_args                               */
+    int32_t ngram_max_draft;
+    int32_t ngram_copy_cap;
     void* prof_begin;            /* optional hipEvent_t pair (created with timing) */
     void* prof_end;              /* attached to the row-statistics kernel's own
                                     dispatch: begin = its start, end = its end    */

@@ -1,0 +1,112 @@
+"""GPU parity of the n-gram draft fused into chain verification: after the
+commit, the drawing workgroup scans each request's committed context.  Its
+outputs must equal the oracle's n-gram draft over the contexts and lengths the
+commit produced (bit-exact, every request), and the verification outputs must
+not change when the draft is fused in."""
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from tests.gpu_helpers import dev, host
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def run_pair(logits, rb, tokens, n_slots, T, ctx, ctx_len, cap, ngram, **kw):
+    """The same verification with and without the fused draft, on copies of
+    the contexts; returns both result dicts and the committed contexts."""
+    import torch
+    import draft_verification_spec_amd as S
+    res = []
+    for fused in (False, True):
+        tc, tl, tn = dev(ctx), dev(ctx_len), dev(np.zeros(len(ctx_len), np.int32))
+        out = S.spec_verify_chain(logits, rb, tokens, n_slots, T, ctx=tc, ctx_len=tl, ctx_cap=cap, ctx_len_out=tn,
+                                  ngram=ngram if fused else None, **kw)
+        torch.cuda.synchronize()
+        r = {k: host(v) for k, v in out.items()}
+        r["ctx"], r["ctx_len"] = host(tc), host(tn)
+        res.append(r)
+    return res
+
+
+def check(plain, fused, ngram):
+    n_min, n_max, L, cap = ngram
+    for k, v in plain.items():
+        assert np.array_equal(v, fused[k]), f"{k} changed by the fused draft"
+    d, dl, f = O.ngram_draft(fused["ctx"], fused["ctx_len"], n_min, n_max, L, cap)
+    assert np.array_equal(fused["ngram_len"], dl), (fused["ngram_len"], dl)
+    assert np.array_equal(fused["ngram_feat"], f)
+    assert np.array_equal(fused["ngram_draft"], d)
+    return dl
+
+
+def test_dense_headline_fused_draft():
+    """The measured step: BS 128, V 151,936, bf16 rows, probabilistic slots,
+    T = 1, 8,192-token contexts, n-gram n 5..15."""
+    c = synth.dense_headline(ctx_extra=64)
+    BS, V, B = c["BS"], c["V"], c["B"]
+    print(f"dense: BS {BS} V {V} ctx {c['ctx'].shape}", flush=True)
+    tgt = synth.as_torch_bf16(c["target_bf16"]).to("cuda:0").reshape(-1, V)
+    dft = synth.as_torch_bf16(c["draft_bf16"]).to("cuda:0").reshape(-1, V)
+    ngram = (c["n_min"], c["n_max"], c["max_draft"], c["copy_cap"])
+    args = (tgt, dev(np.arange(BS, dtype=np.int64) * (B + 1)), dev(c["tokens"]), dev(np.full(BS, B, np.int32)),
+            c["temperature"])
+    kw = dict(u_accept=dev(c["u_acc"]), u_sample=dev(c["u_smp"]), slot_flags=dev(np.zeros((BS, B), np.uint8)),
+              draft_logits=dft, draft_row_base=dev(np.arange(BS, dtype=np.int64) * B), write_flags=True)
+    ctx = c["ctx"].copy()
+    plain, fused = run_pair(*args, ctx, c["ctx_len"], ctx.shape[1], ngram, **kw)
+    check(plain, fused, ngram)
+    # the emitted tokens are random, so the committed suffix rarely recurs;
+    # plant, in every other request, an earlier copy of the last 20 tokens
+    # plus the emitted ones and a continuation, then verify again (the
+    # verification does not read the contexts, so it emits the same tokens)
+    rng = np.random.default_rng(7)
+    for r in range(0, BS, 2):
+        n, L0 = plain["out_num"][r], c["ctx_len"][r]
+        seq = np.concatenate([ctx[r, L0 - 20:L0], plain["out_tokens"][r, :n], rng.integers(0, V, 20)])
+        ctx[r, 1000:1000 + len(seq)] = seq
+    plain, fused = run_pair(*args, ctx, c["ctx_len"], ctx.shape[1], ngram, **kw)
+    dl = check(plain, fused, ngram)
+    assert (dl[0::2] == c["max_draft"]).all() and (fused["ngram_feat"][0::2, 2] >= 20).all()
+
+
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_config0_overflow_and_long_contexts(T):
+    """Commit overflow (the draft then scans the unchanged context), contexts
+    longer than the scan window (three windows), ragged lengths, T = 0 and 1."""
+    c = synth.config0()
+    BS, B, V = c["BS"], c["B"], c["V"]
+    stride = 20100
+    ctx = np.zeros((BS, stride), np.int32)
+    lens = np.array([20003, 511, 19995, 9000], np.int32)
+    for r in range(BS):
+        ctx[r] = np.resize(c["ctx"][r], stride)   # the planted text repeated: long matches
+    cap = np.int32(20003)                          # request 0 is full: its commit overflows
+    ngram = (3, 15, 15, 256)
+    kw = dict(slot_flags=dev(np.zeros((BS, B), np.uint8)), draft_logits=dev(c["draft"]).reshape(-1, V),
+              draft_row_base=dev(np.arange(BS) * B))
+    if T > 0:
+        kw.update(u_accept=dev(c["u_acc"]), u_sample=dev(c["u_smp"]))
+    plain, fused = run_pair(dev(c["target"]).reshape(-1, V), dev(np.arange(BS) * (B + 1)), dev(c["tokens"]),
+                            dev(np.full(BS, B, np.int32)), T, ctx, lens, cap, ngram, **kw)
+    check(plain, fused, ngram)
+    over = (plain["out_flags"].astype(np.uint32) & O.CTX_OVERFLOW) != 0
+    assert over.any() and np.array_equal(fused["ctx_len"][over], lens[over])
+
+
+def test_point_mass_chain_fused_draft():
+    """Point-mass slots (the residual is p without y) and all-accepted bonus
+    draws, fp32 rows at full vocabulary, n = 4."""
+    c = synth.config1()
+    BS, V = c["BS"], c["V"]
+    ng = O.ngram_draft(c["ctx"], c["ctx_len"], 4, 4, 15, 256)
+    toks = np.where(ng[0] >= 0, ng[0], 0).astype(np.int32)
+    stride = c["ctx"].shape[1] + 32
+    ctx = np.zeros((BS, stride), np.int32)
+    ctx[:, :c["ctx"].shape[1]] = c["ctx"]
+    ngram = (4, 4, 15, 256)
+    plain, fused = run_pair(dev(c["ngram_target"]).reshape(-1, V), dev(np.arange(BS) * 16), dev(toks),
+                            dev(ng[1]), 1.0, ctx, c["ctx_len"], stride, ngram, u_accept=dev(c["u_acc_ng"]),
+                            u_sample=dev(c["u_smp_ng"]), slot_flags=dev(np.ones((BS, 15), np.uint8)))
+    check(plain, fused, ngram)
