@@ -290,8 +290,10 @@ def budget_step(K, W, hip, eager_only):
         step()
         torch.cuda.synchronize()
     total_rows = int(bufs["al"]["total_rows"].item())
+    surv = bufs["al"]["survival"].cpu().numpy().ravel()   # the host copy the next step's sizing reads
     outputs = lambda: list(bufs["vf"].values()) + [bufs["al"]["out_flags"], ctx_len_new, ctx]
     t = run_timed(step, outputs, K, W, hip, stream, eager_only)
+    sizing = host_sizing(S, surv, BS)
     rows_bytes = total_rows * V * 2
     step_bytes = rows_bytes + int(c["ctx_len"].sum()) * 4
     return {"workload": "batch budget allocation + verify + commit + n-gram draft: BS=128, V=151936, model chain "
@@ -302,7 +304,22 @@ def budget_step(K, W, hip, eager_only):
             "GBps": step_bytes / (t["ms_per_step"] * 1e-3) / 1e9,
             "frac": step_bytes / (t["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
             "stats_kernel": {"kernel": "k_stats_flat", "avg_launch_ms": t["stats_ms"],
-                             "GBps": rows_bytes / (t["stats_ms"] * 1e-3) / 1e9}}
+                             "GBps": rows_bytes / (t["stats_ms"] * 1e-3) / 1e9},
+            "host_budget_sizing": sizing}
+
+
+def host_sizing(S, surv, BS, calls=2000):
+    """Host time of the next step's budget sizing (spec_size_budget) over the
+    step's survivals, with a linear cost model of one unit per request and a
+    slot cost of 0.3 units (the scale of the slot price the pages report at
+    BS 128)."""
+    b, lam, g = S.spec_size_budget(surv, BS, float(BS), 0.3)
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        S.spec_size_budget(surv, BS, float(BS), 0.3)
+    us = (time.perf_counter() - t0) / calls * 1e6
+    return {"survivals": int(surv.size), "us_per_call": us, "b_star": b, "lambda": lam,
+            "cost_model": "C(b) = BS + 0.3 b", "includes": "ctypes marshalling"}
 
 
 def main():

@@ -1,5 +1,6 @@
 """MI355X (gfx950) speculative-decoding step: n-gram draft, verification-budget
-allocation, lossless chain verification and greedy tree verification.
+allocation (with host budget sizing), lossless chain verification and greedy tree
+verification.
 
 The compute lives in ``libspec_hip.so`` (hand-written HIP kernels behind the C
 ABI of include/spec.h); this package is its thin binding.
@@ -9,6 +10,7 @@ from ._lib import (  # noqa: F401
     POLICIES,
     spec_allocate_budget,
     spec_ngram_draft,
+    spec_size_budget,
     spec_verify_chain,
     spec_verify_tree,
 )

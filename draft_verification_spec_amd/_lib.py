@@ -87,10 +87,15 @@ class TreeVerifyArgs(C.Structure):
                 ("workspace_bytes", sz)]
 
 
-STRUCTS = {"spec_ngram_args": NgramArgs, "spec_estimator": Estimator, "spec_chain_alloc": ChainAlloc,
+class CostModel(C.Structure):
+    _fields_ = [("c0", C.c_double), ("p", C.c_double), ("graph_limit", i32), ("n_tokens", i32), ("eager", vp),
+                ("n_eager", i32)]
+
+
+STRUCTS = {"spec_cost_model": CostModel, "spec_ngram_args": NgramArgs, "spec_estimator": Estimator, "spec_chain_alloc": ChainAlloc,
            "spec_tree_alloc": TreeAlloc, "spec_alloc_args": AllocArgs, "spec_verify_args": VerifyArgs,
            "spec_tree_verify_args": TreeVerifyArgs}
-EXPORTS = ("spec_ngram_draft", "spec_allocate_budget", "spec_verify_chain", "spec_verify_tree",
+EXPORTS = ("spec_size_budget", "spec_ngram_draft", "spec_allocate_budget", "spec_verify_chain", "spec_verify_tree",
            "spec_workspace_bytes", "spec_strerror", "spec_last_hip_error", "spec_abi_version")
 
 
@@ -108,6 +113,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.spec_strerror.restype = C.c_char_p
     lib.spec_last_hip_error.restype = C.c_char_p
     lib.spec_abi_version.restype = C.c_int
+    lib.spec_size_budget.argtypes = [vp, C.c_int64, C.c_int32, vp, C.c_int32, vp, vp, vp, vp]
+    lib.spec_size_budget.restype = C.c_int
     return lib
 
 
@@ -202,6 +209,23 @@ def estimator_struct(est) -> Estimator:
 # ---------------------------------------------------------------------------
 # entry points
 # ---------------------------------------------------------------------------
+
+def spec_size_budget(survival, n_requests, c0, p, b_max=0, graph_limit=0, n_tokens=0, eager=None, curve=False):
+    """Budget sizing on the host from a host copy of the survivals: returns
+    (b*, lambda, G(b*)) and, with ``curve``, G(b) for every b as well."""
+    import numpy as np
+    s = np.ascontiguousarray(np.ravel(survival.cpu().numpy() if isinstance(survival, torch.Tensor) else survival),
+                             dtype=np.float32)
+    eg = None if eager is None else np.ascontiguousarray(eager, dtype=np.float64)
+    cm = CostModel(float(c0), float(p), int(graph_limit), int(n_tokens),
+                   None if eg is None else eg.ctypes.data_as(vp), 0 if eg is None else len(eg))
+    top = len(s) if b_max <= 0 or b_max > len(s) else int(b_max)
+    g = np.empty(top + 1, np.float64) if curve else None
+    b, lam, gb = C.c_int32(0), C.c_double(0.0), C.c_double(0.0)
+    _check(lib().spec_size_budget(s.ctypes.data_as(vp), len(s), int(n_requests), C.byref(cm), int(b_max),
+                                  C.byref(b), C.byref(lam), C.byref(gb), None if g is None else g.ctypes.data_as(vp)))
+    return (b.value, lam.value, gb.value, g) if curve else (b.value, lam.value, gb.value)
+
 
 def spec_ngram_draft(ctx, ctx_len, n_min, n_max, max_draft=15, copy_cap=256, query_req=None, extra=None,
                      extra_len=None, out=None, workspace=None, stream=None):

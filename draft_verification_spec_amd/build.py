@@ -7,7 +7,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libspec_hip.so")
-SOURCES = ["abi.hip", "ngram.hip", "alloc.hip", "verify.hip"]
+SOURCES = ["abi.hip", "ngram.hip", "alloc.hip", "verify.hip", "budget.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -349,6 +349,37 @@ typedef struct spec_tree_verify_args {
     size_t workspace_bytes;
 } spec_tree_verify_args;
 
+/* ========================================================================
+ * spec_size_budget -- budget sizing and slot price, host arithmetic ([HS]
+ * Section 2 "Adaptive verification" and "Asynchronous scheduling", Section
+ * 4.3 "Slot price" Eq. (2), Section 4.4, Appendix F with Eq. (4)).
+ *
+ * survival: host [n] survivals of the batch's chosen chains (the copy of the
+ * allocation's `survival` output a step earlier; entries <= 0 or padding add
+ * nothing).  A(b) = n_requests + (the b largest survivals) is the expected
+ * number of emitted tokens, C(b) the step cost and G(b) = A(b)/C(b) the
+ * goodput.  C(b) = c0 + p b; when graph_limit > 0 and n_tokens + b exceeds it
+ * the step runs eagerly and C(b) = max(c0 + p b, eager[n_tokens + b -
+ * graph_limit - 1]) (Eq. (4)); a b beyond that table cannot run.  Out:
+ * *b_star = the b in [0, b_max] (b_max <= 0: n) with the largest G (ties to
+ * the smaller b), *lambda = G(b*) p (Eq. (2)), *goodput = G(b*) (or NULL);
+ * with goodput_curve (host [1 + min(n, b_max)], b_max <= 0 meaning n, or
+ * NULL) G(b) for every b (-1 where b cannot run).  All in double over the survivals in descending order.
+ * Host memory only; no device work.  SPEC_EINVAL for bad arguments.
+ * ======================================================================== */
+typedef struct spec_cost_model {
+    double c0;                   /* base step cost C0 (any unit of time), > 0     */
+    double p;                    /* cost of one draft slot, >= 0                  */
+    int32_t graph_limit;         /* tokens a captured step holds; 0 = no limit    */
+    int32_t n_tokens;            /* N: the step's non-draft tokens                */
+    const double* eager;         /* host [n_eager]: eager[k] = T(graph_limit + 1 + k)
+                                    + C_KV, the profiled eager step costs         */
+    int32_t n_eager;
+} spec_cost_model;
+
+int spec_size_budget(const float* survival, int64_t n, int32_t n_requests, const spec_cost_model* cost,
+                     int32_t b_max, int32_t* b_star, double* lambda, double* goodput, double* goodput_curve);
+
 int spec_ngram_draft(const spec_ngram_args* args, void* stream);
 int spec_allocate_budget(const spec_alloc_args* args, void* stream);
 int spec_verify_chain(const spec_verify_args* args, void* stream);

@@ -47,6 +47,8 @@ def _load(path):
     h.oracle_chain_value.restype = C.c_double
     h.oracle_select.restype = C.c_int
     h.oracle_tree_build.restype = C.c_int
+    h.oracle_size_budget.restype = C.c_int
+    h.oracle_step_cost.restype = C.c_double
     return h
 
 
@@ -170,6 +172,44 @@ def select(d, c, g, h, lam, policy="proposed", model_point_mass=True, K=None, ld
                             C.c_double(lam), C.c_int(POLICIES[policy]), C.c_int(int(model_point_mass)),
                             C.c_int(ld), _p(tok), _p(fl), _p(S), C.byref(src), C.byref(near))
     return dict(tokens=tok, flags=fl, S=S, len=n, src=src.value, near=bool(near.value))
+
+
+class _Cost(C.Structure):
+    _fields_ = [("c0", C.c_double), ("p", C.c_double), ("graph_limit", C.c_int32), ("n_tokens", C.c_int32),
+                ("eager", C.c_void_p), ("n_eager", C.c_int32)]
+
+
+def _cost(c0, p, graph_limit=0, n_tokens=0, eager=None):
+    eg = None if eager is None else _c(eager, np.float64)
+    cm = _Cost(float(c0), float(p), int(graph_limit), int(n_tokens), _p(eg), 0 if eg is None else len(eg))
+    return cm, eg   # keep the table alive with the struct
+
+
+def step_cost(b, c0, p, graph_limit=0, n_tokens=0, eager=None):
+    """C(b) of the cost model ([HS] Appendix F, Eq. (4)), or a negative value when b cannot run."""
+    cm, keep = _cost(c0, p, graph_limit, n_tokens, eager)
+    lib().oracle_step_cost.restype = C.c_double
+    return lib().oracle_step_cost(C.byref(cm), C.c_int(int(b)))
+
+
+def size_budget(S, n_requests, c0, p, b_max=None, graph_limit=0, n_tokens=0, eager=None):
+    """Budget sizing ([HS] Section 2 and Section 4.3 Eq. (2)): returns (b*, lambda, G[0..b_max])."""
+    S = _c(np.ravel(S), np.float32)
+    n = len(S)
+    b_max = n if b_max is None else int(b_max)
+    G = np.zeros(min(b_max, n) + 1, np.float64)
+    lam = C.c_double(0.0)
+    cm, keep = _cost(c0, p, graph_limit, n_tokens, eager)
+    b = lib().oracle_size_budget(_p(S), C.c_int(n), C.c_int(int(n_requests)), C.byref(cm), C.c_int(b_max), _p(G),
+                                 C.byref(lam))
+    return b, lam.value, G
+
+
+def stale_shortfall(sigma, n_requests):
+    """Eq. (5) of [HS] Appendix O: the mean shortfall of a stale budget on the
+    steps where it is too small, E[-D | D < 0] = sqrt(2/pi) sigma sqrt(B), for a
+    batch miscount D that is normal with standard deviation sigma sqrt(B)."""
+    return np.sqrt(2.0 / np.pi) * sigma * np.sqrt(n_requests)
 
 
 def allocate(lens, S, budget, flags=None):

@@ -328,6 +328,65 @@ void oracle_allocate(int bs, int ld, const int32_t* len, const double* S, int bu
 }
 
 /* ======================================================================
+ * Budget sizing and slot price (host arithmetic).  [HS] Section 2, "Adaptive
+ * verification": the budget b is the number of draft slots verified in one
+ * pass; A(b) = B + (the b largest survivals of the batch) is the expected
+ * number of emitted tokens of B requests, C(b) the step cost, and the budget
+ * b* maximises the goodput G(b) = A(b) / C(b).  Appendix F: C(b) = C0 + p b;
+ * above the graph capture limit (N + b > graph_limit tokens, N = the step's
+ * non-draft tokens) the step runs eagerly and Eq. (4) gives
+ * C(b) = max(C0 + p b, T(N + b) + C_KV), with the profiled eager costs
+ * eager[k] = T(graph_limit + 1 + k) + C_KV; a b past the table cannot run.
+ * Section 4.3, Eq. (2): the slot price is lambda = G(b*) p.  Ties of G go to
+ * the smaller b.  All in fp64 over the survivals sorted in descending order.
+ * ====================================================================== */
+typedef struct {
+    double c0, p;
+    int32_t graph_limit;   /* 0 = no limit */
+    int32_t n_tokens;      /* N */
+    const double* eager;   /* [n_eager] */
+    int32_t n_eager;
+} oracle_cost;
+
+/* C(b), or a negative value when b cannot run. */
+double oracle_step_cost(const oracle_cost* cm, int b)
+{
+    double c = cm->c0 + cm->p * (double)b;
+    if (cm->graph_limit > 0 && (int64_t)cm->n_tokens + b > cm->graph_limit) {
+        int64_t k = (int64_t)cm->n_tokens + b - cm->graph_limit - 1;
+        if (k >= cm->n_eager) return -1.0;
+        if (cm->eager[k] > c) c = cm->eager[k];
+    }
+    return c;
+}
+
+static int desc_double(const void* pa, const void* pb)
+{
+    double a = *(const double*)pa, b = *(const double*)pb;
+    return (a < b) - (a > b);
+}
+
+/* G(b) for every b in [0, b_max] (G[b] < 0: b cannot run); returns b*. */
+int oracle_size_budget(const float* S, int n, int B, const oracle_cost* cm, int b_max, double* G, double* lambda)
+{
+    double* v = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    for (int i = 0; i < n; ++i) v[i] = S[i] > 0.0f ? (double)S[i] : 0.0;
+    qsort(v, (size_t)n, sizeof(double), desc_double);
+    if (b_max > n) b_max = n;
+    double A = (double)B;
+    int best = -1;
+    for (int b = 0; b <= b_max; ++b) {
+        if (b > 0) A += v[b - 1];
+        double c = oracle_step_cost(cm, b);
+        G[b] = c > 0.0 ? A / c : -1.0;
+        if (G[b] >= 0.0 && (best < 0 || G[b] > G[best])) best = b;
+    }
+    *lambda = best >= 0 ? G[best] * cm->p : 0.0;
+    free(v);
+    return best;
+}
+
+/* ======================================================================
  * Chain verification.  [LS] Section 2.1 with the acceptance and correction
  * rules of speculative sampling (the formulas are blank in the page's text;
  * this is the Leviathan / Chen rule that [HS] Section 2 cites):
