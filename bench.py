@@ -4,9 +4,10 @@
 The reported step (the metric: verify + draft at BS 128, V = 151,936, B = 7)
 is the dense one: rejection-sampling verification of every request's 7-token
 model chain against bf16 target rows [128, 8, V] and draft rows [128, 7, V]
-(probabilistic slots, T = 1.0), the commit of the emitted tokens after each
-8,192-token context, then the n-gram draft over the updated contexts
-(synthetic, seeded; see workloads/synth.py).  The commit writes the new
+(probabilistic slots, T = 1.0, uniforms drawn in the kernel with
+Philox4x32-10), the commit of the emitted tokens after each 8,192-token
+context, then the n-gram draft over the updated contexts, fused into the same
+call (synthetic, seeded; see workloads/synth.py).  The commit writes the new
 lengths to a separate buffer, so every timed step does the same work.
 
 A second record times the batch-allocation step (n-gram draft -> chain
@@ -32,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "verify+draft steps/sec at BS128, V=151936, B=7; achieved HBM GB/s vs peak"
+RNG = (20261202, 1)             # the dense step draws its uniforms in the kernel (Philox4x32-10)
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E, AMD's published figure
 STATS_KERNEL = "k_stats_rows"   # the HBM-bound pass of the dense step
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "stats_rows_dense_bs128_v151936_bf16_counters.md")
@@ -122,8 +124,9 @@ def cpu_baseline(c, sample=32, budget_s=12.0):
     dft = c["draft_bf16"][:m].reshape(-1, V)
     n, t0 = 0, time.perf_counter()
     while True:
+        u_acc, u_smp = O.step_uniforms(m, B, *RNG)
         o = O.verify_chain(tgt, np.arange(m) * (B + 1), c["tokens"][:m], np.zeros((m, B), np.uint8),
-                           np.full(m, B, np.int32), c["u_acc"][:m], c["u_smp"][:m], c["temperature"],
+                           np.full(m, B, np.int32), u_acc, u_smp, c["temperature"],
                            draft_logits=dft, draft_row_base=np.arange(m) * B)
         ctx, ctx_len = O.commit(c["ctx"][:m].copy(), c["ctx_len"][:m].copy(), c["ctx"].shape[1], o["out_tokens"],
                                 o["out_num"], o["flags"])
@@ -133,8 +136,8 @@ def cpu_baseline(c, sample=32, budget_s=12.0):
         if el >= budget_s or n >= 200:
             break
     return {"value": n * m / BS / el, "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} runs of the dense step over the first {m} of {BS} requests (verify, commit, n-gram "
-                      f"draft; single-threaded C oracle, fp64) in {el:.1f} s, scaled by {m}/{BS}"}
+            "sample": f"{n} runs of the dense step over the first {m} of {BS} requests (uniforms, verify, commit, "
+                      f"n-gram draft; single-threaded C oracle, fp64) in {el:.1f} s, scaled by {m}/{BS}"}
 
 
 def run_timed(step, outputs, K, W, hip, stream, eager_only=False):
@@ -218,16 +221,17 @@ def headline(K, W, hip, eager_only):
     rb, drb = g(np.arange(BS, dtype=np.int64) * (B + 1)), g(np.arange(BS, dtype=np.int64) * B)
     tokens, flags = g(c["tokens"]), g(np.zeros((BS, B), np.uint8))
     n_slots = g(np.full(BS, B, np.int32))
-    u_acc, u_smp = g(c["u_acc"]), g(c["u_smp"])
     ctx, ctx_len = g(c["ctx"]), g(c["ctx_len"])
     ctx_len_new = torch.empty_like(ctx_len)
     stream = torch.cuda.Stream()
-    bufs = {"ws_v": torch.empty(1 << 26, dtype=torch.uint8, device=dev)}
+    bufs = {"ws_v": torch.empty(1 << 26, dtype=torch.uint8, device=dev),
+            "hist": torch.zeros(B + 1, dtype=torch.int32, device=dev)}
 
     def step(prof=None):
         # verification, commit and the next n-gram draft over the committed
         # contexts, in one call (the draft runs in the drawing workgroups)
-        out = S.spec_verify_chain(target, rb, tokens, n_slots, c["temperature"], u_accept=u_acc, u_sample=u_smp,
+        out = S.spec_verify_chain(target, rb, tokens, n_slots, c["temperature"], rng=RNG,
+                                  accept_hist=bufs["hist"] if prof is not None else None,
                                   slot_flags=flags, draft_logits=draft, draft_row_base=drb, ctx=ctx,
                                   ctx_len=ctx_len, ctx_len_out=ctx_len_new, out=bufs.get("vf"),
                                   out_flags=bufs.get("vfl"), write_flags=True, workspace=bufs["ws_v"],
@@ -242,6 +246,11 @@ def headline(K, W, hip, eager_only):
         step()
     outputs = lambda: list(bufs["vf"].values()) + [bufs["vfl"], ctx_len_new, ctx] + list(bufs["ng"])
     t = run_timed(step, outputs, K, W, hip, stream, eager_only)
+    # acceptance of the timed eager steps (the histogram is fed only there)
+    h = bufs["hist"].cpu().numpy().astype(np.float64)
+    al = float((h * np.arange(B + 1)).sum() / h.sum())
+    t.update(acceptance={"accepted_per_request": al, "tokens_per_request_step": al + 1.0,
+                         "histogram": [int(x) for x in h / max(1, K)]})
     rows_bytes = BS * (2 * B + 1) * V * 2                # every verified target and draft row, bf16
     ctx_bytes = int(c["ctx_len"].sum()) * 4
     t.update(c=c, rows_bytes=rows_bytes, ctx_bytes=ctx_bytes, BS=BS, V=V, B=B, T_ctx=int(c["ctx"].shape[1] - 64))
@@ -360,6 +369,8 @@ def main():
                      "bytes_per_launch": h["rows_bytes"], "avg_launch_ms": h["stats_ms"]},
         "step_hbm": {"algorithmic_bytes": step_bytes, "GBps": step_bytes / (ms_step * 1e-3) / 1e9,
                      "frac": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS},
+        "acceptance": dict(h["acceptance"], us_per_emitted_token=ms_step * 1e3 / (h["BS"] *
+                                                                               h["acceptance"]["tokens_per_request_step"])),
     }
     if not args.no_budget:
         res["budget_step"] = budget_step(K, W, hip, args.eager)

@@ -70,8 +70,10 @@ class VerifyArgs(C.Structure):
                 ("row_stride", i64), ("row_base", vp), ("n_logit_rows", i64), ("draft_logits", vp),
                 ("draft_dtype", i32), ("draft_row_stride", i64), ("draft_row_base", vp), ("n_draft_rows", i64),
                 ("tokens", vp), ("slot_flags", vp), ("ld", i32), ("n_slots", vp), ("max_slots", i32), ("u_accept", vp),
-                ("u_sample", vp), ("out_tokens", vp), ("out_num", vp), ("out_accepted", vp), ("out_p", vp),
-                ("out_q", vp), ("out_flags", vp), ("write_flags", i32), ("ctx", vp), ("ctx_stride", i64),
+                ("u_sample", vp), ("rng", i32), ("rng_seed", C.c_uint64), ("rng_offset", C.c_uint64),
+                ("out_tokens", vp), ("out_num", vp), ("out_accepted", vp), ("out_p", vp),
+                ("out_q", vp), ("out_flags", vp), ("write_flags", i32), ("out_accept_hist", vp), ("ctx", vp),
+                ("ctx_stride", i64),
                 ("ctx_len", vp), ("ctx_len_out", vp), ("ctx_cap", i32), ("ngram_draft", vp),
                 ("ngram_draft_len", vp), ("ngram_feat", vp), ("ngram_n_min", i32), ("ngram_n_max", i32),
                 ("ngram_max_draft", i32), ("ngram_copy_cap", i32), ("prof_begin", vp), ("prof_end", vp),
@@ -331,7 +333,8 @@ def spec_allocate_budget(mode="chain", **kw):
 def spec_verify_chain(logits, row_base, tokens, n_slots, temperature, u_accept=None, u_sample=None,
                       slot_flags=None, draft_logits=None, draft_row_base=None, out_flags=None,
                       ctx=None, ctx_len=None, ctx_cap=None, ctx_len_out=None, out=None, workspace=None,
-                      stream=None, prof_events=None, max_slots=0, write_flags=False, ngram=None, ngram_out=None):
+                      stream=None, prof_events=None, max_slots=0, write_flags=False, ngram=None, ngram_out=None,
+                      rng=None, accept_hist=None):
     """Rejection-sampling verification of one chain per request (optional commit into ctx).
     ``prof_events``: optional pair of raw hipEvent_t handles recorded around the
     row-statistics pass.  ``max_slots``: optional bound of the total slots
@@ -341,7 +344,11 @@ def spec_verify_chain(logits, row_base, tokens, n_slots, temperature, u_accept=N
     ``ngram``: optional (n_min, n_max, max_draft, copy_cap): with a commit, the
     next n-gram draft of every request over its committed context is computed
     in the same launch and returned as out["ngram_draft"], out["ngram_len"],
-    out["ngram_feat"] (into ``ngram_out``, a (draft, len, feat) triple, if given)."""
+    out["ngram_feat"] (into ``ngram_out``, a (draft, len, feat) triple, if given).
+    ``rng``: optional (seed, offset): the call draws its uniforms with
+    Philox4x32-10 instead of reading u_accept / u_sample.  ``accept_hist``:
+    optional int32 [ld + 1] device tensor, increased at each request's
+    accepted count."""
     lg = _rows2d(logits, "logits")
     _dev(row_base, torch.int64, "row_base", 1)
     _dev(tokens, torch.int32, "tokens", 2)
@@ -385,6 +392,13 @@ def spec_verify_chain(logits, row_base, tokens, n_slots, temperature, u_accept=N
         if ctx_len_out is not None:
             _dev(ctx_len_out, torch.int32, "ctx_len_out", 1)
             a.ctx_len_out = _ptr(ctx_len_out)
+    if rng is not None:
+        a.rng, a.rng_seed, a.rng_offset = 1, int(rng[0]) & (2**64 - 1), int(rng[1]) & (2**64 - 1)
+    if accept_hist is not None:
+        _dev(accept_hist, torch.int32, "accept_hist", 1)
+        if accept_hist.shape[0] < ld + 1:
+            raise ValueError("accept_hist must hold ld + 1 counts")
+        a.out_accept_hist = _ptr(accept_hist)
     if ngram is not None:
         if ctx is None:
             raise ValueError("the fused n-gram draft needs the commit (ctx)")

@@ -96,7 +96,8 @@ static int check_verify(const spec_verify_args* a)
         REQUIRE(a->draft_row_stride >= a->vocab && a->n_draft_rows >= 1);
     }
     REQUIRE(a->tokens && a->n_slots && a->ld >= 1 && a->ld <= SPEC_MAX_DRAFT && a->max_slots >= 0);
-    REQUIRE(a->temperature == 0.0f || (a->u_accept && a->u_sample));
+    REQUIRE(a->temperature == 0.0f || a->rng || (a->u_accept && a->u_sample));
+    REQUIRE(a->rng == 0 || a->rng == 1);
     REQUIRE(a->out_tokens && a->out_num && a->out_accepted && a->out_flags);
     if (a->ctx) REQUIRE(a->ctx_len && a->ctx_cap >= 0 && a->ctx_cap <= a->ctx_stride);
     if (a->ngram_draft) {

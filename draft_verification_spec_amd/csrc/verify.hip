@@ -1051,6 +1051,8 @@ struct ChainParams {
     const void* dlogits; int32_t ddt; int64_t dstride; const int64_t* drow_base; int64_t dn_rows;
     const int32_t* tokens; const uint8_t* slot_flags; const int32_t* n_slots;
     const float* u_acc; const float* u_smp;
+    int32_t rng; uint64_t rng_seed, rng_offset;   // uniforms drawn here (Philox4x32-10) instead of read
+    int32_t* accept_hist;       // optional [ld + 1]: += 1 at the request's accepted count
     int32_t* out_tokens; int32_t* out_num; int32_t* out_acc; float* out_p; float* out_q; uint32_t* out_flags;
     int32_t write_flags;        // out_flags written (by the drawing workgroup) rather than OR-ed
     int32_t* ctx; int64_t ctx_stride; const int32_t* ctx_len; int32_t* ctx_len_out; int32_t ctx_cap;
@@ -1071,6 +1073,36 @@ struct Draw {
     int64_t row_t, row_d;
     double ratio;
 };
+
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers:
+// as easy as 1, 2, 3", SC'11): ten rounds of two 32x32 -> 64-bit products of
+// counter words 0 and 2 with the rounds' multipliers, the high halves mixed
+// with the other two words and the key, the key bumped by the Weyl constants.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint2 k)
+{
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+        const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
+        const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+        c = make_uint4(hi1 ^ c.y ^ k.x, lo1, hi0 ^ c.w ^ k.y, lo0);
+        k.x += 0x9E3779B9u;   // the bump after the last round is unused
+        k.y += 0xBB67AE85u;
+    }
+    return c;
+}
+
+// Uniform k of request r at step `offset`: word k mod 4 of block
+// Philox4x32-10(counter (k / 4, r, offset), key seed), as (w >> 8) 2^-24.
+// u_accept[r][i] is uniform i and u_sample[r] uniform SPEC_MAX_DRAFT.
+__device__ __forceinline__ float step_uniform(const ChainParams& P, int r, int k)
+{
+    const uint4 w = philox4x32_10(make_uint4((uint32_t)(k / 4), (uint32_t)r, (uint32_t)P.rng_offset,
+                                             (uint32_t)(P.rng_offset >> 32)),
+                                  make_uint2((uint32_t)P.rng_seed, (uint32_t)(P.rng_seed >> 32)));
+    const int q = k % 4;
+    const uint32_t x = q == 0 ? w.x : (q == 1 ? w.y : (q == 2 ? w.z : w.w));
+    return (float)(x >> 8) * (1.0f / 16777216.0f);
+}
 
 // A decide workgroup is kDBlock threads.
 constexpr int kDBlock = 512;
@@ -1606,6 +1638,7 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
     const int t = threadIdx.x;
     const int ld = P.ld;
     const int32_t len0 = P.ctx ? P.ctx_len[r] : 0;   // loaded early, used by the commit
+    const double usmp = P.greedy ? 0.0 : (P.rng ? (double)step_uniform(P, r, SPEC_MAX_DRAFT) : (double)P.u_smp[r]);
     __shared__ Partial sp[kMaxPartsLds];
     __shared__ float sO[2 * SPEC_MAX_DRAFT + 1];
     __shared__ double sZ[2 * SPEC_MAX_DRAFT + 1];
@@ -1630,7 +1663,7 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
         pm = !P.slot_flags || (P.slot_flags[off] & SPEC_SLOT_POINT_MASS);
         const bool yok = y >= 0 && y < P.vocab;
         if (!P.greedy) {
-            uacc = P.u_acc[off];
+            uacc = P.rng ? step_uniform(P, r, t) : P.u_acc[off];
             const int64_t row = row_base + t;
             if (yok && row >= 0 && row < P.n_rows) zt = logit_at(P.logits, DTT, row, P.stride, y);
             if (!pm && P.dlogits) {
@@ -1766,6 +1799,7 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
         if (lead) {
             P.out_num[r] = nacc + 1;
             P.out_acc[r] = nacc;
+            if (P.accept_hist) atomicAdd(&P.accept_hist[nacc], 1);
         }
         if (nacc == b && !sOk[b]) sFlags |= SPEC_FLAG_BAD_LOGITS;
     }
@@ -1819,11 +1853,11 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
         }
     }
     if (streamed) {
-        last = residual_draw<DTT>(P, d, r, (double)P.u_smp[r], sW);
+        last = residual_draw<DTT>(P, d, r, usmp, sW);
         if (last < 0) {
             // the residual had no mass (not reachable in exact arithmetic): draw from p
             if (t == 0) sFlags |= SPEC_FLAG_RESIDUAL_ZERO;
-            last = draw_from_p<DTT, DTD>(P, d, sW, (double)P.u_smp[r]);
+            last = draw_from_p<DTT, DTD>(P, d, sW, usmp);
         }
     } else if (d.mode != 0) {
         if (d.mode == 2) {
@@ -1852,11 +1886,11 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
             }
             __syncthreads();
         }
-        last = draw_from_chunks<DTT, DTD>(P, d, sW, (double)P.u_smp[r]);
+        last = draw_from_chunks<DTT, DTD>(P, d, sW, usmp);
         if (last < 0) {
             // the residual had no mass (not reachable in exact arithmetic): draw from p
             if (t == 0) sFlags |= SPEC_FLAG_RESIDUAL_ZERO;
-            last = draw_from_p<DTT, DTD>(P, d, sW, (double)P.u_smp[r]);
+            last = draw_from_p<DTT, DTD>(P, d, sW, usmp);
         }
     } else if (!P.greedy) {
         if (t == 0) sFlags |= SPEC_FLAG_BAD_LOGITS;
@@ -2241,6 +2275,8 @@ int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st)
     P.drow_base = a->draft_row_base; P.dn_rows = a->n_draft_rows;
     P.tokens = a->tokens; P.slot_flags = a->slot_flags; P.n_slots = a->n_slots;
     P.u_acc = a->u_accept; P.u_smp = a->u_sample;
+    P.rng = a->rng; P.rng_seed = a->rng_seed; P.rng_offset = a->rng_offset;
+    P.accept_hist = a->out_accept_hist;
     P.out_tokens = a->out_tokens; P.out_num = a->out_num; P.out_acc = a->out_accepted;
     P.out_p = a->out_p; P.out_q = a->out_q; P.out_flags = a->out_flags; P.write_flags = a->write_flags;
     P.ctx = a->ctx; P.ctx_stride = a->ctx_stride; P.ctx_len = a->ctx_len;

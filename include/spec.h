@@ -284,6 +284,15 @@ typedef struct spec_verify_args {
                                     that is too small costs speed, not results   */
     const float* u_accept;       /* device [bs, ld] uniforms in [0,1)             */
     const float* u_sample;       /* device [bs]                                   */
+    int32_t rng;                 /* 1: the call draws its uniforms itself and
+                                    u_accept / u_sample may be NULL: uniform k of
+                                    request r is word k mod 4 of Philox4x32-10
+                                    (Salmon et al., SC'11) with counter (k / 4, r,
+                                    rng_offset low, high) and key rng_seed (low,
+                                    high), as (word >> 8) 2^-24; u_accept[r][i] is
+                                    uniform i, u_sample[r] uniform SPEC_MAX_DRAFT */
+    uint64_t rng_seed;
+    uint64_t rng_offset;         /* e.g. the step number                          */
     int32_t* out_tokens;         /* device [bs, ld+1], -1 padded                  */
     int32_t* out_num;            /* device [bs]                                   */
     int32_t* out_accepted;       /* device [bs]                                   */
@@ -292,6 +301,10 @@ typedef struct spec_verify_args {
     uint32_t* out_flags;         /* device [bs], OR-ed (see write_flags)          */
     int32_t write_flags;         /* 1: out_flags[r] is written with this call's
                                     flags instead (no zeroing needed before)      */
+    int32_t* out_accept_hist;    /* optional device [ld + 1]: entry a is increased
+                                    by the requests that accepted a drafts (the
+                                    acceptance length distribution; the prefix
+                                    advances by a + 1, [LS] Section 2.1)         */
     int32_t* ctx;                /* optional commit: device [bs, ctx_stride]      */
     int64_t ctx_stride;
     int32_t* ctx_len;            /* device [bs]                                   */

@@ -205,6 +205,33 @@ def size_budget(S, n_requests, c0, p, b_max=None, graph_limit=0, n_tokens=0, eag
     return b, lam.value, G
 
 
+def philox4x32_10(ctr, key):
+    """Philox4x32-10 (Salmon et al., SC'11) of a 4-word counter and 2-word key."""
+    c = _c(ctr, np.uint32)
+    k = _c(key, np.uint32)
+    out = np.zeros(4, np.uint32)
+    lib().oracle_philox4x32_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def philox4x64_10(ctr, key):
+    """Philox4x64-10, the 64-bit member of the same family."""
+    c = _c(ctr, np.uint64)
+    k = _c(key, np.uint64)
+    out = np.zeros(4, np.uint64)
+    lib().oracle_philox4x64_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def step_uniforms(bs, ld, seed, offset):
+    """The uniforms a verification step draws for itself: (u_accept [bs, ld], u_sample [bs])."""
+    u_acc = np.zeros((bs, ld), np.float32)
+    u_smp = np.zeros(bs, np.float32)
+    lib().oracle_step_uniforms(C.c_int(bs), C.c_int(ld), C.c_uint64(int(seed)), C.c_uint64(int(offset)),
+                               _p(u_acc), _p(u_smp))
+    return u_acc, u_smp
+
+
 def stale_shortfall(sigma, n_requests):
     """Eq. (5) of [HS] Appendix O: the mean shortfall of a stale budget on the
     steps where it is too small, E[-D | D < 0] = sqrt(2/pi) sigma sqrt(B), for a

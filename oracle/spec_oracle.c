@@ -328,6 +328,76 @@ void oracle_allocate(int bs, int ld, const int32_t* len, const double* S, int bu
 }
 
 /* ======================================================================
+ * Counter-based uniforms: Philox4x32-10 (Salmon, Moraes, Dror and Shaw,
+ * "Parallel random numbers: as easy as 1, 2, 3", SC'11).  A round multiplies
+ * counter words 0 and 2 by M0 and M1 into 64-bit products and forms the new
+ * counter (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0));
+ * the key is bumped by the Weyl constants between rounds.  Philox4x64-10 is
+ * the same with 64-bit words and its own constants (kept here so that the
+ * round structure can be checked against a library generator).
+ *
+ * The step's uniforms (the mapping the verifier uses when it draws its own):
+ * for request r at step `offset` with key `seed`, block j is
+ * Philox4x32-10(counter = (j, r, offset_lo, offset_hi), key = (seed_lo,
+ * seed_hi)); uniform k is word k mod 4 of block k / 4 as (w >> 8) 2^-24 in
+ * [0, 1); u_accept[r][i] = uniform i, u_sample[r] = uniform 32.
+ * ====================================================================== */
+void oracle_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4])
+{
+    uint32_t c[4] = {ctr_in[0], ctr_in[1], ctr_in[2], ctr_in[3]};
+    uint32_t k[2] = {key_in[0], key_in[1]};
+    for (int round = 0; round < 10; ++round) {
+        uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+        uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+        uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k[0];
+        uint32_t n1 = (uint32_t)p1;
+        uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k[1];
+        uint32_t n3 = (uint32_t)p0;
+        c[0] = n0; c[1] = n1; c[2] = n2; c[3] = n3;
+        if (round < 9) { k[0] += 0x9E3779B9u; k[1] += 0xBB67AE85u; }
+    }
+    for (int i = 0; i < 4; ++i) out[i] = c[i];
+}
+
+static void mulhilo64(uint64_t a, uint64_t b, uint64_t* hi, uint64_t* lo)
+{
+    unsigned __int128 p = (unsigned __int128)a * b;
+    *hi = (uint64_t)(p >> 64);
+    *lo = (uint64_t)p;
+}
+
+void oracle_philox4x64_10(const uint64_t ctr_in[4], const uint64_t key_in[2], uint64_t out[4])
+{
+    uint64_t c[4] = {ctr_in[0], ctr_in[1], ctr_in[2], ctr_in[3]};
+    uint64_t k[2] = {key_in[0], key_in[1]};
+    for (int round = 0; round < 10; ++round) {
+        uint64_t hi0, lo0, hi1, lo1;
+        mulhilo64(0xD2E7470EE14C6C93ull, c[0], &hi0, &lo0);
+        mulhilo64(0xCA5A826395121157ull, c[2], &hi1, &lo1);
+        uint64_t n0 = hi1 ^ c[1] ^ k[0], n2 = hi0 ^ c[3] ^ k[1];
+        c[0] = n0; c[1] = lo1; c[2] = n2; c[3] = lo0;
+        if (round < 9) { k[0] += 0x9E3779B97F4A7C15ull; k[1] += 0xBB67AE8584CAA73Bull; }
+    }
+    for (int i = 0; i < 4; ++i) out[i] = c[i];
+}
+
+void oracle_step_uniforms(int bs, int ld, uint64_t seed, uint64_t offset, float* u_acc, float* u_smp)
+{
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    for (int r = 0; r < bs; ++r) {
+        float u[36];
+        for (int j = 0; j < 9; ++j) {
+            const uint32_t ctr[4] = {(uint32_t)j, (uint32_t)r, (uint32_t)offset, (uint32_t)(offset >> 32)};
+            uint32_t w[4];
+            oracle_philox4x32_10(ctr, key, w);
+            for (int q = 0; q < 4; ++q) u[4 * j + q] = (float)((double)(w[q] >> 8) / 16777216.0);
+        }
+        for (int i = 0; i < ld; ++i) u_acc[(int64_t)r * ld + i] = u[i];
+        u_smp[r] = u[32];
+    }
+}
+
+/* ======================================================================
  * Budget sizing and slot price (host arithmetic).  [HS] Section 2, "Adaptive
  * verification": the budget b is the number of draft slots verified in one
  * pass; A(b) = B + (the b largest survivals of the batch) is the expected
