@@ -12,7 +12,8 @@ lengths to a separate buffer, so every timed step does the same work.
 
 A second record times the batch-allocation step (n-gram draft -> chain
 selection and budget allocation of 256 slots -> verification -> commit) at
-BS 128 with the same timing.
+BS 128 with the same timing, a third the tree step (n-gram chains -> tree
+build with the Eq. (6) scores -> greedy verification -> commit) at BS 64.
 
 Timing, per workload, on one stream: K eager steps with an event pair
 attached to the dispatch of every statistics kernel (that kernel's live
@@ -49,6 +50,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=500)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-budget", action="store_true", help="skip the batch-allocation step record")
+    p.add_argument("--no-tree", action="store_true", help="skip the tree step record")
     p.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -317,6 +319,84 @@ def budget_step(K, W, hip, eager_only):
             "host_budget_sizing": sizing}
 
 
+def tree_step(K, W, hip, eager_only):
+    """The tree step (the tree workload: BS 64, V 151,936, fp32 rows, T = 0):
+    n-gram chains from the anchor and each of the 8 picks -> tree build with
+    the Eq. (6) scores and its S(n) curve -> greedy verification of the 16
+    rows -> commit.  The stand-in target rows are made once for the tree the
+    step builds (it is the same every step)."""
+    import numpy as np
+    import torch
+    import draft_verification_spec_amd as S
+    from workloads import synth
+    dev = torch.device("cuda:0")
+    c = synth.config3_inputs()
+    BS, V, P, Kc, R = c["BS"], c["V"], c["P"], c["Kc"], c["rows_cap"]
+    g = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    qr, ex, el = synth.tree_queries(c["ctx"], c["ctx_len"], c["block"])
+    f = synth.tree_score_inputs(BS, P, Kc)
+    stride = c["ctx"].shape[1] + R
+    ctx_h = np.zeros((BS, stride), np.int32)
+    ctx_h[:, :c["ctx"].shape[1]] = c["ctx"]
+    ctx, ctx_len = g(ctx_h), g(c["ctx_len"])
+    ctx_len_new = torch.empty_like(ctx_len)
+    qr_d, ex_d, el_d, block = g(qr), g(ex), g(el), g(c["block"])
+    stream = torch.cuda.Stream()
+    bufs = {"ws_t": torch.empty(1 << 24, dtype=torch.uint8, device=dev),
+            "tfl": torch.zeros(BS, dtype=torch.int32, device=dev)}   # OR-ed flags: the same every step
+
+    feats = dict(coef=f["coef"], h=g(f["h"]), sigma=g(f["sigma"]), r_share=g(f["r_share"]), psi_ctx=g(f["psi_ctx"]),
+                 b_req=g(f["b_req"]), p_src=g(f["p_src"]))
+
+    def build():
+        d, dl, ft = S.spec_ngram_draft(ctx, ctx_len, c["n_min"], c["n_max"], c["L"], c["copy_cap"], query_req=qr_d,
+                                       extra=ex_d, extra_len=el_d, out=bufs.get("ng"))
+        sc = dict(feats, ngram_feat=ft)
+        t = S.spec_allocate_budget(mode="tree", block=block, ngram_draft=d, ngram_len=dl, scores=sc,
+                                   c_max=c["c_max"], depth_max=c["depth_max"], rows_cap=R, s_curve=True,
+                                   out=bufs.get("tr"))
+        bufs.setdefault("ng", (d, dl, ft))
+        bufs.setdefault("tr", t)
+        return t
+
+    with torch.cuda.stream(stream):
+        t = build()
+        torch.cuda.synchronize()
+    rows = synth.tree_target_rows(3, t["node_token"].cpu().numpy(), t["parent_row"].cpu().numpy(),
+                                  t["n_rows"].cpu().numpy(), c["truth"], V, R)
+    logits = g(rows).reshape(-1, V)
+    del rows
+    rb = g(np.arange(BS, dtype=np.int64) * R)
+
+    def step(prof=None):
+        tr = build()
+        out = S.spec_verify_tree(logits, rb, tr["node_token"], tr["parent_row"], tr["n_rows"], out_flags=bufs["tfl"],
+                                 ctx=ctx,
+                                 ctx_len=ctx_len, ctx_len_out=ctx_len_new, out=bufs.get("vt"), prof_events=prof,
+                                 workspace=bufs["ws_t"])
+        bufs.setdefault("vt", out)
+
+    with torch.cuda.stream(stream):
+        step()
+        torch.cuda.synchronize()
+    outputs = lambda: list(bufs["vt"].values()) + [ctx_len_new, ctx] + list(bufs["tr"].values())
+    tm = run_timed(step, outputs, K, W, hip, stream, eager_only)
+    rows_bytes = int(bufs["tr"]["n_rows"].sum().item()) * V * 4
+    step_bytes = rows_bytes + int(c["ctx_len"].sum()) * 4
+    return {"workload": "tree: n-gram chains from the anchor and 8 picks (n 3..15) -> tree build with Eq. (6) "
+                        "scores and S(n) -> greedy verification of up to 16 rows -> commit; BS=64, V=151936, "
+                        "fp32 rows, 4096-token contexts, drafter block 8 x 4",
+            "timing": tm["mode"], "steps_per_s": tm["steps_per_s"], "ms_per_step": tm["ms_per_step"],
+            "verified_rows_per_step": int(bufs["tr"]["n_rows"].sum().item()), "algorithmic_bytes": step_bytes,
+            "GBps": step_bytes / (tm["ms_per_step"] * 1e-3) / 1e9,
+            "frac": step_bytes / (tm["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "mean_S16": float(bufs["tr"]["s_curve"][:, -1].mean().item()),
+            "mean_committed": float(bufs["vt"]["out_num"].float().mean().item()),
+            "stats_kernel": {"kernel": "k_stats_rows (argmax)", "avg_launch_ms": tm["stats_ms"],
+                             "GBps": rows_bytes / (tm["stats_ms"] * 1e-3) / 1e9,
+                             "frac": rows_bytes / (tm["stats_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBPS}}
+
+
 def host_sizing(S, surv, BS, calls=2000):
     """Host time of the next step's budget sizing (spec_size_budget) over the
     step's survivals, with a linear cost model of one unit per request and a
@@ -374,6 +454,8 @@ def main():
     }
     if not args.no_budget:
         res["budget_step"] = budget_step(K, W, hip, args.eager)
+    if not args.no_tree:
+        res["tree_step"] = tree_step(K, W, hip, args.eager)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(h["c"])
     print(json.dumps(res), flush=True)

@@ -53,11 +53,18 @@ class ChainAlloc(C.Structure):
                 ("survival", vp), ("alloc_len", vp), ("row_base", vp), ("total_rows", vp), ("out_flags", vp)]
 
 
+class TreeScores(C.Structure):
+    _fields_ = [("a", C.c_double * 7), ("w_bucket", C.c_double * 32), ("w_agreed", (C.c_double * 2) * 32),
+                ("w_contra", (C.c_double * 2) * 8), ("psi_depth", C.c_double * 16), ("h", vp), ("sigma", vp),
+                ("r_share", vp), ("psi_ctx", vp), ("b_req", vp), ("p_src", vp), ("ngram_feat", vp)]
+
+
 class TreeAlloc(C.Structure):
     _fields_ = [("bs", i32), ("P", i32), ("Kc", i32), ("block", vp), ("ngram_draft", vp), ("ngram_ld", i32),
-                ("ngram_len", vp), ("w_node", vp), ("w_none", vp), ("c_max", i32), ("depth_max", i32),
-                ("rows_cap", i32), ("node_token", vp), ("parent_row", vp), ("Q", vp), ("n_rows", vp),
-                ("row_base", vp), ("total_rows", vp), ("forest_count", vp), ("out_flags", vp)]
+                ("ngram_len", vp), ("w_node", vp), ("w_none", vp), ("scores", vp), ("c_max", i32),
+                ("depth_max", i32), ("rows_cap", i32), ("node_token", vp), ("parent_row", vp), ("Q", vp),
+                ("n_rows", vp), ("row_base", vp), ("total_rows", vp), ("forest_count", vp), ("s_curve", vp),
+                ("out_flags", vp)]
 
 
 class AllocArgs(C.Structure):
@@ -94,7 +101,7 @@ class CostModel(C.Structure):
                 ("n_eager", i32)]
 
 
-STRUCTS = {"spec_cost_model": CostModel, "spec_ngram_args": NgramArgs, "spec_estimator": Estimator, "spec_chain_alloc": ChainAlloc,
+STRUCTS = {"spec_cost_model": CostModel, "spec_tree_scores": TreeScores, "spec_ngram_args": NgramArgs, "spec_estimator": Estimator, "spec_chain_alloc": ChainAlloc,
            "spec_tree_alloc": TreeAlloc, "spec_alloc_args": AllocArgs, "spec_verify_args": VerifyArgs,
            "spec_tree_verify_args": TreeVerifyArgs}
 EXPORTS = ("spec_size_budget", "spec_ngram_draft", "spec_allocate_budget", "spec_verify_chain", "spec_verify_tree",
@@ -294,13 +301,40 @@ def _chain_alloc(model_tokens, model_conf, ngram_draft, ngram_len, ngram_feat, e
     return out
 
 
-def _tree_alloc(block, ngram_draft, ngram_len, w_node, w_none, depth_max=32, rows_cap=16, out=None,
-                stream=None):
+def tree_scores_struct(coef, h, sigma, r_share, psi_ctx, b_req, p_src, ngram_feat):
+    """spec_tree_scores: coefficient tables from ``coef`` (a [7], w_bucket [32],
+    w_agreed [32, 2], w_contra [8, 2], psi_depth [16]) and device feature tensors."""
+    for t, name in ((h, "h"), (sigma, "sigma"), (r_share, "r_share"), (psi_ctx, "psi_ctx"), (b_req, "b_req"),
+                    (p_src, "p_src")):
+        _dev(t, torch.float32, name)
+    _dev(ngram_feat, torch.int32, "ngram_feat", 2)
+    st = TreeScores()
+    st.a[:] = [float(x) for x in coef["a"]]
+    st.w_bucket[:] = [float(x) for x in coef["w_bucket"]]
+    for i in range(32):
+        st.w_agreed[i][:] = [float(x) for x in coef["w_agreed"][i]]
+    for i in range(8):
+        st.w_contra[i][:] = [float(x) for x in coef["w_contra"][i]]
+    st.psi_depth[:] = [float(x) for x in coef["psi_depth"]]
+    st.h, st.sigma, st.r_share = _ptr(h), _ptr(sigma), _ptr(r_share)
+    st.psi_ctx, st.b_req, st.p_src, st.ngram_feat = _ptr(psi_ctx), _ptr(b_req), _ptr(p_src), _ptr(ngram_feat)
+    return st
+
+
+def _tree_alloc(block, ngram_draft, ngram_len, w_node=None, w_none=None, depth_max=32, rows_cap=16, out=None,
+                stream=None, scores=None, c_max=None, s_curve=False):
+    """Tree build; weights w_node / w_none by candidate index, or ``scores``
+    (the keyword arguments of tree_scores_struct) for the Eq. (6) form.  With
+    ``s_curve`` the S(n) curve [bs, rows_cap] is returned as out["s_curve"]."""
     _dev(block, torch.int32, "block", 3)
     _dev(ngram_draft, torch.int32, "ngram_draft", 2)
     _dev(ngram_len, torch.int32, "ngram_len", 1)
-    _dev(w_node, torch.float32, "w_node", 2)
-    _dev(w_none, torch.float32, "w_none", 2)
+    if scores is None:
+        _dev(w_node, torch.float32, "w_node", 2)
+        _dev(w_none, torch.float32, "w_none", 2)
+        c_max = w_node.shape[1]
+    elif c_max is None:
+        raise ValueError("c_max is needed with scores")
     bs, P, Kc = block.shape
     dev = block.device
     if out is None:
@@ -312,9 +346,13 @@ def _tree_alloc(block, ngram_draft, ngram_len, w_node, w_none, depth_max=32, row
                    total_rows=torch.empty(1, dtype=torch.int32, device=dev),
                    forest_count=torch.empty(bs, dtype=torch.int32, device=dev),
                    out_flags=torch.empty(bs, dtype=torch.int32, device=dev))
+        if s_curve:
+            out["s_curve"] = torch.empty((bs, rows_cap), dtype=torch.float32, device=dev)
+    st = None if scores is None else tree_scores_struct(**scores)
     ta = TreeAlloc(bs=bs, P=P, Kc=Kc, block=_ptr(block), ngram_draft=_ptr(ngram_draft),
                    ngram_ld=ngram_draft.shape[1], ngram_len=_ptr(ngram_len), w_node=_ptr(w_node),
-                   w_none=_ptr(w_none), c_max=w_node.shape[1], depth_max=depth_max, rows_cap=rows_cap,
+                   w_none=_ptr(w_none), scores=None if st is None else C.cast(C.pointer(st), vp),
+                   c_max=int(c_max), depth_max=depth_max, rows_cap=rows_cap,
                    **{k: _ptr(v) for k, v in out.items()})
     a = AllocArgs(mode=ALLOC_TREE, tree=ta)
     _check(lib().spec_allocate_budget(C.byref(a), _stream(dev, stream)))

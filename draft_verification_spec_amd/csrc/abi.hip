@@ -67,7 +67,12 @@ static int check_tree_alloc(const spec_tree_alloc* t)
     REQUIRE(t->P == 0 || t->block);
     REQUIRE(t->c_max >= 1 + t->P * t->Kc && t->c_max <= SPEC_MAX_FOREST);
     REQUIRE(t->ngram_ld >= 0 && (t->ngram_ld == 0 || t->ngram_draft) && t->ngram_len);
-    REQUIRE(t->w_node && t->w_none);
+    REQUIRE(t->scores || (t->w_node && t->w_none));
+    if (t->scores) {
+        const spec_tree_scores* sc = t->scores;
+        REQUIRE(t->P == 0 || (sc->h && sc->sigma && (t->Kc == 1 || sc->r_share)));
+        REQUIRE(sc->psi_ctx && sc->b_req && sc->p_src && sc->ngram_feat);
+    }
     REQUIRE(t->depth_max >= 1);
     REQUIRE(t->rows_cap >= 1 && t->rows_cap <= SPEC_MAX_ROWS);
     REQUIRE(t->node_token && t->parent_row && t->Q && t->n_rows && t->row_base && t->total_rows);

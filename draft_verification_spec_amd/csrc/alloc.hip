@@ -19,6 +19,8 @@
 //               the Eq. (6) form, the path products Q, the best-first top
 //               rows_cap-1 (Proposition 1) and the depth-first layout.
 //   k_rows_scan: exclusive prefix sum of the rows per request.
+#include <cstring>
+
 #include "common.hpp"
 
 namespace spec {
@@ -361,7 +363,20 @@ __global__ __launch_bounds__(kAllocBlock) void k_alloc_topk(SelectParams P)
 
 struct TreeBuildParams {
     spec_tree_alloc a;
+    spec_tree_scores sc;   // copied from a.scores when given
+    int32_t scored;
 };
+
+__device__ __forceinline__ double clamp_prob(double x) { return x < 1e-6 ? 1e-6 : (x > 1.0 - 1e-6 ? 1.0 - 1e-6 : x); }
+__device__ __forceinline__ double logit_prob(double x) { x = clamp_prob(x); return log(x / (1.0 - x)); }
+
+// Evidence class of an n-gram chain: floor(log2) of its source's match
+// length (feature m, else n), at most 7.
+__device__ __forceinline__ int evidence_of(const int32_t* feat)
+{
+    const int l = feat[2] > 0 ? feat[2] : feat[0];
+    return l <= 1 ? 0 : min(7, 31 - __clz(l));
+}
 
 __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
 {
@@ -373,68 +388,157 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
     __shared__ double fden[SPEC_MAX_FOREST];
     __shared__ double fQ[SPEC_MAX_FOREST];
     __shared__ uint8_t fsel[SPEC_MAX_FOREST];
-    __shared__ int32_t sh_cnt, sh_cur;
+    // Eq. (6) scoring state: kind (1 pick, 2 sibling, 3 n-gram; +4 agreed),
+    // n-gram nodes above, an n-gram node's bucket, a drafter node's largest
+    // agreeing bucket (-1 none), the weights exp(s)
+    __shared__ uint8_t fkind[SPEC_MAX_FOREST];
+    __shared__ int8_t fabove[SPEC_MAX_FOREST];
+    __shared__ int8_t fbucket[SPEC_MAX_FOREST];
+    __shared__ int8_t fagree[SPEC_MAX_FOREST];
+    __shared__ double fw[SPEC_MAX_FOREST];
+    __shared__ double sQrank[SPEC_MAX_ROWS];
+    __shared__ int32_t sh_cnt;
+    // the chains' tokens and lengths, staged in one round trip when they fit
+    constexpr int kChainLds = 2048;
+    __shared__ int32_t ctok[kChainLds];
+    __shared__ int32_t clen[SPEC_MAX_FOREST];
     const int P_ = A.P, Kc = A.Kc, cmax = A.c_max;
     const int nd = 1 + P_ * Kc;
+    const int64_t q0 = (int64_t)r * (P_ + 1);
+    const bool staged = (int64_t)(P_ + 1) * A.ngram_ld <= kChainLds;
+    for (int i = lane; i <= P_; i += kWave) clen[i] = A.ngram_len[q0 + i];
+    if (staged)
+        for (int i = lane; i < (P_ + 1) * A.ngram_ld; i += kWave) ctok[i] = A.ngram_draft[q0 * A.ngram_ld + i];
     for (int i = lane; i < nd; i += kWave) {
-        if (i == 0) { ftok[0] = -1; fpar[0] = -1; fdep[0] = 0; }
+        if (i == 0) { ftok[0] = -1; fpar[0] = -1; fdep[0] = 0; fkind[0] = 0; }
         else {
             const int p = (i - 1) / Kc + 1, k = (i - 1) % Kc;
             ftok[i] = A.block[((int64_t)r * P_ + (p - 1)) * Kc + k];
             fpar[i] = (p == 1) ? 0 : 1 + (p - 2) * Kc;
             fdep[i] = p;
+            fkind[i] = k == 0 ? 1 : 2;
         }
+        fabove[i] = 0;
+        fbucket[i] = -1;
+        fagree[i] = -1;
     }
-    if (lane == 0) sh_cnt = nd;
     __syncthreads();
-    // n-gram chains from the anchor (s = 0) and each pick s
+    // n-gram chains from the anchor (s = 0) and each pick s.  The workgroup is
+    // one wave, so the walk's state (current node, its depth, kind and
+    // n-gram count, the node count) lives in wave-uniform registers; lane 0
+    // writes each new node, and the wave's LDS accesses stay in order.
     uint32_t flags = 0;
+    int cntr = nd;
     for (int s = 0; s <= P_; ++s) {
-        const int64_t q = (int64_t)r * (P_ + 1) + s;
-        int glen = A.ngram_len[q];
+        const int64_t q = q0 + s;
+        int glen = clen[s];
         if (glen < 0 || glen > A.ngram_ld) { flags |= SPEC_FLAG_BAD_LENGTH; glen = glen < 0 ? 0 : A.ngram_ld; }
-        if (lane == 0) sh_cur = (s == 0) ? 0 : 1 + (s - 1) * Kc;
-        __syncthreads();
+        const int ev = P.scored ? evidence_of(P.sc.ngram_feat + 4 * q) : 0;
+        int cur = (s == 0) ? 0 : 1 + (s - 1) * Kc;
+        int cdep = fdep[cur], ckind = fkind[cur], cabove = fabove[cur];
         for (int t = 0; t < glen; ++t) {
-            const int cur = sh_cur;
-            if (fdep[cur] + 1 > A.depth_max) break;
-            const int32_t tk = A.ngram_draft[q * A.ngram_ld + t];
-            const int cnt = sh_cnt;
+            if (cdep + 1 > A.depth_max) break;
+            const int32_t tk = staged ? ctok[s * A.ngram_ld + t] : A.ngram_draft[q * A.ngram_ld + t];
             int found = -1;
-            for (int base = 1; base < cnt && found < 0; base += kWave) {
+            for (int base = 1; base < cntr && found < 0; base += kWave) {
                 const int c = base + lane;
-                const bool hit = c < cnt && fpar[c] == cur && ftok[c] == tk;
+                const bool hit = c < cntr && fpar[c] == cur && ftok[c] == tk;
                 const uint64_t bal = __ballot(hit);
                 if (bal) found = base + (int)__builtin_ctzll(bal);
             }
-            if (found < 0 && cnt >= cmax) break;
-            if (lane == 0) {
-                if (found >= 0) sh_cur = found;
-                else {
-                    ftok[cnt] = tk; fpar[cnt] = cur; fdep[cnt] = fdep[cur] + 1;
-                    sh_cnt = cnt + 1;
-                    sh_cur = cnt;
+            if (found < 0 && cntr >= cmax) break;
+            const int up = cabove + ((ckind & 3) == 3);   // n-gram nodes above a child of cur
+            const int bucket = 4 * ev + (up < 3 ? up : 3);
+            if (found >= 0) {
+                const int fk = fkind[found];
+                if (lane == 0) {
+                    if ((fk & 3) != 3 && bucket > fagree[found]) fagree[found] = (int8_t)bucket;
+                    fkind[found] = (uint8_t)(fk | 4);
                 }
+                cur = found;
+                cdep = fdep[found];
+                ckind = fk | 4;
+                cabove = fabove[found];
+            } else {
+                // a new node has no children yet, so every later token of the
+                // chain becomes a new node too: lane i writes the i-th one
+                // (the chain's length, the depth limit and c_max bound them)
+                int rem = glen - t;
+                rem = rem < A.depth_max - cdep ? rem : A.depth_max - cdep;
+                rem = rem < cmax - cntr ? rem : cmax - cntr;
+                if (lane < rem) {
+                    const int i = lane, node = cntr + lane, ui = up + i;
+                    ftok[node] = staged ? ctok[s * A.ngram_ld + t + i] : A.ngram_draft[q * A.ngram_ld + t + i];
+                    fpar[node] = i == 0 ? cur : node - 1;
+                    fdep[node] = cdep + 1 + i;
+                    fkind[node] = 3;
+                    fabove[node] = (int8_t)(ui < 127 ? ui : 127);
+                    fbucket[node] = (int8_t)(4 * ev + (ui < 3 ? ui : 3));
+                    fagree[node] = -1;
+                }
+                cntr += rem;
+                break;
             }
-            __syncthreads();
+            __builtin_amdgcn_wave_barrier();
         }
-        __syncthreads();
+        __builtin_amdgcn_wave_barrier();
     }
+    if (lane == 0) sh_cnt = cntr;
+    __syncthreads();
     const int cnt = sh_cnt;
-    // denominators of the Eq. (6) form: w_none[p] + sum of the children's weights (index order)
+    // weights: given by candidate index, or exp of the Eq. (6) scores (none = 1)
     const float* wn = A.w_node + (int64_t)r * cmax;
     const float* wz = A.w_none + (int64_t)r * cmax;
+    if (P.scored) {
+        const spec_tree_scores& S = P.sc;
+        const double lps = logit_prob((double)S.p_src[r]);
+        const double plus = lps > 0.0 ? lps : 0.0;
+        const double pc = (double)S.psi_ctx[r], br = (double)S.b_req[r];
+        for (int j = lane; j < cnt; j += kWave) {
+            double sj = 0.0;
+            const int kind = fkind[j] & 3;
+            if (j == 0) {
+                fw[j] = 0.0;
+                continue;
+            }
+            if (kind == 3) {
+                sj = lps + S.w_bucket[fbucket[j]] + pc + br;
+            } else {
+                const int p = fdep[j], k = (j - 1) % Kc, ps = kind == 1 ? 0 : 1;
+                const double lh = logit_prob((double)S.h[(int64_t)r * P_ + p - 1]);
+                const double ls = logit_prob((double)S.sigma[(int64_t)r * P_ + p - 1]);
+                const double psi = pc + S.psi_depth[p < 15 ? p : 15];
+                if (kind == 1) {
+                    sj = S.a[0] + S.a[1] * lh + S.a[2] * ls + psi + br;
+                } else {
+                    const double rr = clamp_prob((double)S.r_share[((int64_t)r * P_ + p - 1) * Kc + k]);
+                    sj = S.a[3] + S.a[4] * log(rr) + S.a[5] * lh + S.a[6] * ls + psi + br;
+                }
+                if (fagree[j] >= 0) sj += plus + S.w_agreed[fagree[j]][ps];
+                int contra = -1;
+                for (int c = 1; c < cnt; ++c)
+                    if (fpar[c] == fpar[j] && (fkind[c] & 3) == 3 && ftok[c] != ftok[j] && fbucket[c] / 4 > contra)
+                        contra = fbucket[c] / 4;
+                if (contra >= 0) sj += -plus + S.w_contra[contra][ps];
+            }
+            fw[j] = exp(sj);
+        }
+    } else {
+        for (int j = lane; j < cnt; j += kWave) fw[j] = (double)wn[j];
+    }
+    __syncthreads();
+    // denominators of the Eq. (6) form: none + the children's weights (index order)
     for (int p = lane; p < cnt; p += kWave) {
-        double den = (double)wz[p];
+        double den = P.scored ? 1.0 : (double)wz[p];
         for (int c = 1; c < cnt; ++c)
-            if (fpar[c] == p) den += (double)wn[c];
+            if (fpar[c] == p) den += fw[c];
         fden[p] = den;
         fsel[p] = 0;
     }
     __syncthreads();
     if (lane == 0) {
         fQ[0] = 1.0;
-        for (int j = 1; j < cnt; ++j) fQ[j] = fQ[fpar[j]] * ((double)wn[j] / fden[fpar[j]]);
+        for (int j = 1; j < cnt; ++j) fQ[j] = fQ[fpar[j]] * (fw[j] / fden[fpar[j]]);
     }
     __syncthreads();
     // best-first: rank by (fp32 Q desc, index asc); keep rank < rows_cap - 1
@@ -447,28 +551,83 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
             rank += ki > kj;
         }
         fsel[j] = rank < keep;
+        if (rank < A.rows_cap) sQrank[rank] = fQ[j];
     }
     __syncthreads();
-    __shared__ int32_t st_n[SPEC_MAX_ROWS], st_p[SPEC_MAX_ROWS];
-    if (lane == 0) {
-        fsel[0] = 1;
-        // depth-first layout, children in index order
-        int sp = 0, row = 0;
-        st_n[sp] = 0; st_p[sp] = -1; ++sp;
-        int32_t* nt = A.node_token + (int64_t)r * A.rows_cap;
-        int32_t* pr = A.parent_row + (int64_t)r * A.rows_cap;
-        float* Qo = A.Q + (int64_t)r * A.rows_cap;
-        while (sp > 0 && row < A.rows_cap) {
-            --sp;
-            const int u = st_n[sp];
-            nt[row] = (u == 0) ? -1 : ftok[u];
-            pr[row] = st_p[sp];
-            Qo[row] = (float)fQ[u];
-            const int my = row++;
-            for (int c = cnt - 1; c >= 1; --c)
-                if (fsel[c] && fpar[c] == u && sp < SPEC_MAX_ROWS) { st_n[sp] = c; st_p[sp] = my; ++sp; }
+    if (A.s_curve && lane == 0) {
+        // S(n): the first n - 1 nodes of the best-first order, accumulated in order
+        float* Sc = A.s_curve + (int64_t)r * A.rows_cap;
+        double acc = 0.0;
+        for (int n = 1; n <= A.rows_cap; ++n) {
+            Sc[n - 1] = (float)acc;
+            if (n - 1 < cnt - 1) acc += sQrank[n - 1];
         }
-        for (int i = row; i < A.rows_cap; ++i) { nt[i] = -1; pr[i] = -1; Qo[i] = 0.0f; }
+    }
+    // Depth-first layout, children in index order, by the whole wave.  The
+    // selected nodes (the anchor and at most rows_cap - 1 candidates, a
+    // parent-closed set) are compacted in index order, node i on lane i, each
+    // knowing its parent's compact position; a wave-uniform walk then keeps a
+    // mask of the unvisited children of every node on the current path and
+    // always takes the lowest one.
+    __shared__ int32_t scomp[SPEC_MAX_ROWS];      // compact position -> forest node
+    __shared__ int16_t scpos[SPEC_MAX_FOREST];    // forest node -> compact position
+    __shared__ uint64_t stk[SPEC_MAX_ROWS];       // unvisited children per depth
+    __shared__ int32_t stk_row[SPEC_MAX_ROWS];    // the row of that depth's node
+    __shared__ int32_t sorder[SPEC_MAX_ROWS], sprow[SPEC_MAX_ROWS];
+    if (lane == 0) fsel[0] = 1;
+    __syncthreads();
+    int m = 0;
+    for (int base = 0; base < cnt; base += kWave) {
+        const int c = base + lane;
+        const bool sel = c < cnt && fsel[c];
+        const uint64_t bal = __ballot(sel);
+        const int at = m + (int)__popcll(bal & ((1ull << lane) - 1ull));
+        if (sel && at < SPEC_MAX_ROWS) {
+            scomp[at] = c;
+            scpos[c] = (int16_t)at;
+        }
+        m += (int)__popcll(bal);
+    }
+    m = m < A.rows_cap ? m : A.rows_cap;
+    __syncthreads();
+    const int mynode = lane < m ? scomp[lane] : -1;
+    const int myparent = (lane < m && lane > 0) ? (int)scpos[fpar[mynode]] : -1;
+    auto children = [&](int u) -> uint64_t { return __ballot(lane < m && myparent == u); };
+    int row = 1, d = 0;
+    const uint64_t kids0 = children(0);   // every lane votes
+    if (lane == 0) { sorder[0] = 0; sprow[0] = -1; stk[0] = kids0; stk_row[0] = 0; }
+    __syncthreads();
+    while (d >= 0 && row < m) {
+        const uint64_t top = stk[d];
+        if (top == 0) { --d; continue; }
+        const int c = (int)__builtin_ctzll(top);
+        const uint64_t kids = children(c);
+        if (lane == 0) {
+            stk[d] = top & (top - 1);
+            sorder[row] = c;
+            sprow[row] = stk_row[d];
+            stk[d + 1] = kids;
+            stk_row[d + 1] = row;
+        }
+        __syncthreads();
+        ++d;
+        ++row;
+    }
+    __syncthreads();
+    int32_t* nt = A.node_token + (int64_t)r * A.rows_cap;
+    int32_t* pr = A.parent_row + (int64_t)r * A.rows_cap;
+    float* Qo = A.Q + (int64_t)r * A.rows_cap;
+    for (int k = lane; k < A.rows_cap; k += kWave) {
+        if (k < row) {
+            const int u = scomp[sorder[k]];
+            nt[k] = (u == 0) ? -1 : ftok[u];
+            pr[k] = sprow[k];
+            Qo[k] = (float)fQ[u];
+        } else {
+            nt[k] = -1; pr[k] = -1; Qo[k] = 0.0f;
+        }
+    }
+    if (lane == 0) {
         A.n_rows[r] = row;
         A.forest_count[r] = cnt;
         A.out_flags[r] = flags;
@@ -512,6 +671,9 @@ int spec_alloc_launch(const spec_alloc_args* a, hipStream_t st)
     } else {
         TreeBuildParams P;
         P.a = a->tree;
+        P.scored = a->tree.scores != nullptr;
+        if (P.scored) P.sc = *a->tree.scores;
+        else std::memset(&P.sc, 0, sizeof(P.sc));
         hipLaunchKernelGGL(k_tree, dim3(a->tree.bs), dim3(kWave), 0, st, P);
         hipLaunchKernelGGL(k_rows_scan, dim3(1), dim3(kAllocBlock), 0, st, a->tree.n_rows, a->tree.bs, a->tree.row_base,
                            a->tree.total_rows);

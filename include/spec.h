@@ -200,6 +200,40 @@ typedef struct spec_chain_alloc {
     uint32_t* out_flags;         /* device [bs], written (not OR-ed)              */
 } spec_chain_alloc;
 
+/* Acceptance estimates of the Eq. (6) form from its scores ([AS] Section 3.3,
+ * "Form"): q_j = exp(s_j) / (1 + the sum of exp(s) over the parent's
+ * candidates), the 1 being the explicit 'none' outcome, with
+ *   pick:    s = a0 + a1 logit h + a2 logit sigma + psi + b_req
+ *   sibling: s = a3 + a4 log r + a5 logit h + a6 logit sigma + psi + b_req
+ *   n-gram:  s = logit p_src + w_bucket[bucket] + psi_ctx + b_req
+ * with psi = psi_ctx + psi_depth[p] for a drafter candidate at position p.  A
+ * drafter candidate an n-gram chain also proposes (agreed) adds
+ * max(0, logit p_src) + w_agreed[proposal bucket][pick 0 / sibling 1]; one
+ * whose parent has an n-gram proposal of another token (contradicted)
+ * subtracts max(0, logit p_src) and adds w_contra[that proposal's evidence
+ * class][pick 0 / sibling 1]; the largest such bucket or class counts.  An
+ * n-gram node's evidence is its source's match length l (feature m, else n),
+ * class e = min(7, floor(log2 l)); its bucket is 4 e + min(3, n-gram nodes
+ * above it on its path).  Probabilities are clamped to [1e-6, 1 - 1e-6]
+ * before logit / log; everything in fp64.  With the prior a = (ln 2, 1, 0,
+ * 0, 1, 0, 0) and zero weights a pick's estimate is h. */
+typedef struct spec_tree_scores {
+    double a[7];
+    double w_bucket[32];
+    double w_agreed[32][2];
+    double w_contra[8][2];
+    double psi_depth[16];        /* by position p (p >= 15 uses 15)               */
+    const float* h;              /* device [bs, P] confidence head per position   */
+    const float* sigma;          /* device [bs, P] the pick's share               */
+    const float* r_share;        /* device [bs, P, Kc] a sibling's share of its
+                                    siblings' total (k >= 1)                      */
+    const float* psi_ctx;        /* device [bs] context term                      */
+    const float* b_req;          /* device [bs] per-request intercept             */
+    const float* p_src;          /* device [bs] the n-gram source's precision     */
+    const int32_t* ngram_feat;   /* device [bs*(P+1), 4] (n, a, m, j) of each
+                                    chain's draft (spec_ngram_draft's feat)       */
+} spec_tree_scores;
+
 typedef struct spec_tree_alloc {
     int32_t bs;
     int32_t P;                   /* drafter block positions                      */
@@ -211,6 +245,9 @@ typedef struct spec_tree_alloc {
     const int32_t* ngram_len;    /* device [bs*(P+1)]                             */
     const float* w_node;         /* device [bs, c_max] > 0, by candidate index    */
     const float* w_none;         /* device [bs, c_max] > 0, 'none' of a parent    */
+    const spec_tree_scores* scores; /* host, or NULL: with it the weights are
+                                    exp(s) of the Eq. (6) scores (w_none = 1) and
+                                    w_node / w_none are not read                  */
     int32_t c_max;               /* 1 + P*Kc .. SPEC_MAX_FOREST                   */
     int32_t depth_max;           /* >= 1 (32 on the pages)                        */
     int32_t rows_cap;            /* 1 .. SPEC_MAX_ROWS                            */
@@ -221,6 +258,10 @@ typedef struct spec_tree_alloc {
     int64_t* row_base;           /* device [bs] exclusive prefix sum of n_rows    */
     int32_t* total_rows;         /* device [1]                                    */
     int32_t* forest_count;       /* device [bs] candidates incl. the anchor       */
+    float* s_curve;              /* device [bs, rows_cap] or NULL: S(n) for n = 1..
+                                    rows_cap, the sum of Q over the first n - 1
+                                    nodes of the best-first order ([AS] Section
+                                    3.1: one pass over the order gives S(n))      */
     uint32_t* out_flags;         /* device [bs], written                          */
 } spec_tree_alloc;
 

@@ -340,16 +340,46 @@ def commit(ctx, ctx_len, ctx_cap, out_tokens, out_num, flags):
 # trees
 # ---------------------------------------------------------------------------
 
-def tree_build(block, ng_draft, ng_len, w_node, w_none, depth_max=32, rows_cap=16):
-    """block: [P, Kc]; ng_draft: [P+1, L]; returns the verify rows and the forest."""
+class _TreeScore(C.Structure):
+    _fields_ = [("a", C.c_double * 7), ("w_bucket", C.c_double * 32), ("w_agreed", (C.c_double * 2) * 32),
+                ("w_contra", (C.c_double * 2) * 8), ("psi_depth", C.c_double * 16), ("h", C.c_void_p),
+                ("sigma", C.c_void_p), ("r_share", C.c_void_p), ("psi_ctx", C.c_double), ("b_req", C.c_double),
+                ("p_src", C.c_double), ("ng_feat", C.c_void_p)]
+
+
+def tree_score_struct(coef, h, sigma, r_share, psi_ctx, b_req, p_src, ng_feat):
+    """Eq. (6) scoring inputs of one request: coef holds a [7], w_bucket [32],
+    w_agreed [32, 2], w_contra [8, 2], psi_depth [16]; h, sigma [P]; r_share
+    [P, Kc]; ng_feat [P + 1, 4].  Returns (struct, arrays it points to)."""
+    keep = [_c(h, np.float64), _c(sigma, np.float64), _c(r_share, np.float64), _c(ng_feat, np.int32)]
+    st = _TreeScore()
+    st.a[:] = [float(x) for x in coef["a"]]
+    st.w_bucket[:] = [float(x) for x in coef["w_bucket"]]
+    for i in range(32):
+        st.w_agreed[i][:] = [float(x) for x in coef["w_agreed"][i]]
+    for i in range(8):
+        st.w_contra[i][:] = [float(x) for x in coef["w_contra"][i]]
+    st.psi_depth[:] = [float(x) for x in coef["psi_depth"]]
+    st.h, st.sigma, st.r_share, st.ng_feat = (_p(a) for a in keep)
+    st.psi_ctx, st.b_req, st.p_src = float(psi_ctx), float(b_req), float(p_src)
+    return st, keep
+
+
+def tree_build(block, ng_draft, ng_len, w_node=None, w_none=None, depth_max=32, rows_cap=16, scores=None,
+               c_max=None):
+    """block: [P, Kc]; ng_draft: [P+1, L]; returns the verify rows, the S(n)
+    curve and the forest.  Weights by candidate index (w_node, w_none), or the
+    Eq. (6) scores (``scores``: the keyword arguments of tree_score_struct)."""
     block = _c(block, np.int32)
     P, Kc = block.shape
     ng = _c(ng_draft, np.int32)
     L = ng.shape[1]
     ngl = _c(ng_len, np.int32)
-    wn = _c(w_node, np.float32)
-    wz = _c(w_none, np.float32)
-    c_max = len(wn)
+    wn = None if w_node is None else _c(w_node, np.float32)
+    wz = None if w_none is None else _c(w_none, np.float32)
+    c_max = len(wn) if c_max is None else int(c_max)
+    sc, keep = (None, None) if scores is None else tree_score_struct(**scores)
+    S_curve = np.zeros(rows_cap, np.float64)
     node_token = np.full(rows_cap, -1, np.int32)
     parent_row = np.full(rows_cap, -1, np.int32)
     Q = np.zeros(rows_cap, np.float64)
@@ -361,23 +391,31 @@ def tree_build(block, ng_draft, ng_len, w_node, w_none, depth_max=32, rows_cap=1
     flag = C.c_uint32(0)
     cnt = lib().oracle_tree_build(C.c_int(P), C.c_int(Kc), _p(block), C.c_int(L), _p(ng), _p(ngl),
                                   _p(wn), _p(wz), C.c_int(c_max), C.c_int(depth_max), C.c_int(rows_cap),
-                                  _p(node_token), _p(parent_row), _p(Q), C.byref(n_rows),
+                                  None if sc is None else C.byref(sc),
+                                  _p(node_token), _p(parent_row), _p(Q), C.byref(n_rows), _p(S_curve),
                                   _p(ft), _p(fp), _p(fk), _p(fQ), C.byref(flag))
     return dict(node_token=node_token, parent_row=parent_row, Q=Q, n_rows=n_rows.value, count=cnt,
-                f_token=ft[:cnt], f_parent=fp[:cnt], f_kind=fk[:cnt], f_Q=fQ[:cnt], flag=flag.value)
+                S_curve=S_curve, f_token=ft[:cnt], f_parent=fp[:cnt], f_kind=fk[:cnt], f_Q=fQ[:cnt],
+                flag=flag.value)
 
 
-def tree_build_batch(block, ng_draft, ng_len, w_node, w_none, depth_max=32, rows_cap=16):
-    """block [BS,P,Kc], ng_draft [BS*(P+1), L], ng_len [BS*(P+1)], weights [BS, c_max]."""
+def tree_build_batch(block, ng_draft, ng_len, w_node=None, w_none=None, depth_max=32, rows_cap=16, scores=None,
+                     c_max=None):
+    """block [BS,P,Kc], ng_draft [BS*(P+1), L], ng_len [BS*(P+1)], weights [BS, c_max], or ``scores``:
+    a list of per-request keyword dicts of tree_score_struct."""
     BS, P, _ = block.shape
     L = ng_draft.shape[1]
     ng = ng_draft.reshape(BS, P + 1, L)
     ngl = ng_len.reshape(BS, P + 1)
     out = dict(node_token=np.full((BS, rows_cap), -1, np.int32), parent_row=np.full((BS, rows_cap), -1, np.int32),
                Q=np.zeros((BS, rows_cap)), n_rows=np.zeros(BS, np.int32), count=np.zeros(BS, np.int32),
-               flags=np.zeros(BS, np.uint32), forests=[])
+               flags=np.zeros(BS, np.uint32), S_curve=np.zeros((BS, rows_cap)), forests=[])
     for r in range(BS):
-        t = tree_build(block[r], ng[r], ngl[r], w_node[r], w_none[r], depth_max, rows_cap)
+        if scores is None:
+            t = tree_build(block[r], ng[r], ngl[r], w_node[r], w_none[r], depth_max, rows_cap)
+        else:
+            t = tree_build(block[r], ng[r], ngl[r], None, None, depth_max, rows_cap, scores=scores[r], c_max=c_max)
+        out["S_curve"][r] = t["S_curve"]
         for k in ("node_token", "parent_row", "Q"):
             out[k][r] = t[k]
         out["n_rows"][r] = t["n_rows"]

@@ -669,14 +669,63 @@ void oracle_commit(int bs, int32_t* ctx, int64_t ctx_stride, int32_t* ctx_len, i
  * depth-first from the anchor, children in index order.
  * Returns the number of forest nodes.
  * ====================================================================== */
+/* ======================================================================
+ * Acceptance estimates of the Eq. (6) form with its scores ([AS] Section 3.3,
+ * "Form"): q_j = exp(s_j) / (1 + sum over the parent's candidates of exp(s)),
+ * the 1 being the explicit none outcome (score 0), and
+ *   pick:    s = a0 + a1 logit h + a2 logit sigma + psi + b_req
+ *   sibling: s = a3 + a4 log r + a5 logit h + a6 logit sigma + psi + b_req
+ *   n-gram:  s = logit p_src + w_bucket + psi + b_req
+ * where for a drafter candidate at position p psi = psi_ctx + psi_depth[p]
+ * (the context term and the depth term) and for an n-gram node psi = psi_ctx.
+ * A drafter candidate that an n-gram chain also proposes (agreed) adds
+ * max(0, logit p_src) + w_agreed[proposal bucket][pick or sibling]; one whose
+ * parent has an n-gram proposal with another token (contradicted) subtracts
+ * max(0, logit p_src) and adds w_contra[that proposal's evidence][pick or
+ * sibling].  An n-gram node's evidence is the copy its chain continues, the
+ * source's match length l (the feature m, or n when m = 0), in classes
+ * e = min(7, floor(log2 l)); its bucket is 4 e + min(3, the n-gram nodes
+ * above it on its path).  Where several proposals agree with or contradict a
+ * candidate, the one of largest bucket (evidence) counts.  Probabilities are
+ * clamped to [1e-6, 1 - 1e-6] before their logit or log.  All in fp64.
+ * ====================================================================== */
+typedef struct {
+    double a[7];
+    double w_bucket[32];
+    double w_agreed[32][2];
+    double w_contra[8][2];
+    double psi_depth[16];        /* by drafter position p (clamped to 15)           */
+    const double* h;             /* [P] confidence head at each position             */
+    const double* sigma;         /* [P] the pick's share                             */
+    const double* r_share;       /* [P * Kc] a sibling's share of its siblings' total */
+    double psi_ctx, b_req, p_src;
+    const int32_t* ng_feat;      /* [(P + 1) * 4] (n, a, m, j) of each source's draft */
+} oracle_tree_score;
+
+static double clamp_p(double x) { return x < 1e-6 ? 1e-6 : (x > 1.0 - 1e-6 ? 1.0 - 1e-6 : x); }
+static double logit_p(double x) { x = clamp_p(x); return log(x / (1.0 - x)); }
+
+static int evidence_class(const int32_t* feat)
+{
+    int l = feat[2] > 0 ? feat[2] : feat[0];
+    int e = 0;
+    while (e < 7 && (l >> (e + 1)) > 0) ++e;
+    return e;
+}
+
 int oracle_tree_build(int P, int Kc, const int32_t* block, int L, const int32_t* ng, const int32_t* ng_len,
-                      const float* w_node, const float* w_none, int c_max, int depth_max, int rows_cap,
-                      int32_t* node_token, int32_t* parent_row, double* Q_out, int32_t* n_rows,
+                      const float* w_node_in, const float* w_none_in, int c_max, int depth_max, int rows_cap,
+                      const oracle_tree_score* sc,
+                      int32_t* node_token, int32_t* parent_row, double* Q_out, int32_t* n_rows, double* S_curve,
                       int32_t* f_token, int32_t* f_parent, int32_t* f_kind, double* f_Q, uint32_t* flag)
 {
     int cnt = 1 + P * Kc;
     if (cnt > c_max) return -1;
     int* depth = (int*)calloc((size_t)c_max, sizeof(int));
+    int* above = (int*)calloc((size_t)c_max, sizeof(int));      /* n-gram nodes above on the path */
+    int* nbucket = (int*)malloc(sizeof(int) * (size_t)c_max);   /* n-gram node: its bucket */
+    int* agree_b = (int*)malloc(sizeof(int) * (size_t)c_max);   /* drafter node: best agreeing bucket */
+    for (int i = 0; i < c_max; ++i) { nbucket[i] = -1; agree_b[i] = -1; }
     f_token[0] = -1; f_parent[0] = -1; f_kind[0] = 0; depth[0] = 0;
     for (int p = 1; p <= P; ++p)
         for (int k = 0; k < Kc; ++k) {
@@ -688,29 +737,65 @@ int oracle_tree_build(int P, int Kc, const int32_t* block, int L, const int32_t*
         }
     for (int s = 0; s <= P; ++s) {
         int cur = (s == 0) ? 0 : 1 + (s - 1) * Kc;
+        const int e = sc ? evidence_class(sc->ng_feat + 4 * s) : 0;
         for (int t = 0; t < ng_len[s]; ++t) {
             if (depth[cur] + 1 > depth_max) break;
             int tok = ng[s * L + t];
             int found = -1;
             for (int c = 1; c < cnt; ++c)
                 if (f_parent[c] == cur && f_token[c] == tok) { found = c; break; }
+            const int up = above[cur] + ((f_kind[cur] & 3) == 3);   /* n-gram nodes above a child of cur */
+            const int bucket = 4 * e + (up < 3 ? up : 3);
             if (found >= 0) {
                 f_kind[found] |= 4;              /* agreed */
+                if ((f_kind[found] & 3) != 3 && bucket > agree_b[found]) agree_b[found] = bucket;
                 cur = found;
                 continue;
             }
             if (cnt >= c_max) break;
             f_token[cnt] = tok; f_parent[cnt] = cur; f_kind[cnt] = 3; depth[cnt] = depth[cur] + 1;
+            above[cnt] = up;
+            nbucket[cnt] = bucket;
             cur = cnt++;
         }
+    }
+    /* weights: given, or exp of the Eq. (6) scores with the none outcome at 1 */
+    double* wn = (double*)malloc(sizeof(double) * (size_t)cnt);
+    double* wz = (double*)malloc(sizeof(double) * (size_t)cnt);
+    for (int j = 0; j < cnt; ++j) {
+        if (!sc) { wn[j] = (double)w_node_in[j]; wz[j] = (double)w_none_in[j]; continue; }
+        wz[j] = 1.0;
+        if (j == 0) { wn[j] = 0.0; continue; }
+        const int kind = f_kind[j] & 3;
+        double sj;
+        const double lps = logit_p(sc->p_src), plus = lps > 0.0 ? lps : 0.0;
+        if (kind == 3) {
+            sj = lps + sc->w_bucket[nbucket[j]] + sc->psi_ctx + sc->b_req;
+        } else {
+            const int p = depth[j], k = (j - 1) % Kc;
+            const double lh = logit_p(sc->h[p - 1]), ls = logit_p(sc->sigma[p - 1]);
+            const double psi = sc->psi_ctx + sc->psi_depth[p < 15 ? p : 15];
+            const int ps = kind == 1 ? 0 : 1;
+            if (kind == 1) sj = sc->a[0] + sc->a[1] * lh + sc->a[2] * ls + psi + sc->b_req;
+            else sj = sc->a[3] + sc->a[4] * log(clamp_p(sc->r_share[(p - 1) * Kc + k])) + sc->a[5] * lh +
+                      sc->a[6] * ls + psi + sc->b_req;
+            if (agree_b[j] >= 0) sj += plus + sc->w_agreed[agree_b[j]][ps];
+            int contra = -1;   /* largest evidence among the parent's n-gram proposals of another token */
+            for (int c = 1; c < cnt; ++c)
+                if (f_parent[c] == f_parent[j] && (f_kind[c] & 3) == 3 && f_token[c] != f_token[j] &&
+                    nbucket[c] / 4 > contra)
+                    contra = nbucket[c] / 4;
+            if (contra >= 0) sj += -plus + sc->w_contra[contra][ps];
+        }
+        wn[j] = exp(sj);
     }
     /* acceptance estimates and path products (parents precede children) */
     f_Q[0] = 1.0;
     for (int j = 1; j < cnt; ++j) {
         int par = f_parent[j];
-        double den = (double)w_none[par];
-        for (int c = 1; c < cnt; ++c) if (f_parent[c] == par) den += (double)w_node[c];
-        f_Q[j] = f_Q[par] * ((double)w_node[j] / den);
+        double den = wz[par];
+        for (int c = 1; c < cnt; ++c) if (f_parent[c] == par) den += wn[c];
+        f_Q[j] = f_Q[par] * (wn[j] / den);
     }
     /* best-first selection of rows_cap - 1 candidates */
     int* order = (int*)malloc(sizeof(int) * (size_t)cnt);
@@ -737,6 +822,15 @@ int oracle_tree_build(int P, int Kc, const int32_t* block, int L, const int32_t*
     char* sel = (char*)calloc((size_t)cnt, 1);
     sel[0] = 1;
     for (int a = 0; a < take; ++a) sel[order[a]] = 1;
+    /* S(n) for every width n: the first n - 1 nodes of the best-first order
+     * ([AS] Section 3.1: one pass over the order gives S(n) for every n) */
+    if (S_curve) {
+        double acc = 0.0;
+        for (int n = 1; n <= rows_cap; ++n) {
+            S_curve[n - 1] = acc;
+            if (n - 1 < m) acc += f_Q[order[n - 1]];
+        }
+    }
     /* depth-first layout; an explicit stack of (node, parent row) */
     int* stack_n = (int*)malloc(sizeof(int) * (size_t)cnt);
     int* stack_p = (int*)malloc(sizeof(int) * (size_t)cnt);
@@ -756,6 +850,7 @@ int oracle_tree_build(int P, int Kc, const int32_t* block, int L, const int32_t*
     }
     *n_rows = row;
     free(depth); free(order); free(sel); free(stack_n); free(stack_p);
+    free(above); free(nbucket); free(agree_b); free(wn); free(wz);
     return cnt;
 }
 

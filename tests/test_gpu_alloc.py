@@ -131,3 +131,41 @@ def test_tree_build_config3():
             for k in ("node_token", "parent_row", "n_rows"):
                 assert_rows_equal(g[k], o[k], ok, f"{k} cap {rows_cap} depth {dmax}")
             assert_close(g["Q"], o["Q"], "Q")
+
+
+@pytest.mark.parametrize("prior_only", [True, False])
+def test_tree_build_eq6_scores_and_s_curve(prior_only):
+    """The tree build with the Eq. (6) scores computed on the device from the
+    drafter's and the n-gram chains' features (AdaSpark Section 3.3), and the
+    S(n) curve of the best-first order (Section 3.1), on the tree workload."""
+    import torch
+    import draft_verification_spec_amd as S
+    c = synth.config3_inputs()
+    BS, P, Kc = c["BS"], c["P"], c["Kc"]
+    qr, ex, el = synth.tree_queries(c["ctx"], c["ctx_len"], c["block"])
+    draft, dlen, feat = O.ngram_draft(c["ctx"], c["ctx_len"], c["n_min"], c["n_max"], c["L"], 256,
+                                      query_req=qr, extra=ex, extra_len=el)
+    f = synth.tree_score_inputs(BS, P, Kc, prior_only=prior_only)
+    per = [dict(coef=f["coef"], h=f["h"][r], sigma=f["sigma"][r], r_share=f["r_share"][r],
+                psi_ctx=f["psi_ctx"][r], b_req=f["b_req"][r], p_src=f["p_src"][r],
+                ng_feat=feat.reshape(BS, P + 1, 4)[r]) for r in range(BS)]
+    o = O.tree_build_batch(c["block"], draft, dlen, depth_max=c["depth_max"], rows_cap=c["rows_cap"], scores=per,
+                           c_max=c["c_max"])
+    sc = dict(coef=f["coef"], h=dev(f["h"]), sigma=dev(f["sigma"]), r_share=dev(f["r_share"]),
+              psi_ctx=dev(f["psi_ctx"]), b_req=dev(f["b_req"]), p_src=dev(f["p_src"]), ngram_feat=dev(feat))
+    g = S.spec_allocate_budget(mode="tree", block=dev(c["block"]), ngram_draft=dev(draft), ngram_len=dev(dlen),
+                               scores=sc, c_max=c["c_max"], depth_max=c["depth_max"], rows_cap=c["rows_cap"],
+                               s_curve=True)
+    torch.cuda.synchronize()
+    g = {k: host(v) for k, v in g.items()}
+    ok = ok_rows(o["flags"])
+    assert_rows_equal(g["forest_count"], o["count"], np.ones(len(ok), bool), "forest_count")
+    for k in ("node_token", "parent_row", "n_rows"):
+        assert_rows_equal(g[k], o[k], ok, k)
+    assert_close(g["Q"], o["Q"], "Q")
+    assert_close(g["s_curve"], o["S_curve"], "S(n)")
+    # the curve at the built width is the tree's own sum of Q
+    for r in range(BS):
+        n = g["n_rows"][r]
+        assert g["s_curve"][r, n - 1] == pytest.approx(g["Q"][r, 1:n].sum(), rel=1e-5)
+    print(f"  S(16) mean {g['s_curve'][:, -1].mean():.3f}, excused {np.mean(~ok):.3f}")

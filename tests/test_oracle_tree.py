@@ -139,3 +139,114 @@ def test_tree_walk_is_greedy_decode_of_markov_target():
     assert list(res["out_path_rows"][0, :5]) == [0, 1, 3, 4, 6]
     # at most one child of an accepted node matches: a path
     assert len(set(res["out_path_rows"][0, :5])) == 5
+
+
+# ---------------------------------------------------------------------------
+# Eq. (6) scores and the S(n) curve (AdaSpark Section 3.3 "Form" and
+# "Learning"; Section 3.1: one pass over the order gives S(n) for every n)
+# ---------------------------------------------------------------------------
+
+def prior(**over):
+    """The empty-store prior: pick ln 2 + logit h, sibling log r, every other
+    coefficient and bucket weight 0."""
+    coef = dict(a=[np.log(2.0), 1.0, 0.0, 0.0, 1.0, 0.0, 0.0], w_bucket=np.zeros(32), w_agreed=np.zeros((32, 2)),
+                w_contra=np.zeros((8, 2)), psi_depth=np.zeros(16))
+    coef.update(over)
+    return coef
+
+
+def scores(coef, P, Kc, h=None, sigma=None, r=None, psi_ctx=0.0, b_req=0.0, p_src=0.5, feat=None):
+    return dict(coef=coef, h=np.full(P, 0.5) if h is None else h, sigma=np.full(P, 0.5) if sigma is None else sigma,
+                r_share=np.full((P, Kc), 1.0 / max(1, Kc - 1)) if r is None else r, psi_ctx=psi_ctx, b_req=b_req,
+                p_src=p_src, ng_feat=np.zeros((P + 1, 4), np.int32) if feat is None else feat)
+
+
+def test_prior_gives_the_head_to_the_pick_and_shares_to_siblings():
+    """With the prior and siblings' shares summing to 1, a pick's estimate is
+    its confidence head h, each sibling gets its share of half the rest and
+    'none' the other half: odds 2h/(1-h) and r against the none outcome's 1."""
+    block = np.array([[10, 11, 12]], np.int32)
+    ng = np.full((2, 3), -1, np.int32)
+    t = O.tree_build(block, ng, np.zeros(2, np.int32), rows_cap=8, c_max=16,
+                     scores=scores(prior(), 1, 3, h=np.array([0.7]), r=np.array([[0.0, 0.6, 0.4]])))
+    fQ = t["f_Q"]
+    assert fQ[1] == pytest.approx(0.7, rel=1e-12)
+    assert fQ[2] == pytest.approx(0.6 * 0.15, rel=1e-12) and fQ[3] == pytest.approx(0.4 * 0.15, rel=1e-12)
+
+
+def test_ngram_node_prior_and_bucket():
+    """A lone n-gram node takes its source's precision at the prior; its
+    bucket weight multiplies the odds.  The chain continues a 7-token copy
+    (evidence class 2); the second node has one n-gram node above it, so its
+    bucket is 4 * 2 + 1 = 9."""
+    block = np.array([[10]], np.int32)
+    ng = np.array([[20, 21, -1], [-1, -1, -1]], np.int32)        # anchor chain: 20 (not the pick), 21
+    feat = np.array([[7, 1, 0, 100], [0, 0, 0, -1]], np.int32)
+    wb = np.arange(32) * 0.01
+    wb[9] = 0.5
+    t = O.tree_build(block, ng, np.array([2, 0], np.int32), rows_cap=8, c_max=16,
+                     scores=scores(prior(w_bucket=wb), 1, 1, h=np.array([0.6]), p_src=0.8, feat=feat))
+    fp, fk, fQ, ft = t["f_parent"], t["f_kind"], t["f_Q"], t["f_token"]
+    n1, n2 = 2, 3
+    assert ft[n1] == 20 and ft[n2] == 21 and fp[n2] == n1 and (fk[n2] & 3) == 3
+    odds1 = 0.8 / 0.2 * np.exp(wb[8])                 # bucket 4 * 2 + 0 under the anchor
+    odds_pick = 2 * 0.6 / 0.4 * np.exp(-np.log(4.0))  # contradicted: minus max(0, logit 0.8)
+    assert fQ[n1] == pytest.approx(odds1 / (1 + odds1 + odds_pick), rel=1e-12)
+    assert fQ[1] == pytest.approx(odds_pick / (1 + odds1 + odds_pick), rel=1e-12)
+    odds2 = 0.8 / 0.2 * np.exp(0.5)
+    assert fQ[n2] == pytest.approx(fQ[n1] * odds2 / (1 + odds2), rel=1e-12)
+
+
+def test_agreed_and_weak_sources():
+    """An agreed pick adds max(0, logit p_src) plus its agreed-bucket weight;
+    a source below 1/2 neither lifts the tokens it agrees with nor sinks the
+    ones it contradicts."""
+    block = np.array([[10], [11]], np.int32)
+    ng = np.array([[10, 11], [-1, -1], [-1, -1]], np.int32)      # the anchor chain agrees with both picks
+    feat = np.array([[40, 1, 0, 5], [0, 0, 0, -1], [0, 0, 0, -1]], np.int32)   # evidence class 5
+    wa = np.zeros((32, 2))
+    wa[20, 0], wa[21, 0] = 0.25, 0.125        # buckets 4 * 5 + 0 (position 1) and + 0 (position 2: no n-gram above)
+    h = np.array([0.6, 0.7])
+    for p_src, lift in ((0.9, np.log(9.0)), (0.3, 0.0)):
+        t = O.tree_build(block, ng, np.array([2, 0, 0], np.int32), rows_cap=8, c_max=16,
+                         scores=scores(prior(w_agreed=wa), 2, 1, h=h, p_src=p_src, feat=feat))
+        assert t["count"] == 3 and (t["f_kind"][1] & 4) and (t["f_kind"][2] & 4)
+        for node, hp, w in ((1, 0.6, 0.25), (2, 0.7, 0.25)):
+            odds = 2 * hp / (1 - hp) * np.exp(lift + w)
+            q = odds / (1 + odds)
+            got = t["f_Q"][node] / (t["f_Q"][t["f_parent"][node]])
+            assert got == pytest.approx(q, rel=1e-12), (p_src, node)
+
+
+def test_s_curve_is_the_best_tree_of_every_width():
+    """S(n) equals, for every width n, the largest sum of Q over parent-closed
+    sets of n - 1 candidates (Proposition 1 applied at every width), with the
+    Eq. (6) scores under random coefficients."""
+    rng = np.random.Generator(np.random.Philox(77))
+    checked = 0
+    for trial in range(40):
+        P, Kc, L = int(rng.integers(1, 4)), int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        block, ng, ngl, _, _ = random_forest_inputs(rng, P, Kc, L)
+        coef = prior(a=rng.normal(0, 1, 7), w_bucket=rng.normal(0, 1, 32), w_agreed=rng.normal(0, 1, (32, 2)),
+                     w_contra=rng.normal(0, 1, (8, 2)), psi_depth=rng.normal(0, 0.5, 16))
+        feat = np.zeros((P + 1, 4), np.int32)
+        feat[:, 0] = rng.integers(1, 20, P + 1)
+        sc = scores(coef, P, Kc, h=rng.uniform(0.05, 0.95, P), sigma=rng.uniform(0.05, 0.95, P),
+                    r=rng.uniform(0.05, 0.95, (P, Kc)), psi_ctx=rng.normal(), b_req=rng.normal(),
+                    p_src=rng.uniform(0.05, 0.95), feat=feat)
+        c_max = 1 + P * Kc + (P + 1) * L
+        full = O.tree_build(block, ng, ngl, rows_cap=c_max, c_max=c_max, scores=sc)
+        cnt = full["count"]
+        if cnt > 12:
+            continue
+        # the estimates of a parent's children and its 'none' outcome are a distribution
+        fpar, fQ = full["f_parent"], full["f_Q"]
+        for par in range(cnt):
+            kids = [j for j in range(1, cnt) if fpar[j] == par]
+            if kids:
+                assert sum(fQ[j] for j in kids) / fQ[par] < 1.0
+        for n in range(1, cnt + 1):
+            want = 0.0 if n == 1 else parent_closed_best(fpar, fQ, n - 1)
+            assert full["S_curve"][n - 1] == pytest.approx(want, rel=1e-12, abs=1e-300)
+            checked += 1
+    assert checked > 100

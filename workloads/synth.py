@@ -30,7 +30,7 @@ import numpy as np
 SEED_BASE = 20261202
 
 # Seed streams.
-S_CTX, S_LOGITS, S_DRAFT, S_UNIFORM, S_TREE, S_TRUTH = 0, 1, 2, 3, 4, 5
+S_CTX, S_LOGITS, S_DRAFT, S_UNIFORM, S_TREE, S_TRUTH, S_SCORES = 0, 1, 2, 3, 4, 5, 6
 
 # Planted logit for the truth token of a target row: far above the maximum of
 # N(0, 2^2) over 151,936 draws (about 8.6), so at T=1 the truth token carries
@@ -348,6 +348,32 @@ def config3_inputs(BS=64, V=151936, P=8, Kc=4, T_ctx=4096, src_len=3000, rows_ca
     return dict(config=c, BS=BS, V=V, P=P, Kc=Kc, L=L, rows_cap=rows_cap, depth_max=depth_max,
                 c_max=c_max, ctx=ctx, ctx_len=ctx_len, truth=truth, block=block,
                 w_node=w_node, w_none=w_none, n_min=3, n_max=15, max_draft=L, copy_cap=256)
+
+
+def tree_score_inputs(BS, P, Kc, config=3, prior_only=False):
+    """Features and coefficients of the Eq. (6) scores for a tree batch: a
+    confidence head h and pick share sigma per position, sibling shares r
+    (Dirichlet over the siblings), a context term and intercept per request,
+    the n-gram source's precision, and coefficients drawn around the
+    empty-store prior (pick ln 2 + logit h, sibling log r, the rest 0).  Inputs
+    only; the scores are computed by the step."""
+    rng = rng_for(config, S_SCORES)
+    h = rng.uniform(0.2, 0.95, (BS, P)).astype(np.float32)
+    sigma = rng.uniform(0.3, 0.9, (BS, P)).astype(np.float32)
+    r = np.zeros((BS, P, Kc), np.float32)
+    if Kc > 1:
+        r[:, :, 1:] = rng.dirichlet(np.ones(Kc - 1), (BS, P)).astype(np.float32)
+    psi_ctx = rng.normal(0, 0.2, BS).astype(np.float32)
+    b_req = rng.normal(0, 0.2, BS).astype(np.float32)
+    p_src = rng.uniform(0.3, 0.9, BS).astype(np.float32)
+    a = np.array([np.log(2.0), 1.0, 0.0, 0.0, 1.0, 0.0, 0.0])
+    coef = dict(a=a, w_bucket=np.zeros(32), w_agreed=np.zeros((32, 2)), w_contra=np.zeros((8, 2)),
+                psi_depth=np.zeros(16))
+    if not prior_only:
+        coef = dict(a=a + rng.normal(0, 0.3, 7), w_bucket=rng.normal(0, 0.3, 32),
+                    w_agreed=rng.normal(0, 0.3, (32, 2)), w_contra=rng.normal(0, 0.3, (8, 2)),
+                    psi_depth=rng.normal(0, 0.1, 16))
+    return dict(coef=coef, h=h, sigma=sigma, r_share=r, psi_ctx=psi_ctx, b_req=b_req, p_src=p_src)
 
 
 def tree_queries(ctx, ctx_len, block):
