@@ -13,7 +13,9 @@ lengths to a separate buffer, so every timed step does the same work.
 A second record times the batch-allocation step (n-gram draft -> chain
 selection and budget allocation of 256 slots -> verification -> commit) at
 BS 128 with the same timing, a third the tree step (n-gram chains -> tree
-build with the Eq. (6) scores -> greedy verification -> commit) at BS 64.
+build with the Eq. (6) scores -> greedy verification -> commit) at BS 64, a
+fourth the same allocation step on the large-batch stress workload (BS 256,
+32,768-token contexts, budget 512, T = 0.7).
 
 Timing, per workload, on one stream: K eager steps with an event pair
 attached to the dispatch of every statistics kernel (that kernel's live
@@ -51,6 +53,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-budget", action="store_true", help="skip the batch-allocation step record")
     p.add_argument("--no-tree", action="store_true", help="skip the tree step record")
+    p.add_argument("--no-stress", action="store_true", help="skip the large-batch stress step record")
     p.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -259,15 +262,17 @@ def headline(K, W, hip, eager_only):
     return t
 
 
-def budget_step(K, W, hip, eager_only):
+def budget_step(K, W, hip, eager_only, config=2):
     """The batch-allocation step: n-gram draft -> selection and allocation of
-    256 slots -> verification of the chosen chains -> commit."""
+    the budget's slots -> verification of the chosen chains -> commit; at BS
+    128 with a budget of 256 (config=2), or the large-batch stress workload at
+    BS 256, 32,768-token contexts, budget 512 and T = 0.7 (config=4)."""
     import numpy as np
     import torch
     import draft_verification_spec_amd as S
     from workloads import synth
     dev = torch.device("cuda:0")
-    c = synth.config2(ctx_extra=64)
+    c = synth.config2(ctx_extra=64) if config == 2 else synth.config4(ctx_extra=64)
     BS, V, L = c["BS"], c["V"], 15
     g = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     ctx, ctx_len = g(c["ctx"]), g(c["ctx_len"])
@@ -307,9 +312,13 @@ def budget_step(K, W, hip, eager_only):
     sizing = host_sizing(S, surv, BS)
     rows_bytes = total_rows * V * 2
     step_bytes = rows_bytes + int(c["ctx_len"].sum()) * 4
-    return {"workload": "batch budget allocation + verify + commit + n-gram draft: BS=128, V=151936, model chain "
-                        "B=7 (greedy) + n-gram chain up to 15 (n 5..15), budget 256 draft slots, lambda 0.309, "
-                        "bf16 target rows, T=1.0, 8192-token contexts",
+    workload = ("batch budget allocation + verify + commit + n-gram draft: BS=128, V=151936, model chain "
+                "B=7 (greedy) + n-gram chain up to 15 (n 5..15), budget 256 draft slots, lambda 0.309, "
+                "bf16 target rows, T=1.0, 8192-token contexts" if config == 2 else
+                "large-batch stress, n-gram draft + allocation + verify + commit: BS=256, V=151936, Zipf(1.1) "
+                "32768-token contexts with planted repeats, model chain B=7 (greedy) + n-gram up to 15 with the "
+                "Table 5 estimator, budget 512, lambda 0.309, bf16 target rows, T=0.7")
+    return {"workload": workload,
             "timing": t["mode"], "steps_per_s": t["steps_per_s"], "ms_per_step": t["ms_per_step"],
             "verified_rows_per_step": total_rows, "algorithmic_bytes": step_bytes,
             "GBps": step_bytes / (t["ms_per_step"] * 1e-3) / 1e9,
@@ -456,6 +465,8 @@ def main():
         res["budget_step"] = budget_step(K, W, hip, args.eager)
     if not args.no_tree:
         res["tree_step"] = tree_step(K, W, hip, args.eager)
+    if not args.no_stress:
+        res["stress_step"] = budget_step(K, W, hip, args.eager, config=4)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(h["c"])
     print(json.dumps(res), flush=True)
