@@ -961,10 +961,13 @@ __global__ __launch_bounds__(kBlock) void k_stats_flat(StatsParams P)
 }
 
 // The same pass without a row list, for batches whose rows per request are
-// close to their bound: grid ((TM + DM) * splits, bs) with TM the target rows
-// and DM the draft slots a request can have; workgroup (x, r) takes chunk
-// x % splits of request r's target row j = x / splits (j < TM) or of the
-// draft row of slot j - TM, and exits when the request has no such row.  Its
+// close to their bound: grid ((TM + DM) * pairs, bs) with TM the target rows
+// and DM the draft slots a request can have and pairs = ceil(splits / 2);
+// workgroup (x, r) takes chunks 2 (x % pairs) and the next one of request
+// r's target row j = x / pairs (j < TM) or of the draft row of slot j - TM,
+// and exits when the request has no such row.  Both chunks' loads go out
+// first, so the second chunk's data arrives while the first is reduced (a
+// workgroup holds 32 KB in flight; 2% faster than one chunk each).  Its
 // inputs are a handful of uniform words, read with scalar loads in one round
 // trip (the slot's flag byte through its aligned word).  Workgroup (0, r) also
 // resets request r's residual bookkeeping.
@@ -974,8 +977,9 @@ __global__ __launch_bounds__(kBlock) void k_stats_rows(StatsParams P, int32_t TM
     __shared__ GroupRed R;
     const int t = threadIdx.x;
     const int r = blockIdx.y;
-    const int32_t j = (int32_t)blockIdx.x / P.splits;
-    const int32_t s = (int32_t)blockIdx.x - j * P.splits;
+    const int32_t npair = (P.splits + 1) / 2;
+    const int32_t j = (int32_t)blockIdx.x / npair;
+    const int32_t s = 2 * ((int32_t)blockIdx.x - j * npair);   // the first of the two chunks
     const int k = j - TM;   // the draft slot, when j >= TM
     // every input first, before any store (so that they stay scalar loads)
     const int32_t nt = target_rows(P, r);
@@ -1010,10 +1014,15 @@ __global__ __launch_bounds__(kBlock) void k_stats_rows(StatsParams P, int32_t TM
         const int64_t stride = isd ? P.dstride : P.stride;
         const int64_t clo = (int64_t)s * P.chunk;
         const int64_t chi = (clo + P.chunk < P.vocab) ? clo + P.chunk : P.vocab;
-        uint4 raw[kTile];
+        const bool two = s + 1 < P.splits;   // an odd last pair has one chunk
+        const int64_t clo1 = clo + P.chunk;
+        const int64_t chi1 = two ? ((clo1 + P.chunk < P.vocab) ? clo1 + P.chunk : P.vocab) : clo1;
+        uint4 raw[kTile], raw1[kTile];
         group_issue<DT>(base, stride, row, ok, clo, chi, t, raw);
+        group_issue<DT>(base, stride, row, ok && two, clo1, chi1, t, raw1);
         Partial* out = P.part + ((int64_t)r * P.NR + prow) * P.splits + s;
         group_chunk<DT, GREEDY>(raw, clo, ok ? chi : clo, P.c, R, 0, 0, t, out, !ok);
+        group_chunk<DT, GREEDY>(raw1, clo1, (ok && two) ? chi1 : clo1, P.c, R, 1, 0, t, two ? out + 1 : nullptr, !ok);
     }
     if (P.done && blockIdx.x == 0) {
         if (t == 0) P.done[r] = 0;
@@ -2163,7 +2172,7 @@ static void launch_flat_d(const StatsParams& P, bool greedy, bool draft, int64_t
 template <int DT, bool GREEDY, bool DITEMS>
 static void launch_rows_t(const StatsParams& P, int tm, int dm, const StatsLaunch& L)
 {
-    const dim3 grid((unsigned)((tm + dm) * P.splits), (unsigned)P.bs);
+    const dim3 grid((unsigned)((tm + dm) * ((P.splits + 1) / 2)), (unsigned)P.bs);
     auto kern = k_stats_rows<DT, GREEDY, DITEMS>;
     if (L.e0 || L.e1)
         hipExtLaunchKernelGGL(kern, grid, dim3(kBlock), 0, L.st, L.e0, L.e1, 0, P, (int32_t)tm);
