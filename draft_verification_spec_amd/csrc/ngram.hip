@@ -1,11 +1,9 @@
 // N-gram prompt-lookup drafter (Hybrid Spark, Section 4.1 "One step" and
-// Section 4.2 match features; Algorithm 1, NGRAMSCAN): one workgroup of 1024
-// threads per query, one launch (the scan itself is ngram_scan).
+// Section 4.2 match features; Algorithm 1, NGRAMSCAN): one workgroup per
+// query, one launch (the scan itself is ngram_scan).
 #include "ngram_scan.hpp"
 
 namespace spec {
-
-constexpr int kScanBlock = 1024;
 
 struct NgramParams {
     int32_t bs, nq;
@@ -40,29 +38,43 @@ __device__ __forceinline__ Text query_text(const NgramParams& P, int q)
 
 // PLAIN: query q is request q and there is no extra text, so the first batch
 // can be addressed before the length arrives (positions clamped into the row).
-template <bool PLAIN>
-__global__ __launch_bounds__(kScanBlock) void k_ngram(NgramParams P)
+// NT threads and NB positions per thread per batch: the host picks the
+// smallest window (NT * NB tokens) that holds the longest text, so a text
+// takes one batch and the workgroup no more LDS than it needs.
+template <bool PLAIN, int NT, int NB>
+__global__ __launch_bounds__(NT) void k_ngram(NgramParams P)
 {
     const int q = blockIdx.x;
-    int32_t v[kBatch];
+    int32_t v[NB];
     if constexpr (PLAIN) {
         const int32_t* row = P.ctx + (int64_t)q * P.ctx_stride;
         const int64_t last = P.ctx_stride - 1;   // >= 0 (checked by the host)
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int64_t j = threadIdx.x + (int64_t)u * kScanBlock;
+        for (int u = 0; u < NB; ++u) {
+            const int64_t j = threadIdx.x + (int64_t)u * NT;
             v[u] = row[j < last ? j : last];
         }
     }
     const Text x = query_text(P, q);
-    __shared__ int32_t win[kScanBlock * kBatch];
-    __shared__ NgramShared<kScanBlock> S;
+    __shared__ int32_t win[NT * NB];
+    __shared__ NgramShared<NT> S;
     NgramOut O;
     O.n_min = P.n_min; O.n_max = P.n_max; O.max_draft = P.max_draft; O.cap = P.cap;
     O.draft = P.draft + (int64_t)q * P.max_draft;
     O.draft_len = P.draft_len + q;
     O.feat = P.feat + 4 * (int64_t)q;
-    ngram_scan<kScanBlock>(x, win, S, O, v, PLAIN);
+    ngram_scan<NT, NB>(x, win, S, O, v, PLAIN);
+}
+
+template <bool PLAIN>
+static void launch_ngram(const NgramParams& P, int64_t text_max, hipStream_t st)
+{
+    if (text_max <= 512 * 16)
+        hipLaunchKernelGGL((k_ngram<PLAIN, 512, 16>), dim3(P.nq), dim3(512), 0, st, P);
+    else if (text_max <= 1024 * 16)
+        hipLaunchKernelGGL((k_ngram<PLAIN, 1024, 16>), dim3(P.nq), dim3(1024), 0, st, P);
+    else
+        hipLaunchKernelGGL((k_ngram<PLAIN, 1024, 32>), dim3(P.nq), dim3(1024), 0, st, P);
 }
 
 }  // namespace spec
@@ -80,9 +92,8 @@ int spec_ngram_launch(const spec_ngram_args* a, hipStream_t st)
     P.extra = a->extra; P.extra_stride = a->extra ? a->extra_stride : 0; P.extra_len = a->extra_len;
     P.n_min = a->n_min; P.n_max = a->n_max; P.max_draft = a->max_draft; P.cap = a->copy_cap;
     P.draft = a->draft; P.draft_len = a->draft_len; P.feat = a->feat;
-    if (!a->query_req && !a->extra && a->nq == a->bs && a->ctx_stride >= 1)
-        hipLaunchKernelGGL(k_ngram<true>, dim3(a->nq), dim3(kScanBlock), 0, st, P);
-    else
-        hipLaunchKernelGGL(k_ngram<false>, dim3(a->nq), dim3(kScanBlock), 0, st, P);
+    const int64_t text_max = a->ctx_stride + (a->extra ? a->extra_stride : 0);
+    if (!a->query_req && !a->extra && a->nq == a->bs && a->ctx_stride >= 1) launch_ngram<true>(P, text_max, st);
+    else launch_ngram<false>(P, text_max, st);
     return spec_record_hip_error(hipGetLastError());
 }

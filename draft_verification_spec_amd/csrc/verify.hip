@@ -1974,12 +1974,25 @@ __global__ __launch_bounds__(kWave) void k_tree_walk(TreeParams P)
     __shared__ int32_t sPath[SPEC_MAX_ROWS];
     __shared__ int32_t sNum;
     __shared__ uint32_t sFl;
+    // the rows' chunk partials, staged in LDS with every load in flight at
+    // once when they fit (a row's merge would otherwise wait on one
+    // dependent load per chunk)
+    constexpr int kWalkParts = 2048;
+    __shared__ Partial sp[kWalkParts];
+    const int nparts = n * P.splits;
+    const bool staged = nparts <= kWalkParts;
+    const Partial* gp = P.part + (int64_t)r * rm * P.splits;
+    if (staged)
+        for (int i = t; i < nparts; i += kWave) sp[i] = gp[i];
     if (t < n) {
-        int32_t idx;
-        sOk[t] = merge_argmax(P.part + ((int64_t)r * rm + t) * P.splits, P.splits, 1, &idx);
-        sArg[t] = (idx == 0x7FFFFFFF) ? -1 : idx;
         sTok[t] = P.node_token[(int64_t)r * rm + t];
         sPar[t] = P.parent_row[(int64_t)r * rm + t];
+    }
+    __syncthreads();
+    if (t < n) {
+        int32_t idx;
+        sOk[t] = merge_argmax((staged ? sp : gp) + (int64_t)t * P.splits, P.splits, 1, &idx);
+        sArg[t] = (idx == 0x7FFFFFFF) ? -1 : idx;
     }
     for (int i = t; i < rm; i += kWave) { sOut[i] = -1; sPath[i] = -1; }
     __syncthreads();
