@@ -1963,30 +1963,46 @@ __global__ __launch_bounds__(kWave) void k_tree_walk(TreeParams P)
 {
     const int r = blockIdx.x, t = threadIdx.x;
     const int rm = P.rows_max;
+    // the rows' chunk partials (all rows_max rows of the request's slice, so
+    // that no load waits for the row count), the row count and the tree are
+    // all requested before the first use: one memory round trip in all
+    constexpr int kPer = 32;
+    constexpr int kWalkParts = kPer * kWave;
+    __shared__ Partial sp[kWalkParts];
+    const int total = rm * P.splits;
+    const bool staged = total <= kWalkParts;
+    const Partial* gp = P.part + (int64_t)r * rm * P.splits;
+    uint4 held[kPer];
+    {
+        // clamped to the slice's last partial (a repeat that is not stored)
+        const uint4* g4 = (const uint4*)gp;
+        const int last = (staged ? total : 1) - 1;
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int i = t + u * kWave;
+            held[u] = g4[i < last ? i : last];
+        }
+    }
     int n = P.n_rows[r];
+    int32_t tok = -2, par = -2;
+    if (t < rm) {
+        tok = P.node_token[(int64_t)r * rm + t];
+        par = P.parent_row[(int64_t)r * rm + t];
+    }
     const bool badlen = (n < 1 || n > rm);
     n = n < 1 ? 1 : (n > rm ? rm : n);
     __shared__ int32_t sArg[SPEC_MAX_ROWS];
     __shared__ int32_t sOk[SPEC_MAX_ROWS];
-    __shared__ int32_t sTok[SPEC_MAX_ROWS];
-    __shared__ int32_t sPar[SPEC_MAX_ROWS];
     __shared__ int32_t sOut[SPEC_MAX_ROWS];
     __shared__ int32_t sPath[SPEC_MAX_ROWS];
     __shared__ int32_t sNum;
     __shared__ uint32_t sFl;
-    // the rows' chunk partials, staged in LDS with every load in flight at
-    // once when they fit (a row's merge would otherwise wait on one
-    // dependent load per chunk)
-    constexpr int kWalkParts = 2048;
-    __shared__ Partial sp[kWalkParts];
-    const int nparts = n * P.splits;
-    const bool staged = nparts <= kWalkParts;
-    const Partial* gp = P.part + (int64_t)r * rm * P.splits;
-    if (staged)
-        for (int i = t; i < nparts; i += kWave) sp[i] = gp[i];
-    if (t < n) {
-        sTok[t] = P.node_token[(int64_t)r * rm + t];
-        sPar[t] = P.parent_row[(int64_t)r * rm + t];
+    {
+        // every slot is written (those past the slice with its last partial)
+        // so that no load sinks into a branch and waits alone
+        uint4* s4 = (uint4*)sp;
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) s4[t + u * kWave] = held[u];
     }
     __syncthreads();
     if (t < n) {
@@ -1996,23 +2012,26 @@ __global__ __launch_bounds__(kWave) void k_tree_walk(TreeParams P)
     }
     for (int i = t; i < rm; i += kWave) { sOut[i] = -1; sPath[i] = -1; }
     __syncthreads();
-    if (t == 0) {
-        uint32_t fl = badlen ? SPEC_FLAG_BAD_LENGTH : 0u;
-        for (int i = 0; i < n; ++i) if (!sOk[i]) fl |= SPEC_FLAG_BAD_LOGITS;
+    // the path, one step per ballot: lane c holds row c's parent and token
+    // (rows_max <= 64, one wave), and the lowest matching child is taken
+    {
+        const int myPar = t < n ? par : -2, myTok = t < n ? tok : -2;
+        const uint64_t bad = __ballot(t < n && !sOk[t]);
         int u = 0, k = 0;
-        sPath[0] = 0;
+        if (t == 0) sPath[0] = 0;
         for (;;) {
             const int a = sArg[u];
-            int next = -1;
-            for (int c = 1; c < n; ++c)
-                if (sPar[c] == u && sTok[c] == a) { next = c; break; }
-            sOut[k++] = a;
-            if (next < 0 || k >= rm) break;
-            u = next;
-            sPath[k] = u;
+            const uint64_t hit = __ballot(t >= 1 && t < n && myPar == u && myTok == a);
+            if (t == 0) sOut[k] = a;
+            ++k;
+            if (!hit || k >= rm) break;
+            u = (int)__builtin_ctzll(hit);
+            if (t == 0) sPath[k] = u;
         }
-        sNum = k;
-        sFl = fl;
+        if (t == 0) {
+            sNum = k;
+            sFl = (badlen ? SPEC_FLAG_BAD_LENGTH : 0u) | (bad ? SPEC_FLAG_BAD_LOGITS : 0u);
+        }
     }
     __syncthreads();
     for (int i = t; i < rm; i += kWave) {
