@@ -378,6 +378,25 @@ __device__ __forceinline__ int evidence_of(const int32_t* feat)
     return l <= 1 ? 0 : min(7, 31 - __clz(l));
 }
 
+// A double from lane l (wave-uniform l), and a double from lane l of each lane's choosing.
+__device__ __forceinline__ double readlane_f64(double v, int l)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ double shfl_f64(double v, int l)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)b, l, kWave);
+    const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(b >> 32), l, kWave);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// NS register slots per lane: forest node j lives on lane j % 64 in slot
+// j / 64 during the chain walk (NS * 64 >= c_max).
+template <int NS>
 __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
 {
     const spec_tree_alloc& A = P.a;
@@ -398,90 +417,208 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
     __shared__ double fw[SPEC_MAX_FOREST];
     __shared__ double sQrank[SPEC_MAX_ROWS];
     __shared__ int32_t sh_cnt;
-    // the chains' tokens and lengths, staged in one round trip when they fit
+    // the chains' tokens, lengths and evidence classes, staged in one round
+    // trip (the tokens when they fit)
     constexpr int kChainLds = 2048;
     __shared__ int32_t ctok[kChainLds];
     __shared__ int32_t clen[SPEC_MAX_FOREST];
+    __shared__ int8_t cev[SPEC_MAX_FOREST];
     const int P_ = A.P, Kc = A.Kc, cmax = A.c_max;
     const int nd = 1 + P_ * Kc;
     const int64_t q0 = (int64_t)r * (P_ + 1);
     const bool staged = (int64_t)(P_ + 1) * A.ngram_ld <= kChainLds;
-    for (int i = lane; i <= P_; i += kWave) clen[i] = A.ngram_len[q0 + i];
+    for (int i = lane; i <= P_; i += kWave) {
+        clen[i] = A.ngram_len[q0 + i];
+        cev[i] = (int8_t)(P.scored ? evidence_of(P.sc.ngram_feat + 4 * (q0 + i)) : 0);
+    }
     if (staged)
         for (int i = lane; i < (P_ + 1) * A.ngram_ld; i += kWave) ctok[i] = A.ngram_draft[q0 * A.ngram_ld + i];
-    for (int i = lane; i < nd; i += kWave) {
-        if (i == 0) { ftok[0] = -1; fpar[0] = -1; fdep[0] = 0; fkind[0] = 0; }
-        else {
+    // the drafter nodes: parent, token, depth, kind; n-gram nodes above,
+    // bucket, agreeing bucket.  Slots past the node count hold parent -2.
+    int rpar[NS], rtok[NS], rdep[NS], rkind[NS], rabove[NS], rbucket[NS], ragree[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int i = s * kWave + lane;
+        rpar[s] = -2; rtok[s] = -2; rdep[s] = 0; rkind[s] = 0; rabove[s] = 0; rbucket[s] = -1; ragree[s] = -1;
+        if (i == 0) {
+            rpar[s] = -1; rtok[s] = -1;
+        } else if (i < nd) {
             const int p = (i - 1) / Kc + 1, k = (i - 1) % Kc;
-            ftok[i] = A.block[((int64_t)r * P_ + (p - 1)) * Kc + k];
-            fpar[i] = (p == 1) ? 0 : 1 + (p - 2) * Kc;
-            fdep[i] = p;
-            fkind[i] = k == 0 ? 1 : 2;
+            rtok[s] = A.block[((int64_t)r * P_ + (p - 1)) * Kc + k];
+            rpar[s] = (p == 1) ? 0 : 1 + (p - 2) * Kc;
+            rdep[s] = p;
+            rkind[s] = k == 0 ? 1 : 2;
         }
-        fabove[i] = 0;
-        fbucket[i] = -1;
-        fagree[i] = -1;
     }
     __syncthreads();
-    // n-gram chains from the anchor (s = 0) and each pick s.  The workgroup is
-    // one wave, so the walk's state (current node, its depth, kind and
-    // n-gram count, the node count) lives in wave-uniform registers; lane 0
-    // writes each new node, and the wave's LDS accesses stay in order.
+    // n-gram chains from the anchor (s = 0) and each pick s.  The walk's state
+    // (current node, its depth, kind and n-gram count, the node count) is
+    // wave-uniform.  A chain first descends through existing nodes while its
+    // tokens match (the lowest-index matching child each time) and then
+    // appends the rest of its tokens as a new path.
     uint32_t flags = 0;
     int cntr = nd;
-    for (int s = 0; s <= P_; ++s) {
-        const int64_t q = q0 + s;
-        int glen = clen[s];
+    // the chains' lengths and evidence classes on the lanes (chain sc on lane
+    // sc) when there are at most 64 chains
+    const bool lane_chains = P_ < kWave;
+    const int lglen = lane_chains && lane <= P_ ? clen[lane] : 0;
+    const int lev = lane_chains && lane <= P_ ? (int)cev[lane] : 0;
+    for (int sc = 0; sc <= P_; ++sc) {
+        const int64_t q = q0 + sc;
+        int glen = lane_chains ? __builtin_amdgcn_readlane(lglen, sc) : clen[sc];
         if (glen < 0 || glen > A.ngram_ld) { flags |= SPEC_FLAG_BAD_LENGTH; glen = glen < 0 ? 0 : A.ngram_ld; }
-        const int ev = P.scored ? evidence_of(P.sc.ngram_feat + 4 * q) : 0;
-        int cur = (s == 0) ? 0 : 1 + (s - 1) * Kc;
-        int cdep = fdep[cur], ckind = fkind[cur], cabove = fabove[cur];
-        for (int t = 0; t < glen; ++t) {
-            if (cdep + 1 > A.depth_max) break;
-            const int32_t tk = staged ? ctok[s * A.ngram_ld + t] : A.ngram_draft[q * A.ngram_ld + t];
-            int found = -1;
-            for (int base = 1; base < cntr && found < 0; base += kWave) {
-                const int c = base + lane;
-                const bool hit = c < cntr && fpar[c] == cur && ftok[c] == tk;
-                const uint64_t bal = __ballot(hit);
-                if (bal) found = base + (int)__builtin_ctzll(bal);
+        if (glen == 0) continue;   // nothing to walk or add
+        const int ev = lane_chains ? __builtin_amdgcn_readlane(lev, sc) : (int)cev[sc];
+        const int32_t* src = staged ? ctok + (int64_t)sc * A.ngram_ld : A.ngram_draft + q * A.ngram_ld;
+        int cur = (sc == 0) ? 0 : 1 + (sc - 1) * Kc;   // a drafter node (< nd <= 1024)
+        int cdep = 0, ckind = 0, cabove = 0;
+        auto read_cur = [&]() {   // cur's depth, kind and n-gram count, from its lane
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                if (s == (cur >> 6)) {
+                    cdep = __builtin_amdgcn_readlane(rdep[s], cur & 63);
+                    ckind = __builtin_amdgcn_readlane(rkind[s], cur & 63);
+                    cabove = __builtin_amdgcn_readlane(rabove[s], cur & 63);
+                }
+        };
+        read_cur();
+        int ctk = lane < glen ? src[lane] : -1;   // the chain's first 64 tokens
+        int t = 0;
+        bool tail = false;
+        if (glen <= kWave) {
+            // A node can only be the descent's t-th step if it sits at depth
+            // d0 + 1 + t and holds token t; such nodes key on their parent, the
+            // others never match.  The descent then costs one ballot per token.
+            const int d0 = cdep;
+            const int geff = glen < A.depth_max - d0 ? glen : A.depth_max - d0;
+            int key[NS];
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                key[s] = -2;
+                if (s * kWave < cntr) {
+                    const int tn = rdep[s] - d0 - 1;
+                    const int tkn = __shfl(ctk, tn & 63, kWave);
+                    key[s] = (tn >= 0 && tn < geff && rtok[s] == tkn) ? rpar[s] : -2;
+                }
             }
-            if (found < 0 && cntr >= cmax) break;
-            const int up = cabove + ((ckind & 3) == 3);   // n-gram nodes above a child of cur
-            const int bucket = 4 * ev + (up < 3 ? up : 3);
-            if (found >= 0) {
-                const int fk = fkind[found];
-                if (lane == 0) {
-                    if ((fk & 3) != 3 && bucket > fagree[found]) fagree[found] = (int8_t)bucket;
-                    fkind[found] = (uint8_t)(fk | 4);
+            uint64_t pm[NS];   // the nodes passed, as lane masks per slot
+#pragma unroll
+            for (int s = 0; s < NS; ++s) pm[s] = 0;
+            if (cntr <= kWave) {
+                // every node in slot 0: one compare, one ballot per token
+                while (t < geff) {
+                    const uint64_t bal = __builtin_amdgcn_ballot_w64(key[0] == cur);
+                    if (!bal) break;
+                    cur = (int)__builtin_ctzll(bal);
+                    pm[0] |= 1ull << cur;
+                    ++t;
+                }
+            }
+            while (t < geff && cntr > kWave) {
+                int nxt = -1;
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    if (nxt < 0 && s * kWave < cntr) {
+                        const uint64_t bal = __builtin_amdgcn_ballot_w64(key[s] == cur);
+                        if (bal) {
+                            const int l = (int)__builtin_ctzll(bal);
+                            pm[s] |= 1ull << l;
+                            nxt = s * kWave + l;
+                        }
+                    }
+                }
+                if (nxt < 0) break;
+                cur = nxt;
+                ++t;
+            }
+            // every node passed records the agreement: its bucket counts the
+            // n-gram nodes above it, which is its own n-gram count
+            if (t > 0) {
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    if ((pm[s] >> lane) & 1ull) {
+                        const int b = 4 * ev + (rabove[s] < 3 ? rabove[s] : 3);
+                        if ((rkind[s] & 3) != 3 && b > ragree[s]) ragree[s] = b;
+                        rkind[s] |= 4;
+                    }
+                }
+                read_cur();
+            }
+            tail = t < geff && cntr < cmax;
+        } else {
+            // chains longer than a wave: one token per step
+            for (; t < glen; ++t) {
+                if (cdep + 1 > A.depth_max) break;
+                if (t && (t & 63) == 0) ctk = t + lane < glen ? src[t + lane] : -1;   // the next 64
+                const int tk = __builtin_amdgcn_readlane(ctk, t & 63);
+                const int up = cabove + ((ckind & 3) == 3);   // n-gram nodes above a child of cur
+                const int bucket = 4 * ev + (up < 3 ? up : 3);
+                int found = -1, fk = 0, fd = 0, fa = 0;
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    if (found < 0 && s * kWave < cntr) {
+                        const uint64_t bal = __builtin_amdgcn_ballot_w64(rpar[s] == cur && rtok[s] == tk);
+                        if (bal) {
+                            const int l = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(bal));
+                            found = s * kWave + l;
+                            fk = __builtin_amdgcn_readlane(rkind[s], l);
+                            fd = __builtin_amdgcn_readlane(rdep[s], l);
+                            fa = __builtin_amdgcn_readlane(rabove[s], l);
+                            // the match's own lane records the agreement (selects,
+                            // not a branch, so the walk's state stays scalar)
+                            const bool me = lane == l;
+                            ragree[s] = (me && (fk & 3) != 3 && bucket > ragree[s]) ? bucket : ragree[s];
+                            rkind[s] = me ? (fk | 4) : rkind[s];
+                        }
+                    }
+                }
+                if (found < 0) {
+                    tail = cntr < cmax;
+                    break;
                 }
                 cur = found;
-                cdep = fdep[found];
+                cdep = fd;
                 ckind = fk | 4;
-                cabove = fabove[found];
-            } else {
-                // a new node has no children yet, so every later token of the
-                // chain becomes a new node too: lane i writes the i-th one
-                // (the chain's length, the depth limit and c_max bound them)
-                int rem = glen - t;
-                rem = rem < A.depth_max - cdep ? rem : A.depth_max - cdep;
-                rem = rem < cmax - cntr ? rem : cmax - cntr;
-                if (lane < rem) {
-                    const int i = lane, node = cntr + lane, ui = up + i;
-                    ftok[node] = staged ? ctok[s * A.ngram_ld + t + i] : A.ngram_draft[q * A.ngram_ld + t + i];
-                    fpar[node] = i == 0 ? cur : node - 1;
-                    fdep[node] = cdep + 1 + i;
-                    fkind[node] = 3;
-                    fabove[node] = (int8_t)(ui < 127 ? ui : 127);
-                    fbucket[node] = (int8_t)(4 * ev + (ui < 3 ? ui : 3));
-                    fagree[node] = -1;
-                }
-                cntr += rem;
-                break;
+                cabove = fa;
             }
-            __builtin_amdgcn_wave_barrier();
         }
-        __builtin_amdgcn_wave_barrier();
+        if (tail) {
+            // a new node has no children yet, so every later token of the
+            // chain becomes a new node too: node cntr + i is token t + i
+            // (the chain's length, the depth limit and c_max bound them)
+            const int up = cabove + ((ckind & 3) == 3);   // n-gram nodes above a child of cur
+            int rem = glen - t;
+            rem = rem < A.depth_max - cdep ? rem : A.depth_max - cdep;
+            rem = rem < cmax - cntr ? rem : cmax - cntr;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const int n = s * kWave + lane, i = n - cntr;
+                if (i >= 0 && i < rem) {
+                    const int ui = up + i;
+                    rtok[s] = src[t + i];
+                    rpar[s] = i == 0 ? cur : n - 1;
+                    rdep[s] = cdep + 1 + i;
+                    rkind[s] = 3;
+                    rabove[s] = ui < 127 ? ui : 127;
+                    rbucket[s] = 4 * ev + (ui < 3 ? ui : 3);
+                    ragree[s] = -1;
+                }
+            }
+            cntr += rem;
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int n = s * kWave + lane;
+        if (n < cntr) {
+            ftok[n] = rtok[s];
+            fpar[n] = rpar[s];
+            fdep[n] = rdep[s];
+            fkind[n] = (uint8_t)rkind[s];
+            fabove[n] = (int8_t)rabove[s];
+            fbucket[n] = (int8_t)rbucket[s];
+            fagree[n] = (int8_t)ragree[s];
+        }
     }
     if (lane == 0) sh_cnt = cntr;
     __syncthreads();
@@ -516,7 +653,7 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
                 }
                 if (fagree[j] >= 0) sj += plus + S.w_agreed[fagree[j]][ps];
                 int contra = -1;
-                for (int c = 1; c < cnt; ++c)
+                for (int c = nd; c < cnt; ++c)   // n-gram nodes come after the drafter's
                     if (fpar[c] == fpar[j] && (fkind[c] & 3) == 3 && ftok[c] != ftok[j] && fbucket[c] / 4 > contra)
                         contra = fbucket[c] / 4;
                 if (contra >= 0) sj += -plus + S.w_contra[contra][ps];
@@ -527,18 +664,45 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
         for (int j = lane; j < cnt; j += kWave) fw[j] = (double)wn[j];
     }
     __syncthreads();
-    // denominators of the Eq. (6) form: none + the children's weights (index order)
-    for (int p = lane; p < cnt; p += kWave) {
-        double den = P.scored ? 1.0 : (double)wz[p];
-        for (int c = 1; c < cnt; ++c)
-            if (fpar[c] == p) den += fw[c];
-        fden[p] = den;
-        fsel[p] = 0;
-    }
-    __syncthreads();
-    if (lane == 0) {
-        fQ[0] = 1.0;
-        for (int j = 1; j < cnt; ++j) fQ[j] = fQ[fpar[j]] * (fw[j] / fden[fpar[j]]);
+    // denominators of the Eq. (6) form: none + the children's weights (index
+    // order), then Q = the parent's Q times w / den along every path (index
+    // order, so a parent is done before its children)
+    if (cnt <= kWave) {
+        // one node per lane: the sums and the path products pass the children's
+        // weights and the parents' Q from lane to lane, without LDS round trips
+        const bool mine = lane < cnt;
+        const int pj = mine ? fpar[lane] : -2;
+        const double wj = mine ? fw[lane] : 0.0;
+        double den = P.scored ? 1.0 : (mine ? (double)wz[lane] : 0.0);
+        for (int c = 1; c < cnt; ++c) {
+            const int pc = __builtin_amdgcn_readlane(pj, c);
+            const double wc = readlane_f64(wj, c);
+            den = lane == pc ? den + wc : den;
+        }
+        const double ratio = wj / shfl_f64(den, pj < 0 ? 0 : pj);
+        double q = 1.0;
+        for (int j = 1; j < cnt; ++j) {
+            const double qp = readlane_f64(q, __builtin_amdgcn_readlane(pj, j));
+            q = lane == j ? qp * ratio : q;
+        }
+        if (mine) {
+            fden[lane] = den;
+            fQ[lane] = q;
+            fsel[lane] = 0;
+        }
+    } else {
+        for (int p = lane; p < cnt; p += kWave) {
+            double den = P.scored ? 1.0 : (double)wz[p];
+            for (int c = 1; c < cnt; ++c)
+                if (fpar[c] == p) den += fw[c];
+            fden[p] = den;
+            fsel[p] = 0;
+        }
+        __syncthreads();
+        if (lane == 0) {
+            fQ[0] = 1.0;
+            for (int j = 1; j < cnt; ++j) fQ[j] = fQ[fpar[j]] * (fw[j] / fden[fpar[j]]);
+        }
     }
     __syncthreads();
     // best-first: rank by (fp32 Q desc, index asc); keep rank < rows_cap - 1
@@ -554,26 +718,25 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
         if (rank < A.rows_cap) sQrank[rank] = fQ[j];
     }
     __syncthreads();
-    if (A.s_curve && lane == 0) {
-        // S(n): the first n - 1 nodes of the best-first order, accumulated in order
-        float* Sc = A.s_curve + (int64_t)r * A.rows_cap;
-        double acc = 0.0;
+    if (A.s_curve) {
+        // S(n): the first n - 1 nodes of the best-first order, accumulated in
+        // order (lane n - 1 holds the (n - 1)-th Q)
+        const double v = (lane < A.rows_cap && lane < cnt - 1) ? sQrank[lane] : 0.0;
+        double acc = 0.0, mine = 0.0;
         for (int n = 1; n <= A.rows_cap; ++n) {
-            Sc[n - 1] = (float)acc;
-            if (n - 1 < cnt - 1) acc += sQrank[n - 1];
+            mine = lane == n - 1 ? acc : mine;
+            if (n - 1 < cnt - 1) acc += readlane_f64(v, n - 1);
         }
+        if (lane < A.rows_cap) A.s_curve[(int64_t)r * A.rows_cap + lane] = (float)mine;
     }
     // Depth-first layout, children in index order, by the whole wave.  The
     // selected nodes (the anchor and at most rows_cap - 1 candidates, a
     // parent-closed set) are compacted in index order, node i on lane i, each
     // knowing its parent's compact position; a wave-uniform walk then keeps a
-    // mask of the unvisited children of every node on the current path and
-    // always takes the lowest one.
+    // mask of the unvisited children of every node on the current path (lane
+    // d holds depth d's) and always takes the lowest one.
     __shared__ int32_t scomp[SPEC_MAX_ROWS];      // compact position -> forest node
     __shared__ int16_t scpos[SPEC_MAX_FOREST];    // forest node -> compact position
-    __shared__ uint64_t stk[SPEC_MAX_ROWS];       // unvisited children per depth
-    __shared__ int32_t stk_row[SPEC_MAX_ROWS];    // the row of that depth's node
-    __shared__ int32_t sorder[SPEC_MAX_ROWS], sprow[SPEC_MAX_ROWS];
     if (lane == 0) fsel[0] = 1;
     __syncthreads();
     int m = 0;
@@ -592,39 +755,40 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
     __syncthreads();
     const int mynode = lane < m ? scomp[lane] : -1;
     const int myparent = (lane < m && lane > 0) ? (int)scpos[fpar[mynode]] : -1;
-    auto children = [&](int u) -> uint64_t { return __ballot(lane < m && myparent == u); };
+    auto children = [&](int u) -> uint64_t { return __builtin_amdgcn_ballot_w64(lane < m && myparent == u); };
+    // lane d: the unvisited children of the path's depth-d node and that
+    // node's row; lane k: row k's compact node and parent row
+    const uint64_t kids0 = children(0);
+    uint32_t stk_lo = lane == 0 ? (uint32_t)kids0 : 0u, stk_hi = lane == 0 ? (uint32_t)(kids0 >> 32) : 0u;
+    int stk_row = 0, ord = lane == 0 ? 0 : -1, prow = -1;
     int row = 1, d = 0;
-    const uint64_t kids0 = children(0);   // every lane votes
-    if (lane == 0) { sorder[0] = 0; sprow[0] = -1; stk[0] = kids0; stk_row[0] = 0; }
-    __syncthreads();
     while (d >= 0 && row < m) {
-        const uint64_t top = stk[d];
+        const uint64_t top = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)stk_hi, d) << 32)
+                           | (uint32_t)__builtin_amdgcn_readlane((int)stk_lo, d);
         if (top == 0) { --d; continue; }
         const int c = (int)__builtin_ctzll(top);
         const uint64_t kids = children(c);
-        if (lane == 0) {
-            stk[d] = top & (top - 1);
-            sorder[row] = c;
-            sprow[row] = stk_row[d];
-            stk[d + 1] = kids;
-            stk_row[d + 1] = row;
-        }
-        __syncthreads();
+        const int prw = __builtin_amdgcn_readlane(stk_row, d);
+        const uint64_t rest = top & (top - 1);
+        stk_lo = lane == d ? (uint32_t)rest : (lane == d + 1 ? (uint32_t)kids : stk_lo);
+        stk_hi = lane == d ? (uint32_t)(rest >> 32) : (lane == d + 1 ? (uint32_t)(kids >> 32) : stk_hi);
+        stk_row = lane == d + 1 ? row : stk_row;
+        ord = lane == row ? c : ord;
+        prow = lane == row ? prw : prow;
         ++d;
         ++row;
     }
-    __syncthreads();
     int32_t* nt = A.node_token + (int64_t)r * A.rows_cap;
     int32_t* pr = A.parent_row + (int64_t)r * A.rows_cap;
     float* Qo = A.Q + (int64_t)r * A.rows_cap;
-    for (int k = lane; k < A.rows_cap; k += kWave) {
-        if (k < row) {
-            const int u = scomp[sorder[k]];
-            nt[k] = (u == 0) ? -1 : ftok[u];
-            pr[k] = sprow[k];
-            Qo[k] = (float)fQ[u];
+    const int u = __shfl(mynode, ord < 0 ? 0 : ord, kWave);   // row lane's forest node
+    if (lane < A.rows_cap) {
+        if (lane < row) {
+            nt[lane] = (u == 0) ? -1 : ftok[u];
+            pr[lane] = prow;
+            Qo[lane] = (float)fQ[u];
         } else {
-            nt[k] = -1; pr[k] = -1; Qo[k] = 0.0f;
+            nt[lane] = -1; pr[lane] = -1; Qo[lane] = 0.0f;
         }
     }
     if (lane == 0) {
@@ -674,7 +838,13 @@ int spec_alloc_launch(const spec_alloc_args* a, hipStream_t st)
         P.scored = a->tree.scores != nullptr;
         if (P.scored) P.sc = *a->tree.scores;
         else std::memset(&P.sc, 0, sizeof(P.sc));
-        hipLaunchKernelGGL(k_tree, dim3(a->tree.bs), dim3(kWave), 0, st, P);
+        const int c = a->tree.c_max;
+        const dim3 g(a->tree.bs), b(kWave);
+        if (c <= 64) hipLaunchKernelGGL(k_tree<1>, g, b, 0, st, P);
+        else if (c <= 128) hipLaunchKernelGGL(k_tree<2>, g, b, 0, st, P);
+        else if (c <= 256) hipLaunchKernelGGL(k_tree<4>, g, b, 0, st, P);
+        else if (c <= 512) hipLaunchKernelGGL(k_tree<8>, g, b, 0, st, P);
+        else hipLaunchKernelGGL(k_tree<16>, g, b, 0, st, P);
         hipLaunchKernelGGL(k_rows_scan, dim3(1), dim3(kAllocBlock), 0, st, a->tree.n_rows, a->tree.bs, a->tree.row_base,
                            a->tree.total_rows);
     }

@@ -133,6 +133,42 @@ def test_tree_build_config3():
             assert_close(g["Q"], o["Q"], "Q")
 
 
+@pytest.mark.parametrize("c_max", [61, 64, 65, 130, 256, 257, 600, 1024])
+def test_tree_build_large_forests(c_max):
+    """Forests that fill one, several or all of the forest's 64-node groups,
+    chains longer than 64 tokens, and the c_max cap reached mid-chain."""
+    import torch
+    import draft_verification_spec_amd as S
+    rng = np.random.Generator(np.random.Philox(31 + c_max))
+    BS, P, Kc, L, vocab = 24, 15, 4, 70, 40
+    block = np.stack([np.stack([rng.choice(vocab, Kc, replace=False) for _ in range(P)])
+                      for _ in range(BS)]).astype(np.int32)
+    ngl = rng.integers(0, L + 1, BS * (P + 1)).astype(np.int32)
+    ng = rng.integers(0, vocab, (BS * (P + 1), L)).astype(np.int32)
+    # half the chains repeat an earlier chain's prefix, so they descend first
+    for q in range(BS * (P + 1)):
+        if q % (P + 1) and rng.random() < 0.5:
+            src = q - 1 - int(rng.integers(0, q % (P + 1)))
+            k = int(rng.integers(1, L))
+            ng[q, :k] = ng[src, :k]
+    wn = rng.standard_exponential((BS, c_max)).astype(np.float32)
+    wz = rng.standard_exponential((BS, c_max)).astype(np.float32)
+    for dmax, rows_cap in ((100, 64), (32, 16)):
+        print(f"tree build: c_max {c_max} depth {dmax} rows_cap {rows_cap}", flush=True)
+        o = O.tree_build_batch(block, ng, ngl, wn, wz, dmax, rows_cap)
+        g = S.spec_allocate_budget(mode="tree", block=dev(block), ngram_draft=dev(ng), ngram_len=dev(ngl),
+                                   w_node=dev(wn), w_none=dev(wz), depth_max=dmax, rows_cap=rows_cap)
+        torch.cuda.synchronize()
+        g = {k: host(v) for k, v in g.items()}
+        ok = ok_rows(o["flags"])
+        assert_rows_equal(g["forest_count"], o["count"], np.ones(BS, bool), "forest_count")
+        for k in ("node_token", "parent_row", "n_rows"):
+            assert_rows_equal(g[k], o[k], ok, f"{k} c_max {c_max} depth {dmax}")
+        assert_close(g["Q"], o["Q"], "Q")
+    if c_max <= 257:
+        assert o["count"].max() == c_max   # the cap is reached
+
+
 @pytest.mark.parametrize("prior_only", [True, False])
 def test_tree_build_eq6_scores_and_s_curve(prior_only):
     """The tree build with the Eq. (6) scores computed on the device from the
