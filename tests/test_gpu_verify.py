@@ -236,3 +236,70 @@ def test_tree_verify_config3():
     torch.cuda.synchronize()
     o2 = O.verify_tree(bits.reshape(-1, V), rb, t["node_token"], t["parent_row"], t["n_rows"])
     assert_rows_equal(host(g2["out_tokens"]), o2["out_tokens"], every, "bf16 out_tokens")
+
+
+def test_tree_verify_wide_trees_commit_and_flags():
+    """64-row trees over fp32 rows of V 151,936 (the request's chunk partials
+    no longer fit the walk's LDS stage), the commit into the contexts, and the
+    flagged cases: row counts outside [1, rows_max] (clamped), a NaN row, a
+    context without room."""
+    import torch
+    import draft_verification_spec_amd as S
+    rng = np.random.Generator(np.random.Philox(77))
+    BS, R, V = 12, 64, 151936
+    P, Kc, L, vocab = 15, 4, 40, 50
+    block = np.stack([np.stack([rng.choice(vocab, Kc, replace=False) for _ in range(P)])
+                      for _ in range(BS)]).astype(np.int32)
+    ngl = rng.integers(0, L + 1, BS * (P + 1)).astype(np.int32)
+    ng = rng.integers(0, vocab, (BS * (P + 1), L)).astype(np.int32)
+    cm = 1 + P * Kc + (P + 1) * L
+    wn = rng.standard_exponential((BS, cm)).astype(np.float32)
+    wz = rng.standard_exponential((BS, cm)).astype(np.float32)
+    t = O.tree_build_batch(block, ng, ngl, wn, wz, 100, R)
+    nt, pr, nr = t["node_token"], t["parent_row"], t["n_rows"].copy()
+    assert nr.min() == R
+    # the truth follows a random root-to-leaf walk of the tree, so paths run deep
+    truth = rng.integers(0, V, (BS, R + 1)).astype(np.int32)
+    for r in range(BS):
+        u, d = 0, 0
+        while True:
+            kids = [c for c in range(1, nr[r]) if pr[r, c] == u]
+            if not kids or rng.random() < 0.05:
+                break
+            u = kids[int(rng.integers(0, len(kids)))]
+            truth[r, d] = nt[r, u]
+            d += 1
+    rows = synth.tree_target_rows(3, nt, pr, nr, truth, V, R)
+    rows[2, 0, 123] = np.nan                      # a NaN in a row every request reads
+    n_in = nr.copy()
+    n_in[0], n_in[1] = 0, R + 5                   # clamped to 1 and R
+    n_ref = np.clip(n_in, 1, R).astype(np.int32)
+    rb = np.arange(BS, dtype=np.int64) * R
+    o = O.verify_tree(rows.reshape(-1, V), rb, nt, pr, n_ref)
+    print("verify tree (wide): committed per tree", o["out_num"].tolist(), flush=True)
+    assert o["out_num"][3:].max() > 8
+    cap = 300
+    ctx = rng.integers(0, V, (BS, cap)).astype(np.int32)
+    ctx_len = rng.integers(0, 200, BS).astype(np.int32)
+    ctx_len[3] = cap - 1                          # no room for two or more tokens
+    ctx_len[4] = cap - o["out_num"][4]            # exactly enough room
+    fl_ref = o["flags"].copy()
+    ctx_ref, len_ref = O.commit(ctx.copy(), ctx_len.copy(), cap, o["out_tokens"], o["out_num"], fl_ref)
+    tc, tl, tn = dev(ctx), dev(ctx_len), dev(np.zeros(BS, np.int32))
+    g = S.spec_verify_tree(dev(rows).reshape(-1, V), dev(rb), dev(nt), dev(pr), dev(n_in), ctx=tc, ctx_len=tl,
+                           ctx_cap=cap, ctx_len_out=tn)
+    torch.cuda.synchronize()
+    g = {k: host(v) for k, v in g.items()}
+    ok = np.ones(BS, bool)
+    ok[2] = False
+    for k in ("out_tokens", "out_num", "out_path_rows", "out_argmax"):
+        assert_rows_equal(g[k], o[k], ok, k)
+    fl = g["out_flags"].astype(np.uint32)
+    BAD_LENGTH = 1 << 11
+    assert fl[0] & BAD_LENGTH and fl[1] & BAD_LENGTH and not (fl[2:] & BAD_LENGTH).any()
+    assert fl[2] & O.BAD_LOGITS and not (np.delete(fl, 2) & O.BAD_LOGITS).any()
+    assert np.array_equal(fl & O.CTX_OVERFLOW, fl_ref & O.CTX_OVERFLOW) and fl[3] & O.CTX_OVERFLOW
+    assert not fl[4] & O.CTX_OVERFLOW
+    assert np.array_equal(host(tl), ctx_len)      # the input lengths stay; the new ones go to ctx_len_out
+    assert np.array_equal(np.delete(host(tn), 2), np.delete(len_ref, 2))
+    assert np.array_equal(np.delete(host(tc), 2, axis=0), np.delete(ctx_ref, 2, axis=0))
