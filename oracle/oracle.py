@@ -107,7 +107,9 @@ def _est(e) -> _Est:
 # ---------------------------------------------------------------------------
 
 def ngram_draft(ctx, ctx_len, n_min, n_max, max_draft=15, copy_cap=256,
-                query_req=None, extra=None, extra_len=None):
+                query_req=None, extra=None, extra_len=None, follow_ctx=0):
+    """Returns (draft, draft_len, feat), and with follow_ctx > 0 (the tree's
+    n-gram fill with its follower fallback) also the follower counts."""
     ctx = _c(ctx, np.int32)
     ctx_len = _c(ctx_len, np.int32)
     nq = len(query_req) if query_req is not None else ctx.shape[0]
@@ -117,10 +119,13 @@ def ngram_draft(ctx, ctx_len, n_min, n_max, max_draft=15, copy_cap=256,
     draft = np.full((nq, max_draft), -1, np.int32)
     dlen = np.zeros(nq, np.int32)
     feat = np.zeros((nq, 4), np.int32)
+    follow = np.zeros((nq, max_draft), np.int32)
     lib().oracle_ngram_draft(C.c_int(nq), _p(ctx), C.c_int64(ctx.shape[1]), _p(ctx_len), _p(qr), _p(ex),
                              C.c_int64(0 if ex is None else ex.shape[1]), _p(el),
                              C.c_int(n_min), C.c_int(n_max), C.c_int(max_draft), C.c_int(copy_cap),
-                             _p(draft), _p(dlen), _p(feat))
+                             C.c_int(follow_ctx), _p(draft), _p(dlen), _p(feat), _p(follow))
+    if follow_ctx > 0:
+        return draft, dlen, feat, follow
     return draft, dlen, feat
 
 
@@ -341,21 +346,21 @@ def commit(ctx, ctx_len, ctx_cap, out_tokens, out_num, flags):
 # ---------------------------------------------------------------------------
 
 class _TreeScore(C.Structure):
-    _fields_ = [("a", C.c_double * 7), ("w_bucket", C.c_double * 32), ("w_agreed", (C.c_double * 2) * 32),
+    _fields_ = [("a", C.c_double * 7), ("w_bucket", C.c_double * 64), ("w_agreed", (C.c_double * 2) * 64),
                 ("w_contra", (C.c_double * 2) * 8), ("psi_depth", C.c_double * 16), ("h", C.c_void_p),
                 ("sigma", C.c_void_p), ("r_share", C.c_void_p), ("psi_ctx", C.c_double), ("b_req", C.c_double),
                 ("p_src", C.c_double), ("ng_feat", C.c_void_p)]
 
 
 def tree_score_struct(coef, h, sigma, r_share, psi_ctx, b_req, p_src, ng_feat):
-    """Eq. (6) scoring inputs of one request: coef holds a [7], w_bucket [32],
-    w_agreed [32, 2], w_contra [8, 2], psi_depth [16]; h, sigma [P]; r_share
+    """Eq. (6) scoring inputs of one request: coef holds a [7], w_bucket [64],
+    w_agreed [64, 2], w_contra [8, 2], psi_depth [16]; h, sigma [P]; r_share
     [P, Kc]; ng_feat [P + 1, 4].  Returns (struct, arrays it points to)."""
     keep = [_c(h, np.float64), _c(sigma, np.float64), _c(r_share, np.float64), _c(ng_feat, np.int32)]
     st = _TreeScore()
     st.a[:] = [float(x) for x in coef["a"]]
     st.w_bucket[:] = [float(x) for x in coef["w_bucket"]]
-    for i in range(32):
+    for i in range(64):
         st.w_agreed[i][:] = [float(x) for x in coef["w_agreed"][i]]
     for i in range(8):
         st.w_contra[i][:] = [float(x) for x in coef["w_contra"][i]]
@@ -366,15 +371,17 @@ def tree_score_struct(coef, h, sigma, r_share, psi_ctx, b_req, p_src, ng_feat):
 
 
 def tree_build(block, ng_draft, ng_len, w_node=None, w_none=None, depth_max=32, rows_cap=16, scores=None,
-               c_max=None):
+               c_max=None, ng_follow=None):
     """block: [P, Kc]; ng_draft: [P+1, L]; returns the verify rows, the S(n)
     curve and the forest.  Weights by candidate index (w_node, w_none), or the
-    Eq. (6) scores (``scores``: the keyword arguments of tree_score_struct)."""
+    Eq. (6) scores (``scores``: the keyword arguments of tree_score_struct).
+    ng_follow [P+1, L]: follower counts of the chains' tokens (0 = copied)."""
     block = _c(block, np.int32)
     P, Kc = block.shape
     ng = _c(ng_draft, np.int32)
     L = ng.shape[1]
     ngl = _c(ng_len, np.int32)
+    nf = None if ng_follow is None else _c(ng_follow, np.int32)
     wn = None if w_node is None else _c(w_node, np.float32)
     wz = None if w_none is None else _c(w_none, np.float32)
     c_max = len(wn) if c_max is None else int(c_max)
@@ -389,7 +396,7 @@ def tree_build(block, ng_draft, ng_len, w_node=None, w_none=None, depth_max=32, 
     fk = np.zeros(c_max, np.int32)
     fQ = np.zeros(c_max, np.float64)
     flag = C.c_uint32(0)
-    cnt = lib().oracle_tree_build(C.c_int(P), C.c_int(Kc), _p(block), C.c_int(L), _p(ng), _p(ngl),
+    cnt = lib().oracle_tree_build(C.c_int(P), C.c_int(Kc), _p(block), C.c_int(L), _p(ng), _p(ngl), _p(nf),
                                   _p(wn), _p(wz), C.c_int(c_max), C.c_int(depth_max), C.c_int(rows_cap),
                                   None if sc is None else C.byref(sc),
                                   _p(node_token), _p(parent_row), _p(Q), C.byref(n_rows), _p(S_curve),
@@ -400,21 +407,24 @@ def tree_build(block, ng_draft, ng_len, w_node=None, w_none=None, depth_max=32, 
 
 
 def tree_build_batch(block, ng_draft, ng_len, w_node=None, w_none=None, depth_max=32, rows_cap=16, scores=None,
-                     c_max=None):
+                     c_max=None, ng_follow=None):
     """block [BS,P,Kc], ng_draft [BS*(P+1), L], ng_len [BS*(P+1)], weights [BS, c_max], or ``scores``:
-    a list of per-request keyword dicts of tree_score_struct."""
+    a list of per-request keyword dicts of tree_score_struct; ng_follow [BS*(P+1), L] or None."""
     BS, P, _ = block.shape
     L = ng_draft.shape[1]
     ng = ng_draft.reshape(BS, P + 1, L)
     ngl = ng_len.reshape(BS, P + 1)
+    nf = None if ng_follow is None else np.asarray(ng_follow).reshape(BS, P + 1, L)
     out = dict(node_token=np.full((BS, rows_cap), -1, np.int32), parent_row=np.full((BS, rows_cap), -1, np.int32),
                Q=np.zeros((BS, rows_cap)), n_rows=np.zeros(BS, np.int32), count=np.zeros(BS, np.int32),
                flags=np.zeros(BS, np.uint32), S_curve=np.zeros((BS, rows_cap)), forests=[])
     for r in range(BS):
+        f = None if nf is None else nf[r]
         if scores is None:
-            t = tree_build(block[r], ng[r], ngl[r], w_node[r], w_none[r], depth_max, rows_cap)
+            t = tree_build(block[r], ng[r], ngl[r], w_node[r], w_none[r], depth_max, rows_cap, ng_follow=f)
         else:
-            t = tree_build(block[r], ng[r], ngl[r], None, None, depth_max, rows_cap, scores=scores[r], c_max=c_max)
+            t = tree_build(block[r], ng[r], ngl[r], None, None, depth_max, rows_cap, scores=scores[r], c_max=c_max,
+                           ng_follow=f)
         out["S_curve"][r] = t["S_curve"]
         for k in ("node_token", "parent_row", "Q"):
             out[k][r] = t[k]

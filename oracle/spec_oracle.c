@@ -89,9 +89,61 @@ static double logit_at(const void* base, int dtype, int64_t i)
  *   a = 1 if there is no runner-up or it predicts the same next token.
  * The draft is the up-to-max_draft tokens after the best match.
  * ====================================================================== */
-static void ngram_one(const int32_t* x, int64_t T, int n_min, int n_max, int max_draft, int cap,
-                      int32_t* draft, int32_t* draft_len, int32_t* feat)
+/* ======================================================================
+ * N-gram fill's fallback.  [AS] Section 3.3, "N-gram candidates": a chain
+ * reads on along the earlier passage, or else takes the most frequent
+ * follower of its last three tokens (the context length F is a parameter).
+ *
+ * Readings: the fallback takes over for every position after the copy ends
+ * (the passage reaches the end of the text, or there was no match), one
+ * token at a time.  The context is the last F tokens of the text followed by
+ * the chain so far; its occurrences are counted in the text only, each with
+ * its follower inside the text.  The most frequent follower wins, ties going
+ * to the follower seen latest (the later-wins order of the copy rule).  A
+ * context with no follower, or with more than ORACLE_MAX_FOLLOWERS distinct
+ * followers, ends the chain.  follow[k] is the count of the winning follower
+ * at position k (0 for a copied token).
+ * ====================================================================== */
+#define ORACLE_MAX_FOLLOWERS 1024
+
+static void follower_fill(const int32_t* x, int64_t T, int F, int max_draft, int32_t* draft, int64_t* len,
+                          int32_t* follow)
 {
+    int32_t ftok[ORACLE_MAX_FOLLOWERS], fcnt[ORACLE_MAX_FOLLOWERS];
+    int64_t flast[ORACLE_MAX_FOLLOWERS];
+    int32_t c[64];
+    if (F > 64) return;
+    while (*len < max_draft && T + *len >= F) {
+        for (int i = 0; i < F; ++i) {           /* position T + len - F + i of text ++ chain */
+            int64_t q = T + *len - F + i;
+            c[i] = q < T ? x[q] : draft[q - T];
+        }
+        int nd = 0, over = 0;
+        for (int64_t p = F - 1; p + 1 < T; ++p) {
+            int i = 0;
+            while (i < F && x[p - (F - 1) + i] == c[i]) ++i;
+            if (i < F) continue;
+            int32_t f = x[p + 1];
+            int k = 0;
+            while (k < nd && ftok[k] != f) ++k;
+            if (k < nd) { ++fcnt[k]; flast[k] = p; continue; }
+            if (nd == ORACLE_MAX_FOLLOWERS) { over = 1; continue; }
+            ftok[nd] = f; fcnt[nd] = 1; flast[nd] = p; ++nd;
+        }
+        if (over || nd == 0) break;
+        int b = 0;
+        for (int k = 1; k < nd; ++k)
+            if (fcnt[k] > fcnt[b] || (fcnt[k] == fcnt[b] && flast[k] > flast[b])) b = k;
+        draft[*len] = ftok[b];
+        follow[*len] = fcnt[b];
+        ++*len;
+    }
+}
+
+static void ngram_one(const int32_t* x, int64_t T, int n_min, int n_max, int max_draft, int cap, int follow_ctx,
+                      int32_t* draft, int32_t* draft_len, int32_t* feat, int32_t* follow)
+{
+    for (int k = 0; k < max_draft; ++k) follow[k] = 0;
     int64_t best_j = -1, best_l = 0, ru_j = -1, ru_l = 0;
     for (int64_t j = 0; j + 1 < T; ++j) {
         int64_t lim = (j + 1 < cap) ? j + 1 : cap;
@@ -108,7 +160,9 @@ static void ngram_one(const int32_t* x, int64_t T, int n_min, int n_max, int max
     }
     for (int k = 0; k < max_draft; ++k) draft[k] = -1;
     if (best_j < 0) {
-        *draft_len = 0;
+        int64_t len = 0;
+        if (follow_ctx > 0) follower_fill(x, T, follow_ctx, max_draft, draft, &len, follow);
+        *draft_len = (int32_t)len;
         feat[0] = 0; feat[1] = 0; feat[2] = 0; feat[3] = -1;
         return;
     }
@@ -118,6 +172,7 @@ static void ngram_one(const int32_t* x, int64_t T, int n_min, int n_max, int max
     int64_t avail = T - 1 - best_j;
     int64_t len = avail < max_draft ? avail : max_draft;
     for (int64_t k = 0; k < len; ++k) draft[k] = x[best_j + 1 + k];
+    if (follow_ctx > 0) follower_fill(x, T, follow_ctx, max_draft, draft, &len, follow);
     *draft_len = (int32_t)len;
     feat[0] = (int32_t)n;
     feat[1] = a;
@@ -129,9 +184,10 @@ static void ngram_one(const int32_t* x, int64_t T, int n_min, int n_max, int max
  * text is ctx[req][0..ctx_len[req]) followed by extra[q][0..extra_len[q]). */
 void oracle_ngram_draft(int nq, const int32_t* ctx, int64_t ctx_stride, const int32_t* ctx_len,
                         const int32_t* query_req, const int32_t* extra, int64_t extra_stride,
-                        const int32_t* extra_len, int n_min, int n_max, int max_draft, int cap,
-                        int32_t* draft, int32_t* draft_len, int32_t* feat)
+                        const int32_t* extra_len, int n_min, int n_max, int max_draft, int cap, int follow_ctx,
+                        int32_t* draft, int32_t* draft_len, int32_t* feat, int32_t* follow)
 {
+    int32_t* fl_tmp = follow ? NULL : (int32_t*)malloc(sizeof(int32_t) * (size_t)max_draft);
     for (int q = 0; q < nq; ++q) {
         int req = query_req ? query_req[q] : q;
         int64_t tl = ctx_len[req];
@@ -139,10 +195,12 @@ void oracle_ngram_draft(int nq, const int32_t* ctx, int64_t ctx_stride, const in
         int32_t* x = (int32_t*)malloc(sizeof(int32_t) * (size_t)(tl + el + 1));
         memcpy(x, ctx + (int64_t)req * ctx_stride, sizeof(int32_t) * (size_t)tl);
         if (el) memcpy(x + tl, extra + (int64_t)q * extra_stride, sizeof(int32_t) * (size_t)el);
-        ngram_one(x, tl + el, n_min, n_max, max_draft, cap,
-                  draft + (int64_t)q * max_draft, draft_len + q, feat + 4 * (int64_t)q);
+        ngram_one(x, tl + el, n_min, n_max, max_draft, cap, follow_ctx,
+                  draft + (int64_t)q * max_draft, draft_len + q, feat + 4 * (int64_t)q,
+                  follow ? follow + (int64_t)q * max_draft : fl_tmp);
         free(x);
     }
+    free(fl_tmp);
 }
 
 /* ======================================================================
@@ -683,16 +741,18 @@ void oracle_commit(int bs, int32_t* ctx, int64_t ctx_stride, int32_t* ctx_len, i
  * parent has an n-gram proposal with another token (contradicted) subtracts
  * max(0, logit p_src) and adds w_contra[that proposal's evidence][pick or
  * sibling].  An n-gram node's evidence is the copy its chain continues, the
- * source's match length l (the feature m, or n when m = 0), in classes
+ * source's match length l (the feature m, or n when m = 0), or, for a token
+ * of the follower fallback, its follower count l, in classes
  * e = min(7, floor(log2 l)); its bucket is 4 e + min(3, the n-gram nodes
- * above it on its path).  Where several proposals agree with or contradict a
- * candidate, the one of largest bucket (evidence) counts.  Probabilities are
+ * above it on its path), plus 32 for a follower token (the kind).  Where
+ * several proposals agree with or contradict a candidate, the one of largest
+ * bucket (evidence class for a contradiction) counts.  Probabilities are
  * clamped to [1e-6, 1 - 1e-6] before their logit or log.  All in fp64.
  * ====================================================================== */
 typedef struct {
     double a[7];
-    double w_bucket[32];
-    double w_agreed[32][2];
+    double w_bucket[64];
+    double w_agreed[64][2];
     double w_contra[8][2];
     double psi_depth[16];        /* by drafter position p (clamped to 15)           */
     const double* h;             /* [P] confidence head at each position             */
@@ -705,6 +765,13 @@ typedef struct {
 static double clamp_p(double x) { return x < 1e-6 ? 1e-6 : (x > 1.0 - 1e-6 ? 1.0 - 1e-6 : x); }
 static double logit_p(double x) { x = clamp_p(x); return log(x / (1.0 - x)); }
 
+static int class_of(int l)
+{
+    int e = 0;
+    while (e < 7 && (l >> (e + 1)) > 0) ++e;
+    return e;
+}
+
 static int evidence_class(const int32_t* feat)
 {
     int l = feat[2] > 0 ? feat[2] : feat[0];
@@ -714,7 +781,7 @@ static int evidence_class(const int32_t* feat)
 }
 
 int oracle_tree_build(int P, int Kc, const int32_t* block, int L, const int32_t* ng, const int32_t* ng_len,
-                      const float* w_node_in, const float* w_none_in, int c_max, int depth_max, int rows_cap,
+                      const int32_t* ng_follow, const float* w_node_in, const float* w_none_in, int c_max, int depth_max, int rows_cap,
                       const oracle_tree_score* sc,
                       int32_t* node_token, int32_t* parent_row, double* Q_out, int32_t* n_rows, double* S_curve,
                       int32_t* f_token, int32_t* f_parent, int32_t* f_kind, double* f_Q, uint32_t* flag)
@@ -745,7 +812,9 @@ int oracle_tree_build(int P, int Kc, const int32_t* block, int L, const int32_t*
             for (int c = 1; c < cnt; ++c)
                 if (f_parent[c] == cur && f_token[c] == tok) { found = c; break; }
             const int up = above[cur] + ((f_kind[cur] & 3) == 3);   /* n-gram nodes above a child of cur */
-            const int bucket = 4 * e + (up < 3 ? up : 3);
+            const int fc = ng_follow ? ng_follow[s * L + t] : 0;     /* > 0: a follower token */
+            const int base = fc > 0 ? 32 + 4 * class_of(fc) : 4 * e;
+            const int bucket = base + (up < 3 ? up : 3);
             if (found >= 0) {
                 f_kind[found] |= 4;              /* agreed */
                 if ((f_kind[found] & 3) != 3 && bucket > agree_b[found]) agree_b[found] = bucket;
@@ -783,8 +852,8 @@ int oracle_tree_build(int P, int Kc, const int32_t* block, int L, const int32_t*
             int contra = -1;   /* largest evidence among the parent's n-gram proposals of another token */
             for (int c = 1; c < cnt; ++c)
                 if (f_parent[c] == f_parent[j] && (f_kind[c] & 3) == 3 && f_token[c] != f_token[j] &&
-                    nbucket[c] / 4 > contra)
-                    contra = nbucket[c] / 4;
+                    (nbucket[c] % 32) / 4 > contra)
+                    contra = (nbucket[c] % 32) / 4;
             if (contra >= 0) sj += -plus + sc->w_contra[contra][ps];
         }
         wn[j] = exp(sj);

@@ -132,6 +132,89 @@ def test_ngram_edge_cases():
 
 
 # ---------------------------------------------------------------------------
+# n-gram fill's follower fallback (AdaSpark Section 3.3, "N-gram candidates":
+# read on along the earlier passage, or else the most frequent follower of
+# the last three tokens)
+# ---------------------------------------------------------------------------
+
+def test_follower_fallback_hand_examples():
+    # the copy [7, 1, 2, 3] reaches the end of the text; then the last three
+    # tokens 1 2 3 were followed by 9 twice and by 7 once -> 9 (count 2), and
+    # 2 3 9 was followed by 1 twice -> 1 (count 2)
+    x = np.array([[1, 2, 3, 9, 1, 2, 3, 9, 1, 2, 3, 7, 1, 2, 3]], np.int32)
+    d, dl, f, fol = O.ngram_draft(x, np.array([15], np.int32), 3, 15, 6, 256, follow_ctx=3)
+    assert dl[0] == 6 and list(d[0]) == [7, 1, 2, 3, 9, 1] and list(fol[0]) == [0, 0, 0, 0, 2, 2]
+    assert tuple(f[0]) == (3, 0, 0, 10)                    # the copy's own features are unchanged
+    d0, dl0, f0 = O.ngram_draft(x, np.array([15], np.int32), 3, 15, 6, 256)   # fallback off
+    assert dl0[0] == 4 and list(d0[0, :4]) == [7, 1, 2, 3]
+    # no copy (n_min 4): 5 6 7 was followed by 1 and by 2 once each -> the
+    # latest, 2; then 6 7 2 -> 5, 7 2 5 -> 6, 2 5 6 -> 7, and round again
+    x = np.array([[5, 6, 7, 1, 5, 6, 7, 2, 5, 6, 7]], np.int32)
+    d, dl, f, fol = O.ngram_draft(x, np.array([11], np.int32), 4, 15, 6, 256, follow_ctx=3)
+    assert list(d[0]) == [2, 5, 6, 7, 2, 5] and list(fol[0]) == [1] * 6 and tuple(f[0]) == (0, 0, 0, -1)
+    # a context never seen before has no follower
+    x = np.array([[1, 2, 3, 4, 5]], np.int32)
+    d, dl, f, fol = O.ngram_draft(x, np.array([5], np.int32), 3, 15, 6, 256, follow_ctx=3)
+    assert dl[0] == 0 and np.all(d[0] == -1) and np.all(fol[0] == 0)
+    # texts shorter than the context
+    assert O.ngram_draft(x, np.array([2], np.int32), 3, 15, 6, 256, follow_ctx=3)[1][0] == 0
+
+
+def test_follower_fallback_distinct_follower_limit():
+    """A context with 1,024 distinct followers still proposes (all seen once:
+    the latest wins); with 1,025 the chain ends."""
+    for k, want in ((1024, 1), (1025, 0)):
+        x = np.concatenate([np.array([0, 0, 0, 5000 + i], np.int32) for i in range(k)] + [np.zeros(3, np.int32)])
+        d, dl, f, fol = O.ngram_draft(x[None, :], np.array([len(x)], np.int32), 5, 15, 1, 256, follow_ctx=3)
+        assert dl[0] == want
+        if want:
+            assert d[0, 0] == 5000 + k - 1 and fol[0, 0] == 1
+
+
+def brute_follow(x, L, F, primary):
+    """The fallback written with Counter over str.find occurrences."""
+    from collections import Counter
+    T = len(x)
+    s = "".join(chr(65 + int(t)) for t in x)
+    chain = list(primary)
+    fol = [0] * len(chain)
+    while len(chain) < L and T + len(chain) >= F:
+        ctx = (list(x) + chain)[-F:]
+        pat = "".join(chr(65 + int(t)) for t in ctx)
+        ends = _occ_ends(s, pat, T - 1)
+        if not ends:
+            break
+        cnt = Counter(int(x[j + 1]) for j in ends)
+        if len(cnt) > 1024:
+            break
+        last = {int(x[j + 1]): j for j in ends}
+        tok = max(cnt, key=lambda t: (cnt[t], last[t]))
+        chain.append(tok)
+        fol.append(cnt[tok])
+    return chain, fol
+
+
+@pytest.mark.parametrize("V", [2, 3, 5])
+def test_follower_fallback_bruteforce_tiny_alphabets(V):
+    rng = np.random.Generator(np.random.Philox(40 + V))
+    used = 0
+    for trial in range(300):
+        T = int(rng.integers(1, 50))
+        x = rng.integers(0, V, T).astype(np.int32)
+        n_min = int(rng.integers(1, 7))
+        L = int(rng.integers(1, 16))
+        F = int(rng.integers(1, 5))
+        d, dl, f, fol = O.ngram_draft(x[None, :], np.array([T], np.int32), n_min, 15, L, 256, follow_ctx=F)
+        bd, _, _ = brute_ngram(list(x), n_min, 15, L, 256)
+        chain, bfol = brute_follow(x, L, F, bd)
+        assert int(dl[0]) == len(chain), (list(x), n_min, L, F)
+        assert list(d[0, :dl[0]]) == chain and list(fol[0, :dl[0]]) == bfol
+        assert np.all(d[0, dl[0]:] == -1) and np.all(fol[0, dl[0]:] == 0)
+        used += len(chain) > len(bd)
+    assert used > 50
+
+
+# ---------------------------------------------------------------------------
 # allocation
 # ---------------------------------------------------------------------------
 

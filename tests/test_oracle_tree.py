@@ -149,7 +149,7 @@ def test_tree_walk_is_greedy_decode_of_markov_target():
 def prior(**over):
     """The empty-store prior: pick ln 2 + logit h, sibling log r, every other
     coefficient and bucket weight 0."""
-    coef = dict(a=[np.log(2.0), 1.0, 0.0, 0.0, 1.0, 0.0, 0.0], w_bucket=np.zeros(32), w_agreed=np.zeros((32, 2)),
+    coef = dict(a=[np.log(2.0), 1.0, 0.0, 0.0, 1.0, 0.0, 0.0], w_bucket=np.zeros(64), w_agreed=np.zeros((64, 2)),
                 w_contra=np.zeros((8, 2)), psi_depth=np.zeros(16))
     coef.update(over)
     return coef
@@ -182,7 +182,7 @@ def test_ngram_node_prior_and_bucket():
     block = np.array([[10]], np.int32)
     ng = np.array([[20, 21, -1], [-1, -1, -1]], np.int32)        # anchor chain: 20 (not the pick), 21
     feat = np.array([[7, 1, 0, 100], [0, 0, 0, -1]], np.int32)
-    wb = np.arange(32) * 0.01
+    wb = np.arange(64) * 0.01
     wb[9] = 0.5
     t = O.tree_build(block, ng, np.array([2, 0], np.int32), rows_cap=8, c_max=16,
                      scores=scores(prior(w_bucket=wb), 1, 1, h=np.array([0.6]), p_src=0.8, feat=feat))
@@ -197,6 +197,40 @@ def test_ngram_node_prior_and_bucket():
     assert fQ[n2] == pytest.approx(fQ[n1] * odds2 / (1 + odds2), rel=1e-12)
 
 
+def test_follower_node_bucket_and_agreement():
+    """Tokens of the follower fallback are n-gram nodes of their own kind: a
+    follower seen 5 times (evidence class 2) directly under the anchor has
+    bucket 32 + 4 * 2 + 0 = 40, the follower after it (seen once, class 0,
+    one n-gram node above) bucket 32 + 0 + 1 = 33; a follower token that
+    agrees with the pick adds the agreed weight of its own bucket."""
+    block = np.array([[10]], np.int32)
+    ng = np.array([[20, 21, -1], [-1, -1, -1]], np.int32)
+    fol = np.array([[5, 1, 0], [0, 0, 0]], np.int32)
+    feat = np.array([[0, 0, 0, -1], [0, 0, 0, -1]], np.int32)   # no copy: the chain is all followers
+    wb = np.zeros(64)
+    wb[40], wb[33], wb[8] = 0.5, -0.25, 3.0                     # 8: the copy bucket a wrong kind would take
+    t = O.tree_build(block, ng, np.array([2, 0], np.int32), rows_cap=8, c_max=16, ng_follow=fol,
+                     scores=scores(prior(w_bucket=wb), 1, 1, h=np.array([0.6]), p_src=0.8, feat=feat))
+    ft, fp, fQ = t["f_token"], t["f_parent"], t["f_Q"]
+    n1, n2 = 2, 3
+    assert ft[n1] == 20 and ft[n2] == 21 and fp[n2] == n1
+    odds1 = 0.8 / 0.2 * np.exp(0.5)
+    odds_pick = 2 * 0.6 / 0.4 * np.exp(-np.log(4.0))   # contradicted by the follower (its class 2)
+    assert fQ[n1] == pytest.approx(odds1 / (1 + odds1 + odds_pick), rel=1e-12)
+    odds2 = 0.8 / 0.2 * np.exp(-0.25)
+    assert fQ[n2] == pytest.approx(fQ[n1] * odds2 / (1 + odds2), rel=1e-12)
+    # agreement: the follower proposes the pick's own token
+    ng2 = np.array([[10, -1, -1], [-1, -1, -1]], np.int32)
+    fol2 = np.array([[9, 0, 0], [0, 0, 0]], np.int32)           # class 3: bucket 32 + 12 + 0 = 44
+    wa = np.zeros((64, 2))
+    wa[44, 0], wa[12, 0] = 0.375, 5.0
+    t2 = O.tree_build(block, ng2, np.array([1, 0], np.int32), rows_cap=8, c_max=16, ng_follow=fol2,
+                      scores=scores(prior(w_agreed=wa), 1, 1, h=np.array([0.6]), p_src=0.8, feat=feat))
+    assert t2["count"] == 2 and (t2["f_kind"][1] & 4)
+    odds = 2 * 0.6 / 0.4 * np.exp(np.log(4.0) + 0.375)
+    assert t2["f_Q"][1] == pytest.approx(odds / (1 + odds), rel=1e-12)
+
+
 def test_agreed_and_weak_sources():
     """An agreed pick adds max(0, logit p_src) plus its agreed-bucket weight;
     a source below 1/2 neither lifts the tokens it agrees with nor sinks the
@@ -204,7 +238,7 @@ def test_agreed_and_weak_sources():
     block = np.array([[10], [11]], np.int32)
     ng = np.array([[10, 11], [-1, -1], [-1, -1]], np.int32)      # the anchor chain agrees with both picks
     feat = np.array([[40, 1, 0, 5], [0, 0, 0, -1], [0, 0, 0, -1]], np.int32)   # evidence class 5
-    wa = np.zeros((32, 2))
+    wa = np.zeros((64, 2))
     wa[20, 0], wa[21, 0] = 0.25, 0.125        # buckets 4 * 5 + 0 (position 1) and + 0 (position 2: no n-gram above)
     h = np.array([0.6, 0.7])
     for p_src, lift in ((0.9, np.log(9.0)), (0.3, 0.0)):
@@ -227,7 +261,7 @@ def test_s_curve_is_the_best_tree_of_every_width():
     for trial in range(40):
         P, Kc, L = int(rng.integers(1, 4)), int(rng.integers(1, 3)), int(rng.integers(1, 3))
         block, ng, ngl, _, _ = random_forest_inputs(rng, P, Kc, L)
-        coef = prior(a=rng.normal(0, 1, 7), w_bucket=rng.normal(0, 1, 32), w_agreed=rng.normal(0, 1, (32, 2)),
+        coef = prior(a=rng.normal(0, 1, 7), w_bucket=rng.normal(0, 1, 64), w_agreed=rng.normal(0, 1, (64, 2)),
                      w_contra=rng.normal(0, 1, (8, 2)), psi_depth=rng.normal(0, 0.5, 16))
         feat = np.zeros((P + 1, 4), np.int32)
         feat[:, 0] = rng.integers(1, 20, P + 1)

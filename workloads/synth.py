@@ -367,12 +367,16 @@ def tree_score_inputs(BS, P, Kc, config=3, prior_only=False):
     b_req = rng.normal(0, 0.2, BS).astype(np.float32)
     p_src = rng.uniform(0.3, 0.9, BS).astype(np.float32)
     a = np.array([np.log(2.0), 1.0, 0.0, 0.0, 1.0, 0.0, 0.0])
-    coef = dict(a=a, w_bucket=np.zeros(32), w_agreed=np.zeros((32, 2)), w_contra=np.zeros((8, 2)),
+    coef = dict(a=a, w_bucket=np.zeros(64), w_agreed=np.zeros((64, 2)), w_contra=np.zeros((8, 2)),
                 psi_depth=np.zeros(16))
     if not prior_only:
         coef = dict(a=a + rng.normal(0, 0.3, 7), w_bucket=rng.normal(0, 0.3, 32),
                     w_agreed=rng.normal(0, 0.3, (32, 2)), w_contra=rng.normal(0, 0.3, (8, 2)),
                     psi_depth=rng.normal(0, 0.1, 16))
+        # buckets 32..63: tokens of the follower fallback (drawn last, so the
+        # copy buckets keep their values)
+        coef["w_bucket"] = np.concatenate([coef["w_bucket"], rng.normal(0, 0.3, 32)])
+        coef["w_agreed"] = np.concatenate([coef["w_agreed"], rng.normal(0, 0.3, (32, 2))])
     return dict(coef=coef, h=h, sigma=sigma, r_share=r, psi_ctx=psi_ctx, b_req=b_req, p_src=p_src)
 
 
