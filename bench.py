@@ -358,13 +358,16 @@ def tree_step(K, W, hip, eager_only):
                  b_req=g(f["b_req"]), p_src=g(f["p_src"]))
 
     def build():
-        d, dl, ft = S.spec_ngram_draft(ctx, ctx_len, c["n_min"], c["n_max"], c["L"], c["copy_cap"], query_req=qr_d,
-                                       extra=ex_d, extra_len=el_d, out=bufs.get("ng"))
+        # the tree's n-gram fill: copies, then the follower fallback on the
+        # last three tokens
+        d, dl, ft, fol = S.spec_ngram_draft(ctx, ctx_len, c["n_min"], c["n_max"], c["L"], c["copy_cap"],
+                                            query_req=qr_d, extra=ex_d, extra_len=el_d, out=bufs.get("ng"),
+                                            follow_ctx=3)
         sc = dict(feats, ngram_feat=ft)
-        t = S.spec_allocate_budget(mode="tree", block=block, ngram_draft=d, ngram_len=dl, scores=sc,
+        t = S.spec_allocate_budget(mode="tree", block=block, ngram_draft=d, ngram_len=dl, ngram_follow=fol, scores=sc,
                                    c_max=c["c_max"], depth_max=c["depth_max"], rows_cap=R, s_curve=True,
                                    out=bufs.get("tr"))
-        bufs.setdefault("ng", (d, dl, ft))
+        bufs.setdefault("ng", (d, dl, ft, fol))
         bufs.setdefault("tr", t)
         return t
 
@@ -392,7 +395,8 @@ def tree_step(K, W, hip, eager_only):
     tm = run_timed(step, outputs, K, W, hip, stream, eager_only)
     rows_bytes = int(bufs["tr"]["n_rows"].sum().item()) * V * 4
     step_bytes = rows_bytes + int(c["ctx_len"].sum()) * 4
-    return {"workload": "tree: n-gram chains from the anchor and 8 picks (n 3..15) -> tree build with Eq. (6) "
+    return {"workload": "tree: n-gram chains from the anchor and 8 picks (n 3..15, follower fallback on the last "
+                        "3 tokens) -> tree build with Eq. (6) "
                         "scores and S(n) -> greedy verification of up to 16 rows -> commit; BS=64, V=151936, "
                         "fp32 rows, 4096-token contexts, drafter block 8 x 4",
             "timing": tm["mode"], "steps_per_s": tm["steps_per_s"], "ms_per_step": tm["ms_per_step"],

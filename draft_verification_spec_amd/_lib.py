@@ -35,8 +35,9 @@ MAX_DRAFT, MAX_CAP, MAX_ROWS, MAX_FOREST, MAX_VOCAB = 32, 1024, 64, 1024, 838860
 class NgramArgs(C.Structure):
     _fields_ = [("bs", i32), ("nq", i32), ("ctx", vp), ("ctx_stride", i64), ("ctx_len", vp),
                 ("query_req", vp), ("extra", vp), ("extra_stride", i64), ("extra_len", vp),
-                ("n_min", i32), ("n_max", i32), ("max_draft", i32), ("copy_cap", i32),
-                ("draft", vp), ("draft_len", vp), ("feat", vp), ("workspace", vp), ("workspace_bytes", sz)]
+                ("n_min", i32), ("n_max", i32), ("max_draft", i32), ("copy_cap", i32), ("follow_ctx", i32),
+                ("draft", vp), ("draft_len", vp), ("feat", vp), ("draft_follow", vp), ("workspace", vp),
+                ("workspace_bytes", sz)]
 
 
 class Estimator(C.Structure):
@@ -54,14 +55,15 @@ class ChainAlloc(C.Structure):
 
 
 class TreeScores(C.Structure):
-    _fields_ = [("a", C.c_double * 7), ("w_bucket", C.c_double * 32), ("w_agreed", (C.c_double * 2) * 32),
+    _fields_ = [("a", C.c_double * 7), ("w_bucket", C.c_double * 64), ("w_agreed", (C.c_double * 2) * 64),
                 ("w_contra", (C.c_double * 2) * 8), ("psi_depth", C.c_double * 16), ("h", vp), ("sigma", vp),
                 ("r_share", vp), ("psi_ctx", vp), ("b_req", vp), ("p_src", vp), ("ngram_feat", vp)]
 
 
 class TreeAlloc(C.Structure):
     _fields_ = [("bs", i32), ("P", i32), ("Kc", i32), ("block", vp), ("ngram_draft", vp), ("ngram_ld", i32),
-                ("ngram_len", vp), ("w_node", vp), ("w_none", vp), ("scores", vp), ("c_max", i32),
+                ("ngram_len", vp), ("ngram_follow", vp), ("w_node", vp), ("w_none", vp), ("scores", vp),
+                ("c_max", i32),
                 ("depth_max", i32), ("rows_cap", i32), ("node_token", vp), ("parent_row", vp), ("Q", vp),
                 ("n_rows", vp), ("row_base", vp), ("total_rows", vp), ("forest_count", vp), ("s_curve", vp),
                 ("out_flags", vp)]
@@ -237,8 +239,9 @@ def spec_size_budget(survival, n_requests, c0, p, b_max=0, graph_limit=0, n_toke
 
 
 def spec_ngram_draft(ctx, ctx_len, n_min, n_max, max_draft=15, copy_cap=256, query_req=None, extra=None,
-                     extra_len=None, out=None, workspace=None, stream=None):
-    """N-gram drafts for every query; returns (draft [nq, max_draft], draft_len [nq], feat [nq, 4])."""
+                     extra_len=None, out=None, workspace=None, stream=None, follow_ctx=0):
+    """N-gram drafts for every query; returns (draft [nq, max_draft], draft_len [nq], feat [nq, 4]), and with
+    follow_ctx > 0 (the follower fallback) also the follower counts [nq, max_draft]."""
     _dev(ctx, torch.int32, "ctx", 2)
     _dev(ctx_len, torch.int32, "ctx_len", 1)
     dev = ctx.device
@@ -252,17 +255,20 @@ def spec_ngram_draft(ctx, ctx_len, n_min, n_max, max_draft=15, copy_cap=256, que
         out = (torch.empty((nq, max_draft), dtype=torch.int32, device=dev),
                torch.empty(nq, dtype=torch.int32, device=dev),
                torch.empty((nq, 4), dtype=torch.int32, device=dev))
-    draft, dlen, feat = out
+        if follow_ctx > 0:
+            out += (torch.empty((nq, max_draft), dtype=torch.int32, device=dev),)
+    draft, dlen, feat = out[:3]
+    fol = out[3] if len(out) > 3 else None
     a = NgramArgs(bs=ctx.shape[0], nq=nq, ctx=_ptr(ctx), ctx_stride=ctx.shape[1], ctx_len=_ptr(ctx_len),
                   query_req=_ptr(query_req), extra=_ptr(extra),
                   extra_stride=0 if extra is None else extra.shape[1], extra_len=_ptr(extra_len),
-                  n_min=n_min, n_max=n_max, max_draft=max_draft, copy_cap=copy_cap,
-                  draft=_ptr(draft), draft_len=_ptr(dlen), feat=_ptr(feat))
+                  n_min=n_min, n_max=n_max, max_draft=max_draft, copy_cap=copy_cap, follow_ctx=follow_ctx,
+                  draft=_ptr(draft), draft_len=_ptr(dlen), feat=_ptr(feat), draft_follow=_ptr(fol))
     ws, w = _workspace(OP_NGRAM, a, dev, workspace)
     if w:
         a.workspace, a.workspace_bytes = w
     _check(lib().spec_ngram_draft(C.byref(a), _stream(dev, stream)))
-    return draft, dlen, feat
+    return (draft, dlen, feat, fol) if fol is not None else (draft, dlen, feat)
 
 
 def _chain_alloc(model_tokens, model_conf, ngram_draft, ngram_len, ngram_feat, est, lam, budget,
@@ -302,8 +308,8 @@ def _chain_alloc(model_tokens, model_conf, ngram_draft, ngram_len, ngram_feat, e
 
 
 def tree_scores_struct(coef, h, sigma, r_share, psi_ctx, b_req, p_src, ngram_feat):
-    """spec_tree_scores: coefficient tables from ``coef`` (a [7], w_bucket [32],
-    w_agreed [32, 2], w_contra [8, 2], psi_depth [16]) and device feature tensors."""
+    """spec_tree_scores: coefficient tables from ``coef`` (a [7], w_bucket [64],
+    w_agreed [64, 2], w_contra [8, 2], psi_depth [16]) and device feature tensors."""
     for t, name in ((h, "h"), (sigma, "sigma"), (r_share, "r_share"), (psi_ctx, "psi_ctx"), (b_req, "b_req"),
                     (p_src, "p_src")):
         _dev(t, torch.float32, name)
@@ -311,7 +317,7 @@ def tree_scores_struct(coef, h, sigma, r_share, psi_ctx, b_req, p_src, ngram_fea
     st = TreeScores()
     st.a[:] = [float(x) for x in coef["a"]]
     st.w_bucket[:] = [float(x) for x in coef["w_bucket"]]
-    for i in range(32):
+    for i in range(64):
         st.w_agreed[i][:] = [float(x) for x in coef["w_agreed"][i]]
     for i in range(8):
         st.w_contra[i][:] = [float(x) for x in coef["w_contra"][i]]
@@ -322,13 +328,19 @@ def tree_scores_struct(coef, h, sigma, r_share, psi_ctx, b_req, p_src, ngram_fea
 
 
 def _tree_alloc(block, ngram_draft, ngram_len, w_node=None, w_none=None, depth_max=32, rows_cap=16, out=None,
-                stream=None, scores=None, c_max=None, s_curve=False):
+                stream=None, scores=None, c_max=None, s_curve=False, ngram_follow=None):
     """Tree build; weights w_node / w_none by candidate index, or ``scores``
     (the keyword arguments of tree_scores_struct) for the Eq. (6) form.  With
-    ``s_curve`` the S(n) curve [bs, rows_cap] is returned as out["s_curve"]."""
+    ``s_curve`` the S(n) curve [bs, rows_cap] is returned as out["s_curve"].
+    ``ngram_follow``: the chains' follower counts (spec_ngram_draft with
+    follow_ctx), or None when every chain token is copied."""
     _dev(block, torch.int32, "block", 3)
     _dev(ngram_draft, torch.int32, "ngram_draft", 2)
     _dev(ngram_len, torch.int32, "ngram_len", 1)
+    if ngram_follow is not None:
+        _dev(ngram_follow, torch.int32, "ngram_follow", 2)
+        if tuple(ngram_follow.shape) != tuple(ngram_draft.shape):
+            raise ValueError("ngram_follow must have ngram_draft's shape")
     if scores is None:
         _dev(w_node, torch.float32, "w_node", 2)
         _dev(w_none, torch.float32, "w_none", 2)
@@ -350,7 +362,8 @@ def _tree_alloc(block, ngram_draft, ngram_len, w_node=None, w_none=None, depth_m
             out["s_curve"] = torch.empty((bs, rows_cap), dtype=torch.float32, device=dev)
     st = None if scores is None else tree_scores_struct(**scores)
     ta = TreeAlloc(bs=bs, P=P, Kc=Kc, block=_ptr(block), ngram_draft=_ptr(ngram_draft),
-                   ngram_ld=ngram_draft.shape[1], ngram_len=_ptr(ngram_len), w_node=_ptr(w_node),
+                   ngram_ld=ngram_draft.shape[1], ngram_len=_ptr(ngram_len), ngram_follow=_ptr(ngram_follow),
+                   w_node=_ptr(w_node),
                    w_none=_ptr(w_none), scores=None if st is None else C.cast(C.pointer(st), vp),
                    c_max=int(c_max), depth_max=depth_max, rows_cap=rows_cap,
                    **{k: _ptr(v) for k, v in out.items()})

@@ -41,6 +41,7 @@ static int check_ngram(const spec_ngram_args* a)
     REQUIRE(a->max_draft >= 1 && a->max_draft <= SPEC_MAX_DRAFT);
     REQUIRE(a->copy_cap >= a->n_min && a->copy_cap <= SPEC_MAX_CAP);
     REQUIRE(a->nq == 0 || (a->draft && a->draft_len && a->feat));
+    REQUIRE(a->follow_ctx >= 0 && a->follow_ctx <= SPEC_MAX_FOLLOW_CTX);
     return SPEC_OK;
 }
 

@@ -370,6 +370,9 @@ struct TreeBuildParams {
 __device__ __forceinline__ double clamp_prob(double x) { return x < 1e-6 ? 1e-6 : (x > 1.0 - 1e-6 ? 1.0 - 1e-6 : x); }
 __device__ __forceinline__ double logit_prob(double x) { x = clamp_prob(x); return log(x / (1.0 - x)); }
 
+// Evidence class of a follower count l >= 1: floor(log2 l), at most 7.
+__device__ __forceinline__ int follower_class(int l) { return l <= 1 ? 0 : min(7, 31 - __clz(l)); }
+
 // Evidence class of an n-gram chain: floor(log2) of its source's match
 // length (feature m, else n), at most 7.
 __device__ __forceinline__ int evidence_of(const int32_t* feat)
@@ -421,6 +424,7 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
     // trip (the tokens when they fit)
     constexpr int kChainLds = 2048;
     __shared__ int32_t ctok[kChainLds];
+    __shared__ int32_t cfol[kChainLds];   // follower counts (0: a copied token)
     __shared__ int32_t clen[SPEC_MAX_FOREST];
     __shared__ int8_t cev[SPEC_MAX_FOREST];
     const int P_ = A.P, Kc = A.Kc, cmax = A.c_max;
@@ -432,7 +436,10 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
         cev[i] = (int8_t)(P.scored ? evidence_of(P.sc.ngram_feat + 4 * (q0 + i)) : 0);
     }
     if (staged)
-        for (int i = lane; i < (P_ + 1) * A.ngram_ld; i += kWave) ctok[i] = A.ngram_draft[q0 * A.ngram_ld + i];
+        for (int i = lane; i < (P_ + 1) * A.ngram_ld; i += kWave) {
+            ctok[i] = A.ngram_draft[q0 * A.ngram_ld + i];
+            cfol[i] = A.ngram_follow ? A.ngram_follow[q0 * A.ngram_ld + i] : 0;
+        }
     // the drafter nodes: parent, token, depth, kind; n-gram nodes above,
     // bucket, agreeing bucket.  Slots past the node count hold parent -2.
     int rpar[NS], rtok[NS], rdep[NS], rkind[NS], rabove[NS], rbucket[NS], ragree[NS];
@@ -470,6 +477,11 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
         if (glen == 0) continue;   // nothing to walk or add
         const int ev = lane_chains ? __builtin_amdgcn_readlane(lev, sc) : (int)cev[sc];
         const int32_t* src = staged ? ctok + (int64_t)sc * A.ngram_ld : A.ngram_draft + q * A.ngram_ld;
+        const int32_t* fsrc = staged ? cfol + (int64_t)sc * A.ngram_ld
+                                     : (A.ngram_follow ? A.ngram_follow + q * A.ngram_ld : nullptr);
+        // a token's bucket base: 4 x the copy's evidence class, or 32 + 4 x the
+        // class of its follower count
+        auto base_of = [&](int32_t fc) { return fc > 0 ? 32 + 4 * follower_class(fc) : 4 * ev; };
         int cur = (sc == 0) ? 0 : 1 + (sc - 1) * Kc;   // a drafter node (< nd <= 1024)
         int cdep = 0, ckind = 0, cabove = 0;
         auto read_cur = [&]() {   // cur's depth, kind and n-gram count, from its lane
@@ -482,7 +494,8 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
                 }
         };
         read_cur();
-        int ctk = lane < glen ? src[lane] : -1;   // the chain's first 64 tokens
+        int ctk = lane < glen ? src[lane] : -1;   // the chain's first 64 tokens and their bucket bases
+        int cfb = base_of(lane < glen && fsrc ? fsrc[lane] : 0);
         int t = 0;
         bool tail = false;
         if (glen <= kWave) {
@@ -531,13 +544,15 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
                 cur = nxt;
                 ++t;
             }
-            // every node passed records the agreement: its bucket counts the
-            // n-gram nodes above it, which is its own n-gram count
+            // every node passed records the agreement: the proposal's bucket
+            // counts the n-gram nodes above the node, its own n-gram count
             if (t > 0) {
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
+                    const int tn = rdep[s] - d0 - 1;   // the chain token that passed this node
+                    const int tb = __shfl(cfb, tn & 63, kWave);
                     if ((pm[s] >> lane) & 1ull) {
-                        const int b = 4 * ev + (rabove[s] < 3 ? rabove[s] : 3);
+                        const int b = tb + (rabove[s] < 3 ? rabove[s] : 3);
                         if ((rkind[s] & 3) != 3 && b > ragree[s]) ragree[s] = b;
                         rkind[s] |= 4;
                     }
@@ -549,10 +564,13 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
             // chains longer than a wave: one token per step
             for (; t < glen; ++t) {
                 if (cdep + 1 > A.depth_max) break;
-                if (t && (t & 63) == 0) ctk = t + lane < glen ? src[t + lane] : -1;   // the next 64
+                if (t && (t & 63) == 0) {   // the next 64
+                    ctk = t + lane < glen ? src[t + lane] : -1;
+                    cfb = base_of(t + lane < glen && fsrc ? fsrc[t + lane] : 0);
+                }
                 const int tk = __builtin_amdgcn_readlane(ctk, t & 63);
                 const int up = cabove + ((ckind & 3) == 3);   // n-gram nodes above a child of cur
-                const int bucket = 4 * ev + (up < 3 ? up : 3);
+                const int bucket = __builtin_amdgcn_readlane(cfb, t & 63) + (up < 3 ? up : 3);
                 int found = -1, fk = 0, fd = 0, fa = 0;
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
@@ -600,7 +618,7 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
                     rdep[s] = cdep + 1 + i;
                     rkind[s] = 3;
                     rabove[s] = ui < 127 ? ui : 127;
-                    rbucket[s] = 4 * ev + (ui < 3 ? ui : 3);
+                    rbucket[s] = base_of(fsrc ? fsrc[t + i] : 0) + (ui < 3 ? ui : 3);
                     ragree[s] = -1;
                 }
             }
@@ -654,8 +672,8 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
                 if (fagree[j] >= 0) sj += plus + S.w_agreed[fagree[j]][ps];
                 int contra = -1;
                 for (int c = nd; c < cnt; ++c)   // n-gram nodes come after the drafter's
-                    if (fpar[c] == fpar[j] && (fkind[c] & 3) == 3 && ftok[c] != ftok[j] && fbucket[c] / 4 > contra)
-                        contra = fbucket[c] / 4;
+                    if (fpar[c] == fpar[j] && (fkind[c] & 3) == 3 && ftok[c] != ftok[j] && (fbucket[c] & 31) / 4 > contra)
+                        contra = (fbucket[c] & 31) / 4;   // the evidence class, of either kind
                 if (contra >= 0) sj += -plus + S.w_contra[contra][ps];
             }
             fw[j] = exp(sj);

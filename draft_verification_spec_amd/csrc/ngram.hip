@@ -10,8 +10,8 @@ struct NgramParams {
     const int32_t* ctx; int64_t ctx_stride; const int32_t* ctx_len;
     const int32_t* query_req;
     const int32_t* extra; int64_t extra_stride; const int32_t* extra_len;
-    int32_t n_min, n_max, max_draft, cap;
-    int32_t* draft; int32_t* draft_len; int32_t* feat;
+    int32_t n_min, n_max, max_draft, cap, follow_ctx;
+    int32_t* draft; int32_t* draft_len; int32_t* feat; int32_t* follow;
 };
 
 __device__ __forceinline__ Text query_text(const NgramParams& P, int q)
@@ -41,7 +41,8 @@ __device__ __forceinline__ Text query_text(const NgramParams& P, int q)
 // NT threads and NB positions per thread per batch: the host picks the
 // smallest window (NT * NB tokens) that holds the longest text, so a text
 // takes one batch and the workgroup no more LDS than it needs.
-template <bool PLAIN, int NT, int NB>
+// FOLLOW: with the follower fallback (its LDS only in these instances).
+template <bool PLAIN, bool FOLLOW, int NT, int NB>
 __global__ __launch_bounds__(NT) void k_ngram(NgramParams P)
 {
     const int q = blockIdx.x;
@@ -63,18 +64,27 @@ __global__ __launch_bounds__(NT) void k_ngram(NgramParams P)
     O.draft = P.draft + (int64_t)q * P.max_draft;
     O.draft_len = P.draft_len + q;
     O.feat = P.feat + 4 * (int64_t)q;
-    ngram_scan<NT, NB>(x, win, S, O, v, PLAIN);
+    if constexpr (FOLLOW) {
+        __shared__ FollowShared FS;
+        O.follow_ctx = P.follow_ctx;
+        O.follow = P.follow ? P.follow + (int64_t)q * P.max_draft : nullptr;
+        ngram_scan<NT, NB>(x, win, S, O, v, PLAIN, &FS);
+    } else {
+        O.follow_ctx = 0;
+        O.follow = nullptr;
+        ngram_scan<NT, NB>(x, win, S, O, v, PLAIN);
+    }
 }
 
-template <bool PLAIN>
+template <bool PLAIN, bool FOLLOW>
 static void launch_ngram(const NgramParams& P, int64_t text_max, hipStream_t st)
 {
     if (text_max <= 512 * 16)
-        hipLaunchKernelGGL((k_ngram<PLAIN, 512, 16>), dim3(P.nq), dim3(512), 0, st, P);
+        hipLaunchKernelGGL((k_ngram<PLAIN, FOLLOW, 512, 16>), dim3(P.nq), dim3(512), 0, st, P);
     else if (text_max <= 1024 * 16)
-        hipLaunchKernelGGL((k_ngram<PLAIN, 1024, 16>), dim3(P.nq), dim3(1024), 0, st, P);
+        hipLaunchKernelGGL((k_ngram<PLAIN, FOLLOW, 1024, 16>), dim3(P.nq), dim3(1024), 0, st, P);
     else
-        hipLaunchKernelGGL((k_ngram<PLAIN, 1024, 32>), dim3(P.nq), dim3(1024), 0, st, P);
+        hipLaunchKernelGGL((k_ngram<PLAIN, FOLLOW, 1024, 32>), dim3(P.nq), dim3(1024), 0, st, P);
 }
 
 }  // namespace spec
@@ -91,9 +101,17 @@ int spec_ngram_launch(const spec_ngram_args* a, hipStream_t st)
     P.query_req = a->query_req;
     P.extra = a->extra; P.extra_stride = a->extra ? a->extra_stride : 0; P.extra_len = a->extra_len;
     P.n_min = a->n_min; P.n_max = a->n_max; P.max_draft = a->max_draft; P.cap = a->copy_cap;
+    P.follow_ctx = a->follow_ctx;
     P.draft = a->draft; P.draft_len = a->draft_len; P.feat = a->feat;
+    P.follow = a->follow_ctx > 0 ? a->draft_follow : nullptr;
     const int64_t text_max = a->ctx_stride + (a->extra ? a->extra_stride : 0);
-    if (!a->query_req && !a->extra && a->nq == a->bs && a->ctx_stride >= 1) launch_ngram<true>(P, text_max, st);
-    else launch_ngram<false>(P, text_max, st);
+    const bool plain = !a->query_req && !a->extra && a->nq == a->bs && a->ctx_stride >= 1;
+    if (a->follow_ctx > 0) {
+        if (plain) launch_ngram<true, true>(P, text_max, st);
+        else launch_ngram<false, true>(P, text_max, st);
+    } else {
+        if (plain) launch_ngram<true, false>(P, text_max, st);
+        else launch_ngram<false, false>(P, text_max, st);
+    }
     return spec_record_hip_error(hipGetLastError());
 }

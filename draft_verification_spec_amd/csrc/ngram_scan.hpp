@@ -16,7 +16,12 @@
 //   * a match of length l >= n_min becomes the key (l << 32 | j), so "longest,
 //     then latest" is the largest key; the workgroup keeps the top two;
 //   * thread 0 derives (n, a, m, j) and the first lanes copy the draft, from
-//     the window when it holds the continuation.
+//     the window when it holds the continuation;
+//   * with the follower fallback (AdaSpark, Section 3.3, "N-gram candidates"),
+//     each further token after the copy is the most frequent follower of the
+//     last F tokens: every thread tests its positions against the context and
+//     counts the followers in an LDS hash table (token -> count, latest
+//     position), and the largest (count, latest) wins.
 #pragma once
 
 #include "common.hpp"
@@ -56,6 +61,21 @@ struct NgramOut {
     int32_t* draft;      // [max_draft]
     int32_t* draft_len;  // [1]
     int32_t* feat;       // [4]
+    int32_t follow_ctx;  // F > 0: the follower fallback (needs a FollowShared)
+    int32_t* follow;     // [max_draft] follower counts, or null
+};
+
+// LDS of the follower fallback beyond the scan's own (whose suffix and
+// candidate lists hold the hash table's counts and keys).
+constexpr int kFollowers = SPEC_MAX_FOLLOWERS;
+static_assert(kMaxCand * sizeof(int32_t) >= kFollowers * sizeof(uint64_t), "hash keys fit the candidate list");
+static_assert(SPEC_MAX_CAP >= kFollowers, "hash counts fit the suffix");
+struct FollowShared {
+    int32_t last[kFollowers];       // latest position of each follower
+    int32_t dft[SPEC_MAX_DRAFT];    // the draft so far
+    int32_t fol[SPEC_MAX_DRAFT];    // follower counts
+    uint64_t best[16];              // per wave: (count << 32 | latest position)
+    int32_t len, over;
 };
 
 // Scans text x with the whole workgroup (every thread calls it): batches of
@@ -64,8 +84,9 @@ struct NgramOut {
 // text).
 template <int NT, int NB = kBatch>
 __device__ void ngram_scan(const Text& x, int32_t* win, NgramShared<NT>& S, const NgramOut& O, int32_t (&v)[NB],
-                           bool pre)
+                           bool pre, FollowShared* FS = nullptr)
 {
+    static_assert(NT / kWave <= 16, "per-wave slots of FollowShared");
     constexpr int64_t kWin = (int64_t)NT * NB;
     const int t = threadIdx.x;
     const int lane = t % kWave, wid = t / kWave;
@@ -155,14 +176,19 @@ __device__ void ngram_scan(const Text& x, int32_t* win, NgramShared<NT>& S, cons
     best = wave_top2(best);
     if (lane == 0) S.sh[wid] = best;
     __syncthreads();
+    const bool follow = O.follow_ctx > 0 && FS != nullptr;
     if (wid == 0) {
         Top2 tb = lane < NT / kWave ? S.sh[lane] : Top2{0, 0};
         tb = wave_top2(tb);
         int32_t* d = O.draft;
         if (tb.a == 0) {
-            for (int k = lane; k < O.max_draft; k += kWave) d[k] = -1;
+            for (int k = lane; k < O.max_draft; k += kWave) {
+                d[k] = -1;
+                if (follow) FS->dft[k] = -1;
+            }
             if (lane == 0) {
                 *O.draft_len = 0;
+                if (follow) FS->len = 0;
                 O.feat[0] = 0;
                 O.feat[1] = 0;
                 O.feat[2] = 0;
@@ -173,7 +199,11 @@ __device__ void ngram_scan(const Text& x, int32_t* win, NgramShared<NT>& S, cons
             const int64_t j = (int64_t)(tb.a & 0xFFFFFFFFu);
             const int64_t avail = x.n - 1 - j;
             const int64_t len = avail < O.max_draft ? avail : O.max_draft;
-            for (int k = lane; k < O.max_draft; k += kWave) d[k] = (k < len) ? at(j + 1 + k) : -1;
+            for (int k = lane; k < O.max_draft; k += kWave) {
+                const int32_t tk = (k < len) ? at(j + 1 + k) : -1;
+                d[k] = tk;
+                if (follow) FS->dft[k] = tk;
+            }
             if (lane == 0) {
                 int a = 1;
                 if (tb.b != 0) {
@@ -181,6 +211,7 @@ __device__ void ngram_scan(const Text& x, int32_t* win, NgramShared<NT>& S, cons
                     a = at(jr + 1) == at(j + 1);
                 }
                 *O.draft_len = (int32_t)len;
+                if (follow) FS->len = (int32_t)len;
                 O.feat[0] = (int32_t)(l < O.n_max ? l : O.n_max);
                 O.feat[1] = a;
                 O.feat[2] = (l >= O.n_max) ? (int32_t)l : 0;
@@ -188,6 +219,85 @@ __device__ void ngram_scan(const Text& x, int32_t* win, NgramShared<NT>& S, cons
             }
         }
     }
+    if (!follow) return;
+    // follower fallback: one token per round while the draft is short
+    __syncthreads();
+    const int F = O.follow_ctx;
+    uint64_t* hkey = (uint64_t*)S.cand;   // (1 << 32 | token), 0 = empty
+    int32_t* hcnt = S.suf;
+    const int len0 = FS->len;
+    int len = len0;
+    // no copy and F >= n_min: every occurrence of the last F tokens would
+    // have been a match, so there is no follower either
+    const bool none = len0 == 0 && F >= O.n_min;
+    while (!none && len < O.max_draft && x.n + len >= F) {
+        for (int i = t; i < kFollowers; i += NT) {
+            hkey[i] = 0;
+            hcnt[i] = 0;
+            FS->last[i] = -1;
+        }
+        if (t == 0) FS->over = 0;
+        __syncthreads();
+        int32_t c[SPEC_MAX_FOLLOW_CTX];
+#pragma unroll
+        for (int i = 0; i < SPEC_MAX_FOLLOW_CTX; ++i) {
+            const int64_t q = x.n + len - F + i;   // position in text ++ draft
+            c[i] = i < F ? (q < x.n ? at(q) : FS->dft[q - x.n]) : 0;
+        }
+        for (int64_t p = F - 1 + t; p + 1 < x.n; p += NT) {
+            bool m = true;
+            for (int i = 0; i < F && m; ++i) m = at(p - (F - 1) + i) == c[i];
+            if (!m) continue;
+            const int32_t f = at(p + 1);
+            const uint64_t key = (1ull << 32) | (uint32_t)f;
+            uint32_t h = ((uint32_t)f * 2654435761u) >> 22;   // 10 bits: kFollowers slots
+            int probe = 0;
+            for (; probe < kFollowers; ++probe) {
+                const uint64_t old = atomicCAS((unsigned long long*)&hkey[h], 0ull, (unsigned long long)key);
+                if (old == 0 || old == key) {
+                    atomicAdd(&hcnt[h], 1);
+                    atomicMax(&FS->last[h], (int32_t)p);
+                    break;
+                }
+                h = (h + 1) & (kFollowers - 1);
+            }
+            if (probe == kFollowers) FS->over = 1;   // more distinct followers than the table holds
+        }
+        __syncthreads();
+        uint64_t b = 0;
+        for (int i = t; i < kFollowers; i += NT) {
+            const uint64_t e = hcnt[i] > 0 ? ((uint64_t)(uint32_t)hcnt[i] << 32) | (uint32_t)FS->last[i] : 0ull;
+            b = e > b ? e : b;
+        }
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1) {
+            const uint32_t lo = __shfl_xor((uint32_t)b, o, kWave), hi = __shfl_xor((uint32_t)(b >> 32), o, kWave);
+            const uint64_t y = ((uint64_t)hi << 32) | lo;
+            b = y > b ? y : b;
+        }
+        if (lane == 0) FS->best[wid] = b;
+        __syncthreads();
+        if (t == 0) {
+            uint64_t bb = 0;
+            for (int w = 0; w < NT / kWave; ++w) bb = FS->best[w] > bb ? FS->best[w] : bb;
+            if (bb == 0 || FS->over) {
+                FS->over = 1;   // the draft ends here
+            } else {
+                const int64_t plast = (int64_t)(uint32_t)bb;
+                FS->dft[len] = at(plast + 1);
+                FS->fol[len] = (int32_t)(bb >> 32);
+            }
+        }
+        __syncthreads();
+        if (FS->over) break;
+        ++len;
+    }
+    // the fallback's tokens and every count
+    for (int k = t; k < O.max_draft; k += NT) {
+        if (k >= len0 && k < len) O.draft[k] = FS->dft[k];
+        if (O.follow) O.follow[k] = (k >= len0 && k < len) ? FS->fol[k] : 0;
+    }
+    if (t == 0) *O.draft_len = len;
 }
 
 }  // namespace spec

@@ -1942,6 +1942,8 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
         O.draft = P.ng_draft + (int64_t)r * P.ng_ld;
         O.draft_len = P.ng_len + r;
         O.feat = P.ng_feat + 4 * (int64_t)r;
+        O.follow_ctx = 0;   // the chain drafter copies only
+        O.follow = nullptr;
         __syncthreads();
         ngram_scan<kDBlock, kNgBatch>(x, (int32_t*)sp, *(NgramShared<kDBlock>*)sW, O, ngv, true);
     }

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 3
+#define SPEC_ABI_VERSION 4
 
 /* ---- return codes ---------------------------------------------------- */
 #define SPEC_OK          0
@@ -93,6 +93,8 @@ extern "C" {
 /* Limits. */
 #define SPEC_MAX_DRAFT   32   /* n-gram draft length, chain leading dim      */
 #define SPEC_MAX_CAP   1024   /* n-gram comparison cap (copy_cap)            */
+#define SPEC_MAX_FOLLOW_CTX 8 /* follower fallback context (follow_ctx)      */
+#define SPEC_MAX_FOLLOWERS 1024 /* distinct followers a fallback step counts */
 #define SPEC_MAX_ROWS    64   /* tree rows per request                       */
 #define SPEC_MAX_FOREST 1024  /* tree candidates per request                 */
 #define SPEC_MAX_VOCAB  8388608 /* logits per row                            */
@@ -113,6 +115,17 @@ extern "C" {
  * is no runner-up or it is followed by the same token, j = best end position
  * (-1 and zeros when nothing matched).  Integer only; deterministic.
  * Lengths outside [0, stride] are clamped.
+ *
+ * Follower fallback ([AS] Section 3.3, "N-gram candidates": the tree's
+ * n-gram fill reads on along the earlier passage, or else takes the most
+ * frequent follower of its last three tokens), on when follow_ctx = F > 0:
+ * once the copy ends (the passage reaches the end of x, or nothing matched)
+ * each further draft token is the most frequent follower, over x, of the
+ * last F tokens of x ++ the draft so far (occurrences ending at p <= |x|-2,
+ * follower x[p+1]); ties go to the follower seen latest; a context with no
+ * follower or more than SPEC_MAX_FOLLOWERS distinct ones ends the draft.
+ * draft_follow[q][k] = that follower's count (0 for copied tokens and past
+ * the draft).  feat describes the copy only.
  * ======================================================================== */
 typedef struct spec_ngram_args {
     int32_t bs;                  /* requests (rows of ctx)                        */
@@ -128,9 +141,13 @@ typedef struct spec_ngram_args {
     int32_t n_max;               /* >= n_min                                      */
     int32_t max_draft;           /* 1 .. SPEC_MAX_DRAFT                           */
     int32_t copy_cap;            /* n_min .. SPEC_MAX_CAP (256 on the pages)      */
+    int32_t follow_ctx;          /* 0 (no fallback) .. SPEC_MAX_FOLLOW_CTX (3 for
+                                    the tree's n-gram fill on the pages)          */
     int32_t* draft;              /* device [nq, max_draft]                        */
     int32_t* draft_len;          /* device [nq]                                   */
     int32_t* feat;               /* device [nq, 4]                                */
+    int32_t* draft_follow;       /* device [nq, max_draft] or NULL: follower
+                                    counts (follow_ctx > 0)                       */
     void* workspace;             /* device scratch                                */
     size_t workspace_bytes;
 } spec_ngram_args;
@@ -212,15 +229,16 @@ typedef struct spec_chain_alloc {
  * whose parent has an n-gram proposal of another token (contradicted)
  * subtracts max(0, logit p_src) and adds w_contra[that proposal's evidence
  * class][pick 0 / sibling 1]; the largest such bucket or class counts.  An
- * n-gram node's evidence is its source's match length l (feature m, else n),
- * class e = min(7, floor(log2 l)); its bucket is 4 e + min(3, n-gram nodes
- * above it on its path).  Probabilities are clamped to [1e-6, 1 - 1e-6]
+ * n-gram node's evidence is its source's match length l (feature m, else n)
+ * or, for a token of the follower fallback, its follower count l; class
+ * e = min(7, floor(log2 l)); its bucket is 4 e + min(3, n-gram nodes above it
+ * on its path), plus 32 for a follower token.  Probabilities are clamped to [1e-6, 1 - 1e-6]
  * before logit / log; everything in fp64.  With the prior a = (ln 2, 1, 0,
  * 0, 1, 0, 0) and zero weights a pick's estimate is h. */
 typedef struct spec_tree_scores {
     double a[7];
-    double w_bucket[32];
-    double w_agreed[32][2];
+    double w_bucket[64];         /* 0..31 copied tokens, 32..63 followers         */
+    double w_agreed[64][2];
     double w_contra[8][2];
     double psi_depth[16];        /* by position p (p >= 15 uses 15)               */
     const float* h;              /* device [bs, P] confidence head per position   */
@@ -243,6 +261,8 @@ typedef struct spec_tree_alloc {
                                     the anchor, s = i the pick at position i      */
     int32_t ngram_ld;
     const int32_t* ngram_len;    /* device [bs*(P+1)]                             */
+    const int32_t* ngram_follow; /* device [bs*(P+1), ngram_ld] follower counts of
+                                    the chains' tokens (draft_follow), or NULL    */
     const float* w_node;         /* device [bs, c_max] > 0, by candidate index    */
     const float* w_none;         /* device [bs, c_max] > 0, 'none' of a parent    */
     const spec_tree_scores* scores; /* host, or NULL: with it the weights are

@@ -205,3 +205,60 @@ def test_tree_build_eq6_scores_and_s_curve(prior_only):
         n = g["n_rows"][r]
         assert g["s_curve"][r, n - 1] == pytest.approx(g["Q"][r, 1:n].sum(), rel=1e-5)
     print(f"  S(16) mean {g['s_curve'][:, -1].mean():.3f}, excused {np.mean(~ok):.3f}")
+
+
+def test_tree_build_follower_buckets():
+    """Chains whose tokens mix copies and follower-fallback tokens (follower
+    counts 1..300, every evidence class), scored with Eq. (6): the follower
+    buckets 32..63, their agreements and contradictions, on random forests
+    and on the tree workload with its texts ending in a repeated span."""
+    import torch
+    import draft_verification_spec_amd as S
+    rng = np.random.Generator(np.random.Philox(55))
+    BS, P, Kc, L, vocab = 40, 6, 3, 20, 12
+    block = np.stack([np.stack([rng.choice(vocab, Kc, replace=False) for _ in range(P)])
+                      for _ in range(BS)]).astype(np.int32)
+    ngl = rng.integers(0, L + 1, BS * (P + 1)).astype(np.int32)
+    ng = rng.integers(0, vocab, (BS * (P + 1), L)).astype(np.int32)
+    fol = np.where(rng.random((BS * (P + 1), L)) < 0.5, 0, rng.integers(1, 300, (BS * (P + 1), L))).astype(np.int32)
+    feat = np.zeros((BS * (P + 1), 4), np.int32)
+    feat[:, 0] = rng.integers(1, 16, BS * (P + 1))
+    feat[:, 2] = np.where(rng.random(BS * (P + 1)) < 0.5, rng.integers(15, 300, BS * (P + 1)), 0)
+    c_max = 1 + P * Kc + (P + 1) * L
+    f = synth.tree_score_inputs(BS, P, Kc)
+    cases = [("random", block, ng, ngl, fol, feat, f, c_max, 64, 40)]
+    c = synth.config3_inputs()
+    ctx = c["ctx"].copy()
+    for r in range(c["BS"]):
+        T = int(c["ctx_len"][r])
+        span = rng.integers(0, c["V"], 6).astype(np.int32)
+        ctx[r, T - 12:T] = np.concatenate([span, span])
+    qr, ex, el = synth.tree_queries(ctx, c["ctx_len"], c["block"])
+    d3, l3, f3, fol3 = O.ngram_draft(ctx, c["ctx_len"], c["n_min"], c["n_max"], c["L"], 256,
+                                     query_req=qr, extra=ex, extra_len=el, follow_ctx=3)
+    assert (fol3 > 0).any()
+    f3s = synth.tree_score_inputs(c["BS"], c["P"], c["Kc"])
+    cases.append(("tree workload", c["block"], d3, l3, fol3, f3, f3s, c["c_max"], c["depth_max"], c["rows_cap"]))
+    for tag, blk, d, dl, fl, ft, fs, cm, dmax, rows_cap in cases:
+        bs, p_, kc = blk.shape
+        print(f"tree build with followers ({tag}): bs {bs} c_max {cm}", flush=True)
+        per = [dict(coef=fs["coef"], h=fs["h"][r], sigma=fs["sigma"][r], r_share=fs["r_share"][r],
+                    psi_ctx=fs["psi_ctx"][r], b_req=fs["b_req"][r], p_src=fs["p_src"][r],
+                    ng_feat=ft.reshape(bs, p_ + 1, 4)[r]) for r in range(bs)]
+        o = O.tree_build_batch(blk, d, dl, depth_max=dmax, rows_cap=rows_cap, scores=per, c_max=cm, ng_follow=fl)
+        sc = dict(coef=fs["coef"], h=dev(fs["h"]), sigma=dev(fs["sigma"]), r_share=dev(fs["r_share"]),
+                  psi_ctx=dev(fs["psi_ctx"]), b_req=dev(fs["b_req"]), p_src=dev(fs["p_src"]), ngram_feat=dev(ft))
+        g = S.spec_allocate_budget(mode="tree", block=dev(blk), ngram_draft=dev(d), ngram_len=dev(dl),
+                                   ngram_follow=dev(fl), scores=sc, c_max=cm, depth_max=dmax, rows_cap=rows_cap,
+                                   s_curve=True)
+        torch.cuda.synchronize()
+        g = {k: host(v) for k, v in g.items()}
+        ok = ok_rows(o["flags"])
+        assert_rows_equal(g["forest_count"], o["count"], np.ones(bs, bool), "forest_count")
+        for k in ("node_token", "parent_row", "n_rows"):
+            assert_rows_equal(g[k], o[k], ok, f"{k} ({tag})")
+        assert_close(g["Q"], o["Q"], "Q")
+        assert_close(g["s_curve"], o["S_curve"], "S(n)")
+        # the follower weights matter: without the counts the oracle builds other trees
+        o0 = O.tree_build_batch(blk, d, dl, depth_max=dmax, rows_cap=rows_cap, scores=per, c_max=cm)
+        assert not np.allclose(o0["Q"], o["Q"])

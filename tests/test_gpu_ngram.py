@@ -86,3 +86,90 @@ def test_extra_text_long():
     ex = rng.integers(0, 4, (7, 40)).astype(np.int32)
     el = np.array([40, 0, 17, 40, 1, 3, 39], np.int32)
     run_both(ctx, ctx_len, 2, 15, 15, 256, query_req=qr, extra=ex, extra_len=el)
+
+
+# ---------------------------------------------------------------------------
+# the n-gram fill's follower fallback (follow_ctx > 0)
+# ---------------------------------------------------------------------------
+
+def run_follow(ctx, ctx_len, n_min, n_max, L, F, cap=256, query_req=None, extra=None, extra_len=None, tag=""):
+    import torch
+    import draft_verification_spec_amd as S
+    print(f"ngram follow {tag}: ctx {ctx.shape} n {n_min}..{n_max} L {L} F {F} "
+          f"queries {None if query_req is None else len(query_req)}", flush=True)
+    g = S.spec_ngram_draft(dev(ctx), dev(ctx_len), n_min, n_max, L, cap,
+                           query_req=None if query_req is None else dev(query_req),
+                           extra=None if extra is None else dev(extra),
+                           extra_len=None if extra_len is None else dev(extra_len), follow_ctx=F)
+    torch.cuda.synchronize()
+    o = O.ngram_draft(ctx, ctx_len, n_min, n_max, L, cap, query_req=query_req, extra=extra, extra_len=extra_len,
+                      follow_ctx=F)
+    for name, a, b in zip(("draft", "draft_len", "feat", "follow"), g, o):
+        assert np.array_equal(host(a), b), (tag, name, np.argwhere(host(a) != b)[:5])
+    return o
+
+
+def test_follow_random_tiny_alphabets():
+    """Small alphabets and short texts, where copies often reach the end of
+    the text and most contexts have several followers."""
+    rng = np.random.Generator(np.random.Philox(91))
+    extended = 0
+    for V in (2, 3, 5):
+        BS, Tmax = 128, 200
+        ctx = rng.integers(0, V, (BS, Tmax)).astype(np.int32)
+        ctx_len = rng.integers(0, Tmax + 1, BS).astype(np.int32)
+        for F, n_min, L in ((3, 3, 15), (1, 4, 32), (4, 2, 7), (8, 5, 20)):
+            d, dl, f, fol = run_follow(ctx, ctx_len, n_min, 15, L, F, tag=f"V {V}")
+            extended += int((fol > 0).any(axis=1).sum())
+    assert extended > 300
+
+
+def test_follow_window_sizes_and_long_texts():
+    """Texts that take each scan window (up to 8,192, 16,384 and 32,768
+    tokens) and one longer than the largest (read from memory): periodic
+    texts ending in a span written twice, so the copy reaches the end."""
+    rng = np.random.Generator(np.random.Philox(92))
+    for T in (3000, 12000, 30000, 40000):
+        BS = 6
+        ctx = np.zeros((BS, T), np.int32)
+        for r in range(BS):
+            period = int(rng.integers(3, 40))
+            base = rng.integers(0, 50, period)
+            x = np.resize(base, T).astype(np.int32)
+            noise = rng.random(T) < 0.05
+            x[noise] = rng.integers(0, 50, int(noise.sum()))
+            # the text ends with a fresh span twice: the copy stops at the end
+            span = rng.integers(50, 60, int(rng.integers(3, 9))).astype(np.int32)
+            x[T - 2 * len(span):] = np.concatenate([span, span])
+            ctx[r] = x
+        ctx_len = np.full(BS, T, np.int32)
+        ctx_len[-1] = T - 7
+        d, dl, f, fol = run_follow(ctx, ctx_len, 3, 15, 15, 3, tag=f"T {T}")
+        assert (fol[:-1] > 0).any(axis=1).all()
+
+
+def test_follow_distinct_limit_and_edges():
+    rows = []
+    for k in (1024, 1025, 3):
+        rows.append(np.concatenate([np.array([0, 0, 0, 5000 + i], np.int32) for i in range(k)] +
+                                   [np.zeros(3, np.int32)]))
+    rows.append(np.array([1, 2, 3, 9, 1, 2, 3, 9, 1, 2, 3, 7, 1, 2, 3], np.int32))
+    rows.append(np.array([5, 6, 7, 1, 5, 6, 7, 2, 5, 6, 7], np.int32))
+    rows.append(np.array([1, 2], np.int32))
+    rows.append(np.zeros(0, np.int32))
+    T = max(len(x) for x in rows)
+    ctx = np.zeros((len(rows), T), np.int32)
+    for i, x in enumerate(rows):
+        ctx[i, :len(x)] = x
+    ctx_len = np.array([len(x) for x in rows], np.int32)
+    d, dl, f, fol = run_follow(ctx, ctx_len, 5, 15, 6, 3, tag="limits")
+    assert dl[0] >= 1 and dl[1] == 0
+    d, dl, f, fol = run_follow(ctx, ctx_len, 3, 15, 32, 3, tag="limits n_min 3")
+
+
+def test_follow_tree_queries():
+    """The tree workload's n-gram fill (anchor and picks) with the pages'
+    three-token follower context."""
+    c = synth.config3_inputs()
+    qr, ex, el = synth.tree_queries(c["ctx"], c["ctx_len"], c["block"])
+    run_follow(c["ctx"], c["ctx_len"], 3, 15, c["L"], 3, query_req=qr, extra=ex, extra_len=el, tag="tree")
