@@ -1,6 +1,8 @@
 // N-gram prompt-lookup drafter (Hybrid Spark, Section 4.1 "One step" and
-// Section 4.2 match features; Algorithm 1, NGRAMSCAN): one workgroup per
-// query, one launch (the scan itself is ngram_scan).
+// Section 4.2 match features; Algorithm 1, NGRAMSCAN), with the follower
+// fallback of AdaSpark's n-gram fill (Section 3.3, "N-gram candidates") on
+// request: one workgroup per query, one launch (the scan itself is
+// ngram_scan).
 #include "ngram_scan.hpp"
 
 namespace spec {
