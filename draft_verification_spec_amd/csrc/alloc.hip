@@ -433,6 +433,21 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
     const int nd = 1 + P_ * Kc;
     const int64_t q0 = (int64_t)r * (P_ + 1);
     const bool staged = (int64_t)(P_ + 1) * A.ngram_ld <= kChainLds;
+    // the Eq. (6) inputs of the drafter nodes on the first 64 lanes (node i on
+    // lane i) and the request's own terms, requested now so that the weights
+    // do not wait for them after the walk
+    float pf_h = 0.5f, pf_s = 0.5f, pf_r = 1.0f, pf_src = 0.5f, pf_ctx = 0.0f, pf_req = 0.0f;
+    if (P.scored) {
+        pf_src = P.sc.p_src[r];
+        pf_ctx = P.sc.psi_ctx[r];
+        pf_req = P.sc.b_req[r];
+        if (lane >= 1 && lane < nd) {
+            const int p = (lane - 1) / Kc + 1, k = (lane - 1) % Kc;
+            pf_h = P.sc.h[(int64_t)r * P_ + p - 1];
+            pf_s = P.sc.sigma[(int64_t)r * P_ + p - 1];
+            if (k > 0) pf_r = P.sc.r_share[((int64_t)r * P_ + p - 1) * Kc + k];
+        }
+    }
     for (int i = lane; i <= P_; i += kWave) {
         clen[i] = A.ngram_len[q0 + i];
         cev[i] = (int8_t)(P.scored ? evidence_of(P.sc.ngram_feat + 4 * (q0 + i)) : 0);
@@ -648,10 +663,11 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
     const float* wz = A.w_none + (int64_t)r * cmax;
     if (P.scored) {
         const spec_tree_scores& S = P.sc;
-        const double lps = logit_prob((double)S.p_src[r]);
+        const double lps = logit_prob((double)pf_src);
         const double plus = lps > 0.0 ? lps : 0.0;
-        const double pc = (double)S.psi_ctx[r], br = (double)S.b_req[r];
+        const double pc = (double)pf_ctx, br = (double)pf_req;
         for (int j = lane; j < cnt; j += kWave) {
+            const bool pre = j < kWave;   // node j is on lane j: its inputs are in registers
             double sj = 0.0;
             const int kind = fkind[j] & 3;
             if (j == 0) {
@@ -662,13 +678,13 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
                 sj = lps + S.w_bucket[fbucket[j]] + pc + br;
             } else {
                 const int p = fdep[j], k = (j - 1) % Kc, ps = kind == 1 ? 0 : 1;
-                const double lh = logit_prob((double)S.h[(int64_t)r * P_ + p - 1]);
-                const double ls = logit_prob((double)S.sigma[(int64_t)r * P_ + p - 1]);
+                const double lh = logit_prob((double)(pre ? pf_h : S.h[(int64_t)r * P_ + p - 1]));
+                const double ls = logit_prob((double)(pre ? pf_s : S.sigma[(int64_t)r * P_ + p - 1]));
                 const double psi = pc + S.psi_depth[p < 15 ? p : 15];
                 if (kind == 1) {
                     sj = S.a[0] + S.a[1] * lh + S.a[2] * ls + psi + br;
                 } else {
-                    const double rr = clamp_prob((double)S.r_share[((int64_t)r * P_ + p - 1) * Kc + k]);
+                    const double rr = clamp_prob((double)(pre ? pf_r : S.r_share[((int64_t)r * P_ + p - 1) * Kc + k]));
                     sj = S.a[3] + S.a[4] * log(rr) + S.a[5] * lh + S.a[6] * ls + psi + br;
                 }
                 if (fagree[j] >= 0) sj += plus + S.w_agreed[fagree[j]][ps];
