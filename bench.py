@@ -263,10 +263,12 @@ def headline(K, W, hip, eager_only):
 
 
 def budget_step(K, W, hip, eager_only, config=2):
-    """The batch-allocation step: n-gram draft -> selection and allocation of
-    the budget's slots -> verification of the chosen chains -> commit; at BS
-    128 with a budget of 256 (config=2), or the large-batch stress workload at
-    BS 256, 32,768-token contexts, budget 512 and T = 0.7 (config=4)."""
+    """The batch-allocation step: n-gram draft, selection and allocation of
+    the budget's slots, verification of the chosen chains, commit; at BS 128
+    with a budget of 256 (config=2: the draft of the committed contexts runs
+    inside the verify call), or the large-batch stress workload at BS 256,
+    32,768-token contexts, budget 512 and T = 0.7 (config=4: a drafter launch
+    first)."""
     import numpy as np
     import torch
     import draft_verification_spec_amd as S
@@ -286,9 +288,23 @@ def budget_step(K, W, hip, eager_only, config=2):
             "ws_al": torch.empty(1 << 20, dtype=torch.uint8, device=dev),
             "ws_v": torch.empty(1 << 24, dtype=torch.uint8, device=dev)}
 
+    # The 8,192-token contexts are drafted inside the verify call (the drawing
+    # workgroups scan the committed context, as in the dense step); the
+    # 32,768-token ones by the drafter kernel, whose 1,024-thread scan takes
+    # such a text in one batch.  Fused drafts go to a buffer of their own, so
+    # every timed step repeats the same work on the same inputs.
+    fused = config == 2
+    with torch.cuda.stream(stream):
+        bufs["ng0"] = S.spec_ngram_draft(ctx, ctx_len, c["n_min"], c["n_max"], L, c["copy_cap"],
+                                         workspace=bufs["ws_ng"])
+        bufs["ng"] = tuple(torch.empty_like(x) for x in bufs["ng0"])
+
     def step(prof=None):
-        d, dl, f = S.spec_ngram_draft(ctx, ctx_len, c["n_min"], c["n_max"], L, c["copy_cap"],
-                                      out=bufs.get("ng"), workspace=bufs["ws_ng"])
+        if fused:
+            d, dl, f = bufs["ng0"]
+        else:
+            d, dl, f = S.spec_ngram_draft(ctx, ctx_len, c["n_min"], c["n_max"], L, c["copy_cap"],
+                                          out=bufs["ng"], workspace=bufs["ws_ng"])
         al = S.spec_allocate_budget(mode="chain", model_tokens=tokens_d, model_conf=conf_d, ngram_draft=d,
                                     ngram_len=dl, ngram_feat=f, est=c["estimator"], lam=c["lam"],
                                     budget=c["budget"], policy="proposed", conf_is_logit=True,
@@ -297,17 +313,19 @@ def budget_step(K, W, hip, eager_only, config=2):
                                   u_accept=u_acc, u_sample=u_smp, slot_flags=al["slot_flags"],
                                   out_flags=al["out_flags"], ctx=ctx, ctx_len=ctx_len, ctx_len_out=ctx_len_new,
                                   out=bufs.get("vf"), max_slots=c["budget"], workspace=bufs["ws_v"],
-                                  prof_events=prof)
-        bufs.setdefault("ng", (d, dl, f))
+                                  prof_events=prof,
+                                  ngram=(c["n_min"], c["n_max"], L, c["copy_cap"]) if fused else None,
+                                  ngram_out=bufs["ng"] if fused else None)
         bufs.setdefault("al", al)
-        bufs.setdefault("vf", {k: v for k, v in out.items() if k != "out_flags"})
+        bufs.setdefault("vf", {k: v for k, v in out.items()
+                               if k not in ("out_flags", "ngram_draft", "ngram_len", "ngram_feat")})
 
     with torch.cuda.stream(stream):
         step()
         torch.cuda.synchronize()
     total_rows = int(bufs["al"]["total_rows"].item())
     surv = bufs["al"]["survival"].cpu().numpy().ravel()   # the host copy the next step's sizing reads
-    outputs = lambda: list(bufs["vf"].values()) + [bufs["al"]["out_flags"], ctx_len_new, ctx]
+    outputs = lambda: list(bufs["vf"].values()) + [bufs["al"]["out_flags"], ctx_len_new, ctx] + list(bufs["ng"])
     t = run_timed(step, outputs, K, W, hip, stream, eager_only)
     sizing = host_sizing(S, surv, BS)
     rows_bytes = total_rows * V * 2
