@@ -294,17 +294,19 @@ def budget_step(K, W, hip, eager_only, config=2):
     # such a text in one batch.  Fused drafts go to a buffer of their own, so
     # every timed step repeats the same work on the same inputs.
     fused = config == 2
-    with torch.cuda.stream(stream):
-        bufs["ng0"] = S.spec_ngram_draft(ctx, ctx_len, c["n_min"], c["n_max"], L, c["copy_cap"],
-                                         workspace=bufs["ws_ng"])
-        bufs["ng"] = tuple(torch.empty_like(x) for x in bufs["ng0"])
+    if fused:
+        with torch.cuda.stream(stream):
+            bufs["ng0"] = S.spec_ngram_draft(ctx, ctx_len, c["n_min"], c["n_max"], L, c["copy_cap"],
+                                             workspace=bufs["ws_ng"])
+            bufs["ng"] = tuple(torch.empty_like(x) for x in bufs["ng0"])
 
     def step(prof=None):
         if fused:
             d, dl, f = bufs["ng0"]
         else:
             d, dl, f = S.spec_ngram_draft(ctx, ctx_len, c["n_min"], c["n_max"], L, c["copy_cap"],
-                                          out=bufs["ng"], workspace=bufs["ws_ng"])
+                                          out=bufs.get("ng"), workspace=bufs["ws_ng"])
+            bufs.setdefault("ng", (d, dl, f))
         al = S.spec_allocate_budget(mode="chain", model_tokens=tokens_d, model_conf=conf_d, ngram_draft=d,
                                     ngram_len=dl, ngram_feat=f, est=c["estimator"], lam=c["lam"],
                                     budget=c["budget"], policy="proposed", conf_is_logit=True,
