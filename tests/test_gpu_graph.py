@@ -59,3 +59,80 @@ def test_graph_replays_match_eager():
         with torch.cuda.stream(s):
             step()          # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_tree_step_graph_replays_match_eager():
+    """The tree step (n-gram fill with the follower fallback, Eq. (6) tree
+    build with S(n), greedy verification with commit) captured in one graph
+    replays to the eager result."""
+    import torch
+    import draft_verification_spec_amd as S
+    c = synth.config3_inputs(BS=16, V=50000)
+    BS, V, P, Kc, R = c["BS"], c["V"], c["P"], c["Kc"], c["rows_cap"]
+    ctx_h = np.zeros((BS, c["ctx"].shape[1] + R), np.int32)
+    ctx_h[:, :c["ctx"].shape[1]] = c["ctx"]
+    for r in range(BS):                       # texts ending in a repeated span: followers appear
+        T = int(c["ctx_len"][r])
+        ctx_h[r, T - 8:T] = np.tile(ctx_h[r, T - 12:T - 8], 2)
+    ctx, ctx_len = dev(ctx_h), dev(c["ctx_len"])
+    ctx_len_new = torch.zeros_like(ctx_len)
+    qr, ex, el = synth.tree_queries(ctx_h, c["ctx_len"], c["block"])
+    qr, ex, el, block = dev(qr), dev(ex), dev(el), dev(c["block"])
+    f = synth.tree_score_inputs(BS, P, Kc)
+    sc0 = dict(coef=f["coef"], h=dev(f["h"]), sigma=dev(f["sigma"]), r_share=dev(f["r_share"]),
+               psi_ctx=dev(f["psi_ctx"]), b_req=dev(f["b_req"]), p_src=dev(f["p_src"]))
+    ws = torch.empty(1 << 24, dtype=torch.uint8, device="cuda:0")
+    flags = torch.zeros(BS, dtype=torch.int32, device="cuda:0")
+    bufs = {}
+
+    def build():
+        d, dl, ft, fol = S.spec_ngram_draft(ctx, ctx_len, c["n_min"], c["n_max"], c["L"], 256, query_req=qr,
+                                            extra=ex, extra_len=el, out=bufs.get("ng"), follow_ctx=3)
+        t = S.spec_allocate_budget(mode="tree", block=block, ngram_draft=d, ngram_len=dl, ngram_follow=fol,
+                                   scores=dict(sc0, ngram_feat=ft), c_max=c["c_max"], depth_max=c["depth_max"],
+                                   rows_cap=R, s_curve=True, out=bufs.get("tr"))
+        bufs.setdefault("ng", (d, dl, ft, fol))
+        bufs.setdefault("tr", t)
+        return t
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        t = build()
+    torch.cuda.synchronize()
+    assert (bufs["ng"][3] > 0).any()
+    rows = synth.tree_target_rows(3, t["node_token"].cpu().numpy(), t["parent_row"].cpu().numpy(),
+                                  t["n_rows"].cpu().numpy(), c["truth"], V, R)
+    logits = dev(rows).reshape(-1, V)
+    rb = dev(np.arange(BS, dtype=np.int64) * R)
+
+    def step():
+        tr = build()
+        out = S.spec_verify_tree(logits, rb, tr["node_token"], tr["parent_row"], tr["n_rows"], out_flags=flags,
+                                 ctx=ctx, ctx_len=ctx_len, ctx_len_out=ctx_len_new, out=bufs.get("vt"),
+                                 workspace=ws)
+        bufs.setdefault("vt", out)
+        return out
+
+    with torch.cuda.stream(s):
+        step()
+        out = step()
+    torch.cuda.synchronize()
+    watched = lambda: dict(out, ctx_len_new=ctx_len_new, **{f"ng{i}": v for i, v in enumerate(bufs["ng"])},
+                           **{f"tr_{k}": v for k, v in bufs["tr"].items()})
+    ref = {k: v.cpu().clone() for k, v in watched().items()}
+    ref_ctx = ctx.cpu().clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    for rep in range(4):
+        for k, v in watched().items():
+            if k != "out_flags":
+                v.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in watched().items():
+            assert torch.equal(v.cpu(), ref[k]), (rep, k)
+        assert torch.equal(ctx.cpu(), ref_ctx)
+        with torch.cuda.stream(s):
+            step()          # eager work between replays
+        torch.cuda.synchronize()
