@@ -10,25 +10,31 @@
 // Section 2.2).
 //
 // Data flow (one stream, no host synchronisation):
-//   k_plan_rows  : one workgroup lists the rows the statistics pass reads
-//                  (request order: target rows, then the draft rows of
-//                  probabilistic slots) and counts them.
-//   k_stats_flat : the HBM-bound pass.  One workgroup per (row, chunk) item
-//                  of 16 KB, so the hardware dispatcher balances the load.
+//   k_stats_rows : the HBM-bound pass over batches whose rows per request are
+//                  near their bound: one workgroup per two adjacent 16 KB
+//                  chunks of a row, on a grid (rows x chunk pairs, requests);
+//                  workgroups of rows a request does not have exit at once.
+//   k_plan_rows  : otherwise one workgroup lists the rows the pass reads
+//   + k_stats_flat (request order: target rows, then the draft rows of
+//                  probabilistic slots), and the pass takes one (row, chunk)
+//                  item per workgroup from that list.
 //                  Per item: an online maximum m and sum of 2^(z*c - m*c)
 //                  (c = log2(e)/T; pairwise fp32 within a 32-element tile,
 //                  fp64 across tiles), or at T = 0 the maximum and its first
 //                  index.  (k_stats and k_stats_pipe cover rows that are not
 //                  16-byte aligned and draft rows of another dtype.)
-//   k_decide     : one 1024-thread workgroup per request merges its chunk
-//                  partials, finds p(y), q(y) of every slot in parallel and
-//                  the first rejection, then draws: the bonus row and
-//                  point-mass residuals from the chunk sums it already has
-//                  plus one chunk rescan; a probabilistic residual
-//                  max(0, p - q) by streaming its target and draft rows for
-//                  the chunk sums first.  Then it commits and, when asked,
-//                  drafts the request's next n-gram chain from the committed
-//                  context (ngram_scan) in the same workgroup.
+//   k_decide     : K workgroups of 512 threads per request each merge its
+//                  chunk partials and find p(y), q(y) of every slot and the
+//                  first rejection; workgroup 0 draws the bonus row and
+//                  point-mass residuals from the chunk sums plus one chunk
+//                  rescan, while a probabilistic residual max(0, p - q) is
+//                  summed by all K (each streams its share of the chunks of
+//                  both rows) and drawn by the last to finish.  The drawing
+//                  workgroup then commits and, when asked, drafts the
+//                  request's next n-gram chain from the committed context
+//                  (ngram_scan).
+//   k_tree_walk  : trees (T = 0): the argmax of every row, the accepted path
+//                  and its commit, one wave per request.
 #include <algorithm>
 #include <mutex>
 #include <utility>
