@@ -926,7 +926,7 @@ __global__ __launch_bounds__(kBlock) void k_plan_rows(StatsParams P)
     }
     if (t == 0) *P.plan_count = carry;
     if (P.done) {
-        for (int r = t; r < P.bs; r += kBlock) P.done[r] = 0;
+        for (int r = t; r < 2 * P.bs; r += kBlock) P.done[r] = 0;   // counts, then chunk counters
         for (int64_t i = t; i < (int64_t)P.bs * P.splits * kSubSums; i += kBlock) P.sums[i] = -1.0;
     }
 }
@@ -1031,7 +1031,7 @@ __global__ __launch_bounds__(kBlock) void k_stats_rows(StatsParams P, int32_t TM
         group_chunk<DT, GREEDY>(raw1, clo1, (ok && two) ? chi1 : clo1, P.c, R, 1, 0, t, two ? out + 1 : nullptr, !ok);
     }
     if (P.done && blockIdx.x == 0) {
-        if (t == 0) P.done[r] = 0;
+        if (t == 0) { P.done[r] = 0; P.done[P.bs + r] = 0; }   // count, chunk counter
         for (int i = t; i < P.splits * kSubSums; i += kBlock) P.sums[(int64_t)r * P.splits * kSubSums + i] = -1.0;
     }
 }
@@ -1469,48 +1469,62 @@ __device__ __forceinline__ void residual_round(const ChainParams& P, const Draw&
         for (int i = 0; i < kRound * kVecs; ++i) red[wid][i] = part[i];
 }
 
-// This workgroup's residual sums (chunks kk, kk + K, ...) of request r,
-// published as kSubSums per chunk (block q = v * kDWaves + w covers vectors
-// [v * kDBlock + 64 w, + 64) of the chunk, so q runs in entry order); returns
-// true in the workgroup that completes the request's count.
+// This workgroup's residual sums of request r, published as kSubSums per
+// chunk (block q = v * kDWaves + w covers vectors [v * kDBlock + 64 w, + 64)
+// of the chunk, so q runs in entry order); returns true in the workgroup that
+// completes the request's count.  Workgroup kk takes chunks kk and kk + K,
+// then hands out the rest from the request's counter (2K, 2K + 1, ...), one
+// chunk ahead, so the K workgroups finish together; the counter is zeroed by
+// the statistics pass.
 template <int DT>
 __device__ bool residual_publish(const ChainParams& P, const Draw& d, int r, int kk, int K)
 {
     static_assert(kVecs * kDBlock * 16 == kChunkBytes, "whole vectors per thread per chunk");
     static_assert(kVecs * kDWaves == kSubSums, "one residual sum per wave and vector slot");
-    __shared__ double red[2][kDWaves][kRound * kVecs];
+    static_assert(kRound == 1, "one chunk per round");
+    __shared__ double red[2][kDWaves][kVecs];
+    __shared__ int32_t sNext[2];
     __shared__ int32_t sLast;
     const int t = threadIdx.x;
     const char* tp = (const char*)row_ptr<DT>(P.logits, d.row_t, P.stride);
     const char* dp = (const char*)row_ptr<DT>(P.dlogits, d.row_d, P.dstride);
-    const int n = kk < P.splits ? (P.splits - kk + K - 1) / K : 0;   // chunks of this workgroup
-    const int rounds = (n + kRound - 1) / kRound;
-    const int stride = K * kRound;                                    // chunk step between rounds
-    // round i's sums from the wave slots, after the barrier that follows it
-    auto finish = [&](int i, int par) {
-        const int u = t / kSubSums, q = t % kSubSums;
-        const int j = i * kRound + u;
-        if (u < kRound && j < n) {
-            const double sum = red[par][q % kDWaves][u * kVecs + q / kDWaves];
-            __hip_atomic_store(&P.sums[((int64_t)r * P.splits + kk + j * K) * kSubSums + q], sum, __ATOMIC_RELAXED,
+    uint32_t* grab = P.done + P.bs + r;
+    // chunk c's sums from the wave slots, after the barrier that follows its round
+    auto finish = [&](int c, int par) {
+        const int q = t;
+        if (q < kSubSums && c < P.splits) {
+            const double sum = red[par][q % kDWaves][q / kDWaves];
+            __hip_atomic_store(&P.sums[((int64_t)r * P.splits + c) * kSubSums + q], sum, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
     };
-    uint4 a0[kRound * kVecs], b0[kRound * kVecs], a1[kRound * kVecs], b1[kRound * kVecs];
-    residual_issue<DT>(tp, dp, P, kk, K, t, a0, b0);
-    // rounds 2i (buffers 0) and 2i + 1 (buffers 1); red[i & 1] alternates so
-    // one barrier per round suffices (chunks past the row read first vectors)
-    for (int i = 0; i < rounds; i += 2) {
-        const int c0 = kk + i * stride, c1 = c0 + stride;
+    uint4 a0[kVecs], b0[kVecs], a1[kVecs], b1[kVecs];
+    int c0 = kk, c1 = kk + K;
+    residual_issue<DT>(tp, dp, P, c0, K, t, a0, b0);
+    uint32_t g = 0;
+    if (t == 0) g = __hip_atomic_fetch_add(grab, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // rounds alternate between buffers 0 and 1 and between red[0] and red[1],
+    // so one barrier per round suffices (chunks past the row read first
+    // vectors and publish nothing)
+    while (c0 < P.splits) {
         residual_issue<DT>(tp, dp, P, c1, K, t, a1, b1);
         residual_round<DT>(P, d, c0, K, t, a0, b0, red[0]);
+        if (t == 0) sNext[0] = 2 * K + (int)g;
         __syncthreads();
-        finish(i, 0);
-        residual_issue<DT>(tp, dp, P, c1 + stride, K, t, a0, b0);
+        finish(c0, 0);
+        const int c2 = sNext[0];
+        if (t == 0) g = __hip_atomic_fetch_add(grab, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        residual_issue<DT>(tp, dp, P, c2, K, t, a0, b0);
         residual_round<DT>(P, d, c1, K, t, a1, b1, red[1]);
+        if (t == 0) sNext[1] = 2 * K + (int)g;
         __syncthreads();
-        finish(i + 1, 1);
+        finish(c1, 1);
+        c0 = c2;
+        c1 = sNext[1];
+        if (t == 0 && c0 < P.splits) g = __hip_atomic_fetch_add(grab, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    drain(a0);
+    drain(b0);
     // every sum store of the workgroup completes before the count reports them
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -2298,7 +2312,7 @@ size_t spec_verify_chain_ws(int32_t bs, int32_t vocab, int32_t ld, int32_t dtype
     const int NR = 2 * ld + 1;
     return align256((size_t)bs * NR * sp.splits * sizeof(Partial)) + align256((size_t)(bs + 1) * sizeof(int32_t)) +
            plan_bytes((int64_t)bs * NR) + align256((size_t)bs * sp.splits * kSubSums * sizeof(double)) +
-           align256((size_t)bs * sizeof(uint32_t));
+           align256((size_t)2 * bs * sizeof(uint32_t));
 }
 
 // Tree verify workspace: partials [bs, rows_max, splits] | row prefix [bs + 1] | row plan [bs * rows_max]
