@@ -798,10 +798,14 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
     uint32_t stk_lo = lane == 0 ? (uint32_t)kids0 : 0u, stk_hi = lane == 0 ? (uint32_t)(kids0 >> 32) : 0u;
     int stk_row = 0, ord = lane == 0 ? 0 : -1, prow = -1;
     int row = 1, d = 0;
-    while (d >= 0 && row < m) {
+    while (row < m) {
+        // the deepest node on the path with an unvisited child (every level
+        // below it is done: one ballot instead of a pop per level)
+        const uint64_t open = __builtin_amdgcn_ballot_w64(lane <= d && (stk_lo | stk_hi) != 0u);
+        if (!open) break;
+        d = 63 - (int)__builtin_clzll(open);
         const uint64_t top = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)stk_hi, d) << 32)
                            | (uint32_t)__builtin_amdgcn_readlane((int)stk_lo, d);
-        if (top == 0) { --d; continue; }
         const int c = (int)__builtin_ctzll(top);
         const uint64_t kids = children(c);
         const int prw = __builtin_amdgcn_readlane(stk_row, d);
