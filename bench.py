@@ -447,8 +447,8 @@ def host_sizing(S, surv, BS, calls=2000):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the step shards by request; "
-              "see DESIGN.md). Run with --gpus 1.", file=sys.stderr, flush=True)
+        print("bench.py measures one GPU: the library has no multi-GPU path (the step would shard by "
+              "request, each GPU running its own requests). Run with --gpus 1.", file=sys.stderr, flush=True)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
