@@ -262,3 +262,33 @@ def test_tree_build_follower_buckets():
         # the follower weights matter: without the counts the oracle builds other trees
         o0 = O.tree_build_batch(blk, d, dl, depth_max=dmax, rows_cap=rows_cap, scores=per, c_max=cm)
         assert not np.allclose(o0["Q"], o["Q"])
+
+
+@pytest.mark.parametrize("BS", [1, 63, 1000, 1024, 1025, 1500])
+def test_tree_row_bases_any_batch(BS):
+    """Row bases and the total over every batch size the row scan handles in
+    registers (up to 1,024 requests) and beyond."""
+    import torch
+    import draft_verification_spec_amd as S
+    rng = np.random.Generator(np.random.Philox(70 + BS))
+    P, Kc, L = 2, 2, 4
+    block = rng.integers(0, 6, (BS, P, Kc)).astype(np.int32)
+    block[:, :, 1] = (block[:, :, 0] + 1) % 6
+    ngl = rng.integers(0, L + 1, BS * (P + 1)).astype(np.int32)
+    ng = rng.integers(0, 6, (BS * (P + 1), L)).astype(np.int32)
+    cm = 1 + P * Kc + (P + 1) * L
+    wn = rng.standard_exponential((BS, cm)).astype(np.float32)
+    wz = rng.standard_exponential((BS, cm)).astype(np.float32)
+    print(f"tree row bases: bs {BS}", flush=True)
+    o = O.tree_build_batch(block, ng, ngl, wn, wz, 8, 6)
+    g = S.spec_allocate_budget(mode="tree", block=dev(block), ngram_draft=dev(ng), ngram_len=dev(ngl),
+                               w_node=dev(wn), w_none=dev(wz), depth_max=8, rows_cap=6)
+    torch.cuda.synchronize()
+    g = {k: host(v) for k, v in g.items()}
+    ok = ok_rows(o["flags"])
+    assert_rows_equal(g["n_rows"], o["n_rows"], ok, "n_rows")
+    rb = np.concatenate([[0], np.cumsum(g["n_rows"])[:-1]]).astype(np.int64)
+    assert np.array_equal(g["row_base"], rb)
+    assert g["total_rows"][0] == g["n_rows"].sum()
+    if ok.all():
+        assert np.array_equal(g["row_base"], o["row_base"])
