@@ -22,8 +22,8 @@ i32, i64, f32, vp, sz = C.c_int32, C.c_int64, C.c_float, C.c_void_p, C.c_size_t
 # ---- constants mirrored from spec.h ----------------------------------------
 SPEC_OK, SPEC_EINVAL, SPEC_EWORKSPACE, SPEC_EHIP = 0, -1, -2, -3
 SPEC_F32, SPEC_BF16 = 0, 1
-FLAG_RESIDUAL_ZERO, FLAG_BAD_TOKEN, FLAG_BAD_LOGITS, FLAG_CTX_OVERFLOW, FLAG_BAD_LENGTH = (
-    1 << 5, 1 << 8, 1 << 9, 1 << 10, 1 << 11)
+FLAG_RESIDUAL_ZERO, FLAG_BAD_TOKEN, FLAG_BAD_LOGITS, FLAG_CTX_OVERFLOW, FLAG_BAD_LENGTH, FLAG_RESIDUAL_LATE = (
+    1 << 5, 1 << 8, 1 << 9, 1 << 10, 1 << 11, 1 << 12)
 SLOT_POINT_MASS, SLOT_FROM_NGRAM = 1, 2
 SRC_MODEL, SRC_NGRAM, SRC_MERGED, SRC_EXTENDED = 0, 1, 2, 3
 POLICIES = {"proposed": 0, "ngram_first": 1, "extension": 2, "model_only": 3, "ngram_only": 4}
@@ -85,7 +85,8 @@ class VerifyArgs(C.Structure):
                 ("ctx_stride", i64),
                 ("ctx_len", vp), ("ctx_len_out", vp), ("ctx_cap", i32), ("ngram_draft", vp),
                 ("ngram_draft_len", vp), ("ngram_feat", vp), ("ngram_n_min", i32), ("ngram_n_max", i32),
-                ("ngram_max_draft", i32), ("ngram_copy_cap", i32), ("prof_begin", vp), ("prof_end", vp),
+                ("ngram_max_draft", i32), ("ngram_copy_cap", i32), ("residual_wait", i32), ("prof_begin", vp),
+                ("prof_end", vp),
                 ("workspace", vp), ("workspace_bytes", sz)]
 
 
@@ -175,12 +176,19 @@ def _check(rc: int):
         raise RuntimeError(f"libspec_hip: {msg} (code {rc})")
 
 
-def _workspace(op, args, device, workspace):
+def _workspace(op, args, device, workspace, stream=None):
+    """The call's workspace: the caller's, or a new one from torch's caching
+    allocator.  A new one is dropped when the call returns, so when the call
+    runs on another stream than the current one the block is recorded on that
+    stream (the allocator then does not hand it out again until the stream's
+    work is done)."""
     need = lib().spec_workspace_bytes(op, C.byref(args))
     if need == 0:
         return None, 0
     if workspace is None:
         workspace = torch.empty(need + 256, dtype=torch.uint8, device=device)
+        if stream is not None:
+            workspace.record_stream(stream)
     elif workspace.numel() < need + 256:
         raise ValueError(f"workspace too small: {workspace.numel()} < {need + 256}")
     base = workspace.data_ptr()
@@ -264,7 +272,7 @@ def spec_ngram_draft(ctx, ctx_len, n_min, n_max, max_draft=15, copy_cap=256, que
                   extra_stride=0 if extra is None else extra.shape[1], extra_len=_ptr(extra_len),
                   n_min=n_min, n_max=n_max, max_draft=max_draft, copy_cap=copy_cap, follow_ctx=follow_ctx,
                   draft=_ptr(draft), draft_len=_ptr(dlen), feat=_ptr(feat), draft_follow=_ptr(fol))
-    ws, w = _workspace(OP_NGRAM, a, dev, workspace)
+    ws, w = _workspace(OP_NGRAM, a, dev, workspace, stream)
     if w:
         a.workspace, a.workspace_bytes = w
     _check(lib().spec_ngram_draft(C.byref(a), _stream(dev, stream)))
@@ -300,7 +308,7 @@ def _chain_alloc(model_tokens, model_conf, ngram_draft, ngram_len, ngram_feat, e
                     policy=POLICIES[policy] if isinstance(policy, str) else int(policy),
                     **{k: _ptr(v) for k, v in out.items()})
     a = AllocArgs(mode=ALLOC_CHAIN, chain=ca)
-    ws, w = _workspace(OP_ALLOCATE, a, dev, workspace)
+    ws, w = _workspace(OP_ALLOCATE, a, dev, workspace, stream)
     if w:
         a.workspace, a.workspace_bytes = w
     _check(lib().spec_allocate_budget(C.byref(a), _stream(dev, stream)))
@@ -385,7 +393,7 @@ def spec_verify_chain(logits, row_base, tokens, n_slots, temperature, u_accept=N
                       slot_flags=None, draft_logits=None, draft_row_base=None, out_flags=None,
                       ctx=None, ctx_len=None, ctx_cap=None, ctx_len_out=None, out=None, workspace=None,
                       stream=None, prof_events=None, max_slots=0, write_flags=False, ngram=None, ngram_out=None,
-                      rng=None, accept_hist=None):
+                      rng=None, accept_hist=None, residual_wait=0):
     """Rejection-sampling verification of one chain per request (optional commit into ctx).
     ``prof_events``: optional pair of raw hipEvent_t handles recorded around the
     row-statistics pass.  ``max_slots``: optional bound of the total slots
@@ -399,7 +407,9 @@ def spec_verify_chain(logits, row_base, tokens, n_slots, temperature, u_accept=N
     ``rng``: optional (seed, offset): the call draws its uniforms with
     Philox4x32-10 instead of reading u_accept / u_sample.  ``accept_hist``:
     optional int32 [ld + 1] device tensor, increased at each request's
-    accepted count."""
+    accepted count.  ``residual_wait``: polls of a published residual sum
+    before the drawing workgroup sums the residual itself (0 = the library's
+    default; negative = at once, which tests the fallback)."""
     lg = _rows2d(logits, "logits")
     _dev(row_base, torch.int64, "row_base", 1)
     _dev(tokens, torch.int32, "tokens", 2)
@@ -421,7 +431,7 @@ def spec_verify_chain(logits, row_base, tokens, n_slots, temperature, u_accept=N
         out = dict(out_tokens=torch.empty((bs, ld + 1), dtype=torch.int32, device=dev),
                    out_num=torch.empty(bs, dtype=torch.int32, device=dev),
                    out_accepted=torch.empty(bs, dtype=torch.int32, device=dev),
-                   out_p=torch.empty((bs, ld), dtype=torch.float32, device=dev),
+                   out_p=torch.empty((bs, ld + 1), dtype=torch.float32, device=dev),
                    out_q=torch.empty((bs, ld), dtype=torch.float32, device=dev))
     if out_flags is None:
         out_flags = (torch.empty if write_flags else torch.zeros)(bs, dtype=torch.int32, device=dev)
@@ -431,7 +441,8 @@ def spec_verify_chain(logits, row_base, tokens, n_slots, temperature, u_accept=N
                    n_logit_rows=lg.shape[0], tokens=_ptr(tokens), slot_flags=_ptr(slot_flags), ld=ld,
                    n_slots=_ptr(n_slots), max_slots=int(max_slots), u_accept=_ptr(u_accept),
                    u_sample=_ptr(u_sample),
-                   write_flags=int(bool(write_flags)), **{k: _ptr(v) for k, v in out.items()})
+                   write_flags=int(bool(write_flags)), residual_wait=int(residual_wait),
+                   **{k: _ptr(v) for k, v in out.items()})
     if dl is not None:
         a.draft_logits, a.draft_dtype, a.draft_row_stride = _ptr(dl), _logits_dtype(dl), dl.stride(0)
         a.draft_row_base, a.n_draft_rows = _ptr(draft_row_base), dl.shape[0]
@@ -463,7 +474,7 @@ def spec_verify_chain(logits, row_base, tokens, n_slots, temperature, u_accept=N
         a.ngram_n_min, a.ngram_n_max, a.ngram_max_draft, a.ngram_copy_cap = n_min, n_max, max_draft, copy_cap
     if prof_events is not None:
         a.prof_begin, a.prof_end = prof_events
-    ws, w = _workspace(OP_VERIFY_CHAIN, a, dev, workspace)
+    ws, w = _workspace(OP_VERIFY_CHAIN, a, dev, workspace, stream)
     if w:
         a.workspace, a.workspace_bytes = w
     _check(lib().spec_verify_chain(C.byref(a), _stream(dev, stream)))
@@ -504,7 +515,7 @@ def spec_verify_tree(logits, row_base, node_token, parent_row, n_rows, out_flags
             a.ctx_len_out = _ptr(ctx_len_out)
     if prof_events is not None:
         a.prof_begin, a.prof_end = prof_events
-    ws, w = _workspace(OP_VERIFY_TREE, a, dev, workspace)
+    ws, w = _workspace(OP_VERIFY_TREE, a, dev, workspace, stream)
     if w:
         a.workspace, a.workspace_bytes = w
     _check(lib().spec_verify_tree(C.byref(a), _stream(dev, stream)))

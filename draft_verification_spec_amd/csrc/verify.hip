@@ -1076,6 +1076,7 @@ struct ChainParams {
     Partial* part; int32_t NR; int32_t splits; int64_t chunk;
     double* sums;               // [bs, splits, kSubSums] residual sums (-1 until written)
     uint32_t* done;             // [bs] workgroups of a request done with their residual chunks
+    int32_t wait_limit;         // polls of a published residual sum before the drawer sums it itself (< 0: none)
     bool t_aligned, d_aligned;  // rows allow 16-byte vector loads
     bool coal;                  // same dtype, aligned rows, vocab a multiple of a vector
 };
@@ -1537,11 +1538,13 @@ __device__ bool residual_publish(const ChainParams& P, const Draw& d, int r, int
 }
 
 // One published residual sum; a sum still -1 is not yet visible and is read
-// again (a bounded wait that in practice never spins).
-__device__ __forceinline__ double residual_load(const double* w)
+// again, at most `limit` more times (in practice it never spins).  Returns -1
+// if the sum did not arrive (limit < 0: without reading it at all).
+__device__ __forceinline__ double residual_load(const double* w, int32_t limit)
 {
+    if (limit < 0) return -1.0;
     double v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int tries = 0; v < 0.0 && tries < (1 << 20); ++tries)
+    for (int32_t tries = 0; v < 0.0 && tries < limit; ++tries)
         v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return v;
 }
@@ -1550,8 +1553,11 @@ __device__ __forceinline__ double residual_load(const double* w)
 // thread s gathers chunk s's published sums, the chunk is picked from their
 // totals, then wave 0 picks the block of 64 vectors from the chunk's
 // kSubSums and finds the entry among the block's 64 x VEC with one load of
-// both rows per lane.  Returns the token, or -1 if the residual has no usable
-// mass.
+// both rows per lane.  Returns the token, -1 if the residual has no usable
+// mass, or kResidualLate if a published sum did not arrive within the bounded
+// wait (the caller then sums the residual itself).
+constexpr int32_t kResidualLate = -2;
+
 template <int DT>
 __device__ int32_t residual_draw(const ChainParams& P, const Draw& d, int r, double u, double* W)
 {
@@ -1559,19 +1565,26 @@ __device__ int32_t residual_draw(const ChainParams& P, const Draw& d, int r, dou
     constexpr int ES = DT == SPEC_F32 ? 4 : 2;
     __shared__ double sSub[kSubSums];
     __shared__ int32_t sTok;
+    __shared__ int32_t sLate;
     const int t = threadIdx.x;
     double mine[kSubSums];
+    if (t == 0) sLate = 0;
+    __syncthreads();
     if (t < P.splits) {
         const double* src = P.sums + ((int64_t)r * P.splits + t) * kSubSums;
         double tot = 0.0;
+        bool late = false;
 #pragma unroll
         for (int q = 0; q < kSubSums; ++q) {
-            mine[q] = residual_load(src + q);
+            mine[q] = residual_load(src + q, P.wait_limit);
+            late |= mine[q] < 0.0;
             tot += mine[q];
         }
         W[t] = tot;
+        if (late) sLate = 1;
     }
     __syncthreads();
+    if (sLate) return kResidualLate;
     int c;
     double rem;
     if (!pick_chunk(P, W, u, &c, &rem)) return -1;
@@ -1801,14 +1814,15 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
             const double rho = q > 0.0 ? p / q : 0.0;
             acc = (double)uacc < rho;
         }
-        if (P.out_p && lead) P.out_p[off] = (float)p;
+        if (P.out_p && lead) P.out_p[(int64_t)r * (ld + 1) + t] = (float)p;
         if (P.out_q && lead) P.out_q[off] = (float)q;
         rejected = !acc;
         slot_fl = fl;
-    } else if (t < ld && lead) {
-        const int64_t off = (int64_t)r * ld + t;
-        if (P.out_p) P.out_p[off] = 0.0f;
-        if (P.out_q) P.out_q[off] = 0.0f;
+    } else if (t <= ld && lead) {
+        // past the slots; entry b of out_p (the bonus row) is the drawing
+        // workgroup's to write
+        if (P.out_p && t != b) P.out_p[(int64_t)r * (ld + 1) + t] = 0.0f;
+        if (P.out_q && t < ld) P.out_q[(int64_t)r * ld + t] = 0.0f;
     }
     // every slot thread is in wave 0 (b <= ld <= 32): a ballot and an OR
     // across the wave instead of atomics
@@ -1823,7 +1837,9 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
     __syncthreads();
     const uint64_t rej = sRej;
     const int nacc = rej ? (int)__builtin_ctzll(rej) : b;
-    if (lead && t <= ld) P.out_tokens[(int64_t)r * (ld + 1) + t] = (t < nacc) ? y : -1;
+    // token nacc (the correction or bonus) is written by the drawing
+    // workgroup alone, which need not be this one
+    if (lead && t <= ld && t != nacc) P.out_tokens[(int64_t)r * (ld + 1) + t] = (t < nacc) ? y : -1;
     if (t == 0) {
         if (lead) {
             P.out_num[r] = nacc + 1;
@@ -1881,14 +1897,20 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
             ngv[u] = row[j < lastp ? j : lastp];
         }
     }
+    bool resum = false;   // a streamed residual whose published sums did not all arrive
     if (streamed) {
         last = residual_draw<DTT>(P, d, r, usmp, sW);
-        if (last < 0) {
+        if (last == kResidualLate) {
+            if (t == 0) sFlags |= SPEC_FLAG_RESIDUAL_LATE;
+            resum = true;
+        } else if (last < 0) {
             // the residual had no mass (not reachable in exact arithmetic): draw from p
             if (t == 0) sFlags |= SPEC_FLAG_RESIDUAL_ZERO;
             last = draw_from_p<DTT, DTD>(P, d, sW, usmp);
         }
-    } else if (d.mode != 0) {
+    }
+    if (!streamed || resum) {
+      if (d.mode != 0) {
         if (d.mode == 2) {
             // residual max(0, p - q) of rows that do not take the vector path: chunk by chunk
             for (int s = 0; s < P.splits; ++s) {
@@ -1921,10 +1943,24 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
             if (t == 0) sFlags |= SPEC_FLAG_RESIDUAL_ZERO;
             last = draw_from_p<DTT, DTD>(P, d, sW, usmp);
         }
-    } else if (!P.greedy) {
+      } else if (!P.greedy) {
         if (t == 0) sFlags |= SPEC_FLAG_BAD_LOGITS;
+      }
     }
-    if (t == 0) P.out_tokens[(int64_t)r * (ld + 1) + nacc] = last;
+    if (t == 0) {
+        P.out_tokens[(int64_t)r * (ld + 1) + nacc] = last;
+        if (P.out_p) {
+            // p of the bonus row at the bonus token (0 when a slot was rejected)
+            float pb = 0.0f;
+            if (nacc == b && last >= 0 && last < P.vocab && sOk[b]) {
+                if (P.greedy) pb = 1.0f;
+                else if (d.mode == 1)
+                    pb = (float)((double)fast_exp2(fmaf(logit_at(P.logits, DTT, d.row_t, P.stride, last), P.c, -d.Ot)) /
+                                 sZ[b]);
+            }
+            P.out_p[(int64_t)r * (ld + 1) + b] = pb;
+        }
+    }
     __syncthreads();
     uint32_t fl = sFlags;
     if (P.ctx) {
@@ -2346,6 +2382,7 @@ int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st)
     P.ctx_len_out = a->ctx_len_out ? a->ctx_len_out : a->ctx_len; P.ctx_cap = a->ctx_cap;
     P.ng_draft = a->ctx ? a->ngram_draft : nullptr; P.ng_len = a->ngram_draft_len; P.ng_feat = a->ngram_feat;
     P.ng_min = a->ngram_n_min; P.ng_max = a->ngram_n_max; P.ng_ld = a->ngram_max_draft; P.ng_cap = a->ngram_copy_cap;
+    P.wait_limit = a->residual_wait == 0 ? (1 << 20) : (a->residual_wait < 0 ? -1 : a->residual_wait);
     P.part = (Partial*)ws;
     ws += align256((size_t)a->bs * NR * sp.splits * sizeof(Partial));
     int32_t* gpre = (int32_t*)ws;

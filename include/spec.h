@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 4
+#define SPEC_ABI_VERSION 5
 
 /* ---- return codes ---------------------------------------------------- */
 #define SPEC_OK          0
@@ -62,6 +62,11 @@ extern "C" {
                                               entry; its outputs are unspecified     */
 #define SPEC_FLAG_CTX_OVERFLOW  (1u << 10) /* commit skipped: context capacity       */
 #define SPEC_FLAG_BAD_LENGTH    (1u << 11) /* a length argument was clamped          */
+#define SPEC_FLAG_RESIDUAL_LATE (1u << 12) /* the residual's published chunk sums did
+                                              not all arrive within the bounded wait:
+                                              the drawing workgroup summed the
+                                              residual again itself (same result up
+                                              to rounding order)                     */
 
 /* ---- slot flags (chain slots) ----------------------------------------- */
 #define SPEC_SLOT_POINT_MASS 1u  /* verify as a point mass, q = delta_y         */
@@ -308,8 +313,10 @@ typedef struct spec_alloc_args {
  * u_sample[r].  T = 0: accept iff y_i = argmax z (ties to the lowest id); the
  * correction / bonus is the argmax.  Out: out_tokens[r][0..out_num) = the
  * accepted tokens then the correction or bonus, out_num = accepted + 1,
- * out_p / out_q = p(y_i) / q(y_i) for every slot (q = 1 for point masses and
- * at T = 0, where p is 1 or 0).  out_flags is OR-ed (written with
+ * out_p[r][i] / out_q[r][i] = p(y_{i+1}) / q(y_{i+1}) for every slot i < b
+ * (q = 1 for point masses and at T = 0, where p is 1 or 0); out_p[r][b] = p of
+ * the bonus row at the bonus token when every slot passed (1 at T = 0), else 0;
+ * entries past them are 0.  out_flags is OR-ed (written with
  * write_flags).  If ctx is not NULL the
  * emitted tokens are appended to ctx[r] at ctx_len[r] (skipped and flagged if
  * ctx_len + out_num > ctx_cap).  n_slots outside [0, ld] are clamped.
@@ -357,7 +364,7 @@ typedef struct spec_verify_args {
     int32_t* out_tokens;         /* device [bs, ld+1], -1 padded                  */
     int32_t* out_num;            /* device [bs]                                   */
     int32_t* out_accepted;       /* device [bs]                                   */
-    float* out_p;                /* device [bs, ld] or NULL                       */
+    float* out_p;                /* device [bs, ld + 1] or NULL                   */
     float* out_q;                /* device [bs, ld] or NULL                       */
     uint32_t* out_flags;         /* device [bs], OR-ed (see write_flags)          */
     int32_t write_flags;         /* 1: out_flags[r] is written with this call's
@@ -380,6 +387,11 @@ typedef struct spec_verify_args {
     int32_t ngram_n_max;         /* spec_ngram_args                               */
     int32_t ngram_max_draft;
     int32_t ngram_copy_cap;
+    int32_t residual_wait;       /* polls of one published residual chunk sum before
+                                    the drawing workgroup gives up on it and sums
+                                    the residual itself (SPEC_FLAG_RESIDUAL_LATE);
+                                    0 = 2^20, < 0 = give up at once (a test of the
+                                    fallback: the sums are then never waited for) */
     void* prof_begin;            /* optional hipEvent_t pair (created with timing) */
     void* prof_end;              /* attached to the row-statistics kernel's own
                                     dispatch: begin = its start, end = its end    */

@@ -302,7 +302,13 @@ def _logits(x):
 
 def verify_chain(logits, row_base, tokens, slot_flags, n_slots, u_acc, u_smp, temperature,
                  draft_logits=None, draft_row_base=None, flags=None):
-    """logits: [rows, V] (fp32 or bf16 bits); tokens/slot_flags/u_acc: [bs, ld]."""
+    """logits: [rows, V] (fp32 or bf16 bits); tokens/slot_flags/u_acc: [bs, ld].
+
+    Returns out_tokens [bs, ld+1], out_num, out_accepted, out_p [bs, ld+1]
+    (p(y) per slot, then p of the bonus row at the bonus token), out_q
+    [bs, ld], flags, and the final draw's tie window [win_lo, win_hi]: the
+    tokens whose CDF interval meets the band of 1e-6 W around u'W (the drawn
+    token alone unless the request is flagged SAMPLE_NEAR)."""
     lg, dt = _logits(logits)
     dl, ddt = _logits(draft_logits)
     V = lg.shape[-1]
@@ -319,16 +325,19 @@ def verify_chain(logits, row_base, tokens, slot_flags, n_slots, u_acc, u_smp, te
     out_tokens = np.full((bs, ld + 1), -1, np.int32)
     out_num = np.zeros(bs, np.int32)
     out_acc = np.zeros(bs, np.int32)
-    out_p = np.zeros((bs, ld), np.float64)
+    out_p = np.zeros((bs, ld + 1), np.float64)
     out_q = np.zeros((bs, ld), np.float64)
+    win_lo = np.zeros(bs, np.int32)
+    win_hi = np.zeros(bs, np.int32)
     fl = np.zeros(bs, np.uint32) if flags is None else flags.astype(np.uint32).copy()
     lib().oracle_verify_chain(C.c_int(bs), C.c_int(V), C.c_double(temperature),
                               _p(lg2), C.c_int(dt), C.c_int64(V), _p(row_base),
                               _p(dl2), C.c_int(ddt), C.c_int64(V), _p(drb),
                               _p(tokens), _p(slot_flags), C.c_int(ld), _p(n_slots), _p(u_acc), _p(u_smp),
-                              _p(out_tokens), _p(out_num), _p(out_acc), _p(out_p), _p(out_q), _p(fl))
+                              _p(out_tokens), _p(out_num), _p(out_acc), _p(out_p), _p(out_q), _p(fl),
+                              _p(win_lo), _p(win_hi))
     return dict(out_tokens=out_tokens, out_num=out_num, out_accepted=out_acc, out_p=out_p, out_q=out_q,
-                flags=fl)
+                flags=fl, win_lo=win_lo, win_hi=win_hi)
 
 
 def commit(ctx, ctx_len, ctx_cap, out_tokens, out_num, flags):

@@ -41,9 +41,12 @@
 
 #define NEAR_EPS 1e-6
 
-/* A planted mistake, compiled in only by the test that shows the Monte Carlo
- * losslessness check detects one: 1 = sample the correction from p instead of
- * the residual; 2 = accept with probability p(y) ignoring q.  0 = correct. */
+/* A planted mistake, compiled in only by the tests that show the Monte Carlo
+ * losslessness checks detect one: 1 = sample the correction from p instead of
+ * the residual; 2 = accept with probability p(y) ignoring q; 3 = verify the
+ * extension policy's n-gram tail against q instead of as point masses; 4 =
+ * n-gram-first keeps the drafter's chain when its first sampled token is 0
+ * (a choice that reads the drafter's samples).  0 = correct. */
 #ifndef SPEC_ORACLE_MUTATION
 #define SPEC_ORACLE_MUTATION 0
 #endif
@@ -294,7 +297,10 @@ int oracle_select(int K, const int32_t* d, const double* c, int dlen,
             use = (vg >= vd) ? SRC_NGRAM : SRC_MODEL;
         }
         break;
-    case POL_NGRAM_FIRST: use = (glen >= 1) ? SRC_NGRAM : SRC_MODEL; break;
+    case POL_NGRAM_FIRST:
+        use = (glen >= 1) ? SRC_NGRAM : SRC_MODEL;
+        if (SPEC_ORACLE_MUTATION == 4 && dlen >= 1 && d[0] == 0) use = SRC_MODEL;
+        break;
     case POL_EXTENSION: use = prefix ? SRC_EXTENDED : SRC_MODEL; break;
     case POL_MODEL_ONLY: use = SRC_MODEL; break;
     case POL_NGRAM_ONLY: use = SRC_NGRAM; break;
@@ -319,7 +325,7 @@ int oracle_select(int K, const int32_t* d, const double* c, int dlen,
         for (int k = 0; k < glen; ++k) {
             out_tok[k] = g[k];
             if (k < K) { out_flag[k] = mfl; out_S[k] = Sd[k]; }
-            else { out_flag[k] = gfl; out_S[k] = out_S[k - 1] * h[k]; }
+            else { out_flag[k] = SPEC_ORACLE_MUTATION == 3 ? mfl : gfl; out_S[k] = out_S[k - 1] * h[k]; }
         }
         len = glen;
     }
@@ -578,7 +584,12 @@ static double resid_w(const resid_t* R, int64_t v)
     return p > q ? p - q : 0.0;
 }
 
-static int64_t draw(const resid_t* R, int V, double u, uint32_t* flag)
+/* The draw's tie window: every token of positive weight whose CDF interval
+ * [c_v, c_v + w_v) meets the band [t - eps W, t + eps W] around the target
+ * t = u W.  A draw whose arithmetic differs from this one by less than eps W
+ * in any running sum picks a token of the window, and no other.  Outside a
+ * SAMPLE_NEAR case the window is the drawn token alone. */
+static int64_t draw(const resid_t* R, int V, double u, uint32_t* flag, int64_t* win_lo, int64_t* win_hi)
 {
     double W = 0.0;
     for (int64_t v = 0; v < V; ++v) W += resid_w(R, v);
@@ -589,19 +600,35 @@ static int64_t draw(const resid_t* R, int V, double u, uint32_t* flag)
         W = 0.0;
         for (int64_t v = 0; v < V; ++v) W += resid_w(&P, v);
     }
-    double t = u * W, c = 0.0;
+    const double t = u * W, band = NEAR_EPS * W;
+    double c = 0.0;
+    int64_t pick = -1, lo = -1, hi = -1, lastpos = -1;
     for (int64_t v = 0; v < V; ++v) {
         double w = resid_w(&P, v);
         double c2 = c + w;
-        if (c2 > t) {
-            if (t - c <= NEAR_EPS * W || c2 - t <= NEAR_EPS * W) *flag |= OF_SAMPLE_NEAR;
-            return v;
+        if (w > 0.0) {
+            lastpos = v;
+            if (c2 > t - band && c <= t + band) {
+                if (lo < 0) lo = v;
+                hi = v;
+            }
+        }
+        if (pick < 0 && c2 > t) {
+            pick = v;
+            if (t - c <= band || c2 - t <= band) *flag |= OF_SAMPLE_NEAR;
         }
         c = c2;
+        if (pick >= 0 && c > t + band) break;   /* no later interval meets the band */
     }
-    *flag |= OF_SAMPLE_NEAR;  /* rounding left t at the very end */
-    for (int64_t v = V - 1; v >= 0; --v) if (resid_w(&P, v) > 0.0) return v;
-    return V - 1;
+    if (pick < 0) {
+        *flag |= OF_SAMPLE_NEAR;   /* rounding left t at the very end: the last positive token */
+        pick = lastpos >= 0 ? lastpos : V - 1;
+    }
+    if (lo < 0 || pick < lo) lo = pick;
+    if (hi < pick) hi = pick;
+    *win_lo = lo;
+    *win_hi = hi;
+    return pick;
 }
 
 void oracle_verify_chain(int bs, int V, double T,
@@ -610,14 +637,17 @@ void oracle_verify_chain(int bs, int V, double T,
                          const int32_t* tokens, const uint8_t* slot_flags, int ld, const int32_t* n_slots,
                          const float* u_acc, const float* u_smp,
                          int32_t* out_tokens, int32_t* out_num, int32_t* out_accepted,
-                         double* out_p, double* out_q, uint32_t* out_flags)
+                         double* out_p, double* out_q, uint32_t* out_flags,
+                         int32_t* out_win_lo, int32_t* out_win_hi)
 {
     for (int r = 0; r < bs; ++r) {
         int b = n_slots[r];
         uint32_t fl = out_flags[r];
         int32_t* ot = out_tokens + (int64_t)r * (ld + 1);
-        for (int i = 0; i <= ld; ++i) ot[i] = -1;
-        for (int i = 0; i < ld; ++i) { out_p[(int64_t)r * ld + i] = 0.0; out_q[(int64_t)r * ld + i] = 0.0; }
+        double* op = out_p + (int64_t)r * (ld + 1);
+        int64_t wlo = -1, whi = -1;
+        for (int i = 0; i <= ld; ++i) { ot[i] = -1; op[i] = 0.0; }
+        for (int i = 0; i < ld; ++i) out_q[(int64_t)r * ld + i] = 0.0;
         int rej = -1;        /* first rejected slot, -1 if none */
         row_stats rs_rej_t, rs_rej_d;
         int64_t off_rej_t = 0, off_rej_d = 0;
@@ -644,7 +674,7 @@ void oracle_verify_chain(int bs, int V, double T,
             } else {
                 p = (!bad && ts.arg == y) ? 1.0 : 0.0;
             }
-            out_p[(int64_t)r * ld + i] = p;
+            op[i] = p;
             out_q[(int64_t)r * ld + i] = q;
             if (rej >= 0) continue;   /* later slots: statistics only */
             int acc;
@@ -671,7 +701,7 @@ void oracle_verify_chain(int bs, int V, double T,
                               rej_pm ? 2 : 1, tokens[(int64_t)r * ld + rej], T };
                 int32_t yb = tokens[(int64_t)r * ld + rej];
                 if (rej_pm && (yb < 0 || yb >= V)) R.mode = 0;
-                last = (int32_t)draw(&R, V, (double)u_smp[r], &fl);
+                last = (int32_t)draw(&R, V, (double)u_smp[r], &fl, &wlo, &whi);
             } else {
                 last = (int32_t)rs_rej_t.arg;
             }
@@ -681,12 +711,18 @@ void oracle_verify_chain(int bs, int V, double T,
             if (!ts.finite) fl |= OF_BAD_LOGITS;
             if (T > 0.0) {
                 resid_t R = { logits, dtype, toff, ts, 0, 0, 0, ts, 0, -1, T };
-                last = (int32_t)draw(&R, V, (double)u_smp[r], &fl);
+                last = (int32_t)draw(&R, V, (double)u_smp[r], &fl, &wlo, &whi);
+                /* p of the bonus row at the bonus token */
+                if (ts.finite) op[b] = prob_of(logits, dtype, toff, ts, T, last);
             } else {
                 last = (int32_t)ts.arg;
+                if (ts.finite) op[b] = 1.0;   /* the argmax point mass */
             }
         }
         ot[nacc] = last;
+        if (wlo < 0) wlo = whi = last;   /* T = 0: the argmax, no window */
+        out_win_lo[r] = (int32_t)wlo;
+        out_win_hi[r] = (int32_t)whi;
         out_num[r] = nacc + 1;
         out_accepted[r] = nacc;
         out_flags[r] = fl;

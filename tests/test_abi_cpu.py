@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == set(L.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.spec_abi_version() == 4
+    assert lib.spec_abi_version() == 5
     assert lib.spec_strerror(-1).decode() == "invalid argument"
 
 

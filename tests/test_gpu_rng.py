@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 from oracle import oracle as O
-from tests.gpu_helpers import assert_close, assert_rows_equal, dev, excused_fraction, host, ok_rows
+from tests.gpu_helpers import check_verify_chain, dev, host
 from workloads import synth
 
 pytestmark = pytest.mark.gpu
@@ -33,9 +33,7 @@ def test_config0_rng_matches_oracle_and_explicit_uniforms():
     ref = O.verify_chain(c["target"].reshape(-1, V), np.arange(BS) * (B + 1), c["tokens"], np.zeros((BS, B), np.uint8),
                          np.full(BS, B, np.int32), u_acc, u_smp, 1.0, draft_logits=c["draft"].reshape(-1, V),
                          draft_row_base=np.arange(BS) * B)
-    ok = ok_rows(ref["flags"])
-    assert_rows_equal(host(g["out_tokens"]), ref["out_tokens"], ok, "out_tokens")
-    assert_close(host(g["out_p"]), ref["out_p"], "out_p")
+    check_verify_chain({k: host(v) for k, v in g.items()}, ref, np.full(BS, B), "config 0 rng")
     assert np.array_equal(host(hist), np.bincount(host(g["out_accepted"]), minlength=B + 1))
 
 
@@ -59,11 +57,8 @@ def test_dense_headline_rng_and_histogram():
     ref = O.verify_chain(c["target_bf16"].reshape(-1, V), np.arange(BS) * (B + 1), c["tokens"],
                          np.zeros((BS, B), np.uint8), np.full(BS, B, np.int32), u_acc, u_smp, 1.0,
                          draft_logits=c["draft_bf16"].reshape(-1, V), draft_row_base=np.arange(BS) * B)
-    ok = ok_rows(ref["flags"])
-    assert_rows_equal(host(g["out_tokens"]), ref["out_tokens"], ok, "out_tokens")
-    assert_rows_equal(host(g["out_num"]), ref["out_num"], ok, "out_num")
-    assert_close(host(g["out_p"]), ref["out_p"], "out_p")
+    check_verify_chain({k: host(v) for k, v in g.items()}, ref, np.full(BS, B), "dense rng")
     h = host(hist)
     assert h.sum() == BS and np.array_equal(h, np.bincount(host(g["out_accepted"]), minlength=B + 1))
     assert not np.array_equal(host(g["out_tokens"]), host(g2["out_tokens"]))
-    print(f"  accepted per request {host(g['out_accepted']).mean():.2f}, excused {excused_fraction(ref['flags']):.3f}")
+    print(f"  accepted per request {host(g['out_accepted']).mean():.2f}")

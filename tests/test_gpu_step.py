@@ -4,7 +4,8 @@ import numpy as np
 import pytest
 
 from oracle import oracle as O
-from tests.gpu_helpers import assert_close, assert_rows_equal, dev, excused_fraction, host, ok_rows
+from tests.gpu_helpers import (assert_close, assert_rows_equal, check_verify_chain, dev, expected_commit, host,
+                               ok_rows)
 from workloads import synth
 
 pytestmark = pytest.mark.gpu
@@ -42,16 +43,19 @@ def test_full_step_matches_oracle(cfg):
                      c["target_bf16"].reshape(-1, c["V"]), np.arange(c["BS"]) * 16, c["u_acc"], c["u_smp"],
                      c["temperature"], c["n_min"], c["n_max"], 15, 256)
     assert np.array_equal(g["draft"], o["draft"]) and np.array_equal(g["feat"], o["feat"])
-    ok = ok_rows(o["verify"]["flags"])
+    ok = ok_rows(o["alloc"]["flags"])   # selection and allocation near ties
     for k in ("chain_tokens", "alloc_len", "chain_src"):
         ref = o["alloc"]["tokens" if k == "chain_tokens" else k]
         assert_rows_equal(g[k], ref, ok, k)
     assert_close(g["survival"], o["alloc"]["S"], "survival")
-    for k in ("out_tokens", "out_num"):
-        assert_rows_equal(g[k], o["verify"][k], ok, k)
-    assert_rows_equal(g["ctx"], o["ctx"], ok, "ctx after commit")
-    assert_rows_equal(g["ctx_len"], o["ctx_len"], ok, "ctx_len after commit")
-    print(f"  emitted mean {o['verify']['out_num'].mean():.2f}, excused {excused_fraction(o['verify']['flags']):.3f}")
+    full = check_verify_chain(g, o["verify"], o["alloc"]["alloc_len"], f"c{cfg} step")
+    # the commit of the GPU's own emitted tokens, for every request
+    ctx2, len2, fl = expected_commit(c["ctx"], c["ctx_len"], c["ctx"].shape[1], g["out_tokens"], g["out_num"])
+    assert np.array_equal(g["ctx"], ctx2) and np.array_equal(g["ctx_len"], len2)
+    # and for the requests whose emitted tokens are the oracle's, its own commit
+    same = ~full & np.all(g["out_tokens"] == o["verify"]["out_tokens"], axis=1)
+    assert_rows_equal(g["ctx"], o["ctx"], same, "ctx after commit")
+    print(f"  emitted mean {o['verify']['out_num'].mean():.2f}, excused {int(full.sum())}")
 
 
 def test_step_is_bit_identical_run_to_run():

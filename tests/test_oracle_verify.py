@@ -225,3 +225,72 @@ def test_edge_cases_zero_slots_bad_token_commit():
     ctx2, len2 = O.commit(ctx, ctx_len, 6, out, np.array([2, 2], np.int32), fl)
     assert list(len2) == [4, 5] and list(ctx2[0, 2:4]) == [7, 8]
     assert fl[1] & O.CTX_OVERFLOW and not fl[0] & O.CTX_OVERFLOW
+
+
+def _draw_windows(z, u, T, seed):
+    """Bonus draws (no slots) from rows z [n, V] with uniforms u [n]."""
+    n, V = z.shape
+    res = O.verify_chain(z.astype(np.float32), np.arange(n), np.zeros((n, 1), np.int32), np.ones((n, 1), np.uint8),
+                         np.zeros(n, np.int32), np.zeros((n, 1), np.float32), u.astype(np.float32), T)
+    return res
+
+
+def test_tie_window_holds_every_nearby_draw():
+    """The draw's tie window (the tokens whose CDF interval meets the band of
+    1e-6 W around u'W) is one token away from near ties and, at a near tie,
+    holds the token picked by every inverse-CDF draw whose running sums
+    differ from the oracle's by less than the band: here float32 running
+    sums, sums in reversed chunk order and weights perturbed by 1e-9."""
+    rng = np.random.Generator(np.random.Philox(41))
+    n, V, T = 400, 40, 1.0
+    z = (rng.standard_normal((n, V)) * 2).astype(np.float32)
+    P = softmax_rows(z, T)
+    cdf = np.cumsum(P, axis=1)
+    # half the uniforms sit on a CDF boundary (to fp32 precision), half anywhere
+    k = rng.integers(1, V - 1, n)
+    u = np.where(np.arange(n) % 2 == 0, cdf[np.arange(n), k - 1] / cdf[:, -1], rng.random(n)).astype(np.float32)
+    res = _draw_windows(z, u, T, 41)
+    tok, lo, hi = res["out_tokens"][:, 0], res["win_lo"], res["win_hi"]
+    near = (res["flags"] & O.SAMPLE_NEAR) != 0
+    assert near[0::2].mean() > 0.9                       # boundary uniforms are near ties
+    assert np.all(lo <= tok) and np.all(tok <= hi)
+    assert np.array_equal(lo[~near], tok[~near]) and np.array_equal(hi[~near], tok[~near])
+    assert np.all(hi[near] > lo[near])                   # a boundary window spans both sides
+    for r in range(n):
+        t = float(u[r])
+        picks = []
+        w = P[r].astype(np.float32)
+        picks.append(int(np.searchsorted(np.cumsum(w, dtype=np.float32), t * w.sum(dtype=np.float32), "right")))
+        wr = P[r] * (1 + 1e-9 * rng.standard_normal(V))
+        picks.append(int(np.searchsorted(np.cumsum(wr), t * wr.sum(), "right")))
+        chunks = np.array_split(P[r], 5)
+        run = np.concatenate([np.cumsum(c) + sum(x.sum() for x in chunks[:i]) for i, c in enumerate(chunks)])
+        picks.append(int(np.searchsorted(run, t * sum(c.sum() for c in reversed(chunks)), "right")))
+        for p in picks:
+            p = min(p, V - 1)
+            assert lo[r] <= p <= hi[r], (r, p, lo[r], hi[r])
+
+
+def test_bonus_row_probability():
+    """out_p's column b is p of the bonus row at the bonus token (a library
+    softmax) when every slot passed, 1 at T = 0, and 0 after a rejection."""
+    rng = np.random.Generator(np.random.Philox(42))
+    n, V, B = 60, 300, 3
+    z = (rng.standard_normal((n, B + 1, V)) * 2).astype(np.float32)
+    y = rng.integers(0, V, (n, B)).astype(np.int32)
+    y[: n // 2] = np.argmax(z[: n // 2, :B], -1)       # greedy drafts: accepted at T = 0
+    u_acc = np.where(np.arange(n)[:, None] < n // 2, 0.0, rng.random((n, B))).astype(np.float32)
+    u_smp = rng.random(n, dtype=np.float32)
+    for T in (0.0, 0.9):
+        res = O.verify_chain(z.reshape(-1, V), np.arange(n) * (B + 1), y, np.ones((n, B), np.uint8),
+                             np.full(n, B, np.int32), u_acc, u_smp, T)
+        P = softmax_rows(z[:, B], T) if T > 0 else None
+        for r in range(n):
+            a = res["out_accepted"][r]
+            if a < B:
+                assert res["out_p"][r, B] == 0.0
+            elif T == 0:
+                assert res["out_p"][r, B] == 1.0
+            else:
+                assert res["out_p"][r, B] == pytest.approx(P[r, res["out_tokens"][r, B]], rel=1e-12)
+        assert (res["out_accepted"] == B).sum() >= n // 2
