@@ -108,7 +108,9 @@ STRUCTS = {"spec_cost_model": CostModel, "spec_tree_scores": TreeScores, "spec_n
            "spec_tree_alloc": TreeAlloc, "spec_alloc_args": AllocArgs, "spec_verify_args": VerifyArgs,
            "spec_tree_verify_args": TreeVerifyArgs}
 EXPORTS = ("spec_size_budget", "spec_ngram_draft", "spec_allocate_budget", "spec_verify_chain", "spec_verify_tree",
-           "spec_workspace_bytes", "spec_strerror", "spec_last_hip_error", "spec_abi_version")
+           "spec_verify_chain_noalloc", "spec_workspace_bytes", "spec_strerror", "spec_last_hip_error",
+           "spec_abi_version")
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 def load(path: str = LIB_PATH) -> C.CDLL:
@@ -116,7 +118,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         raise ImportError(f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
                           "(the HIP path has no fallback)")
     lib = C.CDLL(path)
-    for name in ("spec_ngram_draft", "spec_allocate_budget", "spec_verify_chain", "spec_verify_tree"):
+    for name in ("spec_ngram_draft", "spec_allocate_budget", "spec_verify_chain", "spec_verify_tree",
+                 "spec_verify_chain_noalloc"):
         getattr(lib, name).argtypes = [vp, vp]
         getattr(lib, name).restype = C.c_int
     lib.spec_workspace_bytes.argtypes = [C.c_int, vp]
@@ -393,7 +396,7 @@ def spec_verify_chain(logits, row_base, tokens, n_slots, temperature, u_accept=N
                       slot_flags=None, draft_logits=None, draft_row_base=None, out_flags=None,
                       ctx=None, ctx_len=None, ctx_cap=None, ctx_len_out=None, out=None, workspace=None,
                       stream=None, prof_events=None, max_slots=0, write_flags=False, ngram=None, ngram_out=None,
-                      rng=None, accept_hist=None, residual_wait=0):
+                      rng=None, accept_hist=None, residual_wait=0, noalloc=False):
     """Rejection-sampling verification of one chain per request (optional commit into ctx).
     ``prof_events``: optional pair of raw hipEvent_t handles recorded around the
     row-statistics pass.  ``max_slots``: optional bound of the total slots
@@ -409,7 +412,10 @@ def spec_verify_chain(logits, row_base, tokens, n_slots, temperature, u_accept=N
     optional int32 [ld + 1] device tensor, increased at each request's
     accepted count.  ``residual_wait``: polls of a published residual sum
     before the drawing workgroup sums the residual itself (0 = the library's
-    default; negative = at once, which tests the fallback)."""
+    default; negative = at once, which tests the fallback).  ``noalloc``: call
+    spec_verify_chain_noalloc, whose scratch is the library's own per-device
+    array (no workspace is allocated or passed; pass ``out`` and
+    ``out_flags`` for a call that allocates nothing at all)."""
     lg = _rows2d(logits, "logits")
     _dev(row_base, torch.int64, "row_base", 1)
     _dev(tokens, torch.int32, "tokens", 2)
@@ -474,10 +480,13 @@ def spec_verify_chain(logits, row_base, tokens, n_slots, temperature, u_accept=N
         a.ngram_n_min, a.ngram_n_max, a.ngram_max_draft, a.ngram_copy_cap = n_min, n_max, max_draft, copy_cap
     if prof_events is not None:
         a.prof_begin, a.prof_end = prof_events
-    ws, w = _workspace(OP_VERIFY_CHAIN, a, dev, workspace, stream)
-    if w:
-        a.workspace, a.workspace_bytes = w
-    _check(lib().spec_verify_chain(C.byref(a), _stream(dev, stream)))
+    if noalloc:
+        _check(lib().spec_verify_chain_noalloc(C.byref(a), _stream(dev, stream)))
+    else:
+        ws, w = _workspace(OP_VERIFY_CHAIN, a, dev, workspace, stream)
+        if w:
+            a.workspace, a.workspace_bytes = w
+        _check(lib().spec_verify_chain(C.byref(a), _stream(dev, stream)))
     if ngram is not None:
         out["ngram_draft"], out["ngram_len"], out["ngram_feat"] = ngram_out
     return out

@@ -10,6 +10,7 @@ size_t spec_alloc_ws(const spec_alloc_args* a);
 int spec_alloc_launch(const spec_alloc_args* a, hipStream_t st);
 size_t spec_verify_chain_ws(int32_t bs, int32_t vocab, int32_t ld, int32_t dtype);
 int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st);
+int spec_verify_chain_noalloc_launch(const spec_verify_args* a, hipStream_t st);
 size_t spec_verify_tree_ws(int32_t bs, int32_t vocab, int32_t rows_max, int32_t dtype);
 int spec_verify_tree_launch(const spec_tree_verify_args* a, hipStream_t st);
 
@@ -203,6 +204,13 @@ int spec_verify_chain(const spec_verify_args* a, void* stream)
     rc = check_workspace(a->workspace, a->workspace_bytes, spec_verify_chain_ws(a->bs, a->vocab, a->ld, a->dtype));
     if (rc) return rc;
     return spec_verify_chain_launch(a, (hipStream_t)stream);
+}
+
+int spec_verify_chain_noalloc(const spec_verify_args* a, void* stream)
+{
+    int rc = check_verify(a);
+    if (rc) return rc;
+    return spec_verify_chain_noalloc_launch(a, (hipStream_t)stream);
 }
 
 int spec_verify_tree(const spec_tree_verify_args* a, void* stream)

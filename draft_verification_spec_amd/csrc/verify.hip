@@ -36,9 +36,8 @@
 //   k_tree_walk  : trees (T = 0): the argmax of every row, the accepted path
 //                  and its commit, one wave per request.
 #include <algorithm>
+#include <atomic>
 #include <mutex>
-#include <utility>
-#include <vector>
 
 #include "common.hpp"
 #include "ngram_scan.hpp"
@@ -2129,12 +2128,19 @@ static int64_t stats_items(int32_t bs, int rows_per_req_max, const RowSplit& sp)
     return (int64_t)bs * rows_per_req_max * sp.splits;
 }
 
+// The only state the library keeps between calls: caches of device
+// properties that never change while the process runs (compute units per
+// device, workgroups per compute unit per kernel), filled on first use under
+// a lock, in fixed-size tables (no heap allocation on any launch path).
+static std::mutex g_cache_mu;
+
 // Compute units of the current device (cached per device).
 static int device_cus()
 {
     static int cus[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lock(g_cache_mu);
     if (cus[dev] == 0) {
         int n = 0;
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
@@ -2144,17 +2150,22 @@ static int device_cus()
 }
 
 // Workgroups of `block` threads that one compute unit holds at once (cached
-// per kernel).
+// per kernel; the kernels' resource use is the same on every gfx950 device).
 static int blocks_per_cu(const void* kernel, int block)
 {
-    static std::mutex mu;
-    static std::vector<std::pair<const void*, int>> cache;
-    std::lock_guard<std::mutex> lock(mu);
-    for (const auto& e : cache)
-        if (e.first == kernel) return e.second;
+    static const void* keys[256];
+    static int vals[256];
+    static int used = 0;
+    std::lock_guard<std::mutex> lock(g_cache_mu);
+    for (int i = 0; i < used; ++i)
+        if (keys[i] == kernel) return vals[i];
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, block, 0) != hipSuccess || n <= 0) n = 1;
-    cache.emplace_back(kernel, n);
+    if (used < 256) {
+        keys[used] = kernel;
+        vals[used] = n;
+        ++used;
+    }
     return n;
 }
 
@@ -2459,4 +2470,57 @@ int spec_verify_tree_launch(const spec_tree_verify_args* a, hipStream_t st)
                  a->rows_max, 0, (int64_t)a->bs * a->rows_max, sp, gpre, L);
     hipLaunchKernelGGL(k_tree_walk, dim3(a->bs), dim3(kWave), 0, st, P);
     return spec_record_hip_error(hipGetLastError());
+}
+
+// ---------------------------------------------------------------------------
+// the chain verifier without a caller workspace
+// ---------------------------------------------------------------------------
+
+// Scratch of spec_verify_chain_noalloc: one array per device, held from the
+// library's first use on the device until the process ends.  Host code never
+// passes `scratch` itself to a kernel (on the host the name is a stand-in,
+// not a device address): it uses the device address looked up once per
+// device below.
+static __device__ __align__(256) unsigned char scratch[SPEC_NOALLOC_SCRATCH_BYTES];
+
+static std::atomic<void*> g_scratch_ptr[64];
+
+// Device address of `scratch` on the current device: hipGetSymbolAddress on
+// the first call on a device (with that device current), then the kept value.
+static int scratch_address(void** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return spec_record_hip_error(e);
+    if (dev < 0 || dev >= 64) return SPEC_EINVAL;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_cache_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return spec_record_hip_error(e);
+            if (!p) return spec_record_hip_error(hipErrorInvalidSymbol);
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return SPEC_OK;
+}
+
+// The scratch the verifier needs (partials, row prefix and plan, residual
+// sums and counters) comes from the device array; every part that must start
+// at a known value is set by the call's own kernels (the statistics pass
+// resets the residual counters and sums), so nothing is cleared here.
+int spec_verify_chain_noalloc_launch(const spec_verify_args* a, hipStream_t st)
+{
+    const size_t need = spec_verify_chain_ws(a->bs, a->vocab, a->ld, a->dtype);
+    if (need > (size_t)SPEC_NOALLOC_SCRATCH_BYTES) return SPEC_EWORKSPACE;
+    void* ws = nullptr;
+    const int rc = scratch_address(&ws);
+    if (rc != SPEC_OK) return rc;
+    spec_verify_args b = *a;
+    b.workspace = ws;
+    b.workspace_bytes = (size_t)SPEC_NOALLOC_SCRATCH_BYTES;
+    return spec_verify_chain_launch(&b, st);
 }

@@ -16,9 +16,13 @@
  * ---------------------------------------
  * - Pointers marked "device" are HIP device (or managed) memory; everything
  *   else is host memory read during the call.  The caller owns every buffer.
- *   The library keeps no state between calls and allocates nothing: scratch
- *   memory comes from the caller's `workspace` (query its size with
- *   spec_workspace_bytes; any alignment of 256 bytes is enough).
+ *   The library allocates nothing: scratch memory comes from the caller's
+ *   `workspace` (query its size with spec_workspace_bytes; any alignment of
+ *   256 bytes is enough), or for spec_verify_chain_noalloc from a fixed array
+ *   per device.  Its only state between calls: caches of device properties
+ *   that do not change while the process runs (compute units per device,
+ *   resident workgroups per kernel, that array's device address), filled
+ *   once under a lock.
  * - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *   and the call returns at once.  The library never synchronises, never
  *   copies device to host and never calls hipDeviceSynchronize, so a whole
@@ -470,6 +474,23 @@ int spec_ngram_draft(const spec_ngram_args* args, void* stream);
 int spec_allocate_budget(const spec_alloc_args* args, void* stream);
 int spec_verify_chain(const spec_verify_args* args, void* stream);
 int spec_verify_tree(const spec_tree_verify_args* args, void* stream);
+
+/* ========================================================================
+ * spec_verify_chain_noalloc -- spec_verify_chain for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, outputs and kernels;
+ * args->workspace and workspace_bytes are ignored: the scratch comes from one
+ * array of SPEC_NOALLOC_SCRATCH_BYTES per device inside the library, which
+ * the device holds from the first call until the process ends.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ * Returns SPEC_EWORKSPACE when the call needs more scratch than that (see
+ * spec_workspace_bytes(SPEC_OP_VERIFY_CHAIN, args)), else as
+ * spec_verify_chain.  All calls on one device share its array: calls that
+ * may overlap on a device (other streams, other threads) race and must be
+ * ordered by the caller; consecutive calls on one stream are safe.
+ * ======================================================================== */
+#define SPEC_NOALLOC_SCRATCH_BYTES (16u << 20)
+int spec_verify_chain_noalloc(const spec_verify_args* args, void* stream);
 
 /* Workspace bytes the call with these arguments needs (0 = none); a host-only
  * query that reads sizes from args and never touches device memory. */
