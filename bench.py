@@ -10,18 +10,23 @@ context, then the n-gram draft over the updated contexts, fused into the same
 call (synthetic, seeded; see workloads/synth.py).  The commit writes the new
 lengths to a separate buffer, so every timed step does the same work.
 
-A second record times the batch-allocation step (n-gram draft -> chain
-selection and budget allocation of 256 slots -> verification -> commit) at
-BS 128 with the same timing, a third the tree step (n-gram chains -> tree
-build with the Eq. (6) scores -> greedy verification -> commit) at BS 64, a
-fourth the same allocation step on the large-batch stress workload (BS 256,
-32,768-token contexts, budget 512, T = 0.7).
+Further records: the batch-allocation step (n-gram draft -> chain selection
+and budget allocation of 256 slots -> verification -> commit) at BS 128; the
+tree step (n-gram chains -> tree build with the Eq. (6) scores -> greedy
+verification -> commit) at BS 64; the same allocation step on the
+large-batch stress workload (BS 256, 32,768-token contexts, budget 512,
+T = 0.7); the reported step with fp32 rows; a plain device copy (the
+achievable HBM rate in the same run); and the CPU oracle on the reported
+step's inputs, on one host core and on all of them.  The secondary records
+run first, the reported step last.
 
-Timing, per workload, on one stream: K eager steps with an event pair
-attached to the dispatch of every statistics kernel (that kernel's live
-average duration), then the K steps captured in one HIP graph (checked
-against the eager step first) replayed once between two events, which gives
-the throughput.  Prints one JSON line.
+Timing, per workload, on one stream: W warm-up steps, K eager steps with an
+event pair attached to the dispatch of every statistics kernel (that
+kernel's live average duration), then the K steps captured in one HIP graph
+(checked against the eager step first), W warm-up replays and one timed
+replay of the K-step graph between two events, which gives the throughput;
+then K replays of a one-step graph, each between two events, which give the
+p10 / p50 / p90 of the step time.  Prints one JSON line.
 """
 import argparse
 import ctypes as C
@@ -54,6 +59,8 @@ def parse():
     p.add_argument("--no-budget", action="store_true", help="skip the batch-allocation step record")
     p.add_argument("--no-tree", action="store_true", help="skip the tree step record")
     p.add_argument("--no-stress", action="store_true", help="skip the large-batch stress step record")
+    p.add_argument("--no-fp32", action="store_true", help="skip the fp32 record of the reported step")
+    p.add_argument("--no-ceiling", action="store_true", help="skip the device-copy ceiling record")
     p.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -116,40 +123,103 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 10}), flush=True)
 
 
-def cpu_baseline(c, sample=32, budget_s=12.0):
-    """The oracle, as it stands, on the first `sample` requests of the dense
-    step's inputs (verify, commit, n-gram draft), repeated until about
-    budget_s seconds of CPU work; scaled to whole BS-128 steps per second."""
+def cpu_threads():
+    """Host cores this process may use (its affinity, capped by OMP_NUM_THREADS when set)."""
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(c, reps=3):
+    """The oracle, as it stands, on the whole reported step (BS 128: draw the
+    uniforms, verify every request, commit, n-gram draft of the committed
+    contexts) on the same inputs as the GPU: single-threaded, and with the
+    requests split over every host core this process may use (threads; the
+    oracle's C calls release the GIL).  Median of `reps` runs of each."""
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
     from oracle import oracle as O
     O.build()
     BS, V, B = c["BS"], c["V"], c["B"]
-    m = min(sample, BS)
-    tgt = c["target_bf16"][:m].reshape(-1, V)
-    dft = c["draft_bf16"][:m].reshape(-1, V)
-    n, t0 = 0, time.perf_counter()
-    while True:
-        u_acc, u_smp = O.step_uniforms(m, B, *RNG)
-        o = O.verify_chain(tgt, np.arange(m) * (B + 1), c["tokens"][:m], np.zeros((m, B), np.uint8),
-                           np.full(m, B, np.int32), u_acc, u_smp, c["temperature"],
-                           draft_logits=dft, draft_row_base=np.arange(m) * B)
-        ctx, ctx_len = O.commit(c["ctx"][:m].copy(), c["ctx_len"][:m].copy(), c["ctx"].shape[1], o["out_tokens"],
+    tgt = c["target_bf16"].reshape(-1, V)
+    dft = c["draft_bf16"].reshape(-1, V)
+    T_ctx = c["ctx"].shape[1]
+
+    def part(lo, hi, u_acc, u_smp):
+        n = hi - lo
+        o = O.verify_chain(tgt[lo * (B + 1):hi * (B + 1)], np.arange(n) * (B + 1), c["tokens"][lo:hi],
+                           np.zeros((n, B), np.uint8), np.full(n, B, np.int32), u_acc[lo:hi], u_smp[lo:hi],
+                           c["temperature"], draft_logits=dft[lo * B:hi * B], draft_row_base=np.arange(n) * B)
+        ctx, ctx_len = O.commit(c["ctx"][lo:hi].copy(), c["ctx_len"][lo:hi].copy(), T_ctx, o["out_tokens"],
                                 o["out_num"], o["flags"])
         O.ngram_draft(ctx, ctx_len, c["n_min"], c["n_max"], c["max_draft"], c["copy_cap"])
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= 200:
-            break
-    return {"value": n * m / BS / el, "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} runs of the dense step over the first {m} of {BS} requests (uniforms, verify, commit, "
-                      f"n-gram draft; single-threaded C oracle, fp64) in {el:.1f} s, scaled by {m}/{BS}"}
+
+    def step(threads):
+        t0 = time.perf_counter()
+        u_acc, u_smp = O.step_uniforms(BS, B, *RNG)
+        if threads == 1:
+            part(0, BS, u_acc, u_smp)
+        else:
+            cuts = np.linspace(0, BS, threads + 1).astype(int)
+            with ThreadPoolExecutor(threads) as ex:
+                list(ex.map(lambda i: part(cuts[i], cuts[i + 1], u_acc, u_smp), range(threads)))
+        return time.perf_counter() - t0
+
+    n = cpu_threads()
+    one = sorted(step(1) for _ in range(reps))[reps // 2]
+    alln = sorted(step(n) for _ in range(reps))[reps // 2]
+    return {"value": 1.0 / alln, "unit": "steps/s", "cores": n, "kind": "oracle",
+            "sample": f"the whole reported step (BS {BS}: uniforms, verify, commit, n-gram draft; C oracle, fp64), "
+                      f"requests split over {n} threads; median of {reps} runs",
+            "cpu_model": cpu_model(), "ms_per_step": alln * 1e3,
+            "single_core": {"value": 1.0 / one, "unit": "steps/s", "cores": 1, "ms_per_step": one * 1e3}}
+
+
+def copy_ceiling(hip, nbytes=1 << 30, reps=5):
+    """A plain device-to-device copy of nbytes (torch), timed with events:
+    bytes read plus written per second, the achievable HBM rate of a
+    streaming kernel on this GPU in this run."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = hip.event(), hip.event()
+    for _ in range(3):
+        dst.copy_(src)
+    ms = []
+    for _ in range(reps):
+        hip.record(e0, stream)
+        dst.copy_(src)
+        hip.record(e1, stream)
+        ms.append(hip.ms(e0, e1))
+    ms.sort()
+    med = ms[reps // 2]
+    return {"kind": "device copy (torch)", "bytes_moved": 2 * nbytes, "ms": med,
+            "GBps": 2 * nbytes / (med * 1e-3) / 1e9, "frac": 2 * nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBPS}
 
 
 def run_timed(step, outputs, K, W, hip, stream, eager_only=False):
-    """Times `step` (already run once, so its buffers exist): K eager steps
-    with the statistics kernel's event pair attached to its dispatch, then K
-    steps in one HIP graph, replayed once.  Every timed region's outputs must
-    equal the reference step's."""
+    """Times `step` (already run once, so its buffers exist).  The graphs are
+    captured first, so that the timed regions follow each other with no host
+    work between them: W eager warm-up steps, K eager steps with the
+    statistics kernel's event pair attached to its dispatch, W warm-up
+    replays of a one-step graph, one replay of a K-step graph between two
+    events (the throughput), and K one-step replays each between two events
+    (the step-time distribution).  Afterwards every region's outputs must
+    equal the reference step's, and the one-step graph is replayed three more
+    times with eager steps in between, each checked."""
     import numpy as np
     import torch
     with torch.cuda.stream(stream):
@@ -158,6 +228,8 @@ def run_timed(step, outputs, K, W, hip, stream, eager_only=False):
         ref = [t.cpu().clone() for t in outputs()]
     ev_b = [hip.event() for _ in range(K)]
     ev_e = [hip.event() for _ in range(K)]
+    pb = [hip.event() for _ in range(K)]
+    pe = [hip.event() for _ in range(K)]
     t0, t1, t2, t3 = (hip.event() for _ in range(4))
     s = stream.cuda_stream
 
@@ -165,19 +237,7 @@ def run_timed(step, outputs, K, W, hip, stream, eager_only=False):
         for i, (a, b) in enumerate(zip(outputs(), ref)):
             assert torch.equal(a.cpu(), b), f"{tag}: output {i} differs from the reference step"
 
-    with torch.cuda.stream(stream):
-        for _ in range(W):
-            step()
-        torch.cuda.synchronize()
-        hip.record(t0, s)
-        for k in range(K):
-            step(prof=(ev_b[k], ev_e[k]))
-        hip.record(t1, s)
-        torch.cuda.synchronize()
-    eager_ms = hip.ms(t0, t1)
-    stats_ms = [hip.ms(a, b) for a, b in zip(ev_b, ev_e)]
-    same("eager timed steps")
-    mode, total_ms = "eager", eager_ms
+    g1 = gK = None
     if not eager_only:
         try:
             g1 = torch.cuda.CUDAGraph()
@@ -187,32 +247,53 @@ def run_timed(step, outputs, K, W, hip, stream, eager_only=False):
             with torch.cuda.graph(gK, stream=stream):
                 for _ in range(K):
                     step()
-            for rep in range(3):   # every replay equals the eager step, with eager work in between
-                g1.replay()
-                torch.cuda.synchronize()
-                same(f"graph replay {rep}")
-                with torch.cuda.stream(stream):
-                    step()
-                torch.cuda.synchronize()
-            with torch.cuda.stream(stream):
-                for _ in range(W):
-                    g1.replay()
-                torch.cuda.synchronize()
-                hip.record(t2, s)
-                gK.replay()
-                hip.record(t3, s)
-                torch.cuda.synchronize()
-            total_ms = hip.ms(t2, t3)
-            same("graph timed steps")
-            mode = "graph"
         except Exception as e:  # capture unsupported here: keep the eager region's figure
             print(f"[bench] graph capture failed ({e}); reporting the eager region", file=sys.stderr, flush=True)
-    return {"mode": mode, "ms_per_step": total_ms / K, "steps_per_s": K / (total_ms * 1e-3),
-            "eager_ms_per_step": eager_ms / K, "stats_ms": float(np.mean(stats_ms))}
+            g1 = gK = None
+    with torch.cuda.stream(stream):
+        for _ in range(W):
+            step()
+        hip.record(t0, s)
+        for k in range(K):
+            step(prof=(ev_b[k], ev_e[k]))
+        hip.record(t1, s)
+        if gK is not None:
+            for _ in range(W):
+                g1.replay()
+            hip.record(t2, s)
+            gK.replay()
+            hip.record(t3, s)
+            for k in range(K):
+                hip.record(pb[k], s)
+                g1.replay()
+                hip.record(pe[k], s)
+        torch.cuda.synchronize()
+    eager_ms = hip.ms(t0, t1)
+    stats_ms = [hip.ms(a, b) for a, b in zip(ev_b, ev_e)]
+    out = {"mode": "eager", "ms_per_step": eager_ms / K, "steps_per_s": K / (eager_ms * 1e-3),
+           "eager_ms_per_step": eager_ms / K, "stats_ms": float(np.mean(stats_ms))}
+    if gK is not None:
+        total_ms = hip.ms(t2, t3)
+        per_ms = [hip.ms(a, b) for a, b in zip(pb, pe)]
+        p10, p50, p90 = (float(np.percentile(per_ms, q)) for q in (10, 50, 90))
+        out.update(mode="graph", ms_per_step=total_ms / K, steps_per_s=K / (total_ms * 1e-3),
+                   step_ms_percentiles={"p10": p10, "p50": p50, "p90": p90, "steps": len(per_ms),
+                                        "of": "single-step graph replays, each between two events"})
+    same("timed steps")
+    if g1 is not None:
+        for rep in range(3):   # every replay equals the eager step, with eager work in between
+            g1.replay()
+            torch.cuda.synchronize()
+            same(f"graph replay {rep}")
+            with torch.cuda.stream(stream):
+                step()
+            torch.cuda.synchronize()
+    return out
 
 
-def headline(K, W, hip, eager_only):
-    """The dense verify + commit + n-gram draft step (the reported one)."""
+def headline(K, W, hip, eager_only, fp32=False):
+    """The dense verify + commit + n-gram draft step (the reported one); with
+    fp32 the same rows stored as fp32 (the bf16 values upcast exactly)."""
     import numpy as np
     import torch
     import draft_verification_spec_amd as S
@@ -223,6 +304,8 @@ def headline(K, W, hip, eager_only):
     g = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     target = synth.as_torch_bf16(c["target_bf16"]).to(dev).reshape(-1, V)
     draft = synth.as_torch_bf16(c["draft_bf16"]).to(dev).reshape(-1, V)
+    if fp32:
+        target, draft = target.float(), draft.float()
     rb, drb = g(np.arange(BS, dtype=np.int64) * (B + 1)), g(np.arange(BS, dtype=np.int64) * B)
     tokens, flags = g(c["tokens"]), g(np.zeros((BS, B), np.uint8))
     n_slots = g(np.full(BS, B, np.int32))
@@ -250,16 +333,19 @@ def headline(K, W, hip, eager_only):
     with torch.cuda.stream(stream):
         step()
     outputs = lambda: list(bufs["vf"].values()) + [bufs["vfl"], ctx_len_new, ctx] + list(bufs["ng"])
-    t = run_timed(step, outputs, K, W, hip, stream, eager_only)
-    # acceptance of the timed eager steps (the histogram is fed only there)
-    h = bufs["hist"].cpu().numpy().astype(np.float64)
-    al = float((h * np.arange(B + 1)).sum() / h.sum())
-    t.update(acceptance={"accepted_per_request": al, "tokens_per_request_step": al + 1.0,
-                         "histogram": [int(x) for x in h / max(1, K)]})
-    rows_bytes = BS * (2 * B + 1) * V * 2                # every verified target and draft row, bf16
-    ctx_bytes = int(c["ctx_len"].sum()) * 4
-    t.update(c=c, rows_bytes=rows_bytes, ctx_bytes=ctx_bytes, BS=BS, V=V, B=B, T_ctx=int(c["ctx"].shape[1] - 64))
-    return t
+
+    def measure():
+        t = run_timed(step, outputs, K, W, hip, stream, eager_only)
+        # acceptance of the timed eager steps (the histogram is fed only there)
+        h = bufs["hist"].cpu().numpy().astype(np.float64)
+        al = float((h * np.arange(B + 1)).sum() / h.sum())
+        t.update(acceptance={"accepted_per_request": al, "tokens_per_request_step": al + 1.0,
+                             "histogram": [int(x) for x in h / max(1, K)]})
+        rows_bytes = BS * (2 * B + 1) * V * (4 if fp32 else 2)   # every verified target and draft row
+        ctx_bytes = int(c["ctx_len"].sum()) * 4
+        t.update(c=c, rows_bytes=rows_bytes, ctx_bytes=ctx_bytes, BS=BS, V=V, B=B, T_ctx=int(c["ctx"].shape[1] - 64))
+        return t
+    return measure
 
 
 def budget_step(K, W, hip, eager_only, config=2):
@@ -328,8 +414,11 @@ def budget_step(K, W, hip, eager_only, config=2):
     total_rows = int(bufs["al"]["total_rows"].item())
     surv = bufs["al"]["survival"].cpu().numpy().ravel()   # the host copy the next step's sizing reads
     outputs = lambda: list(bufs["vf"].values()) + [bufs["al"]["out_flags"], ctx_len_new, ctx] + list(bufs["ng"])
-    t = run_timed(step, outputs, K, W, hip, stream, eager_only)
-    sizing = host_sizing(S, surv, BS)
+    return lambda: _budget_result(run_timed(step, outputs, K, W, hip, stream, eager_only), S, surv, BS, V,
+                                  total_rows, c, config)
+
+
+def _budget_result(t, S, surv, BS, V, total_rows, c, config):
     rows_bytes = total_rows * V * 2
     step_bytes = rows_bytes + int(c["ctx_len"].sum()) * 4
     workload = ("batch budget allocation + verify + commit + n-gram draft: BS=128, V=151936, model chain "
@@ -340,12 +429,14 @@ def budget_step(K, W, hip, eager_only, config=2):
                 "Table 5 estimator, budget 512, lambda 0.309, bf16 target rows, T=0.7")
     return {"workload": workload,
             "timing": t["mode"], "steps_per_s": t["steps_per_s"], "ms_per_step": t["ms_per_step"],
+            "step_ms_percentiles": t.get("step_ms_percentiles"),
             "verified_rows_per_step": total_rows, "algorithmic_bytes": step_bytes,
             "GBps": step_bytes / (t["ms_per_step"] * 1e-3) / 1e9,
             "frac": step_bytes / (t["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
             "stats_kernel": {"kernel": "k_stats_flat", "avg_launch_ms": t["stats_ms"],
                              "GBps": rows_bytes / (t["stats_ms"] * 1e-3) / 1e9},
-            "host_budget_sizing": sizing}
+            # host work, timed after every GPU record (no idle gap between them)
+            "host_budget_sizing": lambda: host_sizing(S, surv, BS)}
 
 
 def tree_step(K, W, hip, eager_only):
@@ -412,7 +503,10 @@ def tree_step(K, W, hip, eager_only):
         step()
         torch.cuda.synchronize()
     outputs = lambda: list(bufs["vt"].values()) + [ctx_len_new, ctx] + list(bufs["tr"].values())
-    tm = run_timed(step, outputs, K, W, hip, stream, eager_only)
+    return lambda: _tree_result(run_timed(step, outputs, K, W, hip, stream, eager_only), bufs, c, V)
+
+
+def _tree_result(tm, bufs, c, V):
     rows_bytes = int(bufs["tr"]["n_rows"].sum().item()) * V * 4
     step_bytes = rows_bytes + int(c["ctx_len"].sum()) * 4
     return {"workload": "tree: n-gram chains from the anchor and 8 picks (n 3..15, follower fallback on the last "
@@ -420,6 +514,7 @@ def tree_step(K, W, hip, eager_only):
                         "scores and S(n) -> greedy verification of up to 16 rows -> commit; BS=64, V=151936, "
                         "fp32 rows, 4096-token contexts, drafter block 8 x 4",
             "timing": tm["mode"], "steps_per_s": tm["steps_per_s"], "ms_per_step": tm["ms_per_step"],
+            "step_ms_percentiles": tm.get("step_ms_percentiles"),
             "verified_rows_per_step": int(bufs["tr"]["n_rows"].sum().item()), "algorithmic_bytes": step_bytes,
             "GBps": step_bytes / (tm["ms_per_step"] * 1e-3) / 1e9,
             "frac": step_bytes / (tm["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
@@ -444,6 +539,34 @@ def host_sizing(S, surv, BS, calls=2000):
             "cost_model": "C(b) = BS + 0.3 b", "includes": "ctypes marshalling"}
 
 
+def read_ceiling(hip, nbytes, reps=5):
+    """The streaming-read probe (libspec_probe.so: the statistics pass's load
+    pattern without its arithmetic) over nbytes, timed with events: the
+    achievable HBM read rate of this kernel shape on this GPU in this run."""
+    import torch
+    from draft_verification_spec_amd import build as hb
+    lib = C.CDLL(hb.PROBE_LIB)
+    lib.spec_probe_stream_read.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(3)
+    out = torch.zeros((nbytes + 32767) // 32768, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = hip.event(), hip.event()
+    call = lambda: lib.spec_probe_stream_read(buf.data_ptr(), nbytes, out.data_ptr(), C.c_void_p(stream))
+    for _ in range(20):
+        assert call() == 0
+    ms = []
+    for _ in range(reps):
+        hip.record(e0, stream)
+        call()
+        hip.record(e1, stream)
+        ms.append(hip.ms(e0, e1))
+    ms.sort()
+    med = ms[reps // 2]
+    return {"kind": "streaming read probe (non-temporal 16-byte loads, 32 KB per 256-thread workgroup)",
+            "bytes": nbytes, "ms": med, "GBps": nbytes / (med * 1e-3) / 1e9,
+            "frac": nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -455,7 +578,35 @@ def main():
         return
     K, W = args.steps, args.warmup
     hip = Hip()
-    h = headline(K, W, hip, args.eager)
+    # every record's inputs are made and resident first; the timed regions
+    # then follow one another, the reported step last
+    plan = []
+    if not args.no_budget:
+        plan.append(("budget_step", budget_step(K, W, hip, args.eager)))
+    if not args.no_tree:
+        plan.append(("tree_step", tree_step(K, W, hip, args.eager)))
+    if not args.no_stress:
+        plan.append(("stress_step", budget_step(K, W, hip, args.eager, config=4)))
+    if not args.no_fp32:
+        plan.append(("fp32_step", headline(K, W, hip, args.eager, fp32=True)))
+    plan.append(("headline", headline(K, W, hip, args.eager)))
+    extra = {}
+    for name, measure in plan:
+        extra[name] = measure()
+    h = extra.pop("headline")
+    if "fp32_step" in extra:
+        f = extra.pop("fp32_step")
+        fb = f["rows_bytes"] + f["ctx_bytes"]
+        extra["fp32_step"] = {
+            "workload": "the reported step with fp32 rows: target [128,8,V] and draft [128,7,V] fp32",
+            "timing": f["mode"], "steps_per_s": f["steps_per_s"], "ms_per_step": f["ms_per_step"],
+            "algorithmic_bytes": fb, "GBps": fb / (f["ms_per_step"] * 1e-3) / 1e9,
+            "frac": fb / (f["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "step_ms_percentiles": f.get("step_ms_percentiles"),
+            "stats_kernel": {"kernel": STATS_KERNEL, "avg_launch_ms": f["stats_ms"],
+                             "GBps": f["rows_bytes"] / (f["stats_ms"] * 1e-3) / 1e9,
+                             "frac": f["rows_bytes"] / (f["stats_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBPS}}
+        del f
     ms_step = h["ms_per_step"]
     step_bytes = h["rows_bytes"] + h["ctx_bytes"]
     achieved = h["rows_bytes"] / (h["stats_ms"] * 1e-3) / 1e9
@@ -477,6 +628,7 @@ def main():
                                "contexts, n-gram n 5..15, up to 15 tokens",
                    "global_batch": h["BS"], "seq_len": h["T_ctx"], "draft_len": h["B"], "timing": h["mode"]},
         "eager": {"ms_per_step": h["eager_ms_per_step"]},
+        "step_ms_percentiles": h.get("step_ms_percentiles"),
         "roofline": {"bound": "hbm", "kernel": STATS_KERNEL, "achieved": achieved, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic_from_profile(),
                      "bytes_per_launch": h["rows_bytes"], "avg_launch_ms": h["stats_ms"]},
@@ -485,12 +637,12 @@ def main():
         "acceptance": dict(h["acceptance"], us_per_emitted_token=ms_step * 1e3 / (h["BS"] *
                                                                                h["acceptance"]["tokens_per_request_step"])),
     }
-    if not args.no_budget:
-        res["budget_step"] = budget_step(K, W, hip, args.eager)
-    if not args.no_tree:
-        res["tree_step"] = tree_step(K, W, hip, args.eager)
-    if not args.no_stress:
-        res["stress_step"] = budget_step(K, W, hip, args.eager, config=4)
+    for rec in extra.values():
+        if callable(rec.get("host_budget_sizing")):
+            rec["host_budget_sizing"] = rec["host_budget_sizing"]()
+    res.update(extra)
+    if not args.no_ceiling:
+        res["hbm_ceiling"] = {"read_probe": read_ceiling(hip, h["rows_bytes"]), "copy": copy_ceiling(hip)}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(h["c"])
     print(json.dumps(res), flush=True)

@@ -17,14 +17,18 @@ HIPCC_FLAGS = [
 ]
 
 
+PROBE_LIB = os.path.join(PKG, "libspec_probe.so")   # the benchmark's streaming-read probe, not the step
+
+
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", LIB + ".tmp"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.check_call(cmd)
-    os.replace(LIB + ".tmp", LIB)
+    for srcs, out in ((SOURCES, LIB), (["probe.hip"], PROBE_LIB)):
+        cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+               *[os.path.join(CSRC, s) for s in srcs], "-o", out + ".tmp"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.check_call(cmd)
+        os.replace(out + ".tmp", out)
     return LIB
 
 

@@ -191,13 +191,13 @@ __device__ __forceinline__ void unpack(const uint4& x, float* v)
 // Fold kTile raw 16-byte vectors into (m, s); the sum is the pairwise tree of
 // sm_update over the kTile * VEC values, unpacked one vector at a time so the
 // values never all sit in registers.
-template <int DT>
+template <int DT, int NV = kTile>
 __device__ __forceinline__ void sm_update_raw(const uint4* raw, float c, float& m, double& s)
 {
     constexpr int VEC = vec_of<DT>();
     float tm = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < kTile; ++u) {
+    for (int u = 0; u < NV; ++u) {
         float v[VEC];
         unpack<DT>(raw[u], v);
 #pragma unroll
@@ -209,16 +209,16 @@ __device__ __forceinline__ void sm_update_raw(const uint4* raw, float c, float& 
     }
     if (m != -INFINITY) {
         const float o = m * c;
-        float vs[kTile];
+        float vs[NV];
 #pragma unroll
-        for (int u = 0; u < kTile; ++u) {
+        for (int u = 0; u < NV; ++u) {
             float v[VEC];
             unpack<DT>(raw[u], v);
 #pragma unroll
             for (int q = 0; q < VEC; ++q) v[q] = fast_exp2(fmaf(v[q], c, -o));
             vs[u] = pairwise_sum<VEC>(v);
         }
-        s += (double)pairwise_sum<kTile>(vs);
+        s += (double)pairwise_sum<NV>(vs);
     } else if (tm != tm) {
         s = __builtin_nan("");
     }
@@ -965,6 +965,106 @@ __global__ __launch_bounds__(kBlock) void k_stats_flat(StatsParams P)
     }
 }
 
+// (m, s) of a wave with DPP, valid in lane 63: the wave's largest m first
+// (an inclusive max scan over rows of 16 lanes, then across rows), then each
+// lane's s rescaled to it and the sum taken in fp64.  A lane with m = -inf
+// adds nothing (or its NaN); the order of the fp64 additions is fixed.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_max_step(float v)
+{
+    const int o = __builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), CTRL, ROWS, 0xf, false);
+    return fmaxf(v, __int_as_float(o));
+}
+
+__device__ __forceinline__ void wave_softmax_dpp(float& m, double& s, float c)
+{
+    float M = m;
+    M = dpp_max_step<0x111, 0xf>(M);   // row_shr:1
+    M = dpp_max_step<0x112, 0xf>(M);   // row_shr:2
+    M = dpp_max_step<0x114, 0xf>(M);   // row_shr:4
+    M = dpp_max_step<0x118, 0xf>(M);   // row_shr:8
+    M = dpp_max_step<0x142, 0xa>(M);   // row_bcast:15
+    M = dpp_max_step<0x143, 0xc>(M);   // row_bcast:31
+    M = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(M), 63));
+    double sc;
+    if (m == -INFINITY) sc = (s != s) ? s : 0.0;
+    else sc = s * (double)fast_exp2((float)((double)(m * c) - (double)(M * c)));
+    s = wave_total_f64(sc);
+    m = M;
+}
+
+// A workgroup of 256 threads reduces two chunks at once: threads 0..127 take
+// the first, 128..255 the second, each thread NV = 2 kTile 16-byte vectors of
+// its chunk (vector u at lo + tt * VEC + u * 128 * VEC, tt = t mod 128), so
+// every wave reduces once per pair.  Vectors at or past hi (and every vector
+// when !go) load the first vector of row 0 instead and read as -inf.
+constexpr int kHalf = kBlock / 2;
+constexpr int kHalfVecs = 2 * kTile;
+
+template <int DT>
+__device__ __forceinline__ void half_issue(const void* logits, int64_t stride, int64_t row, bool go, int64_t lo,
+                                           int64_t hi, int tt, uint4* raw)
+{
+    constexpr int64_t VEC = vec_of<DT>();
+    constexpr int64_t STEP = (int64_t)kHalf * VEC;
+    constexpr int ES = DT == SPEC_F32 ? 4 : 2;
+    const char* rp = (const char*)row_ptr<DT>(logits, go ? row : 0, stride);
+    const int64_t h = go ? hi : 0;
+    const int64_t e0 = lo + (int64_t)tt * VEC;
+#pragma unroll
+    for (int u = 0; u < kHalfVecs; ++u) {
+        const int64_t e = e0 + u * STEP;
+        raw[u] = load_stream(rp + (e < h ? e : 0) * ES);
+    }
+}
+
+struct HalfRed {
+    float m[kBlock / kWave];
+    double s[kBlock / kWave];
+};
+
+// Softmax statistics of the half's chunk [lo, hi) from its registers; thread
+// tt = 0 of the half writes *out (the bad-row value when `bad`) unless out is
+// null.  One barrier, taken by the whole workgroup.
+template <int DT>
+__device__ __forceinline__ void half_softmax(const uint4* raw, int64_t lo, int64_t hi, float c, HalfRed& R, int t,
+                                             Partial* out, bool bad)
+{
+    constexpr int64_t VEC = vec_of<DT>();
+    constexpr int64_t STEP = (int64_t)kHalf * VEC;
+    const uint32_t ninf = DT == SPEC_F32 ? 0xFF800000u : 0xFF80FF80u;   // -inf in every lane of a vector
+    const int tt = t % kHalf;
+    const int64_t e = lo + (int64_t)tt * VEC;
+    float m = -INFINITY;
+    double s = 0.0;
+    if (lo + STEP * kHalfVecs <= hi) {
+        // a whole chunk (every chunk of a row but its last): no masking
+        sm_update_raw<DT, kHalfVecs>(raw, c, m, s);
+    } else {
+        uint4 r2[kHalfVecs];
+#pragma unroll
+        for (int u = 0; u < kHalfVecs; ++u) {
+            const bool ok = e + u * STEP < hi;
+            r2[u].x = ok ? raw[u].x : ninf; r2[u].y = ok ? raw[u].y : ninf;
+            r2[u].z = ok ? raw[u].z : ninf; r2[u].w = ok ? raw[u].w : ninf;
+        }
+        sm_update_raw<DT, kHalfVecs>(r2, c, m, s);
+    }
+    wave_softmax_dpp(m, s, c);
+    const int lane = t % kWave, w = t / kWave;
+    if (lane == kWave - 1) { R.m[w] = m; R.s[w] = s; }
+    __syncthreads();
+    if (tt == 0 && out) {
+        // the half's two waves (each wave's total sits in its lane 63)
+        m = R.m[w];
+        s = R.s[w];
+        sm_combine(m, s, R.m[w + 1], R.s[w + 1], c);
+        Partial p;
+        p.m = m; p.idx = 0; p.s = s;
+        *out = bad ? bad_value() : p;
+    }
+}
+
 // The same pass without a row list, for batches whose rows per request are
 // close to their bound: grid ((TM + DM) * pairs, bs) with TM the target rows
 // and DM the draft slots a request can have and pairs = ceil(splits / 2);
@@ -980,6 +1080,7 @@ template <int DT, bool GREEDY, bool DITEMS>
 __global__ __launch_bounds__(kBlock) void k_stats_rows(StatsParams P, int32_t TM)
 {
     __shared__ GroupRed R;
+    __shared__ HalfRed HR;
     const int t = threadIdx.x;
     const int r = blockIdx.y;
     const int32_t npair = (P.splits + 1) / 2;
@@ -1022,12 +1123,23 @@ __global__ __launch_bounds__(kBlock) void k_stats_rows(StatsParams P, int32_t TM
         const bool two = s + 1 < P.splits;   // an odd last pair has one chunk
         const int64_t clo1 = clo + P.chunk;
         const int64_t chi1 = two ? ((clo1 + P.chunk < P.vocab) ? clo1 + P.chunk : P.vocab) : clo1;
-        uint4 raw[kTile], raw1[kTile];
-        group_issue<DT>(base, stride, row, ok, clo, chi, t, raw);
-        group_issue<DT>(base, stride, row, ok && two, clo1, chi1, t, raw1);
         Partial* out = P.part + ((int64_t)r * P.NR + prow) * P.splits + s;
-        group_chunk<DT, GREEDY>(raw, clo, ok ? chi : clo, P.c, R, 0, 0, t, out, !ok);
-        group_chunk<DT, GREEDY>(raw1, clo1, (ok && two) ? chi1 : clo1, P.c, R, 1, 0, t, two ? out + 1 : nullptr, !ok);
+        if constexpr (GREEDY) {
+            uint4 raw[kTile], raw1[kTile];
+            group_issue<DT>(base, stride, row, ok, clo, chi, t, raw);
+            group_issue<DT>(base, stride, row, ok && two, clo1, chi1, t, raw1);
+            group_chunk<DT, GREEDY>(raw, clo, ok ? chi : clo, P.c, R, 0, 0, t, out, !ok);
+            group_chunk<DT, GREEDY>(raw1, clo1, (ok && two) ? chi1 : clo1, P.c, R, 1, 0, t, two ? out + 1 : nullptr,
+                                    !ok);
+        } else {
+            // each half of the workgroup reduces one chunk of the pair
+            const bool second = t >= kHalf;
+            const int64_t lo = second ? clo1 : clo;
+            const int64_t hi = second ? ((ok && two) ? chi1 : clo1) : (ok ? chi : clo);
+            uint4 raw[kHalfVecs];
+            half_issue<DT>(base, stride, row, second ? (ok && two) : ok, lo, hi, t % kHalf, raw);
+            half_softmax<DT>(raw, lo, hi, P.c, HR, t, second ? (two ? out + 1 : nullptr) : out, !ok);
+        }
     }
     if (P.done && blockIdx.x == 0) {
         if (t == 0) { P.done[r] = 0; P.done[P.bs + r] = 0; }   // count, chunk counter
