@@ -48,11 +48,11 @@ __device__ __forceinline__ int32_t tok(const Text& x, int64_t p)
     return *(const int32_t*)(p < x.na ? pa : pb);
 }
 
-template <int NT>
+template <int NT, int NCAND = kMaxCand>
 struct NgramShared {
     int32_t suf[SPEC_MAX_CAP];
     Top2 sh[NT / kWave];
-    int32_t cand[kMaxCand];
+    int32_t cand[NCAND];
     int32_t n_cand;
 };
 
@@ -68,7 +68,7 @@ struct NgramOut {
 // LDS of the follower fallback beyond the scan's own (whose suffix and
 // candidate lists hold the hash table's counts and keys).
 constexpr int kFollowers = SPEC_MAX_FOLLOWERS;
-static_assert(kMaxCand * sizeof(int32_t) >= kFollowers * sizeof(uint64_t), "hash keys fit the candidate list");
+static_assert(kMaxCand * sizeof(int32_t) >= kFollowers * sizeof(uint64_t), "hash keys fit the full candidate list");
 static_assert(SPEC_MAX_CAP >= kFollowers, "hash counts fit the suffix");
 struct FollowShared {
     int32_t last[kFollowers];       // latest position of each follower
@@ -79,15 +79,19 @@ struct FollowShared {
 };
 
 // Scans text x with the whole workgroup (every thread calls it): batches of
-// NB positions per thread, so win holds NT * NB tokens of LDS.  With `pre`, v
+// NB positions per thread (NT * NB positions), of which the first NWIN per
+// thread are staged in win (NT * NWIN tokens of LDS); the rest of a batch is
+// tested from registers and read from memory where needed.  With `pre`, v
 // already holds the first batch (positions t + u * NT, any value past the
-// text).
-template <int NT, int NB = kBatch>
-__device__ void ngram_scan(const Text& x, int32_t* win, NgramShared<NT>& S, const NgramOut& O, int32_t (&v)[NB],
-                           bool pre, FollowShared* FS = nullptr)
+// text).  NCAND bounds the LDS list of candidates extended by whole waves.
+template <int NT, int NB = kBatch, int NWIN = NB, int NCAND = kMaxCand>
+__device__ void ngram_scan(const Text& x, int32_t* win, NgramShared<NT, NCAND>& S, const NgramOut& O,
+                           int32_t (&v)[NB], bool pre, FollowShared* FS = nullptr)
 {
     static_assert(NT / kWave <= 16, "per-wave slots of FollowShared");
-    constexpr int64_t kWin = (int64_t)NT * NB;
+    static_assert(NWIN >= 1 && NWIN <= NB, "the window is a prefix of the batch");
+    constexpr int64_t kWin = (int64_t)NT * NWIN;    // tokens staged in LDS
+    constexpr int64_t kSpan = (int64_t)NT * NB;     // positions per batch
     const int t = threadIdx.x;
     const int lane = t % kWave, wid = t / kWave;
     const int64_t jend = x.n - 1;                 // end positions j < n - 1
@@ -113,13 +117,13 @@ __device__ void ngram_scan(const Text& x, int32_t* win, NgramShared<NT>& S, cons
     Top2 best{0, 0};
     if (jend > 0) {
         // phase 1: first kPre tokens per position, thread-private
-        for (int64_t base = 0; base < jend; base += kWin) {
+        for (int64_t base = 0; base < jend; base += kSpan) {
             if (base > 0) {
                 __syncthreads();   // the previous window is no longer read
                 load_batch(base);
             }
 #pragma unroll
-            for (int u = 0; u < NB; ++u) win[t + u * NT] = v[u];
+            for (int u = 0; u < NWIN; ++u) win[t + u * NT] = v[u];
             wbase = base;
             __syncthreads();
             if (base == 0 && suf_in_win) {
@@ -142,7 +146,7 @@ __device__ void ngram_scan(const Text& x, int32_t* win, NgramShared<NT>& S, cons
                 while (l < lim && l < kPre && at(j - l) == S.suf[l]) ++l;
                 if (l == kPre && l < lim) {
                     const int c = atomicAdd(&S.n_cand, 1);
-                    if (c < kMaxCand) {
+                    if (c < NCAND) {
                         S.cand[c] = (int32_t)j;
                         continue;
                     }
@@ -154,7 +158,7 @@ __device__ void ngram_scan(const Text& x, int32_t* win, NgramShared<NT>& S, cons
     }
     __syncthreads();
     // phase 2: each wave extends listed candidates 64 tokens per step
-    const int nc = S.n_cand < kMaxCand ? S.n_cand : kMaxCand;
+    const int nc = S.n_cand < NCAND ? S.n_cand : NCAND;
     for (int c = wid; c < nc; c += NT / kWave) {
         const int64_t j = S.cand[c];
         const int64_t lim = (j + 1 < O.cap) ? j + 1 : O.cap;
@@ -219,6 +223,9 @@ __device__ void ngram_scan(const Text& x, int32_t* win, NgramShared<NT>& S, cons
             }
         }
     }
+    if constexpr (NCAND * sizeof(int32_t) < kFollowers * sizeof(uint64_t)) {
+        return;   // no room for the follower hash: instances with NCAND this small never take the fallback
+    } else {
     if (!follow) return;
     // follower fallback: one token per round while the draft is short
     __syncthreads();
@@ -298,6 +305,7 @@ __device__ void ngram_scan(const Text& x, int32_t* win, NgramShared<NT>& S, cons
         if (O.follow) O.follow[k] = (k >= len0 && k < len) ? FS->fol[k] : 0;
     }
     if (t == 0) *O.draft_len = len;
+    }
 }
 
 }  // namespace spec

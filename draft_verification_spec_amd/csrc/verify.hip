@@ -1487,14 +1487,16 @@ __device__ int32_t draw_from_p(const ChainParams& P, const Draw& d, double* W, d
     return draw_from_chunks<DTT, DTD>(P, d1, W, u);
 }
 
-// Appends the emitted tokens (token `last` at position nacc) at ctx_len[r] = len
-// and writes the new length.
-__device__ void commit(const ChainParams& P, int r, int n, int nacc, int32_t last, int32_t len, uint32_t* fl)
+// Appends the emitted tokens (the accepted slot tokens `toks`, already in
+// LDS, then token `last` at position nacc) at ctx_len[r] = len and writes the
+// new length.
+__device__ void commit(const ChainParams& P, int r, int n, int nacc, const int32_t* toks, int32_t last, int32_t len,
+                       uint32_t* fl)
 {
     const bool ok = (len >= 0 && len + n <= P.ctx_cap);
     if (ok) {
         for (int i = threadIdx.x; i < n; i += blockDim.x) {
-            const int32_t tok = (i == nacc) ? last : P.tokens[(int64_t)r * P.ld + i];
+            const int32_t tok = (i == nacc) ? last : toks[i];
             P.ctx[(int64_t)r * P.ctx_stride + len + i] = tok;
         }
     } else if (threadIdx.x == 0) {
@@ -1683,11 +1685,25 @@ __device__ int32_t residual_draw(const ChainParams& P, const Draw& d, int r, dou
     __syncthreads();
     if (t < P.splits) {
         const double* src = P.sums + ((int64_t)r * P.splits + t) * kSubSums;
+        // every sum of the chunk in one round trip; a sum not yet visible
+        // (never seen in practice) is then waited for on its own
+        bool missing = P.wait_limit < 0;
+        if (!missing) {
+#pragma unroll
+            for (int q = 0; q < kSubSums; ++q)
+                mine[q] = __hip_atomic_load(src + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int q = 0; q < kSubSums; ++q) missing |= mine[q] < 0.0;
+        }
+        if (missing) {
+            // the rare case: wait for each sum in turn, within the bound
+#pragma unroll
+            for (int q = 0; q < kSubSums; ++q) mine[q] = residual_load(src + q, P.wait_limit);
+        }
         double tot = 0.0;
         bool late = false;
 #pragma unroll
         for (int q = 0; q < kSubSums; ++q) {
-            mine[q] = residual_load(src + q, P.wait_limit);
             late |= mine[q] < 0.0;
             tot += mine[q];
         }
@@ -1982,6 +1998,7 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
             } else d.mode = 1;   // unusable draft row (flagged): fall back to p
         }
     }
+    double* W = sW;   // chunk sums of the draw
     // which workgroup draws: the lead, or for a streamed residual the last
     // of the K to finish its chunks
     bool streamed = false;
@@ -2010,14 +2027,14 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
     }
     bool resum = false;   // a streamed residual whose published sums did not all arrive
     if (streamed) {
-        last = residual_draw<DTT>(P, d, r, usmp, sW);
+        last = residual_draw<DTT>(P, d, r, usmp, W);
         if (last == kResidualLate) {
             if (t == 0) sFlags |= SPEC_FLAG_RESIDUAL_LATE;
             resum = true;
         } else if (last < 0) {
             // the residual had no mass (not reachable in exact arithmetic): draw from p
             if (t == 0) sFlags |= SPEC_FLAG_RESIDUAL_ZERO;
-            last = draw_from_p<DTT, DTD>(P, d, sW, usmp);
+            last = draw_from_p<DTT, DTD>(P, d, W, usmp);
         }
     }
     if (!streamed || resum) {
@@ -2028,7 +2045,7 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
                 const int64_t lo = (int64_t)s * P.chunk;
                 const int64_t hi = (lo + P.chunk < P.vocab) ? lo + P.chunk : P.vocab;
                 const double x = range_sum<DTT, DTD>(P, d, lo, hi);
-                if (t == 0) sW[s] = x;
+                if (t == 0) W[s] = x;
             }
             __syncthreads();
         } else {
@@ -2036,7 +2053,7 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
             const Partial* row = rp + nacc * rr;
             for (int s = t; s < P.splits; s += kDBlock) {
                 const Partial q = row[s * rs];
-                sW[s] = (q.m == -INFINITY) ? 0.0 : q.s * (double)fast_exp2((float)((double)(q.m * P.c) - (double)d.Ot));
+                W[s] = (q.m == -INFINITY) ? 0.0 : q.s * (double)fast_exp2((float)((double)(q.m * P.c) - (double)d.Ot));
             }
             __syncthreads();
             if (d.mode == 3) {
@@ -2044,15 +2061,15 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
                 const int64_t lo = (int64_t)sy * P.chunk;
                 const int64_t hi = (lo + P.chunk < P.vocab) ? lo + P.chunk : P.vocab;
                 const double wy = range_sum<DTT, DTD>(P, d, lo, hi);
-                if (t == 0) sW[sy] = wy;
+                if (t == 0) W[sy] = wy;
             }
             __syncthreads();
         }
-        last = draw_from_chunks<DTT, DTD>(P, d, sW, usmp);
+        last = draw_from_chunks<DTT, DTD>(P, d, W, usmp);
         if (last < 0) {
             // the residual had no mass (not reachable in exact arithmetic): draw from p
             if (t == 0) sFlags |= SPEC_FLAG_RESIDUAL_ZERO;
-            last = draw_from_p<DTT, DTD>(P, d, sW, usmp);
+            last = draw_from_p<DTT, DTD>(P, d, W, usmp);
         }
       } else if (!P.greedy) {
         if (t == 0) sFlags |= SPEC_FLAG_BAD_LOGITS;
@@ -2078,7 +2095,7 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
         __shared__ uint32_t sCommit;
         if (t == 0) sCommit = 0;
         __syncthreads();
-        commit(P, r, nacc + 1, nacc, last, len0, &sCommit);
+        commit(P, r, nacc + 1, nacc, sTok, last, len0, &sCommit);
         __syncthreads();
         fl |= sCommit;
     }
@@ -2464,7 +2481,7 @@ static int elem_bytes(int dt) { return dt == SPEC_F32 ? 4 : 2; }
 static size_t plan_bytes(int64_t rows) { return align256((size_t)rows * sizeof(int2)) + align256(sizeof(int32_t)); }
 
 // Verify workspace: partials [bs, NR, splits] | row prefix [bs + 1] | row plan [bs * NR] |
-// residual sums [bs, splits, kSubSums] | residual counters [bs]
+// residual sums [bs, splits, kSubSums] | residual counters [2 bs]
 size_t spec_verify_chain_ws(int32_t bs, int32_t vocab, int32_t ld, int32_t dtype)
 {
     RowSplit sp = row_split(vocab, elem_bytes(dtype));
@@ -2542,7 +2559,9 @@ int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st)
     launch_stats(S, a->dtype, at, a->draft_dtype, ad, draft, P.greedy, a->ld + 1, draft ? a->ld : 0,
                  a->bs + slots + (draft ? slots : 0), sp, gpre, L);
     const int tt = a->dtype, dd = P.dlogits ? a->draft_dtype : a->dtype;
-    // residual chunks shared by K workgroups per request, about 5 each
+    // residual chunks shared by K workgroups per request, about 5 each (two
+    // 512-thread decide workgroups fit on a compute unit, so K = 4 keeps a
+    // batch of 128 resident at once)
     const int K = draft && P.coal && sp.splits <= kDBlock ? std::min(16, std::max(1, (sp.splits + 4) / 5)) : 1;
     const dim3 g(a->bs, K), b(kDBlock);
     if (tt == SPEC_F32 && dd == SPEC_F32) hipLaunchKernelGGL((k_decide<SPEC_F32, SPEC_F32>), g, b, 0, st, P);
