@@ -1019,16 +1019,16 @@ __device__ __forceinline__ void half_issue(const void* logits, int64_t stride, i
 }
 
 struct HalfRed {
-    float m[kBlock / kWave];
-    double s[kBlock / kWave];
+    float m[2][kBlock / kWave];   // by item parity, so one barrier per item suffices
+    double s[2][kBlock / kWave];
 };
 
 // Softmax statistics of the half's chunk [lo, hi) from its registers; thread
 // tt = 0 of the half writes *out (the bad-row value when `bad`) unless out is
 // null.  One barrier, taken by the whole workgroup.
 template <int DT>
-__device__ __forceinline__ void half_softmax(const uint4* raw, int64_t lo, int64_t hi, float c, HalfRed& R, int t,
-                                             Partial* out, bool bad)
+__device__ __forceinline__ void half_softmax(const uint4* raw, int64_t lo, int64_t hi, float c, HalfRed& R, int par,
+                                             int t, Partial* out, bool bad)
 {
     constexpr int64_t VEC = vec_of<DT>();
     constexpr int64_t STEP = (int64_t)kHalf * VEC;
@@ -1052,16 +1052,49 @@ __device__ __forceinline__ void half_softmax(const uint4* raw, int64_t lo, int64
     }
     wave_softmax_dpp(m, s, c);
     const int lane = t % kWave, w = t / kWave;
-    if (lane == kWave - 1) { R.m[w] = m; R.s[w] = s; }
+    if (lane == kWave - 1) { R.m[par][w] = m; R.s[par][w] = s; }
     __syncthreads();
     if (tt == 0 && out) {
         // the half's two waves (each wave's total sits in its lane 63)
-        m = R.m[w];
-        s = R.s[w];
-        sm_combine(m, s, R.m[w + 1], R.s[w + 1], c);
+        m = R.m[par][w];
+        s = R.s[par][w];
+        sm_combine(m, s, R.m[par][w + 1], R.s[par][w + 1], c);
         Partial p;
         p.m = m; p.idx = 0; p.s = s;
         *out = bad ? bad_value() : p;
+    }
+}
+
+// The flat pass at T > 0 with workgroups of 128 threads (two waves), one item
+// each, eight 16-byte vectors per thread: each wave reduces once per chunk.
+template <int DT, bool DITEMS>
+__global__ __launch_bounds__(kHalf) void k_stats_flat_half(StatsParams P)
+{
+    __shared__ HalfRed HR;
+    const int t = threadIdx.x;
+    const uint32_t splits = (uint32_t)P.splits;
+    uint32_t it = blockIdx.x;   // < 2^31, and so is the grid: it + grid does not wrap
+    int2 e = P.plan[it / splits];
+    const uint32_t items = (uint32_t)__builtin_amdgcn_readfirstlane(*P.plan_count) * splits;
+    int par = 0;
+    while (it < items) {
+        const uint32_t q = it / splits;
+        const int32_t s = (int32_t)(it - q * splits);
+        const int32_t row = __builtin_amdgcn_readfirstlane(e.x);
+        const int32_t pr = __builtin_amdgcn_readfirstlane(e.y);
+        const bool isd = DITEMS && pr < 0;
+        const void* base = isd ? P.dlogits : P.logits;
+        const int64_t stride = isd ? P.dstride : P.stride;
+        const bool ok = row >= 0;
+        const int64_t clo = (int64_t)s * P.chunk;
+        const int64_t chi = (clo + P.chunk < P.vocab) ? clo + P.chunk : P.vocab;
+        uint4 raw[kHalfVecs];
+        half_issue<DT>(base, stride, row, ok, clo, chi, t, raw);
+        Partial* out = P.part + (int64_t)(pr & 0x7FFFFFFF) * P.splits + s;
+        half_softmax<DT>(raw, clo, ok ? chi : clo, P.c, HR, par, t, out, !ok);
+        par ^= 1;
+        it += gridDim.x;
+        if (it < items) e = P.plan[it / splits];
     }
 }
 
@@ -1138,7 +1171,7 @@ __global__ __launch_bounds__(kBlock) void k_stats_rows(StatsParams P, int32_t TM
             const int64_t hi = second ? ((ok && two) ? chi1 : clo1) : (ok ? chi : clo);
             uint4 raw[kHalfVecs];
             half_issue<DT>(base, stride, row, second ? (ok && two) : ok, lo, hi, t % kHalf, raw);
-            half_softmax<DT>(raw, lo, hi, P.c, HR, t, second ? (two ? out + 1 : nullptr) : out, !ok);
+            half_softmax<DT>(raw, lo, hi, P.c, HR, 0, t, second ? (two ? out + 1 : nullptr) : out, !ok);
         }
     }
     if (P.done && blockIdx.x == 0) {
@@ -2388,7 +2421,8 @@ template <int DT, bool GREEDY, bool DITEMS>
 static void launch_flat_t(const StatsParams& P, int64_t grid, const StatsLaunch& L)
 {
     hipLaunchKernelGGL(k_plan_rows<DITEMS>, dim3(1), dim3(kBlock), 0, L.st, P);
-    launch_timed(k_stats_flat<DT, GREEDY, DITEMS>, (int)grid, kBlock, P, L);
+    if constexpr (GREEDY) launch_timed(k_stats_flat<DT, GREEDY, DITEMS>, (int)grid, kBlock, P, L);
+    else launch_timed(k_stats_flat_half<DT, DITEMS>, (int)grid, kHalf, P, L);
 }
 
 template <int DT>
