@@ -85,7 +85,7 @@ struct FollowShared {
 // already holds the first batch (positions t + u * NT, any value past the
 // text).  NCAND bounds the LDS list of candidates extended by whole waves.
 template <int NT, int NB = kBatch, int NWIN = NB, int NCAND = kMaxCand>
-__device__ void ngram_scan(const Text& x, int32_t* win, NgramShared<NT, NCAND>& S, const NgramOut& O,
+__device__ __forceinline__ void ngram_scan(const Text& x, int32_t* win, NgramShared<NT, NCAND>& S, const NgramOut& O,
                            int32_t (&v)[NB], bool pre, FollowShared* FS = nullptr)
 {
     static_assert(NT / kWave <= 16, "per-wave slots of FollowShared");

@@ -1851,6 +1851,7 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
     __shared__ double sW[kMaxSplits];
     __shared__ uint32_t sFlags;
     __shared__ unsigned long long sRej;
+    __shared__ float sZy;   // target logit of the first rejected slot's token
     // Slot inputs first (thread t = slot t), including the logits of each
     // slot's token, so that these dependent loads overlap the staging and the
     // merges below.
@@ -1890,12 +1891,14 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
             sp[s * P.NR + row] = gp[i];
         }
     __syncthreads();
-    const Partial* rp = staged ? sp : gp;
-    const int rs = staged ? P.NR : 1;               // stride between a row's splits
-    const int rr = staged ? 1 : P.splits;           // stride between rows
     // Rows: target 0..b, draft ld+1 .. ld+b (probabilistic slots, T > 0).
     // kMergeLanes lanes merge one row: each folds every kMergeLanes-th chunk
-    // partial online, then the lanes combine pairwise.
+    // partial online, then the lanes combine pairwise. The merge is
+    // instantiated once for LDS partials and once for global ones, so that
+    // each reads through its own address space (a pointer that may be either
+    // compiles to flat loads, which wait for every outstanding access).
+    // rs: stride between a row's splits; rr: between rows.
+    auto merge = [&](const auto* rp, int rs, int rr) __attribute__((always_inline)) {
     for (int row0 = 0; row0 < P.NR; row0 += kDBlock / kMergeLanes) {
         const int row = row0 + t / kMergeLanes, j = t % kMergeLanes;
         bool is_row = row < P.NR && row <= b;
@@ -1948,6 +1951,9 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
             }
         }
     }
+    };
+    if (staged) merge(sp, P.NR, 1);
+    else merge(gp, 1, P.splits);
     __syncthreads();
     // slot i = t < b: p(y), q(y), accept
     bool rejected = false;
@@ -1997,6 +2003,7 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
     __syncthreads();
     const uint64_t rej = sRej;
     const int nacc = rej ? (int)__builtin_ctzll(rej) : b;
+    if (t == nacc && t < b) sZy = zt;   // read after the next barrier
     // token nacc (the correction or bonus) is written by the drawing
     // workgroup alone, which need not be this one
     if (lead && t <= ld && t != nacc) P.out_tokens[(int64_t)r * (ld + 1) + t] = (t < nacc) ? y : -1;
@@ -2059,15 +2066,14 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
         }
     }
     bool resum = false;   // a streamed residual whose published sums did not all arrive
+    bool zero = false;    // the residual had no mass (not reachable in exact arithmetic)
     if (streamed) {
         last = residual_draw<DTT>(P, d, r, usmp, W);
         if (last == kResidualLate) {
             if (t == 0) sFlags |= SPEC_FLAG_RESIDUAL_LATE;
             resum = true;
         } else if (last < 0) {
-            // the residual had no mass (not reachable in exact arithmetic): draw from p
-            if (t == 0) sFlags |= SPEC_FLAG_RESIDUAL_ZERO;
-            last = draw_from_p<DTT, DTD>(P, d, W, usmp);
+            zero = true;
         }
     }
     if (!streamed || resum) {
@@ -2082,31 +2088,46 @@ __global__ __launch_bounds__(kDBlock) void k_decide(ChainParams P)
             }
             __syncthreads();
         } else {
-            // chunk sums of the row from its partials; the y chunk is rescanned without y
-            const Partial* row = rp + nacc * rr;
-            for (int s = t; s < P.splits; s += kDBlock) {
-                const Partial q = row[s * rs];
-                W[s] = (q.m == -INFINITY) ? 0.0 : q.s * (double)fast_exp2((float)((double)(q.m * P.c) - (double)d.Ot));
-            }
+            // chunk sums of the row from its partials; for a point-mass
+            // residual, y's chunk without y
+            auto sums = [&](const auto* row, int rs) __attribute__((always_inline)) {
+                for (int s = t; s < P.splits; s += kDBlock) {
+                    const Partial q = row[s * rs];
+                    W[s] = (q.m == -INFINITY) ? 0.0 : q.s * (double)fast_exp2((float)((double)(q.m * P.c) - (double)d.Ot));
+                }
+            };
+            if (staged) sums(sp + nacc, P.NR);
+            else sums(gp + nacc * P.splits, 1);
             __syncthreads();
             if (d.mode == 3) {
+                // Subtract y's term from its chunk's sum when that leaves at
+                // least half of the sum (the cancellation then costs at most
+                // one bit); otherwise rescan the chunk without y.
                 const int sy = (int)(d.y / P.chunk);
-                const int64_t lo = (int64_t)sy * P.chunk;
-                const int64_t hi = (lo + P.chunk < P.vocab) ? lo + P.chunk : P.vocab;
-                const double wy = range_sum<DTT, DTD>(P, d, lo, hi);
-                if (t == 0) W[sy] = wy;
+                const double cs = W[sy];
+                const double wy = (double)fast_exp2(fmaf(sZy, P.c, -d.Ot));
+                if (wy <= 0.5 * cs) {
+                    __syncthreads();
+                    if (t == 0) W[sy] = cs - wy;
+                } else {
+                    const int64_t lo = (int64_t)sy * P.chunk;
+                    const int64_t hi = (lo + P.chunk < P.vocab) ? lo + P.chunk : P.vocab;
+                    const double w = range_sum<DTT, DTD>(P, d, lo, hi);
+                    if (t == 0) W[sy] = w;
+                }
             }
             __syncthreads();
         }
         last = draw_from_chunks<DTT, DTD>(P, d, W, usmp);
-        if (last < 0) {
-            // the residual had no mass (not reachable in exact arithmetic): draw from p
-            if (t == 0) sFlags |= SPEC_FLAG_RESIDUAL_ZERO;
-            last = draw_from_p<DTT, DTD>(P, d, W, usmp);
-        }
+        zero = last < 0;
       } else if (!P.greedy) {
         if (t == 0) sFlags |= SPEC_FLAG_BAD_LOGITS;
       }
+    }
+    if (zero) {
+        // a residual without mass: draw from p (one call site, so that it is inlined)
+        if (t == 0) sFlags |= SPEC_FLAG_RESIDUAL_ZERO;
+        last = draw_from_p<DTT, DTD>(P, d, W, usmp);
     }
     if (t == 0) {
         P.out_tokens[(int64_t)r * (ld + 1) + nacc] = last;
