@@ -39,14 +39,26 @@ struct SelectParams {
 
 __device__ __forceinline__ double sigm(double x) { return 1.0 / (1.0 + exp(-x)); }
 
+// A wave-uniform float as a scalar value: selecting between such values
+// stays a select, where a select between two struct fields would become a
+// per-lane load from the selected address.
+__device__ __forceinline__ float sval(float x)
+{
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
 // Eq. (1) logit of position k (1-based); `lnm` = ln(min(max(m,1), m_cap) / m_ref).
 __device__ __forceinline__ double est_logit(const spec_estimator& e, int k, int n, int a, double lnm)
 {
     const bool first = (k == 1);
-    double z = (double)e.beta[(k <= 15 ? k : 15) - 1] +
-               (double)(first ? e.w_first : e.w_rest) * ((double)n - (double)e.n_ref) + (double)e.delta * (double)a;
+    const int bi = (k <= 15 ? k : 15) - 1;
+    float beta = sval(e.beta[0]);
+#pragma unroll
+    for (int i = 1; i < 15; ++i) beta = bi == i ? sval(e.beta[i]) : beta;
+    double z = (double)beta + (double)(first ? sval(e.w_first) : sval(e.w_rest)) * ((double)n - (double)e.n_ref) +
+               (double)e.delta * (double)a;
     if ((double)n >= (double)e.n_full)
-        z += (double)(first ? e.l_first : e.l_rest) + (double)(first ? e.k_first : e.k_rest) * lnm;
+        z += (double)(first ? sval(e.l_first) : sval(e.l_rest)) + (double)(first ? sval(e.k_first) : sval(e.k_rest)) * lnm;
     return z;
 }
 
@@ -73,24 +85,35 @@ __global__ __launch_bounds__(kSlotBlock) void k_alloc_slots(SelectParams P)
     const int r = blockIdx.x * kSlotReqs + (int)(threadIdx.x / kWave);
     if (r >= A.bs) return;   // the whole wave (no workgroup barrier in this kernel)
     const int K = A.K, ld = A.ld;
-    const int rl = A.ngram_len[r];
     const int gcap = A.ngram_ld < ld ? A.ngram_ld : ld;
-    const int glen = rl < 0 ? 0 : (rl > gcap ? gcap : rl);
+    const int k = lane;
+    // Every input first, from in-bounds addresses, and all of them in one
+    // round trip: otherwise the compiler sinks each load into the branch that
+    // uses it, one dependent trip after another.
+    const int kc = k < K ? k : (K > 0 ? K - 1 : 0);
+    const int gc = k < gcap ? k : (gcap > 0 ? gcap - 1 : 0);
+    const int rl = A.ngram_len[r];
     const int n = A.ngram_feat[4 * (int64_t)r + 0];
     const int am = A.ngram_feat[4 * (int64_t)r + 1];
-    double mm = (double)A.ngram_feat[4 * (int64_t)r + 2];
+    const int mf = A.ngram_feat[4 * (int64_t)r + 2];
+    const int32_t td0 = K > 0 ? A.model_tokens[(int64_t)r * K + kc] : -1;
+    const float cv0 = K > 0 ? A.model_conf[(int64_t)r * K + kc] : 0.0f;
+    const int32_t tg0 = gcap > 0 ? A.ngram_draft[(int64_t)r * A.ngram_ld + gc] : -1;
+    const int pm0 = A.model_point_mass ? (int)A.model_point_mass[r] : 1;
+    asm volatile("" : : "v"(rl), "v"(n), "v"(am), "v"(mf), "v"(td0), "v"(cv0), "v"(tg0), "v"(pm0));
+    const int glen = rl < 0 ? 0 : (rl > gcap ? gcap : rl);
+    double mm = (double)mf;
     mm = mm < 1.0 ? 1.0 : (mm > (double)A.est.m_cap ? (double)A.est.m_cap : mm);
     const double lnm = ((double)n >= (double)A.est.n_full) ? log(mm / (double)A.est.m_ref) : 0.0;
-    const bool mpm = !A.model_point_mass || A.model_point_mass[r];
-    const int k = lane;
+    const bool mpm = pm0 != 0;
     int32_t td = -1, tg = -1;
     double h = 0.0, c = 0.0;
     if (k < K) {
-        td = A.model_tokens[(int64_t)r * K + k];
-        const double cv = (double)A.model_conf[(int64_t)r * K + k];
+        td = td0;
+        const double cv = (double)cv0;
         c = A.conf_is_logit ? sigm(cv) : cv;
     }
-    if (k < gcap) tg = A.ngram_draft[(int64_t)r * A.ngram_ld + k];
+    if (k < gcap) tg = tg0;
     if (k < glen) h = sigm(est_logit(A.est, k + 1, n, am, lnm));
     const bool mismatch = __ballot(k < K && td != tg) != 0;
     // chain values (Eq. (3)) from the running products
@@ -229,7 +252,6 @@ __global__ __launch_bounds__(kAllocBlock) void k_alloc_topk(SelectParams P)
     __shared__ int64_t sh_rem, sh_valid;
     __shared__ int sh_done;
     const bool in_lds = N <= kLdsKeys;
-    uint64_t* keys = in_lds ? lkeys : P.keys;
     const int wid = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     if (threadIdx.x == 0) { sh_prefix = 0; sh_valid = 0; sh_done = 0; sh_min = ~0ull; }
     {
@@ -244,6 +266,11 @@ __global__ __launch_bounds__(kAllocBlock) void k_alloc_topk(SelectParams P)
         if (lane == 0) atomicAdd((unsigned long long*)&sh_valid, (unsigned long long)valid);
     }
     __syncthreads();
+    // The selection, instantiated once for keys in LDS and once for keys in
+    // global memory, so that each reads through its own address space (a
+    // pointer that may be either compiles to flat loads, which wait for every
+    // outstanding access).
+    auto select = [&](const uint64_t* keys) __attribute__((always_inline)) {
     const int64_t take = (A.budget < sh_valid) ? A.budget : sh_valid;
     uint64_t theta = ~0ull;  // nothing selected
     if (take > 0) {
@@ -357,6 +384,9 @@ __global__ __launch_bounds__(kAllocBlock) void k_alloc_topk(SelectParams P)
         base += A.alloc_len[r] + 1;
     }
     if (threadIdx.x == 0) A.total_rows[0] = (int32_t)total;
+    };
+    if (in_lds) select(lkeys);
+    else select(P.keys);
 }
 
 // ---------------------------------------------------------------------------
@@ -398,6 +428,9 @@ __device__ __forceinline__ double shfl_f64(double v, int l)
     const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(b >> 32), l, kWave);
     return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
+
+// A global-memory int32 pointer, kept apart from LDS pointers.
+typedef const __attribute__((address_space(1))) int32_t* gi32_ptr;
 
 // NS register slots per lane: forest node j lives on lane j % 64 in slot
 // j / 64 during the chain walk (NS * 64 >= c_max).
@@ -493,9 +526,16 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
         if (glen < 0 || glen > A.ngram_ld) { flags |= SPEC_FLAG_BAD_LENGTH; glen = glen < 0 ? 0 : A.ngram_ld; }
         if (glen == 0) continue;   // nothing to walk or add
         const int ev = lane_chains ? __builtin_amdgcn_readlane(lev, sc) : (int)cev[sc];
-        const int32_t* src = staged ? ctok + (int64_t)sc * A.ngram_ld : A.ngram_draft + q * A.ngram_ld;
-        const int32_t* fsrc = staged ? cfol + (int64_t)sc * A.ngram_ld
-                                     : (A.ngram_follow ? A.ngram_follow + q * A.ngram_ld : nullptr);
+        // token i of the chain and its follower count (0: a copied token),
+        // read from LDS or from global memory through pointers of their own
+        // address space (a pointer that may be either compiles to flat loads,
+        // which wait for every outstanding access)
+        const int32_t* lsrc = ctok + (int64_t)sc * A.ngram_ld;
+        const int32_t* lfol = cfol + (int64_t)sc * A.ngram_ld;
+        const gi32_ptr gsrc = (gi32_ptr)(A.ngram_draft + q * A.ngram_ld);
+        const gi32_ptr gfol = (gi32_ptr)(A.ngram_follow ? A.ngram_follow + q * A.ngram_ld : nullptr);
+        auto tok_at = [&](int i) -> int32_t { return staged ? lsrc[i] : gsrc[i]; };
+        auto fol_at = [&](int i) -> int32_t { return staged ? lfol[i] : (gfol ? gfol[i] : 0); };
         // a token's bucket base: 4 x the copy's evidence class, or 32 + 4 x the
         // class of its follower count
         auto base_of = [&](int32_t fc) { return fc > 0 ? 32 + 4 * follower_class(fc) : 4 * ev; };
@@ -511,8 +551,8 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
                 }
         };
         read_cur();
-        int ctk = lane < glen ? src[lane] : -1;   // the chain's first 64 tokens and their bucket bases
-        int cfb = base_of(lane < glen && fsrc ? fsrc[lane] : 0);
+        int ctk = lane < glen ? tok_at(lane) : -1;   // the chain's first 64 tokens and their bucket bases
+        int cfb = base_of(lane < glen ? fol_at(lane) : 0);
         int t = 0;
         bool tail = false;
         if (glen <= kWave) {
@@ -582,8 +622,8 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
             for (; t < glen; ++t) {
                 if (cdep + 1 > A.depth_max) break;
                 if (t && (t & 63) == 0) {   // the next 64
-                    ctk = t + lane < glen ? src[t + lane] : -1;
-                    cfb = base_of(t + lane < glen && fsrc ? fsrc[t + lane] : 0);
+                    ctk = t + lane < glen ? tok_at(t + lane) : -1;
+                    cfb = base_of(t + lane < glen ? fol_at(t + lane) : 0);
                 }
                 const int tk = __builtin_amdgcn_readlane(ctk, t & 63);
                 const int up = cabove + ((ckind & 3) == 3);   // n-gram nodes above a child of cur
@@ -630,12 +670,12 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
                 const int n = s * kWave + lane, i = n - cntr;
                 if (i >= 0 && i < rem) {
                     const int ui = up + i;
-                    rtok[s] = src[t + i];
+                    rtok[s] = tok_at(t + i);
                     rpar[s] = i == 0 ? cur : n - 1;
                     rdep[s] = cdep + 1 + i;
                     rkind[s] = 3;
                     rabove[s] = ui < 127 ? ui : 127;
-                    rbucket[s] = base_of(fsrc ? fsrc[t + i] : 0) + (ui < 3 ? ui : 3);
+                    rbucket[s] = base_of(fol_at(t + i)) + (ui < 3 ? ui : 3);
                     ragree[s] = -1;
                 }
             }

@@ -40,12 +40,15 @@ struct Text {
 };
 
 // Token p of the text: the address is selected first, so a batch of these is
-// a batch of independent loads rather than branches around them.
+// a batch of independent loads rather than branches around them.  The load
+// goes through a global-memory pointer: the integer arithmetic would
+// otherwise leave a generic one, i.e. a flat load that waits for every
+// outstanding access (LDS ones included).
 __device__ __forceinline__ int32_t tok(const Text& x, int64_t p)
 {
     const uintptr_t pa = (uintptr_t)(x.a + p);
     const uintptr_t pb = (uintptr_t)x.b + (uintptr_t)((p - x.na) * (int64_t)sizeof(int32_t));
-    return *(const int32_t*)(p < x.na ? pa : pb);
+    return *(const __attribute__((address_space(1))) int32_t*)(p < x.na ? pa : pb);
 }
 
 template <int NT, int NCAND = kMaxCand>

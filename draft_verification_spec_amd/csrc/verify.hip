@@ -1185,7 +1185,7 @@ __global__ __launch_bounds__(kBlock) void k_stats_rows(StatsParams P, int32_t TM
 // ---------------------------------------------------------------------------
 
 // Argmax of a row from its chunk partials p[0], p[st], ... (first index on ties).
-__device__ bool merge_argmax(const Partial* p, int splits, int st, int32_t* idx)
+__device__ __forceinline__ bool merge_argmax(const Partial* p, int splits, int st, int32_t* idx)
 {
     ArgAcc acc{-INFINITY, 0x7FFFFFFF, 0};
     for (int s = 0; s < splits; ++s) {
@@ -2247,7 +2247,10 @@ __global__ __launch_bounds__(kWave) void k_tree_walk(TreeParams P)
     __syncthreads();
     if (t < n) {
         int32_t idx;
-        sOk[t] = merge_argmax((staged ? sp : gp) + (int64_t)t * P.splits, P.splits, 1, &idx);
+        // one call per address space (a pointer that may be either compiles
+        // to flat loads)
+        if (staged) sOk[t] = merge_argmax(sp + (int64_t)t * P.splits, P.splits, 1, &idx);
+        else sOk[t] = merge_argmax(gp + (int64_t)t * P.splits, P.splits, 1, &idx);
         sArg[t] = (idx == 0x7FFFFFFF) ? -1 : idx;
     }
     for (int i = t; i < rm; i += kWave) { sOut[i] = -1; sPath[i] = -1; }
