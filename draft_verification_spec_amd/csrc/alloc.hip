@@ -116,16 +116,24 @@ __global__ __launch_bounds__(kSlotBlock) void k_alloc_slots(SelectParams P)
     if (k < gcap) tg = tg0;
     if (k < glen) h = sigm(est_logit(A.est, k + 1, n, am, lnm));
     const bool mismatch = __ballot(k < K && td != tg) != 0;
-    // chain values (Eq. (3)) from the running products
+    // chain values (Eq. (3)) from the running products, both chains in one
+    // loop (independent folds); lane q keeps the products after term q, and
+    // every lane the ones after term K-1
     const double lam = (double)A.lambda;
     double sg = 1.0, sd = 1.0, vg = 0.0, vd = 0.0;
-    for (int q = 0; q < glen; ++q) {
-        sg *= lane_value(h, q);
-        vg += sg > lam ? sg - lam : 0.0;
-    }
-    for (int q = 0; q < K; ++q) {
-        sd *= lane_value(c, q);
-        vd += sd > lam ? sd - lam : 0.0;
+    double mg = 0.0, md = 0.0, sgK = 1.0, sdK = 1.0;
+    const int qn = glen > K ? glen : K;
+    for (int q = 0; q < qn; ++q) {
+        if (q < glen) {
+            sg *= lane_value(h, q);
+            vg += sg > lam ? sg - lam : 0.0;
+        }
+        if (q < K) {
+            sd *= lane_value(c, q);
+            vd += sd > lam ? sd - lam : 0.0;
+        }
+        if (lane == q) { mg = sg; md = sd; }
+        if (q == K - 1) { sgK = sg; sdK = sd; }
     }
     const bool prefix = glen > K && !mismatch;
     int use = SPEC_SRC_MODEL;
@@ -140,22 +148,22 @@ __global__ __launch_bounds__(kSlotBlock) void k_alloc_slots(SelectParams P)
     default: use = SPEC_SRC_MODEL;
     }
     const int len = (use == SPEC_SRC_MODEL) ? K : glen;
-    // survivals of the chosen chain; lane k keeps S_k
-    sg = 1.0;
-    sd = 1.0;
-    double prev = 1.0, mine = 0.0;
-    for (int q = 0; q < len; ++q) {
-        const double hq = (q < glen) ? lane_value(h, q) : 0.0;
-        if (q < glen) sg *= hq;
-        if (q < K) sd *= lane_value(c, q);
-        double S;
-        if (use == SPEC_SRC_MODEL) S = sd;
-        else if (use == SPEC_SRC_NGRAM) S = sg;
-        else if (use == SPEC_SRC_MERGED) S = (q < K) ? (sg > sd ? sg : sd) : prev * hq;
-        else S = (q < K) ? sd : prev * hq;
-        prev = S;
-        if (lane == q) mine = S;
+    // Survival S_k of the chosen chain on lane k: the model or n-gram running
+    // product, the larger of the two on the shared prefix of a merged chain
+    // (the model's on an extended one), and past slot K-1 of those the prefix
+    // value times h_K ... h_k, multiplied in that order.
+    double mine;
+    if (use == SPEC_SRC_MODEL) mine = md;
+    else if (use == SPEC_SRC_NGRAM) mine = mg;
+    else {
+        const bool ext = use == SPEC_SRC_EXTENDED;
+        mine = (lane < K) ? (ext ? md : (mg > md ? mg : md)) : (K > 0 ? (ext ? sdK : (sgK > sdK ? sgK : sdK)) : 1.0);
+        for (int q = K; q < len; ++q) {
+            const double hq = lane_value(h, q);
+            if (q <= lane) mine *= hq;
+        }
     }
+    if (lane >= len) mine = 0.0;
     if (k < ld) {
         int32_t tk = -1;
         uint8_t fl = 0;
@@ -181,11 +189,13 @@ __global__ __launch_bounds__(kSlotBlock) void k_alloc_slots(SelectParams P)
     }
 }
 
+// Exclusive prefix over a workgroup of kAllocBlock threads (the size is a
+// constant: blockDim is a load from the dispatch packet).
 __device__ int64_t block_exclusive_i64(int64_t v, int64_t* total)
 {
     __shared__ int64_t sh[32];
     const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-    const int nw = (int)(blockDim.x / kWave);
+    constexpr int nw = kAllocBlock / kWave;
     int64_t inc = v;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -204,12 +214,13 @@ __device__ int64_t block_exclusive_i64(int64_t v, int64_t* total)
     return before + inc - v;
 }
 
-// Exclusive prefix over the workgroup of 32-bit counts; *total gets the sum.
+// Exclusive prefix over a workgroup of kAllocBlock threads of 32-bit
+// counts; *total gets the sum.
 __device__ uint32_t block_exclusive_u32(uint32_t v, uint32_t* total)
 {
     __shared__ uint32_t sh[32];
     const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-    const int nw = (int)(blockDim.x / kWave);
+    constexpr int nw = kAllocBlock / kWave;
     const uint32_t inc = wave_incl_add(v);
     __syncthreads();
     if (lane == kWave - 1) sh[wid] = inc;
@@ -247,7 +258,9 @@ __global__ __launch_bounds__(kAllocBlock) void k_alloc_topk(SelectParams P)
     const int bs = A.bs, ld = A.ld;
     const int64_t N = (int64_t)bs * ld;
     __shared__ uint64_t lkeys[kLdsKeys];
-    __shared__ uint32_t hist[2][256];
+    // one histogram per wave (double-buffered): at the top digits nearly every
+    // key agrees, and atomics of all waves on one LDS word serialize
+    __shared__ __align__(16) uint32_t hist[2][kAllocBlock / kWave][256];
     __shared__ uint64_t sh_prefix, sh_min;
     __shared__ int64_t sh_rem, sh_valid;
     __shared__ int sh_done;
@@ -276,11 +289,11 @@ __global__ __launch_bounds__(kAllocBlock) void k_alloc_topk(SelectParams P)
     if (take > 0) {
         if (threadIdx.x == 0) sh_rem = take;
         uint64_t mask = 0;
-        for (int i = threadIdx.x; i < 256; i += kAllocBlock) hist[0][i] = 0;
+        for (int i = lane; i < 256; i += kWave) hist[0][wid][i] = 0;
         __syncthreads();
         for (int shift = 56, hb = 0; shift >= 0; shift -= 8, hb ^= 1) {
             // the histogram of this pass was cleared during the previous one
-            uint32_t* H = hist[hb];
+            uint32_t* H = hist[hb][wid];
             const uint64_t pre = sh_prefix;
             const int64_t rounds = (N + kAllocBlock - 1) / kAllocBlock;
             for (int64_t u = 0; u < rounds; ++u) {
@@ -288,14 +301,18 @@ __global__ __launch_bounds__(kAllocBlock) void k_alloc_topk(SelectParams P)
                 const uint64_t k = i < N ? keys[i] : 0ull;
                 hist_add(H, k != 0 && (k & mask) == pre, (int)((k >> shift) & 255u));
             }
-            for (int i = threadIdx.x; i < 256; i += kAllocBlock) hist[hb ^ 1][i] = 0;
+            for (int i = lane; i < 256; i += kWave) hist[hb ^ 1][wid][i] = 0;
             __syncthreads();
             if (wid == 0) {
                 // lane l owns digits 255-4l .. 252-4l (descending); suffix counts from the top
-                uint32_t c4[4];
-                uint32_t own = 0;
+                // (each digit's count summed over the waves' histograms)
+                uint32_t c4[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) { c4[j] = H[255 - 4 * lane - j]; own += c4[j]; }
+                for (int w = 0; w < kAllocBlock / kWave; ++w) {
+                    const uint4 q = *(const uint4*)&hist[hb][w][252 - 4 * lane];
+                    c4[0] += q.w; c4[1] += q.z; c4[2] += q.y; c4[3] += q.x;
+                }
+                const uint32_t own = c4[0] + c4[1] + c4[2] + c4[3];
                 const uint32_t inc = wave_incl_add(own);
                 const int64_t rem = sh_rem;
                 const int64_t above = (int64_t)(inc - own);
@@ -361,27 +378,38 @@ __global__ __launch_bounds__(kAllocBlock) void k_alloc_topk(SelectParams P)
             theta = sh_min;
         }
     }
-    // verified prefix per request, row bases over (alloc + 1)
-    const int per = (bs + (int)blockDim.x - 1) / (int)blockDim.x;
+    // verified prefix per request, row bases over (alloc + 1).  A request's
+    // keys are read in batches of 16 from clamped (in-bounds) positions, so
+    // that each batch is one round of loads; a thread with several requests
+    // counts them again for the row bases rather than rereading alloc_len.
+    const int per = (bs + kAllocBlock - 1) / kAllocBlock;
     const int r0 = threadIdx.x * per;
+    auto count_of = [&](int r) -> int {
+        int cnt = 0;
+        for (int k0 = 0; k0 < ld; k0 += 16) {
+            uint64_t kv[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) kv[j] = keys[(int64_t)r * ld + (k0 + j < ld ? k0 + j : k0)];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) cnt += (k0 + j < ld && kv[j] != 0 && kv[j] >= theta);
+        }
+        return cnt;
+    };
     uint32_t local = 0;
     for (int r = r0; r < r0 + per && r < bs; ++r) {
-        int cnt = 0;
-#pragma unroll
-        for (int k = 0; k < SPEC_MAX_DRAFT; ++k) {
-            if (k < ld) {
-                const uint64_t key = keys[(int64_t)r * ld + k];
-                cnt += (key != 0 && key >= theta);
-            }
-        }
+        const int cnt = count_of(r);
         A.alloc_len[r] = cnt;
         local += cnt + 1;
     }
     uint32_t total;
     int64_t base = block_exclusive_u32(local, &total);
-    for (int r = r0; r < r0 + per && r < bs; ++r) {
-        A.row_base[r] = base;
-        base += A.alloc_len[r] + 1;
+    if (per == 1) {
+        if (r0 < bs) A.row_base[r0] = base;
+    } else {
+        for (int r = r0; r < r0 + per && r < bs; ++r) {
+            A.row_base[r] = base;
+            base += count_of(r) + 1;
+        }
     }
     if (threadIdx.x == 0) A.total_rows[0] = (int32_t)total;
     };

@@ -89,6 +89,34 @@ def test_chain_alloc_random_policies(policy):
     compare_chain_alloc(g, o, 100)
 
 
+@pytest.mark.parametrize("bs,ld,gw", [(300, 32, 32), (257, 20, 15), (1, 32, 32), (600, 15, 15), (33, 16, 16)])
+def test_chain_alloc_widths_and_key_storage(bs, ld, gw):
+    """Chains longer than 16 slots (ld up to 32, n-gram drafts as wide), a
+    batch that ends inside a workgroup of the slot pass, one request, and
+    batches with more ranking keys than the selection keeps in LDS (bs * ld >
+    4096: it reads them from global memory)."""
+    rng = np.random.Generator(np.random.Philox(900 + bs + ld))
+    K = 7
+    truth = rng.integers(0, 40, (bs, gw + 2)).astype(np.int32)
+    d = truth[:, :K].copy()
+    flip = rng.random((bs, K)) < 0.3
+    d[flip] = rng.integers(0, 40, int(flip.sum()))
+    dlen = rng.integers(0, gw + 1, bs).astype(np.int32)
+    draft = np.full((bs, gw), -1, np.int32)
+    for r in range(bs):
+        draft[r, :dlen[r]] = truth[r, :dlen[r]] if rng.random() < 0.6 else rng.integers(0, 40, dlen[r])
+    n = np.where(dlen > 0, rng.integers(5, 16, bs), 0)
+    feat = np.stack([n, rng.integers(0, 2, bs), np.where(n >= 15, rng.integers(15, 400, bs), 0),
+                     np.full(bs, 3)], 1).astype(np.int32)
+    conf = rng.standard_normal((bs, K)).astype(np.float32) + 1.5
+    pm = (rng.random(bs) < 0.5).astype(np.uint8)
+    est = synth.estimator_qwen3_4b()
+    for budget in (0, 5, bs * 3, 10 ** 6):
+        o = O.allocate_budget(d, conf, True, pm, draft, dlen, feat, est, 0.2, budget, "proposed", ld=ld)
+        g = gpu_chain_alloc(d, conf, True, pm, draft, dlen, feat, est, 0.2, budget, "proposed", ld=ld)
+        compare_chain_alloc(g, o, budget)
+
+
 def test_tree_build_config3():
     import torch
     import draft_verification_spec_amd as S
