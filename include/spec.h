@@ -290,7 +290,7 @@ typedef struct spec_tree_alloc {
     float* s_curve;              /* device [bs, rows_cap] or NULL: S(n) for n = 1..
                                     rows_cap, the sum of Q over the first n - 1
                                     nodes of the best-first order ([AS] Section
-                                    3.1: one pass over the order gives S(n))      */
+                                    3.1; one walk down the order gives every n)   */
     uint32_t* out_flags;         /* device [bs], written                          */
 } spec_tree_alloc;
 

@@ -86,8 +86,8 @@ static double logit_at(const void* base, int dtype, int64_t i)
  * a match length l_j: the number of trailing tokens of x[..j] that equal the
  * trailing tokens of the whole text, compared up to min(j+1, cap).  Positions
  * with l_j >= n_min are matches.  The best match is the longest one, ties
- * going to the most recent (readings: "longest match wins"; recency breaks
- * ties); the runner-up is the next one in the same order.  Features:
+ * going to the most recent (readings: the longer match is preferred, and
+ * recency breaks ties); the runner-up is the next one in the same order.  Features:
  *   n = min(l_best, n_max); full = l_best >= n_max; m = l_best if full else 0;
  *   a = 1 if there is no runner-up or it predicts the same next token.
  * The draft is the up-to-max_draft tokens after the best match.
@@ -213,8 +213,9 @@ void oracle_ngram_draft(int nq, const int32_t* ctx, int64_t ctx_stride, const in
  *               + [n >= n_full] (l_pos(k) + kappa_pos(k) ln(min(m, m_cap) / m_ref)))
  * with pos(k) = first iff k = 1 (positions past 15, beyond the pages'
  * chains, reuse beta_15).  The copy term's garbled form is read as
- * ln(min(m,256)/15), the reading under which a 256-token copy adds
- * kappa_first ln(256/15) ~ 5.7 logits (Appendix D).  m >= 1 whenever the
+ * ln(min(m,256)/15): under this reading a copy capped at 256 tokens is
+ * worth kappa_first ln(256/15), about 5.7 logits, the size Appendix D
+ * gives for it.  m >= 1 whenever the
  * term applies in consistent settings; the clamp only guards others.
  * ====================================================================== */
 typedef struct {
@@ -262,7 +263,8 @@ double oracle_chain_value(const double* S, int len, double lambda)
 /* ======================================================================
  * Chain selection for one request.  [HS] Algorithm 1 and Section 4.3:
  *   contains rule: |g| > K and g_1..K = d  ->  keep g; S_k = max(S^g_k, S^d_k)
- *     for k <= K and S_k = S_{k-1} h_k after it ("then continue with h_k");
+ *     for k <= K and S_k = S_{k-1} h_k after it (Algorithm 1 extends the
+ *     merged prefix with the n-gram estimates);
  *   value rule: g matched and V(S^g) >= V(S^d) -> keep g (ties to n-gram);
  *   otherwise keep d.
  * Policies of Section 4.5 / Appendix H: n-gram-first keeps g whenever it
@@ -928,7 +930,8 @@ int oracle_tree_build(int P, int Kc, const int32_t* block, int L, const int32_t*
     sel[0] = 1;
     for (int a = 0; a < take; ++a) sel[order[a]] = 1;
     /* S(n) for every width n: the first n - 1 nodes of the best-first order
-     * ([AS] Section 3.1: one pass over the order gives S(n) for every n) */
+     * ([AS] Section 3.1: a single walk down that order yields S at every
+     * width) */
     if (S_curve) {
         double acc = 0.0;
         for (int n = 1; n <= rows_cap; ++n) {

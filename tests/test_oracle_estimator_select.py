@@ -50,7 +50,7 @@ def test_per_position_intercepts():
 def test_copy_term_scale_and_cap():
     g = gold("estimator_pins.json")["copy_term"]
     e = only(k_first=g["kappa_first"])
-    # a full match (n = 15) with a 256-token copy adds ~5.7 logits at position 1
+    # at n = 15 and m = 256 the copy term at position 1 is kappa_first ln(256/15), about 5.7
     assert O.estimate_logit(e, 1, 15, 0, g["m"]) == pytest.approx(g["logit_increase"], abs=g["tol"])
     # the copy length is capped at 256 ...
     assert O.estimate_logit(e, 1, 15, 0, 1000) == pytest.approx(O.estimate_logit(e, 1, 15, 0, 256), abs=1e-12)

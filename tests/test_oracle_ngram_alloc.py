@@ -133,8 +133,8 @@ def test_ngram_edge_cases():
 
 # ---------------------------------------------------------------------------
 # n-gram fill's follower fallback (AdaSpark Section 3.3, "N-gram candidates":
-# read on along the earlier passage, or else the most frequent follower of
-# the last three tokens)
+# continue the copied passage; when there is none, take the token that most
+# often followed the last three tokens)
 # ---------------------------------------------------------------------------
 
 def test_follower_fallback_hand_examples():

@@ -143,7 +143,8 @@ def test_tree_walk_is_greedy_decode_of_markov_target():
 
 # ---------------------------------------------------------------------------
 # Eq. (6) scores and the S(n) curve (AdaSpark Section 3.3 "Form" and
-# "Learning"; Section 3.1: one pass over the order gives S(n) for every n)
+# "Learning"; Section 3.1: a single walk down the best-first order yields S
+# at every width)
 # ---------------------------------------------------------------------------
 
 def prior(**over):
