@@ -95,9 +95,9 @@ __device__ __forceinline__ double dpp_f64(double v)
     return __hiloint2double(hi, lo);
 }
 
-// Sum over the 64 lanes of a wave, valid in lane 63 (the inclusive scan
-// pattern of wave_incl_add, in fp64).
-__device__ __forceinline__ double wave_total_f64(double v)
+// Inclusive prefix sum over the 64 lanes of a wave in fp64 (the scan pattern
+// of wave_incl_add): lane l gets v_0 + ... + v_l, in a fixed order.
+__device__ __forceinline__ double wave_incl_f64(double v)
 {
     v += dpp_f64<0x111, 0xf, true>(v);
     v += dpp_f64<0x112, 0xf, true>(v);
@@ -106,6 +106,17 @@ __device__ __forceinline__ double wave_total_f64(double v)
     v += dpp_f64<0x142, 0xa, false>(v);
     v += dpp_f64<0x143, 0xc, false>(v);
     return v;
+}
+
+// Sum over the 64 lanes of a wave, valid in lane 63.
+__device__ __forceinline__ double wave_total_f64(double v) { return wave_incl_f64(v); }
+
+// Lane l's double (l wave-uniform), in every lane.
+__device__ __forceinline__ double wave_bcast_f64(double v, int l)
+{
+    const int lo = __builtin_amdgcn_readlane(__double2loint(v), l);
+    const int hi = __builtin_amdgcn_readlane(__double2hiint(v), l);
+    return __hiloint2double(hi, lo);
 }
 
 __device__ __forceinline__ uint32_t wave_or(uint32_t v)

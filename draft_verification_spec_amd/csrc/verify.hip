@@ -1271,36 +1271,14 @@ constexpr int kDWaves = kDBlock / kWave;
 __device__ double block_sum_f64(double v)
 {
     __shared__ double sh[kDWaves];
-    v = wave_sum(v);
+    v = wave_incl_f64(v);   // the wave's total in lane 63
     const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
     __syncthreads();
-    if (lane == 0) sh[wid] = v;
+    if (lane == kWave - 1) sh[wid] = v;
     __syncthreads();
     double tot = 0.0;
     for (int w = 0; w < kDWaves; ++w) tot += sh[w];
     return tot;
-}
-
-__device__ double block_exclusive_f64(double v, double* total)
-{
-    __shared__ double sh[kDWaves];
-    const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-    double inc = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        double u = __shfl_up(inc, o, kWave);
-        if (lane >= o) inc += u;
-    }
-    __syncthreads();
-    if (lane == kWave - 1) sh[wid] = inc;
-    __syncthreads();
-    double before = 0.0, tot = 0.0;
-    for (int w = 0; w < kDWaves; ++w) {
-        if (w < wid) before += sh[w];
-        tot += sh[w];
-    }
-    *total = tot;
-    return before + inc - v;
 }
 
 // Each thread owns a contiguous segment of up to kSeg entries of a chunk and
@@ -1376,55 +1354,55 @@ __device__ double range_sum(const ChainParams& P, const Draw& d, int64_t lo, int
 
 // First token of the chunk [lo, hi) whose running weight (index order)
 // exceeds t; when rounding leaves t past the chunk, its last positive-weight
-// token; -1 if the chunk has no weight.  Only the thread whose segment holds
-// the crossing walks its weights; the threads past it can only offer their
-// first positive weight (adding a positive weight to a running sum already
-// above t stays above t), which the minimum over candidates discards.
+// token; -1 if the chunk has no weight.  Each thread keeps the running sums
+// of its own segment (fp64) from the one pass over its logits; the
+// segments' offsets come from a DPP scan in each wave and the waves' totals
+// in LDS.  A thread then marks the entries of positive weight whose running
+// sum passes t; the first thread with a mark holds the token (a segment past
+// the crossing marks only entries after it, and the minimum discards them).
 template <int DTT, int DTD>
 __device__ int64_t search_range(const ChainParams& P, const Draw& d, int64_t lo, int64_t hi, double t)
 {
+    __shared__ double sh_w[kDWaves];          // each wave's total
     __shared__ long long sh_found[kDWaves];   // each wave's first candidate
     __shared__ long long sh_lp[kDWaves];
     const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
     int64_t a, b;
     seg_of(lo, hi, &a, &b);
-    // the logits stay in registers; weights are recomputed where needed
-    float z[kSeg], x[kSeg];
+    double run[kSeg];
     double mine = 0.0;
     uint32_t posmask = 0;   // segment offsets with positive weight
-    if (a < b) {
-        seg_load<DTT, DTD>(P, d, a, b, z, x);
+    {
+        float z[kSeg], x[kSeg];
+        if (a < b) seg_load<DTT, DTD>(P, d, a, b, z, x);
 #pragma unroll
         for (int u = 0; u < kSeg; ++u) {
-            const double w = seg_w(P, d, a, b, u, z[u], x[u]);
+            const double w = a < b ? seg_w(P, d, a, b, u, z[u], x[u]) : 0.0;
             mine += w;
+            run[u] = mine;
             posmask |= (w > 0.0 ? 1u : 0u) << u;
         }
     }
-    double total;
-    const double cum = block_exclusive_f64(mine, &total);
+    const double inc = wave_incl_f64(mine);
+    if (lane == kWave - 1) sh_w[wid] = inc;
+    __syncthreads();
+    double cum = inc - mine;
+    for (int w2 = 0; w2 < kDWaves; ++w2)
+        if (w2 < wid) cum += sh_w[w2];
+    uint32_t hit = 0;
+#pragma unroll
+    for (int u = 0; u < kSeg; ++u) hit |= (uint32_t)(cum + run[u] > t) << u;
+    hit &= posmask;
     // candidates are ordered like their positions, so a wave's first
     // candidate lane holds its smallest position
-    const uint64_t cand = __ballot(a < b && posmask != 0u && cum + mine > t);
-    if (cand == 0) {
-        if (lane == 0) sh_found[wid] = -1;
-    } else if (lane == (int)__builtin_ctzll(cand)) {
-        int pu;
-        if (cum > t) {
-            pu = __builtin_ctz(posmask);
-        } else {
-            pu = -1;
-            double run = cum;
-#pragma unroll
-            for (int u = 0; u < kSeg; ++u) {
-                const double w = seg_w(P, d, a, b, u, z[u], x[u]);
-                run += w;
-                if (pu < 0 && w > 0.0 && run > t) pu = u;
-            }
-            if (pu < 0) pu = 31 - __builtin_clz(posmask);
-        }
-        sh_found[wid] = (long long)(a + pu);
-    }
+    // (read across lanes with the whole wave active: under `lane == 0` the
+    // compiler may compute pos for lane 0 alone)
+    const uint64_t cand = __ballot(hit != 0u);
+    const long long pos = a + (hit ? __builtin_ctz(hit) : 0);
+    const int fl = cand ? (int)__builtin_ctzll(cand) : 0;
+    const long long first = ((long long)__builtin_amdgcn_readlane((int)(pos >> 32), fl) << 32) |
+                            (unsigned)__builtin_amdgcn_readlane((int)pos, fl);
+    if (lane == 0) sh_found[wid] = cand ? first : -1;
     __syncthreads();
     int64_t res = -1;
     for (int w2 = 0; w2 < kDWaves; ++w2)
@@ -1455,28 +1433,23 @@ __device__ bool pick_chunk(const ChainParams& P, const double* W, double u, int*
         const int lane = threadIdx.x;
         double tot = 0.0;
         for (int s0 = 0; s0 < P.splits; s0 += kWave) tot += (s0 + lane < P.splits) ? W[s0 + lane] : 0.0;
-        tot = wave_sum(tot);
+        tot = wave_bcast_f64(wave_incl_f64(tot), kWave - 1);
         const double t = u * tot;
         double carry = 0.0;
         int found = -1, lastpos = -1;
         double before = 0.0;
         for (int s0 = 0; s0 < P.splits && found < 0; s0 += kWave) {
             const double x = (s0 + lane < P.splits) ? W[s0 + lane] : 0.0;
-            double inc = x;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const double y = __shfl_up(inc, o, kWave);
-                if (lane >= o) inc += y;
-            }
+            const double inc = wave_incl_f64(x);
             const uint64_t hit = __ballot(s0 + lane < P.splits && carry + inc > t);
             const uint64_t pos = __ballot(s0 + lane < P.splits && x > 0.0);
             if (pos) lastpos = s0 + 63 - (int)__builtin_clzll(pos);
             if (hit) {
                 const int l = (int)__builtin_ctzll(hit);
                 found = s0 + l;
-                before = carry + __shfl(inc - x, l, kWave);
+                before = carry + wave_bcast_f64(inc - x, l);
             }
-            carry += __shfl(inc, kWave - 1, kWave);
+            carry += wave_bcast_f64(inc, kWave - 1);
         }
         if (lane == 0) {
             sh_ok = tot > 0.0 && tot < INFINITY && (found >= 0 || lastpos >= 0);
@@ -1756,16 +1729,11 @@ __device__ int32_t residual_draw(const ChainParams& P, const Draw& d, int r, dou
         const int lane = t;
         // the block of the chunk: inclusive running sums over kSubSums lanes
         const double x = lane < kSubSums ? sSub[lane] : 0.0;
-        double inc = x;
-#pragma unroll
-        for (int o = 1; o < kSubSums; o <<= 1) {
-            const double y = __shfl_up(inc, o, kWave);
-            if (lane >= o) inc += y;
-        }
+        const double inc = wave_incl_f64(x);
         const uint64_t hit = __ballot(lane < kSubSums && inc > rem);
         const uint64_t pos = __ballot(lane < kSubSums && x > 0.0);
         const int q = hit ? (int)__builtin_ctzll(hit) : (pos ? 63 - (int)__builtin_clzll(pos) : 0);
-        const double remq = hit ? rem - __shfl(inc - x, q, kWave) : INFINITY;
+        const double remq = hit ? rem - wave_bcast_f64(inc - x, q) : INFINITY;
         // lane l: vector v * kDBlock + 64 w + l of chunk c, both rows
         const int v = q / kDWaves, w = q % kDWaves;
         const int64_t e = (int64_t)c * P.chunk + ((int64_t)v * kDBlock + 64 * w + lane) * VEC;
@@ -1780,12 +1748,7 @@ __device__ int32_t residual_draw(const ChainParams& P, const Draw& d, int r, dou
             for (int k = 0; k < VEC; ++k) run[k] = 0.0f;
         }
         // running sum over the lanes (fp64), then the first lane that passes
-        double li = (double)wl;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const double y = __shfl_up(li, o, kWave);
-            if (lane >= o) li += y;
-        }
+        const double li = wave_incl_f64((double)wl);
         const double before = li - (double)wl;
         const uint64_t cross = __ballot(wl > 0.0f && li > remq);
         const uint64_t lpos = __ballot(wl > 0.0f);
