@@ -133,20 +133,43 @@ __device__ __forceinline__ void ngram_scan(const Text& x, int32_t* win, NgramSha
                 for (int64_t i = t; i < ns; i += NT) S.suf[i] = win[x.n - 1 - i];
                 __syncthreads();
             }
-            const int32_t s0 = S.suf[0];
+            static_assert(kPre == 4, "the first check reads three tokens back");
+            const int32_t s0 = S.suf[0], s1 = S.suf[1], s2 = S.suf[2], s3 = S.suf[3];
             uint32_t hits = 0;
 #pragma unroll
             for (int u = 0; u < NB; ++u) {
                 const int64_t j = base + t + (int64_t)u * NT;
                 hits |= (uint32_t)(j < jend && v[u] == s0) << u;
             }
+            // one text in one window (the usual case): its tokens straight from LDS
+            const bool whole = suf_in_win;
             while (hits) {
                 const int u = __builtin_ctz(hits);
                 hits &= hits - 1;
                 const int64_t j = base + t + (int64_t)u * NT;
                 const int64_t lim = (j + 1 < O.cap) ? j + 1 : O.cap;
+                // the three tokens before j read together (positions below 0
+                // read position 0; lim keeps them out of the count), then the
+                // run of matches they start: l as the token-by-token check
+                // up to kPre would find it
+                int32_t b1, b2, b3;
+                if (whole) {
+                    b1 = win[j >= 1 ? j - 1 : 0];
+                    b2 = win[j >= 2 ? j - 2 : 0];
+                    b3 = win[j >= 3 ? j - 3 : 0];
+                } else {
+                    b1 = at(j >= 1 ? j - 1 : 0);
+                    b2 = at(j >= 2 ? j - 2 : 0);
+                    b3 = at(j >= 3 ? j - 3 : 0);
+                }
                 int64_t l = 1;
-                while (l < lim && l < kPre && at(j - l) == S.suf[l]) ++l;
+                if (l < lim && b1 == s1) {
+                    l = 2;
+                    if (l < lim && b2 == s2) {
+                        l = 3;
+                        if (l < lim && b3 == s3) l = 4;
+                    }
+                }
                 if (l == kPre && l < lim) {
                     const int c = atomicAdd(&S.n_cand, 1);
                     if (c < NCAND) {
