@@ -143,6 +143,20 @@ __device__ __forceinline__ void ngram_scan(const Text& x, int32_t* win, NgramSha
             }
             // one text in one window (the usual case): its tokens straight from LDS
             const bool whole = suf_in_win;
+            // A hit whose previous token differs from s1 has l = 1, which
+            // matters only when n_min is 1.  With the text in the window, a
+            // wave that has hits reads every previous token at once (one
+            // independent LDS read per batch slot) and drops those hits, so a
+            // frequent last token does not cost a loop round per hit.
+            if (whole && O.n_min >= 2 && __ballot(hits != 0u) != 0) {
+                uint32_t keep = 0;
+#pragma unroll
+                for (int u = 0; u < NB; ++u) {
+                    const int64_t j = t + (int64_t)u * NT;
+                    keep |= (uint32_t)(win[j >= 1 ? j - 1 : 0] == s1) << u;
+                }
+                hits &= keep;
+            }
             while (hits) {
                 const int u = __builtin_ctz(hits);
                 hits &= hits - 1;
