@@ -71,6 +71,50 @@ def test_dense_headline_fused_draft():
     assert (dl[0::2] == c["max_draft"]).all() and (fused["ngram_feat"][0::2, 2] >= 20).all()
 
 
+def test_dense_draft_periodic_texts_and_full_candidate_list():
+    """The dense step's fused draft on periodic texts (n_min 5).  Requests 0
+    mod 4: 8,680-token texts whose body repeats the last four tokens of the
+    text before the drawn token, so about 2,170 positions match four tokens
+    and the candidate list (2,048) fills: the rest are extended in place.
+    Requests 1 and 2 mod 4: the body repeats those four tokens and the drawn
+    one, so every fifth position starts a match that runs to the comparison
+    cap.  Caps 5 and 256."""
+    c = synth.dense_headline(ctx_extra=64)
+    BS, V, B = c["BS"], c["V"], c["B"]
+    tgt = synth.as_torch_bf16(c["target_bf16"]).to("cuda:0").reshape(-1, V)
+    dft = synth.as_torch_bf16(c["draft_bf16"]).to("cuda:0").reshape(-1, V)
+    args = (tgt, dev(np.arange(BS, dtype=np.int64) * (B + 1)), dev(c["tokens"]), dev(np.full(BS, B, np.int32)),
+            c["temperature"])
+    kw = dict(u_accept=dev(c["u_acc"]), u_sample=dev(c["u_smp"]), slot_flags=dev(np.zeros((BS, B), np.uint8)),
+              draft_logits=dft, draft_row_base=dev(np.arange(BS, dtype=np.int64) * B), write_flags=True)
+    stride = 8704 + 16
+    ctx = np.zeros((BS, stride), np.int32)
+    ctx[:, :c["ctx"].shape[1]] = c["ctx"]
+    lens = c["ctx_len"].astype(np.int32).copy()
+    for cap in (256, 5):
+        ngram = (c["n_min"], c["n_max"], c["max_draft"], cap)
+        plain, _ = run_pair(*args, ctx, lens, stride, ngram, **kw)
+        acc = plain["out_accepted"]
+        cc, ll = ctx.copy(), lens.copy()
+        for r in range(BS):
+            if r % 4 == 3:
+                continue   # untouched
+            L0 = 8680 - int(acc[r]) if r % 4 == 0 else int(lens[r])   # long (overflow) or as generated
+            text = np.concatenate([c["ctx"][r, :min(L0, c["ctx"].shape[1])], np.zeros(max(0, L0 - c["ctx"].shape[1]),
+                                                                                     np.int32)])
+            tail = np.concatenate([text[L0 - 4:L0], plain["out_tokens"][r, :acc[r]]])[-4:]
+            y = plain["out_tokens"][r, acc[r]]
+            body = np.resize(tail if r % 4 == 0 else np.concatenate([tail, [y]]), L0 - 4)
+            cc[r, :L0 - 4] = body
+            cc[r, L0 - 4:L0] = text[L0 - 4:L0]
+            ll[r] = L0
+        print(f"periodic texts: cap {cap}, {int((np.arange(BS) % 4 == 0).sum())} of 8,680 tokens", flush=True)
+        plain, fused = run_pair(*args, cc, ll, stride, ngram, **kw)
+        dl = check(plain, fused, ngram)
+        ext = (np.arange(BS) % 4 == 1) | (np.arange(BS) % 4 == 2)
+        assert (dl[ext] > 0).all(), dl
+
+
 @pytest.mark.parametrize("T", [0.0, 1.0])
 def test_config0_overflow_and_long_contexts(T):
     """Commit overflow (the draft then scans the unchanged context), contexts
@@ -93,6 +137,12 @@ def test_config0_overflow_and_long_contexts(T):
     check(plain, fused, ngram)
     over = (plain["out_flags"].astype(np.uint32) & O.CTX_OVERFLOW) != 0
     assert over.any() and np.array_equal(fused["ctx_len"][over], lens[over])
+    # n_min 5 and the same texts (one decide workgroup per request at this
+    # vocabulary)
+    ngram5 = (5, 15, 15, 256)
+    plain, fused = run_pair(dev(c["target"]).reshape(-1, V), dev(np.arange(BS) * (B + 1)), dev(c["tokens"]),
+                            dev(np.full(BS, B, np.int32)), T, ctx, lens, cap, ngram5, **kw)
+    check(plain, fused, ngram5)
 
 
 def test_point_mass_chain_fused_draft():
