@@ -66,7 +66,7 @@ class TreeAlloc(C.Structure):
                 ("c_max", i32),
                 ("depth_max", i32), ("rows_cap", i32), ("node_token", vp), ("parent_row", vp), ("Q", vp),
                 ("n_rows", vp), ("row_base", vp), ("total_rows", vp), ("forest_count", vp), ("s_curve", vp),
-                ("out_flags", vp)]
+                ("out_flags", vp), ("forest_token", vp), ("forest_parent", vp), ("forest_q", vp), ("forest_n", vp)]
 
 
 class AllocArgs(C.Structure):
@@ -338,13 +338,17 @@ def tree_scores_struct(coef, h, sigma, r_share, psi_ctx, b_req, p_src, ngram_fea
     return st
 
 
-def _tree_alloc(block, ngram_draft, ngram_len, w_node=None, w_none=None, depth_max=32, rows_cap=16, out=None,
-                stream=None, scores=None, c_max=None, s_curve=False, ngram_follow=None):
+def _tree_alloc(block=None, ngram_draft=None, ngram_len=None, w_node=None, w_none=None, depth_max=32, rows_cap=16,
+                out=None, stream=None, scores=None, c_max=None, s_curve=False, ngram_follow=None, forest=None):
     """Tree build; weights w_node / w_none by candidate index, or ``scores``
     (the keyword arguments of tree_scores_struct) for the Eq. (6) form.  With
     ``s_curve`` the S(n) curve [bs, rows_cap] is returned as out["s_curve"].
     ``ngram_follow``: the chains' follower counts (spec_ngram_draft with
-    follow_ctx), or None when every chain token is copied."""
+    follow_ctx), or None when every chain token is copied.  ``forest``: a
+    caller-built forest (token int32 [bs, c_max], parent int32 [bs, c_max],
+    q float32 [bs, c_max], n int32 [bs]) instead of block and chains."""
+    if forest is not None:
+        return _tree_from_forest(forest, rows_cap, out, stream, s_curve)
     _dev(block, torch.int32, "block", 3)
     _dev(ngram_draft, torch.int32, "ngram_draft", 2)
     _dev(ngram_len, torch.int32, "ngram_len", 1)
@@ -361,16 +365,7 @@ def _tree_alloc(block, ngram_draft, ngram_len, w_node=None, w_none=None, depth_m
     bs, P, Kc = block.shape
     dev = block.device
     if out is None:
-        out = dict(node_token=torch.empty((bs, rows_cap), dtype=torch.int32, device=dev),
-                   parent_row=torch.empty((bs, rows_cap), dtype=torch.int32, device=dev),
-                   Q=torch.empty((bs, rows_cap), dtype=torch.float32, device=dev),
-                   n_rows=torch.empty(bs, dtype=torch.int32, device=dev),
-                   row_base=torch.empty(bs, dtype=torch.int64, device=dev),
-                   total_rows=torch.empty(1, dtype=torch.int32, device=dev),
-                   forest_count=torch.empty(bs, dtype=torch.int32, device=dev),
-                   out_flags=torch.empty(bs, dtype=torch.int32, device=dev))
-        if s_curve:
-            out["s_curve"] = torch.empty((bs, rows_cap), dtype=torch.float32, device=dev)
+        out = _tree_outputs(bs, rows_cap, dev, s_curve)
     st = None if scores is None else tree_scores_struct(**scores)
     ta = TreeAlloc(bs=bs, P=P, Kc=Kc, block=_ptr(block), ngram_draft=_ptr(ngram_draft),
                    ngram_ld=ngram_draft.shape[1], ngram_len=_ptr(ngram_len), ngram_follow=_ptr(ngram_follow),
@@ -380,6 +375,38 @@ def _tree_alloc(block, ngram_draft, ngram_len, w_node=None, w_none=None, depth_m
                    **{k: _ptr(v) for k, v in out.items()})
     a = AllocArgs(mode=ALLOC_TREE, tree=ta)
     _check(lib().spec_allocate_budget(C.byref(a), _stream(dev, stream)))
+    return out
+
+
+def _tree_outputs(bs, rows_cap, dev, s_curve):
+    out = dict(node_token=torch.empty((bs, rows_cap), dtype=torch.int32, device=dev),
+               parent_row=torch.empty((bs, rows_cap), dtype=torch.int32, device=dev),
+               Q=torch.empty((bs, rows_cap), dtype=torch.float32, device=dev),
+               n_rows=torch.empty(bs, dtype=torch.int32, device=dev),
+               row_base=torch.empty(bs, dtype=torch.int64, device=dev),
+               total_rows=torch.empty(1, dtype=torch.int32, device=dev),
+               forest_count=torch.empty(bs, dtype=torch.int32, device=dev),
+               out_flags=torch.empty(bs, dtype=torch.int32, device=dev))
+    if s_curve:
+        out["s_curve"] = torch.empty((bs, rows_cap), dtype=torch.float32, device=dev)
+    return out
+
+
+def _tree_from_forest(forest, rows_cap, out, stream, s_curve):
+    token, parent, q, n = forest
+    _dev(token, torch.int32, "forest token", 2)
+    _dev(parent, torch.int32, "forest parent", 2)
+    _dev(q, torch.float32, "forest q", 2)
+    _dev(n, torch.int32, "forest n", 1)
+    bs, c_max = token.shape
+    if tuple(parent.shape) != (bs, c_max) or tuple(q.shape) != (bs, c_max) or n.shape[0] != bs:
+        raise ValueError("forest token, parent and q must be [bs, c_max] and n [bs]")
+    if out is None:
+        out = _tree_outputs(bs, rows_cap, token.device, s_curve)
+    ta = TreeAlloc(bs=bs, c_max=int(c_max), rows_cap=rows_cap, forest_token=_ptr(token), forest_parent=_ptr(parent),
+                   forest_q=_ptr(q), forest_n=_ptr(n), **{k: _ptr(v) for k, v in out.items()})
+    a = AllocArgs(mode=ALLOC_TREE, tree=ta)
+    _check(lib().spec_allocate_budget(C.byref(a), _stream(token.device, stream)))
     return out
 
 

@@ -460,6 +460,111 @@ __device__ __forceinline__ double shfl_f64(double v, int l)
 // A global-memory int32 pointer, kept apart from LDS pointers.
 typedef const __attribute__((address_space(1))) int32_t* gi32_ptr;
 
+// Best-first rank of nodes 1..cnt-1 by (fp32 Q descending, index ascending),
+// S(n), the depth-first layout of the chosen set and the request's outputs
+// ([AS] Section 3.1).  The forest's tokens, parents and Q are in LDS, with
+// fsel zero for every node; one wave per request.
+__device__ __forceinline__ void tree_rows(const spec_tree_alloc& A, int r, int lane, int cnt, uint32_t flags,
+                                          const int32_t* ftok, const int32_t* fpar, const double* fQ, uint8_t* fsel)
+{
+    __shared__ double sQrank[SPEC_MAX_ROWS];
+    // best-first: rank by (fp32 Q desc, index asc); keep rank < rows_cap - 1
+    const int keep = A.rows_cap - 1;
+    for (int j = 1 + lane; j < cnt; j += kWave) {
+        const uint64_t kj = ((uint64_t)__float_as_uint((float)fQ[j]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+        int rank = 0;
+        for (int i = 1; i < cnt; ++i) {
+            const uint64_t ki = ((uint64_t)__float_as_uint((float)fQ[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+            rank += ki > kj;
+        }
+        fsel[j] = rank < keep;
+        if (rank < A.rows_cap) sQrank[rank] = fQ[j];
+    }
+    __syncthreads();
+    if (A.s_curve) {
+        // S(n): the first n - 1 nodes of the best-first order, accumulated in
+        // order (lane n - 1 holds the (n - 1)-th Q)
+        const double v = (lane < A.rows_cap && lane < cnt - 1) ? sQrank[lane] : 0.0;
+        double acc = 0.0, mine = 0.0;
+        for (int n = 1; n <= A.rows_cap; ++n) {
+            mine = lane == n - 1 ? acc : mine;
+            if (n - 1 < cnt - 1) acc += readlane_f64(v, n - 1);
+        }
+        if (lane < A.rows_cap) A.s_curve[(int64_t)r * A.rows_cap + lane] = (float)mine;
+    }
+    // Depth-first layout, children in index order, by the whole wave.  The
+    // selected nodes (the anchor and at most rows_cap - 1 candidates, a
+    // parent-closed set) are compacted in index order, node i on lane i, each
+    // knowing its parent's compact position; a wave-uniform walk then keeps a
+    // mask of the unvisited children of every node on the current path (lane
+    // d holds depth d's) and always takes the lowest one.
+    __shared__ int32_t scomp[SPEC_MAX_ROWS];      // compact position -> forest node
+    __shared__ int16_t scpos[SPEC_MAX_FOREST];    // forest node -> compact position
+    if (lane == 0) fsel[0] = 1;
+    __syncthreads();
+    int m = 0;
+    for (int base = 0; base < cnt; base += kWave) {
+        const int c = base + lane;
+        const bool sel = c < cnt && fsel[c];
+        const uint64_t bal = __ballot(sel);
+        const int at = m + (int)__popcll(bal & ((1ull << lane) - 1ull));
+        if (sel && at < SPEC_MAX_ROWS) {
+            scomp[at] = c;
+            scpos[c] = (int16_t)at;
+        }
+        m += (int)__popcll(bal);
+    }
+    m = m < A.rows_cap ? m : A.rows_cap;
+    __syncthreads();
+    const int mynode = lane < m ? scomp[lane] : -1;
+    const int myparent = (lane < m && lane > 0) ? (int)scpos[fpar[mynode]] : -1;
+    auto children = [&](int u) -> uint64_t { return __builtin_amdgcn_ballot_w64(lane < m && myparent == u); };
+    // lane d: the unvisited children of the path's depth-d node and that
+    // node's row; lane k: row k's compact node and parent row
+    const uint64_t kids0 = children(0);
+    uint32_t stk_lo = lane == 0 ? (uint32_t)kids0 : 0u, stk_hi = lane == 0 ? (uint32_t)(kids0 >> 32) : 0u;
+    int stk_row = 0, ord = lane == 0 ? 0 : -1, prow = -1;
+    int row = 1, d = 0;
+    while (row < m) {
+        // the deepest node on the path with an unvisited child (every level
+        // below it is done: one ballot instead of a pop per level)
+        const uint64_t open = __builtin_amdgcn_ballot_w64(lane <= d && (stk_lo | stk_hi) != 0u);
+        if (!open) break;
+        d = 63 - (int)__builtin_clzll(open);
+        const uint64_t top = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)stk_hi, d) << 32)
+                           | (uint32_t)__builtin_amdgcn_readlane((int)stk_lo, d);
+        const int c = (int)__builtin_ctzll(top);
+        const uint64_t kids = children(c);
+        const int prw = __builtin_amdgcn_readlane(stk_row, d);
+        const uint64_t rest = top & (top - 1);
+        stk_lo = lane == d ? (uint32_t)rest : (lane == d + 1 ? (uint32_t)kids : stk_lo);
+        stk_hi = lane == d ? (uint32_t)(rest >> 32) : (lane == d + 1 ? (uint32_t)(kids >> 32) : stk_hi);
+        stk_row = lane == d + 1 ? row : stk_row;
+        ord = lane == row ? c : ord;
+        prow = lane == row ? prw : prow;
+        ++d;
+        ++row;
+    }
+    int32_t* nt = A.node_token + (int64_t)r * A.rows_cap;
+    int32_t* pr = A.parent_row + (int64_t)r * A.rows_cap;
+    float* Qo = A.Q + (int64_t)r * A.rows_cap;
+    const int u = __shfl(mynode, ord < 0 ? 0 : ord, kWave);   // row lane's forest node
+    if (lane < A.rows_cap) {
+        if (lane < row) {
+            nt[lane] = (u == 0) ? -1 : ftok[u];
+            pr[lane] = prow;
+            Qo[lane] = (float)fQ[u];
+        } else {
+            nt[lane] = -1; pr[lane] = -1; Qo[lane] = 0.0f;
+        }
+    }
+    if (lane == 0) {
+        A.n_rows[r] = row;
+        A.forest_count[r] = cnt;
+        A.out_flags[r] = flags;
+    }
+}
+
 // NS register slots per lane: forest node j lives on lane j % 64 in slot
 // j / 64 during the chain walk (NS * 64 >= c_max).
 template <int NS>
@@ -481,7 +586,6 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
     __shared__ int8_t fbucket[SPEC_MAX_FOREST];
     __shared__ int8_t fagree[SPEC_MAX_FOREST];
     __shared__ double fw[SPEC_MAX_FOREST];
-    __shared__ double sQrank[SPEC_MAX_ROWS];
     __shared__ int32_t sh_cnt;
     // the chains' tokens, lengths and evidence classes, staged in one round
     // trip (the tokens when they fit)
@@ -809,101 +913,67 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
         }
     }
     __syncthreads();
-    // best-first: rank by (fp32 Q desc, index asc); keep rank < rows_cap - 1
-    const int keep = A.rows_cap - 1;
-    for (int j = 1 + lane; j < cnt; j += kWave) {
-        const uint64_t kj = ((uint64_t)__float_as_uint((float)fQ[j]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
-        int rank = 0;
-        for (int i = 1; i < cnt; ++i) {
-            const uint64_t ki = ((uint64_t)__float_as_uint((float)fQ[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
-            rank += ki > kj;
-        }
-        fsel[j] = rank < keep;
-        if (rank < A.rows_cap) sQrank[rank] = fQ[j];
+    tree_rows(A, r, lane, cnt, flags, ftok, fpar, fQ, fsel);
+}
+
+// Rows from a forest the caller built ([AS] Section 3.1): one wave per
+// request.  Node j's path probability is its parent's times q_j (fp64, in
+// index order, parents first); the rows are then chosen and laid out as in
+// the tree build.  A parent outside [0, j) or a q outside [0, 1] breaks the
+// forest: the request is flagged and keeps the anchor alone.
+__global__ __launch_bounds__(kWave) void k_tree_forest(spec_tree_alloc A)
+{
+    const int r = blockIdx.x, lane = threadIdx.x;
+    __shared__ int32_t ftok[SPEC_MAX_FOREST];
+    __shared__ int32_t fpar[SPEC_MAX_FOREST];
+    __shared__ float fq[SPEC_MAX_FOREST];
+    __shared__ double fQ[SPEC_MAX_FOREST];
+    __shared__ uint8_t fsel[SPEC_MAX_FOREST];
+    const int cmax = A.c_max;
+    const int64_t o = (int64_t)r * cmax;
+    uint32_t flags = 0;
+    int n = A.forest_n[r];
+    if (n < 1 || n > cmax) {
+        flags |= SPEC_FLAG_BAD_LENGTH;
+        n = n < 1 ? 1 : cmax;
+    }
+    bool bad = false;
+    for (int j = lane; j < n; j += kWave) {
+        const int32_t tk = A.forest_token[o + j];
+        const int32_t p = A.forest_parent[o + j];
+        const float q = A.forest_q[o + j];
+        ftok[j] = tk;
+        fpar[j] = j == 0 ? -1 : p;
+        fq[j] = q;
+        fsel[j] = 0;
+        bad |= j > 0 && (p < 0 || p >= j || !(q >= 0.0f && q <= 1.0f));
+    }
+    if (__ballot(bad)) {
+        flags |= SPEC_FLAG_BAD_FOREST;
+        n = 1;
     }
     __syncthreads();
-    if (A.s_curve) {
-        // S(n): the first n - 1 nodes of the best-first order, accumulated in
-        // order (lane n - 1 holds the (n - 1)-th Q)
-        const double v = (lane < A.rows_cap && lane < cnt - 1) ? sQrank[lane] : 0.0;
-        double acc = 0.0, mine = 0.0;
-        for (int n = 1; n <= A.rows_cap; ++n) {
-            mine = lane == n - 1 ? acc : mine;
-            if (n - 1 < cnt - 1) acc += readlane_f64(v, n - 1);
+    // Q in batches of 64 nodes, node base + l on lane l: a parent in an
+    // earlier batch is read from LDS, one in the same batch from its lane, in
+    // index order so that it is final when its children read it
+    for (int base = 0; base < n; base += kWave) {
+        const int j = base + lane;
+        const bool mine = j < n;
+        const int p = mine ? fpar[j] : -1;
+        const double qj = mine ? (double)fq[j] : 0.0;
+        double Qv = j == 0 ? 1.0 : ((mine && p < base) ? fQ[p] * qj : 0.0);
+        const int hi = n - base < kWave ? n - base : kWave;
+        for (int l = 0; l < hi; ++l) {
+            const int pl = __builtin_amdgcn_readlane(p, l);
+            if (pl >= base) {   // wave-uniform
+                const double qp = readlane_f64(Qv, pl - base);
+                Qv = lane == l ? qp * qj : Qv;
+            }
         }
-        if (lane < A.rows_cap) A.s_curve[(int64_t)r * A.rows_cap + lane] = (float)mine;
+        if (mine) fQ[j] = Qv;
+        __syncthreads();
     }
-    // Depth-first layout, children in index order, by the whole wave.  The
-    // selected nodes (the anchor and at most rows_cap - 1 candidates, a
-    // parent-closed set) are compacted in index order, node i on lane i, each
-    // knowing its parent's compact position; a wave-uniform walk then keeps a
-    // mask of the unvisited children of every node on the current path (lane
-    // d holds depth d's) and always takes the lowest one.
-    __shared__ int32_t scomp[SPEC_MAX_ROWS];      // compact position -> forest node
-    __shared__ int16_t scpos[SPEC_MAX_FOREST];    // forest node -> compact position
-    if (lane == 0) fsel[0] = 1;
-    __syncthreads();
-    int m = 0;
-    for (int base = 0; base < cnt; base += kWave) {
-        const int c = base + lane;
-        const bool sel = c < cnt && fsel[c];
-        const uint64_t bal = __ballot(sel);
-        const int at = m + (int)__popcll(bal & ((1ull << lane) - 1ull));
-        if (sel && at < SPEC_MAX_ROWS) {
-            scomp[at] = c;
-            scpos[c] = (int16_t)at;
-        }
-        m += (int)__popcll(bal);
-    }
-    m = m < A.rows_cap ? m : A.rows_cap;
-    __syncthreads();
-    const int mynode = lane < m ? scomp[lane] : -1;
-    const int myparent = (lane < m && lane > 0) ? (int)scpos[fpar[mynode]] : -1;
-    auto children = [&](int u) -> uint64_t { return __builtin_amdgcn_ballot_w64(lane < m && myparent == u); };
-    // lane d: the unvisited children of the path's depth-d node and that
-    // node's row; lane k: row k's compact node and parent row
-    const uint64_t kids0 = children(0);
-    uint32_t stk_lo = lane == 0 ? (uint32_t)kids0 : 0u, stk_hi = lane == 0 ? (uint32_t)(kids0 >> 32) : 0u;
-    int stk_row = 0, ord = lane == 0 ? 0 : -1, prow = -1;
-    int row = 1, d = 0;
-    while (row < m) {
-        // the deepest node on the path with an unvisited child (every level
-        // below it is done: one ballot instead of a pop per level)
-        const uint64_t open = __builtin_amdgcn_ballot_w64(lane <= d && (stk_lo | stk_hi) != 0u);
-        if (!open) break;
-        d = 63 - (int)__builtin_clzll(open);
-        const uint64_t top = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)stk_hi, d) << 32)
-                           | (uint32_t)__builtin_amdgcn_readlane((int)stk_lo, d);
-        const int c = (int)__builtin_ctzll(top);
-        const uint64_t kids = children(c);
-        const int prw = __builtin_amdgcn_readlane(stk_row, d);
-        const uint64_t rest = top & (top - 1);
-        stk_lo = lane == d ? (uint32_t)rest : (lane == d + 1 ? (uint32_t)kids : stk_lo);
-        stk_hi = lane == d ? (uint32_t)(rest >> 32) : (lane == d + 1 ? (uint32_t)(kids >> 32) : stk_hi);
-        stk_row = lane == d + 1 ? row : stk_row;
-        ord = lane == row ? c : ord;
-        prow = lane == row ? prw : prow;
-        ++d;
-        ++row;
-    }
-    int32_t* nt = A.node_token + (int64_t)r * A.rows_cap;
-    int32_t* pr = A.parent_row + (int64_t)r * A.rows_cap;
-    float* Qo = A.Q + (int64_t)r * A.rows_cap;
-    const int u = __shfl(mynode, ord < 0 ? 0 : ord, kWave);   // row lane's forest node
-    if (lane < A.rows_cap) {
-        if (lane < row) {
-            nt[lane] = (u == 0) ? -1 : ftok[u];
-            pr[lane] = prow;
-            Qo[lane] = (float)fQ[u];
-        } else {
-            nt[lane] = -1; pr[lane] = -1; Qo[lane] = 0.0f;
-        }
-    }
-    if (lane == 0) {
-        A.n_rows[r] = row;
-        A.forest_count[r] = cnt;
-        A.out_flags[r] = flags;
-    }
+    tree_rows(A, r, lane, n, flags, ftok, fpar, fQ, fsel);
 }
 
 __global__ __launch_bounds__(kAllocBlock) void k_rows_scan(const int32_t* n_rows, int bs, int64_t* row_base, int32_t* total_rows)
@@ -948,7 +1018,8 @@ int spec_alloc_launch(const spec_alloc_args* a, hipStream_t st)
         else std::memset(&P.sc, 0, sizeof(P.sc));
         const int c = a->tree.c_max;
         const dim3 g(a->tree.bs), b(kWave);
-        if (c <= 64) hipLaunchKernelGGL(k_tree<1>, g, b, 0, st, P);
+        if (a->tree.forest_token) hipLaunchKernelGGL(k_tree_forest, g, b, 0, st, a->tree);
+        else if (c <= 64) hipLaunchKernelGGL(k_tree<1>, g, b, 0, st, P);
         else if (c <= 128) hipLaunchKernelGGL(k_tree<2>, g, b, 0, st, P);
         else if (c <= 256) hipLaunchKernelGGL(k_tree<4>, g, b, 0, st, P);
         else if (c <= 512) hipLaunchKernelGGL(k_tree<8>, g, b, 0, st, P);

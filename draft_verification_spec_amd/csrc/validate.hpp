@@ -51,6 +51,14 @@ inline int check_chain_alloc(const spec_chain_alloc* c)
 inline int check_tree_alloc(const spec_tree_alloc* t)
 {
     REQUIRE(t->bs >= 1);
+    REQUIRE(t->rows_cap >= 1 && t->rows_cap <= SPEC_MAX_ROWS);
+    REQUIRE(t->node_token && t->parent_row && t->Q && t->n_rows && t->row_base && t->total_rows);
+    REQUIRE(t->forest_count && t->out_flags);
+    if (t->forest_token) {   // a caller-built forest
+        REQUIRE(t->forest_parent && t->forest_q && t->forest_n && !t->scores);
+        REQUIRE(t->c_max >= 1 && t->c_max <= SPEC_MAX_FOREST);
+        return SPEC_OK;
+    }
     REQUIRE(t->P >= 0 && t->Kc >= 1);
     REQUIRE(t->P == 0 || t->block);
     REQUIRE(t->c_max >= 1 + t->P * t->Kc && t->c_max <= SPEC_MAX_FOREST);
@@ -62,9 +70,6 @@ inline int check_tree_alloc(const spec_tree_alloc* t)
         REQUIRE(sc->psi_ctx && sc->b_req && sc->p_src && sc->ngram_feat);
     }
     REQUIRE(t->depth_max >= 1);
-    REQUIRE(t->rows_cap >= 1 && t->rows_cap <= SPEC_MAX_ROWS);
-    REQUIRE(t->node_token && t->parent_row && t->Q && t->n_rows && t->row_base && t->total_rows);
-    REQUIRE(t->forest_count && t->out_flags);
     return SPEC_OK;
 }
 

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 5
+#define SPEC_ABI_VERSION 6
 
 /* ---- return codes ---------------------------------------------------- */
 #define SPEC_OK          0
@@ -71,6 +71,10 @@ extern "C" {
                                               the drawing workgroup summed the
                                               residual again itself (same result up
                                               to rounding order)                     */
+#define SPEC_FLAG_BAD_FOREST    (1u << 13) /* a caller-built forest broke its rules
+                                              (a parent not below its child, or a q
+                                              outside [0, 1]): its rows are the
+                                              anchor alone                           */
 
 /* ---- slot flags (chain slots) ----------------------------------------- */
 #define SPEC_SLOT_POINT_MASS 1u  /* verify as a point mass, q = delta_y         */
@@ -186,6 +190,14 @@ typedef struct spec_ngram_args {
  * parent's children), Q = product of q along the path; the best rows_cap-1
  * candidates by Q (ties to the lower index) laid out depth-first (row 0 = the
  * anchor, children in index order).
+ * A forest the caller built (forest_token != NULL; [AS] Section 3.1 takes any
+ * drafter's candidate forest): node j's parent index lies in [0, j), node 0
+ * is the anchor, and q_j in [0, 1] is its acceptance estimate given that its
+ * parent is accepted.  Then Q_j = Q_parent q_j (fp64, Q = 1 at the anchor) and
+ * the rows are chosen and laid out as above; block, the n-gram chains, the
+ * weights and depth_max are not read (scores must be NULL).  A forest that
+ * breaks a rule is flagged (SPEC_FLAG_BAD_FOREST) and keeps the anchor
+ * alone; forest_n outside [1, c_max] is clamped (SPEC_FLAG_BAD_LENGTH).
  * ======================================================================== */
 typedef struct spec_estimator {
     float beta[15];              /* per-position intercepts                       */
@@ -292,6 +304,12 @@ typedef struct spec_tree_alloc {
                                     nodes of the best-first order ([AS] Section
                                     3.1; one walk down the order gives every n)   */
     uint32_t* out_flags;         /* device [bs], written                          */
+    const int32_t* forest_token; /* device [bs, c_max] or NULL: a caller-built
+                                    forest's tokens (node 0, the anchor: unread)  */
+    const int32_t* forest_parent;/* device [bs, c_max] parent index, in [0, j)    */
+    const float* forest_q;       /* device [bs, c_max] acceptance estimate of a
+                                    node given its parent, in [0, 1]              */
+    const int32_t* forest_n;     /* device [bs] nodes incl. the anchor, 1..c_max  */
 } spec_tree_alloc;
 
 typedef struct spec_alloc_args {

@@ -25,7 +25,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 # flag bits (same meanings as the library's per-request out_flags)
 ACCEPT_NEAR, SAMPLE_NEAR, SELECT_NEAR, ALLOC_NEAR, TREE_NEAR, RESIDUAL_ZERO = (1 << i for i in range(6))
-BAD_TOKEN, BAD_LOGITS, CTX_OVERFLOW = 1 << 8, 1 << 9, 1 << 10
+BAD_TOKEN, BAD_LOGITS, CTX_OVERFLOW, BAD_LENGTH, BAD_FOREST = 1 << 8, 1 << 9, 1 << 10, 1 << 11, 1 << 13
 NEAR_MASK = ACCEPT_NEAR | SAMPLE_NEAR | SELECT_NEAR | ALLOC_NEAR | TREE_NEAR
 SLOT_POINT_MASS, SLOT_FROM_NGRAM = 1, 2
 POLICIES = {"proposed": 0, "ngram_first": 1, "extension": 2, "model_only": 3, "ngram_only": 4}
@@ -47,6 +47,7 @@ def _load(path):
     h.oracle_chain_value.restype = C.c_double
     h.oracle_select.restype = C.c_int
     h.oracle_tree_build.restype = C.c_int
+    h.oracle_tree_forest.restype = C.c_int
     h.oracle_size_budget.restype = C.c_int
     h.oracle_step_cost.restype = C.c_double
     return h
@@ -441,6 +442,46 @@ def tree_build_batch(block, ng_draft, ng_len, w_node=None, w_none=None, depth_ma
         out["count"][r] = t["count"]
         out["flags"][r] = t["flag"]
         out["forests"].append(t)
+    out["row_base"] = np.concatenate([[0], np.cumsum(out["n_rows"])[:-1]]).astype(np.int64)
+    return out
+
+
+def tree_forest(token, parent, q, n, rows_cap=16):
+    """Rows from a caller-built forest of one request: token, parent [c_max]
+    (node 0 = the anchor), q [c_max] fp32 acceptance estimates given the
+    parent, n nodes incl. the anchor.  Returns the verify rows, the S(n)
+    curve, the path products and the flags."""
+    token = _c(token, np.int32)
+    parent = _c(parent, np.int32)
+    q = _c(q, np.float32)
+    c_max = len(token)
+    node_token = np.full(rows_cap, -1, np.int32)
+    parent_row = np.full(rows_cap, -1, np.int32)
+    Q = np.zeros(rows_cap, np.float64)
+    S_curve = np.zeros(rows_cap, np.float64)
+    fQ = np.zeros(c_max, np.float64)
+    n_rows = C.c_int32(0)
+    flag = C.c_uint32(0)
+    used = lib().oracle_tree_forest(C.c_int(int(n)), C.c_int(c_max), _p(token), _p(parent), _p(q), C.c_int(rows_cap),
+                                    _p(node_token), _p(parent_row), _p(Q), C.byref(n_rows), _p(S_curve), _p(fQ),
+                                    C.byref(flag))
+    return dict(node_token=node_token, parent_row=parent_row, Q=Q, n_rows=n_rows.value, count=used,
+                S_curve=S_curve, f_Q=fQ[:used], flag=flag.value)
+
+
+def tree_forest_batch(token, parent, q, n, rows_cap=16):
+    """token, parent, q [BS, c_max]; n [BS]."""
+    BS = token.shape[0]
+    out = dict(node_token=np.full((BS, rows_cap), -1, np.int32), parent_row=np.full((BS, rows_cap), -1, np.int32),
+               Q=np.zeros((BS, rows_cap)), n_rows=np.zeros(BS, np.int32), count=np.zeros(BS, np.int32),
+               flags=np.zeros(BS, np.uint32), S_curve=np.zeros((BS, rows_cap)))
+    for r in range(BS):
+        t = tree_forest(token[r], parent[r], q[r], n[r], rows_cap)
+        for k in ("node_token", "parent_row", "Q", "S_curve"):
+            out[k][r] = t[k]
+        out["n_rows"][r] = t["n_rows"]
+        out["count"][r] = t["count"]
+        out["flags"][r] = t["flag"]
     out["row_base"] = np.concatenate([[0], np.cumsum(out["n_rows"])[:-1]]).astype(np.int64)
     return out
 

@@ -38,6 +38,8 @@
 #define OF_BAD_TOKEN     (1u << 8)  /* a draft token outside [0, V)              */
 #define OF_BAD_LOGITS    (1u << 9)  /* a row with non-finite statistics          */
 #define OF_CTX_OVERFLOW  (1u << 10) /* commit would exceed the context capacity  */
+#define OF_BAD_LENGTH    (1u << 11) /* a length argument was clamped             */
+#define OF_BAD_FOREST    (1u << 13) /* a given forest broke its rules            */
 
 #define NEAR_EPS 1e-6
 
@@ -745,6 +747,71 @@ void oracle_commit(int bs, int32_t* ctx, int64_t ctx_stride, int32_t* ctx_len, i
     }
 }
 
+/* Best-first selection of rows_cap - 1 candidates by Q (fp32 Q descending,
+ * then index ascending), the S(n) curve, and the depth-first row layout
+ * with children in index order ([AS] Section 3.1; Proposition 1 makes the
+ * selected set parent-closed when Q does not grow along a path).  Node 0 is
+ * the anchor; every parent index is below its child's. */
+static void select_layout(int cnt, const int32_t* f_token, const int32_t* f_parent, const double* f_Q,
+                          int rows_cap, int32_t* node_token, int32_t* parent_row, double* Q_out,
+                          int32_t* n_rows, double* S_curve, uint32_t* flag)
+{
+    /* best-first selection of rows_cap - 1 candidates */
+    int* order = (int*)malloc(sizeof(int) * (size_t)cnt);
+    int m = 0;
+    for (int j = 1; j < cnt; ++j) order[m++] = j;
+    for (int a = 1; a < m; ++a) {           /* insertion sort: Q desc (fp32), index asc */
+        int x = order[a];
+        int b = a - 1;
+        while (b >= 0) {
+            float qb = (float)f_Q[order[b]], qx = (float)f_Q[x];
+            int before = (qx > qb) || (qx == qb && x < order[b]);
+            if (!before) break;
+            order[b + 1] = order[b]; --b;
+        }
+        order[b + 1] = x;
+    }
+    int take = rows_cap - 1 < m ? rows_cap - 1 : m;
+    for (int a = 0; a < take; ++a)
+        for (int b = take; b < m; ++b) {
+            double qa = f_Q[order[a]], qb = f_Q[order[b]];
+            double d = fabs(qa - qb), ref = qa > qb ? qa : qb;
+            if (d > 0.0 && d <= NEAR_EPS * ref) *flag |= OF_TREE_NEAR;
+        }
+    char* sel = (char*)calloc((size_t)cnt, 1);
+    sel[0] = 1;
+    for (int a = 0; a < take; ++a) sel[order[a]] = 1;
+    /* S(n) for every width n: the first n - 1 nodes of the best-first order
+     * ([AS] Section 3.1: a single walk down that order yields S at every
+     * width) */
+    if (S_curve) {
+        double acc = 0.0;
+        for (int n = 1; n <= rows_cap; ++n) {
+            S_curve[n - 1] = acc;
+            if (n - 1 < m) acc += f_Q[order[n - 1]];
+        }
+    }
+    /* depth-first layout; an explicit stack of (node, parent row) */
+    int* stack_n = (int*)malloc(sizeof(int) * (size_t)cnt);
+    int* stack_p = (int*)malloc(sizeof(int) * (size_t)cnt);
+    int sp = 0, row = 0;
+    stack_n[sp] = 0; stack_p[sp] = -1; ++sp;
+    for (int i = 0; i < rows_cap; ++i) { node_token[i] = -1; parent_row[i] = -1; Q_out[i] = 0.0; }
+    while (sp > 0) {
+        --sp;
+        int u = stack_n[sp], pr = stack_p[sp];
+        node_token[row] = (u == 0) ? -1 : f_token[u];
+        parent_row[row] = pr;
+        Q_out[row] = f_Q[u];
+        int my = row++;
+        /* push children in reverse index order so the lowest index pops first */
+        for (int c = cnt - 1; c >= 1; --c)
+            if (sel[c] && f_parent[c] == u) { stack_n[sp] = c; stack_p[sp] = my; ++sp; }
+    }
+    *n_rows = row;
+    free(order); free(sel); free(stack_n); free(stack_p);
+}
+
 /* ======================================================================
  * Tree build for one request.  [AS] Section 2.2 (tree shape), Section 3.1
  * (best-first order, Proposition 1, Eq. (1)), Section 3.3 ("N-gram
@@ -904,62 +971,45 @@ int oracle_tree_build(int P, int Kc, const int32_t* block, int L, const int32_t*
         for (int c = 1; c < cnt; ++c) if (f_parent[c] == par) den += wn[c];
         f_Q[j] = f_Q[par] * (wn[j] / den);
     }
-    /* best-first selection of rows_cap - 1 candidates */
-    int* order = (int*)malloc(sizeof(int) * (size_t)cnt);
-    int m = 0;
-    for (int j = 1; j < cnt; ++j) order[m++] = j;
-    for (int a = 1; a < m; ++a) {           /* insertion sort: Q desc (fp32), index asc */
-        int x = order[a];
-        int b = a - 1;
-        while (b >= 0) {
-            float qb = (float)f_Q[order[b]], qx = (float)f_Q[x];
-            int before = (qx > qb) || (qx == qb && x < order[b]);
-            if (!before) break;
-            order[b + 1] = order[b]; --b;
-        }
-        order[b + 1] = x;
-    }
-    int take = rows_cap - 1 < m ? rows_cap - 1 : m;
-    for (int a = 0; a < take; ++a)
-        for (int b = take; b < m; ++b) {
-            double qa = f_Q[order[a]], qb = f_Q[order[b]];
-            double d = fabs(qa - qb), ref = qa > qb ? qa : qb;
-            if (d > 0.0 && d <= NEAR_EPS * ref) *flag |= OF_TREE_NEAR;
-        }
-    char* sel = (char*)calloc((size_t)cnt, 1);
-    sel[0] = 1;
-    for (int a = 0; a < take; ++a) sel[order[a]] = 1;
-    /* S(n) for every width n: the first n - 1 nodes of the best-first order
-     * ([AS] Section 3.1: a single walk down that order yields S at every
-     * width) */
-    if (S_curve) {
-        double acc = 0.0;
-        for (int n = 1; n <= rows_cap; ++n) {
-            S_curve[n - 1] = acc;
-            if (n - 1 < m) acc += f_Q[order[n - 1]];
-        }
-    }
-    /* depth-first layout; an explicit stack of (node, parent row) */
-    int* stack_n = (int*)malloc(sizeof(int) * (size_t)cnt);
-    int* stack_p = (int*)malloc(sizeof(int) * (size_t)cnt);
-    int sp = 0, row = 0;
-    stack_n[sp] = 0; stack_p[sp] = -1; ++sp;
-    for (int i = 0; i < rows_cap; ++i) { node_token[i] = -1; parent_row[i] = -1; Q_out[i] = 0.0; }
-    while (sp > 0) {
-        --sp;
-        int u = stack_n[sp], pr = stack_p[sp];
-        node_token[row] = (u == 0) ? -1 : f_token[u];
-        parent_row[row] = pr;
-        Q_out[row] = f_Q[u];
-        int my = row++;
-        /* push children in reverse index order so the lowest index pops first */
-        for (int c = cnt - 1; c >= 1; --c)
-            if (sel[c] && f_parent[c] == u) { stack_n[sp] = c; stack_p[sp] = my; ++sp; }
-    }
-    *n_rows = row;
-    free(depth); free(order); free(sel); free(stack_n); free(stack_p);
+    select_layout(cnt, f_token, f_parent, f_Q, rows_cap, node_token, parent_row, Q_out, n_rows, S_curve, flag);
+    free(depth);
     free(above); free(nbucket); free(agree_b); free(wn); free(wz);
     return cnt;
+}
+
+/* ======================================================================
+ * Rows from a forest the caller built.  [AS] Section 3.1: the candidate
+ * forest is any drafter's; a node's acceptance estimate q_j is the chance
+ * it is accepted given that its parent is, so its path probability is
+ * Q_j = Q_parent(j) q_j with Q = 1 at the anchor (node 0), taken in index
+ * order since every parent index is below its child's.  The rows are then
+ * the best-first selection and depth-first layout of the tree build.
+ * n is clamped to [1, c_max] (flagged).  A node whose parent is not in
+ * [0, j) or whose q is not in [0, 1] (NaN included) breaks the forest: the
+ * request is flagged and its rows are the anchor alone.  Returns the number
+ * of nodes used.
+ * ====================================================================== */
+int oracle_tree_forest(int n, int c_max, const int32_t* token, const int32_t* parent, const float* q, int rows_cap,
+                       int32_t* node_token, int32_t* parent_row, double* Q_out, int32_t* n_rows, double* S_curve,
+                       double* f_Q, uint32_t* flag)
+{
+    if (n < 1 || n > c_max) {
+        *flag |= OF_BAD_LENGTH;
+        n = n < 1 ? 1 : c_max;
+    }
+    int ok = 1;
+    for (int j = 1; j < n; ++j) {
+        const double qj = (double)q[j];
+        if (parent[j] < 0 || parent[j] >= j || !(qj >= 0.0 && qj <= 1.0)) ok = 0;
+    }
+    if (!ok) {
+        *flag |= OF_BAD_FOREST;
+        n = 1;
+    }
+    f_Q[0] = 1.0;
+    for (int j = 1; j < n; ++j) f_Q[j] = f_Q[parent[j]] * (double)q[j];
+    select_layout(n, token, parent, f_Q, rows_cap, node_token, parent_row, Q_out, n_rows, S_curve, flag);
+    return n;
 }
 
 /* ======================================================================

@@ -32,6 +32,9 @@ void oracle_verify_chain(int bs, int V, double T, const void* logits, int dtype,
                          int32_t* out_num, int32_t* out_accepted, double* out_p, double* out_q,
                          uint32_t* out_flags, int32_t* out_win_lo, int32_t* out_win_hi);
 void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
+int oracle_tree_forest(int n, int c_max, const int32_t* token, const int32_t* parent, const float* q, int rows_cap,
+                       int32_t* node_token, int32_t* parent_row, double* Q_out, int32_t* n_rows, double* S_curve,
+                       double* f_Q, uint32_t* flag);
 }
 
 static unsigned g_seed = 12345u;
@@ -124,6 +127,19 @@ static int validation()
     CHECK(check_alloc(&al) == SPEC_EINVAL);
     al.mode = SPEC_ALLOC_CHAIN;
     CHECK(check_alloc(&al) == SPEC_EINVAL);
+    al.mode = SPEC_ALLOC_TREE;   // a caller-built forest
+    al.tree.bs = 3; al.tree.c_max = 40; al.tree.rows_cap = 16;
+    al.tree.node_token = dummy; al.tree.parent_row = dummy; al.tree.Q = (float*)dummy; al.tree.n_rows = dummy;
+    al.tree.row_base = (int64_t*)dummy; al.tree.total_rows = dummy; al.tree.forest_count = dummy;
+    al.tree.out_flags = (uint32_t*)dummy;
+    al.tree.forest_token = dummy;
+    CHECK(check_alloc(&al) == SPEC_EINVAL);
+    al.tree.forest_parent = dummy; al.tree.forest_q = (const float*)dummy; al.tree.forest_n = dummy;
+    CHECK(check_alloc(&al) == SPEC_OK);
+    al.tree.c_max = SPEC_MAX_FOREST + 1;
+    CHECK(check_alloc(&al) == SPEC_EINVAL);
+    al.tree.c_max = 40; al.tree.rows_cap = SPEC_MAX_ROWS + 1;
+    CHECK(check_alloc(&al) == SPEC_EINVAL);
     CHECK(check_workspace(nullptr, 0, 0) == SPEC_OK);
     CHECK(check_workspace(nullptr, 0, 16) == SPEC_EWORKSPACE);
     CHECK(check_workspace((void*)(uintptr_t)0x1000, 8, 16) == SPEC_EWORKSPACE);
@@ -191,6 +207,26 @@ static int oracle_functions()
                 CHECK(lo[r] <= ot[r * (ld + 1) + oa[r]] && ot[r * (ld + 1) + oa[r]] <= hi[r]);
             }
         }
+    }
+    // rows from caller-built forests, broken ones included
+    for (int trial = 0; trial < 300; ++trial) {
+        const int c_max = 1 + (int)(rnd() % 80), rows_cap = 1 + (int)(rnd() % 64);
+        const int n = (int)(rnd() % (c_max + 3)) - 1;
+        std::vector<int32_t> tok(c_max), par(c_max, -1), nt(rows_cap), pr(rows_cap), nr(1);
+        std::vector<float> q(c_max, 0.0f);
+        std::vector<double> Q(rows_cap), Sc(rows_cap), fQ(c_max);
+        for (int j = 1; j < c_max; ++j) {
+            tok[j] = (int32_t)(rnd() % 9);
+            par[j] = (int32_t)(rnd() % j);
+            q[j] = (float)urand();
+        }
+        if (trial % 7 == 0 && c_max > 2) par[1 + rnd() % (c_max - 1)] = c_max + 5;
+        if (trial % 11 == 0 && c_max > 2) q[1 + rnd() % (c_max - 1)] = NAN;
+        uint32_t fl = 0;
+        const int used = oracle_tree_forest(n, c_max, tok.data(), par.data(), q.data(), rows_cap, nt.data(), pr.data(),
+                                            Q.data(), nr.data(), Sc.data(), fQ.data(), &fl);
+        CHECK(used >= 1 && used <= c_max && nr[0] >= 1 && nr[0] <= rows_cap && nr[0] <= used);
+        for (int i = 1; i < nr[0]; ++i) CHECK(pr[i] >= 0 && pr[i] < i && Q[i] <= Q[pr[i]]);
     }
     // Philox4x32-10 known-answer vector of its authors (counter and key all zero)
     {

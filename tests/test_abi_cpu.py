@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == set(L.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.spec_abi_version() == 5
+    assert lib.spec_abi_version() == 6
     assert lib.spec_strerror(-1).decode() == "invalid argument"
 
 
@@ -90,6 +90,19 @@ def test_validation_rejects_bad_arguments_without_gpu(L):
     al.chain.K = 7
     al.chain.budget = -1
     assert lib.spec_allocate_budget(C.byref(al), None) == L.SPEC_EINVAL      # negative budget
+    t = L.AllocArgs(mode=L.ALLOC_TREE)
+    t.tree.bs, t.tree.c_max, t.tree.rows_cap = 2, 8, 4
+    for f in ("node_token", "parent_row", "Q", "n_rows", "row_base", "total_rows", "forest_count", "out_flags"):
+        setattr(t.tree, f, fake)
+    t.tree.forest_token = fake
+    assert lib.spec_allocate_budget(C.byref(t), None) == L.SPEC_EINVAL       # a forest without parents, q, n
+    t.tree.forest_parent = t.tree.forest_q = t.tree.forest_n = fake
+    t.tree.scores = fake
+    assert lib.spec_allocate_budget(C.byref(t), None) == L.SPEC_EINVAL       # a given forest with scores
+    t.tree.scores = None
+    for c_max, rows_cap in ((0, 4), (1025, 4), (8, 0), (8, 65)):
+        t.tree.c_max, t.tree.rows_cap = c_max, rows_cap
+        assert lib.spec_allocate_budget(C.byref(t), None) == L.SPEC_EINVAL   # sizes out of range
 
 
 def test_binding_fails_loudly_without_library(L, tmp_path):

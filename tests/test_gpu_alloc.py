@@ -320,3 +320,86 @@ def test_tree_row_bases_any_batch(BS):
     assert g["total_rows"][0] == g["n_rows"].sum()
     if ok.all():
         assert np.array_equal(g["row_base"], o["row_base"])
+
+
+def random_forests(rng, BS, c_max, tie_q=False, shape="random"):
+    """Caller-built forests: parents below their children, q in [0, 1]."""
+    token = rng.integers(0, 1000, (BS, c_max)).astype(np.int32)
+    parent = np.full((BS, c_max), -1, np.int32)
+    n = rng.integers(1, c_max + 1, BS).astype(np.int32)
+    n[: min(BS, 3)] = c_max
+    j = np.arange(1, c_max)
+    if c_max > 1:
+        if shape == "chain":
+            parent[:, 1:] = j - 1
+        elif shape == "star":
+            parent[:, 1:] = 0
+        else:
+            parent[:, 1:] = (rng.random((BS, c_max - 1)) * j).astype(np.int32)
+    if tie_q:
+        q = rng.choice(np.float32([0.0, 0.25, 0.5, 1.0]), (BS, c_max))
+    else:
+        q = rng.random((BS, c_max)).astype(np.float32)
+    return token, parent, q.astype(np.float32), n
+
+
+def gpu_tree_forest(token, parent, q, n, rows_cap):
+    import torch
+    import draft_verification_spec_amd as S
+    print(f"tree from a given forest: bs {token.shape[0]} c_max {token.shape[1]} rows_cap {rows_cap}", flush=True)
+    g = S.spec_allocate_budget(mode="tree", forest=(dev(token), dev(parent), dev(q), dev(n)), rows_cap=rows_cap,
+                               s_curve=True)
+    torch.cuda.synchronize()
+    return {k: host(v) for k, v in g.items()}
+
+
+def compare_tree_forest(g, o):
+    """The same fp64 path products and fp32 keys on both sides: every output
+    is compared exactly, near ties included."""
+    assert np.array_equal(g["forest_count"], o["count"])
+    assert np.array_equal(g["out_flags"].astype(np.uint32), o["flags"] & ~np.uint32(O.NEAR_MASK))
+    for k in ("node_token", "parent_row", "n_rows", "row_base"):
+        assert_rows_equal(g[k], o[k], np.ones(len(o["n_rows"]), bool), k)
+    assert np.array_equal(g["Q"], o["Q"].astype(np.float32))
+    assert np.array_equal(g["s_curve"], o["S_curve"].astype(np.float32))
+    assert g["total_rows"][0] == o["n_rows"].sum()
+
+
+@pytest.mark.parametrize("c_max", [1, 2, 63, 64, 65, 200, 1024])
+def test_tree_from_given_forest(c_max):
+    """Forests a caller built (any drafter's, AdaSpark Section 3.1): random,
+    chain and star shapes, tied estimates, every row cap."""
+    rng = np.random.Generator(np.random.Philox(4400 + c_max))
+    for shape in ("random", "chain", "star"):
+        for tie_q in (False, True):
+            token, parent, q, n = random_forests(rng, 97, c_max, tie_q, shape)
+            for rows_cap in (1, 2, 16, 64):
+                o = O.tree_forest_batch(token, parent, q, n, rows_cap)
+                g = gpu_tree_forest(token, parent, q, n, rows_cap)
+                compare_tree_forest(g, o)
+
+
+def test_tree_from_given_forest_broken_rules():
+    """A parent not below its child, q outside [0, 1] or NaN: the request keeps
+    the anchor alone and is flagged; node counts outside [1, c_max] are
+    clamped and flagged; the other requests are unaffected."""
+    rng = np.random.Generator(np.random.Philox(4500))
+    BS, c_max = 64, 150
+    token, parent, q, n = random_forests(rng, BS, c_max)
+    n[:] = c_max
+    parent[1, 7] = 7
+    parent[2, 100] = 120
+    parent[3, 5] = -1
+    q[4, 9] = 1.5
+    q[5, 140] = -0.25
+    q[6, 77] = np.nan
+    q[7, 3] = np.inf
+    n[8], n[9], n[10] = 0, -5, c_max + 1
+    parent[11, c_max - 1] = c_max   # past the node count of request 11 only
+    n[11] = c_max - 1
+    o = O.tree_forest_batch(token, parent, q, n, 16)
+    assert all(o["flags"][r] == O.BAD_FOREST for r in range(1, 8))
+    assert all(o["flags"][r] == O.BAD_LENGTH for r in (8, 9, 10))
+    assert o["flags"][11] == 0 and o["flags"][0] == 0
+    g = gpu_tree_forest(token, parent, q, n, 16)
+    compare_tree_forest(g, o)

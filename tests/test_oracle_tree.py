@@ -285,3 +285,111 @@ def test_s_curve_is_the_best_tree_of_every_width():
             assert full["S_curve"][n - 1] == pytest.approx(want, rel=1e-12, abs=1e-300)
             checked += 1
     assert checked > 100
+
+
+# --- rows from a forest the caller built (AdaSpark Section 3.1) ---------------
+
+def random_given_forest(rng, n, c_max, V=50, tie_q=False):
+    """Parents below their children, tokens, acceptance estimates in [0, 1]."""
+    token = np.full(c_max, -1, np.int32)
+    parent = np.full(c_max, -1, np.int32)
+    q = np.zeros(c_max, np.float32)
+    for j in range(1, n):
+        parent[j] = rng.integers(0, j)
+        token[j] = rng.integers(0, V)
+        q[j] = rng.choice([0.25, 0.5, 1.0]) if tie_q else rng.uniform(0.0, 1.0)
+    return token, parent, q
+
+
+def dfs_rows(parent, sel):
+    """Pre-order of the selected nodes from node 0, children in index order."""
+    rows, prow = [], []
+
+    def visit(u, pr):
+        rows.append(u)
+        prow.append(pr)
+        me = len(rows) - 1
+        for c in range(1, len(parent)):
+            if c in sel and parent[c] == u:
+                visit(c, me)
+    visit(0, -1)
+    return rows, prow
+
+
+def test_given_forest_hand_example():
+    """Anchor with children 1 (q .9) and 2 (q .5); node 1 with children 3 (q .6)
+    and 4 (q .95): Q = .9, .5, .54, .855; the best three are 1, 4, 3, laid out
+    anchor, 1, 3, 4."""
+    t = O.tree_forest([-1, 5, 6, 7, 8], [-1, 0, 0, 1, 1], [0, 0.9, 0.5, 0.6, 0.95], 5, rows_cap=4)
+    assert t["n_rows"] == 4 and t["flag"] == 0
+    assert list(t["node_token"]) == [-1, 5, 7, 8]
+    assert list(t["parent_row"]) == [-1, 0, 1, 1]
+    q = np.float32([0.9, 0.6, 0.95]).astype(np.float64)
+    assert t["Q"][1:] == pytest.approx([q[0], q[0] * q[1], q[0] * q[2]], rel=0, abs=0)
+    assert t["S_curve"] == pytest.approx([0.0, q[0], q[0] + q[0] * q[2], q[0] + q[0] * q[2] + q[0] * q[1]], rel=1e-15)
+    # a cap above the forest keeps every node; a cap of one keeps the anchor
+    assert O.tree_forest([-1, 5, 6, 7, 8], [-1, 0, 0, 1, 1], [0, 0.9, 0.5, 0.6, 0.95], 5, rows_cap=16)["n_rows"] == 5
+    one = O.tree_forest([-1, 5, 6, 7, 8], [-1, 0, 0, 1, 1], [0, 0.9, 0.5, 0.6, 0.95], 5, rows_cap=1)
+    assert one["n_rows"] == 1 and list(one["node_token"]) == [-1]
+
+
+@pytest.mark.parametrize("tie_q", [False, True])
+def test_given_forest_rows_are_the_best_tree_of_every_width(tie_q):
+    """Proposition 1 on random forests: the rows hold the largest sum of Q over
+    parent-closed sets of their size, S(n) is that sum at every width, Q is the
+    product of q along the path, and the rows are the pre-order of the chosen
+    set with children in index order."""
+    rng = np.random.Generator(np.random.Philox(5150 + tie_q))
+    checked = 0
+    for trial in range(40):
+        n = int(rng.integers(1, 12))
+        token, parent, q = random_given_forest(rng, n, 12, tie_q=tie_q)
+        full = O.tree_forest(token, parent, q, n, rows_cap=n)
+        assert full["flag"] == 0 and full["count"] == n
+        for j in range(1, n):   # the path product, root first
+            path, u = [], j
+            while u != 0:
+                path.append(u)
+                u = parent[u]
+            want = 1.0
+            for v in reversed(path):
+                want *= float(q[v])
+            assert full["f_Q"][j] == want
+        for rows in range(1, n + 1):
+            t = O.tree_forest(token, parent, q, n, rows_cap=rows)
+            assert t["n_rows"] == rows
+            best = 0.0 if rows == 1 else parent_closed_best(parent[:n], full["f_Q"], rows - 1)
+            assert t["Q"][1:rows].sum() == pytest.approx(best, rel=1e-12, abs=1e-300)
+            assert full["S_curve"][rows - 1] == pytest.approx(best, rel=1e-12, abs=1e-300)
+            # the chosen set: fp32 Q descending, index ascending
+            key = sorted(range(1, n), key=lambda j: (-np.float32(full["f_Q"][j]), j))
+            sel = set(key[:rows - 1])
+            order, prow = dfs_rows(parent[:n], sel)
+            assert list(t["node_token"][:rows]) == [-1] + [int(token[u]) for u in order[1:]]
+            assert list(t["parent_row"][:rows]) == prow
+            checked += 1
+    assert checked > 150
+
+
+def test_given_forest_broken_rules_keep_the_anchor_alone():
+    base_tok, base_par = [-1, 3, 4, 5], [-1, 0, 1, 1]
+    good = [0.0, 0.5, 0.5, 0.5]
+    assert O.tree_forest(base_tok, base_par, good, 4)["flag"] == 0
+    for par, q in (([-1, 0, 2, 1], good),            # a parent not below its child
+                   ([-1, 0, 1, 3], good),
+                   ([-1, -1, 1, 1], good),           # a node without a parent
+                   (base_par, [0.0, 0.5, 1.5, 0.5]),  # q above 1
+                   (base_par, [0.0, -0.1, 0.5, 0.5]),  # q below 0
+                   (base_par, [0.0, 0.5, float("nan"), 0.5])):
+        t = O.tree_forest(base_tok, par, q, 4, rows_cap=4)
+        assert t["flag"] == O.BAD_FOREST
+        assert t["n_rows"] == 1 and list(t["node_token"]) == [-1, -1, -1, -1]
+        assert list(t["S_curve"]) == [0.0, 0.0, 0.0, 0.0]
+    # node counts outside [1, c_max] are clamped and flagged
+    t = O.tree_forest(base_tok, base_par, good, 0, rows_cap=4)
+    assert t["flag"] == O.BAD_LENGTH and t["n_rows"] == 1
+    t = O.tree_forest(base_tok, base_par, good, 9, rows_cap=4)
+    assert t["flag"] == O.BAD_LENGTH and t["n_rows"] == 4 and t["count"] == 4
+    # q of exactly 0 and 1 are allowed: a zero-Q node is still a candidate
+    t = O.tree_forest(base_tok, base_par, [0.0, 1.0, 0.0, 1.0], 4, rows_cap=4)
+    assert t["flag"] == 0 and list(t["node_token"]) == [-1, 3, 4, 5] and list(t["Q"]) == [1.0, 1.0, 0.0, 1.0]
