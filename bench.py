@@ -386,7 +386,7 @@ def budget_step(K, W, hip, eager_only, config=2):
                                              workspace=bufs["ws_ng"])
             bufs["ng"] = tuple(torch.empty_like(x) for x in bufs["ng0"])
 
-    def step(prof=None):
+    def step(prof=None, lam=c["lam"], budget=c["budget"]):
         if fused:
             d, dl, f = bufs["ng0"]
         else:
@@ -394,13 +394,13 @@ def budget_step(K, W, hip, eager_only, config=2):
                                           out=bufs.get("ng"), workspace=bufs["ws_ng"])
             bufs.setdefault("ng", (d, dl, f))
         al = S.spec_allocate_budget(mode="chain", model_tokens=tokens_d, model_conf=conf_d, ngram_draft=d,
-                                    ngram_len=dl, ngram_feat=f, est=c["estimator"], lam=c["lam"],
-                                    budget=c["budget"], policy="proposed", conf_is_logit=True,
+                                    ngram_len=dl, ngram_feat=f, est=c["estimator"], lam=lam,
+                                    budget=budget, policy="proposed", conf_is_logit=True,
                                     model_point_mass=pm_d, ld=L, out=bufs.get("al"), workspace=bufs["ws_al"])
         out = S.spec_verify_chain(target, row_base, al["chain_tokens"], al["alloc_len"], c["temperature"],
                                   u_accept=u_acc, u_sample=u_smp, slot_flags=al["slot_flags"],
                                   out_flags=al["out_flags"], ctx=ctx, ctx_len=ctx_len, ctx_len_out=ctx_len_new,
-                                  out=bufs.get("vf"), max_slots=c["budget"], workspace=bufs["ws_v"],
+                                  out=bufs.get("vf"), max_slots=budget, workspace=bufs["ws_v"],
                                   prof_events=prof,
                                   ngram=(c["n_min"], c["n_max"], L, c["copy_cap"]) if fused else None,
                                   ngram_out=bufs["ng"] if fused else None)
@@ -414,8 +414,64 @@ def budget_step(K, W, hip, eager_only, config=2):
     total_rows = int(bufs["al"]["total_rows"].item())
     surv = bufs["al"]["survival"].cpu().numpy().ravel()   # the host copy the next step's sizing reads
     outputs = lambda: list(bufs["vf"].values()) + [bufs["al"]["out_flags"], ctx_len_new, ctx] + list(bufs["ng"])
-    return lambda: _budget_result(run_timed(step, outputs, K, W, hip, stream, eager_only), S, surv, BS, V,
-                                  total_rows, c, config)
+
+    def measure():
+        t = run_timed(step, outputs, K, W, hip, stream, eager_only)
+        if config == 2:
+            t["sizing_loop"] = sizing_loop(step, bufs, surv, BS, K, stream)
+        return _budget_result(t, S, surv, BS, V, total_rows, c, config)
+    return measure
+
+
+def sizing_loop(step, bufs, surv, BS, K, stream, c0=None, p=0.3):
+    """Eager steps whose budget b* and slot price lambda = G(b*) p the host
+    sizes from survivals ([HS] Section 2 "Asynchronous scheduling", Section
+    4.4): "async" from the survivals of two steps before, copied to pinned
+    host memory after each allocation and waited for by their event only;
+    "sync" from the step just run, waiting for it before the next launch;
+    "fixed" with the scalars held (no sizing).  Host wall time per step,
+    launches included; every step repeats the same inputs, so all three run
+    the same work."""
+    import torch
+    import draft_verification_spec_amd as S
+    c0 = float(BS) if c0 is None else c0
+    ring = [torch.empty(surv.size, dtype=torch.float32).pin_memory() for _ in range(3)]
+    evs = [torch.cuda.Event() for _ in range(3)]
+    # the scalars the sizing settles on (the price changes the chains chosen,
+    # and so the survivals it is sized from)
+    b0, lam0, _ = S.spec_size_budget(surv, BS, c0, p)
+    with torch.cuda.stream(stream):
+        for _ in range(10):
+            step(lam=lam0, budget=b0)
+            b1, lam1, _ = S.spec_size_budget(bufs["al"]["survival"].cpu().numpy(), BS, c0, p)
+            if (b1, lam1) == (b0, lam0):
+                break
+            b0, lam0 = b1, lam1
+    res = {"b_star": b0, "lambda": lam0, "cost_model": "C(b) = BS + 0.3 b", "steps": K}
+    with torch.cuda.stream(stream):
+        for _ in range(20):
+            step(lam=lam0, budget=b0)
+        for mode in ("fixed", "async", "sync"):
+            b, lam = b0, lam0
+            seen = set()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for t in range(K):
+                if mode == "async" and t >= 2:
+                    evs[(t - 2) % 3].synchronize()
+                    b, lam, _ = S.spec_size_budget(ring[(t - 2) % 3].numpy(), BS, c0, p)
+                step(lam=lam, budget=b)
+                seen.add(b)
+                if mode != "fixed":
+                    ring[t % 3].copy_(bufs["al"]["survival"].view(-1), non_blocking=True)
+                    evs[t % 3].record(stream)
+                if mode == "sync":
+                    evs[t % 3].synchronize()
+                    b, lam, _ = S.spec_size_budget(ring[t % 3].numpy(), BS, c0, p)
+            torch.cuda.synchronize()
+            res[mode + "_ms_per_step"] = (time.perf_counter() - t0) / K * 1e3
+            res[mode + "_budgets"] = sorted(seen)
+    return res
 
 
 def _budget_result(t, S, surv, BS, V, total_rows, c, config):
@@ -430,6 +486,7 @@ def _budget_result(t, S, surv, BS, V, total_rows, c, config):
     return {"workload": workload,
             "timing": t["mode"], "steps_per_s": t["steps_per_s"], "ms_per_step": t["ms_per_step"],
             "step_ms_percentiles": t.get("step_ms_percentiles"),
+            "sizing_loop": t.get("sizing_loop"),
             "verified_rows_per_step": total_rows, "algorithmic_bytes": step_bytes,
             "GBps": step_bytes / (t["ms_per_step"] * 1e-3) / 1e9,
             "frac": step_bytes / (t["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,

@@ -458,3 +458,60 @@ def dense_headline(BS=128, V=151936, B=7, T_ctx=8192, src_len=6000, temperature=
     return dict(BS=BS, V=V, B=B, temperature=temperature, target_bf16=tgt, draft_bf16=dft, tokens=toks,
                 u_acc=urng.random((BS, B), dtype=np.float32), u_smp=urng.random(BS, dtype=np.float32),
                 ctx=ctx, ctx_len=ctx_len, n_min=5, n_max=15, max_draft=15, copy_cap=256)
+
+
+# ---------------------------------------------------------------------------
+# a batch served over several steps (the host's sizing loop)
+# ---------------------------------------------------------------------------
+
+class ServingLoop:
+    """Requests served over several steps.  Each request's output follows a
+    fixed stream: for the first half, the rest of a passage that its prompt
+    holds once in full and ends by repeating the passage's opening (so the
+    n-gram drafter can continue it), for the rest random tokens.  A step's
+    inputs are its raw draws (``step_raw``) put in place by how many tokens
+    each request has emitted so far (``assemble``): a greedy model chain that
+    agrees with the stream at rate p_agree, its confidence logits ~ N(1, 1),
+    and fp32 target rows of N(0, 2^2) noise whose row k is planted on the
+    stream's token k from the current position (argmax at T = 0)."""
+
+    def __init__(self, BS=32, V=1024, T_prompt=600, passage=240, steps=8, K=7, rows=16, config=7, p_agree=0.8):
+        self.BS, self.V, self.K, self.rows, self.steps = BS, V, K, rows, steps
+        self.T_prompt, self.config, self.p_agree = T_prompt, config, p_agree
+        rng = rng_for(config, S_CTX)
+        self.cap = T_prompt + steps * rows
+        self.ctx = np.zeros((BS, self.cap), np.int32)
+        self.ctx_len = np.full(BS, T_prompt, np.int32)
+        span = steps * rows + rows
+        self.stream = np.zeros((BS, span), np.int32)
+        for r in range(BS):
+            if r < BS // 2:
+                p = uniform_tokens(rng, passage, V)
+                head = int(rng.integers(20, 60))
+                pre = uniform_tokens(rng, T_prompt - passage - head - 40, V)
+                mid = uniform_tokens(rng, 40, V)
+                self.ctx[r, :T_prompt] = np.concatenate([pre, p, mid, p[:head]])
+                tail = p[head:]
+                self.stream[r] = np.concatenate([tail, uniform_tokens(rng, max(0, span - len(tail)), V)])[:span]
+            else:
+                self.ctx[r, :T_prompt] = uniform_tokens(rng, T_prompt, V)
+                self.stream[r] = uniform_tokens(rng, span, V)
+
+    def step_raw(self, t):
+        BS, K, V = self.BS, self.K, self.V
+        drng = rng_for(self.config, 100 + 3 * t + S_DRAFT)
+        rand = uniform_tokens(drng, BS * K, V).reshape(BS, K)
+        agree = drng.random((BS, K)) < self.p_agree
+        conf = (drng.standard_normal((BS, K), dtype=np.float32) + np.float32(1.0)).astype(np.float32)
+        noise = noise_rows(rng_for(self.config, 100 + 3 * t + S_LOGITS), (BS, self.rows, V))
+        return dict(rand=rand, agree=agree, conf=conf, noise=noise)
+
+    def assemble(self, raw, emitted):
+        """The step's inputs given the tokens each request has emitted."""
+        BS, K, rows = self.BS, self.K, self.rows
+        truth = np.stack([self.stream[r, emitted[r]:emitted[r] + rows] for r in range(BS)])
+        model = np.where(raw["agree"], truth[:, :K], raw["rand"]).astype(np.int32)
+        target = raw["noise"].copy()
+        for r in range(BS):
+            target[r, np.arange(rows), truth[r]] = np.float32(PLANT_LOGIT)
+        return dict(model_tokens=model, model_conf_logit=raw["conf"], target=target.reshape(BS * rows, self.V))
