@@ -463,14 +463,18 @@ typedef const __attribute__((address_space(1))) int32_t* gi32_ptr;
 // Best-first rank of nodes 1..cnt-1 by (fp32 Q descending, index ascending),
 // S(n), the depth-first layout of the chosen set and the request's outputs
 // ([AS] Section 3.1).  The forest's tokens, parents and Q are in LDS, with
-// fsel zero for every node; one wave per request.
+// fsel zero for every node; every thread of the workgroup (one request)
+// calls it: the ranks are shared out over all of them, S(n) and the layout
+// are wave 0's, and flags are thread 0's.
 __device__ __forceinline__ void tree_rows(const spec_tree_alloc& A, int r, int lane, int cnt, uint32_t flags,
                                           const int32_t* ftok, const int32_t* fpar, const double* fQ, uint8_t* fsel)
 {
     __shared__ double sQrank[SPEC_MAX_ROWS];
+    const int t = threadIdx.x, nthr = blockDim.x;
+    const bool w0 = t < kWave;
     // best-first: rank by (fp32 Q desc, index asc); keep rank < rows_cap - 1
     const int keep = A.rows_cap - 1;
-    for (int j = 1 + lane; j < cnt; j += kWave) {
+    for (int j = 1 + t; j < cnt; j += nthr) {
         const uint64_t kj = ((uint64_t)__float_as_uint((float)fQ[j]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
         int rank = 0;
         for (int i = 1; i < cnt; ++i) {
@@ -481,7 +485,7 @@ __device__ __forceinline__ void tree_rows(const spec_tree_alloc& A, int r, int l
         if (rank < A.rows_cap) sQrank[rank] = fQ[j];
     }
     __syncthreads();
-    if (A.s_curve) {
+    if (A.s_curve && w0) {
         // S(n): the first n - 1 nodes of the best-first order, accumulated in
         // order (lane n - 1 holds the (n - 1)-th Q)
         const double v = (lane < A.rows_cap && lane < cnt - 1) ? sQrank[lane] : 0.0;
@@ -500,10 +504,10 @@ __device__ __forceinline__ void tree_rows(const spec_tree_alloc& A, int r, int l
     // d holds depth d's) and always takes the lowest one.
     __shared__ int32_t scomp[SPEC_MAX_ROWS];      // compact position -> forest node
     __shared__ int16_t scpos[SPEC_MAX_FOREST];    // forest node -> compact position
-    if (lane == 0) fsel[0] = 1;
+    if (t == 0) fsel[0] = 1;
     __syncthreads();
     int m = 0;
-    for (int base = 0; base < cnt; base += kWave) {
+    for (int base = 0; w0 && base < cnt; base += kWave) {
         const int c = base + lane;
         const bool sel = c < cnt && fsel[c];
         const uint64_t bal = __ballot(sel);
@@ -516,6 +520,7 @@ __device__ __forceinline__ void tree_rows(const spec_tree_alloc& A, int r, int l
     }
     m = m < A.rows_cap ? m : A.rows_cap;
     __syncthreads();
+    if (!w0) return;
     const int mynode = lane < m ? scomp[lane] : -1;
     const int myparent = (lane < m && lane > 0) ? (int)scpos[fpar[mynode]] : -1;
     auto children = [&](int u) -> uint64_t { return __builtin_amdgcn_ballot_w64(lane < m && myparent == u); };
@@ -558,7 +563,7 @@ __device__ __forceinline__ void tree_rows(const spec_tree_alloc& A, int r, int l
             nt[lane] = -1; pr[lane] = -1; Qo[lane] = 0.0f;
         }
     }
-    if (lane == 0) {
+    if (t == 0) {
         A.n_rows[r] = row;
         A.forest_count[r] = cnt;
         A.out_flags[r] = flags;
@@ -566,12 +571,16 @@ __device__ __forceinline__ void tree_rows(const spec_tree_alloc& A, int r, int l
 }
 
 // NS register slots per lane: forest node j lives on lane j % 64 in slot
-// j / 64 during the chain walk (NS * 64 >= c_max).
+// j / 64 during the chain walk (NS * 64 >= c_max).  Four waves per request:
+// wave 0 walks the chains; the weights, denominators and ranks of large
+// forests are shared out over all four.
+constexpr int kTreeBlock = 256;
+
 template <int NS>
-__global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
+__global__ __launch_bounds__(kTreeBlock) void k_tree(TreeBuildParams P)
 {
     const spec_tree_alloc& A = P.a;
-    const int r = blockIdx.x, lane = threadIdx.x;
+    const int r = blockIdx.x, t = threadIdx.x, lane = t % kWave, wid = t / kWave;
     __shared__ int32_t ftok[SPEC_MAX_FOREST];
     __shared__ int32_t fpar[SPEC_MAX_FOREST];
     __shared__ int32_t fdep[SPEC_MAX_FOREST];
@@ -585,6 +594,7 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
     __shared__ int8_t fabove[SPEC_MAX_FOREST];
     __shared__ int8_t fbucket[SPEC_MAX_FOREST];
     __shared__ int8_t fagree[SPEC_MAX_FOREST];
+    __shared__ int32_t fcontra[SPEC_MAX_FOREST];   // a drafter node's largest contradicting class (-1 none)
     __shared__ double fw[SPEC_MAX_FOREST];
     __shared__ int32_t sh_cnt;
     // the chains' tokens, lengths and evidence classes, staged in one round
@@ -598,27 +608,27 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
     const int nd = 1 + P_ * Kc;
     const int64_t q0 = (int64_t)r * (P_ + 1);
     const bool staged = (int64_t)(P_ + 1) * A.ngram_ld <= kChainLds;
-    // the Eq. (6) inputs of the drafter nodes on the first 64 lanes (node i on
-    // lane i) and the request's own terms, requested now so that the weights
-    // do not wait for them after the walk
+    // the Eq. (6) inputs of the drafter nodes on the first threads (node i on
+    // thread i) and the request's own terms, requested now so that the
+    // weights do not wait for them after the walk
     float pf_h = 0.5f, pf_s = 0.5f, pf_r = 1.0f, pf_src = 0.5f, pf_ctx = 0.0f, pf_req = 0.0f;
     if (P.scored) {
         pf_src = P.sc.p_src[r];
         pf_ctx = P.sc.psi_ctx[r];
         pf_req = P.sc.b_req[r];
-        if (lane >= 1 && lane < nd) {
-            const int p = (lane - 1) / Kc + 1, k = (lane - 1) % Kc;
+        if (t >= 1 && t < nd) {
+            const int p = (t - 1) / Kc + 1, k = (t - 1) % Kc;
             pf_h = P.sc.h[(int64_t)r * P_ + p - 1];
             pf_s = P.sc.sigma[(int64_t)r * P_ + p - 1];
             if (k > 0) pf_r = P.sc.r_share[((int64_t)r * P_ + p - 1) * Kc + k];
         }
     }
-    for (int i = lane; i <= P_; i += kWave) {
+    for (int i = t; i <= P_; i += kTreeBlock) {
         clen[i] = A.ngram_len[q0 + i];
         cev[i] = (int8_t)(P.scored ? evidence_of(P.sc.ngram_feat + 4 * (q0 + i)) : 0);
     }
     if (staged)
-        for (int i = lane; i < (P_ + 1) * A.ngram_ld; i += kWave) {
+        for (int i = t; i < (P_ + 1) * A.ngram_ld; i += kTreeBlock) {
             ctok[i] = A.ngram_draft[q0 * A.ngram_ld + i];
             cfol[i] = A.ngram_follow ? A.ngram_follow[q0 * A.ngram_ld + i] : 0;
         }
@@ -652,7 +662,7 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
     const bool lane_chains = P_ < kWave;
     const int lglen = lane_chains && lane <= P_ ? clen[lane] : 0;
     const int lev = lane_chains && lane <= P_ ? (int)cev[lane] : 0;
-    for (int sc = 0; sc <= P_; ++sc) {
+    for (int sc = 0; wid == 0 && sc <= P_; ++sc) {
         const int64_t q = q0 + sc;
         int glen = lane_chains ? __builtin_amdgcn_readlane(lglen, sc) : clen[sc];
         if (glen < 0 || glen > A.ngram_ld) { flags |= SPEC_FLAG_BAD_LENGTH; glen = glen < 0 ? 0 : A.ngram_ld; }
@@ -817,7 +827,7 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const int n = s * kWave + lane;
-        if (n < cntr) {
+        if (wid == 0 && n < cntr) {
             ftok[n] = rtok[s];
             fpar[n] = rpar[s];
             fdep[n] = rdep[s];
@@ -827,19 +837,37 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
             fagree[n] = (int8_t)ragree[s];
         }
     }
-    if (lane == 0) sh_cnt = cntr;
+    for (int j = t; j < nd; j += kTreeBlock) fcontra[j] = -1;
+    if (t == 0) sh_cnt = cntr;
     __syncthreads();
     const int cnt = sh_cnt;
     // weights: given by candidate index, or exp of the Eq. (6) scores (none = 1)
     const float* wn = A.w_node + (int64_t)r * cmax;
     const float* wz = A.w_none + (int64_t)r * cmax;
     if (P.scored) {
+        // contradictions: an n-gram node whose parent is the anchor or a pick
+        // hands its evidence class to the drafter nodes of the next position
+        // (those that share its parent) that hold another token; the largest
+        // class counts
+        for (int c = nd + t; c < cnt; c += kTreeBlock) {
+            const int pn = fpar[c];
+            const int pos = pn == 0 ? 1 : ((pn < nd && (pn - 1) % Kc == 0) ? fdep[pn] + 1 : 0);
+            if (pos >= 1 && pos <= P_) {
+                const int cls = (fbucket[c] & 31) / 4;   // the evidence class, of either kind
+                const int32_t tk = ftok[c];
+                for (int k = 0; k < Kc; ++k) {
+                    const int j = 1 + (pos - 1) * Kc + k;
+                    if (ftok[j] != tk) atomicMax(&fcontra[j], cls);
+                }
+            }
+        }
+        __syncthreads();
         const spec_tree_scores& S = P.sc;
         const double lps = logit_prob((double)pf_src);
         const double plus = lps > 0.0 ? lps : 0.0;
         const double pc = (double)pf_ctx, br = (double)pf_req;
-        for (int j = lane; j < cnt; j += kWave) {
-            const bool pre = j < kWave;   // node j is on lane j: its inputs are in registers
+        for (int j = t; j < cnt; j += kTreeBlock) {
+            const bool pre = j < kTreeBlock;   // node j is on thread j: its inputs are in registers
             double sj = 0.0;
             const int kind = fkind[j] & 3;
             if (j == 0) {
@@ -860,22 +888,20 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
                     sj = S.a[3] + S.a[4] * log(rr) + S.a[5] * lh + S.a[6] * ls + psi + br;
                 }
                 if (fagree[j] >= 0) sj += plus + S.w_agreed[fagree[j]][ps];
-                int contra = -1;
-                for (int c = nd; c < cnt; ++c)   // n-gram nodes come after the drafter's
-                    if (fpar[c] == fpar[j] && (fkind[c] & 3) == 3 && ftok[c] != ftok[j] && (fbucket[c] & 31) / 4 > contra)
-                        contra = (fbucket[c] & 31) / 4;   // the evidence class, of either kind
+                const int contra = fcontra[j];
                 if (contra >= 0) sj += -plus + S.w_contra[contra][ps];
             }
             fw[j] = exp(sj);
         }
     } else {
-        for (int j = lane; j < cnt; j += kWave) fw[j] = (double)wn[j];
+        for (int j = t; j < cnt; j += kTreeBlock) fw[j] = (double)wn[j];
     }
     __syncthreads();
     // denominators of the Eq. (6) form: none + the children's weights (index
     // order), then Q = the parent's Q times w / den along every path (index
     // order, so a parent is done before its children)
     if (cnt <= kWave) {
+      if (wid == 0) {
         // one node per lane: the sums and the path products pass the children's
         // weights and the parents' Q from lane to lane, without LDS round trips
         const bool mine = lane < cnt;
@@ -898,8 +924,9 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
             fQ[lane] = q;
             fsel[lane] = 0;
         }
+      }
     } else {
-        for (int p = lane; p < cnt; p += kWave) {
+        for (int p = t; p < cnt; p += kTreeBlock) {
             double den = P.scored ? 1.0 : (double)wz[p];
             for (int c = 1; c < cnt; ++c)
                 if (fpar[c] == p) den += fw[c];
@@ -907,7 +934,7 @@ __global__ __launch_bounds__(kWave) void k_tree(TreeBuildParams P)
             fsel[p] = 0;
         }
         __syncthreads();
-        if (lane == 0) {
+        if (t == 0) {
             fQ[0] = 1.0;
             for (int j = 1; j < cnt; ++j) fQ[j] = fQ[fpar[j]] * (fw[j] / fden[fpar[j]]);
         }
@@ -1017,8 +1044,8 @@ int spec_alloc_launch(const spec_alloc_args* a, hipStream_t st)
         if (P.scored) P.sc = *a->tree.scores;
         else std::memset(&P.sc, 0, sizeof(P.sc));
         const int c = a->tree.c_max;
-        const dim3 g(a->tree.bs), b(kWave);
-        if (a->tree.forest_token) hipLaunchKernelGGL(k_tree_forest, g, b, 0, st, a->tree);
+        const dim3 g(a->tree.bs), b(kTreeBlock);
+        if (a->tree.forest_token) hipLaunchKernelGGL(k_tree_forest, g, dim3(kWave), 0, st, a->tree);
         else if (c <= 64) hipLaunchKernelGGL(k_tree<1>, g, b, 0, st, P);
         else if (c <= 128) hipLaunchKernelGGL(k_tree<2>, g, b, 0, st, P);
         else if (c <= 256) hipLaunchKernelGGL(k_tree<4>, g, b, 0, st, P);
