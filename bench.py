@@ -61,6 +61,8 @@ def parse():
     p.add_argument("--no-stress", action="store_true", help="skip the large-batch stress step record")
     p.add_argument("--no-fp32", action="store_true", help="skip the fp32 record of the reported step")
     p.add_argument("--no-ceiling", action="store_true", help="skip the device-copy ceiling record")
+    p.add_argument("--no-sizing-loop", action="store_true",
+                   help="skip the host sizing loop timing of the batch-allocation step")
     p.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -348,7 +350,7 @@ def headline(K, W, hip, eager_only, fp32=False):
     return measure
 
 
-def budget_step(K, W, hip, eager_only, config=2):
+def budget_step(K, W, hip, eager_only, config=2, sizing=True):
     """The batch-allocation step: n-gram draft, selection and allocation of
     the budget's slots, verification of the chosen chains, commit; at BS 128
     with a budget of 256 (config=2: the draft of the committed contexts runs
@@ -417,7 +419,7 @@ def budget_step(K, W, hip, eager_only, config=2):
 
     def measure():
         t = run_timed(step, outputs, K, W, hip, stream, eager_only)
-        if config == 2:
+        if config == 2 and sizing:
             t["sizing_loop"] = sizing_loop(step, bufs, surv, BS, K, stream)
         return _budget_result(t, S, surv, BS, V, total_rows, c, config)
     return measure
@@ -639,7 +641,7 @@ def main():
     # then follow one another, the reported step last
     plan = []
     if not args.no_budget:
-        plan.append(("budget_step", budget_step(K, W, hip, args.eager)))
+        plan.append(("budget_step", budget_step(K, W, hip, args.eager, sizing=not args.no_sizing_loop)))
     if not args.no_tree:
         plan.append(("tree_step", tree_step(K, W, hip, args.eager)))
     if not args.no_stress:
