@@ -14,12 +14,13 @@
 //     wave-wide suffix scan), stopping as soon as the boundary bucket is taken
 //     whole, then each request's verified prefix and the CSR row bases.
 // Trees (AdaSpark, Sections 2.2, 3.1, 3.3):
-//   k_tree    : one wave per request builds the candidate forest (drafter
-//               block + n-gram chains, copied or follower tokens) with the
-//               nodes in lane registers during the chain walk, then in LDS;
-//               the acceptance estimates of the Eq. (6) form, the path
-//               products Q, the best-first top rows_cap-1 (Proposition 1) and
-//               the depth-first layout.
+//   k_tree    : four waves per request; wave 0 builds the candidate forest
+//               (drafter block + n-gram chains, copied or follower tokens)
+//               with the nodes in lane registers during the chain walk, then
+//               in LDS; the acceptance estimates of the Eq. (6) form (shared
+//               out over the waves), the path products Q, the best-first top
+//               rows_cap-1 (Proposition 1) and the depth-first layout.
+//   k_tree_forest: the same rows from a forest the caller built.
 //   k_rows_scan: exclusive prefix sum of the rows per request.
 #include <cstring>
 
