@@ -81,7 +81,9 @@ __global__ __launch_bounds__(NT) void k_ngram(NgramParams P)
 template <bool PLAIN, bool FOLLOW>
 static void launch_ngram(const NgramParams& P, int64_t text_max, hipStream_t st)
 {
-    if (text_max <= 512 * 16)
+    if (text_max <= 512 * 10)
+        hipLaunchKernelGGL((k_ngram<PLAIN, FOLLOW, 512, 10>), dim3(P.nq), dim3(512), 0, st, P);
+    else if (text_max <= 512 * 16)
         hipLaunchKernelGGL((k_ngram<PLAIN, FOLLOW, 512, 16>), dim3(P.nq), dim3(512), 0, st, P);
     else if (text_max <= 1024 * 16)
         hipLaunchKernelGGL((k_ngram<PLAIN, FOLLOW, 1024, 16>), dim3(P.nq), dim3(1024), 0, st, P);
