@@ -2162,14 +2162,15 @@ struct TreeParams {
     Partial* part; int32_t splits;
 };
 
+template <int kPer>
 __global__ __launch_bounds__(kWave) void k_tree_walk(TreeParams P)
 {
     const int r = blockIdx.x, t = threadIdx.x;
     const int rm = P.rows_max;
     // the rows' chunk partials (all rows_max rows of the request's slice, so
     // that no load waits for the row count), the row count and the tree are
-    // all requested before the first use: one memory round trip in all
-    constexpr int kPer = 32;
+    // all requested before the first use: one memory round trip in all (kPer
+    // partials per lane: the host picks the smaller instance when they fit)
     constexpr int kWalkParts = kPer * kWave;
     __shared__ Partial sp[kWalkParts];
     const int total = rm * P.splits;
@@ -2620,7 +2621,10 @@ int spec_verify_tree_launch(const spec_tree_verify_args* a, hipStream_t st)
     const StatsLaunch L{st, (hipEvent_t)a->prof_begin, (hipEvent_t)a->prof_end};
     launch_stats(S, a->dtype, aligned16(a->logits, a->row_stride, a->dtype), SPEC_F32, false, false, true,
                  a->rows_max, 0, (int64_t)a->bs * a->rows_max, sp, gpre, L);
-    hipLaunchKernelGGL(k_tree_walk, dim3(a->bs), dim3(kWave), 0, st, P);
+    if ((int64_t)P.rows_max * P.splits <= 16 * kWave)
+        hipLaunchKernelGGL(k_tree_walk<16>, dim3(a->bs), dim3(kWave), 0, st, P);
+    else
+        hipLaunchKernelGGL(k_tree_walk<32>, dim3(a->bs), dim3(kWave), 0, st, P);
     return spec_record_hip_error(hipGetLastError());
 }
 
