@@ -160,3 +160,45 @@ def test_point_mass_chain_fused_draft():
                             dev(ng[1]), 1.0, ctx, c["ctx_len"], stride, ngram, u_accept=dev(c["u_acc_ng"]),
                             u_sample=dev(c["u_smp_ng"]), slot_flags=dev(np.ones((BS, 15), np.uint8)))
     check(plain, fused, ngram)
+
+
+def test_measured_step_call_matches_oracle():
+    """The reported step exactly as it is timed: one call with uniforms drawn
+    in the kernel (Philox4x32-10, seed 20261202, step 1), the acceptance
+    histogram, written flags, the commit into the contexts with new lengths
+    apart, and the next n-gram draft fused in.  Its verification outputs
+    against the oracle's with the oracle's own uniforms; the contexts against
+    the commit of the emitted tokens; the draft against the oracle's scan of
+    the committed contexts; the histogram against the accepted counts."""
+    import torch
+    import draft_verification_spec_amd as S
+    from tests.gpu_helpers import check_verify_chain, expected_commit
+    seed, step = 20261202, 1
+    c = synth.dense_headline(ctx_extra=64)
+    BS, V, B = c["BS"], c["V"], c["B"]
+    print(f"measured step call: BS {BS} V {V} B {B}", flush=True)
+    tgt = synth.as_torch_bf16(c["target_bf16"]).to("cuda:0").reshape(-1, V)
+    dft = synth.as_torch_bf16(c["draft_bf16"]).to("cuda:0").reshape(-1, V)
+    ctx, ctx_len = dev(c["ctx"]), dev(c["ctx_len"])
+    ctx_len_new = torch.empty_like(ctx_len)
+    hist = torch.zeros(B + 1, dtype=torch.int32, device="cuda:0")
+    out = S.spec_verify_chain(tgt, dev(np.arange(BS, dtype=np.int64) * (B + 1)), dev(c["tokens"]),
+                              dev(np.full(BS, B, np.int32)), c["temperature"], rng=(seed, step), accept_hist=hist,
+                              slot_flags=dev(np.zeros((BS, B), np.uint8)), draft_logits=dft,
+                              draft_row_base=dev(np.arange(BS, dtype=np.int64) * B), ctx=ctx, ctx_len=ctx_len,
+                              ctx_len_out=ctx_len_new, write_flags=True,
+                              ngram=(c["n_min"], c["n_max"], c["max_draft"], c["copy_cap"]))
+    torch.cuda.synchronize()
+    g = {k: host(v) for k, v in out.items()}
+    u_acc, u_smp = O.step_uniforms(BS, B, seed, step)
+    ref = O.verify_chain(c["target_bf16"].reshape(-1, V), np.arange(BS) * (B + 1), c["tokens"],
+                         np.zeros((BS, B), np.uint8), np.full(BS, B, np.int32), u_acc, u_smp, c["temperature"],
+                         draft_logits=c["draft_bf16"].reshape(-1, V), draft_row_base=np.arange(BS) * B)
+    check_verify_chain(g, ref, np.full(BS, B), "measured step")
+    c2, l2, _ = expected_commit(c["ctx"], c["ctx_len"], c["ctx"].shape[1], g["out_tokens"], g["out_num"])
+    assert np.array_equal(host(ctx), c2) and np.array_equal(host(ctx_len_new), l2)
+    assert np.array_equal(host(ctx_len), c["ctx_len"])   # the old lengths are left as they were
+    d, dl, f = O.ngram_draft(c2, l2, c["n_min"], c["n_max"], c["max_draft"], c["copy_cap"])
+    assert np.array_equal(g["ngram_len"], dl) and np.array_equal(g["ngram_feat"], f)
+    assert np.array_equal(g["ngram_draft"], d)
+    assert np.array_equal(host(hist), np.bincount(g["out_accepted"], minlength=B + 1))
