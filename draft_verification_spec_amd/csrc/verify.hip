@@ -2581,10 +2581,19 @@ int spec_verify_chain_launch(const spec_verify_args* a, hipStream_t st)
     launch_stats(S, a->dtype, at, a->draft_dtype, ad, draft, P.greedy, a->ld + 1, draft ? a->ld : 0,
                  a->bs + slots + (draft ? slots : 0), sp, gpre, L);
     const int tt = a->dtype, dd = P.dlogits ? a->draft_dtype : a->dtype;
-    // residual chunks shared by K workgroups per request, about 5 each (two
-    // 512-thread decide workgroups fit on a compute unit, so K = 4 keeps a
-    // batch of 128 resident at once)
-    const int K = draft && P.coal && sp.splits <= kDBlock ? std::min(16, std::max(1, (sp.splits + 4) / 5)) : 1;
+    // residual chunks shared by K workgroups per request, about 5 each, and
+    // no more than the chip holds at once for the batch: a workgroup that
+    // starts after the others have taken every chunk still runs its whole
+    // prologue, and the draw waits for its report
+    const void* kern = (tt == SPEC_F32 && dd == SPEC_F32) ? (const void*)k_decide<SPEC_F32, SPEC_F32>
+                     : (tt == SPEC_F32) ? (const void*)k_decide<SPEC_F32, SPEC_BF16>
+                     : (dd == SPEC_F32) ? (const void*)k_decide<SPEC_BF16, SPEC_F32>
+                                        : (const void*)k_decide<SPEC_BF16, SPEC_BF16>;
+    int K = draft && P.coal && sp.splits <= kDBlock ? std::min(16, std::max(1, (sp.splits + 4) / 5)) : 1;
+    if (K > 1) {
+        const int64_t fit = (int64_t)blocks_per_cu(kern, kDBlock) * device_cus() / a->bs;
+        K = (int)std::max<int64_t>(1, std::min<int64_t>(K, fit));
+    }
     const dim3 g(a->bs, K), b(kDBlock);
     if (tt == SPEC_F32 && dd == SPEC_F32) hipLaunchKernelGGL((k_decide<SPEC_F32, SPEC_F32>), g, b, 0, st, P);
     else if (tt == SPEC_F32) hipLaunchKernelGGL((k_decide<SPEC_F32, SPEC_BF16>), g, b, 0, st, P);
