@@ -249,7 +249,7 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, bool active, int dg)
     else if (active && dg != ldg) atomicAdd(&hist[dg], 1u);
 }
 
-// The exact budget-th largest ranking key by an 8-bit radix select over the
+// The threshold of the budget largest ranking keys by an 8-bit radix select over the
 // survival and position bytes (stopping as soon as the boundary bucket is
 // taken whole), the request bits by one ordered scan, then each request's
 // verified prefix and the row bases.  One workgroup.
@@ -262,12 +262,12 @@ __global__ __launch_bounds__(kAllocBlock) void k_alloc_topk(SelectParams P)
     // one histogram per wave (double-buffered): at the top digits nearly every
     // key agrees, and atomics of all waves on one LDS word serialize
     __shared__ __align__(16) uint32_t hist[2][kAllocBlock / kWave][256];
-    __shared__ uint64_t sh_prefix, sh_min;
+    __shared__ uint64_t sh_prefix;
     __shared__ int64_t sh_rem, sh_valid;
     __shared__ int sh_done;
     const bool in_lds = N <= kLdsKeys;
     const int wid = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    if (threadIdx.x == 0) { sh_prefix = 0; sh_valid = 0; sh_done = 0; sh_min = ~0ull; }
+    if (threadIdx.x == 0) { sh_prefix = 0; sh_valid = 0; sh_done = 0; }
     {
         int64_t valid = 0;
         for (int64_t i = threadIdx.x; i < N; i += kAllocBlock) {
@@ -362,22 +362,10 @@ __global__ __launch_bounds__(kAllocBlock) void k_alloc_topk(SelectParams P)
                 break;
             }
         }
+        // the threshold: the boundary key, or, when the boundary bucket is
+        // taken whole, its prefix with the lower bits zero (every key of the
+        // bucket is at least that, every key below the bucket less)
         theta = sh_prefix;
-        if (sh_done && mask != ~0ull) {
-            uint64_t mn = ~0ull;
-            for (int64_t i = threadIdx.x; i < N; i += kAllocBlock) {
-                const uint64_t k = keys[i];
-                if (k != 0 && (k & mask) == theta && k < mn) mn = k;
-            }
-#pragma unroll
-            for (int o = kWave / 2; o > 0; o >>= 1) {
-                const uint64_t v = __shfl_xor(mn, o, kWave);
-                mn = v < mn ? v : mn;
-            }
-            if (lane == 0) atomicMin((unsigned long long*)&sh_min, (unsigned long long)mn);
-            __syncthreads();
-            theta = sh_min;
-        }
     }
     // verified prefix per request, row bases over (alloc + 1).  A request's
     // keys are read in batches of 16 from clamped (in-bounds) positions, so
