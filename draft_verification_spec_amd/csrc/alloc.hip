@@ -93,15 +93,20 @@ __global__ __launch_bounds__(kSlotBlock) void k_alloc_slots(SelectParams P)
     // uses it, one dependent trip after another.
     const int kc = k < K ? k : (K > 0 ? K - 1 : 0);
     const int gc = k < gcap ? k : (gcap > 0 ? gcap - 1 : 0);
-    const int rl = A.ngram_len[r];
-    const int n = A.ngram_feat[4 * (int64_t)r + 0];
-    const int am = A.ngram_feat[4 * (int64_t)r + 1];
-    const int mf = A.ngram_feat[4 * (int64_t)r + 2];
+    const int rl0 = A.ngram_len[r];
+    const int n0 = A.ngram_feat[4 * (int64_t)r + 0];
+    const int am0 = A.ngram_feat[4 * (int64_t)r + 1];
+    const int mf0 = A.ngram_feat[4 * (int64_t)r + 2];
     const int32_t td0 = K > 0 ? A.model_tokens[(int64_t)r * K + kc] : -1;
     const float cv0 = K > 0 ? A.model_conf[(int64_t)r * K + kc] : 0.0f;
     const int32_t tg0 = gcap > 0 ? A.ngram_draft[(int64_t)r * A.ngram_ld + gc] : -1;
-    const int pm0 = A.model_point_mass ? (int)A.model_point_mass[r] : 1;
-    asm volatile("" : : "v"(rl), "v"(n), "v"(am), "v"(mf), "v"(td0), "v"(cv0), "v"(tg0), "v"(pm0));
+    const int pm1 = A.model_point_mass ? (int)A.model_point_mass[r] : 1;
+    asm volatile("" : : "v"(rl0), "v"(n0), "v"(am0), "v"(mf0), "v"(td0), "v"(cv0), "v"(tg0), "v"(pm1));
+    // the request's own words are the same on every lane: as scalars, the
+    // chain lengths make the folds below uniform loops and branches
+    const int rl = __builtin_amdgcn_readfirstlane(rl0), n = __builtin_amdgcn_readfirstlane(n0);
+    const int am = __builtin_amdgcn_readfirstlane(am0), mf = __builtin_amdgcn_readfirstlane(mf0);
+    const int pm0 = __builtin_amdgcn_readfirstlane(pm1);
     const int glen = rl < 0 ? 0 : (rl > gcap ? gcap : rl);
     double mm = (double)mf;
     mm = mm < 1.0 ? 1.0 : (mm > (double)A.est.m_cap ? (double)A.est.m_cap : mm);
