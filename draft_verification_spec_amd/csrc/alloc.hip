@@ -458,8 +458,9 @@ typedef const __attribute__((address_space(1))) int32_t* gi32_ptr;
 // S(n), the depth-first layout of the chosen set and the request's outputs
 // ([AS] Section 3.1).  The forest's tokens, parents and Q are in LDS, with
 // fsel zero for every node; every thread of the workgroup (one request)
-// calls it: the ranks are shared out over all of them, S(n) and the layout
-// are wave 0's, and flags are thread 0's.
+// calls it: the ranks are shared out over all of them, the layout is wave
+// 0's, S(n) wave 1's (wave 0's in a one-wave workgroup), and flags are
+// thread 0's.
 __device__ __forceinline__ void tree_rows(const spec_tree_alloc& A, int r, int lane, int cnt, uint32_t flags,
                                           const int32_t* ftok, const int32_t* fpar, const double* fQ, uint8_t* fsel)
 {
@@ -468,7 +469,27 @@ __device__ __forceinline__ void tree_rows(const spec_tree_alloc& A, int r, int l
     const bool w0 = t < kWave;
     // best-first: rank by (fp32 Q desc, index asc); keep rank < rows_cap - 1
     const int keep = A.rows_cap - 1;
-    for (int j = 1 + t; j < cnt; j += nthr) {
+    if (cnt <= kWave) {
+        // a forest within one wave: the keys in registers, node j on lane j
+        if (w0) {
+            const bool mine = lane >= 1 && lane < cnt;
+            const double qj = mine ? fQ[lane] : 0.0;
+            const uint64_t kj = mine ? ((uint64_t)__float_as_uint((float)qj) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)lane) : 0;
+            // (lanes outside 1..cnt-1 hold key 0, which outranks nothing: the
+            // loop runs over every lane with constant lane indices)
+            int rank = 0;
+#pragma unroll
+            for (int i = 1; i < kWave; ++i) {
+                const uint64_t ki = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(kj >> 32), i) << 32)
+                                  | (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)kj, i);
+                rank += ki > kj;
+            }
+            if (mine) {
+                fsel[lane] = rank < keep;
+                if (rank < A.rows_cap) sQrank[rank] = qj;
+            }
+        }
+    } else for (int j = 1 + t; j < cnt; j += nthr) {
         const uint64_t kj = ((uint64_t)__float_as_uint((float)fQ[j]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
         int rank = 0;
         for (int i = 1; i < cnt; ++i) {
@@ -478,25 +499,14 @@ __device__ __forceinline__ void tree_rows(const spec_tree_alloc& A, int r, int l
         fsel[j] = rank < keep;
         if (rank < A.rows_cap) sQrank[rank] = fQ[j];
     }
-    __syncthreads();
-    if (A.s_curve && w0) {
-        // S(n): the first n - 1 nodes of the best-first order, accumulated in
-        // order (lane n - 1 holds the (n - 1)-th Q)
-        const double v = (lane < A.rows_cap && lane < cnt - 1) ? sQrank[lane] : 0.0;
-        double acc = 0.0, mine = 0.0;
-        for (int n = 1; n <= A.rows_cap; ++n) {
-            mine = lane == n - 1 ? acc : mine;
-            if (n - 1 < cnt - 1) acc += readlane_f64(v, n - 1);
-        }
-        if (lane < A.rows_cap) A.s_curve[(int64_t)r * A.rows_cap + lane] = (float)mine;
-    }
-    // Depth-first layout, children in index order, by the whole wave.  The
-    // selected nodes (the anchor and at most rows_cap - 1 candidates, a
-    // parent-closed set) are compacted in index order, node i on lane i, each
-    // knowing its parent's compact position; a wave-uniform walk then keeps a
-    // mask of the unvisited children of every node on the current path (lane
-    // d holds depth d's) and always takes the lowest one.
+    // Depth-first layout, children in index order.  The selected nodes (the
+    // anchor and at most rows_cap - 1 candidates) are compacted in index
+    // order, node i on lane i; a parent precedes its children in that order.
+    // Each lane's row is then the number of nodes that precede it depth-first:
+    // its ancestors, and every node whose path leaves their deepest common
+    // ancestor through a lower-index child.
     __shared__ int32_t scomp[SPEC_MAX_ROWS];      // compact position -> forest node
+    __shared__ int32_t scpar[SPEC_MAX_ROWS];      // compact position -> its node's parent
     __shared__ int16_t scpos[SPEC_MAX_FOREST];    // forest node -> compact position
     if (t == 0) fsel[0] = 1;
     __syncthreads();
@@ -508,57 +518,90 @@ __device__ __forceinline__ void tree_rows(const spec_tree_alloc& A, int r, int l
         const int at = m + (int)__popcll(bal & ((1ull << lane) - 1ull));
         if (sel && at < SPEC_MAX_ROWS) {
             scomp[at] = c;
+            scpar[at] = c > 0 ? fpar[c] : -1;
             scpos[c] = (int16_t)at;
         }
         m += (int)__popcll(bal);
     }
-    m = m < A.rows_cap ? m : A.rows_cap;
+    // m as a scalar: the loop above runs on wave 0 only, which the compiler
+    // cannot tell, and the layout walk below would otherwise run divergent
+    m = __builtin_amdgcn_readfirstlane(m < A.rows_cap ? m : A.rows_cap);
     __syncthreads();
-    if (!w0) return;
-    const int mynode = lane < m ? scomp[lane] : -1;
-    const int myparent = (lane < m && lane > 0) ? (int)scpos[fpar[mynode]] : -1;
-    auto children = [&](int u) -> uint64_t { return __builtin_amdgcn_ballot_w64(lane < m && myparent == u); };
-    // lane d: the unvisited children of the path's depth-d node and that
-    // node's row; lane k: row k's compact node and parent row
-    const uint64_t kids0 = children(0);
-    uint32_t stk_lo = lane == 0 ? (uint32_t)kids0 : 0u, stk_hi = lane == 0 ? (uint32_t)(kids0 >> 32) : 0u;
-    int stk_row = 0, ord = lane == 0 ? 0 : -1, prow = -1;
-    int row = 1, d = 0;
-    while (row < m) {
-        // the deepest node on the path with an unvisited child (every level
-        // below it is done: one ballot instead of a pop per level)
-        const uint64_t open = __builtin_amdgcn_ballot_w64(lane <= d && (stk_lo | stk_hi) != 0u);
-        if (!open) break;
-        d = 63 - (int)__builtin_clzll(open);
-        const uint64_t top = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)stk_hi, d) << 32)
-                           | (uint32_t)__builtin_amdgcn_readlane((int)stk_lo, d);
-        const int c = (int)__builtin_ctzll(top);
-        const uint64_t kids = children(c);
-        const int prw = __builtin_amdgcn_readlane(stk_row, d);
-        const uint64_t rest = top & (top - 1);
-        stk_lo = lane == d ? (uint32_t)rest : (lane == d + 1 ? (uint32_t)kids : stk_lo);
-        stk_hi = lane == d ? (uint32_t)(rest >> 32) : (lane == d + 1 ? (uint32_t)(kids >> 32) : stk_hi);
-        stk_row = lane == d + 1 ? row : stk_row;
-        ord = lane == row ? c : ord;
-        prow = lane == row ? prw : prow;
-        ++d;
-        ++row;
+    if (A.s_curve && (nthr > kWave ? (t >= kWave && t < 2 * kWave) : w0)) {
+        // S(n): the first n - 1 nodes of the best-first order, accumulated in
+        // order (lane n - 1 holds the (n - 1)-th Q); on the second wave when
+        // there is one, beside wave 0's layout
+        const double v = (lane < A.rows_cap && lane < cnt - 1) ? sQrank[lane] : 0.0;
+        double acc = 0.0, mine = 0.0;
+        for (int n = 1; n <= A.rows_cap; ++n) {
+            mine = lane == n - 1 ? acc : mine;
+            if (n - 1 < cnt - 1) acc += readlane_f64(v, n - 1);
+        }
+        if (lane < A.rows_cap) A.s_curve[(int64_t)r * A.rows_cap + lane] = (float)mine;
     }
+    if (!w0) return;
+    const bool in = lane < m;
+    const int mynode = in ? scomp[lane] : -1;
+    // the parent's compact position (-1 at the anchor; -2 for a parent left
+    // out of the set, which cuts the node and its subtree off the layout;
+    // -3 past the set)
+    int jmp = in ? -1 : -3;
+    if (in && lane > 0) {
+        const int pf = scpar[lane];
+        jmp = fsel[pf] ? (int)scpos[pf] : -2;
+    }
+    const int up = jmp;
+    // ancestors-or-self as a lane mask, by pointer doubling: anc holds the
+    // first nodes of the path up from the lane and jmp the next one above
+    // them (-1: the anchor was reached)
+    uint64_t anc = in ? (1ull << lane) : 0ull;
+    while (__builtin_amdgcn_ballot_w64(jmp >= 0)) {
+        const int src = jmp >= 0 ? jmp : lane;
+        const uint64_t a2 = ((uint64_t)(uint32_t)__shfl((int)(anc >> 32), src, kWave) << 32)
+                          | (uint32_t)__shfl((int)(uint32_t)anc, src, kWave);
+        const int j2 = __shfl(jmp, src, kWave);
+        if (jmp >= 0) {
+            anc |= a2;
+            jmp = j2;
+        }
+    }
+    const bool reach = in && jmp == -1;
+    // the nodes before this one: w is an ancestor (w's set within ours), or
+    // both paths continue below the common ancestor and w's continues through
+    // the lower index (along a path the indices grow with depth, so the
+    // lowest index of a path's part below the common ancestor is its child
+    // there)
+    // With lowest(empty) = -1 one signed compare decides: an ancestor has
+    // x empty (-1 < anything), a descendant has y empty (never before).
+    // Four lanes w per round (lanes past the set hold jmp -3 and never count).
+    int row = 0;
+    for (int wb = 0; wb < m; wb += 4) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int w = wb + k;
+            const uint64_t aw = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(anc >> 32), w) << 32)
+                              | (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)anc, w);
+            const int jw = __builtin_amdgcn_readlane(jmp, w);
+            const int cx = __ffsll((unsigned long long)(aw & ~anc)) - 1;
+            const int cy = __ffsll((unsigned long long)(anc & ~aw)) - 1;
+            row += (int)((jw == -1) & (w != lane) & (cx < cy));
+        }
+    }
+    const int prow = __shfl(row, up < 0 ? 0 : up, kWave);
+    const int nrows = (int)__popcll(__builtin_amdgcn_ballot_w64(reach));
     int32_t* nt = A.node_token + (int64_t)r * A.rows_cap;
     int32_t* pr = A.parent_row + (int64_t)r * A.rows_cap;
     float* Qo = A.Q + (int64_t)r * A.rows_cap;
-    const int u = __shfl(mynode, ord < 0 ? 0 : ord, kWave);   // row lane's forest node
-    if (lane < A.rows_cap) {
-        if (lane < row) {
-            nt[lane] = (u == 0) ? -1 : ftok[u];
-            pr[lane] = prow;
-            Qo[lane] = (float)fQ[u];
-        } else {
-            nt[lane] = -1; pr[lane] = -1; Qo[lane] = 0.0f;
-        }
+    if (reach) {
+        nt[row] = (mynode == 0) ? -1 : ftok[mynode];
+        pr[row] = lane == 0 ? -1 : prow;
+        Qo[row] = (float)fQ[mynode];
+    }
+    if (lane >= nrows && lane < A.rows_cap) {
+        nt[lane] = -1; pr[lane] = -1; Qo[lane] = 0.0f;
     }
     if (t == 0) {
-        A.n_rows[r] = row;
+        A.n_rows[r] = nrows;
         A.forest_count[r] = cnt;
         A.out_flags[r] = flags;
     }
@@ -590,6 +633,7 @@ __global__ __launch_bounds__(kTreeBlock) void k_tree(TreeBuildParams P)
     __shared__ int8_t fagree[SPEC_MAX_FOREST];
     __shared__ int32_t fcontra[SPEC_MAX_FOREST];   // a drafter node's largest contradicting class (-1 none)
     __shared__ double fw[SPEC_MAX_FOREST];
+    __shared__ unsigned long long fkids[kWave];   // a small forest's children, as lane masks
     __shared__ int32_t sh_cnt;
     // the chains' tokens, lengths and evidence classes, staged in one round
     // trip (the tokens when they fit)
@@ -656,7 +700,17 @@ __global__ __launch_bounds__(kTreeBlock) void k_tree(TreeBuildParams P)
     const bool lane_chains = P_ < kWave;
     const int lglen = lane_chains && lane <= P_ ? clen[lane] : 0;
     const int lev = lane_chains && lane <= P_ ? (int)cev[lane] : 0;
-    for (int sc = 0; wid == 0 && sc <= P_; ++sc) {
+    // with the chains on the lanes, the walk visits only those with tokens
+    // (an empty chain adds nothing and passes no node)
+    uint64_t live = __builtin_amdgcn_ballot_w64(lglen > 0);
+    if (__builtin_amdgcn_ballot_w64(lglen < 0)) flags |= SPEC_FLAG_BAD_LENGTH;
+    for (int it = 0; wid == 0 && it <= P_; ++it) {
+        int sc = it;
+        if (lane_chains) {
+            if (!live) break;
+            sc = (int)__builtin_ctzll(live);
+            live &= live - 1;
+        }
         const int64_t q = q0 + sc;
         int glen = lane_chains ? __builtin_amdgcn_readlane(lglen, sc) : clen[sc];
         if (glen < 0 || glen > A.ngram_ld) { flags |= SPEC_FLAG_BAD_LENGTH; glen = glen < 0 ? 0 : A.ngram_ld; }
@@ -896,22 +950,33 @@ __global__ __launch_bounds__(kTreeBlock) void k_tree(TreeBuildParams P)
     // order, so a parent is done before its children)
     if (cnt <= kWave) {
       if (wid == 0) {
-        // one node per lane: the sums and the path products pass the children's
-        // weights and the parents' Q from lane to lane, without LDS round trips
+        // one node per lane.  Each node's children as a lane mask (index
+        // order); a parent adds its lowest remaining child per round, so the
+        // sums keep index order and take as many rounds as the widest node
+        // has children.  Q then goes one depth level per round (a child is one
+        // level below its parent).
         const bool mine = lane < cnt;
         const int pj = mine ? fpar[lane] : -2;
+        const int dj = mine ? fdep[lane] : -1;
         const double wj = mine ? fw[lane] : 0.0;
+        // (one wave: its LDS operations run in order; the fences keep the
+        // compiler from moving the zeroing, the ors and the read past each other)
+        fkids[lane] = 0;
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        if (mine && lane > 0) atomicOr(&fkids[pj], 1ull << lane);
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        uint64_t kids = mine ? fkids[lane] : 0;
         double den = P.scored ? 1.0 : (mine ? (double)wz[lane] : 0.0);
-        for (int c = 1; c < cnt; ++c) {
-            const int pc = __builtin_amdgcn_readlane(pj, c);
-            const double wc = readlane_f64(wj, c);
-            den = lane == pc ? den + wc : den;
+        while (__builtin_amdgcn_ballot_w64(kids != 0)) {
+            const double wc = shfl_f64(wj, kids ? (int)__builtin_ctzll(kids) : 0);
+            den = kids ? den + wc : den;
+            kids &= kids - 1;
         }
         const double ratio = wj / shfl_f64(den, pj < 0 ? 0 : pj);
         double q = 1.0;
-        for (int j = 1; j < cnt; ++j) {
-            const double qp = readlane_f64(q, __builtin_amdgcn_readlane(pj, j));
-            q = lane == j ? qp * ratio : q;
+        for (int d = 1; __builtin_amdgcn_ballot_w64(dj == d); ++d) {
+            const double qp = shfl_f64(q, pj < 0 ? 0 : pj);
+            q = dj == d ? qp * ratio : q;
         }
         if (mine) {
             fden[lane] = den;
