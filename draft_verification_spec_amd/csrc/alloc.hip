@@ -607,6 +607,176 @@ __device__ __forceinline__ void tree_rows(const spec_tree_alloc& A, int r, int l
     }
 }
 
+// An int32 view of LDS scratch that the walk borrows from arrays written only
+// after it.
+typedef int32_t __attribute__((may_alias)) wi32;
+
+// The chain walk without a walk: every (chain, token) entry finds its node at
+// once, over the whole workgroup.  Chain c starts at the anchor (c = 0, depth
+// 0) or at pick c (depth c); its token i sits at depth c + 1 + i.  A node is
+// fixed by the tokens on its path from the anchor, so:
+//   - entries before fp_c, the chain's first token off the pick path, are the
+//     picks of their positions (the lowest candidate holding a pick's token is
+//     the pick itself); the entry at fp_c, if its position is in the block, is
+//     the lowest other candidate holding its token, if any; every later entry
+//     is an n-gram node (neither a sibling nor an n-gram node has drafter
+//     children);
+//   - two chains c' < c reach the same n-gram node at depth d exactly when c'
+//     passes pick c and their tokens agree from depth c + 1 to d: the node was
+//     made by the lowest such c' (c itself if none).
+// A chain's own nodes are the tail of its entries; they are numbered in chain
+// order and then depth order, the order a chain-by-chain walk appends them in,
+// so c_max keeps the same ones.  A node passed by a later chain is marked
+// agreed; a drafter node also takes the largest bucket of the tokens that pass
+// it.  All threads of the workgroup call this (it holds barriers); the drafter
+// nodes are in the forest arrays already.  Writes the n-gram nodes and the
+// marks and returns the node count.
+__device__ __forceinline__ int walk_parallel(const spec_tree_alloc& A, int P_, int Kc, int nd, int cmax, int nthr,
+                                             const int32_t* clen, const int8_t* cev, const int32_t* ctok,
+                                             const int32_t* cfol, int32_t* ftok, int32_t* fpar, int32_t* fdep,
+                                             uint8_t* fkind, int8_t* fabove, int8_t* fbucket, int8_t* fagree,
+                                             wi32* went, wi32* wagr, wi32* wscr, uint32_t& flags)
+{
+    constexpr int kPass = 1 << 20;      // on a made node's entry: a later chain passes it
+    constexpr int kNone = 1 << 30;
+    wi32* wpass = wscr;                  // [nd]: a drafter node's largest passing bucket (-1: none)
+    wi32* cgeff = wscr + SPEC_MAX_FOREST;        // per chain: entries (tokens within the depth limit)
+    wi32* cfp = cgeff + kWave;                   // per chain: first entry off the pick path
+    wi32* cndr = cfp + kWave;                    // per chain: entries that are drafter nodes
+    wi32* cdn = cndr + kWave;                    // per chain: depth of its first own node (kNone: none)
+    wi32* cbase = cdn + kWave;                   // per chain: index of its first own node
+    wi32* ctotal = cbase + kWave;                // own nodes of all chains
+    const int t = threadIdx.x, lane = t % kWave;
+    const int L = A.ngram_ld, C = P_ + 1, E = C * L, npair = C * (C - 1) / 2;
+    const bool w0 = t < kWave;
+    const int pick0 = 1;   // node of position d's pick: pick0 + (d - 1) * Kc
+    if (w0) {
+        const int gl = lane < C ? clen[lane] : 0;
+        if (__builtin_amdgcn_ballot_w64(gl < 0 || gl > L)) flags |= SPEC_FLAG_BAD_LENGTH;
+        if (lane < C) {
+            const int g = gl < 0 ? 0 : (gl > L ? L : gl);
+            int ge = A.depth_max - lane < g ? A.depth_max - lane : g;
+            ge = ge > 0 ? ge : 0;
+            cgeff[lane] = ge;
+            cfp[lane] = ge;
+            cndr[lane] = ge;
+            cdn[lane] = kNone;
+        }
+    }
+    for (int n = t; n < nd; n += nthr) wpass[n] = -1;
+    for (int q = t; q < npair; q += nthr) wagr[q] = kNone;
+    __syncthreads();
+    // departures from the pick path, and the pairs' agreement lengths (pair
+    // (c', c), c' < c, at c (c - 1) / 2 + c': the first j at which chain c's
+    // token j and chain c''s token at the same depth differ or either ends)
+    for (int e = t; e < E; e += nthr) {
+        const int c = e / L, i = e - c * L;
+        if (i >= cgeff[c]) continue;
+        const int d = c + 1 + i;
+        if (d > P_ || ctok[e] != ftok[pick0 + (d - 1) * Kc]) atomicMin(&cfp[c], i);
+    }
+    for (int w = t; w < npair * L; w += nthr) {
+        const int q = w / L, j = w - q * L;
+        int c = 1;
+        while ((c + 1) * c / 2 <= q) ++c;   // c (c - 1) / 2 <= q < (c + 1) c / 2
+        const int cp = q - c * (c - 1) / 2, jp = c - cp + j;
+        const bool differ = j >= cgeff[c] || jp >= cgeff[cp] || ctok[c * L + j] != ctok[cp * L + jp];
+        if (differ) atomicMin(&wagr[q], j);
+    }
+    __syncthreads();
+    // each entry's node: a drafter node's index, or 1024 + the chain that
+    // makes the n-gram node
+    for (int e = t; e < E; e += nthr) {
+        const int c = e / L, i = e - c * L;
+        if (i >= cgeff[c]) continue;
+        const int d = c + 1 + i, fp = cfp[c];
+        int code = -1;
+        if (i < fp) {
+            code = pick0 + (d - 1) * Kc;
+        } else if (i == fp && d <= P_) {
+            const int tk = ctok[e];
+            for (int k = 1; k < Kc; ++k)
+                if (ftok[pick0 + (d - 1) * Kc + k] == tk) {
+                    code = pick0 + (d - 1) * Kc + k;
+                    break;
+                }
+        }
+        if (i == fp) cndr[c] = fp + (code >= 0 ? 1 : 0);
+        if (code >= 0) {
+            const int fc = cfol[e];
+            atomicMax(&wpass[code], fc > 0 ? 32 + 4 * follower_class(fc) : 4 * (int)cev[c]);
+        } else {
+            int cr = c;
+            for (int cp = 0; cp < c; ++cp)
+                if (cfp[cp] >= c - cp && wagr[c * (c - 1) / 2 + cp] >= d - c) {
+                    cr = cp;
+                    break;
+                }
+            code = 1024 + cr;
+            if (cr == c) atomicMin(&cdn[c], d);
+        }
+        went[e] = code;
+    }
+    __syncthreads();
+    // passes of other chains' nodes; the chains' first indices
+    for (int e = t; e < E; e += nthr) {
+        const int c = e / L, i = e - c * L;
+        if (i >= cgeff[c]) continue;
+        const int code = went[e] & ~kPass;   // (another thread may be marking this entry)
+        if (code >= 1024 && code - 1024 != c) {
+            const int cr = code - 1024, d = c + 1 + i;
+            atomicOr(&went[cr * L + (d - cr - 1)], kPass);
+        }
+    }
+    if (w0) {
+        const int dn = lane < C ? cdn[lane] : kNone;
+        const int nnew = dn < kNone ? cgeff[lane] - (dn - lane - 1) : 0;
+        int incl = nnew;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int v = __shfl_up(incl, o, kWave);
+            if (lane >= o) incl += v;
+        }
+        if (lane < C) cbase[lane] = nd + incl - nnew;
+        if (lane == kWave - 1) ctotal[0] = incl;
+    }
+    __syncthreads();
+    // the new nodes
+    for (int e = t; e < E; e += nthr) {
+        const int c = e / L, i = e - c * L;
+        if (i >= cgeff[c]) continue;
+        const int code = went[e];
+        if ((code & ~kPass) != 1024 + c) continue;
+        const int d = c + 1 + i, dn = cdn[c], idx = cbase[c] + (d - dn);
+        if (idx >= cmax) continue;
+        int par = idx - 1;
+        if (i == 0) {
+            par = c == 0 ? 0 : pick0 + (c - 1) * Kc;
+        } else if (d == dn) {
+            const int pc = went[e - 1] & ~kPass;
+            par = pc < 1024 ? pc : cbase[pc - 1024] + (d - 1 - cdn[pc - 1024]);
+        }
+        const int ui = i - cndr[c];
+        const int fc = cfol[e];
+        ftok[idx] = ctok[e];
+        fpar[idx] = par;
+        fdep[idx] = d;
+        fkind[idx] = (uint8_t)(3 | ((code & kPass) ? 4 : 0));
+        fabove[idx] = (int8_t)(ui < 127 ? ui : 127);
+        fbucket[idx] = (int8_t)((fc > 0 ? 32 + 4 * follower_class(fc) : 4 * (int)cev[c]) + (ui < 3 ? ui : 3));
+        fagree[idx] = -1;
+    }
+    for (int n = t; n < nd; n += nthr) {
+        const int b = wpass[n];
+        if (b >= 0) {
+            fkind[n] = (uint8_t)(fkind[n] | 4);
+            fagree[n] = (int8_t)b;
+        }
+    }
+    const int total = ctotal[0];
+    return nd + total < cmax ? nd + total : cmax;
+}
+
 // NS register slots per lane: forest node j lives on lane j % 64 in slot
 // j / 64 during the chain walk (NS * 64 >= c_max).  Four waves per request:
 // wave 0 walks the chains; the weights, denominators and ranks of large
@@ -704,6 +874,32 @@ __global__ __launch_bounds__(kTreeBlock) void k_tree(TreeBuildParams P)
     // (an empty chain adds nothing and passes no node)
     uint64_t live = __builtin_amdgcn_ballot_w64(lglen > 0);
     if (__builtin_amdgcn_ballot_w64(lglen < 0)) flags |= SPEC_FLAG_BAD_LENGTH;
+    // With the chains on the lanes and their tokens in LDS, all chains walk
+    // together, one depth per round (below); otherwise, and for the largest
+    // forests (whose register slots leave no room for both walks), one chain
+    // after another.
+    const bool by_depth = NS <= 8 && lane_chains && staged;
+    if (by_depth) {
+      if (wid == 0) {
+        // The drafter nodes go to LDS first: the walk reads their tokens.
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int n = s * kWave + lane;
+            if (n < nd) {
+                ftok[n] = rtok[s];
+                fpar[n] = rpar[s];
+                fdep[n] = rdep[s];
+                fkind[n] = (uint8_t)rkind[s];
+                fabove[n] = 0;
+                fbucket[n] = -1;
+                fagree[n] = -1;
+            }
+        }
+      }
+      cntr = walk_parallel(A, P_, Kc, nd, cmax, kTreeBlock, clen, cev, ctok, cfol, ftok, fpar, fdep, fkind, fabove,
+                           fbucket, fagree, reinterpret_cast<wi32*>(fw), reinterpret_cast<wi32*>(fQ),
+                           reinterpret_cast<wi32*>(fden), flags);
+    } else {
     for (int it = 0; wid == 0 && it <= P_; ++it) {
         int sc = it;
         if (lane_chains) {
@@ -884,6 +1080,7 @@ __global__ __launch_bounds__(kTreeBlock) void k_tree(TreeBuildParams P)
             fbucket[n] = (int8_t)rbucket[s];
             fagree[n] = (int8_t)ragree[s];
         }
+    }
     }
     for (int j = t; j < nd; j += kTreeBlock) fcontra[j] = -1;
     if (t == 0) sh_cnt = cntr;
