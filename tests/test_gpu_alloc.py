@@ -292,6 +292,80 @@ def test_tree_build_follower_buckets():
         assert not np.allclose(o0["Q"], o["Q"])
 
 
+@pytest.mark.parametrize("P,Kc,L,vocab", [(8, 4, 15, 6), (20, 2, 12, 5), (63, 1, 8, 4), (5, 3, 40, 3)])
+def test_tree_build_shared_paths(P, Kc, L, vocab):
+    """Chains that follow the drafter's picks and then one another's n-gram
+    nodes (AdaSpark Section 3.1: a chain extends the forest where its tokens
+    leave the existing paths): each request has a text; the picks mostly
+    follow it, the siblings are random (duplicates allowed); chain c is mostly
+    the text's continuation from pick c, sometimes with one token changed, else
+    random.  Small vocabularies make sibling matches and shared continuations
+    common.  c_max caps from a few nodes past the block to unbounded, depth
+    limits, given weights and Eq. (6) scores with follower counts."""
+    import torch
+    import draft_verification_spec_amd as S
+    rng = np.random.Generator(np.random.Philox(4100 + 7 * P + Kc))
+    BS = 48
+    tr = rng.integers(0, vocab, (BS, P + L + 8)).astype(np.int32)
+    block = rng.integers(0, vocab, (BS, P, Kc)).astype(np.int32)
+    follow = rng.random((BS, P)) < 0.8
+    block[:, :, 0] = np.where(follow, tr[:, :P], block[:, :, 0])
+    ng = rng.integers(0, vocab, (BS * (P + 1), L)).astype(np.int32)
+    ngl = rng.integers(0, L + 1, BS * (P + 1)).astype(np.int32)
+    for r in range(BS):
+        for c in range(P + 1):
+            q = r * (P + 1) + c
+            u = rng.random()
+            if u < 0.7:
+                ng[q] = tr[r, c:c + L]
+                if rng.random() < 0.3:
+                    j = int(rng.integers(0, L))
+                    ng[q, j] = (ng[q, j] + 1) % vocab
+    fol = np.where(rng.random((BS * (P + 1), L)) < 0.6, 0, rng.integers(1, 300, (BS * (P + 1), L))).astype(np.int32)
+    feat = np.zeros((BS * (P + 1), 4), np.int32)
+    feat[:, 0] = rng.integers(1, 16, BS * (P + 1))
+    feat[:, 2] = np.where(rng.random(BS * (P + 1)) < 0.5, rng.integers(15, 300, BS * (P + 1)), 0)
+    nd = 1 + P * Kc
+    full = nd + (P + 1) * L
+    f = synth.tree_score_inputs(BS, P, Kc)
+    per = [dict(coef=f["coef"], h=f["h"][r], sigma=f["sigma"][r], r_share=f["r_share"][r], psi_ctx=f["psi_ctx"][r],
+                b_req=f["b_req"][r], p_src=f["p_src"][r], ng_feat=feat.reshape(BS, P + 1, 4)[r]) for r in range(BS)]
+    sc = dict(coef=f["coef"], h=dev(f["h"]), sigma=dev(f["sigma"]), r_share=dev(f["r_share"]),
+              psi_ctx=dev(f["psi_ctx"]), b_req=dev(f["b_req"]), p_src=dev(f["p_src"]), ngram_feat=dev(feat))
+    shared = 0
+    for c_max in sorted({nd + 3, nd + 10, min(full, 512), max(full, 513)}):
+        wn = rng.standard_exponential((BS, c_max)).astype(np.float32)
+        wz = rng.standard_exponential((BS, c_max)).astype(np.float32)
+        for dmax, rows_cap in ((64, 64), (P // 2 + 3, 16), (3, 8)):
+            for scored in (False, True):
+                print(f"tree build, shared paths: P {P} Kc {Kc} L {L} c_max {c_max} depth {dmax} rows_cap {rows_cap}"
+                      f" scored {scored}", flush=True)
+                if scored:
+                    o = O.tree_build_batch(block, ng, ngl, depth_max=dmax, rows_cap=rows_cap, scores=per, c_max=c_max,
+                                           ng_follow=fol)
+                    g = S.spec_allocate_budget(mode="tree", block=dev(block), ngram_draft=dev(ng), ngram_len=dev(ngl),
+                                               ngram_follow=dev(fol), scores=sc, c_max=c_max, depth_max=dmax,
+                                               rows_cap=rows_cap, s_curve=True)
+                else:
+                    o = O.tree_build_batch(block, ng, ngl, wn, wz, dmax, rows_cap)
+                    g = S.spec_allocate_budget(mode="tree", block=dev(block), ngram_draft=dev(ng), ngram_len=dev(ngl),
+                                               w_node=dev(wn), w_none=dev(wz), depth_max=dmax, rows_cap=rows_cap)
+                torch.cuda.synchronize()
+                g = {k: host(v) for k, v in g.items()}
+                ok = ok_rows(o["flags"])
+                assert_rows_equal(g["forest_count"], o["count"], np.ones(BS, bool), f"forest_count c_max {c_max}")
+                for k in ("node_token", "parent_row", "n_rows"):
+                    assert_rows_equal(g[k], o[k], ok, f"{k} c_max {c_max} depth {dmax} scored {scored}")
+                assert_close(g["Q"], o["Q"], "Q")
+                if scored:
+                    assert_close(g["s_curve"], o["S_curve"], "S(n)")
+                if c_max >= full and dmax == 64:
+                    # without caps, a forest smaller than the block plus every
+                    # chain token: chains passed nodes that were there already
+                    shared += int((o["count"] < nd + ngl.reshape(BS, P + 1).sum(1)).sum())
+    assert shared > 0
+
+
 @pytest.mark.parametrize("BS", [1, 63, 1000, 1024, 1025, 1500])
 def test_tree_row_bases_any_batch(BS):
     """Row bases and the total over every batch size the row scan handles in
