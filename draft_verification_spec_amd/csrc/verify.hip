@@ -2209,13 +2209,33 @@ __global__ __launch_bounds__(kWave) void k_tree_walk(TreeParams P)
         for (int u = 0; u < kPer; ++u) s4[t + u * kWave] = held[u];
     }
     __syncthreads();
-    if (t < n) {
-        int32_t idx;
-        // one call per address space (a pointer that may be either compiles
-        // to flat loads)
-        if (staged) sOk[t] = merge_argmax(sp + (int64_t)t * P.splits, P.splits, 1, &idx);
-        else sOk[t] = merge_argmax(gp + (int64_t)t * P.splits, P.splits, 1, &idx);
-        sArg[t] = (idx == 0x7FFFFFFF) ? -1 : idx;
+    {
+        // each row's partials merged by g lanes, then across them (the merge
+        // keeps the largest value and its lowest index, in any grouping); one
+        // loop per address space (a pointer that may be either compiles to
+        // flat loads)
+        const int lg = n <= kWave / 4 ? 2 : (n <= kWave / 2 ? 1 : 0), g = 1 << lg;
+        const int row = t >> lg, sub = t & (g - 1);
+        ArgAcc acc{-INFINITY, 0x7FFFFFFF, 0};
+        auto take = [&](const Partial q) {
+            ArgAcc b{q.m, q.idx & 0x7FFFFFFF, (q.idx >> 31) & 1};
+            if (q.m != q.m) b.bad = 1;
+            am_combine(acc, b);
+        };
+        if (row < n) {
+            if (staged)
+                for (int s = sub; s < P.splits; s += g) take(sp[(int64_t)row * P.splits + s]);
+            else
+                for (int s = sub; s < P.splits; s += g) take(gp[(int64_t)row * P.splits + s]);
+        }
+        for (int o = 1; o < g; o <<= 1) {
+            ArgAcc b{__shfl_xor(acc.best, o, kWave), __shfl_xor(acc.idx, o, kWave), __shfl_xor(acc.bad, o, kWave)};
+            am_combine(acc, b);
+        }
+        if (row < n && sub == 0) {
+            sOk[row] = !acc.bad && acc.idx != 0x7FFFFFFF;
+            sArg[row] = (acc.idx == 0x7FFFFFFF) ? -1 : acc.idx;
+        }
     }
     for (int i = t; i < rm; i += kWave) { sOut[i] = -1; sPath[i] = -1; }
     __syncthreads();
