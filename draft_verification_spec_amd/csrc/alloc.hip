@@ -649,6 +649,11 @@ __device__ __forceinline__ int walk_parallel(const spec_tree_alloc& A, int P_, i
     const int t = threadIdx.x, lane = t % kWave;
     const int L = A.ngram_ld, C = P_ + 1, E = C * L, npair = C * (C - 1) / 2;
     const bool w0 = t < kWave;
+    // x / L for 0 <= x < 2^20 as a multiply-high by ceil(2^32 / L) (exact:
+    // the error is below x / 2^32, less than the distance to the next
+    // multiple of 1 / L); L = 1 apart, whose factor does not fit 32 bits
+    const uint32_t mL = L > 1 ? 0xFFFFFFFFu / (uint32_t)L + 1u : 0u;
+    auto divL = [&](int x) { return L > 1 ? (int)__umulhi((uint32_t)x, mL) : x; };
     const int pick0 = 1;   // node of position d's pick: pick0 + (d - 1) * Kc
     if (w0) {
         const int gl = lane < C ? clen[lane] : 0;
@@ -670,15 +675,16 @@ __device__ __forceinline__ int walk_parallel(const spec_tree_alloc& A, int P_, i
     // (c', c), c' < c, at c (c - 1) / 2 + c': the first j at which chain c's
     // token j and chain c''s token at the same depth differ or either ends)
     for (int e = t; e < E; e += nthr) {
-        const int c = e / L, i = e - c * L;
+        const int c = divL(e), i = e - c * L;
         if (i >= cgeff[c]) continue;
         const int d = c + 1 + i;
         if (d > P_ || ctok[e] != ftok[pick0 + (d - 1) * Kc]) atomicMin(&cfp[c], i);
     }
     for (int w = t; w < npair * L; w += nthr) {
-        const int q = w / L, j = w - q * L;
-        int c = 1;
-        while ((c + 1) * c / 2 <= q) ++c;   // c (c - 1) / 2 <= q < (c + 1) c / 2
+        const int q = divL(w), j = w - q * L;
+        // c with c (c - 1) / 2 <= q < (c + 1) c / 2
+        int c = (int)((1.0f + sqrtf(1.0f + 8.0f * (float)q)) * 0.5f);
+        c = c * (c - 1) / 2 > q ? c - 1 : ((c + 1) * c / 2 <= q ? c + 1 : c);
         const int cp = q - c * (c - 1) / 2, jp = c - cp + j;
         const bool differ = j >= cgeff[c] || jp >= cgeff[cp] || ctok[c * L + j] != ctok[cp * L + jp];
         if (differ) atomicMin(&wagr[q], j);
@@ -687,7 +693,7 @@ __device__ __forceinline__ int walk_parallel(const spec_tree_alloc& A, int P_, i
     // each entry's node: a drafter node's index, or 1024 + the chain that
     // makes the n-gram node
     for (int e = t; e < E; e += nthr) {
-        const int c = e / L, i = e - c * L;
+        const int c = divL(e), i = e - c * L;
         if (i >= cgeff[c]) continue;
         const int d = c + 1 + i, fp = cfp[c];
         int code = -1;
@@ -706,12 +712,11 @@ __device__ __forceinline__ int walk_parallel(const spec_tree_alloc& A, int P_, i
             const int fc = cfol[e];
             atomicMax(&wpass[code], fc > 0 ? 32 + 4 * follower_class(fc) : 4 * (int)cev[c]);
         } else {
+            // (every earlier chain is looked at, with no early exit, so that
+            // the loads go out together)
             int cr = c;
-            for (int cp = 0; cp < c; ++cp)
-                if (cfp[cp] >= c - cp && wagr[c * (c - 1) / 2 + cp] >= d - c) {
-                    cr = cp;
-                    break;
-                }
+            for (int cp = c - 1; cp >= 0; --cp)
+                if (cfp[cp] >= c - cp && wagr[c * (c - 1) / 2 + cp] >= d - c) cr = cp;
             code = 1024 + cr;
             if (cr == c) atomicMin(&cdn[c], d);
         }
@@ -720,7 +725,7 @@ __device__ __forceinline__ int walk_parallel(const spec_tree_alloc& A, int P_, i
     __syncthreads();
     // passes of other chains' nodes; the chains' first indices
     for (int e = t; e < E; e += nthr) {
-        const int c = e / L, i = e - c * L;
+        const int c = divL(e), i = e - c * L;
         if (i >= cgeff[c]) continue;
         const int code = went[e] & ~kPass;   // (another thread may be marking this entry)
         if (code >= 1024 && code - 1024 != c) {
@@ -743,7 +748,7 @@ __device__ __forceinline__ int walk_parallel(const spec_tree_alloc& A, int P_, i
     __syncthreads();
     // the new nodes
     for (int e = t; e < E; e += nthr) {
-        const int c = e / L, i = e - c * L;
+        const int c = divL(e), i = e - c * L;
         if (i >= cgeff[c]) continue;
         const int code = went[e];
         if ((code & ~kPass) != 1024 + c) continue;
@@ -804,6 +809,11 @@ __global__ __launch_bounds__(kTreeBlock) void k_tree(TreeBuildParams P)
     __shared__ int32_t fcontra[SPEC_MAX_FOREST];   // a drafter node's largest contradicting class (-1 none)
     __shared__ double fw[SPEC_MAX_FOREST];
     __shared__ unsigned long long fkids[kWave];   // a small forest's children, as lane masks
+    // the Eq. (6) tables that nodes index by bucket, class or depth, copied
+    // at the start (their per-lane reads would otherwise wait on memory after
+    // the walk): buckets 64, agreements 64 x 2, contradictions 8 x 2, depths 16
+    constexpr int kCoefAg = 64, kCoefCo = kCoefAg + 128, kCoefPsi = kCoefCo + 16, kCoefN = kCoefPsi + 16;
+    __shared__ double scoef[kCoefN];
     __shared__ int32_t sh_cnt;
     // the chains' tokens, lengths and evidence classes, staged in one round
     // trip (the tokens when they fit)
@@ -830,6 +840,13 @@ __global__ __launch_bounds__(kTreeBlock) void k_tree(TreeBuildParams P)
             pf_s = P.sc.sigma[(int64_t)r * P_ + p - 1];
             if (k > 0) pf_r = P.sc.r_share[((int64_t)r * P_ + p - 1) * Kc + k];
         }
+    }
+    if (P.scored && t < kCoefN) {
+        const spec_tree_scores& S = P.sc;
+        scoef[t] = t < kCoefAg ? S.w_bucket[t]
+                 : t < kCoefCo ? S.w_agreed[(t - kCoefAg) >> 1][(t - kCoefAg) & 1]
+                 : t < kCoefPsi ? S.w_contra[(t - kCoefCo) >> 1][(t - kCoefCo) & 1]
+                 : S.psi_depth[t - kCoefPsi];
     }
     for (int i = t; i <= P_; i += kTreeBlock) {
         clen[i] = A.ngram_len[q0 + i];
@@ -1120,21 +1137,21 @@ __global__ __launch_bounds__(kTreeBlock) void k_tree(TreeBuildParams P)
                 continue;
             }
             if (kind == 3) {
-                sj = lps + S.w_bucket[fbucket[j]] + pc + br;
+                sj = lps + scoef[fbucket[j]] + pc + br;
             } else {
                 const int p = fdep[j], k = (j - 1) % Kc, ps = kind == 1 ? 0 : 1;
                 const double lh = logit_prob((double)(pre ? pf_h : S.h[(int64_t)r * P_ + p - 1]));
                 const double ls = logit_prob((double)(pre ? pf_s : S.sigma[(int64_t)r * P_ + p - 1]));
-                const double psi = pc + S.psi_depth[p < 15 ? p : 15];
+                const double psi = pc + scoef[kCoefPsi + (p < 15 ? p : 15)];
                 if (kind == 1) {
                     sj = S.a[0] + S.a[1] * lh + S.a[2] * ls + psi + br;
                 } else {
                     const double rr = clamp_prob((double)(pre ? pf_r : S.r_share[((int64_t)r * P_ + p - 1) * Kc + k]));
                     sj = S.a[3] + S.a[4] * log(rr) + S.a[5] * lh + S.a[6] * ls + psi + br;
                 }
-                if (fagree[j] >= 0) sj += plus + S.w_agreed[fagree[j]][ps];
+                if (fagree[j] >= 0) sj += plus + scoef[kCoefAg + 2 * fagree[j] + ps];
                 const int contra = fcontra[j];
-                if (contra >= 0) sj += -plus + S.w_contra[contra][ps];
+                if (contra >= 0) sj += -plus + scoef[kCoefCo + 2 * contra + ps];
             }
             fw[j] = exp(sj);
         }
