@@ -611,6 +611,47 @@ __device__ __forceinline__ void tree_rows(const spec_tree_alloc& A, int r, int l
 // after it.
 typedef int32_t __attribute__((may_alias)) wi32;
 
+// The parallel walk's words, in LDS borrowed from an array written only after
+// the walk: a drafter node's largest passing bucket (-1: none), and per chain
+// its entries (tokens within the depth limit), first entry off the pick path,
+// entries that are drafter nodes, depth of its first own node (kWalkNone:
+// none), index of its first own node; then the own nodes of all chains.
+constexpr int kWalkPass = 1 << 20;   // on a made node's entry: a later chain passes it
+constexpr int kWalkNone = 1 << 30;
+struct WalkWords {
+    wi32 *pass, *geff, *fp, *ndr, *dn, *base, *total;
+    __device__ explicit WalkWords(wi32* w)
+        : pass(w), geff(w + SPEC_MAX_FOREST), fp(geff + kWave), ndr(fp + kWave), dn(ndr + kWave),
+          base(dn + kWave), total(base + kWave) {}
+};
+
+// The parallel walk's starting values, set before the workgroup's first
+// barrier (the chain lengths are read from memory: their LDS copy is being
+// written meanwhile): the per-chain words on wave 0, the marks and the pairs'
+// agreement lengths by every thread.
+__device__ __forceinline__ void walk_parallel_init(const spec_tree_alloc& A, int P_, int nd, int64_t q0, int nthr,
+                                                   wi32* wagr, wi32* wscr, uint32_t& flags)
+{
+    const WalkWords W(wscr);
+    const int t = threadIdx.x, lane = t % kWave;
+    const int L = A.ngram_ld, C = P_ + 1, npair = C * (C - 1) / 2;
+    if (t < kWave) {
+        const int gl = lane < C ? A.ngram_len[q0 + lane] : 0;
+        if (__builtin_amdgcn_ballot_w64(gl < 0 || gl > L)) flags |= SPEC_FLAG_BAD_LENGTH;
+        if (lane < C) {
+            const int g = gl < 0 ? 0 : (gl > L ? L : gl);
+            int ge = A.depth_max - lane < g ? A.depth_max - lane : g;
+            ge = ge > 0 ? ge : 0;
+            W.geff[lane] = ge;
+            W.fp[lane] = ge;
+            W.ndr[lane] = ge;
+            W.dn[lane] = kWalkNone;
+        }
+    }
+    for (int n = t; n < nd; n += nthr) W.pass[n] = -1;
+    for (int q = t; q < npair; q += nthr) wagr[q] = kWalkNone;
+}
+
 // The chain walk without a walk: every (chain, token) entry finds its node at
 // once, over the whole workgroup.  Chain c starts at the anchor (c = 0, depth
 // 0) or at pick c (depth c); its token i sits at depth c + 1 + i.  A node is
@@ -630,22 +671,23 @@ typedef int32_t __attribute__((may_alias)) wi32;
 // agreed; a drafter node also takes the largest bucket of the tokens that pass
 // it.  All threads of the workgroup call this (it holds barriers); the drafter
 // nodes are in the forest arrays already.  Writes the n-gram nodes and the
-// marks and returns the node count.
+// marks and returns the node count.  Its starting values come from
+// walk_parallel_init, before the barrier this begins after.
 __device__ __forceinline__ int walk_parallel(const spec_tree_alloc& A, int P_, int Kc, int nd, int cmax, int nthr,
                                              const int32_t* clen, const int8_t* cev, const int32_t* ctok,
                                              const int32_t* cfol, int32_t* ftok, int32_t* fpar, int32_t* fdep,
                                              uint8_t* fkind, int8_t* fabove, int8_t* fbucket, int8_t* fagree,
                                              wi32* went, wi32* wagr, wi32* wscr, uint32_t& flags)
 {
-    constexpr int kPass = 1 << 20;      // on a made node's entry: a later chain passes it
-    constexpr int kNone = 1 << 30;
-    wi32* wpass = wscr;                  // [nd]: a drafter node's largest passing bucket (-1: none)
-    wi32* cgeff = wscr + SPEC_MAX_FOREST;        // per chain: entries (tokens within the depth limit)
-    wi32* cfp = cgeff + kWave;                   // per chain: first entry off the pick path
-    wi32* cndr = cfp + kWave;                    // per chain: entries that are drafter nodes
-    wi32* cdn = cndr + kWave;                    // per chain: depth of its first own node (kNone: none)
-    wi32* cbase = cdn + kWave;                   // per chain: index of its first own node
-    wi32* ctotal = cbase + kWave;                // own nodes of all chains
+    constexpr int kPass = kWalkPass, kNone = kWalkNone;
+    const WalkWords W(wscr);
+    wi32* wpass = W.pass;
+    wi32* cgeff = W.geff;
+    wi32* cfp = W.fp;
+    wi32* cndr = W.ndr;
+    wi32* cdn = W.dn;
+    wi32* cbase = W.base;
+    wi32* ctotal = W.total;
     const int t = threadIdx.x, lane = t % kWave;
     const int L = A.ngram_ld, C = P_ + 1, E = C * L, npair = C * (C - 1) / 2;
     const bool w0 = t < kWave;
@@ -655,22 +697,6 @@ __device__ __forceinline__ int walk_parallel(const spec_tree_alloc& A, int P_, i
     const uint32_t mL = L > 1 ? 0xFFFFFFFFu / (uint32_t)L + 1u : 0u;
     auto divL = [&](int x) { return L > 1 ? (int)__umulhi((uint32_t)x, mL) : x; };
     const int pick0 = 1;   // node of position d's pick: pick0 + (d - 1) * Kc
-    if (w0) {
-        const int gl = lane < C ? clen[lane] : 0;
-        if (__builtin_amdgcn_ballot_w64(gl < 0 || gl > L)) flags |= SPEC_FLAG_BAD_LENGTH;
-        if (lane < C) {
-            const int g = gl < 0 ? 0 : (gl > L ? L : gl);
-            int ge = A.depth_max - lane < g ? A.depth_max - lane : g;
-            ge = ge > 0 ? ge : 0;
-            cgeff[lane] = ge;
-            cfp[lane] = ge;
-            cndr[lane] = ge;
-            cdn[lane] = kNone;
-        }
-    }
-    for (int n = t; n < nd; n += nthr) wpass[n] = -1;
-    for (int q = t; q < npair; q += nthr) wagr[q] = kNone;
-    __syncthreads();
     // departures from the pick path, and the pairs' agreement lengths (pair
     // (c', c), c' < c, at c (c - 1) / 2 + c': the first j at which chain c's
     // token j and chain c''s token at the same depth differ or either ends)
@@ -874,13 +900,38 @@ __global__ __launch_bounds__(kTreeBlock) void k_tree(TreeBuildParams P)
             rkind[s] = k == 0 ? 1 : 2;
         }
     }
+    // With the chains on the lanes and their tokens in LDS, all chains walk
+    // together in one parallel pass (below); otherwise, and for the largest
+    // forests (whose register slots leave no room for both walks), one chain
+    // after another.  The parallel walk's set-up and its drafter nodes (whose
+    // tokens it reads) go in before the first barrier.
+    const bool by_depth = NS <= 8 && P_ < kWave && staged;
+    uint32_t flags = 0;
+    if (by_depth) {
+        if (wid == 0) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const int n = s * kWave + lane;
+                if (n < nd) {
+                    ftok[n] = rtok[s];
+                    fpar[n] = rpar[s];
+                    fdep[n] = rdep[s];
+                    fkind[n] = (uint8_t)rkind[s];
+                    fabove[n] = 0;
+                    fbucket[n] = -1;
+                    fagree[n] = -1;
+                }
+            }
+        }
+        walk_parallel_init(A, P_, nd, q0, kTreeBlock, reinterpret_cast<wi32*>(fQ), reinterpret_cast<wi32*>(fden),
+                           flags);
+    }
     __syncthreads();
     // n-gram chains from the anchor (s = 0) and each pick s.  The walk's state
     // (current node, its depth, kind and n-gram count, the node count) is
     // wave-uniform.  A chain first descends through existing nodes while its
     // tokens match (the lowest-index matching child each time) and then
     // appends the rest of its tokens as a new path.
-    uint32_t flags = 0;
     int cntr = nd;
     // the chains' lengths and evidence classes on the lanes (chain sc on lane
     // sc) when there are at most 64 chains
@@ -891,28 +942,7 @@ __global__ __launch_bounds__(kTreeBlock) void k_tree(TreeBuildParams P)
     // (an empty chain adds nothing and passes no node)
     uint64_t live = __builtin_amdgcn_ballot_w64(lglen > 0);
     if (__builtin_amdgcn_ballot_w64(lglen < 0)) flags |= SPEC_FLAG_BAD_LENGTH;
-    // With the chains on the lanes and their tokens in LDS, all chains walk
-    // together, one depth per round (below); otherwise, and for the largest
-    // forests (whose register slots leave no room for both walks), one chain
-    // after another.
-    const bool by_depth = NS <= 8 && lane_chains && staged;
     if (by_depth) {
-      if (wid == 0) {
-        // The drafter nodes go to LDS first: the walk reads their tokens.
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const int n = s * kWave + lane;
-            if (n < nd) {
-                ftok[n] = rtok[s];
-                fpar[n] = rpar[s];
-                fdep[n] = rdep[s];
-                fkind[n] = (uint8_t)rkind[s];
-                fabove[n] = 0;
-                fbucket[n] = -1;
-                fagree[n] = -1;
-            }
-        }
-      }
       cntr = walk_parallel(A, P_, Kc, nd, cmax, kTreeBlock, clen, cev, ctok, cfol, ftok, fpar, fdep, fkind, fabove,
                            fbucket, fagree, reinterpret_cast<wi32*>(fw), reinterpret_cast<wi32*>(fQ),
                            reinterpret_cast<wi32*>(fden), flags);
@@ -1187,10 +1217,23 @@ __global__ __launch_bounds__(kTreeBlock) void k_tree(TreeBuildParams P)
             kids &= kids - 1;
         }
         const double ratio = wj / shfl_f64(den, pj < 0 ? 0 : pj);
+        // Q four levels per round: a node k levels below the round's first
+        // depth d takes Q of its ancestor at depth d - 1 (final since the last
+        // round) and multiplies in the ratios down its path, top first: the
+        // parent-times-ratio product in the same order
+        const int a1 = pj < 0 ? 0 : pj;
+        const int a2 = __shfl(a1, a1, kWave), a3 = __shfl(a1, a2, kWave), a4 = __shfl(a1, a3, kWave);
+        const double r1 = shfl_f64(ratio, a1), r2 = shfl_f64(ratio, a2), r3 = shfl_f64(ratio, a3);
         double q = 1.0;
-        for (int d = 1; __builtin_amdgcn_ballot_w64(dj == d); ++d) {
-            const double qp = shfl_f64(q, pj < 0 ? 0 : pj);
-            q = dj == d ? qp * ratio : q;
+        for (int d = 1; __builtin_amdgcn_ballot_w64(dj >= d); d += 4) {
+            const int k = dj - d;
+            const double qa = shfl_f64(q, k <= 0 ? a1 : (k == 1 ? a2 : (k == 2 ? a3 : a4)));
+            double v = qa;
+            if (k >= 3) v = v * r3;
+            if (k >= 2) v = v * r2;
+            if (k >= 1) v = v * r1;
+            v = v * ratio;
+            q = (k >= 0 && k < 4) ? v : q;
         }
         if (mine) {
             fden[lane] = den;
