@@ -14,12 +14,13 @@
 //     wave-wide suffix scan), stopping as soon as the boundary bucket is taken
 //     whole, then each request's verified prefix and the CSR row bases.
 // Trees (AdaSpark, Sections 2.2, 3.1, 3.3):
-//   k_tree    : four waves per request; wave 0 builds the candidate forest
-//               (drafter block + n-gram chains, copied or follower tokens)
-//               with the nodes in lane registers during the chain walk, then
-//               in LDS; the acceptance estimates of the Eq. (6) form (shared
-//               out over the waves), the path products Q, the best-first top
-//               rows_cap-1 (Proposition 1) and the depth-first layout.
+//   k_tree    : four waves per request build the candidate forest (drafter
+//               block + n-gram chains, copied or follower tokens) in one
+//               parallel pass over the chains' tokens (or chain by chain on
+//               wave 0 for the largest forests), then the acceptance
+//               estimates of the Eq. (6) form, the path products Q, the
+//               best-first top rows_cap-1 (Proposition 1) and the
+//               depth-first layout.
 //   k_tree_forest: the same rows from a forest the caller built.
 //   k_rows_scan: exclusive prefix sum of the rows per request.
 #include <cstring>
@@ -566,14 +567,14 @@ __device__ __forceinline__ void tree_rows(const spec_tree_alloc& A, int r, int l
         }
     }
     const bool reach = in && jmp == -1;
-    // the nodes before this one: w is an ancestor (w's set within ours), or
+    // The nodes before this one: w is an ancestor (w's set within ours), or
     // both paths continue below the common ancestor and w's continues through
     // the lower index (along a path the indices grow with depth, so the
     // lowest index of a path's part below the common ancestor is its child
-    // there)
-    // With lowest(empty) = -1 one signed compare decides: an ancestor has
-    // x empty (-1 < anything), a descendant has y empty (never before).
-    // Four lanes w per round (lanes past the set hold jmp -3 and never count).
+    // there).  With lowest(empty) = -1 one signed compare decides: an
+    // ancestor has x empty (-1 < anything), a descendant has y empty (never
+    // before).  Four lanes w per round (lanes past the set hold jmp -3 and
+    // never count).
     int row = 0;
     for (int wb = 0; wb < m; wb += 4) {
 #pragma unroll
@@ -674,7 +675,7 @@ __device__ __forceinline__ void walk_parallel_init(const spec_tree_alloc& A, int
 // marks and returns the node count.  Its starting values come from
 // walk_parallel_init, before the barrier this begins after.
 __device__ __forceinline__ int walk_parallel(const spec_tree_alloc& A, int P_, int Kc, int nd, int cmax, int nthr,
-                                             const int32_t* clen, const int8_t* cev, const int32_t* ctok,
+                                             const int8_t* cev, const int32_t* ctok,
                                              const int32_t* cfol, int32_t* ftok, int32_t* fpar, int32_t* fdep,
                                              uint8_t* fkind, int8_t* fabove, int8_t* fbucket, int8_t* fagree,
                                              wi32* went, wi32* wagr, wi32* wscr, uint32_t& flags)
@@ -808,10 +809,11 @@ __device__ __forceinline__ int walk_parallel(const spec_tree_alloc& A, int P_, i
     return nd + total < cmax ? nd + total : cmax;
 }
 
-// NS register slots per lane: forest node j lives on lane j % 64 in slot
-// j / 64 during the chain walk (NS * 64 >= c_max).  Four waves per request:
-// wave 0 walks the chains; the weights, denominators and ranks of large
-// forests are shared out over all four.
+// Four waves per request.  The chain walk is walk_parallel's pass over the
+// (chain, token) entries, or, for the largest forests and chains not staged
+// in LDS, a chain-by-chain walk on wave 0 with forest node j in lane
+// registers (lane j % 64, slot j / 64; NS * 64 >= c_max).  The weights,
+// denominators and ranks of large forests are shared out over all four.
 constexpr int kTreeBlock = 256;
 
 template <int NS>
@@ -905,9 +907,9 @@ __global__ __launch_bounds__(kTreeBlock) void k_tree(TreeBuildParams P)
     // forests (whose register slots leave no room for both walks), one chain
     // after another.  The parallel walk's set-up and its drafter nodes (whose
     // tokens it reads) go in before the first barrier.
-    const bool by_depth = NS <= 8 && P_ < kWave && staged;
+    const bool parallel_walk = NS <= 8 && P_ < kWave && staged;
     uint32_t flags = 0;
-    if (by_depth) {
+    if (parallel_walk) {
         if (wid == 0) {
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
@@ -927,11 +929,7 @@ __global__ __launch_bounds__(kTreeBlock) void k_tree(TreeBuildParams P)
                            flags);
     }
     __syncthreads();
-    // n-gram chains from the anchor (s = 0) and each pick s.  The walk's state
-    // (current node, its depth, kind and n-gram count, the node count) is
-    // wave-uniform.  A chain first descends through existing nodes while its
-    // tokens match (the lowest-index matching child each time) and then
-    // appends the rest of its tokens as a new path.
+    // n-gram chains from the anchor (s = 0) and each pick s
     int cntr = nd;
     // the chains' lengths and evidence classes on the lanes (chain sc on lane
     // sc) when there are at most 64 chains
@@ -942,11 +940,16 @@ __global__ __launch_bounds__(kTreeBlock) void k_tree(TreeBuildParams P)
     // (an empty chain adds nothing and passes no node)
     uint64_t live = __builtin_amdgcn_ballot_w64(lglen > 0);
     if (__builtin_amdgcn_ballot_w64(lglen < 0)) flags |= SPEC_FLAG_BAD_LENGTH;
-    if (by_depth) {
-      cntr = walk_parallel(A, P_, Kc, nd, cmax, kTreeBlock, clen, cev, ctok, cfol, ftok, fpar, fdep, fkind, fabove,
+    if (parallel_walk) {
+      cntr = walk_parallel(A, P_, Kc, nd, cmax, kTreeBlock, cev, ctok, cfol, ftok, fpar, fdep, fkind, fabove,
                            fbucket, fagree, reinterpret_cast<wi32*>(fw), reinterpret_cast<wi32*>(fQ),
                            reinterpret_cast<wi32*>(fden), flags);
     } else {
+    // One chain after another on wave 0.  The walk's state (current node, its
+    // depth, kind and n-gram count, the node count) is wave-uniform.  A chain
+    // first descends through existing nodes while its tokens match (the
+    // lowest-index matching child each time) and then appends the rest of its
+    // tokens as a new path.
     for (int it = 0; wid == 0 && it <= P_; ++it) {
         int sc = it;
         if (lane_chains) {
