@@ -366,6 +366,45 @@ def test_tree_build_shared_paths(P, Kc, L, vocab):
     assert shared > 0
 
 
+@pytest.mark.parametrize("P,Kc,L,extra", [(0, 1, 6, 0), (0, 3, 6, 4), (4, 1, 6, 0), (3, 2, 0, 0), (3, 2, 5, 0)])
+def test_tree_build_degenerate_shapes(P, Kc, L, extra):
+    """Shapes at the edges of the tree build's arguments: no drafter block
+    (the anchor's chain alone), one candidate per position, no n-gram tokens
+    (ngram_ld 0), every chain empty, c_max leaving no room past the block or
+    only `extra` nodes, depth limit 1 and a single row."""
+    import torch
+    import draft_verification_spec_amd as S
+    rng = np.random.Generator(np.random.Philox(7700 + 100 * P + 10 * Kc + L))
+    BS, vocab = 24, 4
+    block = rng.integers(0, vocab, (BS, P, Kc)).astype(np.int32)
+    ng = rng.integers(0, vocab, (BS * (P + 1), L)).astype(np.int32)
+    for r in range(BS):
+        for c in range(P + 1):
+            if P and c < P and L and rng.random() < 0.5:
+                ng[r * (P + 1) + c, 0] = block[r, c, 0]   # follow the next pick
+    nd = 1 + P * Kc
+    for empty in (False, True):
+        ngl = np.zeros(BS * (P + 1), np.int32) if empty or L == 0 else rng.integers(0, L + 1, BS * (P + 1)).astype(
+            np.int32)
+        for c_max in sorted({nd, nd + extra, nd + (P + 1) * L}):
+            wn = rng.standard_exponential((BS, c_max)).astype(np.float32)
+            wz = rng.standard_exponential((BS, c_max)).astype(np.float32)
+            for dmax, rows_cap in ((1, 1), (1, 8), (6, 64)):
+                print(f"tree build, edge shape: P {P} Kc {Kc} L {L} empty {empty} c_max {c_max} depth {dmax} "
+                      f"rows_cap {rows_cap}", flush=True)
+                o = O.tree_build_batch(block, ng, ngl, wn, wz, dmax, rows_cap)
+                g = S.spec_allocate_budget(mode="tree", block=dev(block), ngram_draft=dev(ng), ngram_len=dev(ngl),
+                                           w_node=dev(wn), w_none=dev(wz), depth_max=dmax, rows_cap=rows_cap)
+                torch.cuda.synchronize()
+                g = {k: host(v) for k, v in g.items()}
+                ok = ok_rows(o["flags"])
+                assert_rows_equal(g["forest_count"], o["count"], np.ones(BS, bool), "forest_count")
+                for k in ("node_token", "parent_row", "n_rows"):
+                    assert_rows_equal(g[k], o[k], ok, f"{k} c_max {c_max} depth {dmax} rows_cap {rows_cap}")
+                assert_close(g["Q"], o["Q"], "Q")
+                assert np.array_equal(g["row_base"], np.concatenate([[0], np.cumsum(g["n_rows"])[:-1]]))
+
+
 @pytest.mark.parametrize("BS", [1, 63, 1000, 1024, 1025, 1500])
 def test_tree_row_bases_any_batch(BS):
     """Row bases and the total over every batch size the row scan handles in
