@@ -197,25 +197,44 @@ __device__ __forceinline__ void ngram_scan(const Text& x, int32_t* win, NgramSha
         }
     }
     __syncthreads();
-    // phase 2: each wave extends listed candidates 64 tokens per step
+    // phase 2: the listed candidates, four per wave (16 lanes each) for their
+    // 16 tokens past kPre (most stop there); each one still matching then
+    // takes the whole wave, 64 tokens per step
     const int nc = S.n_cand < NCAND ? S.n_cand : NCAND;
-    for (int c = wid; c < nc; c += NT / kWave) {
-        const int64_t j = S.cand[c];
-        const int64_t lim = (j + 1 < O.cap) ? j + 1 : O.cap;
-        int64_t l = kPre;
-        for (;;) {
-            const int64_t i = l + lane;
-            const bool eq = i < lim && at(j - i) == S.suf[i];
-            const uint64_t miss = ~__ballot(eq);
-            if (miss == 0) {
-                l += kWave;
-                continue;
-            }
-            l += (int64_t)__builtin_ctzll(miss);
-            break;
+    constexpr int kSeg = 16, kSegs = kWave / kSeg;
+    const int sub = lane / kSeg, sl = lane % kSeg;
+    for (int c0 = wid * kSegs; c0 < nc; c0 += (NT / kWave) * kSegs) {
+        const int c = c0 + sub;
+        const bool has = c < nc;
+        const int32_t j = has ? S.cand[c] : 0;
+        const int32_t lim = has ? ((j + 1 < O.cap) ? j + 1 : O.cap) : 0;
+        const int64_t i0 = kPre + sl;
+        const bool eq0 = i0 < lim && at(j - i0) == S.suf[i0];
+        const uint32_t seg = (uint32_t)(__ballot(eq0) >> (sub * kSeg)) & 0xFFFFu;
+        const bool longer = has && seg == 0xFFFFu;
+        if (has && sl == 0 && !longer) {
+            int64_t l = kPre + __builtin_ctz(~seg);
+            if (l > lim) l = lim;
+            if (l >= O.n_min) best = top2_insert(best, ((uint64_t)l << 32) | (uint64_t)j);
         }
-        if (l > lim) l = lim;
-        if (lane == 0 && l >= O.n_min) best = top2_insert(best, ((uint64_t)l << 32) | (uint64_t)j);
+        for (uint64_t lm = __ballot(longer && sl == 0); lm; lm &= lm - 1) {
+            const int g = (int)__builtin_ctzll(lm);
+            const int32_t jj = __builtin_amdgcn_readlane(j, g), ll = __builtin_amdgcn_readlane(lim, g);
+            int64_t l = kPre + kSeg;
+            for (;;) {
+                const int64_t i = l + lane;
+                const bool eq = i < ll && at(jj - i) == S.suf[i];
+                const uint64_t miss = ~__ballot(eq);
+                if (miss == 0) {
+                    l += kWave;
+                    continue;
+                }
+                l += (int64_t)__builtin_ctzll(miss);
+                break;
+            }
+            if (l > ll) l = ll;
+            if (lane == 0 && l >= O.n_min) best = top2_insert(best, ((uint64_t)l << 32) | (uint64_t)jj);
+        }
     }
     best = wave_top2(best);
     if (lane == 0) S.sh[wid] = best;
