@@ -678,7 +678,7 @@ __device__ __forceinline__ int walk_parallel(const spec_tree_alloc& A, int P_, i
                                              const int8_t* cev, const int32_t* ctok,
                                              const int32_t* cfol, int32_t* ftok, int32_t* fpar, int32_t* fdep,
                                              uint8_t* fkind, int8_t* fabove, int8_t* fbucket, int8_t* fagree,
-                                             wi32* went, wi32* wagr, wi32* wscr, uint32_t& flags)
+                                             wi32* went, wi32* wagr, wi32* wscr)
 {
     constexpr int kPass = kWalkPass, kNone = kWalkNone;
     const WalkWords W(wscr);
@@ -943,7 +943,7 @@ __global__ __launch_bounds__(kTreeBlock) void k_tree(TreeBuildParams P)
     if (parallel_walk) {
       cntr = walk_parallel(A, P_, Kc, nd, cmax, kTreeBlock, cev, ctok, cfol, ftok, fpar, fdep, fkind, fabove,
                            fbucket, fagree, reinterpret_cast<wi32*>(fw), reinterpret_cast<wi32*>(fQ),
-                           reinterpret_cast<wi32*>(fden), flags);
+                           reinterpret_cast<wi32*>(fden));
     } else {
     // One chain after another on wave 0.  The walk's state (current node, its
     // depth, kind and n-gram count, the node count) is wave-uniform.  A chain
