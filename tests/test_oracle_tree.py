@@ -93,6 +93,77 @@ def test_ngram_fill_agrees_and_branches():
     assert t2["count"] == 1 + 6 + 1 + 0     # only 99 at depth 3 from the anchor chain; 50 would be depth 4
 
 
+def path_forest(block, chains, depth_max, c_max):
+    """The candidate forest from its definition (AdaSpark Section 3.3, n-gram
+    fill): a node is a token path from the anchor.  The drafter block gives
+    position p's candidates below pick p - 1 (a path through a token that
+    several candidates hold goes through the lowest of them); chain s starts
+    at the anchor (s = 0) or at pick s, and each of its tokens within the
+    depth limit extends its path by one.  The first appearance of a path, in
+    chain order and then token order, makes its node, numbered after the
+    block; c_max drops the nodes past it (and every path below them).  A node
+    that a chain reaches without making it is agreed."""
+    P, Kc = block.shape
+    index, info = {(): 0}, {0: ((), -1)}
+    for p in range(1, P + 1):
+        prefix = tuple(int(block[q, 0]) for q in range(p - 1))
+        for k in range(Kc):
+            j = 1 + (p - 1) * Kc + k
+            path = prefix + (int(block[p - 1, k]),)
+            index.setdefault(path, j)
+            info[j] = (path, 0 if p == 1 else 1 + (p - 2) * Kc)
+    n, agreed = 1 + P * Kc, set()
+    for s_, chain in enumerate(chains):
+        path = tuple(int(block[q, 0]) for q in range(s_))
+        for i, tok in enumerate(chain):
+            if len(path) + 1 > depth_max:
+                break
+            parent = index.get(path)
+            path = path + (int(tok),)
+            if path in index:
+                agreed.add(index[path])
+            elif parent is not None and n < c_max:
+                index[path] = n
+                info[n] = (path, parent)
+                n += 1
+    return n, index, info, agreed
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_forest_is_the_set_of_chain_paths(seed):
+    """The oracle's chain walk (a descent per chain, then a new path) against
+    the forest of distinct token paths: the node count, every node's token
+    and parent, the order new nodes are made in and the agreed marks, on
+    blocks whose picks follow a text and chains that continue it from each
+    pick, with duplicate candidates, depth limits and c_max caps."""
+    rng = np.random.default_rng(900 + seed)
+    for _ in range(60):
+        P, Kc, L, V = int(rng.integers(0, 7)), int(rng.integers(1, 4)), int(rng.integers(1, 9)), int(rng.integers(2, 5))
+        text = rng.integers(0, V, P + L + 4)
+        block = rng.integers(0, V, (P, Kc)).astype(np.int32)
+        if P:
+            block[:, 0] = np.where(rng.random(P) < 0.8, text[:P], block[:, 0])
+        ng = np.full((P + 1, L), -1, np.int32)
+        ngl = rng.integers(0, L + 1, P + 1).astype(np.int32)
+        for s_ in range(P + 1):
+            seq = text[s_:s_ + L] if rng.random() < 0.7 else rng.integers(0, V, L)
+            ng[s_] = seq
+        nd = 1 + P * Kc
+        depth_max = int(rng.choice([64, int(rng.integers(1, 8))]))
+        c_max = int(rng.choice([nd + (P + 1) * L, nd + int(rng.integers(0, 6))]))
+        t = O.tree_build(block, ng, ngl, np.ones(c_max, np.float32), np.ones(c_max, np.float32),
+                         depth_max=depth_max, rows_cap=8)
+        chains = [ng[s_, :ngl[s_]] for s_ in range(P + 1)]
+        n, index, info, agreed = path_forest(block, chains, depth_max, c_max)
+        tok, par, kind = t["f_token"], t["f_parent"], t["f_kind"]
+        assert t["count"] == n
+        for j in range(1, n):
+            path, parent = info[j]
+            assert tok[j] == path[-1] and par[j] == parent, (j, path)
+            assert bool(kind[j] & 4) == (j in agreed), j
+            assert (kind[j] & 3) == (3 if j >= nd else (1 if (j - 1) % Kc == 0 else 2))
+
+
 def chain_tree(tokens):
     n = len(tokens) + 1
     node_token = np.full(n, -1, np.int32)
