@@ -164,6 +164,34 @@ def test_forest_is_the_set_of_chain_paths(seed):
             assert (kind[j] & 3) == (3 if j >= nd else (1 if (j - 1) % Kc == 0 else 2))
 
 
+@pytest.mark.parametrize("rows_cap", [1, 2, 5, 16, 64])
+def test_rows_are_the_depth_first_order_of_the_best_nodes(rows_cap):
+    """The rows of the tree build from their definition (AdaSpark Section
+    3.1): the rows_cap - 1 best candidates by Q (fp32, ties to the lower
+    index), with the anchor, laid out depth first from the anchor with each
+    node's children in index order, by a recursive walk."""
+    rng = np.random.default_rng(31 + rows_cap)
+    for _ in range(40):
+        P, Kc, L = int(rng.integers(0, 6)), int(rng.integers(1, 4)), int(rng.integers(0, 8))
+        block, ng, ngl, wn, wz = random_forest_inputs(rng, P, Kc, L, V=5)
+        t = O.tree_build(block, ng, ngl, wn, wz, depth_max=int(rng.integers(1, 10)), rows_cap=rows_cap)
+        cnt, tok, par, fq = t["count"], t["f_token"], t["f_parent"], t["f_Q"]
+        order = sorted(range(1, cnt), key=lambda j: (-float(np.float32(fq[j])), j))
+        chosen = {0} | set(order[:rows_cap - 1])
+        rows = []
+        def visit(u, prow):
+            me = len(rows)
+            rows.append((-1 if u == 0 else int(tok[u]), prow, float(fq[u])))
+            for c in range(1, cnt):
+                if c in chosen and par[c] == u:
+                    visit(c, me)
+        visit(0, -1)
+        n = t["n_rows"]
+        assert n == len(rows) == min(rows_cap, cnt)
+        assert [(int(t["node_token"][i]), int(t["parent_row"][i]), float(t["Q"][i])) for i in range(n)] == rows
+        assert all(t["node_token"][i] == -1 and t["parent_row"][i] == -1 for i in range(n, rows_cap))
+
+
 def chain_tree(tokens):
     n = len(tokens) + 1
     node_token = np.full(n, -1, np.int32)
