@@ -192,6 +192,27 @@ def test_rows_are_the_depth_first_order_of_the_best_nodes(rows_cap):
         assert all(t["node_token"][i] == -1 and t["parent_row"][i] == -1 for i in range(n, rows_cap))
 
 
+def test_path_probabilities_from_the_weights():
+    """Q of every node from its definition (AdaSpark Section 3.3, the
+    Eq. (6) form with given weights): a node's share of its parent is its
+    weight over the parent's 'none' weight plus all its children's weights
+    (summed in index order), and Q is the product of the shares down the
+    path, in fp64, on random forests and weights."""
+    rng = np.random.default_rng(4242)
+    for _ in range(80):
+        P, Kc, L = int(rng.integers(0, 6)), int(rng.integers(1, 4)), int(rng.integers(0, 8))
+        block, ng, ngl, wn, wz = random_forest_inputs(rng, P, Kc, L, V=5)
+        t = O.tree_build(block, ng, ngl, wn, wz, depth_max=int(rng.integers(1, 10)), rows_cap=4)
+        cnt, par, fq = t["count"], t["f_parent"], t["f_Q"]
+        den = [float(wz[p]) for p in range(cnt)]
+        for c in range(1, cnt):
+            den[par[c]] += float(wn[c])
+        q = [1.0] * cnt
+        for j in range(1, cnt):
+            q[j] = q[par[j]] * (float(wn[j]) / den[par[j]])
+        assert list(map(float, fq)) == q
+
+
 def chain_tree(tokens):
     n = len(tokens) + 1
     node_token = np.full(n, -1, np.int32)
