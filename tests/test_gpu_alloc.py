@@ -405,6 +405,71 @@ def test_tree_build_degenerate_shapes(P, Kc, L, extra):
                 assert np.array_equal(g["row_base"], np.concatenate([[0], np.cumsum(g["n_rows"])[:-1]]))
 
 
+def test_tree_build_random_sweep():
+    """400 random tree builds (AdaSpark Sections 3.1 and 3.3) against the
+    oracle: 0 to 20 positions, 1 to 4 candidates, chains of up to 40 tokens
+    that mostly continue a text from each pick (picks mostly follow it),
+    vocabularies of 2 to 6 tokens, c_max from the block's size to 1,024 (both
+    chain walks), depth limits, 1 to 64 rows, given weights or Eq. (6)
+    scores with follower counts."""
+    import torch
+    import draft_verification_spec_amd as S
+    rng = np.random.default_rng(20261203)
+    BS, done = 16, 0
+    while done < 400:
+        P, Kc, L, V = int(rng.integers(0, 21)), int(rng.integers(1, 5)), int(rng.integers(0, 41)), int(rng.integers(2, 7))
+        if (P + 1) * L > 2048:
+            continue
+        text = rng.integers(0, V, (BS, P + L + 8))
+        block = rng.integers(0, V, (BS, P, Kc)).astype(np.int32)
+        if P:
+            block[:, :, 0] = np.where(rng.random((BS, P)) < 0.8, text[:, :P], block[:, :, 0])
+        ng = rng.integers(0, V, (BS * (P + 1), L)).astype(np.int32)
+        for r in range(BS):
+            for c in range(P + 1):
+                if L and rng.random() < 0.7:
+                    ng[r * (P + 1) + c] = text[r, c:c + L]
+        ngl = rng.integers(0, L + 1, BS * (P + 1)).astype(np.int32)
+        nd = 1 + P * Kc
+        c_max = max(nd, int(min(1024, rng.choice([nd + (P + 1) * L, nd + int(rng.integers(0, 30)), 1024]))))
+        dmax = int(rng.choice([64, int(rng.integers(1, 12))]))
+        rows_cap = int(rng.choice([1, 2, 8, 16, 24, 64]))
+        scored = P > 0 and bool(rng.random() < 0.5)
+        tag = f"P {P} Kc {Kc} L {L} V {V} c_max {c_max} depth {dmax} rows {rows_cap} scored {scored}"
+        if done % 50 == 0:
+            print(f"tree build, random sweep {done}: {tag}", flush=True)
+        if scored:
+            fol = np.where(rng.random((BS * (P + 1), L)) < 0.6, 0, rng.integers(1, 300, (BS * (P + 1), L))).astype(
+                np.int32)
+            feat = np.zeros((BS * (P + 1), 4), np.int32)
+            feat[:, 0] = rng.integers(1, 16, BS * (P + 1))
+            f = synth.tree_score_inputs(BS, P, Kc)
+            per = [dict(coef=f["coef"], h=f["h"][r], sigma=f["sigma"][r], r_share=f["r_share"][r],
+                        psi_ctx=f["psi_ctx"][r], b_req=f["b_req"][r], p_src=f["p_src"][r],
+                        ng_feat=feat.reshape(BS, P + 1, 4)[r]) for r in range(BS)]
+            sc = dict(coef=f["coef"], h=dev(f["h"]), sigma=dev(f["sigma"]), r_share=dev(f["r_share"]),
+                      psi_ctx=dev(f["psi_ctx"]), b_req=dev(f["b_req"]), p_src=dev(f["p_src"]), ngram_feat=dev(feat))
+            o = O.tree_build_batch(block, ng, ngl, depth_max=dmax, rows_cap=rows_cap, scores=per, c_max=c_max,
+                                   ng_follow=fol)
+            g = S.spec_allocate_budget(mode="tree", block=dev(block), ngram_draft=dev(ng), ngram_len=dev(ngl),
+                                       ngram_follow=dev(fol), scores=sc, c_max=c_max, depth_max=dmax,
+                                       rows_cap=rows_cap, s_curve=True)
+        else:
+            wn = rng.standard_exponential((BS, c_max)).astype(np.float32)
+            wz = rng.standard_exponential((BS, c_max)).astype(np.float32)
+            o = O.tree_build_batch(block, ng, ngl, wn, wz, dmax, rows_cap)
+            g = S.spec_allocate_budget(mode="tree", block=dev(block), ngram_draft=dev(ng), ngram_len=dev(ngl),
+                                       w_node=dev(wn), w_none=dev(wz), depth_max=dmax, rows_cap=rows_cap)
+        torch.cuda.synchronize()
+        g = {k: host(v) for k, v in g.items()}
+        ok = ok_rows(o["flags"])
+        assert_rows_equal(g["forest_count"], o["count"], np.ones(BS, bool), f"forest_count ({tag})")
+        for k in ("node_token", "parent_row", "n_rows"):
+            assert_rows_equal(g[k], o[k], ok, f"{k} ({tag})")
+        assert_close(g["Q"], o["Q"], f"Q ({tag})")
+        done += 1
+
+
 @pytest.mark.parametrize("BS", [1, 63, 1000, 1024, 1025, 1500])
 def test_tree_row_bases_any_batch(BS):
     """Row bases and the total over every batch size the row scan handles in
